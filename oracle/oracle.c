@@ -1,0 +1,583 @@
+/*
+ * oracle.c -- CPU oracle of the exact block-quantized dot product (decode GEMV and its
+ * batched-column form).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg load this library.  It shares no source, header, table or helper with the GPU path,
+ * and it reads a matrix only through its logical fields (codes, sub-block scales and
+ * offsets, binary16 block scales), never through the packed GPU image.
+ *
+ * What it follows (page title, then the item on that page):
+ *   [N]  rustdoc page "Module numerics" of logicaffeine_compile::spatial::decode_engine:
+ *        the module description (the two activation scalings, in-order row sums, the f32
+ *        model), Structs ActRow / ActScale / CodedRow / Scale / Segment / Unreadable,
+ *        Constants COEF_BOUND / SUM_WINDOW / NAN / WIDE_BITS / ACT_BLOCK / GROUP, Functions
+ *        absmax / block_scale / wide_scale / rne / rne_div / quantize / quantize_blocks /
+ *        exact_sum / scaled_to_f32 / ftz / fadd / dot.
+ *   [L]  rustdoc page "Module lane" of the same crate: the module description (a block's
+ *        coefficient sum and offset sum, times the block scales and the activation scale,
+ *        summed exactly, rounded once, added into the row) and Functions block_sums / group /
+ *        lane.
+ *
+ * Readings taken where the pages leave a step open (each is also listed in the design notes):
+ *   R1  Q4_K-style weight w = d*sc*q - dmin*mn; the second scale multiplies the offset term
+ *       with a minus sign.  Q6_K-style w = d*sc*(q-32), no offset term.
+ *   R2  binary16 block scales are read exactly, subnormals and zeros included; an exponent
+ *       field of 31 (inf/NaN) makes the block Unreadable.
+ *   R3  every activation element is read through ftz before the absmax and before coding;
+ *       a NaN element is passed over by the absmax and gets code 0; +-inf is an error.
+ *   R4  an all-zero activation block (absmax +0) takes the scale m = lo (128 or 8), e = 0,
+ *       with every code 0.
+ *   R5  "rounded once to f32, denormal flushed" = IEEE binary32 round-to-nearest-even on the
+ *       gradual-underflow grid, then a subnormal result becomes a zero of its sign;
+ *       a result past the largest finite value is infinite; an exact zero is +0.
+ *   R6  a row's sum starts at +0 and adds the pieces in ascending block (group) order with
+ *       binary32 adds, each result flushed; any NaN output is 0x7FC00000.
+ *   R7  SUM_WINDOW (its value is not printed) is taken as 64.  A term's "least place" is the
+ *       exponent it is formed with; the largest term is the one of largest magnitude, the
+ *       lowest index among equals; a term below the window is floored (toward -inf) to a
+ *       multiple of 2^(L - 64).  The window never engages at the shipped workloads.
+ *   R8  PerBlock activation blocks are the weight format's own 256-element block; Sub32
+ *       blocks are 32 elements and a 256-element group is one weight block.
+ *
+ * Build: plain C11 + GCC's __int128, -O2 -ffp-contract=off, no fast-math (SSE binary32
+ * adds with the default MXCSR: no FTZ/DAZ).  Rows may be spread over OpenMP threads; the
+ * arithmetic of each row is the same sequential loop whatever the thread count.
+ *
+ * OR_MUTANT (0 = none) plants one deliberate mistake; only the oracle's own pin tests build
+ * such variants, to show that some pin fails for each.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#ifndef OR_MUTANT
+#define OR_MUTANT 0
+#endif
+
+typedef __int128 i128;
+typedef unsigned __int128 u128;
+
+#define OR_SUM_WINDOW 64
+#define OR_COEF_BOUND 4096
+#define OR_BLOCK 256
+
+enum {
+    OR_OK = 0,
+    OR_E_NONFINITE = 1,   /* an activation block holds +-inf */
+    OR_E_SHAPE = 2,       /* columns not a whole number of 256-element blocks, bad mode */
+    OR_E_UNREADABLE = 3,  /* a block scale is inf or NaN (Unreadable) */
+    OR_E_RANGE = 4,       /* a code, sub-scale or offset outside its field */
+    OR_E_INTERNAL = 5     /* an exactness assertion failed */
+};
+
+static int g_threads = 1;
+
+void or_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
+int or_get_threads(void) { return g_threads; }
+
+/* ------------------------------------------------------------------------------------- */
+/* binary32 bits                                                                           */
+
+static uint32_t bits_of(float x) { uint32_t u; memcpy(&u, &x, 4); return u; }
+static float float_of(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
+
+/* [N] ftz: a denormal becomes a zero of the same sign. */
+float or_ftz(float x)
+{
+    uint32_t u = bits_of(x);
+    if ((u & 0x7F800000u) == 0) u &= 0x80000000u;
+    return float_of(u);
+}
+
+/* A finite nonzero binary32 as X * 2^ex with X a signed integer of at most 24 bits. */
+static void f32_split(float x, int64_t *X, int *ex)
+{
+    uint32_t u = bits_of(x);
+    int E = (int)((u >> 23) & 255u);
+    int64_t M = (int64_t)(u & 0x7FFFFFu);
+    if (E == 0) { *X = M; *ex = -149; }
+    else { *X = M | 0x800000; *ex = E - 150; }
+    if (u >> 31) *X = -*X;
+}
+
+static int bitlen_u128(u128 v)
+{
+    int n = 0;
+    while (v) { v >>= 1; n++; }
+    return n;
+}
+
+/* [N] scaled_to_f32 (reading R5): v * 2^exp rounded once to binary32, nearest with ties to
+ * even on the gradual-underflow grid, past the top infinite, then a subnormal result
+ * flushed to a zero of its sign. */
+float or_r32(i128 v, int exp)
+{
+    if (v == 0) return 0.0f;
+    uint32_t sign = v < 0 ? 0x80000000u : 0u;
+    u128 M = v < 0 ? (u128)(-v) : (u128)v;
+    int n = bitlen_u128(M);
+    int top = exp + n - 1;                          /* place of the leading bit */
+    int q = top - 23;                               /* place of the last kept bit ... */
+    if (q < -149) q = -149;                         /* ... never finer than the subnormal grid */
+    u128 R;
+    int shift = q - exp;
+    if (shift <= 0) {
+        R = M << (-shift);                          /* exact, fewer than 24 bits */
+    } else if (shift >= 128) {
+        R = 0;                                      /* below half the quantum: rounds to 0 */
+    } else {
+        R = M >> shift;
+        u128 rem = M - (R << shift);
+        u128 half = (u128)1 << (shift - 1);
+#if OR_MUTANT == 3
+        if (rem >= half) R += 1;                    /* MUTANT: ties away from zero */
+#else
+        if (rem > half || (rem == half && (R & 1))) R += 1;
+#endif
+    }
+    if (R == ((u128)1 << 24)) { R >>= 1; q += 1; }  /* rounding carried into a new binade */
+#if OR_MUTANT == 4
+    /* MUTANT: decide the flush before rounding (24-bit significand, then flush) */
+    if (top < -126) return float_of(sign);
+#endif
+    if (R < ((u128)1 << 23)) return float_of(sign);   /* subnormal or zero: flushed */
+    int biased = q + 23 + 127;
+    if (biased > 254) return float_of(sign | 0x7F800000u);
+    return float_of(sign | ((uint32_t)biased << 23) | (uint32_t)(R - ((u128)1 << 23)));
+}
+
+float or_scaled_to_f32(int64_t v, int exp) { return or_r32((i128)v, exp); }
+
+/* ------------------------------------------------------------------------------------- */
+/* [N] exact_sum, reading R7                                                                */
+
+typedef struct { i128 v; int e; } term_t;
+
+/* -1, 0, 1 as |a.v|*2^a.e is below, equal to, above |b.v|*2^b.e */
+static int mag_cmp(term_t a, term_t b)
+{
+    u128 A = a.v < 0 ? (u128)(-a.v) : (u128)a.v;
+    u128 B = b.v < 0 ? (u128)(-b.v) : (u128)b.v;
+    if (A == 0 || B == 0) return (A != 0) - (B != 0);
+    int ta = a.e + bitlen_u128(A), tb = b.e + bitlen_u128(B);
+    if (ta != tb) return ta > tb ? 1 : -1;
+    /* same leading place: bring both to the smaller exponent (no overflow: same bit length) */
+    if (a.e > b.e) A <<= (a.e - b.e); else B <<= (b.e - a.e);
+    return (A > B) - (A < B);
+}
+
+static i128 floor_shift(i128 v, int s)
+{
+    if (s >= 127) return v < 0 ? -1 : 0;
+    return v >> s;                                  /* GCC: arithmetic shift = floor */
+}
+
+/* Sum of v*2^e over the terms, rounded once: exact while every term's exponent is at least
+ * SUM_WINDOW below the largest term's exponent; a term further down is floored there. */
+static int exact_sum(const term_t *t, int n, float *out)
+{
+    if (n == 0) { *out = 0.0f; return OR_OK; }
+    int L = 0;
+    for (int i = 1; i < n; i++)
+        if (mag_cmp(t[i], t[L]) > 0) L = i;         /* strict: the first of equals stays */
+    int floor_e = t[L].e - OR_SUM_WINDOW;
+    term_t u[32];
+    if (n > 32) return OR_E_INTERNAL;
+    int emin = 0;
+    for (int i = 0; i < n; i++) {
+        u[i] = t[i];
+        if (u[i].e < floor_e) { u[i].v = floor_shift(u[i].v, floor_e - u[i].e); u[i].e = floor_e; }
+        if (i == 0 || u[i].e < emin) emin = u[i].e;
+    }
+    i128 s = 0;
+    const i128 lim = (i128)1 << 120;
+    for (int i = 0; i < n; i++) {
+        int sh = u[i].e - emin;
+        if (u[i].v == 0) continue;
+        if (sh > 118) return OR_E_INTERNAL;
+        i128 w = u[i].v * ((i128)1 << sh);
+        if (w > lim || w < -lim) return OR_E_INTERNAL;
+        s += w;
+    }
+    *out = or_r32(s, emin);
+    return OR_OK;
+}
+
+int or_exact_sum_i64(int n, const int64_t *v, const int32_t *e, float *out)
+{
+    term_t t[32];
+    if (n < 0 || n > 32) return OR_E_SHAPE;
+    for (int i = 0; i < n; i++) { t[i].v = v[i]; t[i].e = e[i]; }
+    return exact_sum(t, n, out);
+}
+
+/* ------------------------------------------------------------------------------------- */
+/* [N] Scale / Unreadable (reading R2): a binary16 block scale as sig * 2^exp, exactly.      */
+
+static int f16_scale(uint16_t h, int64_t *sig, int *ex)
+{
+    int s = h >> 15, E = (h >> 10) & 31, M = h & 1023;
+    if (E == 31) return OR_E_UNREADABLE;
+    if (E == 0) { *sig = M; *ex = -24; }
+    else { *sig = 1024 + M; *ex = E - 25; }
+    if (s) *sig = -*sig;
+    return OR_OK;
+}
+
+int or_f16_scale(uint16_t h, int64_t *sig, int32_t *ex)
+{
+    int e = 0;
+    int r = f16_scale(h, sig, &e);
+    *ex = e;
+    return r;
+}
+
+/* ------------------------------------------------------------------------------------- */
+/* Activation quantization                                                                 */
+
+/* ceil(A * 2^a / (127 * 2^e)), A > 0, exact; a - e stays within a few dozen places here. */
+static i128 ceil_ratio(int64_t A, int a, int e)
+{
+    int k = a - e;
+    if (k >= 0) {
+        i128 num = (i128)A << k;
+        return (num + 126) / 127;
+    }
+    k = -k;
+    if (k > 100) return 1;
+    i128 den = (i128)127 << k;
+    return ((i128)A + den - 1) / den;
+}
+
+/* [N] wide_scale (lo = 128, an 8-bit significand) and block_scale (lo = 8, a 4-bit one):
+ * the least m * 2^e with lo <= m < 2*lo and 127 * m * 2^e >= amax, amax finite and > 0.
+ * Walk the exponent down from a grid so coarse that m = lo is already enough, for as long
+ * as a finer grid still has an admissible significand; the least value sits at the last
+ * such exponent, with the least m there that reaches amax. */
+static void least_scale(float amax, int lo, int *m, int *e)
+{
+    int64_t A; int a;
+    f32_split(amax, &A, &a);
+    int ee = a + 26;                                /* 127 * 2^ee > A * 2^a: one grid step covers amax */
+#if OR_MUTANT == 8
+    while (ceil_ratio(A, a, ee - 1) <= 2 * lo - 2) ee--;   /* MUTANT: admits one m too few */
+#else
+    while (ceil_ratio(A, a, ee - 1) <= 2 * lo - 1) ee--;
+#endif
+    i128 mm = ceil_ratio(A, a, ee);
+    if (mm < lo) mm = lo;
+    *m = (int)mm;
+    *e = ee;
+}
+
+int or_least_scale(int lo, float amax, int32_t *m, int32_t *e)
+{
+    if (!(amax > 0.0f) || isinf(amax)) return OR_E_NONFINITE;
+    int mm, ee;
+    least_scale(amax, lo, &mm, &ee);
+    *m = mm; *e = ee;
+    return OR_OK;
+}
+
+/* [N] rne_div / rne: the nearest integer to x / (m * 2^e), ties to even, exactly. */
+static int64_t rne_div(float x, int m, int e)
+{
+    if (x == 0.0f) return 0;
+    int64_t X; int ex;
+    f32_split(x, &X, &ex);
+    int k = ex - e;                                 /* x / s = X * 2^k / m */
+    u128 num = X < 0 ? (u128)(-X) : (u128)X;
+    u128 den = (u128)m;
+    if (k >= 0) {
+        if (k > 60) return X < 0 ? -(1LL << 40) : (1LL << 40);   /* never: |x/s| <= 127 */
+        num <<= k;
+    } else {
+        if (-k > 100) return 0;
+        den <<= -k;
+    }
+    u128 q = num / den, r = num - q * den;
+#if OR_MUTANT == 5
+    if (2 * r >= den) q++;                          /* MUTANT: ties away from zero */
+#else
+    if (2 * r > den || (2 * r == den && (q & 1))) q++;
+#endif
+    return X < 0 ? -(int64_t)q : (int64_t)q;
+}
+
+int64_t or_rne_div(float x, int m, int e) { return rne_div(or_ftz(x), m, e); }
+
+/* [N] absmax: the largest magnitude, a denormal read as 0, folded from +0, NaN passed over. */
+static float absmax(const float *x, int64_t n)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < n; i++) {
+#if OR_MUTANT == 6
+        float v = x[i];                             /* MUTANT: no flush of denormal operands */
+#else
+        float v = or_ftz(x[i]);
+#endif
+        if (isnan(v)) continue;
+        v = fabsf(v);
+        if (v > a) a = v;
+    }
+    return a;
+}
+
+/* [N] quantize_blocks (mode 0: PerBlock, one scale per `block` elements, 8-bit significand)
+ * and quantize (mode 1: Sub32, one scale per 32 elements, 4-bit significand).
+ * x: f32 [n][cols]; codes: int8 [n][cols]; sm, se: the scale's m and e per activation
+ * block, [n][cols/ablk]; sums16: int32 [n][cols/16], the sum of the codes of each run of
+ * 16 elements (the activation side's per-unit code sums of the lane page). */
+int or_quantize(int mode, int block, int64_t n, int64_t cols, const float *x, int8_t *codes,
+                uint8_t *sm, int16_t *se, int32_t *sums16)
+{
+    if (mode != 0 && mode != 1) return OR_E_SHAPE;
+    if (cols < 0 || n < 0 || cols % OR_BLOCK) return OR_E_SHAPE;
+    int ablk = mode == 0 ? block : 32;
+    int lo = mode == 0 ? 128 : 8;
+    if (ablk <= 0 || cols % ablk || ablk % 16) return OR_E_SHAPE;
+    int64_t nb = cols / ablk;
+    int status = OR_OK;
+    for (int64_t r = 0; r < n; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const float *xb = x + r * cols + b * ablk;
+            float amax = absmax(xb, ablk);
+            int m, e;
+            if (isinf(amax)) { status = OR_E_NONFINITE; m = 0; e = 0; }
+            else if (amax == 0.0f) { m = lo; e = 0; }
+            else least_scale(amax, lo, &m, &e);
+            sm[r * nb + b] = (uint8_t)m;
+            se[r * nb + b] = (int16_t)e;
+            for (int i = 0; i < ablk; i++) {
+                float v = or_ftz(xb[i]);
+                int64_t c = 0;
+                if (m != 0 && !isnan(v)) c = rne_div(v, m, e);
+                if (c > 127 || c < -127) return OR_E_INTERNAL;   /* 127*m*2^e >= amax bounds it */
+                codes[r * cols + b * ablk + i] = (int8_t)c;
+            }
+        }
+        for (int64_t u = 0; u < cols / 16; u++) {
+            int32_t s = 0;
+            for (int i = 0; i < 16; i++) s += codes[r * cols + u * 16 + i];
+            sums16[r * (cols / 16) + u] = s;
+        }
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------------------------- */
+/* The dot: one row of a block-format matrix against one quantized activation row          */
+
+/* [N] fadd + ftz, f32 model of the module description: binary32 add, nearest-even, result
+ * flushed.  Operands here are already normal or zero. */
+static float fadd(float a, float b) { return or_ftz(a + b); }
+
+static float canon_nan(float y)
+{
+    return isnan(y) ? float_of(0x7FC00000u) : y;    /* [N] NAN: quiet, no payload, no sign */
+}
+
+/* Integer sums of one 32-element sub-block of a Q4_K-style block, element by element
+ * ([L] block_sums): coefficient sum sum(sc*q*c) and offset sum sum(mn*c). */
+static void q4k_sub_sums(const uint8_t *q, int sc, int mn, const int8_t *c, int64_t *Cs, int64_t *Os)
+{
+    int64_t C = 0, O = 0;
+    for (int i = 0; i < 32; i++) {
+        int64_t coef = (int64_t)sc * q[i];
+        int64_t offs = mn;
+        C += coef * c[i];
+        O += offs * c[i];
+    }
+    *Cs = C; *Os = O;
+}
+
+/* Integer coefficient sum of one 16-element sub-block of a Q6_K-style block. */
+static int64_t q6k_sub_sum(const uint8_t *q, int sc, const int8_t *c)
+{
+    int64_t C = 0;
+    for (int i = 0; i < 16; i++) {
+        int64_t coef = (int64_t)sc * ((int64_t)q[i] - 32);
+        C += coef * c[i];
+    }
+    return C;
+}
+
+static int check_q4k_row(const uint8_t *q, const uint8_t *sc, const uint8_t *mn, int64_t cols)
+{
+    for (int64_t i = 0; i < cols; i++) if (q[i] > 15) return OR_E_RANGE;
+    for (int64_t j = 0; j < cols / 32; j++) if (sc[j] > 63 || mn[j] > 63) return OR_E_RANGE;
+    return OR_OK;
+}
+
+/* One Q4_K-style row.  mode 0: per block the two terms m*2^e * d * C_b and
+ * -m*2^e * dmin * O_b, summed exactly and rounded once ([N] module description, PerBlock;
+ * [L] lane).  mode 1: per 256-element group the 16 terms of its eight 32-element
+ * sub-blocks, each under its own activation scale, summed exactly and rounded once ([N]
+ * module description, Sub32; [L] group).  The pieces are then added in order. */
+static int q4k_row(int mode, int64_t cols, const uint8_t *q, const uint8_t *sc, const uint8_t *mn,
+                   const uint16_t *d, const uint16_t *dmin, const int8_t *c, const uint8_t *sm,
+                   const int16_t *se, float *out)
+{
+    int st = check_q4k_row(q, sc, mn, cols);
+    if (st) return st;
+    int64_t G = cols / OR_BLOCK;
+    float y = 0.0f;
+    float piece[4096];
+    if (G > 4096) return OR_E_SHAPE;
+    for (int64_t b = 0; b < G; b++) {
+        int64_t sd, sm2; int ed, em;
+        if (f16_scale(d[b], &sd, &ed) || f16_scale(dmin[b], &sm2, &em)) return OR_E_UNREADABLE;
+        term_t t[16];
+        int nt = 0;
+        if (mode == 0) {
+            int64_t Cb = 0, Ob = 0;
+            for (int j = 0; j < 8; j++) {
+                int64_t Cj, Oj;
+#if OR_MUTANT == 7
+                int jj = (j * 32) / 16 % 8;         /* MUTANT: sub-scale indexed per 16 elements */
+                q4k_sub_sums(q + b * 256 + j * 32, sc[b * 8 + jj], mn[b * 8 + jj], c + b * 256 + j * 32, &Cj, &Oj);
+#else
+                q4k_sub_sums(q + b * 256 + j * 32, sc[b * 8 + j], mn[b * 8 + j], c + b * 256 + j * 32, &Cj, &Oj);
+#endif
+                Cb += Cj; Ob += Oj;
+            }
+            int m = sm[b], e = se[b];
+            t[nt].v = (i128)m * sd * Cb; t[nt].e = e + ed; nt++;
+#if OR_MUTANT == 1
+            (void)em; (void)sm2;                    /* MUTANT: offset term dropped */
+#elif OR_MUTANT == 2
+            t[nt].v = (i128)m * sm2 * Ob; t[nt].e = e + em; nt++;     /* MUTANT: sign of offset term */
+#else
+            t[nt].v = -(i128)m * sm2 * Ob; t[nt].e = e + em; nt++;
+#endif
+        } else {
+            for (int j = 0; j < 8; j++) {
+                int64_t Cj, Oj;
+                q4k_sub_sums(q + b * 256 + j * 32, sc[b * 8 + j], mn[b * 8 + j], c + b * 256 + j * 32, &Cj, &Oj);
+                int m = sm[b * 8 + j], e = se[b * 8 + j];
+                t[nt].v = (i128)m * sd * Cj; t[nt].e = e + ed; nt++;
+                t[nt].v = -(i128)m * sm2 * Oj; t[nt].e = e + em; nt++;
+            }
+        }
+        st = exact_sum(t, nt, &piece[b]);
+        if (st) return st;
+    }
+#if OR_MUTANT == 9
+    /* MUTANT: pieces folded by a balanced pairwise tree instead of in order */
+    for (int64_t w = 1; w < G; w *= 2)
+        for (int64_t i = 0; i + w < G; i += 2 * w) piece[i] = fadd(piece[i], piece[i + w]);
+    y = G ? fadd(0.0f, piece[0]) : 0.0f;
+#else
+    for (int64_t b = 0; b < G; b++) y = fadd(y, piece[b]);
+#endif
+    *out = canon_nan(y);
+    return OR_OK;
+}
+
+static int q6k_row(int mode, int64_t cols, const uint8_t *q, const int8_t *sc, const uint16_t *d,
+                   const int8_t *c, const uint8_t *sm, const int16_t *se, float *out)
+{
+    for (int64_t i = 0; i < cols; i++) if (q[i] > 63) return OR_E_RANGE;
+    int64_t G = cols / OR_BLOCK;
+    float y = 0.0f;
+    for (int64_t b = 0; b < G; b++) {
+        int64_t sd; int ed;
+        if (f16_scale(d[b], &sd, &ed)) return OR_E_UNREADABLE;
+        term_t t[8];
+        int nt = 0;
+        if (mode == 0) {
+            int64_t Cb = 0;
+            for (int k = 0; k < 16; k++) Cb += q6k_sub_sum(q + b * 256 + k * 16, sc[b * 16 + k], c + b * 256 + k * 16);
+            t[nt].v = (i128)sm[b] * sd * Cb; t[nt].e = se[b] + ed; nt++;
+        } else {
+            /* a 32-element activation block covers two 16-element weight sub-blocks */
+            for (int j = 0; j < 8; j++) {
+                int64_t Cj = q6k_sub_sum(q + b * 256 + j * 32, sc[b * 16 + 2 * j], c + b * 256 + j * 32)
+                           + q6k_sub_sum(q + b * 256 + j * 32 + 16, sc[b * 16 + 2 * j + 1], c + b * 256 + j * 32 + 16);
+                t[nt].v = (i128)sm[b * 8 + j] * sd * Cj; t[nt].e = se[b * 8 + j] + ed; nt++;
+            }
+        }
+        float p;
+        int st = exact_sum(t, nt, &p);
+        if (st) return st;
+        y = fadd(y, p);
+    }
+    *out = canon_nan(y);
+    return OR_OK;
+}
+
+/* [N] dot, batched: out[col * rows + r] = dot(row r, activation row col).
+ * A single column (ncol = 1) is the decode GEMV. */
+int or_gemm_q4k(int mode, int64_t rows, int64_t cols, int64_t ncol, const uint8_t *q, const uint8_t *sc,
+                const uint8_t *mn, const uint16_t *d, const uint16_t *dmin, const int8_t *codes,
+                const uint8_t *sm, const int16_t *se, float *out)
+{
+    if ((mode != 0 && mode != 1) || cols % OR_BLOCK || rows < 0 || ncol < 0) return OR_E_SHAPE;
+    int64_t G = cols / OR_BLOCK, nsc = mode == 0 ? G : cols / 32;
+    int status = OR_OK;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(g_threads) if (g_threads > 1)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t k = 0; k < ncol; k++) {
+            int st = q4k_row(mode, cols, q + r * cols, sc + r * (cols / 32), mn + r * (cols / 32),
+                             d + r * G, dmin + r * G, codes + k * cols, sm + k * nsc, se + k * nsc,
+                             &out[k * rows + r]);
+            if (st) {
+#pragma omp critical
+                status = st;
+            }
+        }
+    }
+    return status;
+}
+
+int or_gemm_q6k(int mode, int64_t rows, int64_t cols, int64_t ncol, const uint8_t *q, const int8_t *sc,
+                const uint16_t *d, const int8_t *codes, const uint8_t *sm, const int16_t *se, float *out)
+{
+    if ((mode != 0 && mode != 1) || cols % OR_BLOCK || rows < 0 || ncol < 0) return OR_E_SHAPE;
+    int64_t G = cols / OR_BLOCK, nsc = mode == 0 ? G : cols / 32;
+    int status = OR_OK;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(g_threads) if (g_threads > 1)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t k = 0; k < ncol; k++) {
+            int st = q6k_row(mode, cols, q + r * cols, sc + r * (cols / 16), d + r * G,
+                             codes + k * cols, sm + k * nsc, se + k * nsc, &out[k * rows + r]);
+            if (st) {
+#pragma omp critical
+                status = st;
+            }
+        }
+    }
+    return status;
+}
+
+/* Integer sums per (row, 32-element sub-block) of a Q4_K-style matrix against one code row:
+ * Cs = sum sc*q*c and Os = sum mn*c ([L] block_sums, before any scale). [rows][cols/32]. */
+int or_sub_sums_q4k(int64_t rows, int64_t cols, const uint8_t *q, const uint8_t *sc, const uint8_t *mn,
+                    const int8_t *codes, int64_t *Cs, int64_t *Os)
+{
+    if (cols % OR_BLOCK) return OR_E_SHAPE;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t j = 0; j < cols / 32; j++)
+            q4k_sub_sums(q + r * cols + j * 32, sc[r * (cols / 32) + j], mn[r * (cols / 32) + j],
+                         codes + j * 32, &Cs[r * (cols / 32) + j], &Os[r * (cols / 32) + j]);
+    return OR_OK;
+}
+
+/* Coefficient sums per (row, 16-element sub-block) of a Q6_K-style matrix: sum sc*(q-32)*c. */
+int or_sub_sums_q6k(int64_t rows, int64_t cols, const uint8_t *q, const int8_t *sc, const int8_t *codes,
+                    int64_t *Cs)
+{
+    if (cols % OR_BLOCK) return OR_E_SHAPE;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t k = 0; k < cols / 16; k++)
+            Cs[r * (cols / 16) + k] = q6k_sub_sum(q + r * cols + k * 16, sc[r * (cols / 16) + k], codes + k * 16);
+    return OR_OK;
+}
+
+int or_mutant(void) { return OR_MUTANT; }
+int or_coef_bound(void) { return OR_COEF_BOUND; }
+int or_sum_window(void) { return OR_SUM_WINDOW; }
