@@ -1,0 +1,286 @@
+"""Benchmark of the exact block-quantized decode GEMV on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic activation row: quantize the
+f32 row (qg_quantize_act) and run the GEMV over the packed matrix (qg_gemv_q), both on the
+current stream, inputs resident in HBM.  The default workload is the Llama-8B-shaped FFN
+up-projection, 14336 x 4096 Q4_K-style, PerBlock scaling, fresh activations every step,
+and the weights are read cold: each step uses the next of C copies of the image
+(C * 33 MB >= 512 MB, twice the 256 MB Infinity Cache).
+
+Timing:
+  * ms_per_step: the K timed steps are captured in HIP graphs (one graph node per kernel)
+    and replayed between two events after a synchronize; whole-job weight GB/s = K * image
+    bytes / elapsed.
+  * roofline.achieved: the GEMV kernel's own duration, from HIP events that the launch
+    records around the kernel (hipExtLaunchKernelGGL via qg_time_next_launch) on the
+    stream it runs on, averaged over the same rotated-cold launches.
+  * cpu_baseline: the CPU oracle on the same workload, all rows, fresh activations, for
+    about --cpu-seconds of host time, on the host's cores (threads stated).
+
+Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "quantized GEMV weight-stream HBM GB/s (% of peak) and rows/s at 1 GPU"
+
+WORKLOADS = {
+    # name: (format, rows, cols, scaling, columns)
+    "q4k_ffn_up_14336x4096": ("q4k", 14336, 4096, 0, 1),
+    "q4k_attn_4096x4096": ("q4k", 4096, 4096, 0, 1),
+    "q6k_output_128256x4096": ("q6k", 128256, 4096, 0, 1),
+    "q4k_sub32_14336x4096": ("q4k", 14336, 4096, 1, 1),
+    "q4k_gemm_n2_14336x4096": ("q4k", 14336, 4096, 0, 2),
+    "q4k_gemm_n8_14336x4096": ("q4k", 14336, 4096, 0, 8),
+    "q4k_gemm_n64_14336x4096": ("q4k", 14336, 4096, 0, 64),
+}
+DEFAULT = "q4k_ffn_up_14336x4096"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=1600)
+    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    p.add_argument("--cold-bytes", type=float, default=512e6, help="rotate over at least this many weight bytes")
+    p.add_argument("--warm", action="store_true", help="one copy of the weights (cache-resident)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--kernel-launches", type=int, default=400)
+    return p.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls bench.py makes itself (events)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.L.hipEventSynchronize(ctypes.c_void_p(b)) == 0
+        assert self.L.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def make_inputs(wl, n_act):
+    from workloads import gen
+
+    fmt, rows, cols, mode, ncol = wl
+    if fmt == "q4k":
+        fields = gen.q4k_fields(rows, cols, gen.SEED_ATTN_W if rows == 4096 else gen.SEED_FFN_W)
+    else:
+        fields, _ = gen.output_q6k()
+    if ncol > 1:
+        xs = [gen.act_normal(ncol, cols, gen.SEED_BATCH_X + ncol + 1000 * k) for k in range(n_act)]
+    elif mode == 1:
+        xs = [gen.sub32_act(k, cols)[0] for k in range(n_act)]
+    elif fmt == "q6k":
+        xs = [gen.act_normal(1, cols, gen.SEED_OUT_X + 1000 * k) for k in range(n_act)]
+    else:
+        xs = [gen.decode_act(k, cols) for k in range(n_act)]
+    return fields, xs
+
+
+def cpu_baseline(fields, xs, mode, seconds, image_bytes):
+    import oracle
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(16, cores))
+    oracle.set_threads(threads)
+    t0 = time.perf_counter()
+    steps = 0
+    outs = []
+    while True:
+        x = xs[steps % len(xs)]
+        c, m, e, _ = oracle.quantize(x, mode)
+        out = oracle.gemm(fields, c, m, e, mode)
+        if steps < 2:
+            outs.append(out)
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    rows = fields["rows"] * xs[0].shape[0]
+    return {
+        "value": round(steps * image_bytes / dt / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{steps} whole steps (quantize + all {fields['rows']} rows x {xs[0].shape[0]} column(s)) "
+                  f"of the same workload with fresh activations, {dt:.1f} s",
+        "rows_per_s": round(steps * rows / dt, 1),
+    }, outs
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_format_gemv_amd as qg
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = WORKLOADS[args.workload]
+    fmt_s, rows, cols, mode, ncol = wl
+    fmt = qg.FMT_CODES[fmt_s]
+    dev = torch.device("cuda:0")
+    hip = Hip()
+
+    n_act = 64
+    fields, xs = make_inputs(wl, n_act)
+    img_host = qg.pack(fields)
+    image_bytes = img_host.nbytes
+    copies = 1 if args.warm else max(1, int(np.ceil(args.cold_bytes / image_bytes)))
+    base = torch.from_numpy(img_host).to(dev)
+    images = [base] + [base.clone() for _ in range(copies - 1)]
+    x_dev = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in xs]
+    slots = max(copies, 16)
+    acts = [qg.alloc_act(ncol, cols, mode, dev) for _ in range(slots)]
+    outs = [torch.empty((ncol, rows), dtype=torch.float32, device=dev) for _ in range(slots)]
+    act_bytes = ncol * (cols + 4 * qg._nsc(mode, cols) + 4 * (cols // 16))
+    out_bytes = 4 * ncol * rows
+    algo_bytes = image_bytes + act_bytes + out_bytes
+
+    def step(i, stream=None):
+        a = acts[i % slots]
+        qg.qg_quantize_act(fmt, mode, ncol, cols, x_dev[i % n_act], a.codes, a.scales, a.csums, None, stream)
+        qg.qg_gemm_q(fmt, mode, rows, cols, ncol, images[i % copies], a.codes, a.scales, a.csums,
+                     outs[i % slots], stream)
+
+    # eager first pass, then a bitwise check of step 0 against the oracle on sampled rows
+    torch.cuda.synchronize()
+    step(0)
+    torch.cuda.synchronize()
+    first = outs[0].cpu().numpy().copy()
+
+    # HIP graphs of `gsteps` steps each: the timed K steps are replays, exactly K steps
+    gsteps = slots
+    s = torch.cuda.Stream()
+    graphs = {}
+
+    def graph_of(nsteps, offset):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(nsteps):
+                step(offset + i)
+        return g
+
+    full = graph_of(gsteps, 0)
+    rest = args.steps % gsteps
+    tail = graph_of(rest, 0) if rest else None
+    torch.cuda.synchronize()
+    for _ in range(max(1, -(-args.warmup // gsteps))):
+        full.replay()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        torch.cuda.synchronize()
+        t_start.record(s)
+        for _ in range(args.steps // gsteps):
+            full.replay()
+        if tail is not None:
+            tail.replay()
+        t_end.record(s)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+
+    # the GEMV kernel's own duration: events recorded by the launch around the kernel
+    evs = [(hip.event(), hip.event()) for _ in range(args.kernel_launches)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(evs):
+        a = acts[i % slots]
+        qg.qg_quantize_act(fmt, mode, ncol, cols, x_dev[i % n_act], a.codes, a.scales, a.csums, None, None)
+        qg.qg_time_next_launch(e0, e1)
+        qg.qg_gemm_q(fmt, mode, rows, cols, ncol, images[i % copies], a.codes, a.scales, a.csums, outs[i % slots])
+    torch.cuda.synchronize()
+    k_ms = np.array([hip.elapsed_ms(e0, e1) for e0, e1 in evs])
+    for e0, e1 in evs:
+        hip.destroy(e0)
+        hip.destroy(e1)
+    k_us = float(np.mean(k_ms[len(k_ms) // 8:]) * 1e3)   # the first launches warm the code path
+    achieved = algo_bytes / (k_us * 1e-6) / 1e9
+
+    value = args.steps * image_bytes / (ms_total * 1e-3) / 1e9
+    record = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "format": fmt_s,
+            "rows": rows,
+            "cols": cols,
+            "act_scaling": "perblock" if mode == 0 else "sub32",
+            "columns": ncol,
+            "weights": "cold, rotating over %d copies (%.0f MB)" % (copies, copies * image_bytes / 1e6)
+                       if copies > 1 else "warm, one copy (cache-resident)",
+            "step": "quantize_act + gemv_q, HIP graph replay",
+        },
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "rows_per_s": round(rows * ncol / (ms_per_step * 1e-3), 1),
+        "kernel_us": round(k_us, 3),
+        "kernel_us_p10_p90": [round(float(np.percentile(k_ms, 10)) * 1e3, 3),
+                              round(float(np.percentile(k_ms, 90)) * 1e3, 3)],
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "gemv_kernel (qg_gemm_q)",
+            "algorithmic_bytes_per_launch": algo_bytes,
+        },
+    }
+    if not args.no_cpu:
+        cb, cpu_outs = cpu_baseline(fields, xs, mode, args.cpu_seconds, image_bytes)
+        record["cpu_baseline"] = cb
+        record["parity_step0"] = bool(np.array_equal(cpu_outs[0].view(np.uint32),
+                                                     first.reshape(-1).view(np.uint32)))
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,265 @@
+"""Python binding of libqgemv.so: the exact block-quantized GEMV / GEMM for MI355X (gfx950).
+
+The functions named qg_* mirror the C ABI of include/qgemv.h one for one and only marshal
+arguments: torch tensors on the ROCm device are passed as device pointers, numpy arrays as
+host pointers, and the stream defaults to torch's current stream.  Every step of the path
+runs in the library's HIP kernels; there is no CPU fallback.  A nonzero status raises
+QGError with the library's reason.
+
+Convenience wrappers (pack, quantize_act, gemv, gemm) allocate outputs with torch and
+call the qg_* functions.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqgemv.so")
+
+Q4K, Q6K = 1, 2
+PERBLOCK, SUB32 = 0, 1
+OK, E_INVALID, E_SHAPE, E_UNSUPPORTED, E_UNREADABLE, E_NONFINITE, E_RUNTIME = range(7)
+TUNE_WAVES_PER_CU, TUNE_GRID_WGS, TUNE_PIPELINE = 1, 2, 3
+BLOCK = 256
+MAX_COLS = 32768
+
+EXPORTS = ("qg_reads", "qg_image_bytes", "qg_pack_q4k", "qg_pack_q6k", "qg_quantize_act", "qg_gemv_q",
+           "qg_gemm_q", "qg_block_sums", "qg_set_tuning", "qg_time_next_launch", "qg_last_error", "qg_version")
+
+
+class QGError(RuntimeError):
+    def __init__(self, status: int, reason: str):
+        super().__init__(f"status {status}: {reason}")
+        self.status = status
+        self.reason = reason
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+    L.qg_reads.argtypes = [i32, i32]
+    L.qg_image_bytes.argtypes = [i32, i64, i64]
+    L.qg_image_bytes.restype = ctypes.c_size_t
+    L.qg_pack_q4k.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp]
+    L.qg_pack_q6k.argtypes = [i64, i64, vp, vp, vp, vp]
+    L.qg_quantize_act.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.qg_gemv_q.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.qg_gemm_q.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.qg_block_sums.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
+    L.qg_set_tuning.argtypes = [i32, i64]
+    L.qg_time_next_launch.argtypes = [vp, vp]
+    L.qg_last_error.restype = ctypes.c_char_p
+    return L
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise QGError(status, _lib.qg_last_error().decode(errors="replace"))
+
+
+def _dptr(t):
+    """Device pointer of a torch tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a tensor on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _hptr(a: np.ndarray):
+    if not a.flags.c_contiguous:
+        raise ValueError("expected a C-contiguous array")
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# --- the C ABI, one for one ----------------------------------------------------------------
+
+def qg_reads(fmt: int, mode: int) -> bool:
+    return bool(_lib.qg_reads(fmt, mode))
+
+
+def qg_image_bytes(fmt: int, rows: int, cols: int) -> int:
+    return int(_lib.qg_image_bytes(fmt, rows, cols))
+
+
+def qg_pack_q4k(rows, cols, q, sc, mn, d, dmin, image) -> None:
+    _check(_lib.qg_pack_q4k(rows, cols, _hptr(q), _hptr(sc), _hptr(mn), _hptr(d), _hptr(dmin), _hptr(image)))
+
+
+def qg_pack_q6k(rows, cols, q, sc, d, image) -> None:
+    _check(_lib.qg_pack_q6k(rows, cols, _hptr(q), _hptr(sc), _hptr(d), _hptr(image)))
+
+
+def _need(t, nbytes: int, name: str) -> None:
+    """Refuse a device buffer smaller than the call will touch (the C ABI cannot see sizes)."""
+    if t is None:
+        return
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise QGError(E_SHAPE, f"{name} holds {have} bytes, the call needs {nbytes}")
+
+
+def _nsc(mode: int, cols: int) -> int:
+    return cols // (BLOCK if mode == PERBLOCK else 32)
+
+
+def _check_act(mode, n, cols, codes, scales, csums):
+    _need(codes, n * cols, "codes")
+    _need(scales, 4 * n * _nsc(mode, cols), "scales")
+    _need(csums, 4 * n * (cols // 16), "csums")
+
+
+def qg_quantize_act(fmt, mode, n, cols, x, codes, scales, csums, err_flag=None, stream=None) -> None:
+    if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32):
+        _need(x, 4 * n * cols, "x")
+        _check_act(mode, n, cols, codes, scales, csums)
+        _need(err_flag, 4, "err_flag")
+    _check(_lib.qg_quantize_act(fmt, mode, n, cols, _dptr(x), _dptr(codes), _dptr(scales), _dptr(csums),
+                                _dptr(err_flag), _stream(stream)))
+
+
+def _check_gemm(fmt, mode, rows, cols, n, image, codes, scales, csums, out):
+    if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32) and fmt in (Q4K, Q6K) and rows > 0:
+        _need(image, qg_image_bytes(fmt, rows, cols), "image")
+        _check_act(mode, n, cols, codes, scales, csums)
+        _need(out, 4 * n * rows, "out")
+
+
+def qg_gemv_q(fmt, mode, rows, cols, image, codes, scales, csums, out, stream=None) -> None:
+    _check_gemm(fmt, mode, rows, cols, 1, image, codes, scales, csums, out)
+    _check(_lib.qg_gemv_q(fmt, mode, rows, cols, _dptr(image), _dptr(codes), _dptr(scales), _dptr(csums),
+                          _dptr(out), _stream(stream)))
+
+
+def qg_gemm_q(fmt, mode, rows, cols, n, image, codes, scales, csums, out, stream=None) -> None:
+    _check_gemm(fmt, mode, rows, cols, n, image, codes, scales, csums, out)
+    _check(_lib.qg_gemm_q(fmt, mode, rows, cols, n, _dptr(image), _dptr(codes), _dptr(scales), _dptr(csums),
+                          _dptr(out), _stream(stream)))
+
+
+def qg_block_sums(fmt, rows, cols, image, codes, csum_out, osum_out=None, stream=None) -> None:
+    if cols > 0 and cols % BLOCK == 0 and fmt in (Q4K, Q6K) and rows > 0:
+        per = 32 if fmt == Q4K else 16
+        _need(image, qg_image_bytes(fmt, rows, cols), "image")
+        _need(codes, cols, "codes")
+        _need(csum_out, 4 * rows * (cols // per), "csum_out")
+        if fmt == Q4K:
+            _need(osum_out, 4 * rows * (cols // 32), "osum_out")
+    _check(_lib.qg_block_sums(fmt, rows, cols, _dptr(image), _dptr(codes), _dptr(csum_out), _dptr(osum_out),
+                              _stream(stream)))
+
+
+def qg_set_tuning(key: int, value: int) -> None:
+    _check(_lib.qg_set_tuning(key, value))
+
+
+def qg_time_next_launch(start_event, stop_event) -> None:
+    """Raw hipEvent_t handles (ints) or None."""
+    _check(_lib.qg_time_next_launch(ctypes.c_void_p(start_event) if start_event else None,
+                                    ctypes.c_void_p(stop_event) if stop_event else None))
+
+
+def qg_last_error() -> str:
+    return _lib.qg_last_error().decode(errors="replace")
+
+
+def qg_version() -> int:
+    return int(_lib.qg_version())
+
+
+# --- convenience wrappers ------------------------------------------------------------------
+
+FMT_CODES = {"q4k": Q4K, "q6k": Q6K}
+
+
+def pack(fields: dict) -> np.ndarray:
+    """Logical fields (see workloads/gen.py for the layout) -> host image (uint8)."""
+    fmt = FMT_CODES[fields["fmt"]]
+    rows, cols = int(fields["rows"]), int(fields["cols"])
+    img = np.empty(qg_image_bytes(fmt, rows, cols), np.uint8)
+    c = {k: np.ascontiguousarray(v) for k, v in fields.items() if isinstance(v, np.ndarray)}
+    if fmt == Q4K:
+        qg_pack_q4k(rows, cols, c["q"].astype(np.uint8, copy=False), c["sc"].astype(np.uint8, copy=False),
+                    c["mn"].astype(np.uint8, copy=False), c["d"].astype(np.uint16, copy=False),
+                    c["dmin"].astype(np.uint16, copy=False), img)
+    else:
+        qg_pack_q6k(rows, cols, c["q"].astype(np.uint8, copy=False), c["sc"].astype(np.int8, copy=False),
+                    c["d"].astype(np.uint16, copy=False), img)
+    return img
+
+
+class Act:
+    """A quantized activation batch on the GPU: codes [n, C] int8, scales [n, nsc] as int32
+    words (qg_act_scale), csums [n, C/16] int32."""
+
+    def __init__(self, codes, scales, csums, mode):
+        self.codes, self.scales, self.csums, self.mode = codes, scales, csums, mode
+
+    @property
+    def n(self):
+        return int(self.codes.shape[0])
+
+    def scale_fields(self):
+        """(m uint8 [n, nsc], e int16 [n, nsc]) as host numpy arrays."""
+        raw = self.scales.cpu().numpy().view(np.uint8).reshape(self.n, -1, 4)
+        e = raw[..., 0:2].copy().view(np.int16)[..., 0]
+        return raw[..., 2].copy(), e
+
+
+def alloc_act(n: int, cols: int, mode: int, device="cuda"):
+    import torch
+    nsc = cols // (BLOCK if mode == PERBLOCK else 32)
+    codes = torch.empty((n, cols), dtype=torch.int8, device=device)
+    scales = torch.empty((n, nsc), dtype=torch.int32, device=device)
+    csums = torch.empty((n, cols // 16), dtype=torch.int32, device=device)
+    return Act(codes, scales, csums, mode)
+
+
+def quantize_act(x, mode: int, fmt: int = Q4K, err_flag=None, stream=None, out: Act | None = None) -> Act:
+    """x: float32 [n, C] (or [C]) on the GPU -> Act."""
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    n, cols = x.shape
+    a = out if out is not None else alloc_act(n, cols, mode, x.device)
+    qg_quantize_act(fmt, mode, n, cols, x, a.codes, a.scales, a.csums, err_flag, stream)
+    return a
+
+
+def gemv(fmt: int, rows: int, cols: int, image, act: Act, out=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=act.codes.device)
+    qg_gemv_q(fmt, act.mode, rows, cols, image, act.codes, act.scales, act.csums, out, stream)
+    return out
+
+
+def gemm(fmt: int, rows: int, cols: int, image, act: Act, out=None, stream=None):
+    """out[c, r] (a [n, rows] view of the flat out[c*rows + r])."""
+    import torch
+    if out is None:
+        out = torch.empty((act.n, rows), dtype=torch.float32, device=act.codes.device)
+    qg_gemm_q(fmt, act.mode, rows, cols, act.n, image, act.codes, act.scales, act.csums, out, stream)
+    return out

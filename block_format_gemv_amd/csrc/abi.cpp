@@ -1,0 +1,202 @@
+// abi.cpp -- the extern "C" entry points: argument validation, reasons, launches.
+//
+// Refusals happen before any work, each with a reason naming what was wrong (the pages'
+// convention of refusing up front with a reason: bankML forward.md, "Technical usage",
+// plan; "Module numerics", Structs Unreadable and Functions reads).
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <mutex>
+
+#include "qg_internal.hpp"
+
+namespace qg {
+
+namespace {
+thread_local char g_reason[512] = "";
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+Tuning g_tuning = {0, 0, 1};
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];
+std::once_flag g_cu_once[kMaxDevices];
+}  // namespace
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_reason, sizeof g_reason, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+const Tuning &tuning() { return g_tuning; }
+
+void take_timing_events(hipEvent_t *start, hipEvent_t *stop)
+{
+    *start = g_ev_start;
+    *stop = g_ev_stop;
+    g_ev_start = g_ev_stop = nullptr;
+}
+
+int device_cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    std::call_once(g_cu_once[dev], [dev] {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        g_cu_count[dev] = n;
+    });
+    return g_cu_count[dev];
+}
+
+}  // namespace qg
+
+using namespace qg;
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_fmt_mode(const char *who, int fmt, int mode)
+{
+    if (fmt != QG_Q4K && fmt != QG_Q6K) return fail(QG_E_INVALID, "%s: unknown format %d", who, fmt);
+    if (mode != QG_PERBLOCK && mode != QG_SUB32) return fail(QG_E_INVALID, "%s: unknown scaling %d", who, mode);
+    if (!qg_reads(fmt, mode)) return fail(QG_E_UNSUPPORTED, "%s: format %d is not read under scaling %d", who, fmt, mode);
+    return QG_OK;
+}
+
+int check_cols(const char *who, int64_t cols)
+{
+    if (cols <= 0 || cols % QG_BLOCK)
+        return fail(QG_E_SHAPE, "%s: cols %lld is not a positive multiple of %d", who, (long long)cols, QG_BLOCK);
+    if (cols > QG_MAX_COLS) return fail(QG_E_SHAPE, "%s: cols %lld exceeds %d", who, (long long)cols, QG_MAX_COLS);
+    return QG_OK;
+}
+
+int check_ptr(const char *who, const char *name, const void *p, uintptr_t align)
+{
+    if (!p) return fail(QG_E_INVALID, "%s: %s is NULL", who, name);
+    if (!aligned(p, align)) return fail(QG_E_INVALID, "%s: %s is not %u-byte aligned", who, name, (unsigned)align);
+    return QG_OK;
+}
+
+int check_act(const char *who, const int8_t *codes, const qg_act_scale *scales, const int32_t *csums)
+{
+    int st;
+    if ((st = check_ptr(who, "codes", codes, 16))) return st;
+    if ((st = check_ptr(who, "scales", scales, 4))) return st;
+    if ((st = check_ptr(who, "csums", csums, 4))) return st;
+    return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qg_version(void) { return 100; }
+
+const char *qg_last_error(void) { return g_reason; }
+
+int qg_reads(int fmt, int mode)
+{
+    const bool f = fmt == QG_Q4K || fmt == QG_Q6K;
+    const bool m = mode == QG_PERBLOCK || mode == QG_SUB32;
+    return f && m ? 1 : 0;
+}
+
+int qg_set_tuning(int key, int64_t value)
+{
+    if (value < 0) return fail(QG_E_INVALID, "qg_set_tuning: negative value");
+    switch (key) {
+    case QG_TUNE_WAVES_PER_CU:
+        if (value > 64) return fail(QG_E_INVALID, "qg_set_tuning: waves per CU above 64");
+        g_tuning.waves_per_cu = (int)value;
+        return QG_OK;
+    case QG_TUNE_PIPELINE:
+        g_tuning.pipeline = value ? 1 : 0;
+        return QG_OK;
+    case QG_TUNE_GRID_WGS:
+        if (value > 0x7fffffff) return fail(QG_E_INVALID, "qg_set_tuning: grid too large");
+        g_tuning.grid_wgs = value;
+        return QG_OK;
+    default:
+        return fail(QG_E_INVALID, "qg_set_tuning: unknown key %d", key);
+    }
+}
+
+int qg_time_next_launch(void *start_event, void *stop_event)
+{
+    if ((start_event == nullptr) != (stop_event == nullptr))
+        return fail(QG_E_INVALID, "qg_time_next_launch: give both events or neither");
+    g_ev_start = static_cast<hipEvent_t>(start_event);
+    g_ev_stop = static_cast<hipEvent_t>(stop_event);
+    return QG_OK;
+}
+
+int qg_quantize_act(int fmt, int mode, int64_t n, int64_t cols, const float *x, int8_t *codes,
+                    qg_act_scale *scales, int32_t *csums, int32_t *err_flag, void *stream)
+{
+    const char *who = "qg_quantize_act";
+    int st;
+    if ((st = check_fmt_mode(who, fmt, mode))) return st;
+    if ((st = check_cols(who, cols))) return st;
+    if (n < 0 || n > (int64_t)1 << 24) return fail(QG_E_SHAPE, "%s: n %lld out of range", who, (long long)n);
+    if (n == 0) return QG_OK;
+    if ((st = check_ptr(who, "x", x, 16))) return st;
+    if ((st = check_act(who, codes, scales, csums))) return st;
+    if (err_flag && !aligned(err_flag, 4)) return fail(QG_E_INVALID, "%s: err_flag is not 4-byte aligned", who);
+    return launch_quantize(mode, QG_BLOCK, n, cols, x, codes, scales, csums, err_flag,
+                           static_cast<hipStream_t>(stream));
+}
+
+static int gemm_common(const char *who, int fmt, int mode, int64_t rows, int64_t cols, int64_t n,
+                       const void *image, const int8_t *codes, const qg_act_scale *scales,
+                       const int32_t *csums, float *out, void *stream)
+{
+    int st;
+    if ((st = check_fmt_mode(who, fmt, mode))) return st;
+    if ((st = check_cols(who, cols))) return st;
+    if (rows < 0 || rows > 0x7fffffff) return fail(QG_E_SHAPE, "%s: rows %lld out of range", who, (long long)rows);
+    if (n < 0 || n > 65535) return fail(QG_E_SHAPE, "%s: n %lld out of range", who, (long long)n);
+    if (rows == 0 || n == 0) return QG_OK;
+    if ((st = check_ptr(who, "image", image, 16))) return st;
+    if ((st = check_act(who, codes, scales, csums))) return st;
+    if ((st = check_ptr(who, "out", out, 4))) return st;
+    return launch_gemv(fmt, mode, rows, cols, n, image, codes, scales, csums, out, static_cast<hipStream_t>(stream));
+}
+
+int qg_gemv_q(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
+              const qg_act_scale *scales, const int32_t *csums, float *out, void *stream)
+{
+    return gemm_common("qg_gemv_q", fmt, mode, rows, cols, 1, image, codes, scales, csums, out, stream);
+}
+
+int qg_gemm_q(int fmt, int mode, int64_t rows, int64_t cols, int64_t n, const void *image, const int8_t *codes,
+              const qg_act_scale *scales, const int32_t *csums, float *out, void *stream)
+{
+    return gemm_common("qg_gemm_q", fmt, mode, rows, cols, n, image, codes, scales, csums, out, stream);
+}
+
+int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
+                  int32_t *csum_out, int32_t *osum_out, void *stream)
+{
+    const char *who = "qg_block_sums";
+    int st;
+    if (fmt != QG_Q4K && fmt != QG_Q6K) return fail(QG_E_INVALID, "%s: unknown format %d", who, fmt);
+    if ((st = check_cols(who, cols))) return st;
+    if (rows < 0 || rows > 0x7fffffff) return fail(QG_E_SHAPE, "%s: rows %lld out of range", who, (long long)rows);
+    if (rows == 0) return QG_OK;
+    if ((st = check_ptr(who, "image", image, 16))) return st;
+    if ((st = check_ptr(who, "codes", codes, 16))) return st;
+    if ((st = check_ptr(who, "csum_out", csum_out, 4))) return st;
+    if (fmt == QG_Q4K && (st = check_ptr(who, "osum_out", osum_out, 4))) return st;
+    return launch_block_sums(fmt, rows, cols, image, codes, csum_out, osum_out, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

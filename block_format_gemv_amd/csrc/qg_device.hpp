@@ -1,0 +1,204 @@
+// qg_device.hpp -- device-side exact arithmetic of the block combine and the row sum.
+//
+// Everything here is exact integer or exact f64 work followed by one binary32 rounding,
+// as the method prescribes (rustdoc "Module numerics" of
+// logicaffeine_compile::spatial::decode_engine: module description, the two ActScaling
+// modes and the f32 model; Functions exact_sum, scaled_to_f32, ftz, fadd; "Module lane":
+// module description and Functions lane, group).
+//
+// The code is compiled with -ffp-contract=off and IEEE f32/f64 denormal handling (the
+// kernel descriptor's default), so every f64 operation below rounds exactly once, to
+// nearest even, and binary32 conversions round on the gradual-underflow grid before the
+// explicit flush.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+constexpr int kSumWindow = 64;   // places an exact sum keeps below its largest term's exponent
+
+// ---------------------------------------------------------------------------------------
+// binary16 block scale -> signed integer significand and exponent (value sig * 2^ex).
+// The packer refuses inf/NaN scales, so the exponent field is 0..30 here.
+struct F16Scale {
+    int sig;
+    int ex;
+};
+
+__device__ __forceinline__ F16Scale f16_scale(uint32_t h)
+{
+    const int E = (h >> 10) & 31;
+    const int M = h & 1023;
+    F16Scale s;
+    s.sig = E ? (M | 1024) : M;
+    s.ex = E ? E - 25 : -24;
+    if (h & 0x8000u) s.sig = -s.sig;
+    return s;
+}
+
+// ---------------------------------------------------------------------------------------
+// binary32 helpers
+
+__device__ __forceinline__ float ftz(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    return (u & 0x7F800000u) ? x : __uint_as_float(u & 0x80000000u);
+}
+
+// in-order row accumulation: binary32 add (nearest even), result flushed
+__device__ __forceinline__ float fadd_ftz(float acc, float piece) { return ftz(acc + piece); }
+
+__device__ __forceinline__ float canon_nan(float y)
+{
+    return (y != y) ? __uint_as_float(0x7FC00000u) : y;
+}
+
+// ---------------------------------------------------------------------------------------
+// One binary32 rounding of a value held exactly in one double (|significand| <= 53 bits).
+// An exact zero is +0 whatever the signs of the factors that made it.
+__device__ __forceinline__ float r32_exact_double(double x) { return x == 0.0 ? 0.0f : ftz((float)x); }
+
+// One binary32 rounding of a + b for doubles a, b (each exact).  TwoSum gives the rounded
+// sum s and its exact error t; nudging s to the odd neighbour when t != 0 (round to odd at
+// 53 bits) makes the later rounding to <= 24 bits equal the rounding of a + b itself.
+__device__ __forceinline__ float r32_sum2(double a, double b)
+{
+    double s = a + b;
+    double bv = s - a;
+    double av = s - bv;
+    double t = (a - av) + (b - bv);
+    if (s == 0.0) return 0.0f;              // exact cancellation (or two zeros): +0
+    if (t != 0.0) {
+        unsigned long long u = (unsigned long long)__double_as_longlong(s);
+        if ((u & 1ull) == 0ull) {
+            const bool away = (t > 0.0) == (s > 0.0);
+            u = away ? u + 1ull : u - 1ull;
+            s = __longlong_as_double((long long)u);
+        }
+    }
+    return ftz((float)s);
+}
+
+// ---------------------------------------------------------------------------------------
+// 128-bit exact sums (Sub32 groups)
+
+typedef __int128 i128;
+typedef unsigned __int128 u128;
+
+__device__ __forceinline__ int bitlen64(uint64_t v) { return v ? 64 - __clzll((long long)v) : 0; }
+
+// v * 2^exp rounded once to binary32: nearest even on the gradual-underflow grid, past the
+// top infinite, then a subnormal result flushed to a zero of its sign; 0 -> +0.
+__device__ inline float r32_i128(i128 v, int exp)
+{
+    if (v == 0) return 0.0f;
+    const uint32_t sign = v < 0 ? 0x80000000u : 0u;
+    const u128 M = v < 0 ? (u128)0 - (u128)v : (u128)v;
+    const uint64_t hi = (uint64_t)(M >> 64), lo = (uint64_t)M;
+    const int n = hi ? 64 + bitlen64(hi) : bitlen64(lo);
+    int q = exp + n - 24;                   // exponent of the last kept place
+    if (q < -149) q = -149;
+    const int shift = q - exp;
+    uint64_t R;
+    if (shift <= 0) {
+        R = (uint64_t)(M << (-shift));      // fewer than 24 significant bits: exact
+    } else if (shift >= 127) {
+        R = 0;
+    } else {
+        R = (uint64_t)(M >> shift);
+        const u128 rem = M & (((u128)1 << shift) - 1);
+        const u128 half = (u128)1 << (shift - 1);
+        if (rem > half || (rem == half && (R & 1ull))) R += 1;
+    }
+    if (R == (1ull << 24)) { R >>= 1; q += 1; }
+    if (R < (1ull << 23)) return __uint_as_float(sign);          // subnormal or zero: flushed
+    const int biased = q + 150;
+    if (biased > 254) return __uint_as_float(sign | 0x7F800000u);
+    return __uint_as_float(sign | ((uint32_t)biased << 23) | (uint32_t)(R & 0x7FFFFFull));
+}
+
+// |a| * 2^ea > |b| * 2^eb ?
+__device__ inline bool mag_greater(long long a, int ea, long long b, int eb)
+{
+    uint64_t A = a < 0 ? 0ull - (uint64_t)a : (uint64_t)a;
+    uint64_t B = b < 0 ? 0ull - (uint64_t)b : (uint64_t)b;
+    if (A == 0) return false;
+    if (B == 0) return true;
+    const int ta = ea + bitlen64(A), tb = eb + bitlen64(B);
+    if (ta != tb) return ta > tb;
+    if (ea > eb) A <<= (ea - eb); else B <<= (eb - ea);   // same leading place: no overflow
+    return A > B;
+}
+
+// The windowed exact sum when some exponent lies more than kSumWindow below another: the
+// largest-magnitude term (first of equals) fixes L; a term whose exponent is below
+// L - kSumWindow is floored to a multiple of 2^(L - kSumWindow).  Rare: kept out of line.
+__device__ __noinline__ float exact_sum_windowed(const long long *v, const int *e, int n)
+{
+    int L = 0;
+    for (int i = 1; i < n; i++)
+        if (mag_greater(v[i], e[i], v[L], e[L])) L = i;
+    const int fe = e[L] - kSumWindow;
+    int emin = 0x7fffffff;
+    for (int i = 0; i < n; i++) {
+        const int ei = e[i] < fe ? fe : e[i];
+        emin = ei < emin ? ei : emin;
+    }
+    u128 s = 0;
+    for (int i = 0; i < n; i++) {
+        long long vi = v[i];
+        int ei = e[i];
+        if (ei < fe) {
+            const int sh = fe - ei;
+            vi = sh >= 63 ? (vi < 0 ? -1 : 0) : (vi >> sh);   // arithmetic shift = floor
+            ei = fe;
+        }
+        if (vi == 0) continue;
+        s += (u128)(i128)vi << (ei - emin);
+    }
+    return r32_i128((i128)s, emin);
+}
+
+// Sum of v[i] * 2^e[i] rounded once ("Module numerics", Functions exact_sum).  Terms are
+// below 2^45 in magnitude here.  When every exponent is within kSumWindow of every other
+// no term can lie past the window, and the aligned sum fits 128 bits.
+template <int N>
+__device__ __forceinline__ float exact_sum(const long long (&v)[N], const int (&e)[N])
+{
+    int emin = e[0], emax = e[0];
+#pragma unroll
+    for (int i = 1; i < N; i++) {
+        emin = e[i] < emin ? e[i] : emin;
+        emax = e[i] > emax ? e[i] : emax;
+    }
+    if (emax - emin > kSumWindow) return exact_sum_windowed(v, e, N);
+    u128 s = 0;
+#pragma unroll
+    for (int i = 0; i < N; i++) s += (u128)(i128)v[i] << (e[i] - emin);
+    return r32_i128((i128)s, emin);
+}
+
+// ---------------------------------------------------------------------------------------
+// Block pieces
+
+// PerBlock, Q4_K-style: R32(m*2^e * (d*C - dmin*O)).  With sig_d*m < 2^19 and |C| < 2^25 each
+// product is below 2^44 and exact in f64; ldexp by the combined exponent is exact too.
+__device__ __forceinline__ float piece_q4k_perblock(int C, int O, uint32_t d_dmin, int m, int e)
+{
+    const F16Scale d = f16_scale(d_dmin & 0xFFFFu);
+    const F16Scale dm = f16_scale(d_dmin >> 16);
+    const double a = __builtin_ldexp((double)C * (double)(d.sig * m), d.ex + e);
+    const double b = __builtin_ldexp(-(double)O * (double)(dm.sig * m), dm.ex + e);
+    return r32_sum2(a, b);
+}
+
+// PerBlock, Q6_K-style: one term R32(m*2^e * d*C); |C| < 2^27 so the product is < 2^46.
+__device__ __forceinline__ float piece_q6k_perblock(int C, uint32_t dbits, int m, int e)
+{
+    const F16Scale d = f16_scale(dbits);
+    return r32_exact_double(__builtin_ldexp((double)C * (double)(d.sig * m), d.ex + e));
+}
+
+}  // namespace qg

@@ -1,0 +1,45 @@
+// qg_internal.hpp -- host-side internals shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qgemv.h"
+
+namespace qg {
+
+// image tile geometry (see the layout in qgemv.h)
+constexpr int kTilePairs = 64;
+constexpr int kTileBytesQ4K = 64 * 144;   // 9216
+constexpr int kTileBytesQ6K = 64 * 210;   // 13440
+
+// per-thread failure reason
+int fail(int status, const char *fmt, ...);
+
+struct Tuning {
+    int waves_per_cu;   // 0 = default
+    int64_t grid_wgs;   // 0 = derived
+    int pipeline;       // 1: load each tile's successor during its compute (single column)
+};
+const Tuning &tuning();
+
+int device_cu_count();   // compute units of the current device
+
+// events the next GEMV launch on this thread records around its kernel (both null: none);
+// taking them clears them
+void take_timing_events(hipEvent_t *start, hipEvent_t *stop);
+
+// kernel launchers (return QG_OK or a failure already reported through fail())
+int launch_quantize(int mode, int block, int64_t n, int64_t cols, const float *x, int8_t *codes,
+                    qg_act_scale *scales, int32_t *csums, int32_t *err_flag, hipStream_t s);
+
+int launch_gemv(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, const void *image,
+                const int8_t *codes, const qg_act_scale *scales, const int32_t *csums, float *out,
+                hipStream_t s);
+
+int launch_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
+                      int32_t *csum_out, int32_t *osum_out, hipStream_t s);
+
+}  // namespace qg
+
+static_assert(sizeof(qg_act_scale) == 4, "qg_act_scale must be 4 bytes");

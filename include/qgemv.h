@@ -1,0 +1,202 @@
+/*
+ * qgemv.h -- C ABI of libqgemv.so: the exact block-quantized matrix-row x activation-row
+ * dot product (decode GEMV) and its batched-column form (GEMM) on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method (rustdoc "Module numerics" of logicaffeine_compile::spatial::decode_engine,
+ * module description, and "Module lane", module description):
+ *   - a weight is exactly a block scale times an integer: Q4_K-style w = d*sc*q - dmin*mn,
+ *     Q6_K-style w = d*sc*(q - 32);
+ *   - activations are quantized under scales m*2^e to the exact nearest integer codes,
+ *     either per weight block with an 8-bit significand (PerBlock) or per 32 elements with a
+ *     4-bit significand (Sub32);
+ *   - per 256-element block the terms (block scale x integer sum, second scale x offset sum,
+ *     times the activation scale) are summed exactly and rounded to binary32 once, a
+ *     subnormal result flushed to a zero of its sign;
+ *   - a row's rounded pieces are added in ascending block order with binary32 adds (each
+ *     result flushed), from +0.  A NaN output is 0x7FC00000.
+ * Output bits depend only on the inputs: not on the stream, the launch configuration, the
+ * tuning knobs or, for qg_gemm_q, on the number of columns.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_host are host memory; every other data pointer is device memory
+ *     (hipMalloc / torch on the ROCm device).  All memory is owned by the caller; the
+ *     library allocates no device memory and keeps no state except a per-thread reason
+ *     string and the tuning knobs.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Launches are asynchronous on it;
+ *     the returned status covers only argument validation and launch errors.
+ *   - Device pointers must be 16-byte aligned (4-byte for scales, csums, out, err_flag).
+ *   - Errors return a nonzero qg_status and set a reason readable with qg_last_error().
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight block formats.  Both use 256-element blocks. */
+typedef enum {
+    QG_Q4K = 1,   /* 4-bit codes, 8 sub-blocks of 32 with 6-bit scale and offset, f16 d, dmin */
+    QG_Q6K = 2    /* 6-bit codes offset by -32, 16 sub-blocks of 16 with int8 scales, f16 d */
+} qg_format;
+
+/* How an activation row is scaled ("Module numerics", Enums ActScaling). */
+typedef enum {
+    QG_PERBLOCK = 0,  /* one scale per 256-element weight block, m in 128..255 */
+    QG_SUB32 = 1      /* one scale per 32 elements, m in 8..15; a 256-group rounds once */
+} qg_act_scaling;
+
+/* An activation block's scale m * 2^e ("Module numerics", Structs ActScale).  For PerBlock
+ * 128 <= m <= 255; for Sub32 8 <= m <= 15.  An all-zero block gets m = 128 (or 8), e = 0.
+ * A block holding +-inf gets m = 0, e = 0 and raises the error flag. */
+typedef struct {
+    int16_t e;
+    uint8_t m;
+    uint8_t pad;
+} qg_act_scale;
+
+typedef enum {
+    QG_OK = 0,
+    QG_E_INVALID = 1,      /* null or misaligned pointer, bad enum, field out of range */
+    QG_E_SHAPE = 2,        /* cols not a positive multiple of 256, cols > QG_MAX_COLS, n < 1 */
+    QG_E_UNSUPPORTED = 3,  /* a (format, scaling) pair qg_reads() rejects */
+    QG_E_UNREADABLE = 4,   /* a block scale is inf or NaN ("Module numerics", Structs Unreadable) */
+    QG_E_NONFINITE = 5,    /* an activation is +-inf (reported through err_flag) */
+    QG_E_RUNTIME = 6       /* a HIP call failed */
+} qg_status;
+
+#define QG_BLOCK 256
+#define QG_MAX_COLS 32768
+
+/* Whether the kernels read matrices of `fmt` under `mode` ("Module numerics", Functions
+ * reads).  1 for (Q4K, PerBlock), (Q4K, Sub32), (Q6K, PerBlock), (Q6K, Sub32); else 0. */
+int qg_reads(int fmt, int mode);
+
+/*
+ * Weight image ------------------------------------------------------------------------
+ *
+ * A matrix of R rows and C columns (C = 256*G) is G blocks per row.  Its (row, block) pairs
+ * are numbered p = r*G + b and cut into tiles of 64 consecutive pairs; tile t holds pairs
+ * 64t .. 64t+63 (pairs past R*G are zero padding).  Lane l of a tile is pair 64t + l.  The
+ * image is the tiles one after another.
+ *
+ * Q4_K-style tile, 9216 bytes (= 64 x 144):
+ *   chunk i (i = 0..7) at byte 1024*i: 16 bytes per lane at 1024*i + 16*l.  Byte k (0..15)
+ *       holds the code of element 32i+k in its low nibble and of element 32i+16+k in its
+ *       high nibble.
+ *   meta at byte 8192: 16 bytes per lane at 8192 + 16*l:
+ *       bytes 0..1  d    (binary16 bits, little endian)
+ *       bytes 2..3  dmin (binary16 bits)
+ *       bytes 4..15 a 96-bit little-endian field string; sub-block j's scale sc_j is bits
+ *                   12j .. 12j+5 and its offset mn_j bits 12j+6 .. 12j+11.
+ *
+ * Q6_K-style tile, 13440 bytes (= 64 x 210):
+ *   ql chunk i (i = 0..7) at byte 1024*i, 16 bytes per lane: byte k holds the low 4 bits of
+ *       the code of element 32i+k (low nibble) and of element 32i+16+k (high nibble).
+ *   qh chunk h (h = 0..3) at byte 8192 + 1024*h, 16 bytes per lane: byte k holds the high 2
+ *       bits of the codes of elements 64h+k, 64h+16+k, 64h+32+k, 64h+48+k at bit pairs
+ *       0-1, 2-3, 4-5, 6-7.
+ *   scales at byte 12288, 16 bytes per lane: sub-block k's int8 scale in byte k.
+ *   d at byte 13312, 2 bytes per lane: binary16 bits.
+ */
+
+/* Bytes of the image of an R x C matrix: ceil(R*C/256 / 64) * 64 * (144 or 210).
+ * 0 for a bad format or shape. */
+size_t qg_image_bytes(int fmt, int64_t rows, int64_t cols);
+
+/* Pack Q4_K-style logical fields (host memory, row-major) into an image (host memory,
+ * qg_image_bytes(QG_Q4K, rows, cols) bytes, no alignment needed):
+ *   q    uint8  [rows][cols]      codes 0..15
+ *   sc   uint8  [rows][cols/32]   sub-block scales 0..63
+ *   mn   uint8  [rows][cols/32]   sub-block offsets 0..63
+ *   d    uint16 [rows][cols/256]  binary16 bits of the block scale
+ *   dmin uint16 [rows][cols/256]  binary16 bits of the second block scale
+ * The weight of element i of block b is d*sc_j*q_i - dmin*mn_j with j the sub-block
+ * ("Module numerics", Structs CodedRow, Segment, Scale).  Errors: QG_E_INVALID for a field
+ * out of range, QG_E_UNREADABLE for an inf/NaN scale (the reason names row and block),
+ * QG_E_SHAPE for a bad shape.  Nothing is written to the image on error. */
+int qg_pack_q4k(int64_t rows, int64_t cols, const uint8_t *q_host, const uint8_t *sc_host,
+                const uint8_t *mn_host, const uint16_t *d_host, const uint16_t *dmin_host,
+                void *image_host);
+
+/* Pack Q6_K-style logical fields into an image (host memory):
+ *   q   uint8  [rows][cols]      codes 0..63 (the weight uses q - 32)
+ *   sc  int8   [rows][cols/16]   sub-block scales -128..127
+ *   d   uint16 [rows][cols/256]  binary16 bits of the block scale
+ * Weight w = d*sc_k*(q_i - 32), k = i/16; |sc*(q-32)| <= 4096 ("Module numerics",
+ * Constants COEF_BOUND).  Errors as qg_pack_q4k. */
+int qg_pack_q6k(int64_t rows, int64_t cols, const uint8_t *q_host, const int8_t *sc_host,
+                const uint16_t *d_host, void *image_host);
+
+/* Quantize n activation rows ("Module numerics", Functions quantize_blocks (PerBlock) and
+ * quantize (Sub32), absmax, wide_scale, block_scale, rne_div):
+ *   x       f32 [n][cols]                       device
+ *   codes   int8 [n][cols]                      device, out: rne(x / s), |code| <= 127
+ *   scales  qg_act_scale [n][cols/B]            device, out; B = 256 (PerBlock) or 32 (Sub32)
+ *   csums   int32 [n][cols/16]                  device, out: sum of the codes of each run of
+ *                                                16 elements (the activation-side unit sums
+ *                                                of "Module lane")
+ *   err_flag int32 [1]                          device; set to 1 when a block holds +-inf.
+ *                                                Never cleared by the library (clear it
+ *                                                before the call).  May be NULL.
+ * Each element is read with denormals as zero; the scale is the least m*2^e with
+ * 127*m*2^e >= the block's largest magnitude (NaN passed over); a NaN element gets code 0.
+ * fmt selects the PerBlock block (256 for both formats). */
+int qg_quantize_act(int fmt, int mode, int64_t n, int64_t cols, const float *x, int8_t *codes,
+                    qg_act_scale *scales, int32_t *csums, int32_t *err_flag, void *stream);
+
+/* Decode GEMV ("Module numerics", Functions dot; "Module lane", Functions lane and group):
+ *   image   the packed matrix (device), qg_image_bytes(fmt, rows, cols) bytes
+ *   codes, scales, csums   one quantized activation row as written by qg_quantize_act
+ *   out     f32 [rows] (device)
+ * out[r] = the engine's f32 for row r . activation. */
+int qg_gemv_q(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
+              const qg_act_scale *scales, const int32_t *csums, float *out, void *stream);
+
+/* Batched columns: n activation rows (codes [n][cols], scales [n][cols/B], csums
+ * [n][cols/16]) against the same matrix; out f32 [n*rows] with out[c*rows + r] equal, bit
+ * for bit, to qg_gemv_q of row r with activation c. */
+int qg_gemm_q(int fmt, int mode, int64_t rows, int64_t cols, int64_t n, const void *image,
+              const int8_t *codes, const qg_act_scale *scales, const int32_t *csums, float *out,
+              void *stream);
+
+/* Integer sums per (row, sub-block), before any scale ("Module lane", Functions
+ * block_sums), for one activation row:
+ *   Q4K: csum_out int32 [rows][cols/32] = sum sc_j*q*c over sub-block j,
+ *        osum_out int32 [rows][cols/32] = sum mn_j*c.
+ *   Q6K: csum_out int32 [rows][cols/16] = sum sc_k*(q-32)*c over sub-block k; osum_out is
+ *        not written (may be NULL).
+ * A debugging view of the kernels' integer stage. */
+int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
+                  int32_t *csum_out, int32_t *osum_out, void *stream);
+
+/* Speed-only tuning knobs; they never change output bits.
+ *   QG_TUNE_WAVES_PER_CU  resident waves per compute unit the GEMV grid is sized for
+ *                         (0 = default)
+ *   QG_TUNE_GRID_WGS      exact number of workgroups for the GEMV grid (0 = derived)
+ *   QG_TUNE_PIPELINE      1 (default): a single-column GEMV loads each tile's successor while
+ *                         the tile is computed; 0: one tile in flight per wave */
+enum { QG_TUNE_WAVES_PER_CU = 1, QG_TUNE_GRID_WGS = 2, QG_TUNE_PIPELINE = 3 };
+int qg_set_tuning(int key, int64_t value);
+
+/* Measurement hook: the next qg_gemv_q / qg_gemm_q call made on this thread launches its
+ * kernel with hipExtLaunchKernelGGL, which records start_event as the kernel begins and
+ * stop_event as it ends (hipEvent_t handles owned by the caller; both NULL cancels).
+ * Later launches are not timed.  Changes no output bits. */
+int qg_time_next_launch(void *start_event, void *stop_event);
+
+/* The reason for the last nonzero status returned on this thread ("" if none). */
+const char *qg_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int qg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

@@ -1,0 +1,354 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, bit for bit.
+
+Activation codes, scales and code sums are compared byte for byte; integer block sums
+exactly; every f32 output by its bits (compared as uint32, NaN canonical), never within a
+tolerance.  Shapes span several tiles with ragged tails; the named workloads run at full
+size in the launch configuration the benchmark times, with the oracle computing either
+every output or a seeded sample of rows.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def qg():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import block_format_gemv_amd as q
+    q.qg_set_tuning(q.TUNE_WAVES_PER_CU, 0)
+    q.qg_set_tuning(q.TUNE_GRID_WGS, 0)
+    oracle.set_threads(8)
+    return q
+
+
+DEV = "cuda:0"
+
+
+def dev(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bits(a) -> np.ndarray:
+    a = a.detach().cpu().numpy() if hasattr(a, "detach") else np.asarray(a)
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def first_mismatch(got, want):
+    g, w = bits(got).reshape(-1), bits(want).reshape(-1)
+    bad = np.nonzero(g != w)[0]
+    if len(bad) == 0:
+        return None
+    i = bad[0]
+    return f"{len(bad)} mismatches; first at {i}: got {g[i]:08x} want {w[i]:08x}"
+
+
+def gpu_quant(q, x: np.ndarray, mode: int, fmt=None):
+    xd = dev(x.astype(np.float32))
+    a = q.quantize_act(xd, mode, fmt or q.Q4K)
+    m, e = a.scale_fields()
+    return a, a.codes.cpu().numpy(), m, e, a.csums.cpu().numpy()
+
+
+class Mat:
+    """A matrix's logical fields, its image on the GPU, and its format code."""
+
+    def __init__(self, q, fields):
+        self.f = fields
+        self.fmt = q.FMT_CODES[fields["fmt"]]
+        self.rows, self.cols = fields["rows"], fields["cols"]
+        self.img = dev(q.pack(fields))
+
+
+def run_gemv(q, M: Mat, act, out=None):
+    return q.gemv(M.fmt, M.rows, M.cols, M.img, act, out=out)
+
+
+# --- the quantizer -------------------------------------------------------------------------
+
+def _quant_inputs():
+    g = np.random.Generator(np.random.PCG64(5))
+    x = gen.act_outliers(4, 4096, 9)
+    adv = g.standard_normal((6, 1024)).astype(np.float32)
+    adv[0, :256] = 0                                         # all-zero block
+    adv[1, 3] = np.nan                                       # NaN: code 0, passed over
+    adv[1, 700] = np.nan
+    adv[2] *= np.float32(2.0 ** -126)                        # many subnormals (read as 0)
+    adv[3] *= np.float32(2.0 ** 120)                         # huge
+    adv[4] = np.round(adv[4] * 8) / 8                        # many exact ties
+    adv[5, 256:512] = np.float32(1.0)                        # exact boundary 127*m*2^e cases
+    adv[5, 300] = np.float32(127.0 * 130 * 2.0 ** -14)
+    sub, _ = gen.sub32_act(3)
+    return [("outliers", x), ("adversarial", adv), ("sub32", sub), ("normal", gen.act_normal(64, 4096, 140 + 64))]
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_quantize_matches_oracle(qg, mode):
+    for name, x in _quant_inputs():
+        say("quantize", name, x.shape, "mode", mode)
+        _, c, m, e, s = gpu_quant(qg, x, mode)
+        oc, om, oe, os_ = oracle.quantize(x, mode)
+        assert np.array_equal(c, oc), name
+        assert np.array_equal(m, om) and np.array_equal(e, oe), name
+        assert np.array_equal(s, os_), name
+
+
+def test_quantize_infinity_raises_the_flag(qg):
+    x = gen.act_normal(2, 1024, 4)
+    x[1, 600] = np.inf
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for mode in (0, 1):
+        flag.zero_()
+        a = qg.quantize_act(dev(x), mode, err_flag=flag)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == 1
+        oc, om, oe, os_ = oracle.quantize(x, mode, check=False)
+        m, e = a.scale_fields()
+        assert np.array_equal(a.codes.cpu().numpy(), oc) and np.array_equal(m, om) and np.array_equal(e, oe)
+    flag.zero_()
+    qg.quantize_act(dev(gen.act_normal(1, 1024, 5)), 0, err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+
+
+# --- GEMV on assorted shapes ----------------------------------------------------------------
+
+def _adversarial_fields(fmt, rows, cols, seed):
+    if fmt == "q4k":
+        f = gen.q4k_fields(rows, cols, seed)
+        keys = ("d", "dmin")
+    else:
+        f = gen.q6k_fields(rows, cols, seed)
+        keys = ("d",)
+    g = np.random.Generator(np.random.PCG64(seed + 99))
+    choices = np.array([0x0000, 0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0x8001, 0xFBFF, 0x2E66], np.uint16)
+    for k in keys:
+        pick = g.random(f[k].shape) < 0.05
+        f[k][pick] = g.choice(choices, size=int(pick.sum()))
+    return f
+
+
+SHAPES = [(1, 256), (3, 768), (63, 1024), (65, 1280), (257, 4096), (9, 14336), (130, 3072), (2, 32768)]
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_gemv_shapes(qg, fmt, mode):
+    for rows, cols in SHAPES:
+        say("gemv", fmt, "mode", mode, "shape", rows, cols)
+        f = _adversarial_fields(fmt, rows, cols, rows * 131 + cols)
+        M = Mat(qg, f)
+        x = gen.act_outliers(1, cols, rows + cols)
+        if mode == 1:
+            x, _ = gen.act_sub32(1, cols, rows + cols)
+        act, c, m, e, _ = gpu_quant(qg, x, mode)
+        out = run_gemv(qg, M, act)
+        want = oracle.gemv(f, c, m, e, mode)
+        assert first_mismatch(out, want) is None, (rows, cols, first_mismatch(out, want))
+
+
+def test_gemv_tiny_workload(qg):
+    f, x = gen.tiny_q4k()
+    M = Mat(qg, f)
+    act, c, m, e, _ = gpu_quant(qg, x, 0)
+    out = run_gemv(qg, M, act)
+    want = oracle.gemv(f, c, m, e, 0)
+    assert first_mismatch(out, want) is None
+    assert np.isfinite(want).all() and np.abs(want).max() > 0
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_block_sums_exact(qg, fmt):
+    for rows, cols in [(5, 768), (64, 4096)]:
+        f = _adversarial_fields(fmt, rows, cols, 7 + rows)
+        M = Mat(qg, f)
+        x = gen.act_outliers(1, cols, 3 + rows)
+        act, c, _, _, _ = gpu_quant(qg, x, 0)
+        per = 32 if fmt == "q4k" else 16
+        cs = torch.empty((rows, cols // per), dtype=torch.int32, device=DEV)
+        os_ = torch.empty((rows, cols // 32), dtype=torch.int32, device=DEV) if fmt == "q4k" else None
+        qg.qg_block_sums(M.fmt, rows, cols, M.img, act.codes, cs, os_)
+        if fmt == "q4k":
+            oC, oO = oracle.sub_sums(f, c[0])
+            assert np.array_equal(cs.cpu().numpy(), oC) and np.array_equal(os_.cpu().numpy(), oO)
+        else:
+            assert np.array_equal(cs.cpu().numpy(), oracle.sub_sums(f, c[0]))
+
+
+def test_edge_pieces(qg):
+    """Pieces that flush at 2^-126, overflow to inf, and inf - inf rows (canonical NaN)."""
+    f = gen.q4k_fields(6, 512, 1)
+    f["d"][:] = 0x0001
+    f["dmin"][:] = 0
+    f["d"][2:4] = 0x7BFF
+    f["d"][3, 1] = 0xFBFF
+    M = Mat(qg, f)
+    for scale in (2.0 ** -100, 2.0 ** -60, 3.0e38):
+        x = np.full((1, 512), np.float32(scale), np.float32)
+        x[0, ::3] *= -1
+        act, c, m, e, _ = gpu_quant(qg, x, 0)
+        out = run_gemv(qg, M, act)
+        want = oracle.gemv(f, c, m, e, 0)
+        assert first_mismatch(out, want) is None, scale
+    assert (bits(out)[3] == 0x7FC00000) or np.isinf(want[3])
+
+
+def test_sub32_window_engaged(qg):
+    """Sub32 groups whose 32-blocks lie 2^+-120 apart engage the SUM_WINDOW floor (value not
+    printed by the pages; reading 64 places): GPU and oracle take the same reading."""
+    g = np.random.Generator(np.random.PCG64(17))
+    for fmt in ("q4k", "q6k"):
+        f = _adversarial_fields(fmt, 40, 1024, 23)
+        M = Mat(qg, f)
+        x = g.standard_normal((1, 1024)).astype(np.float32)
+        k = g.integers(-120, 101, 32)
+        x = (x.reshape(32, 32) * np.exp2(k)[:, None]).astype(np.float32).reshape(1, 1024)
+        act, c, m, e, _ = gpu_quant(qg, x, 1)
+        out = run_gemv(qg, M, act)
+        want = oracle.gemv(f, c, m, e, 1)
+        assert first_mismatch(out, want) is None, fmt
+
+
+def test_launch_configuration_does_not_change_bits(qg):
+    f = _adversarial_fields("q4k", 1000, 4096, 5)
+    M = Mat(qg, f)
+    act, c, m, e, _ = gpu_quant(qg, gen.act_outliers(1, 4096, 8), 0)
+    ref = bits(run_gemv(qg, M, act))
+    try:
+        for key, val in ((qg.TUNE_GRID_WGS, 1), (qg.TUNE_GRID_WGS, 7), (qg.TUNE_GRID_WGS, 5000),
+                         (qg.TUNE_WAVES_PER_CU, 1), (qg.TUNE_WAVES_PER_CU, 32)):
+            qg.qg_set_tuning(qg.TUNE_GRID_WGS, 0)
+            qg.qg_set_tuning(qg.TUNE_WAVES_PER_CU, 0)
+            qg.qg_set_tuning(key, val)
+            say("tuning", key, val)
+            assert np.array_equal(bits(run_gemv(qg, M, act)), ref), (key, val)
+    finally:
+        qg.qg_set_tuning(qg.TUNE_GRID_WGS, 0)
+        qg.qg_set_tuning(qg.TUNE_WAVES_PER_CU, 0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = torch.empty(1000, dtype=torch.float32, device=DEV)
+        qg.qg_gemv_q(M.fmt, 0, 1000, 4096, M.img, act.codes, act.scales, act.csums, out, stream=s)
+    s.synchronize()
+    assert np.array_equal(bits(out), ref)
+    assert np.array_equal(ref, bits(oracle.gemv(f, c, m, e, 0)))
+
+
+def test_binding_refuses_short_buffers(qg):
+    M = Mat(qg, gen.q4k_fields(8, 512, 1))
+    act, _, _, _, _ = gpu_quant(qg, gen.act_normal(1, 512, 2), 0)
+    # 8 rows x 2 blocks fill one 64-pair tile; 64 rows would need two
+    with pytest.raises(qg.QGError):
+        qg.qg_gemv_q(M.fmt, 0, 64, 512, M.img, act.codes, act.scales, act.csums,
+                     torch.empty(64, dtype=torch.float32, device=DEV))
+    with pytest.raises(qg.QGError):
+        qg.qg_gemv_q(M.fmt, 0, 8, 512, M.img, act.codes, act.scales, act.csums,
+                     torch.empty(4, dtype=torch.float32, device=DEV))
+
+
+# --- the named workloads at full size ------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def llama(qg):
+    say("packing the 4096x4096 and 14336x4096 Q4_K-style matrices")
+    return {k: Mat(qg, gen.llama_q4k(k)) for k in ("attn", "ffn")}
+
+
+def test_decode_workload_full_rows_and_1000_reps(qg, llama):
+    """Both Llama-8B-shaped matrices; repetition 0 compared on every row, all 1000
+    repetitions (fresh activations each) on a seeded sample of 48 rows."""
+    g = np.random.Generator(np.random.PCG64(2024))
+    for name, M in llama.items():
+        say("decode workload", name, M.rows, "x", M.cols)
+        out = torch.empty(M.rows, dtype=torch.float32, device=DEV)
+        xs = np.concatenate([gen.decode_act(k) for k in range(1000)])
+        oc, om, oe, _ = oracle.quantize(xs, 0)
+        xd = dev(xs)
+        sample = np.sort(g.choice(M.rows, 48, replace=False))
+        sub = gen.slice_rows(M.f, sample)
+        got = np.empty((1000, 48), np.float32)
+        act = qg.alloc_act(1, M.cols, 0)
+        for k in range(1000):
+            qg.quantize_act(xd[k:k + 1], 0, out=act)
+            run_gemv(qg, M, act, out=out)
+            if k == 0:
+                full = out.cpu().numpy()
+                assert np.array_equal(act.codes.cpu().numpy(), oc[:1])
+                want = oracle.gemv(M.f, oc[:1], om[:1], oe[:1], 0)
+                assert first_mismatch(full, want) is None, name
+            got[k] = out[torch.from_numpy(sample).to(DEV)].cpu().numpy()
+        want = oracle.gemm(sub, oc, om, oe, 0).reshape(1000, 48)
+        assert first_mismatch(got, want) is None, name
+
+
+def test_output_projection_q6k_logits(qg):
+    say("generating the 128256x4096 Q6_K-style matrix")
+    f, x = gen.output_q6k()
+    M = Mat(qg, f)
+    act, c, m, e, _ = gpu_quant(qg, x, 0)
+    out = run_gemv(qg, M, act)
+    say("oracle over 128256 rows")
+    want = oracle.gemv(f, c, m, e, 0)
+    assert first_mismatch(out, want) is None
+    del M
+    torch.cuda.empty_cache()
+
+
+def test_sub32_workload_reps(qg, llama):
+    """Sub32 on the 14336x4096 matrix: repetition 0 on every row, 100 repetitions on a
+    sample of 64 rows; exponents of each row span -12..4."""
+    M = llama["ffn"]
+    g = np.random.Generator(np.random.PCG64(77))
+    sample = np.sort(g.choice(M.rows, 64, replace=False))
+    sub = gen.slice_rows(M.f, sample)
+    out = torch.empty(M.rows, dtype=torch.float32, device=DEV)
+    got, wants = [], []
+    for k in range(100):
+        x, t = gen.sub32_act(k)
+        act, c, m, e, _ = gpu_quant(qg, x, 1)
+        assert np.array_equal(e.astype(np.int32), t)
+        run_gemv(qg, M, act, out=out)
+        if k == 0:
+            want = oracle.gemv(M.f, c, m, e, 1)
+            assert first_mismatch(out, want) is None
+        got.append(out.cpu().numpy()[sample])
+        wants.append(oracle.gemv(sub, c, m, e, 1))
+    assert first_mismatch(np.stack(got), np.stack(wants)) is None
+
+
+@pytest.mark.parametrize("n", [2, 8, 64])
+def test_batched_columns(qg, llama, n):
+    xs = gen.batch_act(n)
+    for name, M in llama.items():
+        say("gemm", name, "n", n)
+        act, c, m, e, _ = gpu_quant(qg, xs, 0)
+        out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+        if name == "ffn" and n == 64:
+            g = np.random.Generator(np.random.PCG64(n))
+            sample = np.sort(g.choice(M.rows, 1024, replace=False))
+            want = oracle.gemm(gen.slice_rows(M.f, sample), c, m, e, 0).reshape(n, -1)
+            assert first_mismatch(out[:, torch.from_numpy(sample).to(DEV)], want) is None
+        else:
+            want = oracle.gemm(M.f, c, m, e, 0).reshape(n, M.rows)
+            assert first_mismatch(out, want) is None, (name, n)
+        # each column carries the GEMV's bits
+        one = qg.alloc_act(1, M.cols, 0)
+        for k in (0, n - 1):
+            one.codes.copy_(act.codes[k:k + 1])
+            one.scales.copy_(act.scales[k:k + 1])
+            one.csums.copy_(act.csums[k:k + 1])
+            assert np.array_equal(bits(run_gemv(qg, M, one)), bits(out[k]))

@@ -1,0 +1,180 @@
+"""Host-side checks of libqgemv.so (no GPU): the library loads and exports every entry point
+include/qgemv.h declares; the packer writes exactly the documented tile layout (checked by
+an independent numpy unpacker written from the header's description); argument
+validation refuses bad calls before any GPU work, with a reason."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_format_gemv_amd as qg
+from workloads import gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "qgemv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 11
+    L = ctypes.CDLL(qg.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(qg.EXPORTS)
+
+
+# --- independent unpackers (from the layout described in qgemv.h) ---------------------------
+
+def unpack_q4k(img: np.ndarray, rows: int, cols: int) -> dict:
+    G = cols // 256
+    npairs = rows * G
+    ntiles = -(-npairs // 64)
+    t = img.reshape(ntiles, 9216)
+    chunks = t[:, :8192].reshape(ntiles, 8, 64, 16)              # [tile, chunk i, lane, byte k]
+    meta = t[:, 8192:].reshape(ntiles, 64, 16)                   # [tile, lane, 16]
+    lo = chunks & 15
+    hi = chunks >> 4
+    sub = np.concatenate([lo, hi], axis=3)                       # element 32i + (k | 16 + k)
+    q = sub.transpose(0, 2, 1, 3).reshape(ntiles * 64, 256)[:npairs]
+    m = meta.reshape(ntiles * 64, 16)[:npairs].astype(np.uint64)
+    d = (m[:, 0] | (m[:, 1] << 8)).astype(np.uint16)
+    dmin = (m[:, 2] | (m[:, 3] << 8)).astype(np.uint16)
+    bits = np.zeros(npairs, dtype=object)
+    for k in range(12):
+        bits = bits + (m[:, 4 + k].astype(object) << (8 * k))
+    sc = np.zeros((npairs, 8), np.uint8)
+    mn = np.zeros((npairs, 8), np.uint8)
+    for j in range(8):
+        field = np.array([(int(v) >> (12 * j)) & 0xFFF for v in bits], np.uint32)
+        sc[:, j] = field & 63
+        mn[:, j] = field >> 6
+    return {"q": q.reshape(rows, cols), "sc": sc.reshape(rows, G * 8), "mn": mn.reshape(rows, G * 8),
+            "d": d.reshape(rows, G), "dmin": dmin.reshape(rows, G)}
+
+
+def unpack_q6k(img: np.ndarray, rows: int, cols: int) -> dict:
+    G = cols // 256
+    npairs = rows * G
+    ntiles = -(-npairs // 64)
+    t = img.reshape(ntiles, 13440)
+    ql = t[:, :8192].reshape(ntiles, 8, 64, 16)
+    qh = t[:, 8192:12288].reshape(ntiles, 4, 64, 16)
+    sc = t[:, 12288:13312].reshape(ntiles, 64, 16).view(np.int8)
+    d = t[:, 13312:13440].reshape(ntiles, 64, 2).astype(np.uint16)
+    low = np.concatenate([ql & 15, ql >> 4], axis=3)               # [tile, i, lane, 32]
+    low = low.transpose(0, 2, 1, 3).reshape(ntiles, 64, 256)
+    high = np.zeros((ntiles, 64, 256), np.uint8)
+    for h in range(4):
+        for f in range(4):
+            high[:, :, 64 * h + 16 * f:64 * h + 16 * f + 16] = (qh[:, h] >> (2 * f)) & 3
+    q = (low | (high << 4)).reshape(ntiles * 64, 256)[:npairs]
+    dd = (d[..., 0] | (d[..., 1] << 8)).reshape(-1)[:npairs]
+    return {"q": q.reshape(rows, cols), "sc": sc.reshape(-1, 16)[:npairs].reshape(rows, G * 16),
+            "d": dd.reshape(rows, G)}
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 256), (5, 768), (64, 1024), (3, 14336 // 7), (37, 4096)])
+def test_q4k_pack_roundtrip(rows, cols):
+    f = gen.q4k_fields(rows, cols, rows * 7 + cols)
+    img = qg.pack(f)
+    assert img.nbytes == qg.qg_image_bytes(qg.Q4K, rows, cols) == -(-rows * cols // 256 // 64) * 9216
+    u = unpack_q4k(img, rows, cols)
+    for k in ("q", "sc", "mn", "d", "dmin"):
+        assert np.array_equal(u[k], f[k]), k
+    # zero padding past the last pair
+    npairs = rows * cols // 256
+    if npairs % 64:
+        last = img.reshape(-1, 9216)[-1]
+        lanes = np.arange(64) >= npairs % 64
+        assert not last[:8192].reshape(8, 64, 16)[:, lanes].any()
+        assert not last[8192:].reshape(64, 16)[lanes].any()
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 256), (5, 768), (64, 1024), (9, 4096)])
+def test_q6k_pack_roundtrip(rows, cols):
+    f = gen.q6k_fields(rows, cols, rows * 11 + cols)
+    img = qg.pack(f)
+    assert img.nbytes == qg.qg_image_bytes(qg.Q6K, rows, cols) == -(-rows * cols // 256 // 64) * 13440
+    u = unpack_q6k(img, rows, cols)
+    for k in ("q", "sc", "d"):
+        assert np.array_equal(u[k], f[k]), k
+
+
+def test_pack_refuses_unreadable_and_out_of_range_fields():
+    f = gen.q4k_fields(4, 512, 3)
+    f["dmin"][2, 1] = 0x7E00                                     # NaN
+    with pytest.raises(qg.QGError) as ei:
+        qg.pack(f)
+    assert ei.value.status == qg.E_UNREADABLE and "row 2 block 1" in ei.value.reason
+    f = gen.q4k_fields(4, 512, 3)
+    f["q"][1, 7] = 16
+    with pytest.raises(qg.QGError) as ei:
+        qg.pack(f)
+    assert ei.value.status == qg.E_INVALID
+    f = gen.q4k_fields(4, 512, 3)
+    f["mn"][0, 3] = 64
+    with pytest.raises(qg.QGError) as ei:
+        qg.pack(f)
+    assert ei.value.status == qg.E_INVALID
+    f6 = gen.q6k_fields(2, 256, 4)
+    f6["d"][1, 0] = 0xFC00                                       # -inf
+    with pytest.raises(qg.QGError) as ei:
+        qg.pack(f6)
+    assert ei.value.status == qg.E_UNREADABLE and "row 1 block 0" in ei.value.reason
+    f6 = gen.q6k_fields(2, 256, 4)
+    f6["q"][0, 0] = 64
+    with pytest.raises(qg.QGError) as ei:
+        qg.pack(f6)
+    assert ei.value.status == qg.E_INVALID
+
+
+def test_image_bytes_and_reads():
+    assert qg.qg_image_bytes(qg.Q4K, 14336, 4096) == 33_030_144
+    assert qg.qg_image_bytes(qg.Q4K, 4096, 4096) == 9_437_184
+    assert qg.qg_image_bytes(qg.Q6K, 128256, 4096) == 430_940_160
+    assert qg.qg_image_bytes(qg.Q4K, 256, 1024) == 147_456
+    assert qg.qg_image_bytes(qg.Q4K, 4, 100) == 0
+    assert qg.qg_image_bytes(3, 4, 256) == 0
+    for fmt in (qg.Q4K, qg.Q6K):
+        for mode in (qg.PERBLOCK, qg.SUB32):
+            assert qg.qg_reads(fmt, mode)
+    assert not qg.qg_reads(0, 0) and not qg.qg_reads(qg.Q4K, 7)
+
+
+def _raw(name):
+    return getattr(qg.lib(), name)
+
+
+def test_validation_refuses_before_any_gpu_work():
+    """Every refusal below returns before the library touches the GPU, so it runs here."""
+    L = qg.lib()
+    fake = ctypes.c_void_p(0x1000)           # never dereferenced: validation fails first
+    odd = ctypes.c_void_p(0x1001)
+    assert L.qg_gemv_q(qg.Q4K, qg.PERBLOCK, 8, 100, fake, fake, fake, fake, fake, None) == qg.E_SHAPE
+    assert "multiple of 256" in qg.qg_last_error()
+    assert L.qg_gemv_q(qg.Q4K, qg.PERBLOCK, 8, 65536, fake, fake, fake, fake, fake, None) == qg.E_SHAPE
+    assert L.qg_gemv_q(9, qg.PERBLOCK, 8, 256, fake, fake, fake, fake, fake, None) == qg.E_INVALID
+    assert L.qg_gemv_q(qg.Q4K, 5, 8, 256, fake, fake, fake, fake, fake, None) == qg.E_INVALID
+    assert L.qg_gemv_q(qg.Q4K, qg.PERBLOCK, 8, 256, None, fake, fake, fake, fake, None) == qg.E_INVALID
+    assert "image is NULL" in qg.qg_last_error()
+    assert L.qg_gemv_q(qg.Q4K, qg.PERBLOCK, 8, 256, odd, fake, fake, fake, fake, None) == qg.E_INVALID
+    assert "aligned" in qg.qg_last_error()
+    assert L.qg_gemv_q(qg.Q4K, qg.PERBLOCK, -1, 256, fake, fake, fake, fake, fake, None) == qg.E_SHAPE
+    assert L.qg_gemm_q(qg.Q4K, qg.PERBLOCK, 8, 256, -2, fake, fake, fake, fake, fake, None) == qg.E_SHAPE
+    assert L.qg_gemm_q(qg.Q4K, qg.PERBLOCK, 8, 256, 3, fake, fake, fake, fake, None, None) == qg.E_INVALID
+    assert L.qg_quantize_act(qg.Q4K, qg.SUB32, 1, 300, fake, fake, fake, fake, None, None) == qg.E_SHAPE
+    assert L.qg_quantize_act(qg.Q4K, qg.SUB32, 1, 256, odd, fake, fake, fake, None, None) == qg.E_INVALID
+    assert L.qg_block_sums(qg.Q6K, 4, 512, fake, fake, None, None, None) == qg.E_INVALID
+    assert L.qg_set_tuning(77, 1) == qg.E_INVALID
+    # empty work is not an error and launches nothing
+    assert L.qg_gemv_q(qg.Q4K, qg.PERBLOCK, 0, 256, None, None, None, None, None, None) == qg.OK
+    assert L.qg_quantize_act(qg.Q4K, qg.PERBLOCK, 0, 256, None, None, None, None, None, None) == qg.OK
