@@ -18,7 +18,7 @@ namespace qg {
 namespace {
 thread_local char g_reason[512] = "";
 thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
-Tuning g_tuning = {0, 0, 1};
+Tuning g_tuning = {0};
 
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices];
@@ -114,16 +114,10 @@ int qg_set_tuning(int key, int64_t value)
 {
     if (value < 0) return fail(QG_E_INVALID, "qg_set_tuning: negative value");
     switch (key) {
-    case QG_TUNE_WAVES_PER_CU:
-        if (value > 64) return fail(QG_E_INVALID, "qg_set_tuning: waves per CU above 64");
-        g_tuning.waves_per_cu = (int)value;
-        return QG_OK;
-    case QG_TUNE_PIPELINE:
-        g_tuning.pipeline = value ? 1 : 0;
-        return QG_OK;
-    case QG_TUNE_GRID_WGS:
-        if (value > 0x7fffffff) return fail(QG_E_INVALID, "qg_set_tuning: grid too large");
-        g_tuning.grid_wgs = value;
+    case QG_TUNE_WAVES_PER_WG:
+        if (value != 0 && value != 4 && value != 8 && value != 16)
+            return fail(QG_E_INVALID, "qg_set_tuning: waves per workgroup must be 0, 4, 8 or 16");
+        g_tuning.waves_per_wg = (int)value;
         return QG_OK;
     default:
         return fail(QG_E_INVALID, "qg_set_tuning: unknown key %d", key);

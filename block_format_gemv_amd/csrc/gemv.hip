@@ -1,15 +1,18 @@
 // gemv.hip -- decode GEMV and batched-column GEMM over packed Q4_K-/Q6_K-style images.
 //
-// One lane owns one (row, block) pair of a 64-pair image tile: its nine (Q4_K) or fourteen
-// (Q6_K) 16-byte loads per tile are each a contiguous 1 KiB per wave.  The lane forms the
-// pair's integer sub-block sums with v_dot4 on int8 activation codes staged in LDS
-// ("Module lane", Functions block_sums), turns them into the block's piece with one
-// binary32 rounding (Functions lane / group; "Module numerics", module description and
-// Functions exact_sum, scaled_to_f32), and the row's pieces are then added in block order
-// by the lane that owns the row (module description: pieces added in order).
+// A tile is 64 consecutive rows x one 256-element block; lane l of a wave owns row 64g + l
+// of its tile.  Its nine (Q4_K) or fourteen (Q6_K) 16-byte loads are each a contiguous
+// 1 KiB per wave.  Every lane of a wave works on the same block, so the block's activation
+// codes, code sums and scale are wave-uniform: a single column reads them with scalar loads
+// straight from global memory (SGPR operands of v_dot4), several columns read them from
+// LDS with broadcast reads.
 //
-// A wave walks "super-tiles": K consecutive tiles that hold RT whole rows (RT*G = 64*K), so
-// the in-order fold of every row stays inside one wave.  Bits do not depend on the grid.
+// Per pair the lane forms the integer sub-block sums ("Module lane", Functions block_sums),
+// turns them into the block's piece with one binary32 rounding (Functions lane / group;
+// "Module numerics", module description and Functions exact_sum, scaled_to_f32) and parks
+// the piece in LDS.  A workgroup owns one 64-row group; after a barrier its first wave adds
+// each row's pieces in ascending block order (module description: pieces added in order),
+// one row per lane.  Bits do not depend on the launch configuration.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -20,35 +23,59 @@
 namespace qg {
 namespace {
 
-constexpr int kWaves = 4;                 // waves per workgroup
-constexpr int kThreads = 64 * kWaves;
-
 __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c)
 {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
-// LDS staging of NC activation rows: one record per (column, 256-element block) holding
-// the block's 256 codes, its code sums (Q4K: eight per-32 sums; Q6K: sixteen per-16 sums)
-// and its scale(s) (PerBlock: one; Sub32: eight).  The record stride is an odd multiple of
-// 16 bytes, so the 16-byte reads of 16 lanes on 16 different blocks fall in different banks.
+// ---------------------------------------------------------------------------------------
+// Activation sources.  Both hand out wave-uniform addresses.
+
+// One column straight from global memory: codes [C], csums [C/16], scales [nsc].
+struct ActGlobal {
+    const int8_t *codes;
+    const int32_t *csums;
+    const qg_act_scale *sc;
+    __device__ __forceinline__ const int8_t *block_codes(int b) const { return codes + (size_t)b * 256; }
+    __device__ __forceinline__ int sum32(int b, int j) const { return csums[b * 16 + 2 * j] + csums[b * 16 + 2 * j + 1]; }
+    __device__ __forceinline__ int sum16(int b, int k) const { return csums[b * 16 + k]; }
+    __device__ __forceinline__ qg_act_scale scale(int b, int j, int per_block) const { return sc[b * per_block + j]; }
+};
+
+// NC columns staged in LDS, one record per (column, 256-element block) holding the block's
+// 256 codes, its code sums (Q4K: eight per-32 sums; Q6K: sixteen per-16 sums) and its
+// scale(s) (PerBlock: one; Sub32: eight).
 template <int FMT, int MODE>
 struct ActRec {
     static constexpr int kSums = FMT == QG_Q4K ? 8 : 16;
     static constexpr int kScales = MODE == QG_PERBLOCK ? 1 : 8;
     static constexpr int kSumOff = 256;
     static constexpr int kScOff = 256 + 4 * kSums;
-    static constexpr int kRaw = kScOff + 4 * kScales;
-    static constexpr int kStride = ((kRaw + 15) / 16) % 2 ? ((kRaw + 15) / 16) * 16 : ((kRaw + 15) / 16 + 1) * 16;
+    static constexpr int kStride = (kScOff + 4 * kScales + 15) / 16 * 16;
 };
-static_assert(ActRec<QG_Q4K, QG_PERBLOCK>::kStride == 304, "record stride");
-static_assert(ActRec<QG_Q6K, QG_SUB32>::kStride == 368, "record stride");
 
-struct ActView {
-    const unsigned char *base;  // record of (column 0, block 0)
-    int stride;                 // bytes between blocks
-    int col_stride;             // bytes between columns (G records)
+template <int FMT, int MODE>
+struct ActLds {
+    using R = ActRec<FMT, MODE>;
+    const unsigned char *col;   // record of (this column, block 0)
+    __device__ __forceinline__ const unsigned char *rec(int b) const { return col + (size_t)b * R::kStride; }
+    __device__ __forceinline__ const int8_t *block_codes(int b) const { return reinterpret_cast<const int8_t *>(rec(b)); }
+    __device__ __forceinline__ int sum32(int b, int j) const
+    {
+        return reinterpret_cast<const int32_t *>(rec(b) + R::kSumOff)[j];
+    }
+    __device__ __forceinline__ int sum16(int b, int k) const
+    {
+        return reinterpret_cast<const int32_t *>(rec(b) + R::kSumOff)[k];
+    }
+    __device__ __forceinline__ qg_act_scale scale(int b, int j, int) const
+    {
+        return reinterpret_cast<const qg_act_scale *>(rec(b) + R::kScOff)[j];
+    }
 };
+
+// ---------------------------------------------------------------------------------------
+// Weight-side decoding
 
 // 12-bit (sc | mn << 6) field of sub-block i from the 96-bit meta string (y, z, w)
 template <int I>
@@ -121,12 +148,6 @@ struct TileRegs<QG_Q4K> {
         for (int i = 0; i < 8; i++) w[i] = *reinterpret_cast<const uint4 *>(tile + 1024 * i + 16 * lane);
         meta = *reinterpret_cast<const uint4 *>(tile + 8192 + 16 * lane);
     }
-    __device__ __forceinline__ void zero()
-    {
-#pragma unroll
-        for (int i = 0; i < 8; i++) w[i] = make_uint4(0, 0, 0, 0);
-        meta = make_uint4(0, 0, 0, 0);
-    }
 };
 
 template <>
@@ -145,23 +166,13 @@ struct TileRegs<QG_Q6K> {
         sc = *reinterpret_cast<const uint4 *>(tile + 12288 + 16 * lane);
         d = *reinterpret_cast<const uint16_t *>(tile + 13312 + 2 * lane);
     }
-    __device__ __forceinline__ void zero()
-    {
-#pragma unroll
-        for (int i = 0; i < 8; i++) L[i] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int h = 0; h < 4; h++) H[h] = make_uint4(0, 0, 0, 0);
-        sc = make_uint4(0, 0, 0, 0);
-        d = 0;
-    }
 };
 
 // ---------------------------------------------------------------------------------------
-// Pieces of one pair for NC activation columns.
+// The piece of one (row, block) pair for one activation column.
 
-template <int MODE, int NC>
-__device__ __forceinline__ void pair_pieces(const TileRegs<QG_Q4K> &T, int b, int C, const ActView &av, int nsc,
-                                            float (&piece)[NC])
+template <int MODE, class Act>
+__device__ __forceinline__ float pair_piece(const TileRegs<QG_Q4K> &T, int b, const Act &act)
 {
     uint32_t f[8];
     f[0] = q4k_field<0>(T.meta.y, T.meta.z, T.meta.w);
@@ -172,332 +183,300 @@ __device__ __forceinline__ void pair_pieces(const TileRegs<QG_Q4K> &T, int b, in
     f[5] = q4k_field<5>(T.meta.y, T.meta.z, T.meta.w);
     f[6] = q4k_field<6>(T.meta.y, T.meta.z, T.meta.w);
     f[7] = q4k_field<7>(T.meta.y, T.meta.z, T.meta.w);
-    using R = ActRec<QG_Q4K, MODE>;
+    const int8_t *a = act.block_codes(b);
+    if constexpr (MODE == QG_PERBLOCK) {
+        int Cb = 0, Ob = 0;
 #pragma unroll
-    for (int c = 0; c < NC; c++) {
-        const unsigned char *rec = av.base + (size_t)c * av.col_stride + (size_t)b * av.stride;
-        const int8_t *a = reinterpret_cast<const int8_t *>(rec);
-        const int32_t *S32 = reinterpret_cast<const int32_t *>(rec + R::kSumOff);
-        const qg_act_scale *sc = reinterpret_cast<const qg_act_scale *>(rec + R::kScOff);
-        if constexpr (MODE == QG_PERBLOCK) {
-            int Cb = 0, Ob = 0;
+        for (int i = 0; i < 8; i++) {
+            const int P = q4k_sub_dot(T.w[i], a + 32 * i);
+            Cb += __mul24((int)(f[i] & 63u), P);
+            Ob += __mul24((int)(f[i] >> 6), act.sum32(b, i));
+        }
+        const qg_act_scale s = act.scale(b, 0, 1);
+        return piece_q4k_perblock(Cb, Ob, T.meta.x, s.m, s.e);
+    } else {
+        const F16Scale d = f16_scale(T.meta.x & 0xFFFFu);
+        const F16Scale dm = f16_scale(T.meta.x >> 16);
+        long long v[16];
+        int e[16];
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int P = q4k_sub_dot(T.w[i], a + 32 * i);
-                Cb += __mul24((int)(f[i] & 63u), P);
-                Ob += __mul24((int)(f[i] >> 6), S32[i]);
+        for (int i = 0; i < 8; i++) {
+            const int P = q4k_sub_dot(T.w[i], a + 32 * i);
+            const int Cj = __mul24((int)(f[i] & 63u), P);
+            const int Oj = __mul24((int)(f[i] >> 6), act.sum32(b, i));
+            const qg_act_scale s = act.scale(b, i, 8);
+            v[2 * i] = (long long)(d.sig * (int)s.m) * Cj;
+            e[2 * i] = s.e + d.ex;
+            v[2 * i + 1] = -(long long)(dm.sig * (int)s.m) * Oj;
+            e[2 * i + 1] = s.e + dm.ex;
+        }
+        return exact_sum<16>(v, e);
+    }
+}
+
+template <int MODE, class Act>
+__device__ __forceinline__ float pair_piece(const TileRegs<QG_Q6K> &T, int b, const Act &act)
+{
+    const uint32_t sw[4] = {T.sc.x, T.sc.y, T.sc.z, T.sc.w};
+    const int8_t *a = act.block_codes(b);
+    int Ck[16];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        int P0, P1;
+        if (i & 1) q6k_sub_dots<1>(T.L[i], T.H[i >> 1], a + 32 * i, P0, P1);
+        else q6k_sub_dots<0>(T.L[i], T.H[i >> 1], a + 32 * i, P0, P1);
+        // (q - 32) . a = q . a - 32 * sum(a)
+        const int s0 = (int)(int8_t)(sw[(2 * i) >> 2] >> (8 * ((2 * i) & 3)));
+        const int s1 = (int)(int8_t)(sw[(2 * i + 1) >> 2] >> (8 * ((2 * i + 1) & 3)));
+        Ck[2 * i] = __mul24(s0, P0 - 32 * act.sum16(b, 2 * i));
+        Ck[2 * i + 1] = __mul24(s1, P1 - 32 * act.sum16(b, 2 * i + 1));
+    }
+    if constexpr (MODE == QG_PERBLOCK) {
+        int Cb = 0;
+#pragma unroll
+        for (int k = 0; k < 16; k++) Cb += Ck[k];
+        const qg_act_scale s = act.scale(b, 0, 1);
+        return piece_q6k_perblock(Cb, T.d, s.m, s.e);
+    } else {
+        const F16Scale d = f16_scale(T.d);
+        long long v[8];
+        int e[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const qg_act_scale s = act.scale(b, j, 8);
+            v[j] = (long long)(d.sig * (int)s.m) * (long long)(Ck[2 * j] + Ck[2 * j + 1]);
+            e[j] = s.e + d.ex;
+        }
+        return exact_sum<8>(v, e);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// The kernel.  blockIdx.x = 64-row group, blockIdx.y = batch of NC activation columns.
+// W waves split the group's G blocks (wave w takes blocks w, w+W, ...); with DB (more
+// blocks than waves) each wave loads its next tile while the current one is computed.
+
+template <int FMT, int MODE, int NC, int W, bool DB>
+__global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict__ image, int rows, int G,
+                                                      const int8_t *__restrict__ codes,
+                                                      const qg_act_scale *__restrict__ scales,
+                                                      const int32_t *__restrict__ csums, int ncol,
+                                                      float *__restrict__ out)
+{
+    extern __shared__ __align__(16) unsigned char lds[];
+    using T = TileRegs<FMT>;
+    const int C = G * 256;
+    const int nsc = MODE == QG_PERBLOCK ? G : G * 8;
+    const int g = blockIdx.x;
+    const int col0 = blockIdx.y * NC;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint8_t *gbase = image + (size_t)g * G * T::kBytes;
+
+    // the wave's first tile: loads in flight before anything else
+    T t0;
+    [[maybe_unused]] T t1;
+    if (wid < G) t0.load(gbase + (size_t)wid * T::kBytes, lane);
+
+    float *s_piece;
+    const unsigned char *s_rec = nullptr;
+    if constexpr (NC > 1) {
+        // stage NC columns as per-block records (codes, code sums, scales)
+        using R = ActRec<FMT, MODE>;
+        unsigned char *rec = lds;
+        for (int c = 0; c < NC; c++) {
+            const int col = col0 + c;
+            const bool have = col < ncol;
+            unsigned char *rc = rec + (size_t)c * G * R::kStride;
+            const uint4 *src = reinterpret_cast<const uint4 *>(codes + (size_t)col * C);
+            for (int i = threadIdx.x; i < C / 16; i += 64 * W)
+                *reinterpret_cast<uint4 *>(rc + (size_t)(i >> 4) * R::kStride + 16 * (i & 15)) =
+                    have ? src[i] : make_uint4(0, 0, 0, 0);
+            const int32_t *cs = csums + (size_t)col * (C / 16);
+            for (int i = threadIdx.x; i < G * R::kSums; i += 64 * W) {
+                int32_t v = 0;
+                if (have) v = R::kSums == 8 ? cs[2 * i] + cs[2 * i + 1] : cs[i];
+                *reinterpret_cast<int32_t *>(rc + (size_t)(i / R::kSums) * R::kStride + R::kSumOff +
+                                             4 * (i % R::kSums)) = v;
             }
-            const qg_act_scale s = sc[0];
-            piece[c] = piece_q4k_perblock(Cb, Ob, T.meta.x, s.m, s.e);
-        } else {
-            const F16Scale d = f16_scale(T.meta.x & 0xFFFFu);
-            const F16Scale dm = f16_scale(T.meta.x >> 16);
-            long long v[16];
-            int e[16];
+            // qg_act_scale is 4 bytes: copy it as one word
+            const uint32_t *scw = reinterpret_cast<const uint32_t *>(scales) + (size_t)col * nsc;
+            for (int i = threadIdx.x; i < nsc; i += 64 * W)
+                *reinterpret_cast<uint32_t *>(rc + (size_t)(i / R::kScales) * R::kStride + R::kScOff +
+                                              4 * (i % R::kScales)) = have ? scw[i] : 0u;
+        }
+        s_rec = rec;
+        s_piece = reinterpret_cast<float *>(lds + (size_t)NC * G * R::kStride);
+        __syncthreads();
+    } else {
+        s_piece = reinterpret_cast<float *>(lds);
+    }
+
+    auto compute = [&](const T &tile, int b) {
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int P = q4k_sub_dot(T.w[i], a + 32 * i);
-                const int Cj = __mul24((int)(f[i] & 63u), P);
-                const int Oj = __mul24((int)(f[i] >> 6), S32[i]);
-                const qg_act_scale s = sc[i];
-                v[2 * i] = (long long)(d.sig * (int)s.m) * Cj;
-                e[2 * i] = s.e + d.ex;
-                v[2 * i + 1] = -(long long)(dm.sig * (int)s.m) * Oj;
-                e[2 * i + 1] = s.e + dm.ex;
+        for (int c = 0; c < NC; c++) {
+            float p;
+            if constexpr (NC == 1) {
+                const ActGlobal act{codes + (size_t)col0 * C, csums + (size_t)col0 * (C / 16),
+                                    scales + (size_t)col0 * nsc};
+                p = pair_piece<MODE>(tile, b, act);
+            } else {
+                const ActLds<FMT, MODE> act{s_rec + (size_t)c * G * ActRec<FMT, MODE>::kStride};
+                p = pair_piece<MODE>(tile, b, act);
             }
-            piece[c] = exact_sum<16>(v, e);
+            s_piece[((size_t)c * G + b) * 64 + lane] = p;
+        }
+    };
+
+    if constexpr (DB) {
+        // two register sets, no copies: t0 holds blocks wid, wid+2W, ...; t1 holds wid+W, ...
+        for (int b = wid; b < G; b += 2 * W) {
+            if (b + W < G) t1.load(gbase + (size_t)(b + W) * T::kBytes, lane);
+            compute(t0, b);
+            if (b + W >= G) break;
+            if (b + 2 * W < G) t0.load(gbase + (size_t)(b + 2 * W) * T::kBytes, lane);
+            compute(t1, b + W);
+        }
+    } else {
+        // at most one block per wave
+        if (wid < G) compute(t0, wid);
+    }
+    __syncthreads();
+
+    // the first wave adds each row's pieces in block order, one row per lane
+    if (wid == 0) {
+        const int64_t row = (int64_t)g * 64 + lane;
+#pragma unroll
+        for (int c = 0; c < NC; c++) {
+            float y = 0.0f;
+            const float *pc = s_piece + (size_t)c * G * 64 + lane;
+            for (int b = 0; b < G; b++) y = fadd_ftz(y, pc[(size_t)b * 64]);
+            if (row < rows && col0 + c < ncol) out[(int64_t)(col0 + c) * rows + row] = canon_nan(y);
         }
     }
 }
 
-template <int MODE, int NC>
-__device__ __forceinline__ void pair_pieces(const TileRegs<QG_Q6K> &T, int b, int C, const ActView &av, int nsc,
-                                            float (&piece)[NC])
+// ---------------------------------------------------------------------------------------
+// Integer sums per (row, sub-block) for one activation row (debug view of the integer
+// stage).  One wave per tile.
+
+template <int FMT>
+__global__ __launch_bounds__(256) void block_sums_kernel(const uint8_t *__restrict__ image, int rows, int G,
+                                                         int64_t ntiles, const int8_t *__restrict__ codes,
+                                                         int32_t *__restrict__ csum_out,
+                                                         int32_t *__restrict__ osum_out)
 {
-    using R = ActRec<QG_Q6K, MODE>;
-    const uint32_t sw[4] = {T.sc.x, T.sc.y, T.sc.z, T.sc.w};
-#pragma unroll
-    for (int c = 0; c < NC; c++) {
-        const unsigned char *rec = av.base + (size_t)c * av.col_stride + (size_t)b * av.stride;
-        const int8_t *a = reinterpret_cast<const int8_t *>(rec);
-        const int32_t *S16 = reinterpret_cast<const int32_t *>(rec + R::kSumOff);
-        const qg_act_scale *sc = reinterpret_cast<const qg_act_scale *>(rec + R::kScOff);
-        int Ck[16];
-#pragma unroll
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= ntiles) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t g = t / G;
+    const int b = (int)(t - g * G);
+    const int64_t r = g * 64 + lane;
+    const int8_t *a = codes + (size_t)b * 256;
+    if constexpr (FMT == QG_Q4K) {
+        TileRegs<QG_Q4K> T;
+        T.load(image + t * kTileBytesQ4K, lane);
+        if (r >= rows) return;
+        uint32_t f[8];
+        f[0] = q4k_field<0>(T.meta.y, T.meta.z, T.meta.w);
+        f[1] = q4k_field<1>(T.meta.y, T.meta.z, T.meta.w);
+        f[2] = q4k_field<2>(T.meta.y, T.meta.z, T.meta.w);
+        f[3] = q4k_field<3>(T.meta.y, T.meta.z, T.meta.w);
+        f[4] = q4k_field<4>(T.meta.y, T.meta.z, T.meta.w);
+        f[5] = q4k_field<5>(T.meta.y, T.meta.z, T.meta.w);
+        f[6] = q4k_field<6>(T.meta.y, T.meta.z, T.meta.w);
+        f[7] = q4k_field<7>(T.meta.y, T.meta.z, T.meta.w);
+        for (int i = 0; i < 8; i++) {
+            int S = 0;
+            for (int k = 0; k < 32; k++) S += a[32 * i + k];
+            csum_out[(r * G + b) * 8 + i] = (int)(f[i] & 63u) * q4k_sub_dot(T.w[i], a + 32 * i);
+            osum_out[(r * G + b) * 8 + i] = (int)(f[i] >> 6) * S;
+        }
+    } else {
+        TileRegs<QG_Q6K> T;
+        T.load(image + t * kTileBytesQ6K, lane);
+        if (r >= rows) return;
+        const uint32_t sw[4] = {T.sc.x, T.sc.y, T.sc.z, T.sc.w};
         for (int i = 0; i < 8; i++) {
             int P0, P1;
             if (i & 1) q6k_sub_dots<1>(T.L[i], T.H[i >> 1], a + 32 * i, P0, P1);
             else q6k_sub_dots<0>(T.L[i], T.H[i >> 1], a + 32 * i, P0, P1);
-            // (q - 32) . a = q . a - 32 * sum(a)
-            const int s0 = (int)(int8_t)(sw[(2 * i) >> 2] >> (8 * ((2 * i) & 3)));
-            const int s1 = (int)(int8_t)(sw[(2 * i + 1) >> 2] >> (8 * ((2 * i + 1) & 3)));
-            Ck[2 * i] = __mul24(s0, P0 - 32 * S16[2 * i]);
-            Ck[2 * i + 1] = __mul24(s1, P1 - 32 * S16[2 * i + 1]);
-        }
-        if constexpr (MODE == QG_PERBLOCK) {
-            int Cb = 0;
-#pragma unroll
-            for (int k = 0; k < 16; k++) Cb += Ck[k];
-            const qg_act_scale s = sc[0];
-            piece[c] = piece_q6k_perblock(Cb, T.d, s.m, s.e);
-        } else {
-            const F16Scale d = f16_scale(T.d);
-            long long v[8];
-            int e[8];
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const qg_act_scale s = sc[j];
-                v[j] = (long long)(d.sig * (int)s.m) * (long long)(Ck[2 * j] + Ck[2 * j + 1]);
-                e[j] = s.e + d.ex;
-            }
-            piece[c] = exact_sum<8>(v, e);
-        }
-    }
-}
-
-__device__ __forceinline__ void wave_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// ---------------------------------------------------------------------------------------
-// The kernel.  blockIdx.y selects a batch of NC activation columns (col0 = NC*blockIdx.y).
-// The first tile's loads are issued before the activations are staged, and with PIPE each
-// tile's successor is loaded while the tile itself is being computed.
-
-template <int FMT, int MODE, int NC, bool PIPE>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t *__restrict__ image, int64_t n_tiles,
-                                                        int rows, int G, int K, int RT, int n_super,
-                                                        const int8_t *__restrict__ codes,
-                                                        const qg_act_scale *__restrict__ scales,
-                                                        const int32_t *__restrict__ csums, int ncol,
-                                                        float *__restrict__ out)
-{
-    extern __shared__ __align__(16) unsigned char lds[];
-    constexpr int kTileBytes = TileRegs<FMT>::kBytes;
-    const int C = G * 256;
-    const int nsc = MODE == QG_PERBLOCK ? G : G * 8;
-    const int col0 = blockIdx.y * NC;
-    const int lane = threadIdx.x & 63;
-    const int wid = threadIdx.x >> 6;
-    const int nwaves = gridDim.x * kWaves;
-    const int st0 = blockIdx.x * kWaves + wid;
-
-    // the wave's first tile: loads in flight before anything else
-    TileRegs<FMT> cur;
-    {
-        const int64_t t0 = (int64_t)st0 * K;
-        if (st0 < n_super && t0 < n_tiles) cur.load(image + t0 * kTileBytes, lane);
-        else cur.zero();
-    }
-
-    // stage NC activation columns as per-block records (codes, code sums, scales)
-    using R = ActRec<FMT, MODE>;
-    unsigned char *s_rec = lds;
-    float *s_piece = reinterpret_cast<float *>(lds + (size_t)NC * G * R::kStride);
-    for (int c = 0; c < NC; c++) {
-        const int col = col0 + c;
-        const bool have = col < ncol;
-        unsigned char *rc = s_rec + (size_t)c * G * R::kStride;
-        const uint4 *src = reinterpret_cast<const uint4 *>(codes + (size_t)col * C);
-        for (int i = threadIdx.x; i < C / 16; i += kThreads)
-            *reinterpret_cast<uint4 *>(rc + (size_t)(i >> 4) * R::kStride + 16 * (i & 15)) =
-                have ? src[i] : make_uint4(0, 0, 0, 0);
-        const int32_t *cs = csums + (size_t)col * (C / 16);
-        for (int i = threadIdx.x; i < G * R::kSums; i += kThreads) {
-            int32_t v = 0;
-            if (have) v = R::kSums == 8 ? cs[2 * i] + cs[2 * i + 1] : cs[i];
-            *reinterpret_cast<int32_t *>(rc + (size_t)(i / R::kSums) * R::kStride + R::kSumOff + 4 * (i % R::kSums)) = v;
-        }
-        // qg_act_scale is 4 bytes: copy it as one word
-        const uint32_t *scw = reinterpret_cast<const uint32_t *>(scales) + (size_t)col * nsc;
-        for (int i = threadIdx.x; i < nsc; i += kThreads)
-            *reinterpret_cast<uint32_t *>(rc + (size_t)(i / R::kScales) * R::kStride + R::kScOff + 4 * (i % R::kScales)) =
-                have ? scw[i] : 0u;
-    }
-    __syncthreads();
-
-    const ActView av{s_rec, R::kStride, G * R::kStride};
-    float *wp = s_piece + (size_t)wid * 64 * NC;
-
-    for (int st = st0; st < n_super; st += nwaves) {
-        float y[NC];
-#pragma unroll
-        for (int c = 0; c < NC; c++) y[c] = 0.0f;
-        for (int k = 0; k < K; k++) {
-            const int64_t t = (int64_t)st * K + k;
-            if (!PIPE && (k > 0 || st != st0)) {
-                if (t < n_tiles) cur.load(image + t * kTileBytes, lane);
-                else cur.zero();
-            }
-            TileRegs<FMT> nxt;
-            if constexpr (PIPE) {
-                // successor in this wave's walk: next tile of the super-tile, else the next super-tile's first
-                const int64_t tn = k + 1 < K ? t + 1 : (int64_t)(st + nwaves) * K;
-                const bool more = k + 1 < K || st + nwaves < n_super;
-                if (more && tn < n_tiles) nxt.load(image + tn * kTileBytes, lane);
-                else nxt.zero();
-            }
-            const int lp = k * 64 + lane;            // pair within the super-tile
-            const int rl = lp / G;
-            const int b = lp - rl * G;
-            float piece[NC];
-            pair_pieces<MODE, NC>(cur, b, C, av, nsc, piece);
-#pragma unroll
-            for (int c = 0; c < NC; c++) wp[c * 64 + lane] = piece[c];
-            wave_sync();
-            // lane i < RT owns local row i: pairs [i*G, (i+1)*G); this tile has [64k, 64k+64)
-            if (lane < RT) {
-                if (K == 1 && (G & 3) == 0) {
-                    // whole row in this tile, four pieces per LDS read
-                    for (int q = lane * G; q < lane * G + G; q += 4) {
-#pragma unroll
-                        for (int c = 0; c < NC; c++) {
-                            const float4 p4 = *reinterpret_cast<const float4 *>(wp + c * 64 + q);
-                            y[c] = fadd_ftz(y[c], p4.x);
-                            y[c] = fadd_ftz(y[c], p4.y);
-                            y[c] = fadd_ftz(y[c], p4.z);
-                            y[c] = fadd_ftz(y[c], p4.w);
-                        }
-                    }
-                } else {
-                    int q0 = lane * G, q1 = q0 + G;
-                    q0 = q0 > k * 64 ? q0 : k * 64;
-                    q1 = q1 < k * 64 + 64 ? q1 : k * 64 + 64;
-                    for (int q = q0; q < q1; q++) {
-#pragma unroll
-                        for (int c = 0; c < NC; c++) y[c] = fadd_ftz(y[c], wp[c * 64 + q - k * 64]);
-                    }
-                }
-            }
-            wave_sync();
-            if constexpr (PIPE) cur = nxt;
-        }
-        const int64_t row = (int64_t)st * RT + lane;
-        if (lane < RT && row < rows) {
-#pragma unroll
-            for (int c = 0; c < NC; c++)
-                if (col0 + c < ncol) out[(int64_t)(col0 + c) * rows + row] = canon_nan(y[c]);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// Integer sums per (row, sub-block) for one activation row (debug view of the integer stage)
-
-template <int FMT>
-__global__ __launch_bounds__(kThreads) void block_sums_kernel(const uint8_t *__restrict__ image, int64_t npairs,
-                                                              int G, const int8_t *__restrict__ codes,
-                                                              int32_t *__restrict__ csum_out,
-                                                              int32_t *__restrict__ osum_out)
-{
-    const int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (p >= npairs) return;
-    const int64_t t = p / 64;
-    const int lane = (int)(p - t * 64);
-    const int b = (int)(p % G);
-    const int8_t *a = codes + (size_t)b * 256;
-    if constexpr (FMT == QG_Q4K) {
-        const uint8_t *tile = image + t * kTileBytesQ4K;
-        const uint4 meta = *reinterpret_cast<const uint4 *>(tile + 8192 + 16 * lane);
-        uint32_t f[8];
-        f[0] = q4k_field<0>(meta.y, meta.z, meta.w);
-        f[1] = q4k_field<1>(meta.y, meta.z, meta.w);
-        f[2] = q4k_field<2>(meta.y, meta.z, meta.w);
-        f[3] = q4k_field<3>(meta.y, meta.z, meta.w);
-        f[4] = q4k_field<4>(meta.y, meta.z, meta.w);
-        f[5] = q4k_field<5>(meta.y, meta.z, meta.w);
-        f[6] = q4k_field<6>(meta.y, meta.z, meta.w);
-        f[7] = q4k_field<7>(meta.y, meta.z, meta.w);
-        for (int i = 0; i < 8; i++) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(tile + 1024 * i + 16 * lane);
-            int S = 0;
-            for (int k = 0; k < 32; k++) S += a[32 * i + k];
-            csum_out[p * 8 + i] = (int)(f[i] & 63u) * q4k_sub_dot(w, a + 32 * i);
-            osum_out[p * 8 + i] = (int)(f[i] >> 6) * S;
-        }
-    } else {
-        const uint8_t *tile = image + t * kTileBytesQ6K;
-        const uint4 scv = *reinterpret_cast<const uint4 *>(tile + 12288 + 16 * lane);
-        const uint32_t sw[4] = {scv.x, scv.y, scv.z, scv.w};
-        for (int i = 0; i < 8; i++) {
-            const uint4 L = *reinterpret_cast<const uint4 *>(tile + 1024 * i + 16 * lane);
-            const uint4 H = *reinterpret_cast<const uint4 *>(tile + 8192 + 1024 * (i >> 1) + 16 * lane);
-            int P0, P1;
-            if (i & 1) q6k_sub_dots<1>(L, H, a + 32 * i, P0, P1);
-            else q6k_sub_dots<0>(L, H, a + 32 * i, P0, P1);
             int S0 = 0, S1 = 0;
             for (int k = 0; k < 16; k++) { S0 += a[32 * i + k]; S1 += a[32 * i + 16 + k]; }
             const int s0 = (int)(int8_t)(sw[(2 * i) >> 2] >> (8 * ((2 * i) & 3)));
             const int s1 = (int)(int8_t)(sw[(2 * i + 1) >> 2] >> (8 * ((2 * i + 1) & 3)));
-            csum_out[p * 16 + 2 * i] = s0 * (P0 - 32 * S0);
-            csum_out[p * 16 + 2 * i + 1] = s1 * (P1 - 32 * S1);
+            csum_out[(r * G + b) * 16 + 2 * i] = s0 * (P0 - 32 * S0);
+            csum_out[(r * G + b) * 16 + 2 * i + 1] = s1 * (P1 - 32 * S1);
         }
     }
 }
 
-int gcd_int(int a, int b)
+// LDS bytes the kernel needs for NC columns
+template <int FMT, int MODE>
+size_t gemv_lds(int G, int nc)
 {
-    while (b) { const int t = a % b; a = b; b = t; }
-    return a;
+    const size_t pieces = (size_t)nc * G * 64 * 4;
+    return nc > 1 ? (size_t)nc * G * ActRec<FMT, MODE>::kStride + pieces : pieces;
 }
 
-template <int FMT, int MODE, int NC, bool PIPE>
+template <int FMT, int MODE, int NC, int W, bool DB>
 int launch_typed(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
                  const qg_act_scale *scales, const int32_t *csums, float *out, hipStream_t s)
 {
-    const int g = gcd_int(G, 64);
-    const int RT = 64 / g;                    // rows per super-tile
-    const int K = G / g;                      // tiles per super-tile
-    const int64_t n_super64 = (rows + RT - 1) / RT;
-    const int64_t n_tiles = (rows * G + 63) / 64;
-    if (n_super64 > 0x7fffffff) return fail(QG_E_SHAPE, "too many rows: %lld", (long long)rows);
-    const int n_super = (int)n_super64;
-    const size_t lds = (size_t)NC * G * ActRec<FMT, MODE>::kStride + (size_t)kWaves * 64 * NC * 4;
-    const Tuning &tn = tuning();
-    int64_t wgs;
-    if (tn.grid_wgs > 0) {
-        wgs = tn.grid_wgs;
-    } else {
-        const int wpc = tn.waves_per_cu > 0 ? tn.waves_per_cu : 16;
-        const int64_t max_waves = (int64_t)device_cu_count() * wpc;
-        const int64_t waves = n_super64 < max_waves ? n_super64 : max_waves;
-        wgs = (waves + kWaves - 1) / kWaves;
-    }
-    if (wgs < 1) wgs = 1;
-    if (wgs > 0x7fffffff) wgs = 0x7fffffff;
-    const int64_t ybatches = (ncol + NC - 1) / NC;
-    dim3 grid((unsigned)wgs, (unsigned)ybatches);
+    const int64_t groups = (rows + 63) / 64;
+    if (groups > 0x7fffffff) return fail(QG_E_SHAPE, "too many rows: %lld", (long long)rows);
+    const size_t lds = gemv_lds<FMT, MODE>(G, NC);
+    const dim3 grid((unsigned)groups, (unsigned)((ncol + NC - 1) / NC));
     hipEvent_t ev0, ev1;
     take_timing_events(&ev0, &ev1);
     if (ev0 && ev1)
-        hipExtLaunchKernelGGL((gemv_kernel<FMT, MODE, NC, PIPE>), grid, dim3(kThreads), lds, s, ev0, ev1, 0,
-                              static_cast<const uint8_t *>(image), n_tiles, (int)rows, G, K, RT, n_super,
-                              codes, scales, csums, (int)ncol, out);
+        hipExtLaunchKernelGGL((gemv_kernel<FMT, MODE, NC, W, DB>), grid, dim3(64 * W), lds, s, ev0, ev1, 0,
+                              static_cast<const uint8_t *>(image), (int)rows, G, codes, scales, csums, (int)ncol, out);
     else
-        hipLaunchKernelGGL((gemv_kernel<FMT, MODE, NC, PIPE>), grid, dim3(kThreads), lds, s,
-                           static_cast<const uint8_t *>(image), n_tiles, (int)rows, G, K, RT, n_super, codes,
-                           scales, csums, (int)ncol, out);
+        hipLaunchKernelGGL((gemv_kernel<FMT, MODE, NC, W, DB>), grid, dim3(64 * W), lds, s,
+                           static_cast<const uint8_t *>(image), (int)rows, G, codes, scales, csums, (int)ncol, out);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemv launch: %s", hipGetErrorString(e));
     return QG_OK;
+}
+
+template <int FMT, int MODE, int NC, int W>
+int launch_db(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
+              const qg_act_scale *scales, const int32_t *csums, float *out, hipStream_t s)
+{
+    // 16-wave workgroups are used only with at most one tile per wave: their 128-register
+    // budget does not hold two tiles' loads without spilling
+    if constexpr (W < 16)
+        if (G > W) return launch_typed<FMT, MODE, NC, W, true>(rows, G, ncol, image, codes, scales, csums, out, s);
+    return launch_typed<FMT, MODE, NC, W, false>(rows, G, ncol, image, codes, scales, csums, out, s);
+}
+
+template <int FMT, int MODE, int NC>
+int launch_w(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
+             const qg_act_scale *scales, const int32_t *csums, float *out, hipStream_t s)
+{
+    // waves per workgroup: the tuning knob if set, else one wave per block up to 16 (8 when
+    // several columns share the workgroup, whose registers do not fit 16 waves)
+    int w = tuning().waves_per_wg;
+    if (w <= 0) w = G >= 16 ? 16 : G >= 8 ? 8 : 4;
+    if (NC > 1 && w > 8) w = 8;
+    if (w > 8 && G > 16) w = 8;
+    if constexpr (NC == 1)
+        if (w >= 16) return launch_db<FMT, MODE, NC, 16>(rows, G, ncol, image, codes, scales, csums, out, s);
+    if (w >= 8) return launch_db<FMT, MODE, NC, 8>(rows, G, ncol, image, codes, scales, csums, out, s);
+    return launch_db<FMT, MODE, NC, 4>(rows, G, ncol, image, codes, scales, csums, out, s);
 }
 
 template <int FMT, int MODE>
 int launch_nc(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
               const qg_act_scale *scales, const int32_t *csums, float *out, hipStream_t s)
 {
-    // widest column batch whose staging fits 64 KiB of LDS
-    auto fits = [&](int nc) {
-        return (size_t)nc * G * ActRec<FMT, MODE>::kStride + (size_t)kWaves * 64 * nc * 4 <= 65536;
-    };
-    if (ncol >= 8 && fits(8)) return launch_typed<FMT, MODE, 8, false>(rows, G, ncol, image, codes, scales, csums, out, s);
-    if (ncol >= 4 && fits(4)) return launch_typed<FMT, MODE, 4, false>(rows, G, ncol, image, codes, scales, csums, out, s);
-    if (ncol >= 2 && fits(2)) return launch_typed<FMT, MODE, 2, false>(rows, G, ncol, image, codes, scales, csums, out, s);
-    if (tuning().pipeline) return launch_typed<FMT, MODE, 1, true>(rows, G, ncol, image, codes, scales, csums, out, s);
-    return launch_typed<FMT, MODE, 1, false>(rows, G, ncol, image, codes, scales, csums, out, s);
+    // widest column batch whose LDS fits 64 KiB
+    auto fits = [&](int nc) { return gemv_lds<FMT, MODE>(G, nc) <= 65536; };
+    if (ncol >= 8 && fits(8)) return launch_w<FMT, MODE, 8>(rows, G, ncol, image, codes, scales, csums, out, s);
+    if (ncol >= 4 && fits(4)) return launch_w<FMT, MODE, 4>(rows, G, ncol, image, codes, scales, csums, out, s);
+    if (ncol >= 2 && fits(2)) return launch_w<FMT, MODE, 2>(rows, G, ncol, image, codes, scales, csums, out, s);
+    return launch_w<FMT, MODE, 1>(rows, G, ncol, image, codes, scales, csums, out, s);
 }
 
 }  // namespace
@@ -521,15 +500,15 @@ int launch_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, co
                       int32_t *csum_out, int32_t *osum_out, hipStream_t s)
 {
     const int G = (int)(cols / 256);
-    const int64_t npairs = rows * G;
-    if (npairs == 0) return QG_OK;
-    const int64_t wgs = (npairs + kThreads - 1) / kThreads;
+    const int64_t ntiles = (rows + 63) / 64 * G;
+    if (ntiles == 0) return QG_OK;
+    const int64_t wgs = (ntiles + 3) / 4;
     if (fmt == QG_Q4K)
-        hipLaunchKernelGGL(block_sums_kernel<QG_Q4K>, dim3((unsigned)wgs), dim3(kThreads), 0, s,
-                           static_cast<const uint8_t *>(image), npairs, G, codes, csum_out, osum_out);
+        hipLaunchKernelGGL(block_sums_kernel<QG_Q4K>, dim3((unsigned)wgs), dim3(256), 0, s,
+                           static_cast<const uint8_t *>(image), (int)rows, G, ntiles, codes, csum_out, osum_out);
     else
-        hipLaunchKernelGGL(block_sums_kernel<QG_Q6K>, dim3((unsigned)wgs), dim3(kThreads), 0, s,
-                           static_cast<const uint8_t *>(image), npairs, G, codes, csum_out, osum_out);
+        hipLaunchKernelGGL(block_sums_kernel<QG_Q6K>, dim3((unsigned)wgs), dim3(256), 0, s,
+                           static_cast<const uint8_t *>(image), (int)rows, G, ntiles, codes, csum_out, osum_out);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_E_RUNTIME, "block_sums launch: %s", hipGetErrorString(e));
     return QG_OK;

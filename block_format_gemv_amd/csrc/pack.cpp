@@ -3,8 +3,8 @@
 // The pages store a weight as "a scale times an integer" with the codes and scales kept as
 // stored ("Module numerics" of logicaffeine_compile::spatial::decode_engine, Structs
 // CodedRow, Segment, Scale, Unreadable).  The packer only rearranges those fields into
-// 64-pair tiles so that every GPU load is a contiguous 1 KiB per wave; it validates every
-// field and refuses a block whose scale is inf or NaN.
+// tiles of 64 rows x one block so that every GPU load is a contiguous 1 KiB per wave; it
+// validates every field and refuses a block whose scale is inf or NaN.
 #include <stdint.h>
 #include <string.h>
 
@@ -25,8 +25,8 @@ using namespace qg;
 extern "C" size_t qg_image_bytes(int fmt, int64_t rows, int64_t cols)
 {
     if ((fmt != QG_Q4K && fmt != QG_Q6K) || rows < 0 || cols <= 0 || cols % QG_BLOCK) return 0;
-    const int64_t pairs = rows * (cols / QG_BLOCK);
-    const int64_t tiles = (pairs + kTilePairs - 1) / kTilePairs;
+    const int64_t groups = (rows + kTileRows - 1) / kTileRows;
+    const int64_t tiles = groups * (cols / QG_BLOCK);
     return (size_t)tiles * (size_t)(fmt == QG_Q4K ? kTileBytesQ4K : kTileBytesQ6K);
 }
 
@@ -57,11 +57,9 @@ extern "C" int qg_pack_q4k(int64_t rows, int64_t cols, const uint8_t *q, const u
     const size_t bytes = qg_image_bytes(QG_Q4K, rows, cols);
     uint8_t *img = static_cast<uint8_t *>(image_host);
     memset(img, 0, bytes);
-    const int64_t npairs = rows * G;
-    for (int64_t p = 0; p < npairs; p++) {
-        const int64_t r = p / G, b = p % G;
-        uint8_t *tile = img + (p / kTilePairs) * kTileBytesQ4K;
-        const int l = (int)(p % kTilePairs);
+    for (int64_t r = 0; r < rows; r++) for (int64_t b = 0; b < G; b++) {
+        uint8_t *tile = img + ((r / kTileRows) * G + b) * kTileBytesQ4K;
+        const int l = (int)(r % kTileRows);
         const uint8_t *qb = q + r * cols + b * QG_BLOCK;
         for (int i = 0; i < 8; i++) {
             uint8_t *dst = tile + 1024 * i + 16 * l;
@@ -109,11 +107,9 @@ extern "C" int qg_pack_q6k(int64_t rows, int64_t cols, const uint8_t *q, const i
     const size_t bytes = qg_image_bytes(QG_Q6K, rows, cols);
     uint8_t *img = static_cast<uint8_t *>(image_host);
     memset(img, 0, bytes);
-    const int64_t npairs = rows * G;
-    for (int64_t p = 0; p < npairs; p++) {
-        const int64_t r = p / G, b = p % G;
-        uint8_t *tile = img + (p / kTilePairs) * kTileBytesQ6K;
-        const int l = (int)(p % kTilePairs);
+    for (int64_t r = 0; r < rows; r++) for (int64_t b = 0; b < G; b++) {
+        uint8_t *tile = img + ((r / kTileRows) * G + b) * kTileBytesQ6K;
+        const int l = (int)(r % kTileRows);
         const uint8_t *qb = q + r * cols + b * QG_BLOCK;
         for (int i = 0; i < 8; i++) {
             uint8_t *dst = tile + 1024 * i + 16 * l;

@@ -132,38 +132,12 @@ __device__ inline bool mag_greater(long long a, int ea, long long b, int eb)
     return A > B;
 }
 
-// The windowed exact sum when some exponent lies more than kSumWindow below another: the
-// largest-magnitude term (first of equals) fixes L; a term whose exponent is below
-// L - kSumWindow is floored to a multiple of 2^(L - kSumWindow).  Rare: kept out of line.
-__device__ __noinline__ float exact_sum_windowed(const long long *v, const int *e, int n)
-{
-    int L = 0;
-    for (int i = 1; i < n; i++)
-        if (mag_greater(v[i], e[i], v[L], e[L])) L = i;
-    const int fe = e[L] - kSumWindow;
-    int emin = 0x7fffffff;
-    for (int i = 0; i < n; i++) {
-        const int ei = e[i] < fe ? fe : e[i];
-        emin = ei < emin ? ei : emin;
-    }
-    u128 s = 0;
-    for (int i = 0; i < n; i++) {
-        long long vi = v[i];
-        int ei = e[i];
-        if (ei < fe) {
-            const int sh = fe - ei;
-            vi = sh >= 63 ? (vi < 0 ? -1 : 0) : (vi >> sh);   // arithmetic shift = floor
-            ei = fe;
-        }
-        if (vi == 0) continue;
-        s += (u128)(i128)vi << (ei - emin);
-    }
-    return r32_i128((i128)s, emin);
-}
-
 // Sum of v[i] * 2^e[i] rounded once ("Module numerics", Functions exact_sum).  Terms are
-// below 2^45 in magnitude here.  When every exponent is within kSumWindow of every other
-// no term can lie past the window, and the aligned sum fits 128 bits.
+// below 2^45 in magnitude here.  When every exponent is within kSumWindow of every other,
+// no term can lie past the window and the aligned sum fits 128 bits.  Otherwise the
+// largest-magnitude term (first of equals) fixes L, and a term whose exponent is below
+// L - kSumWindow is floored to a multiple of 2^(L - kSumWindow) first.  Every index is a
+// compile-time constant, so the terms stay in registers.
 template <int N>
 __device__ __forceinline__ float exact_sum(const long long (&v)[N], const int (&e)[N])
 {
@@ -173,11 +147,38 @@ __device__ __forceinline__ float exact_sum(const long long (&v)[N], const int (&
         emin = e[i] < emin ? e[i] : emin;
         emax = e[i] > emax ? e[i] : emax;
     }
-    if (emax - emin > kSumWindow) return exact_sum_windowed(v, e, N);
+    if (emax - emin <= kSumWindow) {
+        u128 s = 0;
+#pragma unroll
+        for (int i = 0; i < N; i++) s += (u128)(i128)v[i] << (e[i] - emin);
+        return r32_i128((i128)s, emin);
+    }
+    // the window is engaged: rare, never at the shipped workloads
+    long long vL = v[0];
+    int eL = e[0];
+#pragma unroll
+    for (int i = 1; i < N; i++)
+        if (mag_greater(v[i], e[i], vL, eL)) { vL = v[i]; eL = e[i]; }
+    const int fe = eL - kSumWindow;
+    int emin2 = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        const int ei = e[i] < fe ? fe : e[i];
+        emin2 = ei < emin2 ? ei : emin2;
+    }
     u128 s = 0;
 #pragma unroll
-    for (int i = 0; i < N; i++) s += (u128)(i128)v[i] << (e[i] - emin);
-    return r32_i128((i128)s, emin);
+    for (int i = 0; i < N; i++) {
+        long long vi = v[i];
+        int ei = e[i];
+        if (ei < fe) {
+            const int sh = fe - ei;
+            vi = sh >= 63 ? (vi < 0 ? -1 : 0) : (vi >> sh);   // arithmetic shift = floor
+            ei = fe;
+        }
+        if (vi != 0) s += (u128)(i128)vi << (ei - emin2);
+    }
+    return r32_i128((i128)s, emin2);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -9,7 +9,7 @@
 namespace qg {
 
 // image tile geometry (see the layout in qgemv.h)
-constexpr int kTilePairs = 64;
+constexpr int kTileRows = 64;     // rows per tile (one 256-element block each)
 constexpr int kTileBytesQ4K = 64 * 144;   // 9216
 constexpr int kTileBytesQ6K = 64 * 210;   // 13440
 
@@ -17,9 +17,7 @@ constexpr int kTileBytesQ6K = 64 * 210;   // 13440
 int fail(int status, const char *fmt, ...);
 
 struct Tuning {
-    int waves_per_cu;   // 0 = default
-    int64_t grid_wgs;   // 0 = derived
-    int pipeline;       // 1: load each tile's successor during its compute (single column)
+    int waves_per_wg;   // waves per GEMV workgroup (2, 4, 8, 16); 0 = derived from the block count
 };
 const Tuning &tuning();
 

@@ -79,10 +79,10 @@ int qg_reads(int fmt, int mode);
 /*
  * Weight image ------------------------------------------------------------------------
  *
- * A matrix of R rows and C columns (C = 256*G) is G blocks per row.  Its (row, block) pairs
- * are numbered p = r*G + b and cut into tiles of 64 consecutive pairs; tile t holds pairs
- * 64t .. 64t+63 (pairs past R*G are zero padding).  Lane l of a tile is pair 64t + l.  The
- * image is the tiles one after another.
+ * A matrix of R rows and C columns (C = 256*G) is cut into tiles of 64 consecutive rows x
+ * one 256-element block: tile (g, b) holds rows 64g .. 64g+63 of block b (rows past R are
+ * zero padding) and sits at byte offset (g*G + b) * tile_bytes.  Lane l of a tile is row
+ * 64g + l.
  *
  * Q4_K-style tile, 9216 bytes (= 64 x 144):
  *   chunk i (i = 0..7) at byte 1024*i: 16 bytes per lane at 1024*i + 16*l.  Byte k (0..15)
@@ -104,7 +104,7 @@ int qg_reads(int fmt, int mode);
  *   d at byte 13312, 2 bytes per lane: binary16 bits.
  */
 
-/* Bytes of the image of an R x C matrix: ceil(R*C/256 / 64) * 64 * (144 or 210).
+/* Bytes of the image of an R x C matrix: ceil(R/64) * (C/256) * 64 * (144 or 210).
  * 0 for a bad format or shape. */
 size_t qg_image_bytes(int fmt, int64_t rows, int64_t cols);
 
@@ -175,12 +175,10 @@ int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const 
                   int32_t *csum_out, int32_t *osum_out, void *stream);
 
 /* Speed-only tuning knobs; they never change output bits.
- *   QG_TUNE_WAVES_PER_CU  resident waves per compute unit the GEMV grid is sized for
- *                         (0 = default)
- *   QG_TUNE_GRID_WGS      exact number of workgroups for the GEMV grid (0 = derived)
- *   QG_TUNE_PIPELINE      1 (default): a single-column GEMV loads each tile's successor while
- *                         the tile is computed; 0: one tile in flight per wave */
-enum { QG_TUNE_WAVES_PER_CU = 1, QG_TUNE_GRID_WGS = 2, QG_TUNE_PIPELINE = 3 };
+ *   QG_TUNE_WAVES_PER_WG  waves per GEMV workgroup, splitting a 64-row group's blocks:
+ *                         4, 8 or 16 (0 = one wave per block, at most 16).  16 applies
+ *                         only to a single column of at most 16 blocks; otherwise 8 is used */
+enum { QG_TUNE_WAVES_PER_WG = 1 };
 int qg_set_tuning(int key, int64_t value);
 
 /* Measurement hook: the next qg_gemv_q / qg_gemm_q call made on this thread launches its

@@ -30,8 +30,7 @@ def say(*a):
 def qg():
     assert torch.cuda.is_available(), "GPU tests need a ROCm device"
     import block_format_gemv_amd as q
-    q.qg_set_tuning(q.TUNE_WAVES_PER_CU, 0)
-    q.qg_set_tuning(q.TUNE_GRID_WGS, 0)
+    q.qg_set_tuning(q.TUNE_WAVES_PER_WG, 0)
     oracle.set_threads(8)
     return q
 
@@ -229,16 +228,12 @@ def test_launch_configuration_does_not_change_bits(qg):
     act, c, m, e, _ = gpu_quant(qg, gen.act_outliers(1, 4096, 8), 0)
     ref = bits(run_gemv(qg, M, act))
     try:
-        for key, val in ((qg.TUNE_GRID_WGS, 1), (qg.TUNE_GRID_WGS, 7), (qg.TUNE_GRID_WGS, 5000),
-                         (qg.TUNE_WAVES_PER_CU, 1), (qg.TUNE_WAVES_PER_CU, 32)):
-            qg.qg_set_tuning(qg.TUNE_GRID_WGS, 0)
-            qg.qg_set_tuning(qg.TUNE_WAVES_PER_CU, 0)
-            qg.qg_set_tuning(key, val)
-            say("tuning", key, val)
-            assert np.array_equal(bits(run_gemv(qg, M, act)), ref), (key, val)
+        for w in (4, 8, 16):
+            qg.qg_set_tuning(qg.TUNE_WAVES_PER_WG, w)
+            say("waves per workgroup", w)
+            assert np.array_equal(bits(run_gemv(qg, M, act)), ref), w
     finally:
-        qg.qg_set_tuning(qg.TUNE_GRID_WGS, 0)
-        qg.qg_set_tuning(qg.TUNE_WAVES_PER_CU, 0)
+        qg.qg_set_tuning(qg.TUNE_WAVES_PER_WG, 0)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         out = torch.empty(1000, dtype=torch.float32, device=DEV)
@@ -251,10 +246,10 @@ def test_launch_configuration_does_not_change_bits(qg):
 def test_binding_refuses_short_buffers(qg):
     M = Mat(qg, gen.q4k_fields(8, 512, 1))
     act, _, _, _, _ = gpu_quant(qg, gen.act_normal(1, 512, 2), 0)
-    # 8 rows x 2 blocks fill one 64-pair tile; 64 rows would need two
+    # 8 rows fill one 64-row group; 65 rows would need two
     with pytest.raises(qg.QGError):
-        qg.qg_gemv_q(M.fmt, 0, 64, 512, M.img, act.codes, act.scales, act.csums,
-                     torch.empty(64, dtype=torch.float32, device=DEV))
+        qg.qg_gemv_q(M.fmt, 0, 65, 512, M.img, act.codes, act.scales, act.csums,
+                     torch.empty(65, dtype=torch.float32, device=DEV))
     with pytest.raises(qg.QGError):
         qg.qg_gemv_q(M.fmt, 0, 8, 512, M.img, act.codes, act.scales, act.csums,
                      torch.empty(4, dtype=torch.float32, device=DEV))

@@ -34,76 +34,73 @@ def test_library_exports_every_declared_function():
 
 # --- independent unpackers (from the layout described in qgemv.h) ---------------------------
 
-def unpack_q4k(img: np.ndarray, rows: int, cols: int) -> dict:
+def _tiles(img: np.ndarray, rows: int, cols: int, tile_bytes: int):
+    """Image -> array [groups, G, tile_bytes]; tile (g, b) holds rows 64g..64g+63 of block b."""
     G = cols // 256
-    npairs = rows * G
-    ntiles = -(-npairs // 64)
-    t = img.reshape(ntiles, 9216)
-    chunks = t[:, :8192].reshape(ntiles, 8, 64, 16)              # [tile, chunk i, lane, byte k]
-    meta = t[:, 8192:].reshape(ntiles, 64, 16)                   # [tile, lane, 16]
-    lo = chunks & 15
-    hi = chunks >> 4
-    sub = np.concatenate([lo, hi], axis=3)                       # element 32i + (k | 16 + k)
-    q = sub.transpose(0, 2, 1, 3).reshape(ntiles * 64, 256)[:npairs]
-    m = meta.reshape(ntiles * 64, 16)[:npairs].astype(np.uint64)
-    d = (m[:, 0] | (m[:, 1] << 8)).astype(np.uint16)
-    dmin = (m[:, 2] | (m[:, 3] << 8)).astype(np.uint16)
-    bits = np.zeros(npairs, dtype=object)
-    for k in range(12):
-        bits = bits + (m[:, 4 + k].astype(object) << (8 * k))
-    sc = np.zeros((npairs, 8), np.uint8)
-    mn = np.zeros((npairs, 8), np.uint8)
-    for j in range(8):
-        field = np.array([(int(v) >> (12 * j)) & 0xFFF for v in bits], np.uint32)
-        sc[:, j] = field & 63
-        mn[:, j] = field >> 6
-    return {"q": q.reshape(rows, cols), "sc": sc.reshape(rows, G * 8), "mn": mn.reshape(rows, G * 8),
-            "d": d.reshape(rows, G), "dmin": dmin.reshape(rows, G)}
+    groups = -(-rows // 64)
+    return img.reshape(groups, G, tile_bytes), G, groups
+
+
+def unpack_q4k(img: np.ndarray, rows: int, cols: int) -> dict:
+    t, G, groups = _tiles(img, rows, cols, 9216)
+    chunks = t[..., :8192].reshape(groups, G, 8, 64, 16)        # [g, b, chunk i, lane, byte k]
+    meta = t[..., 8192:].reshape(groups, G, 64, 16)             # [g, b, lane, 16]
+    sub = np.concatenate([chunks & 15, chunks >> 4], axis=4)    # element 32i + (k | 16 + k)
+    q = sub.transpose(0, 3, 1, 2, 4).reshape(groups * 64, cols)[:rows]
+    m = meta.transpose(0, 2, 1, 3).reshape(groups * 64, G, 16)[:rows].astype(np.uint64)
+    d = (m[..., 0] | (m[..., 1] << 8)).astype(np.uint16)
+    dmin = (m[..., 2] | (m[..., 3] << 8)).astype(np.uint16)
+    sc = np.zeros((rows, G, 8), np.uint8)
+    mn = np.zeros((rows, G, 8), np.uint8)
+    for r in range(rows):
+        for b in range(G):
+            bits = int.from_bytes(bytes(m[r, b, 4:16].astype(np.uint8)), "little")
+            for j in range(8):
+                field = (bits >> (12 * j)) & 0xFFF
+                sc[r, b, j] = field & 63
+                mn[r, b, j] = field >> 6
+    return {"q": q, "sc": sc.reshape(rows, G * 8), "mn": mn.reshape(rows, G * 8), "d": d, "dmin": dmin}
 
 
 def unpack_q6k(img: np.ndarray, rows: int, cols: int) -> dict:
-    G = cols // 256
-    npairs = rows * G
-    ntiles = -(-npairs // 64)
-    t = img.reshape(ntiles, 13440)
-    ql = t[:, :8192].reshape(ntiles, 8, 64, 16)
-    qh = t[:, 8192:12288].reshape(ntiles, 4, 64, 16)
-    sc = t[:, 12288:13312].reshape(ntiles, 64, 16).view(np.int8)
-    d = t[:, 13312:13440].reshape(ntiles, 64, 2).astype(np.uint16)
-    low = np.concatenate([ql & 15, ql >> 4], axis=3)               # [tile, i, lane, 32]
-    low = low.transpose(0, 2, 1, 3).reshape(ntiles, 64, 256)
-    high = np.zeros((ntiles, 64, 256), np.uint8)
+    t, G, groups = _tiles(img, rows, cols, 13440)
+    ql = t[..., :8192].reshape(groups, G, 8, 64, 16)
+    qh = t[..., 8192:12288].reshape(groups, G, 4, 64, 16)
+    sc = t[..., 12288:13312].reshape(groups, G, 64, 16).view(np.int8)
+    d = t[..., 13312:13440].reshape(groups, G, 64, 2).astype(np.uint16)
+    low = np.concatenate([ql & 15, ql >> 4], axis=4)             # [g, b, i, lane, 32]
+    low = low.transpose(0, 1, 3, 2, 4).reshape(groups, G, 64, 256)
+    high = np.zeros((groups, G, 64, 256), np.uint8)
     for h in range(4):
         for f in range(4):
-            high[:, :, 64 * h + 16 * f:64 * h + 16 * f + 16] = (qh[:, h] >> (2 * f)) & 3
-    q = (low | (high << 4)).reshape(ntiles * 64, 256)[:npairs]
-    dd = (d[..., 0] | (d[..., 1] << 8)).reshape(-1)[:npairs]
-    return {"q": q.reshape(rows, cols), "sc": sc.reshape(-1, 16)[:npairs].reshape(rows, G * 16),
-            "d": dd.reshape(rows, G)}
+            high[..., 64 * h + 16 * f:64 * h + 16 * f + 16] = (qh[:, :, h] >> (2 * f)) & 3
+    q = (low | (high << 4)).transpose(0, 2, 1, 3).reshape(groups * 64, cols)[:rows]
+    dd = (d[..., 0] | (d[..., 1] << 8)).transpose(0, 2, 1).reshape(groups * 64, G)[:rows]
+    scs = sc.transpose(0, 2, 1, 3).reshape(groups * 64, G * 16)[:rows]
+    return {"q": q, "sc": scs, "d": dd}
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 256), (5, 768), (64, 1024), (3, 14336 // 7), (37, 4096)])
+@pytest.mark.parametrize("rows,cols", [(1, 256), (5, 768), (64, 1024), (3, 2048), (37, 4096), (130, 1280)])
 def test_q4k_pack_roundtrip(rows, cols):
     f = gen.q4k_fields(rows, cols, rows * 7 + cols)
     img = qg.pack(f)
-    assert img.nbytes == qg.qg_image_bytes(qg.Q4K, rows, cols) == -(-rows * cols // 256 // 64) * 9216
+    assert img.nbytes == qg.qg_image_bytes(qg.Q4K, rows, cols) == -(-rows // 64) * (cols // 256) * 9216
     u = unpack_q4k(img, rows, cols)
     for k in ("q", "sc", "mn", "d", "dmin"):
         assert np.array_equal(u[k], f[k]), k
-    # zero padding past the last pair
-    npairs = rows * cols // 256
-    if npairs % 64:
-        last = img.reshape(-1, 9216)[-1]
-        lanes = np.arange(64) >= npairs % 64
-        assert not last[:8192].reshape(8, 64, 16)[:, lanes].any()
-        assert not last[8192:].reshape(64, 16)[lanes].any()
+    # zero padding past the last row, in every tile of the last row group
+    if rows % 64:
+        t, G, groups = _tiles(img, rows, cols, 9216)
+        lanes = np.arange(64) >= rows % 64
+        assert not t[-1, :, :8192].reshape(G, 8, 64, 16)[:, :, lanes].any()
+        assert not t[-1, :, 8192:].reshape(G, 64, 16)[:, lanes].any()
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 256), (5, 768), (64, 1024), (9, 4096)])
 def test_q6k_pack_roundtrip(rows, cols):
     f = gen.q6k_fields(rows, cols, rows * 11 + cols)
     img = qg.pack(f)
-    assert img.nbytes == qg.qg_image_bytes(qg.Q6K, rows, cols) == -(-rows * cols // 256 // 64) * 13440
+    assert img.nbytes == qg.qg_image_bytes(qg.Q6K, rows, cols) == -(-rows // 64) * (cols // 256) * 13440
     u = unpack_q6k(img, rows, cols)
     for k in ("q", "sc", "d"):
         assert np.array_equal(u[k], f[k]), k
@@ -175,6 +172,7 @@ def test_validation_refuses_before_any_gpu_work():
     assert L.qg_quantize_act(qg.Q4K, qg.SUB32, 1, 256, odd, fake, fake, fake, None, None) == qg.E_INVALID
     assert L.qg_block_sums(qg.Q6K, 4, 512, fake, fake, None, None, None) == qg.E_INVALID
     assert L.qg_set_tuning(77, 1) == qg.E_INVALID
+    assert L.qg_set_tuning(qg.TUNE_WAVES_PER_WG, 3) == qg.E_INVALID
     # empty work is not an error and launches nothing
     assert L.qg_gemv_q(qg.Q4K, qg.PERBLOCK, 0, 256, None, None, None, None, None, None) == qg.OK
     assert L.qg_quantize_act(qg.Q4K, qg.PERBLOCK, 0, 256, None, None, None, None, None, None) == qg.OK
