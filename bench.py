@@ -36,6 +36,37 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+# HBM traffic of the GEMV kernel per launch, from two rocprofv3 --pmc passes (FETCH_SIZE,
+# then WRITE_SIZE, medians in KiB per dispatch), each scaled by what the same counter reads
+# for a plain device copy of 256 MiB (FETCH_SIZE 131083.5 KiB, WRITE_SIZE 262144 KiB).
+# A figure is reported only while the kernel sources still hash to the value it was taken
+# on; the commands and readings are kept under profiles/.
+COPY_BYTES = 268435456
+FETCH_FACTOR = COPY_BYTES / (131083.5 * 1024)
+WRITE_FACTOR = COPY_BYTES / (262144.0 * 1024)
+KERNEL_SOURCES = ("block_format_gemv_amd/csrc/gemv.hip", "block_format_gemv_amd/csrc/qg_device.hpp",
+                  "block_format_gemv_amd/csrc/qg_internal.hpp")
+MEASURED_TRAFFIC = {
+    "q4k_ffn_up_14336x4096": {"kernel_sha": "6a75fd51162b73f0", "fetch_kib": 16198.0, "write_kib": 56.0},
+}
+
+
+def kernel_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for src in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    t = MEASURED_TRAFFIC.get(workload)
+    if not t or t["kernel_sha"] != kernel_sha():
+        return None
+    return round(t["fetch_kib"] * 1024 * FETCH_FACTOR + t["write_kib"] * 1024 * WRITE_FACTOR)
 METRIC = "quantized GEMV weight-stream HBM GB/s (% of peak) and rows/s at 1 GPU"
 
 WORKLOADS = {
@@ -312,7 +343,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload),
             "kernel": "gemv_kernel (qg_gemm_q)",
             "algorithmic_bytes_per_launch": algo_bytes,
         },
