@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "libqgemv.so")
 Q4K, Q6K = 1, 2
 PERBLOCK, SUB32 = 0, 1
 OK, E_INVALID, E_SHAPE, E_UNSUPPORTED, E_UNREADABLE, E_NONFINITE, E_RUNTIME = range(7)
-TUNE_WAVES_PER_WG = 1
+TUNE_WAVES_PER_WG, TUNE_MFMA_MIN_COLS, TUNE_MFMA_COL_TILES = 1, 2, 3
 BLOCK = 256
 MAX_COLS = 32768
 

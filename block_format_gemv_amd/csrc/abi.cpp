@@ -18,7 +18,7 @@ namespace qg {
 namespace {
 thread_local char g_reason[512] = "";
 thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
-Tuning g_tuning = {0};
+Tuning g_tuning = {0, 0, 0};
 
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices];
@@ -119,6 +119,14 @@ int qg_set_tuning(int key, int64_t value)
             return fail(QG_E_INVALID, "qg_set_tuning: waves per workgroup must be 0, 4, 8 or 16");
         g_tuning.waves_per_wg = (int)value;
         return QG_OK;
+    case QG_TUNE_MFMA_MIN_COLS:
+        g_tuning.mfma_min_cols = value > 65536 ? 65536 : (int)value;
+        return QG_OK;
+    case QG_TUNE_MFMA_COL_TILES:
+        if (value != 0 && value != 1 && value != 2 && value != 4)
+            return fail(QG_E_INVALID, "qg_set_tuning: column tiles must be 0, 1, 2 or 4");
+        g_tuning.mfma_col_tiles = (int)value;
+        return QG_OK;
     default:
         return fail(QG_E_INVALID, "qg_set_tuning: unknown key %d", key);
     }
@@ -162,6 +170,9 @@ static int gemm_common(const char *who, int fmt, int mode, int64_t rows, int64_t
     if ((st = check_ptr(who, "image", image, 16))) return st;
     if ((st = check_act(who, codes, scales, csums))) return st;
     if ((st = check_ptr(who, "out", out, 4))) return st;
+    const int min_cols = g_tuning.mfma_min_cols > 0 ? g_tuning.mfma_min_cols : 8;
+    if (fmt == QG_Q4K && mode == QG_PERBLOCK && n >= min_cols)
+        return launch_gemm_mfma(rows, cols, n, image, codes, scales, out, static_cast<hipStream_t>(stream));
     return launch_gemv(fmt, mode, rows, cols, n, image, codes, scales, csums, out, static_cast<hipStream_t>(stream));
 }
 

@@ -195,6 +195,16 @@ __device__ __forceinline__ float piece_q4k_perblock(int C, int O, uint32_t d_dmi
     return r32_sum2(a, b);
 }
 
+// PerBlock, Q4_K-style, when the two block-scale exponents differ by at most 8.  With
+// Dd = sig_d*2^ex_d and Dm = sig_m*2^ex_m, X = C*Dd - O*Dm has at most 45 significant bits,
+// so one fma forms it exactly; times S = m*2^e (8 significant bits) it stays exact in f64;
+// the conversion is the one rounding.  Gives the same bits as piece_q4k_perblock.
+__device__ __forceinline__ float piece_q4k_perblock_near(int C, int O, double Dd, double Dm, double S)
+{
+    const double X = __builtin_fma((double)C, Dd, -((double)O * Dm));
+    return r32_exact_double(X * S);
+}
+
 // PerBlock, Q6_K-style: one term R32(m*2^e * d*C); |C| < 2^27 so the product is < 2^46.
 __device__ __forceinline__ float piece_q6k_perblock(int C, uint32_t dbits, int m, int e)
 {

@@ -17,7 +17,9 @@ constexpr int kTileBytesQ6K = 64 * 210;   // 13440
 int fail(int status, const char *fmt, ...);
 
 struct Tuning {
-    int waves_per_wg;   // waves per GEMV workgroup (2, 4, 8, 16); 0 = derived from the block count
+    int waves_per_wg;     // waves per GEMV workgroup (4, 8, 16); 0 = derived from the block count
+    int mfma_min_cols;    // columns from which a Q4_K PerBlock GEMM uses the matrix cores; 0 = 16
+    int mfma_col_tiles;   // 16-column tiles per matrix-core workgroup (1, 2, 4); 0 = derived
 };
 const Tuning &tuning();
 
@@ -34,6 +36,9 @@ int launch_quantize(int mode, int block, int64_t n, int64_t cols, const float *x
 int launch_gemv(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, const void *image,
                 const int8_t *codes, const qg_act_scale *scales, const int32_t *csums, float *out,
                 hipStream_t s);
+
+int launch_gemm_mfma(int64_t rows, int64_t cols, int64_t ncol, const void *image, const int8_t *codes,
+                     const qg_act_scale *scales, float *out, hipStream_t s);
 
 int launch_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
                       int32_t *csum_out, int32_t *osum_out, hipStream_t s);

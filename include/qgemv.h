@@ -177,8 +177,12 @@ int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const 
 /* Speed-only tuning knobs; they never change output bits.
  *   QG_TUNE_WAVES_PER_WG  waves per GEMV workgroup, splitting a 64-row group's blocks:
  *                         4, 8 or 16 (0 = one wave per block, at most 16).  16 applies
- *                         only to a single column of at most 16 blocks; otherwise 8 is used */
-enum { QG_TUNE_WAVES_PER_WG = 1 };
+ *                         only to a single column of at most 16 blocks; otherwise 8 is used
+ *   QG_TUNE_MFMA_MIN_COLS number of columns from which qg_gemm_q on a Q4_K PerBlock matrix
+ *                         runs on the int8 matrix cores, columns padded to 16 (0 = 8;
+ *                         above 65535 = never)
+ *   QG_TUNE_MFMA_COL_TILES 16-column tiles per matrix-core workgroup: 1, 2 or 4 (0 = derived) */
+enum { QG_TUNE_WAVES_PER_WG = 1, QG_TUNE_MFMA_MIN_COLS = 2, QG_TUNE_MFMA_COL_TILES = 3 };
 int qg_set_tuning(int key, int64_t value);
 
 /* Measurement hook: the next qg_gemv_q / qg_gemm_q call made on this thread launches its

@@ -31,6 +31,8 @@ def qg():
     assert torch.cuda.is_available(), "GPU tests need a ROCm device"
     import block_format_gemv_amd as q
     q.qg_set_tuning(q.TUNE_WAVES_PER_WG, 0)
+    q.qg_set_tuning(q.TUNE_MFMA_MIN_COLS, 0)
+    q.qg_set_tuning(q.TUNE_MFMA_COL_TILES, 0)
     oracle.set_threads(8)
     return q
 
@@ -347,3 +349,31 @@ def test_batched_columns(qg, llama, n):
             one.scales.copy_(act.scales[k:k + 1])
             one.csums.copy_(act.csums[k:k + 1])
             assert np.array_equal(bits(run_gemv(qg, M, one)), bits(out[k]))
+
+
+# --- batched columns on the int8 matrix cores -----------------------------------------------
+
+@pytest.mark.parametrize("ncol", [3, 8, 16, 17, 33, 64, 100])
+def test_matrix_core_gemm_matches_oracle(qg, ncol):
+    """Q4_K PerBlock with >= 16 columns runs on v_mfma_i32_16x16x64_i8; every (row, column)
+    must carry the oracle's bits, across column-tile settings, ragged rows and columns, and
+    block scales that take both the near-exponent and the general combine."""
+    f = _adversarial_fields("q4k", 130, 1280, 900 + ncol)
+    M = Mat(qg, f)
+    xs = gen.act_outliers(ncol, 1280, 901 + ncol)
+    xs[min(3, ncol - 1), 256:512] = 0.0                         # an all-zero activation block
+    act, c, m, e, _ = gpu_quant(qg, xs, 0)
+    want = oracle.gemm(f, c, m, e, 0).reshape(ncol, 130)
+    try:
+        qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 1)                # matrix cores for any column count
+        for ct in (1, 2, 4):
+            qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, ct)
+            say("matrix-core gemm", ncol, "column tiles", ct)
+            out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+            assert first_mismatch(out, want) is None, (ncol, ct, first_mismatch(out, want))
+        qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 65536)          # force the vector-ALU kernel
+        out_valu = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+        assert first_mismatch(out_valu, want) is None
+    finally:
+        qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 0)
+        qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 0)

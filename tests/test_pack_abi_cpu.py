@@ -173,6 +173,7 @@ def test_validation_refuses_before_any_gpu_work():
     assert L.qg_block_sums(qg.Q6K, 4, 512, fake, fake, None, None, None) == qg.E_INVALID
     assert L.qg_set_tuning(77, 1) == qg.E_INVALID
     assert L.qg_set_tuning(qg.TUNE_WAVES_PER_WG, 3) == qg.E_INVALID
+    assert L.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 3) == qg.E_INVALID
     # empty work is not an error and launches nothing
     assert L.qg_gemv_q(qg.Q4K, qg.PERBLOCK, 0, 256, None, None, None, None, None, None) == qg.OK
     assert L.qg_quantize_act(qg.Q4K, qg.PERBLOCK, 0, 256, None, None, None, None, None, None) == qg.OK
