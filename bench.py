@@ -1,21 +1,23 @@
 """Benchmark of the exact block-quantized decode GEMV on one MI355X.
 
 A step is one pass of the whole hot path over one synthetic activation row: quantize the
-f32 row (qg_quantize_act) and run the GEMV over the packed matrix (qg_gemv_q), both on the
-current stream, inputs resident in HBM.  The default workload is the Llama-8B-shaped FFN
-up-projection, 14336 x 4096 Q4_K-style, PerBlock scaling, fresh activations every step,
-and the weights are read cold: each step uses the next of C copies of the image
-(C * 33 MB >= 512 MB, twice the 256 MB Infinity Cache).
+f32 row and run the GEMV over the packed matrix.  At one column that is one launch of
+qg_quantize_gemv (--two-launch: qg_quantize_act then qg_gemv_q); batched workloads run
+qg_quantize_act then qg_gemm_q.  Everything runs on one stream with inputs resident in HBM.
+The default workload is the Llama-8B-shaped FFN up-projection, 14336 x 4096 Q4_K-style,
+PerBlock scaling, fresh activations every step, and the weights are read cold: each step
+uses the next of C copies of the image (C * 33 MB >= 512 MB, twice the 256 MB Infinity
+Cache).
 
 Timing:
   * ms_per_step: the K timed steps are captured in HIP graphs (one graph node per kernel)
     and replayed between two events after a synchronize; whole-job weight GB/s = K * image
     bytes / elapsed.
-  * roofline.achieved: algorithmic bytes per GEMV launch over the GEMV kernel's duration,
-    from HIP events around replays of a graph of GEMV-only launches over the same
-    rotated-cold copies (on the stream they run on).  The median of single eager launches
-    timed by events the launch itself records (hipExtLaunchKernelGGL, qg_time_next_launch)
-    is reported beside it.
+  * roofline.achieved: algorithmic bytes per launch of the step's dominant kernel (the
+    fused kernel, or the GEMV/GEMM kernel) over that kernel's duration, from HIP events
+    around replays of a graph of kernel-only launches over the same rotated-cold copies (on
+    the stream they run on).  The median of single eager launches timed by events the
+    launch itself records (hipExtLaunchKernelGGL, qg_time_next_launch) is reported beside it.
   * cpu_baseline: the CPU oracle on the same workload, all rows, fresh activations, for
     about --cpu-seconds of host time, on the host's cores (threads stated).
 
@@ -93,6 +95,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--kernel-launches", type=int, default=1600)
+    p.add_argument("--two-launch", action="store_true",
+                   help="time the step as qg_quantize_act + qg_gemv_q instead of qg_quantize_gemv")
     p.add_argument("--copy-probe", type=float, default=0,
                    help="only run 20 device-to-device copies of this many bytes (counter calibration) and exit")
     return p.parse_args()
@@ -221,13 +225,34 @@ def main():
     outs = [torch.empty((ncol, rows), dtype=torch.float32, device=dev) for _ in range(slots)]
     act_bytes = ncol * (cols + 4 * qg._nsc(mode, cols) + 4 * (cols // 16))
     out_bytes = 4 * ncol * rows
-    algo_bytes = image_bytes + act_bytes + out_bytes
+    fused = ncol == 1 and not args.two_launch
 
-    def step(i, stream=None):
+    def quantize(i, stream=None):
         a = acts[i % slots]
         qg.qg_quantize_act(fmt, mode, ncol, cols, x_dev[i % n_act], a.codes, a.scales, a.csums, None, stream)
+
+    def multiply(i, stream=None):
+        a = acts[i % slots]
         qg.qg_gemm_q(fmt, mode, rows, cols, ncol, images[i % copies], a.codes, a.scales, a.csums,
                      outs[i % slots], stream)
+
+    def fused_call(i, stream=None):
+        a = acts[i % slots]
+        qg.qg_quantize_gemv(fmt, mode, rows, cols, images[i % copies], x_dev[i % n_act], a.codes, a.scales,
+                            a.csums, None, outs[i % slots], stream)
+
+    def two_launch(i, stream=None):
+        quantize(i, stream)
+        multiply(i, stream)
+
+    step = fused_call if fused else two_launch
+    # the step's dominant kernel: the fused kernel (reads x, writes the quantized row once)
+    # or the GEMV/GEMM kernel (reads the quantized row)
+    kernel_fn = fused_call if fused else multiply
+    if fused:
+        algo_bytes = image_bytes + 4 * cols + act_bytes + out_bytes
+    else:
+        algo_bytes = image_bytes + act_bytes + out_bytes
 
     # eager first pass, then a bitwise check of step 0 against the oracle on sampled rows
     torch.cuda.synchronize()
@@ -235,72 +260,66 @@ def main():
     torch.cuda.synchronize()
     first = outs[0].cpu().numpy().copy()
 
-    # HIP graphs of `gsteps` steps each: the timed K steps are replays, exactly K steps
+    # HIP graphs of `gsteps` calls each, replayed between two events on the stream they run on
     gsteps = slots
     s = torch.cuda.Stream()
-    graphs = {}
 
-    def graph_of(nsteps, offset):
+    def graph_of(fn, nsteps, offset=0):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
             for i in range(nsteps):
-                step(offset + i)
+                fn(offset + i)
         return g
 
-    full = graph_of(gsteps, 0)
+    def replay_ms(graphs_in_order):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            torch.cuda.synchronize()
+            t0.record(s)
+            for g in graphs_in_order:
+                g.replay()
+            t1.record(s)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
+    def per_call_us(fn, launches):
+        g = graph_of(fn, gsteps)
+        for _ in range(4):
+            g.replay()
+        reps = max(1, launches // gsteps)
+        return replay_ms([g] * reps) * 1e3 / (reps * gsteps), reps
+
+    # the timed K steps: exactly K steps of graph replays
+    full = graph_of(step, gsteps)
     rest = args.steps % gsteps
-    tail = graph_of(rest, 0) if rest else None
+    tail = graph_of(step, rest) if rest else None
     torch.cuda.synchronize()
     for _ in range(max(1, -(-args.warmup // gsteps))):
         full.replay()
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(s):
-        torch.cuda.synchronize()
-        t_start.record(s)
-        for _ in range(args.steps // gsteps):
-            full.replay()
-        if tail is not None:
-            tail.replay()
-        t_end.record(s)
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
+    ms_total = replay_ms([full] * (args.steps // gsteps) + ([tail] if tail is not None else []))
     ms_per_step = ms_total / args.steps
 
-    # The GEMV kernel's duration as the workload runs it: a HIP graph of `gsteps` GEMV-only
-    # launches over the same rotated cold copies (activations already quantized), replayed
-    # between two events on the stream it runs on; per-launch time = elapsed / launches.
-    def gemv_only(i):
-        a = acts[i % slots]
-        qg.qg_gemm_q(fmt, mode, rows, cols, ncol, images[i % copies], a.codes, a.scales, a.csums, outs[i % slots])
-
-    kg = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(kg, stream=s):
-        for i in range(gsteps):
-            gemv_only(i)
-    reps = max(1, args.kernel_launches // gsteps)
-    for _ in range(4):
-        kg.replay()
-    torch.cuda.synchronize()
-    k0 = torch.cuda.Event(enable_timing=True)
-    k1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(s):
-        k0.record(s)
-        for _ in range(reps):
-            kg.replay()
-        k1.record(s)
-    torch.cuda.synchronize()
-    k_us = k0.elapsed_time(k1) * 1e3 / (reps * gsteps)
+    # the dominant kernel's duration as the workload runs it (graph of kernel-only launches
+    # over the same rotated cold copies)
+    k_us, reps = per_call_us(kernel_fn, args.kernel_launches)
     achieved = algo_bytes / (k_us * 1e-6) / 1e9
+    extra = {}
+    if fused:
+        # the same step as two launches, and the GEMV kernel alone, for comparison
+        extra["two_launch_us_per_step"] = round(per_call_us(two_launch, args.kernel_launches // 4)[0], 3)
+        gemv_us = per_call_us(multiply, args.kernel_launches // 4)[0]
+        extra["gemv_kernel_us"] = round(gemv_us, 3)
+        extra["gemv_kernel_frac_of_peak"] = round((image_bytes + act_bytes + out_bytes) / (gemv_us * 1e-6) / 1e9
+                                                  / HBM_PEAK_GBS, 4)
 
     # secondary: single eager launches, each bracketed by events the launch itself records
     evs = [(hip.event(), hip.event()) for _ in range(64)]
     torch.cuda.synchronize()
     for i, (e0, e1) in enumerate(evs):
-        a = acts[i % slots]
         qg.qg_time_next_launch(e0, e1)
-        qg.qg_gemm_q(fmt, mode, rows, cols, ncol, images[i % copies], a.codes, a.scales, a.csums, outs[i % slots])
+        kernel_fn(i)
     torch.cuda.synchronize()
     k_ms = np.array([hip.elapsed_ms(e0, e1) for e0, e1 in evs])[8:]
     for e0, e1 in evs:
@@ -330,12 +349,13 @@ def main():
             "columns": ncol,
             "weights": "cold, rotating over %d copies (%.0f MB)" % (copies, copies * image_bytes / 1e6)
                        if copies > 1 else "warm, one copy (cache-resident)",
-            "step": "quantize_act + gemv_q, HIP graph replay",
+            "step": ("qg_quantize_gemv (one launch)" if fused else "qg_quantize_act + qg_gemm_q")
+                    + ", HIP graph replay",
         },
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "rows_per_s": round(rows * ncol / (ms_per_step * 1e-3), 1),
         "kernel_us": round(k_us, 3),
-        "kernel_timing": f"HIP events around {reps} replays of a graph of {gsteps} GEMV launches",
+        "kernel_timing": f"HIP events around {reps} replays of a graph of {gsteps} launches",
         "kernel_us_eager_launch_events_median": round(float(np.median(k_ms)) * 1e3, 3),
         "roofline": {
             "bound": "hbm",
@@ -344,10 +364,12 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(args.workload),
-            "kernel": "gemv_kernel (qg_gemm_q)",
+            "kernel": "gemv_fused_kernel (qg_quantize_gemv)" if fused else
+                      ("gemm_mfma_q4k" if ncol >= 8 and fmt_s == "q4k" and mode == 0 else "gemv_kernel") + " (qg_gemm_q)",
             "algorithmic_bytes_per_launch": algo_bytes,
         },
     }
+    record.update(extra)
     if not args.no_cpu:
         cb, cpu_outs = cpu_baseline(fields, xs, mode, args.cpu_seconds, image_bytes)
         record["cpu_baseline"] = cb

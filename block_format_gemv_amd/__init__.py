@@ -6,7 +6,7 @@ host pointers, and the stream defaults to torch's current stream.  Every step of
 runs in the library's HIP kernels; there is no CPU fallback.  A nonzero status raises
 QGError with the library's reason.
 
-Convenience wrappers (pack, quantize_act, gemv, gemm) allocate outputs with torch and
+Convenience wrappers (pack, quantize_act, gemv, quantize_gemv, gemm) allocate outputs with torch and
 call the qg_* functions.
 """
 from __future__ import annotations
@@ -27,7 +27,7 @@ BLOCK = 256
 MAX_COLS = 32768
 
 EXPORTS = ("qg_reads", "qg_image_bytes", "qg_pack_q4k", "qg_pack_q6k", "qg_quantize_act", "qg_gemv_q",
-           "qg_gemm_q", "qg_block_sums", "qg_set_tuning", "qg_time_next_launch", "qg_last_error", "qg_version")
+           "qg_gemm_q", "qg_quantize_gemv", "qg_block_sums", "qg_set_tuning", "qg_time_next_launch", "qg_last_error", "qg_version")
 
 
 class QGError(RuntimeError):
@@ -50,6 +50,7 @@ def _load():
     L.qg_quantize_act.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp]
     L.qg_gemv_q.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp]
     L.qg_gemm_q.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.qg_quantize_gemv.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     L.qg_block_sums.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
     L.qg_set_tuning.argtypes = [i32, i64]
     L.qg_time_next_launch.argtypes = [vp, vp]
@@ -160,6 +161,18 @@ def qg_gemm_q(fmt, mode, rows, cols, n, image, codes, scales, csums, out, stream
                           _dptr(out), _stream(stream)))
 
 
+def qg_quantize_gemv(fmt, mode, rows, cols, image, x, codes, scales, csums, err_flag, out, stream=None) -> None:
+    if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32) and fmt in (Q4K, Q6K):
+        _need(x, 4 * cols, "x")
+        _check_act(mode, 1, cols, codes, scales, csums)
+        _need(err_flag, 4, "err_flag")
+        if rows > 0:
+            _need(image, qg_image_bytes(fmt, rows, cols), "image")
+            _need(out, 4 * rows, "out")
+    _check(_lib.qg_quantize_gemv(fmt, mode, rows, cols, _dptr(image), _dptr(x), _dptr(codes), _dptr(scales),
+                                 _dptr(csums), _dptr(err_flag), _dptr(out), _stream(stream)))
+
+
 def qg_block_sums(fmt, rows, cols, image, codes, csum_out, osum_out=None, stream=None) -> None:
     if cols > 0 and cols % BLOCK == 0 and fmt in (Q4K, Q6K) and rows > 0:
         per = 32 if fmt == Q4K else 16
@@ -254,6 +267,18 @@ def gemv(fmt: int, rows: int, cols: int, image, act: Act, out=None, stream=None)
         out = torch.empty(rows, dtype=torch.float32, device=act.codes.device)
     qg_gemv_q(fmt, act.mode, rows, cols, image, act.codes, act.scales, act.csums, out, stream)
     return out
+
+
+def quantize_gemv(fmt: int, rows: int, cols: int, image, x, mode: int, act: Act | None = None, out=None,
+                  err_flag=None, stream=None):
+    """One f32 activation row x [C] on the GPU: quantize and multiply in one call.
+    Returns (out [rows], the Act holding the quantized row)."""
+    import torch
+    a = act if act is not None else alloc_act(1, cols, mode, x.device)
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=x.device)
+    qg_quantize_gemv(fmt, mode, rows, cols, image, x, a.codes, a.scales, a.csums, err_flag, out, stream)
+    return out, a
 
 
 def gemm(fmt: int, rows: int, cols: int, image, act: Act, out=None, stream=None):

@@ -188,6 +188,30 @@ int qg_gemm_q(int fmt, int mode, int64_t rows, int64_t cols, int64_t n, const vo
     return gemm_common("qg_gemm_q", fmt, mode, rows, cols, n, image, codes, scales, csums, out, stream);
 }
 
+int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const float *x,
+                     int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
+                     void *stream)
+{
+    const char *who = "qg_quantize_gemv";
+    int st;
+    if ((st = check_fmt_mode(who, fmt, mode))) return st;
+    if ((st = check_cols(who, cols))) return st;
+    if (rows < 0 || rows > 0x7fffffff) return fail(QG_E_SHAPE, "%s: rows %lld out of range", who, (long long)rows);
+    if ((st = check_ptr(who, "x", x, 16))) return st;
+    if ((st = check_act(who, codes, scales, csums))) return st;
+    if (err_flag && !aligned(err_flag, 4)) return fail(QG_E_INVALID, "%s: err_flag is not 4-byte aligned", who);
+    if (rows > 0) {
+        if ((st = check_ptr(who, "image", image, 16))) return st;
+        if ((st = check_ptr(who, "out", out, 4))) return st;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (rows > 0 && cols / QG_BLOCK <= kFusedMaxBlocks)
+        return launch_gemv_fused(fmt, mode, rows, cols, image, x, codes, scales, csums, err_flag, out, s);
+    // no rows to multiply, or a row too wide for one launch: quantize, then the GEMV
+    if ((st = launch_quantize(mode, QG_BLOCK, 1, cols, x, codes, scales, csums, err_flag, s))) return st;
+    return launch_gemv(fmt, mode, rows, cols, 1, image, codes, scales, csums, out, s);
+}
+
 int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
                   int32_t *csum_out, int32_t *osum_out, void *stream)
 {

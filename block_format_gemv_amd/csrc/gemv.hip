@@ -36,7 +36,11 @@ struct ActGlobal {
     const int8_t *codes;
     const int32_t *csums;
     const qg_act_scale *sc;
-    __device__ __forceinline__ const int8_t *block_codes(int b) const { return codes + (size_t)b * 256; }
+    // codes 16i .. 16i+15 of block b
+    __device__ __forceinline__ uint4 codes16(int b, int i) const
+    {
+        return *reinterpret_cast<const uint4 *>(codes + (size_t)b * 256 + 16 * i);
+    }
     __device__ __forceinline__ int sum32(int b, int j) const { return csums[b * 16 + 2 * j] + csums[b * 16 + 2 * j + 1]; }
     __device__ __forceinline__ int sum16(int b, int k) const { return csums[b * 16 + k]; }
     __device__ __forceinline__ qg_act_scale scale(int b, int j, int per_block) const { return sc[b * per_block + j]; }
@@ -59,7 +63,10 @@ struct ActLds {
     using R = ActRec<FMT, MODE>;
     const unsigned char *col;   // record of (this column, block 0)
     __device__ __forceinline__ const unsigned char *rec(int b) const { return col + (size_t)b * R::kStride; }
-    __device__ __forceinline__ const int8_t *block_codes(int b) const { return reinterpret_cast<const int8_t *>(rec(b)); }
+    __device__ __forceinline__ uint4 codes16(int b, int i) const
+    {
+        return *reinterpret_cast<const uint4 *>(rec(b) + 16 * i);
+    }
     __device__ __forceinline__ int sum32(int b, int j) const
     {
         return reinterpret_cast<const int32_t *>(rec(b) + R::kSumOff)[j];
@@ -72,6 +79,53 @@ struct ActLds {
     {
         return reinterpret_cast<const qg_act_scale *>(rec(b) + R::kScOff)[j];
     }
+};
+
+// One block of one activation row quantized by the wave itself, four codes per lane (lane
+// l holds codes 4l..4l+3).  Every value the dot needs is read out of its lane with
+// v_readlane, so it reaches the dot as a scalar (SGPR) operand like ActGlobal's.
+struct ActWave {
+    uint32_t packed;   // lane l: codes 4l..4l+3
+    int s16;           // lane l: sum of the 16 codes of its quad
+    int s32;           // lane l: sum of the 32 codes of its octet
+    int m, e;          // lane l: the scale of its activation block
+    __device__ __forceinline__ uint4 codes16(int, int i) const
+    {
+        return make_uint4((uint32_t)__builtin_amdgcn_readlane((int)packed, 4 * i),
+                          (uint32_t)__builtin_amdgcn_readlane((int)packed, 4 * i + 1),
+                          (uint32_t)__builtin_amdgcn_readlane((int)packed, 4 * i + 2),
+                          (uint32_t)__builtin_amdgcn_readlane((int)packed, 4 * i + 3));
+    }
+    __device__ __forceinline__ int sum32(int, int j) const { return __builtin_amdgcn_readlane(s32, 8 * j); }
+    __device__ __forceinline__ int sum16(int, int k) const { return __builtin_amdgcn_readlane(s16, 4 * k); }
+    __device__ __forceinline__ qg_act_scale scale(int, int j, int per_block) const
+    {
+        const int l = per_block == 1 ? 0 : 8 * j;
+        qg_act_scale s;
+        s.e = (int16_t)__builtin_amdgcn_readlane(e, l);
+        s.m = (uint8_t)__builtin_amdgcn_readlane(m, l);
+        s.pad = 0;
+        return s;
+    }
+};
+
+// The same with the block's 256 codes already read out into 64 scalar registers (done
+// before the weight tile arrives, so the readouts stay off the tile's critical path).
+struct ActWaveCodes {
+    uint32_t c[64];
+    ActWave w;
+    __device__ __forceinline__ explicit ActWaveCodes(const ActWave &a) : w(a)
+    {
+#pragma unroll
+        for (int i = 0; i < 64; i++) c[i] = (uint32_t)__builtin_amdgcn_readlane((int)a.packed, i);
+    }
+    __device__ __forceinline__ uint4 codes16(int, int i) const
+    {
+        return make_uint4(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
+    }
+    __device__ __forceinline__ int sum32(int b, int j) const { return w.sum32(b, j); }
+    __device__ __forceinline__ int sum16(int b, int k) const { return w.sum16(b, k); }
+    __device__ __forceinline__ qg_act_scale scale(int b, int j, int per_block) const { return w.scale(b, j, per_block); }
 };
 
 // ---------------------------------------------------------------------------------------
@@ -92,10 +146,8 @@ __device__ __forceinline__ uint32_t q4k_field(uint32_t y, uint32_t z, uint32_t w
 
 // Integer dot of one 32-element Q4_K sub-block (16 code bytes, nibble-split) with 32
 // activation codes: low nibbles meet elements 0..15, high nibbles elements 16..31.
-__device__ __forceinline__ int q4k_sub_dot(uint4 w, const int8_t *a)
+__device__ __forceinline__ int q4k_sub_dot(uint4 w, uint4 a0, uint4 a1)
 {
-    const uint4 a0 = *reinterpret_cast<const uint4 *>(a);
-    const uint4 a1 = *reinterpret_cast<const uint4 *>(a + 16);
     int P = 0;
     P = sdot4(w.x & 0x0F0F0F0Fu, a0.x, P);
     P = sdot4((w.x >> 4) & 0x0F0F0F0Fu, a1.x, P);
@@ -111,10 +163,8 @@ __device__ __forceinline__ int q4k_sub_dot(uint4 w, const int8_t *a)
 // Integer dots of two 16-element Q6_K sub-blocks (2i, 2i+1): 4-bit low parts from ql, 2-bit
 // high parts from the qh bit pairs 4s..4s+1 (sub-block 2i) and 4s+2..4s+3 (sub-block 2i+1).
 template <int S>
-__device__ __forceinline__ void q6k_sub_dots(uint4 L, uint4 H, const int8_t *a, int &P0, int &P1)
+__device__ __forceinline__ void q6k_sub_dots(uint4 L, uint4 H, uint4 a0, uint4 a1, int &P0, int &P1)
 {
-    const uint4 a0 = *reinterpret_cast<const uint4 *>(a);
-    const uint4 a1 = *reinterpret_cast<const uint4 *>(a + 16);
     const uint32_t l[4] = {L.x, L.y, L.z, L.w};
     const uint32_t h[4] = {H.x, H.y, H.z, H.w};
     const uint32_t x0[4] = {a0.x, a0.y, a0.z, a0.w};
@@ -132,7 +182,15 @@ __device__ __forceinline__ void q6k_sub_dots(uint4 L, uint4 H, const int8_t *a, 
 }
 
 // ---------------------------------------------------------------------------------------
-// One lane's share of a tile, held in registers between its loads and its use.
+// One lane's share of a tile, held in registers between its loads and its use.  The image is
+// read once per call, so its loads are non-temporal (streamed past the caches).
+
+__device__ __forceinline__ uint4 ld_stream(const uint8_t *p)
+{
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <int FMT>
 struct TileRegs;
@@ -145,8 +203,8 @@ struct TileRegs<QG_Q4K> {
     __device__ __forceinline__ void load(const uint8_t *tile, int lane)
     {
 #pragma unroll
-        for (int i = 0; i < 8; i++) w[i] = *reinterpret_cast<const uint4 *>(tile + 1024 * i + 16 * lane);
-        meta = *reinterpret_cast<const uint4 *>(tile + 8192 + 16 * lane);
+        for (int i = 0; i < 8; i++) w[i] = ld_stream(tile + 1024 * i + 16 * lane);
+        meta = ld_stream(tile + 8192 + 16 * lane);
     }
 };
 
@@ -160,10 +218,10 @@ struct TileRegs<QG_Q6K> {
     __device__ __forceinline__ void load(const uint8_t *tile, int lane)
     {
 #pragma unroll
-        for (int i = 0; i < 8; i++) L[i] = *reinterpret_cast<const uint4 *>(tile + 1024 * i + 16 * lane);
+        for (int i = 0; i < 8; i++) L[i] = ld_stream(tile + 1024 * i + 16 * lane);
 #pragma unroll
-        for (int h = 0; h < 4; h++) H[h] = *reinterpret_cast<const uint4 *>(tile + 8192 + 1024 * h + 16 * lane);
-        sc = *reinterpret_cast<const uint4 *>(tile + 12288 + 16 * lane);
+        for (int h = 0; h < 4; h++) H[h] = ld_stream(tile + 8192 + 1024 * h + 16 * lane);
+        sc = ld_stream(tile + 12288 + 16 * lane);
         d = *reinterpret_cast<const uint16_t *>(tile + 13312 + 2 * lane);
     }
 };
@@ -183,16 +241,21 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q4K> &T, int b, co
     f[5] = q4k_field<5>(T.meta.y, T.meta.z, T.meta.w);
     f[6] = q4k_field<6>(T.meta.y, T.meta.z, T.meta.w);
     f[7] = q4k_field<7>(T.meta.y, T.meta.z, T.meta.w);
-    const int8_t *a = act.block_codes(b);
     if constexpr (MODE == QG_PERBLOCK) {
         int Cb = 0, Ob = 0;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int P = q4k_sub_dot(T.w[i], a + 32 * i);
+            const int P = q4k_sub_dot(T.w[i], act.codes16(b, 2 * i), act.codes16(b, 2 * i + 1));
             Cb += __mul24((int)(f[i] & 63u), P);
             Ob += __mul24((int)(f[i] >> 6), act.sum32(b, i));
         }
         const qg_act_scale s = act.scale(b, 0, 1);
+        const F16Scale d = f16_scale(T.meta.x & 0xFFFFu);
+        const F16Scale dm = f16_scale(T.meta.x >> 16);
+        const int gap = d.ex > dm.ex ? d.ex - dm.ex : dm.ex - d.ex;
+        if (__all(gap <= 8))
+            return piece_q4k_perblock_near(Cb, Ob, __builtin_ldexp((double)d.sig, d.ex),
+                                           __builtin_ldexp((double)dm.sig, dm.ex), __builtin_ldexp((double)s.m, s.e));
         return piece_q4k_perblock(Cb, Ob, T.meta.x, s.m, s.e);
     } else {
         const F16Scale d = f16_scale(T.meta.x & 0xFFFFu);
@@ -201,7 +264,7 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q4K> &T, int b, co
         int e[16];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int P = q4k_sub_dot(T.w[i], a + 32 * i);
+            const int P = q4k_sub_dot(T.w[i], act.codes16(b, 2 * i), act.codes16(b, 2 * i + 1));
             const int Cj = __mul24((int)(f[i] & 63u), P);
             const int Oj = __mul24((int)(f[i] >> 6), act.sum32(b, i));
             const qg_act_scale s = act.scale(b, i, 8);
@@ -218,13 +281,13 @@ template <int MODE, class Act>
 __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q6K> &T, int b, const Act &act)
 {
     const uint32_t sw[4] = {T.sc.x, T.sc.y, T.sc.z, T.sc.w};
-    const int8_t *a = act.block_codes(b);
     int Ck[16];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         int P0, P1;
-        if (i & 1) q6k_sub_dots<1>(T.L[i], T.H[i >> 1], a + 32 * i, P0, P1);
-        else q6k_sub_dots<0>(T.L[i], T.H[i >> 1], a + 32 * i, P0, P1);
+        const uint4 a0 = act.codes16(b, 2 * i), a1 = act.codes16(b, 2 * i + 1);
+        if (i & 1) q6k_sub_dots<1>(T.L[i], T.H[i >> 1], a0, a1, P0, P1);
+        else q6k_sub_dots<0>(T.L[i], T.H[i >> 1], a0, a1, P0, P1);
         // (q - 32) . a = q . a - 32 * sum(a)
         const int s0 = (int)(int8_t)(sw[(2 * i) >> 2] >> (8 * ((2 * i) & 3)));
         const int s1 = (int)(int8_t)(sw[(2 * i + 1) >> 2] >> (8 * ((2 * i + 1) & 3)));
@@ -252,9 +315,51 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q6K> &T, int b, co
 }
 
 // ---------------------------------------------------------------------------------------
+// A workgroup's work on its 64-row group once the activations are in place.  W waves split
+// the group's G blocks (wave w takes blocks w, w+W, ...); with DB (more blocks than waves)
+// each wave loads its next tile while the current one is computed.  Pieces are parked in
+// LDS; after a barrier the first wave adds each row's pieces in block order, one row per
+// lane.  `act_of(c)` hands out column c's activation source.
+
+template <int FMT, int MODE, int NC, int W, bool DB, class ActOf>
+__device__ __forceinline__ void group_pieces_and_rows(const uint8_t *gbase, int G, int wid, int lane,
+                                                      TileRegs<FMT> &t0, TileRegs<FMT> &t1,
+                                                      const ActOf &act_of, float *s_piece, int64_t row0,
+                                                      int rows, int col0, int ncol, float *__restrict__ out)
+{
+    using T = TileRegs<FMT>;
+    auto compute = [&](const T &tile, int b) {
+#pragma unroll
+        for (int c = 0; c < NC; c++) s_piece[((size_t)c * G + b) * 64 + lane] = pair_piece<MODE>(tile, b, act_of(c));
+    };
+    if constexpr (DB) {
+        // two register sets, no copies: t0 holds blocks wid, wid+2W, ...; t1 holds wid+W, ...
+        for (int b = wid; b < G; b += 2 * W) {
+            if (b + W < G) t1.load(gbase + (size_t)(b + W) * T::kBytes, lane);
+            compute(t0, b);
+            if (b + W >= G) break;
+            if (b + 2 * W < G) t0.load(gbase + (size_t)(b + 2 * W) * T::kBytes, lane);
+            compute(t1, b + W);
+        }
+    } else {
+        // at most one block per wave
+        if (wid < G) compute(t0, wid);
+    }
+    __syncthreads();
+
+    if (wid == 0) {
+        const int64_t row = row0 + lane;
+#pragma unroll
+        for (int c = 0; c < NC; c++) {
+            float y = 0.0f;
+            const float *pc = s_piece + (size_t)c * G * 64 + lane;
+            for (int b = 0; b < G; b++) y = fadd_ftz(y, pc[(size_t)b * 64]);
+            if (row < rows && col0 + c < ncol) out[(int64_t)(col0 + c) * rows + row] = canon_nan(y);
+        }
+    }
+}
+
 // The kernel.  blockIdx.x = 64-row group, blockIdx.y = batch of NC activation columns.
-// W waves split the group's G blocks (wave w takes blocks w, w+W, ...); with DB (more
-// blocks than waves) each wave loads its next tile while the current one is computed.
 
 template <int FMT, int MODE, int NC, int W, bool DB>
 __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict__ image, int rows, int G,
@@ -265,6 +370,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
 {
     extern __shared__ __align__(16) unsigned char lds[];
     using T = TileRegs<FMT>;
+    using R = ActRec<FMT, MODE>;
     const int C = G * 256;
     const int nsc = MODE == QG_PERBLOCK ? G : G * 8;
     const int g = blockIdx.x;
@@ -278,11 +384,8 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
     [[maybe_unused]] T t1;
     if (wid < G) t0.load(gbase + (size_t)wid * T::kBytes, lane);
 
-    float *s_piece;
-    const unsigned char *s_rec = nullptr;
     if constexpr (NC > 1) {
         // stage NC columns as per-block records (codes, code sums, scales)
-        using R = ActRec<FMT, MODE>;
         unsigned char *rec = lds;
         for (int c = 0; c < NC; c++) {
             const int col = col0 + c;
@@ -305,54 +408,119 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
                 *reinterpret_cast<uint32_t *>(rc + (size_t)(i / R::kScales) * R::kStride + R::kScOff +
                                               4 * (i % R::kScales)) = have ? scw[i] : 0u;
         }
-        s_rec = rec;
-        s_piece = reinterpret_cast<float *>(lds + (size_t)NC * G * R::kStride);
         __syncthreads();
+        float *s_piece = reinterpret_cast<float *>(lds + (size_t)NC * G * R::kStride);
+        auto act_of = [&](int c) { return ActLds<FMT, MODE>{lds + (size_t)c * G * R::kStride}; };
+        group_pieces_and_rows<FMT, MODE, NC, W, DB>(gbase, G, wid, lane, t0, t1, act_of, s_piece, (int64_t)g * 64,
+                                                    rows, col0, ncol, out);
     } else {
-        s_piece = reinterpret_cast<float *>(lds);
+        float *s_piece = reinterpret_cast<float *>(lds);
+        const ActGlobal act{codes + (size_t)col0 * C, csums + (size_t)col0 * (C / 16), scales + (size_t)col0 * nsc};
+        auto act_of = [&](int) { return act; };
+        group_pieces_and_rows<FMT, MODE, NC, W, DB>(gbase, G, wid, lane, t0, t1, act_of, s_piece, (int64_t)g * 64,
+                                                    rows, col0, ncol, out);
     }
+}
 
-    auto compute = [&](const T &tile, int b) {
-#pragma unroll
-        for (int c = 0; c < NC; c++) {
-            float p;
-            if constexpr (NC == 1) {
-                const ActGlobal act{codes + (size_t)col0 * C, csums + (size_t)col0 * (C / 16),
-                                    scales + (size_t)col0 * nsc};
-                p = pair_piece<MODE>(tile, b, act);
-            } else {
-                const ActLds<FMT, MODE> act{s_rec + (size_t)c * G * ActRec<FMT, MODE>::kStride};
-                p = pair_piece<MODE>(tile, b, act);
+// ---------------------------------------------------------------------------------------
+// Quantize + GEMV in one launch, for one activation row.  Each wave quantizes the
+// activation blocks it multiplies (wave w: blocks w, w+W, ...) in its own registers, four
+// values per lane, so no block's codes travel through LDS or wait for another wave.  The
+// row's f32 values are loaded before the weight tiles, so the quantization waits for them
+// alone and overlaps the weight stream.  Workgroup 0 also writes the quantized row out
+// exactly as qg_quantize_act does; the per-lane arithmetic is the same function.
+
+// Quantizes one block (a wave past the row's last block quantizes a copy of it, so the
+// loads feeding this have one unconditional use); workgroup 0 writes block b < G out.
+template <int MODE>
+__device__ __forceinline__ ActWave quantize_block_in_wave(float4 v, int b, int G, int lane, bool emit,
+                                                          int8_t *__restrict__ codes,
+                                                          qg_act_scale *__restrict__ scales,
+                                                          int32_t *__restrict__ csums, int32_t *__restrict__ err_flag)
+{
+    constexpr int GROUP_LANES = MODE == QG_PERBLOCK ? 64 : 8;
+    const QuantLane q = quantize_lane<MODE>(v);
+    ActWave a;
+    a.packed = q.packed;
+    a.s16 = quad_sum(q.sum4);                  // sums of 16 consecutive codes = 4 lanes
+    a.s32 = octet_sum_of_quads(a.s16);
+    a.m = q.m;
+    a.e = q.e;
+    if (b < G) {
+        const bool leader = (lane & (GROUP_LANES - 1)) == 0;
+        if (emit) {
+            reinterpret_cast<uint32_t *>(codes + (size_t)b * 256)[lane] = q.packed;
+            if ((lane & 3) == 0) csums[(size_t)b * 16 + (lane >> 2)] = a.s16;
+            if (leader) {
+                qg_act_scale sc;
+                sc.e = (int16_t)q.e;
+                sc.m = (uint8_t)q.m;
+                sc.pad = 0;
+                scales[(size_t)b * (64 / GROUP_LANES) + lane / GROUP_LANES] = sc;
             }
-            s_piece[((size_t)c * G + b) * 64 + lane] = p;
         }
-    };
+        if (q.inf && leader && err_flag) *err_flag = 1;
+    }
+    return a;
+}
 
-    if constexpr (DB) {
-        // two register sets, no copies: t0 holds blocks wid, wid+2W, ...; t1 holds wid+W, ...
-        for (int b = wid; b < G; b += 2 * W) {
-            if (b + W < G) t1.load(gbase + (size_t)(b + W) * T::kBytes, lane);
-            compute(t0, b);
-            if (b + W >= G) break;
-            if (b + 2 * W < G) t0.load(gbase + (size_t)(b + 2 * W) * T::kBytes, lane);
-            compute(t1, b + W);
-        }
+template <int FMT, int MODE, int W, int KX>
+__global__ __launch_bounds__(64 * W) void gemv_fused_kernel(const uint8_t *__restrict__ image, int rows, int G,
+                                                            const float *__restrict__ x, int8_t *__restrict__ codes,
+                                                            qg_act_scale *__restrict__ scales,
+                                                            int32_t *__restrict__ csums,
+                                                            int32_t *__restrict__ err_flag, float *__restrict__ out)
+{
+    extern __shared__ __align__(16) unsigned char lds[];
+    using T = TileRegs<FMT>;
+    const int g = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint8_t *gbase = image + (size_t)g * G * T::kBytes;
+    float *s_piece = reinterpret_cast<float *>(lds);
+
+    // this wave's activation blocks (KX of them), then its first weight tile.  The loads are
+    // unconditional (indices clamped into the row) and kept in this order, so that the
+    // quantization waits for the activation loads alone.
+    float4 xv[KX];
+#pragma unroll
+    for (int k = 0; k < KX; k++) {
+        const int b = min(wid + k * W, G - 1);
+        xv[k] = *reinterpret_cast<const float4 *>(x + (size_t)b * 256 + 4 * lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    T t[2];
+    t[0].load(gbase + (size_t)min(wid, G - 1) * T::kBytes, lane);
+    __builtin_amdgcn_sched_barrier(0);
+
+    ActWave aw[KX];
+#pragma unroll
+    for (int k = 0; k < KX; k++)
+        aw[k] = quantize_block_in_wave<MODE>(xv[k], wid + k * W, G, lane, g == 0, codes, scales, csums, err_flag);
+
+    if constexpr (KX == 1) {
+        // one block per wave: its codes go to scalar registers before the tile is waited for
+        const ActWaveCodes ac(aw[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (wid < G) s_piece[(size_t)wid * 64 + lane] = pair_piece<MODE>(t[0], wid, ac);
     } else {
-        // at most one block per wave
-        if (wid < G) compute(t0, wid);
+        // blocks wid + kW in turn; the next tile loads while this one is computed
+#pragma unroll
+        for (int k = 0; k < KX; k++) {
+            const int b = wid + k * W;
+            if (b >= G) break;
+            if (k + 1 < KX && b + W < G) t[(k + 1) & 1].load(gbase + (size_t)(b + W) * T::kBytes, lane);
+            s_piece[(size_t)b * 64 + lane] = pair_piece<MODE>(t[k & 1], b, aw[k]);
+        }
     }
     __syncthreads();
 
     // the first wave adds each row's pieces in block order, one row per lane
     if (wid == 0) {
         const int64_t row = (int64_t)g * 64 + lane;
-#pragma unroll
-        for (int c = 0; c < NC; c++) {
-            float y = 0.0f;
-            const float *pc = s_piece + (size_t)c * G * 64 + lane;
-            for (int b = 0; b < G; b++) y = fadd_ftz(y, pc[(size_t)b * 64]);
-            if (row < rows && col0 + c < ncol) out[(int64_t)(col0 + c) * rows + row] = canon_nan(y);
-        }
+        float y = 0.0f;
+        for (int b = 0; b < G; b++) y = fadd_ftz(y, s_piece[(size_t)b * 64 + lane]);
+        if (row < rows) out[row] = canon_nan(y);
     }
 }
 
@@ -389,7 +557,9 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const uint8_t *__restri
         for (int i = 0; i < 8; i++) {
             int S = 0;
             for (int k = 0; k < 32; k++) S += a[32 * i + k];
-            csum_out[(r * G + b) * 8 + i] = (int)(f[i] & 63u) * q4k_sub_dot(T.w[i], a + 32 * i);
+            const uint4 a0 = *reinterpret_cast<const uint4 *>(a + 32 * i);
+            const uint4 a1 = *reinterpret_cast<const uint4 *>(a + 32 * i + 16);
+            csum_out[(r * G + b) * 8 + i] = (int)(f[i] & 63u) * q4k_sub_dot(T.w[i], a0, a1);
             osum_out[(r * G + b) * 8 + i] = (int)(f[i] >> 6) * S;
         }
     } else {
@@ -399,8 +569,10 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const uint8_t *__restri
         const uint32_t sw[4] = {T.sc.x, T.sc.y, T.sc.z, T.sc.w};
         for (int i = 0; i < 8; i++) {
             int P0, P1;
-            if (i & 1) q6k_sub_dots<1>(T.L[i], T.H[i >> 1], a + 32 * i, P0, P1);
-            else q6k_sub_dots<0>(T.L[i], T.H[i >> 1], a + 32 * i, P0, P1);
+            const uint4 a0 = *reinterpret_cast<const uint4 *>(a + 32 * i);
+            const uint4 a1 = *reinterpret_cast<const uint4 *>(a + 32 * i + 16);
+            if (i & 1) q6k_sub_dots<1>(T.L[i], T.H[i >> 1], a0, a1, P0, P1);
+            else q6k_sub_dots<0>(T.L[i], T.H[i >> 1], a0, a1, P0, P1);
             int S0 = 0, S1 = 0;
             for (int k = 0; k < 16; k++) { S0 += a[32 * i + k]; S1 += a[32 * i + 16 + k]; }
             const int s0 = (int)(int8_t)(sw[(2 * i) >> 2] >> (8 * ((2 * i) & 3)));
@@ -479,7 +651,67 @@ int launch_nc(int64_t rows, int G, int64_t ncol, const void *image, const int8_t
     return launch_w<FMT, MODE, 1>(rows, G, ncol, image, codes, scales, csums, out, s);
 }
 
+template <int FMT, int MODE, int W, int KX>
+int launch_fused_typed(int64_t rows, int G, const void *image, const float *x, int8_t *codes, qg_act_scale *scales,
+                       int32_t *csums, int32_t *err_flag, float *out, hipStream_t s)
+{
+    const int64_t groups = (rows + 63) / 64;
+    if (groups > 0x7fffffff) return fail(QG_E_SHAPE, "too many rows: %lld", (long long)rows);
+    const size_t lds = (size_t)G * 64 * sizeof(float);
+    hipEvent_t ev0, ev1;
+    take_timing_events(&ev0, &ev1);
+    if (ev0 && ev1)
+        hipExtLaunchKernelGGL((gemv_fused_kernel<FMT, MODE, W, KX>), dim3((unsigned)groups), dim3(64 * W), lds, s,
+                              ev0, ev1, 0, static_cast<const uint8_t *>(image), (int)rows, G, x, codes, scales, csums,
+                              err_flag, out);
+    else
+        hipLaunchKernelGGL((gemv_fused_kernel<FMT, MODE, W, KX>), dim3((unsigned)groups), dim3(64 * W), lds, s,
+                           static_cast<const uint8_t *>(image), (int)rows, G, x, codes, scales, csums, err_flag, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_E_RUNTIME, "fused gemv launch: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+template <int FMT, int MODE>
+int launch_fused_w(int64_t rows, int G, const void *image, const float *x, int8_t *codes, qg_act_scale *scales,
+                   int32_t *csums, int32_t *err_flag, float *out, hipStream_t s)
+{
+    // waves per workgroup as in the GEMV; each wave takes at most KX = 8 blocks (G <= 64)
+    int w = tuning().waves_per_wg;
+    if (w <= 0) w = G >= 16 ? 16 : G >= 8 ? 8 : 4;
+    if (w > 8 && G > 16) w = 8;
+    if (w < 8 && G > 8) w = 8;
+#define QG_FUSED(W_, KX_) \
+    launch_fused_typed<FMT, MODE, W_, KX_>(rows, G, image, x, codes, scales, csums, err_flag, out, s)
+    if (w >= 16) return QG_FUSED(16, 1);
+    if (w >= 8) {
+        if (G <= 8) return QG_FUSED(8, 1);
+        if (G <= 16) return QG_FUSED(8, 2);
+        if (G <= 32) return QG_FUSED(8, 4);
+        return QG_FUSED(8, 8);
+    }
+    if (G <= 4) return QG_FUSED(4, 1);
+    return QG_FUSED(4, 2);
+#undef QG_FUSED
+}
+
 }  // namespace
+
+int launch_gemv_fused(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const float *x,
+                      int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
+                      hipStream_t s)
+{
+    const int G = (int)(cols / 256);
+    if (rows == 0) return QG_OK;
+    if (G > kFusedMaxBlocks) return fail(QG_E_SHAPE, "fused gemv: %d blocks per row exceed %d", G, kFusedMaxBlocks);
+    if (fmt == QG_Q4K && mode == QG_PERBLOCK)
+        return launch_fused_w<QG_Q4K, QG_PERBLOCK>(rows, G, image, x, codes, scales, csums, err_flag, out, s);
+    if (fmt == QG_Q4K && mode == QG_SUB32)
+        return launch_fused_w<QG_Q4K, QG_SUB32>(rows, G, image, x, codes, scales, csums, err_flag, out, s);
+    if (fmt == QG_Q6K && mode == QG_PERBLOCK)
+        return launch_fused_w<QG_Q6K, QG_PERBLOCK>(rows, G, image, x, codes, scales, csums, err_flag, out, s);
+    return launch_fused_w<QG_Q6K, QG_SUB32>(rows, G, image, x, codes, scales, csums, err_flag, out, s);
+}
 
 int launch_gemv(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, const void *image,
                 const int8_t *codes, const qg_act_scale *scales, const int32_t *csums, float *out,

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qgemv.h"
+
 namespace qg {
 
 constexpr int kSumWindow = 64;   // places an exact sum keeps below its largest term's exponent
@@ -179,6 +181,111 @@ __device__ __forceinline__ float exact_sum(const long long (&v)[N], const int (&
         if (vi != 0) s += (u128)(i128)vi << (ei - emin2);
     }
     return r32_i128((i128)s, emin2);
+}
+
+// ---------------------------------------------------------------------------------------
+// Activation quantization of 256 consecutive elements by one wave, four per lane (lane l
+// holds elements 4l..4l+3) ("Module numerics": Functions absmax, wide_scale, block_scale,
+// rne_div, quantize, quantize_blocks).  One PerBlock block spans the wave; a Sub32 block
+// spans eight lanes.
+//
+// The scale comes from amax/127 in f64: the quotient is within 2^-53 of amax/127, and the
+// nearest grid point of `bits` significant bits lies at least 2^-25 of it away unless it
+// equals it, so rounding the f64 quotient up to `bits` significant bits gives the least
+// admissible scale.  Codes are rint(x / s) in f64: |x/s| <= 127, and an f64 quotient that
+// is not a half-integer cannot round onto one, so ties are exactly the true ties and go
+// to even.
+
+// least m*2^e (m with BITS significant bits) not below amax/127, amax finite and > 0
+template <int BITS>
+__device__ __forceinline__ void least_scale(float amax, int &m, int &e)
+{
+    const double t = (double)amax / 127.0;
+    int k;
+    const double f = __builtin_frexp(t, &k);                // t = f * 2^k, f in [0.5, 1)
+    double mm = __builtin_ceil(__builtin_ldexp(f, BITS));   // in [2^(BITS-1), 2^BITS]
+    int ee = k - BITS;
+    if (mm == (double)(1 << BITS)) { mm = (double)(1 << (BITS - 1)); ee += 1; }
+    m = (int)mm;
+    e = ee;
+}
+
+// Lane exchanges within rows of 16 lanes through DPP (every source lane is valid)
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowMirror = 0x140;    // lane i of a row <- lane 15 - i
+constexpr int kDppHalfMirror = 0x141;   // lane i of a half-row <- lane 7 - i
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// sum over each group of 4 lanes (4l..4l+3), in every lane of the group
+__device__ __forceinline__ int quad_sum(int v)
+{
+    v += dpp<kDppQuadSwap1>(v);
+    return v + dpp<kDppQuadSwap2>(v);
+}
+
+// given quad sums, the sum over each group of 8 lanes
+__device__ __forceinline__ int octet_sum_of_quads(int v) { return v + dpp<kDppHalfMirror>(v); }
+
+struct QuantLane {
+    uint32_t packed;   // the lane's four int8 codes, element 4l in the low byte
+    int sum4;          // their sum
+    int m, e;          // scale m*2^e of the lane's activation block (m = 0: block holds an inf)
+    int inf;           // the lane's activation block holds an infinity
+};
+
+template <int MODE>
+__device__ __forceinline__ QuantLane quantize_lane(float4 v4)
+{
+    constexpr int BITS = MODE == QG_PERBLOCK ? 8 : 4;
+    const float v[4] = {ftz(v4.x), ftz(v4.y), ftz(v4.z), ftz(v4.w)};
+    // largest magnitude, NaN passed over; non-negative floats order as integers, and an
+    // infinity is the largest value left
+    uint32_t amax_bits = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t a = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+        if (a <= 0x7F800000u && a > amax_bits) amax_bits = a;
+    }
+    auto umax = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    amax_bits = umax(amax_bits, (uint32_t)dpp<kDppQuadSwap1>((int)amax_bits));
+    amax_bits = umax(amax_bits, (uint32_t)dpp<kDppQuadSwap2>((int)amax_bits));
+    amax_bits = umax(amax_bits, (uint32_t)dpp<kDppHalfMirror>((int)amax_bits));   // 8 lanes: a Sub32 block
+    if constexpr (MODE == QG_PERBLOCK) {
+        amax_bits = umax(amax_bits, (uint32_t)dpp<kDppRowMirror>((int)amax_bits));  // 16 lanes
+        const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)amax_bits, 0);
+        const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)amax_bits, 16);
+        const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)amax_bits, 32);
+        const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)amax_bits, 48);
+        amax_bits = umax(umax(r0, r1), umax(r2, r3));                              // the wave
+    }
+    QuantLane q;
+    q.inf = amax_bits == 0x7F800000u;
+    if (q.inf) {
+        q.m = 0; q.e = 0;
+    } else if (amax_bits == 0) {
+        q.m = 1 << (BITS - 1); q.e = 0;                   // all-zero block
+    } else {
+        least_scale<BITS>(__uint_as_float(amax_bits), q.m, q.e);
+    }
+    q.packed = 0;
+    q.sum4 = 0;
+    if (q.m != 0) {
+        const double s = __builtin_ldexp((double)q.m, q.e);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            int c = 0;
+            if (v[i] == v[i]) c = (int)__builtin_rint((double)v[i] / s);
+            q.sum4 += c;
+            q.packed |= ((uint32_t)c & 0xFFu) << (8 * i);
+        }
+    }
+    return q;
 }
 
 // ---------------------------------------------------------------------------------------

@@ -13,12 +13,16 @@ constexpr int kTileRows = 64;     // rows per tile (one 256-element block each)
 constexpr int kTileBytesQ4K = 64 * 144;   // 9216
 constexpr int kTileBytesQ6K = 64 * 210;   // 13440
 
+// widest row (in 256-element blocks) the one-launch quantize + GEMV handles; wider rows
+// take the two-launch path
+constexpr int kFusedMaxBlocks = 64;
+
 // per-thread failure reason
 int fail(int status, const char *fmt, ...);
 
 struct Tuning {
     int waves_per_wg;     // waves per GEMV workgroup (4, 8, 16); 0 = derived from the block count
-    int mfma_min_cols;    // columns from which a Q4_K PerBlock GEMM uses the matrix cores; 0 = 16
+    int mfma_min_cols;    // columns from which a Q4_K PerBlock GEMM uses the matrix cores; 0 = 8
     int mfma_col_tiles;   // 16-column tiles per matrix-core workgroup (1, 2, 4); 0 = derived
 };
 const Tuning &tuning();
@@ -36,6 +40,11 @@ int launch_quantize(int mode, int block, int64_t n, int64_t cols, const float *x
 int launch_gemv(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, const void *image,
                 const int8_t *codes, const qg_act_scale *scales, const int32_t *csums, float *out,
                 hipStream_t s);
+
+// one activation row: quantize it and run the GEMV in one launch (cols <= 256 * kFusedMaxBlocks)
+int launch_gemv_fused(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const float *x,
+                      int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
+                      hipStream_t s);
 
 int launch_gemm_mfma(int64_t rows, int64_t cols, int64_t ncol, const void *image, const int8_t *codes,
                      const qg_act_scale *scales, float *out, hipStream_t s);

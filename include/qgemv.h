@@ -164,6 +164,20 @@ int qg_gemm_q(int fmt, int mode, int64_t rows, int64_t cols, int64_t n, const vo
               const int8_t *codes, const qg_act_scale *scales, const int32_t *csums, float *out,
               void *stream);
 
+/* Quantize one activation row and run the decode GEMV on it, in one launch where the row
+ * has at most 64 blocks (cols <= 16384), else as qg_quantize_act then qg_gemv_q:
+ *   x       f32 [cols] (device, 16-byte aligned)
+ *   codes, scales, csums, err_flag   as qg_quantize_act with n = 1 (codes, scales and csums
+ *           required: they receive the quantized row)
+ *   image, out   as qg_gemv_q
+ * out and the quantized row are bit for bit those of qg_quantize_act followed by qg_gemv_q
+ * (the pages' dot of a row with a quantized activation row: "Module numerics", Functions
+ * quantize and dot).  In the one-launch form every workgroup quantizes the row itself; the
+ * first writes it out.  rows = 0 only quantizes. */
+int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const float *x,
+                     int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
+                     void *stream);
+
 /* Integer sums per (row, sub-block), before any scale ("Module lane", Functions
  * block_sums), for one activation row:
  *   Q4K: csum_out int32 [rows][cols/32] = sum sc_j*q*c over sub-block j,
@@ -185,8 +199,8 @@ int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const 
 enum { QG_TUNE_WAVES_PER_WG = 1, QG_TUNE_MFMA_MIN_COLS = 2, QG_TUNE_MFMA_COL_TILES = 3 };
 int qg_set_tuning(int key, int64_t value);
 
-/* Measurement hook: the next qg_gemv_q / qg_gemm_q call made on this thread launches its
- * kernel with hipExtLaunchKernelGGL, which records start_event as the kernel begins and
+/* Measurement hook: the next qg_gemv_q / qg_gemm_q / qg_quantize_gemv call made on this
+ * thread launches its (GEMV or GEMM) kernel with hipExtLaunchKernelGGL, which records start_event as the kernel begins and
  * stop_event as it ends (hipEvent_t handles owned by the caller; both NULL cancels).
  * Later launches are not timed.  Changes no output bits. */
 int qg_time_next_launch(void *start_event, void *stop_event);

@@ -355,9 +355,10 @@ def test_batched_columns(qg, llama, n):
 
 @pytest.mark.parametrize("ncol", [3, 8, 16, 17, 33, 64, 100])
 def test_matrix_core_gemm_matches_oracle(qg, ncol):
-    """Q4_K PerBlock with >= 16 columns runs on v_mfma_i32_16x16x64_i8; every (row, column)
-    must carry the oracle's bits, across column-tile settings, ragged rows and columns, and
-    block scales that take both the near-exponent and the general combine."""
+    """Q4_K PerBlock batches run on v_mfma_i32_16x16x64_i8 (by default from 8 columns; here
+    forced for every count); every (row, column) must carry the oracle's bits, across
+    column-tile settings, ragged rows and columns, and block scales that take both the
+    near-exponent and the general combine."""
     f = _adversarial_fields("q4k", 130, 1280, 900 + ncol)
     M = Mat(qg, f)
     xs = gen.act_outliers(ncol, 1280, 901 + ncol)
@@ -377,3 +378,91 @@ def test_matrix_core_gemm_matches_oracle(qg, ncol):
     finally:
         qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 0)
+
+
+# --- quantize + GEMV in one launch ------------------------------------------------------------
+
+def _fused(qg, M, x: np.ndarray, mode: int, err_flag=None):
+    out, act = qg.quantize_gemv(M.fmt, M.rows, M.cols, M.img, dev(x.reshape(-1)), mode, err_flag=err_flag)
+    m, e = act.scale_fields()
+    return out, act.codes.cpu().numpy(), m, e, act.csums.cpu().numpy()
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_fused_quantize_gemv_shapes(qg, fmt, mode):
+    """qg_quantize_gemv against the oracle's quantize then dot: the output row and the
+    quantized row it writes, on every shape (one launch up to 64 blocks per row, the
+    two-launch form above)."""
+    for rows, cols in SHAPES + [(70, 16384), (3, 16640)]:
+        say("fused", fmt, "mode", mode, "shape", rows, cols)
+        f = _adversarial_fields(fmt, rows, cols, rows * 17 + cols)
+        M = Mat(qg, f)
+        x = gen.act_outliers(1, cols, rows + 3 * cols)
+        if mode == 1:
+            x, _ = gen.act_sub32(1, cols, rows + 3 * cols)
+        out, c, m, e, s = _fused(qg, M, x, mode)
+        oc, om, oe, os_ = oracle.quantize(x, mode)
+        assert np.array_equal(c, oc) and np.array_equal(m, om) and np.array_equal(e, oe) and np.array_equal(s, os_)
+        want = oracle.gemv(f, oc, om, oe, mode)
+        assert first_mismatch(out, want) is None, (rows, cols, first_mismatch(out, want))
+
+
+def test_fused_launch_configuration_and_streams(qg):
+    f = _adversarial_fields("q4k", 1000, 4096, 15)
+    M = Mat(qg, f)
+    x = gen.act_outliers(1, 4096, 18)
+    ref, c, m, e, _ = _fused(qg, M, x, 0)
+    ref = bits(ref)
+    assert np.array_equal(ref, bits(oracle.gemv(f, c, m, e, 0)))
+    try:
+        for w in (4, 8, 16):
+            qg.qg_set_tuning(qg.TUNE_WAVES_PER_WG, w)
+            say("fused, waves per workgroup", w)
+            assert np.array_equal(bits(_fused(qg, M, x, 0)[0]), ref), w
+    finally:
+        qg.qg_set_tuning(qg.TUNE_WAVES_PER_WG, 0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, _ = qg.quantize_gemv(M.fmt, M.rows, M.cols, M.img, dev(x.reshape(-1)), 0, stream=s)
+    s.synchronize()
+    assert np.array_equal(bits(out), ref)
+
+
+def test_fused_decode_workload_matches_two_launches(qg, llama):
+    """The benchmark's step: fused and two-launch paths give the same bits on the
+    14336x4096 matrix for 50 fresh activation rows; row 0 checked against the oracle."""
+    M = llama["ffn"]
+    act = qg.alloc_act(1, M.cols, 0)
+    two = torch.empty(M.rows, dtype=torch.float32, device=DEV)
+    one = torch.empty(M.rows, dtype=torch.float32, device=DEV)
+    for k in range(50):
+        xd = dev(gen.decode_act(k).reshape(-1))
+        qg.quantize_act(xd[None], 0, out=act)
+        run_gemv(qg, M, act, out=two)
+        qg.quantize_gemv(M.fmt, M.rows, M.cols, M.img, xd, 0, out=one)
+        assert np.array_equal(bits(one), bits(two)), k
+        if k == 0:
+            oc, om, oe, _ = oracle.quantize(gen.decode_act(0), 0)
+            assert first_mismatch(one, oracle.gemv(M.f, oc, om, oe, 0)) is None
+
+
+def test_fused_infinity_flag_and_zero_rows(qg):
+    f = gen.q4k_fields(100, 1024, 41)
+    M = Mat(qg, f)
+    x = gen.act_normal(1, 1024, 42)
+    x[0, 300] = -np.inf
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for mode in (0, 1):
+        flag.zero_()
+        out, c, m, e, _ = _fused(qg, M, x, mode, err_flag=flag)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == 1
+        oc, om, oe, _ = oracle.quantize(x, mode, check=False)
+        assert np.array_equal(c, oc) and np.array_equal(m, om) and np.array_equal(e, oe)
+        assert first_mismatch(out, oracle.gemv(f, oc, om, oe, mode)) is None
+    # rows = 0: the call only quantizes
+    act = qg.alloc_act(1, 1024, 0)
+    xg = gen.act_normal(1, 1024, 43)
+    qg.qg_quantize_gemv(M.fmt, 0, 0, 1024, None, dev(xg.reshape(-1)), act.codes, act.scales, act.csums, None, None)
+    assert np.array_equal(act.codes.cpu().numpy(), oracle.quantize(xg, 0)[0])

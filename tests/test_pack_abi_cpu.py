@@ -171,6 +171,13 @@ def test_validation_refuses_before_any_gpu_work():
     assert L.qg_quantize_act(qg.Q4K, qg.SUB32, 1, 300, fake, fake, fake, fake, None, None) == qg.E_SHAPE
     assert L.qg_quantize_act(qg.Q4K, qg.SUB32, 1, 256, odd, fake, fake, fake, None, None) == qg.E_INVALID
     assert L.qg_block_sums(qg.Q6K, 4, 512, fake, fake, None, None, None) == qg.E_INVALID
+    assert L.qg_quantize_gemv(qg.Q4K, qg.PERBLOCK, 8, 300, fake, fake, fake, fake, fake, None, fake, None) == qg.E_SHAPE
+    assert L.qg_quantize_gemv(qg.Q4K, qg.PERBLOCK, 8, 256, fake, odd, fake, fake, fake, None, fake, None) == qg.E_INVALID
+    assert "x is not 16-byte aligned" in qg.qg_last_error()
+    assert L.qg_quantize_gemv(qg.Q4K, qg.PERBLOCK, 8, 256, fake, fake, None, fake, fake, None, fake, None) == qg.E_INVALID
+    assert "codes is NULL" in qg.qg_last_error()
+    assert L.qg_quantize_gemv(qg.Q4K, qg.PERBLOCK, 8, 256, None, fake, fake, fake, fake, None, fake, None) == qg.E_INVALID
+    assert "image is NULL" in qg.qg_last_error()
     assert L.qg_set_tuning(77, 1) == qg.E_INVALID
     assert L.qg_set_tuning(qg.TUNE_WAVES_PER_WG, 3) == qg.E_INVALID
     assert L.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 3) == qg.E_INVALID
