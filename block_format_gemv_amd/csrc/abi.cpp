@@ -205,11 +205,9 @@ int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *
         if ((st = check_ptr(who, "out", out, 4))) return st;
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (rows > 0 && cols / QG_BLOCK <= kFusedMaxBlocks)
-        return launch_gemv_fused(fmt, mode, rows, cols, image, x, codes, scales, csums, err_flag, out, s);
-    // no rows to multiply, or a row too wide for one launch: quantize, then the GEMV
-    if ((st = launch_quantize(mode, QG_BLOCK, 1, cols, x, codes, scales, csums, err_flag, s))) return st;
-    return launch_gemv(fmt, mode, rows, cols, 1, image, codes, scales, csums, out, s);
+    if (rows > 0) return launch_gemv_fused(fmt, mode, rows, cols, image, x, codes, scales, csums, err_flag, out, s);
+    // no rows to multiply: only the quantized row
+    return launch_quantize(mode, QG_BLOCK, 1, cols, x, codes, scales, csums, err_flag, s);
 }
 
 int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,

@@ -3,9 +3,10 @@
 // A tile is 64 consecutive rows x one 256-element block; lane l of a wave owns row 64g + l
 // of its tile.  Its nine (Q4_K) or fourteen (Q6_K) 16-byte loads are each a contiguous
 // 1 KiB per wave.  Every lane of a wave works on the same block, so the block's activation
-// codes, code sums and scale are wave-uniform: a single column reads them with scalar loads
-// straight from global memory (SGPR operands of v_dot4), several columns read them from
-// LDS with broadcast reads.
+// codes, code sums and scale are wave-uniform.  With one activation column each wave
+// brings its blocks' activations into its own registers (quantizing the f32 row itself,
+// or loading the codes) and reads them out into scalar registers, the SGPR operands of the
+// dot products; several columns share per-block records staged in LDS.
 //
 // Per pair the lane forms the integer sub-block sums ("Module lane", Functions block_sums),
 // turns them into the block's piece with one binary32 rounding (Functions lane / group;
@@ -29,22 +30,8 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c)
 }
 
 // ---------------------------------------------------------------------------------------
-// Activation sources.  Both hand out wave-uniform addresses.
-
-// One column straight from global memory: codes [C], csums [C/16], scales [nsc].
-struct ActGlobal {
-    const int8_t *codes;
-    const int32_t *csums;
-    const qg_act_scale *sc;
-    // codes 16i .. 16i+15 of block b
-    __device__ __forceinline__ uint4 codes16(int b, int i) const
-    {
-        return *reinterpret_cast<const uint4 *>(codes + (size_t)b * 256 + 16 * i);
-    }
-    __device__ __forceinline__ int sum32(int b, int j) const { return csums[b * 16 + 2 * j] + csums[b * 16 + 2 * j + 1]; }
-    __device__ __forceinline__ int sum16(int b, int k) const { return csums[b * 16 + k]; }
-    __device__ __forceinline__ qg_act_scale scale(int b, int j, int per_block) const { return sc[b * per_block + j]; }
-};
+// Activation sources.  Each hands out wave-uniform values: codes16(b, i) = codes 16i..16i+15
+// of block b, sum32 / sum16 = code sums of a 32- / 16-element run, scale(b, j, per_block).
 
 // NC columns staged in LDS, one record per (column, 256-element block) holding the block's
 // 256 codes, its code sums (Q4K: eight per-32 sums; Q6K: sixteen per-16 sums) and its
@@ -128,6 +115,44 @@ struct ActWaveCodes {
     __device__ __forceinline__ qg_act_scale scale(int b, int j, int per_block) const { return w.scale(b, j, per_block); }
 };
 
+// The block's codes as two nibble planes for the 4-bit dot products of a Q4_K-style tile.
+// A code is a = 16*ah + al with al = a & 15 (unsigned) and ah = a >> 4 (signed, -8..7).  A
+// tile's code byte holds the codes of elements k (low nibble) and k + 16 (high nibble) of
+// a 32-element sub-block, so plane dword (i, d) holds, nibble for nibble in the same order,
+// the al (or ah) of elements 32i + 4d + t and 32i + 16 + 4d + t, t = 0..3.  Then with
+// q' = q - 8 (the code nibble with its top bit flipped: a signed nibble),
+//     sum q*a = 16 * (sum q'*ah + 8 * sum ah) + sum q*al,
+// one signed and one unsigned v_dot8 per code dword.  kh[i] = 8 * (sum of ah over
+// sub-block i).  Built once per block from the lanes' codes, before the tile is waited for.
+struct ActPlanes {
+    uint32_t al[32], ah[32];
+    int kh[8];
+    ActWave w;
+    __device__ __forceinline__ explicit ActPlanes(const ActWave &a) : w(a)
+    {
+        const uint32_t lo = a.packed & 0x0F0F0F0Fu;
+        const uint32_t hi = (a.packed >> 4) & 0x0F0F0F0Fu;
+        // lane 8i + d (d < 4) pairs its codes with those of lane 8i + 4 + d (elements + 16)
+        const uint32_t lo16 = (uint32_t)dpp<kDppRowShl4>((int)lo);
+        const uint32_t hi16 = (uint32_t)dpp<kDppRowShl4>((int)hi);
+        const uint32_t AL = lo | (lo16 << 4);
+        const uint32_t AH = hi | (hi16 << 4);
+        const int sh = quad_sum(__builtin_amdgcn_sdot8((int)AH, 0x11111111, 0, false));
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+#pragma unroll
+            for (int d = 0; d < 4; d++) {
+                al[4 * i + d] = (uint32_t)__builtin_amdgcn_readlane((int)AL, 8 * i + d);
+                ah[4 * i + d] = (uint32_t)__builtin_amdgcn_readlane((int)AH, 8 * i + d);
+            }
+            kh[i] = 8 * __builtin_amdgcn_readlane(sh, 8 * i);
+        }
+    }
+    __device__ __forceinline__ int sum32(int b, int j) const { return w.sum32(b, j); }
+    __device__ __forceinline__ int sum16(int b, int k) const { return w.sum16(b, k); }
+    __device__ __forceinline__ qg_act_scale scale(int b, int j, int per_block) const { return w.scale(b, j, per_block); }
+};
+
 // ---------------------------------------------------------------------------------------
 // Weight-side decoding
 
@@ -158,6 +183,26 @@ __device__ __forceinline__ int q4k_sub_dot(uint4 w, uint4 a0, uint4 a1)
     P = sdot4(w.w & 0x0F0F0F0Fu, a0.w, P);
     P = sdot4((w.w >> 4) & 0x0F0F0F0Fu, a1.w, P);
     return P;
+}
+
+// The integer dot of sub-block i of a Q4_K-style tile with the activation source.
+template <class Act>
+__device__ __forceinline__ int q4k_sub(const uint4 &w, int b, int i, const Act &act)
+{
+    return q4k_sub_dot(w, act.codes16(b, 2 * i), act.codes16(b, 2 * i + 1));
+}
+
+__device__ __forceinline__ int q4k_sub(const uint4 &w, int, int i, const ActPlanes &p)
+{
+    int X = p.kh[i];
+    uint32_t Y = 0;
+    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        X = __builtin_amdgcn_sdot8((int)(q[d] ^ 0x88888888u), (int)p.ah[4 * i + d], X, false);
+        Y = __builtin_amdgcn_udot8(q[d], p.al[4 * i + d], Y, false);
+    }
+    return 16 * X + (int)Y;
 }
 
 // Integer dots of two 16-element Q6_K sub-blocks (2i, 2i+1): 4-bit low parts from ql, 2-bit
@@ -245,17 +290,14 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q4K> &T, int b, co
         int Cb = 0, Ob = 0;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int P = q4k_sub_dot(T.w[i], act.codes16(b, 2 * i), act.codes16(b, 2 * i + 1));
+            const int P = q4k_sub(T.w[i], b, i, act);
             Cb += __mul24((int)(f[i] & 63u), P);
             Ob += __mul24((int)(f[i] >> 6), act.sum32(b, i));
         }
         const qg_act_scale s = act.scale(b, 0, 1);
-        const F16Scale d = f16_scale(T.meta.x & 0xFFFFu);
-        const F16Scale dm = f16_scale(T.meta.x >> 16);
-        const int gap = d.ex > dm.ex ? d.ex - dm.ex : dm.ex - d.ex;
-        if (__all(gap <= 8))
-            return piece_q4k_perblock_near(Cb, Ob, __builtin_ldexp((double)d.sig, d.ex),
-                                           __builtin_ldexp((double)dm.sig, dm.ex), __builtin_ldexp((double)s.m, s.e));
+        const float fd = f16_value(T.meta.x), fm = f16_value(T.meta.x >> 16);
+        if (__all(q4k_near(fd, fm)))
+            return piece_q4k_perblock_near(Cb, Ob, (double)fd, (double)fm, __builtin_ldexp((double)s.m, s.e));
         return piece_q4k_perblock(Cb, Ob, T.meta.x, s.m, s.e);
     } else {
         const F16Scale d = f16_scale(T.meta.x & 0xFFFFu);
@@ -264,7 +306,7 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q4K> &T, int b, co
         int e[16];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int P = q4k_sub_dot(T.w[i], act.codes16(b, 2 * i), act.codes16(b, 2 * i + 1));
+            const int P = q4k_sub(T.w[i], b, i, act);
             const int Cj = __mul24((int)(f[i] & 63u), P);
             const int Oj = __mul24((int)(f[i] >> 6), act.sum32(b, i));
             const qg_act_scale s = act.scale(b, i, 8);
@@ -359,7 +401,7 @@ __device__ __forceinline__ void group_pieces_and_rows(const uint8_t *gbase, int 
     }
 }
 
-// The kernel.  blockIdx.x = 64-row group, blockIdx.y = batch of NC activation columns.
+// Several columns.  blockIdx.x = 64-row group, blockIdx.y = batch of NC activation columns.
 
 template <int FMT, int MODE, int NC, int W, bool DB>
 __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict__ image, int rows, int G,
@@ -384,7 +426,8 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
     [[maybe_unused]] T t1;
     if (wid < G) t0.load(gbase + (size_t)wid * T::kBytes, lane);
 
-    if constexpr (NC > 1) {
+    static_assert(NC > 1, "one column runs in gemv1_kernel");
+    {
         // stage NC columns as per-block records (codes, code sums, scales)
         unsigned char *rec = lds;
         for (int c = 0; c < NC; c++) {
@@ -413,30 +456,69 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
         auto act_of = [&](int c) { return ActLds<FMT, MODE>{lds + (size_t)c * G * R::kStride}; };
         group_pieces_and_rows<FMT, MODE, NC, W, DB>(gbase, G, wid, lane, t0, t1, act_of, s_piece, (int64_t)g * 64,
                                                     rows, col0, ncol, out);
-    } else {
-        float *s_piece = reinterpret_cast<float *>(lds);
-        const ActGlobal act{codes + (size_t)col0 * C, csums + (size_t)col0 * (C / 16), scales + (size_t)col0 * nsc};
-        auto act_of = [&](int) { return act; };
-        group_pieces_and_rows<FMT, MODE, NC, W, DB>(gbase, G, wid, lane, t0, t1, act_of, s_piece, (int64_t)g * 64,
-                                                    rows, col0, ncol, out);
     }
 }
 
 // ---------------------------------------------------------------------------------------
-// Quantize + GEMV in one launch, for one activation row.  Each wave quantizes the
-// activation blocks it multiplies (wave w: blocks w, w+W, ...) in its own registers, four
-// values per lane, so no block's codes travel through LDS or wait for another wave.  The
-// row's f32 values are loaded before the weight tiles, so the quantization waits for them
-// alone and overlaps the weight stream.  Workgroup 0 also writes the quantized row out
-// exactly as qg_quantize_act does; the per-lane arithmetic is the same function.
+// One activation column.  Each wave brings the activation blocks it multiplies (wave w:
+// blocks w, w+W, ...) into its own registers, four codes per lane: SRC_F32 quantizes the
+// f32 row itself (the one-launch quantize + GEMV), SRC_CODES loads the quantized row.  A
+// block's activation load is issued ahead of its weight tile, so getting the codes ready
+// (quantizing, summing, reading them out into scalar registers) waits for that load alone
+// and overlaps the weight stream.  With SRC_F32 workgroup 0 also writes the quantized row
+// out exactly as qg_quantize_act does; the per-lane arithmetic is the same function.
 
-// Quantizes one block (a wave past the row's last block quantizes a copy of it, so the
-// loads feeding this have one unconditional use); workgroup 0 writes block b < G out.
+enum { SRC_F32 = 0, SRC_CODES = 1 };
+
+struct ActIO {
+    const float *x;               // SRC_F32: the f32 row
+    const int8_t *codes_in;       // SRC_CODES: the quantized row
+    const uint32_t *scales_in;    //   and its qg_act_scale words
+    int8_t *codes_out;            // SRC_F32: where workgroup 0 writes the quantized row
+    qg_act_scale *scales_out;
+    int32_t *csums_out;
+    int32_t *err_flag;            // may be null
+};
+
+// Keeps the loads issued above here: a compiler-only barrier (no instruction, no wait) that
+// neither the IR passes nor the scheduler move memory operations across.  (Loads through a
+// const __restrict__ kernel argument count as invariant and would still move, so the
+// kernel's image pointer is a plain one.)
+__device__ __forceinline__ void load_fence()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int SRC>
+struct ActRaw;
+template <>
+struct ActRaw<SRC_F32> {
+    float4 v;                     // elements 4l .. 4l+3 of the block
+};
+template <>
+struct ActRaw<SRC_CODES> {
+    uint32_t packed;              // codes 4l .. 4l+3 of the block
+    uint32_t scale;               // the qg_act_scale word of the lane's activation block
+};
+
+template <int SRC, int MODE>
+__device__ __forceinline__ ActRaw<SRC> load_act(const ActIO &io, int b, int lane)
+{
+    ActRaw<SRC> r;
+    if constexpr (SRC == SRC_F32) {
+        r.v = *reinterpret_cast<const float4 *>(io.x + (size_t)b * 256 + 4 * lane);
+    } else {
+        r.packed = reinterpret_cast<const uint32_t *>(io.codes_in + (size_t)b * 256)[lane];
+        r.scale = io.scales_in[MODE == QG_PERBLOCK ? (size_t)b : (size_t)b * 8 + (lane >> 3)];
+    }
+    return r;
+}
+
+// Quantizes one block; workgroup 0 (emit) writes block b < G out.
 template <int MODE>
 __device__ __forceinline__ ActWave quantize_block_in_wave(float4 v, int b, int G, int lane, bool emit,
-                                                          int8_t *__restrict__ codes,
-                                                          qg_act_scale *__restrict__ scales,
-                                                          int32_t *__restrict__ csums, int32_t *__restrict__ err_flag)
+                                                          const ActIO &io)
 {
     constexpr int GROUP_LANES = MODE == QG_PERBLOCK ? 64 : 8;
     const QuantLane q = quantize_lane<MODE>(v);
@@ -449,69 +531,110 @@ __device__ __forceinline__ ActWave quantize_block_in_wave(float4 v, int b, int G
     if (b < G) {
         const bool leader = (lane & (GROUP_LANES - 1)) == 0;
         if (emit) {
-            reinterpret_cast<uint32_t *>(codes + (size_t)b * 256)[lane] = q.packed;
-            if ((lane & 3) == 0) csums[(size_t)b * 16 + (lane >> 2)] = a.s16;
+            reinterpret_cast<uint32_t *>(io.codes_out + (size_t)b * 256)[lane] = q.packed;
+            if ((lane & 3) == 0) io.csums_out[(size_t)b * 16 + (lane >> 2)] = a.s16;
             if (leader) {
                 qg_act_scale sc;
                 sc.e = (int16_t)q.e;
                 sc.m = (uint8_t)q.m;
                 sc.pad = 0;
-                scales[(size_t)b * (64 / GROUP_LANES) + lane / GROUP_LANES] = sc;
+                io.scales_out[(size_t)b * (64 / GROUP_LANES) + lane / GROUP_LANES] = sc;
             }
         }
-        if (q.inf && leader && err_flag) *err_flag = 1;
+        if (q.inf && leader && io.err_flag) *io.err_flag = 1;
     }
     return a;
 }
 
-template <int FMT, int MODE, int W, int KX>
-__global__ __launch_bounds__(64 * W) void gemv_fused_kernel(const uint8_t *__restrict__ image, int rows, int G,
-                                                            const float *__restrict__ x, int8_t *__restrict__ codes,
-                                                            qg_act_scale *__restrict__ scales,
-                                                            int32_t *__restrict__ csums,
-                                                            int32_t *__restrict__ err_flag, float *__restrict__ out)
+template <int SRC, int MODE>
+__device__ __forceinline__ ActWave ready_act(const ActRaw<SRC> &r, int b, int G, int lane, bool emit, const ActIO &io)
 {
-    extern __shared__ __align__(16) unsigned char lds[];
+    if constexpr (SRC == SRC_F32) {
+        return quantize_block_in_wave<MODE>(r.v, b, G, lane, emit, io);
+    } else {
+        ActWave a;
+        a.packed = r.packed;
+        a.s16 = quad_sum(__builtin_amdgcn_sdot4((int)r.packed, 0x01010101, 0, false));
+        a.s32 = octet_sum_of_quads(a.s16);
+        a.m = (int)((r.scale >> 16) & 0xFFu);
+        a.e = (int)(int16_t)(r.scale & 0xFFFFu);
+        return a;
+    }
+}
+
+// The block's piece: its codes go to scalar registers (as nibble planes for Q4_K-style
+// tiles) before the tile's data is waited for.
+template <int FMT, int MODE>
+__device__ __forceinline__ float piece_one(const TileRegs<FMT> &t, int b, const ActWave &a)
+{
+    if constexpr (FMT == QG_Q4K) {
+        const ActPlanes p(a);
+        __builtin_amdgcn_sched_barrier(0);
+        return pair_piece<MODE>(t, b, p);
+    } else {
+        const ActWaveCodes c(a);
+        __builtin_amdgcn_sched_barrier(0);
+        return pair_piece<MODE>(t, b, c);
+    }
+}
+
+template <int FMT, int MODE, int SRC, int W, bool DB>
+__global__ __launch_bounds__(64 * W) void gemv1_kernel(const uint8_t *image, int rows, int G, ActIO io,
+                                                       float *__restrict__ out)
+{
+    extern __shared__ __align__(16) float s_piece[];
     using T = TileRegs<FMT>;
     const int g = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool emit = g == 0;
     const uint8_t *gbase = image + (size_t)g * G * T::kBytes;
-    float *s_piece = reinterpret_cast<float *>(lds);
 
-    // this wave's activation blocks (KX of them), then its first weight tile.  The loads are
-    // unconditional (indices clamped into the row) and kept in this order, so that the
-    // quantization waits for the activation loads alone.
-    float4 xv[KX];
-#pragma unroll
-    for (int k = 0; k < KX; k++) {
-        const int b = min(wid + k * W, G - 1);
-        xv[k] = *reinterpret_cast<const float4 *>(x + (size_t)b * 256 + 4 * lane);
-    }
+    // the first block's activations, then its tile: both loads unconditional (a wave past
+    // the last block works on a copy of it and stores nothing), kept in this order
+    const int bf = min(wid, G - 1);
+    ActRaw<SRC> r0 = load_act<SRC, MODE>(io, bf, lane);
     __builtin_amdgcn_sched_barrier(0);
-    T t[2];
-    t[0].load(gbase + (size_t)min(wid, G - 1) * T::kBytes, lane);
-    __builtin_amdgcn_sched_barrier(0);
+    T t0;
+    [[maybe_unused]] T t1;
+    t0.load(gbase + (size_t)bf * T::kBytes, lane);
+    load_fence();
+    ActWave a0 = ready_act<SRC, MODE>(r0, wid, G, lane, emit, io);
 
-    ActWave aw[KX];
-#pragma unroll
-    for (int k = 0; k < KX; k++)
-        aw[k] = quantize_block_in_wave<MODE>(xv[k], wid + k * W, G, lane, g == 0, codes, scales, csums, err_flag);
-
-    if constexpr (KX == 1) {
-        // one block per wave: its codes go to scalar registers before the tile is waited for
-        const ActWaveCodes ac(aw[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (wid < G) s_piece[(size_t)wid * 64 + lane] = pair_piece<MODE>(t[0], wid, ac);
+    // Every use of the first tile is unconditional too, so the compiler cannot sink its loads
+    // below the wait for the activation load.
+    if constexpr (DB) {
+        // blocks wid, wid + W, ...: t0 / t1 alternate, the next block's loads in flight
+        // while this one is computed.  DB means G > W, so every wave has a first block.
+        int b = wid;
+        do {
+            const int b1 = b + W;
+            ActRaw<SRC> r1;
+            if (b1 < G) {
+                r1 = load_act<SRC, MODE>(io, b1, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                t1.load(gbase + (size_t)b1 * T::kBytes, lane);
+                load_fence();
+            }
+            s_piece[(size_t)b * 64 + lane] = piece_one<FMT, MODE>(t0, b, a0);
+            if (b1 >= G) break;
+            const ActWave a1 = ready_act<SRC, MODE>(r1, b1, G, lane, emit, io);
+            const int b2 = b + 2 * W;
+            if (b2 < G) {
+                r0 = load_act<SRC, MODE>(io, b2, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                t0.load(gbase + (size_t)b2 * T::kBytes, lane);
+                load_fence();
+            }
+            s_piece[(size_t)b1 * 64 + lane] = piece_one<FMT, MODE>(t1, b1, a1);
+            if (b2 >= G) break;
+            a0 = ready_act<SRC, MODE>(r0, b2, G, lane, emit, io);
+            b = b2;
+        } while (true);
     } else {
-        // blocks wid + kW in turn; the next tile loads while this one is computed
-#pragma unroll
-        for (int k = 0; k < KX; k++) {
-            const int b = wid + k * W;
-            if (b >= G) break;
-            if (k + 1 < KX && b + W < G) t[(k + 1) & 1].load(gbase + (size_t)(b + W) * T::kBytes, lane);
-            s_piece[(size_t)b * 64 + lane] = pair_piece<MODE>(t[k & 1], b, aw[k]);
-        }
+        // at most one block per wave; a wave past the last block computes a copy and drops it
+        const float p = piece_one<FMT, MODE>(t0, bf, a0);
+        if (wid < G) s_piece[(size_t)wid * 64 + lane] = p;
     }
     __syncthreads();
 
@@ -583,6 +706,52 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const uint8_t *__restri
     }
 }
 
+template <int FMT, int MODE, int SRC, int W, bool DB>
+int launch_one_typed(int64_t rows, int G, const void *image, const ActIO &io, float *out, hipStream_t s)
+{
+    const int64_t groups = (rows + 63) / 64;
+    if (groups > 0x7fffffff) return fail(QG_E_SHAPE, "too many rows: %lld", (long long)rows);
+    const size_t lds = (size_t)G * 64 * sizeof(float);
+    hipEvent_t ev0, ev1;
+    take_timing_events(&ev0, &ev1);
+    if (ev0 && ev1)
+        hipExtLaunchKernelGGL((gemv1_kernel<FMT, MODE, SRC, W, DB>), dim3((unsigned)groups), dim3(64 * W), lds, s,
+                              ev0, ev1, 0, static_cast<const uint8_t *>(image), (int)rows, G, io, out);
+    else
+        hipLaunchKernelGGL((gemv1_kernel<FMT, MODE, SRC, W, DB>), dim3((unsigned)groups), dim3(64 * W), lds, s,
+                           static_cast<const uint8_t *>(image), (int)rows, G, io, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemv launch: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+template <int FMT, int MODE, int SRC>
+int launch_one(int64_t rows, int G, const void *image, const ActIO &io, float *out, hipStream_t s)
+{
+    // waves per workgroup: the tuning knob if set, else one wave per block up to 16; with
+    // more blocks than 16 two tiles per wave (double-buffered), which takes 8-wave groups
+    int w = tuning().waves_per_wg;
+    if (w <= 0) w = G >= 16 ? 16 : G >= 8 ? 8 : 4;
+    if (w > 8 && G > 16) w = 8;
+    if (w >= 16) return launch_one_typed<FMT, MODE, SRC, 16, false>(rows, G, image, io, out, s);
+    if (w >= 8) {
+        if (G > 8) return launch_one_typed<FMT, MODE, SRC, 8, true>(rows, G, image, io, out, s);
+        return launch_one_typed<FMT, MODE, SRC, 8, false>(rows, G, image, io, out, s);
+    }
+    if (G > 4) return launch_one_typed<FMT, MODE, SRC, 4, true>(rows, G, image, io, out, s);
+    return launch_one_typed<FMT, MODE, SRC, 4, false>(rows, G, image, io, out, s);
+}
+
+template <int SRC>
+int launch_one_any(int fmt, int mode, int64_t rows, int G, const void *image, const ActIO &io, float *out,
+                   hipStream_t s)
+{
+    if (fmt == QG_Q4K && mode == QG_PERBLOCK) return launch_one<QG_Q4K, QG_PERBLOCK, SRC>(rows, G, image, io, out, s);
+    if (fmt == QG_Q4K && mode == QG_SUB32) return launch_one<QG_Q4K, QG_SUB32, SRC>(rows, G, image, io, out, s);
+    if (fmt == QG_Q6K && mode == QG_PERBLOCK) return launch_one<QG_Q6K, QG_PERBLOCK, SRC>(rows, G, image, io, out, s);
+    return launch_one<QG_Q6K, QG_SUB32, SRC>(rows, G, image, io, out, s);
+}
+
 // LDS bytes the kernel needs for NC columns
 template <int FMT, int MODE>
 size_t gemv_lds(int G, int nc)
@@ -616,10 +785,7 @@ template <int FMT, int MODE, int NC, int W>
 int launch_db(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
               const qg_act_scale *scales, const int32_t *csums, float *out, hipStream_t s)
 {
-    // 16-wave workgroups are used only with at most one tile per wave: their 128-register
-    // budget does not hold two tiles' loads without spilling
-    if constexpr (W < 16)
-        if (G > W) return launch_typed<FMT, MODE, NC, W, true>(rows, G, ncol, image, codes, scales, csums, out, s);
+    if (G > W) return launch_typed<FMT, MODE, NC, W, true>(rows, G, ncol, image, codes, scales, csums, out, s);
     return launch_typed<FMT, MODE, NC, W, false>(rows, G, ncol, image, codes, scales, csums, out, s);
 }
 
@@ -627,14 +793,10 @@ template <int FMT, int MODE, int NC>
 int launch_w(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
              const qg_act_scale *scales, const int32_t *csums, float *out, hipStream_t s)
 {
-    // waves per workgroup: the tuning knob if set, else one wave per block up to 16 (8 when
-    // several columns share the workgroup, whose registers do not fit 16 waves)
+    // waves per workgroup: the tuning knob if set (16 is taken as 8: several columns'
+    // registers do not fit 16 waves), else 8
     int w = tuning().waves_per_wg;
-    if (w <= 0) w = G >= 16 ? 16 : G >= 8 ? 8 : 4;
-    if (NC > 1 && w > 8) w = 8;
-    if (w > 8 && G > 16) w = 8;
-    if constexpr (NC == 1)
-        if (w >= 16) return launch_db<FMT, MODE, NC, 16>(rows, G, ncol, image, codes, scales, csums, out, s);
+    if (w <= 0 || w > 8) w = 8;
     if (w >= 8) return launch_db<FMT, MODE, NC, 8>(rows, G, ncol, image, codes, scales, csums, out, s);
     return launch_db<FMT, MODE, NC, 4>(rows, G, ncol, image, codes, scales, csums, out, s);
 }
@@ -647,52 +809,16 @@ int launch_nc(int64_t rows, int G, int64_t ncol, const void *image, const int8_t
     auto fits = [&](int nc) { return gemv_lds<FMT, MODE>(G, nc) <= 65536; };
     if (ncol >= 8 && fits(8)) return launch_w<FMT, MODE, 8>(rows, G, ncol, image, codes, scales, csums, out, s);
     if (ncol >= 4 && fits(4)) return launch_w<FMT, MODE, 4>(rows, G, ncol, image, codes, scales, csums, out, s);
-    if (ncol >= 2 && fits(2)) return launch_w<FMT, MODE, 2>(rows, G, ncol, image, codes, scales, csums, out, s);
-    return launch_w<FMT, MODE, 1>(rows, G, ncol, image, codes, scales, csums, out, s);
-}
-
-template <int FMT, int MODE, int W, int KX>
-int launch_fused_typed(int64_t rows, int G, const void *image, const float *x, int8_t *codes, qg_act_scale *scales,
-                       int32_t *csums, int32_t *err_flag, float *out, hipStream_t s)
-{
-    const int64_t groups = (rows + 63) / 64;
-    if (groups > 0x7fffffff) return fail(QG_E_SHAPE, "too many rows: %lld", (long long)rows);
-    const size_t lds = (size_t)G * 64 * sizeof(float);
-    hipEvent_t ev0, ev1;
-    take_timing_events(&ev0, &ev1);
-    if (ev0 && ev1)
-        hipExtLaunchKernelGGL((gemv_fused_kernel<FMT, MODE, W, KX>), dim3((unsigned)groups), dim3(64 * W), lds, s,
-                              ev0, ev1, 0, static_cast<const uint8_t *>(image), (int)rows, G, x, codes, scales, csums,
-                              err_flag, out);
-    else
-        hipLaunchKernelGGL((gemv_fused_kernel<FMT, MODE, W, KX>), dim3((unsigned)groups), dim3(64 * W), lds, s,
-                           static_cast<const uint8_t *>(image), (int)rows, G, x, codes, scales, csums, err_flag, out);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(QG_E_RUNTIME, "fused gemv launch: %s", hipGetErrorString(e));
-    return QG_OK;
-}
-
-template <int FMT, int MODE>
-int launch_fused_w(int64_t rows, int G, const void *image, const float *x, int8_t *codes, qg_act_scale *scales,
-                   int32_t *csums, int32_t *err_flag, float *out, hipStream_t s)
-{
-    // waves per workgroup as in the GEMV; each wave takes at most KX = 8 blocks (G <= 64)
-    int w = tuning().waves_per_wg;
-    if (w <= 0) w = G >= 16 ? 16 : G >= 8 ? 8 : 4;
-    if (w > 8 && G > 16) w = 8;
-    if (w < 8 && G > 8) w = 8;
-#define QG_FUSED(W_, KX_) \
-    launch_fused_typed<FMT, MODE, W_, KX_>(rows, G, image, x, codes, scales, csums, err_flag, out, s)
-    if (w >= 16) return QG_FUSED(16, 1);
-    if (w >= 8) {
-        if (G <= 8) return QG_FUSED(8, 1);
-        if (G <= 16) return QG_FUSED(8, 2);
-        if (G <= 32) return QG_FUSED(8, 4);
-        return QG_FUSED(8, 8);
+    if (fits(2)) return launch_w<FMT, MODE, 2>(rows, G, ncol, image, codes, scales, csums, out, s);
+    // rows too wide for two columns' records: one launch per column
+    const int64_t C = (int64_t)G * 256, nsc = MODE == QG_PERBLOCK ? G : (int64_t)G * 8;
+    for (int64_t c = 0; c < ncol; c++) {
+        const ActIO io{nullptr, codes + c * C, reinterpret_cast<const uint32_t *>(scales + c * nsc), nullptr, nullptr,
+                       nullptr, nullptr};
+        const int st = launch_one<FMT, MODE, SRC_CODES>(rows, G, image, io, out + c * rows, s);
+        if (st != QG_OK) return st;
     }
-    if (G <= 4) return QG_FUSED(4, 1);
-    return QG_FUSED(4, 2);
-#undef QG_FUSED
+    return QG_OK;
 }
 
 }  // namespace
@@ -701,16 +827,9 @@ int launch_gemv_fused(int fmt, int mode, int64_t rows, int64_t cols, const void 
                       int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
                       hipStream_t s)
 {
-    const int G = (int)(cols / 256);
     if (rows == 0) return QG_OK;
-    if (G > kFusedMaxBlocks) return fail(QG_E_SHAPE, "fused gemv: %d blocks per row exceed %d", G, kFusedMaxBlocks);
-    if (fmt == QG_Q4K && mode == QG_PERBLOCK)
-        return launch_fused_w<QG_Q4K, QG_PERBLOCK>(rows, G, image, x, codes, scales, csums, err_flag, out, s);
-    if (fmt == QG_Q4K && mode == QG_SUB32)
-        return launch_fused_w<QG_Q4K, QG_SUB32>(rows, G, image, x, codes, scales, csums, err_flag, out, s);
-    if (fmt == QG_Q6K && mode == QG_PERBLOCK)
-        return launch_fused_w<QG_Q6K, QG_PERBLOCK>(rows, G, image, x, codes, scales, csums, err_flag, out, s);
-    return launch_fused_w<QG_Q6K, QG_SUB32>(rows, G, image, x, codes, scales, csums, err_flag, out, s);
+    const ActIO io{x, nullptr, nullptr, codes, scales, csums, err_flag};
+    return launch_one_any<SRC_F32>(fmt, mode, rows, (int)(cols / 256), image, io, out, s);
 }
 
 int launch_gemv(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, const void *image,
@@ -719,6 +838,10 @@ int launch_gemv(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, con
 {
     if (rows == 0 || ncol == 0) return QG_OK;
     const int G = (int)(cols / 256);
+    if (ncol == 1) {
+        const ActIO io{nullptr, codes, reinterpret_cast<const uint32_t *>(scales), nullptr, nullptr, nullptr, nullptr};
+        return launch_one_any<SRC_CODES>(fmt, mode, rows, G, image, io, out, s);
+    }
     if (fmt == QG_Q4K && mode == QG_PERBLOCK)
         return launch_nc<QG_Q4K, QG_PERBLOCK>(rows, G, ncol, image, codes, scales, csums, out, s);
     if (fmt == QG_Q4K && mode == QG_SUB32)

@@ -215,6 +215,7 @@ constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]: lane ^ 1
 constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]: lane ^ 2
 constexpr int kDppRowMirror = 0x140;    // lane i of a row <- lane 15 - i
 constexpr int kDppHalfMirror = 0x141;   // lane i of a half-row <- lane 7 - i
+constexpr int kDppRowShl4 = 0x104;      // lane i of a row <- lane i + 4 (none for i >= 12: 0)
 
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v)
@@ -302,14 +303,32 @@ __device__ __forceinline__ float piece_q4k_perblock(int C, int O, uint32_t d_dmi
     return r32_sum2(a, b);
 }
 
-// PerBlock, Q4_K-style, when the two block-scale exponents differ by at most 8.  With
-// Dd = sig_d*2^ex_d and Dm = sig_m*2^ex_m, X = C*Dd - O*Dm has at most 45 significant bits,
-// so one fma forms it exactly; times S = m*2^e (8 significant bits) it stays exact in f64;
-// the conversion is the one rounding.  Gives the same bits as piece_q4k_perblock.
+// binary16 bits -> the value as a binary32 (exact: every binary16 is one)
+__device__ __forceinline__ float f16_value(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
+}
+
+// PerBlock, Q4_K-style, when X = C*Dd - O*Dm fits 45 significant bits: one fma forms it
+// exactly, times S = m*2^e (8 significant bits) it stays exact in f64, and the conversion
+// is the one rounding.  Gives the same bits as piece_q4k_perblock.
 __device__ __forceinline__ float piece_q4k_perblock_near(int C, int O, double Dd, double Dm, double S)
 {
     const double X = __builtin_fma((double)C, Dd, -((double)O * Dm));
     return r32_exact_double(X * S);
+}
+
+// Whether piece_q4k_perblock_near applies, from the binary exponents of the two block scales
+// (frexp: value = f * 2^k, f in [0.5, 1)).  A binary16 value with exponent k has its last
+// significant place at 2^(k-11) or above; |C| < 2^25 and |O| < 2^21 (8 sub-blocks of 32
+// codes of at most 127 times 6-bit sub-scales and 4-bit codes, or times 6-bit offsets).  So
+// X spans at most 37 + (kd - km) places when kd >= km and at most max(37, 33 + km - kd)
+// otherwise: 45 or fewer when -12 <= kd - km <= 8.  A zero scale (k = 0) may fail the test;
+// the general combine is exact for every input.
+__device__ __forceinline__ bool q4k_near(float fd, float fm)
+{
+    const int gap = __builtin_amdgcn_frexp_expf(fd) - __builtin_amdgcn_frexp_expf(fm);
+    return gap >= -12 && gap <= 8;
 }
 
 // PerBlock, Q6_K-style: one term R32(m*2^e * d*C); |C| < 2^27 so the product is < 2^46.

@@ -13,10 +13,6 @@ constexpr int kTileRows = 64;     // rows per tile (one 256-element block each)
 constexpr int kTileBytesQ4K = 64 * 144;   // 9216
 constexpr int kTileBytesQ6K = 64 * 210;   // 13440
 
-// widest row (in 256-element blocks) the one-launch quantize + GEMV handles; wider rows
-// take the two-launch path
-constexpr int kFusedMaxBlocks = 64;
-
 // per-thread failure reason
 int fail(int status, const char *fmt, ...);
 
@@ -41,7 +37,7 @@ int launch_gemv(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, con
                 const int8_t *codes, const qg_act_scale *scales, const int32_t *csums, float *out,
                 hipStream_t s);
 
-// one activation row: quantize it and run the GEMV in one launch (cols <= 256 * kFusedMaxBlocks)
+// one activation row: quantize it and run the GEMV in one launch
 int launch_gemv_fused(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const float *x,
                       int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
                       hipStream_t s);

@@ -164,16 +164,15 @@ int qg_gemm_q(int fmt, int mode, int64_t rows, int64_t cols, int64_t n, const vo
               const int8_t *codes, const qg_act_scale *scales, const int32_t *csums, float *out,
               void *stream);
 
-/* Quantize one activation row and run the decode GEMV on it, in one launch where the row
- * has at most 64 blocks (cols <= 16384), else as qg_quantize_act then qg_gemv_q:
+/* Quantize one activation row and run the decode GEMV on it, in one launch:
  *   x       f32 [cols] (device, 16-byte aligned)
  *   codes, scales, csums, err_flag   as qg_quantize_act with n = 1 (codes, scales and csums
  *           required: they receive the quantized row)
  *   image, out   as qg_gemv_q
  * out and the quantized row are bit for bit those of qg_quantize_act followed by qg_gemv_q
  * (the pages' dot of a row with a quantized activation row: "Module numerics", Functions
- * quantize and dot).  In the one-launch form every workgroup quantizes the row itself; the
- * first writes it out.  rows = 0 only quantizes. */
+ * quantize and dot).  Every workgroup quantizes the blocks it needs itself; the first
+ * writes the quantized row out.  rows = 0 only quantizes. */
 int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const float *x,
                      int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
                      void *stream);
