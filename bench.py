@@ -18,6 +18,9 @@ Timing:
     around replays of a graph of kernel-only launches over the same rotated-cold copies (on
     the stream they run on).  The median of single eager launches timed by events the
     launch itself records (hipExtLaunchKernelGGL, qg_time_next_launch) is reported beside it.
+  * measured_ceiling: qg_stream_read, a plain read with the GEMV's load pattern, over the same
+    bytes per launch and rotated copies (what one launch of this size can reach), and over
+    2 GiB (the sustained rate).
   * cpu_baseline: the CPU oracle on the same workload, all rows, fresh activations, for
     about --cpu-seconds of host time, on the host's cores (threads stated).
 
@@ -50,7 +53,9 @@ WRITE_FACTOR = COPY_BYTES / (262144.0 * 1024)
 KERNEL_SOURCES = ("block_format_gemv_amd/csrc/gemv.hip", "block_format_gemv_amd/csrc/qg_device.hpp",
                   "block_format_gemv_amd/csrc/qg_internal.hpp")
 MEASURED_TRAFFIC = {
-    "q4k_ffn_up_14336x4096": {"kernel_sha": "6a75fd51162b73f0", "fetch_kib": 16198.0, "write_kib": 56.0},
+    # (workload, dominant kernel): medians per dispatch, kernel sources hash
+    ("q4k_ffn_up_14336x4096", "fused"): {"kernel_sha": "fc15d83fa511d335", "fetch_kib": 16237.0, "write_kib": 61.0625},
+    ("q4k_ffn_up_14336x4096", "gemv"): {"kernel_sha": "fc15d83fa511d335", "fetch_kib": 16171.5, "write_kib": 56.0},
 }
 
 
@@ -64,8 +69,8 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    t = MEASURED_TRAFFIC.get(workload)
+def measured_traffic(workload: str, kernel: str):
+    t = MEASURED_TRAFFIC.get((workload, kernel))
     if not t or t["kernel_sha"] != kernel_sha():
         return None
     return round(t["fetch_kib"] * 1024 * FETCH_FACTOR + t["write_kib"] * 1024 * WRITE_FACTOR)
@@ -314,6 +319,30 @@ def main():
         extra["gemv_kernel_frac_of_peak"] = round((image_bytes + act_bytes + out_bytes) / (gemv_us * 1e-6) / 1e9
                                                   / HBM_PEAK_GBS, 4)
 
+    # the measured ceiling: a plain streaming read (qg_stream_read, the GEMV's load pattern and
+    # nothing else) of the same bytes per launch over the same rotated copies, and of 2 GiB
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def read_same(i, stream=None):
+        qg.qg_stream_read(images[i % copies], image_bytes, 0x9E3779B9, sink, stream)
+
+    ceil_us = per_call_us(read_same, args.kernel_launches // 4)[0]
+    big = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+
+    def read_big(i, stream=None):
+        qg.qg_stream_read(big, big.numel(), 0x9E3779B9, sink, stream)
+
+    big_us = per_call_us(read_big, 3 * gsteps)[0]
+    del big
+    ceiling = {
+        "kernel": "qg_stream_read",
+        "same_bytes_us": round(ceil_us, 3),
+        "same_bytes_GBs": round(image_bytes / (ceil_us * 1e-6) / 1e9, 1),
+        "same_bytes_frac_of_peak": round(image_bytes / (ceil_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "read_2GiB_GBs": round((2 << 30) / (big_us * 1e-6) / 1e9, 1),
+        "kernel_vs_same_bytes_ceiling": round(ceil_us / k_us, 4),
+    }
+
     # secondary: single eager launches, each bracketed by events the launch itself records
     evs = [(hip.event(), hip.event()) for _ in range(64)]
     torch.cuda.synchronize()
@@ -363,12 +392,13 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload),
+            "traffic": measured_traffic(args.workload, "fused" if fused else "gemv" if ncol == 1 else "gemm"),
             "kernel": "gemv_fused_kernel (qg_quantize_gemv)" if fused else
                       ("gemm_mfma_q4k" if ncol >= 8 and fmt_s == "q4k" and mode == 0 else "gemv_kernel") + " (qg_gemm_q)",
             "algorithmic_bytes_per_launch": algo_bytes,
         },
     }
+    record["measured_ceiling"] = ceiling
     record.update(extra)
     if not args.no_cpu:
         cb, cpu_outs = cpu_baseline(fields, xs, mode, args.cpu_seconds, image_bytes)

@@ -27,7 +27,7 @@ BLOCK = 256
 MAX_COLS = 32768
 
 EXPORTS = ("qg_reads", "qg_image_bytes", "qg_pack_q4k", "qg_pack_q6k", "qg_quantize_act", "qg_gemv_q",
-           "qg_gemm_q", "qg_quantize_gemv", "qg_block_sums", "qg_set_tuning", "qg_time_next_launch", "qg_last_error", "qg_version")
+           "qg_gemm_q", "qg_quantize_gemv", "qg_block_sums", "qg_stream_read", "qg_set_tuning", "qg_time_next_launch", "qg_last_error", "qg_version")
 
 
 class QGError(RuntimeError):
@@ -52,6 +52,7 @@ def _load():
     L.qg_gemm_q.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]
     L.qg_quantize_gemv.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     L.qg_block_sums.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
+    L.qg_stream_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_uint32, vp, vp]
     L.qg_set_tuning.argtypes = [i32, i64]
     L.qg_time_next_launch.argtypes = [vp, vp]
     L.qg_last_error.restype = ctypes.c_char_p
@@ -183,6 +184,13 @@ def qg_block_sums(fmt, rows, cols, image, codes, csum_out, osum_out=None, stream
             _need(osum_out, 4 * rows * (cols // 32), "osum_out")
     _check(_lib.qg_block_sums(fmt, rows, cols, _dptr(image), _dptr(codes), _dptr(csum_out), _dptr(osum_out),
                               _stream(stream)))
+
+
+def qg_stream_read(buf, nbytes: int, magic: int, sink, stream=None) -> None:
+    """Diagnostic streaming read (the measured ceiling); see qgemv.h."""
+    _need(buf, nbytes, "buf")
+    _need(sink, 4, "sink")
+    _check(_lib.qg_stream_read(_dptr(buf), nbytes, magic & 0xFFFFFFFF, _dptr(sink), _stream(stream)))
 
 
 def qg_set_tuning(key: int, value: int) -> None:

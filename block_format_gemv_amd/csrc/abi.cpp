@@ -210,6 +210,16 @@ int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *
     return launch_quantize(mode, QG_BLOCK, 1, cols, x, codes, scales, csums, err_flag, s);
 }
 
+int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink, void *stream)
+{
+    const char *who = "qg_stream_read";
+    int st;
+    if (bytes < 1024) return QG_OK;
+    if ((st = check_ptr(who, "buf", buf, 16))) return st;
+    if ((st = check_ptr(who, "sink", sink, 4))) return st;
+    return launch_stream_read(buf, bytes, magic, sink, static_cast<hipStream_t>(stream));
+}
+
 int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
                   int32_t *csum_out, int32_t *osum_out, void *stream)
 {

@@ -45,6 +45,10 @@ int launch_gemv_fused(int fmt, int mode, int64_t rows, int64_t cols, const void 
 int launch_gemm_mfma(int64_t rows, int64_t cols, int64_t ncol, const void *image, const int8_t *codes,
                      const qg_act_scale *scales, float *out, hipStream_t s);
 
+// diagnostic: read `bytes` (a multiple of 1 KiB is read; the rest ignored) with the GEMV's
+// load pattern; sink[0] is written only if some lane's XOR of what it read equals magic
+int launch_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink, hipStream_t s);
+
 int launch_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
                       int32_t *csum_out, int32_t *osum_out, hipStream_t s);
 

@@ -187,6 +187,16 @@ int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *
 int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
                   int32_t *csum_out, int32_t *osum_out, void *stream);
 
+/* Diagnostic, not part of the method: reads the first floor(bytes / 1024) KiB of buf once
+ * with the GEMV's load pattern (each wave nine contiguous 1 KiB chunks, non-temporal 16-byte
+ * loads) and nothing else, to measure the streaming ceiling a launch of that size reaches.
+ *   buf    device, 16-byte aligned; bytes < 1024 launches nothing
+ *   sink   device uint32 [1]; written (with magic) only if, for some lane, the XOR of the
+ *          16-byte pieces it read equals magic: a dependence that keeps the loads from
+ *          being optimised away (an all-zero buffer never writes a nonzero magic)
+ * Honours qg_time_next_launch. */
+int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink, void *stream);
+
 /* Speed-only tuning knobs; they never change output bits.
  *   QG_TUNE_WAVES_PER_WG  waves per GEMV workgroup, splitting a 64-row group's blocks:
  *                         4, 8 or 16 (0 = one wave per block, at most 16).  16 applies
@@ -198,8 +208,8 @@ int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const 
 enum { QG_TUNE_WAVES_PER_WG = 1, QG_TUNE_MFMA_MIN_COLS = 2, QG_TUNE_MFMA_COL_TILES = 3 };
 int qg_set_tuning(int key, int64_t value);
 
-/* Measurement hook: the next qg_gemv_q / qg_gemm_q / qg_quantize_gemv call made on this
- * thread launches its (GEMV or GEMM) kernel with hipExtLaunchKernelGGL, which records start_event as the kernel begins and
+/* Measurement hook: the next qg_gemv_q / qg_gemm_q / qg_quantize_gemv / qg_stream_read call
+ * made on this thread launches its (GEMV, GEMM or read) kernel with hipExtLaunchKernelGGL, which records start_event as the kernel begins and
  * stop_event as it ends (hipEvent_t handles owned by the caller; both NULL cancels).
  * Later launches are not timed.  Changes no output bits. */
 int qg_time_next_launch(void *start_event, void *stop_event);

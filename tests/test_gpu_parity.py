@@ -466,3 +466,17 @@ def test_fused_infinity_flag_and_zero_rows(qg):
     xg = gen.act_normal(1, 1024, 43)
     qg.qg_quantize_gemv(M.fmt, 0, 0, 1024, None, dev(xg.reshape(-1)), act.codes, act.scales, act.csums, None, None)
     assert np.array_equal(act.codes.cpu().numpy(), oracle.quantize(xg, 0)[0])
+
+
+def test_stream_read_diagnostic(qg):
+    """The measured-ceiling read: zeros never meet a nonzero magic; a 16-byte piece at the
+    right place does (lane 0 of the first wave reads bytes 0..15 of every chunk it owns)."""
+    buf = torch.zeros(9 * 1024 * 3 + 512, dtype=torch.uint8, device=DEV)
+    sink = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    qg.qg_stream_read(buf, buf.numel(), 0x1234, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == -1
+    buf[0:4] = torch.tensor([0x34, 0x12, 0, 0], dtype=torch.uint8, device=DEV)
+    qg.qg_stream_read(buf, buf.numel(), 0x1234, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0x1234
