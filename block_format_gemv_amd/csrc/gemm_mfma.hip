@@ -1,5 +1,5 @@
 // gemm_mfma.hip -- batched-column GEMM of a Q4_K-style image under PerBlock scaling on the
-// int8 matrix cores (v_mfma_i32_16x16x64_i8), for 16 or more activation columns.
+// int8 matrix cores (v_mfma_i32_16x16x64_i8).
 //
 // The method's per-block integer sums ("Module lane", Functions block_sums) are a dense
 // contraction once there are enough columns: per 256-element block,
@@ -14,6 +14,13 @@
 //
 // Operand roles: the MFMA's M dimension is 16 activation columns, N is 16 weight rows, so
 // lane l of a result owns weight row l%16 and activation columns 4*(l/16) .. +3.
+//
+// The shared-operand form (48 columns and more): a workgroup owns one 64-row group and 16*CW
+// columns: wave (r, c) computes rows 16r..16r+15
+// against columns 16c..16c+15.  Per block the workgroup builds, once, the weight operands of
+// its 64 rows (wave (r, c) prepares the 64-element steps c, c+CW, .. of row quarter r) and the
+// activation operands of its columns in an LDS stage; every wave reads what it needs from
+// there.  Two stages alternate, and each thread's global loads run two blocks ahead.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -36,16 +43,228 @@ __device__ __forceinline__ int bytes_times(uint32_t q, uint32_t k)
     return __builtin_bit_cast(int, a * b);
 }
 
+// 12-bit (sc | mn << 6) field of sub-block j (0..7, any value) of the 96-bit string (y, z, w)
+__device__ __forceinline__ uint32_t field_at(uint32_t y, uint32_t z, uint32_t w, int j)
+{
+    const int bit = 12 * j;                 // 0 .. 84
+    const int word = bit >> 5, off = bit & 31;
+    const uint32_t lo = word == 0 ? y : word == 1 ? z : w;
+    const uint32_t hi = word == 0 ? z : w;  // word 2 never straddles (84 + 12 <= 96)
+    return (uint32_t)((((uint64_t)hi << 32) | lo) >> off) & 0xFFFu;
+}
+
+// One LDS stage (bytes).
+template <int CW>
+struct Stage {
+    static constexpr int kBH = 0;                          // uint4 [4 row quarters][4 steps][64 lanes]: h*q
+    static constexpr int kBL = kBH + 4 * 4 * 64 * 16;      // uint4 [4][4][64]: l*q
+    static constexpr int kBO = kBL + 4 * 4 * 64 * 16;      // uint32 [4][4][64]: mn repeated
+    static constexpr int kA = kBO + 4 * 4 * 64 * 4;        // uint4 [CW][4 steps][64 lanes]: activation codes
+    static constexpr int kS = kA + CW * 4 * 64 * 16;       // double [16*CW]: activation scale m*2^e
+    static constexpr int kW = kS + 16 * CW * 8;            // uint32 [16*CW]: qg_act_scale words
+    static constexpr int kM = kW + 16 * CW * 4;            // uint32 [64]: d | dmin << 16 per row
+    static constexpr int kBytes = (kM + 64 * 4 + 15) / 16 * 16;
+};
+
+// What one thread loads for one block, two blocks ahead of its use.
+template <int CW>
+struct Pref {
+    uint4 ch[4 / CW];   // code chunk of each step this wave prepares
+    uint4 meta;         // its row's d, dmin and sub-block fields
+    uint4 a;            // 16 activation codes (its share of the stage's operands)
+    uint32_t scw;       // a column's qg_act_scale word (used by threads < 16*CW)
+};
+
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// float ftz through the class test: a subnormal becomes a zero of its sign
+__device__ __forceinline__ float ftz_c(float x)
+{
+    const bool sub = __builtin_amdgcn_classf(x, 0x090);    // negative or positive subnormal (binary32 test)
+    return sub ? __uint_as_float(__float_as_uint(x) & 0x80000000u) : x;
+}
+
+// grid: x = 64-row group, y = batch of 16*CW activation columns
+template <int CW>
+__global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, int rows, int G,
+                                                          const int8_t *__restrict__ codes,
+                                                          const uint32_t *__restrict__ scw, int ncol,
+                                                          float *__restrict__ out)
+{
+    using St = Stage<CW>;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int C = G * 256;
+    const int g = blockIdx.x;
+    const int colbase = blockIdx.y * 16 * CW;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = wid & 3;                 // row quarter
+    const int c = wid >> 2;                // column tile
+    const int n = lane & 15;               // weight row within the quarter / activation column within the tile
+    const int grp = lane >> 4;             // K group (16 of each 64-element step)
+    const int trow = 16 * r + n;           // row within the 64-row tile
+
+    // this thread's share of the activation operands: (column tile ta, step pa, lane la)
+    const int ta = tid >> 8, pa = (tid >> 6) & 3, la = tid & 63;
+    const int acol = min(colbase + 16 * ta + (la & 15), ncol - 1);
+    const int8_t *abase = codes + (size_t)acol * C + 64 * pa + 16 * (la >> 4);
+    const int scol = min(colbase + min(tid, 16 * CW - 1), ncol - 1);   // every thread loads one (in bounds)
+    const uint8_t *gbase = image + (size_t)g * G * kTileBytesQ4K;
+
+    auto load = [&](Pref<CW> &pf, int b) {
+        const uint8_t *tile = gbase + (size_t)b * kTileBytesQ4K;
+#pragma unroll
+        for (int k = 0; k < 4 / CW; k++) {
+            const int p = c + k * CW;
+            pf.ch[k] = ld16(tile + 1024 * (2 * p + (grp >> 1)) + 16 * trow);
+        }
+        pf.meta = ld16(tile + 8192 + 16 * trow);
+        pf.a = ld16(abase + (size_t)b * 256);
+        pf.scw = scw[(size_t)scol * G + b];
+    };
+
+    // prepare this wave's weight steps and this thread's activation share into stage st
+    auto stage_write = [&](const Pref<CW> &pf, unsigned char *st) {
+#pragma unroll
+        for (int k = 0; k < 4 / CW; k++) {
+            const int p = c + k * CW;
+            const uint32_t f = field_at(pf.meta.y, pf.meta.z, pf.meta.w, 2 * p + (grp >> 1));
+            const uint32_t sc = f & 63u, hi = sc >> 3, lo = sc & 7u, mn = f >> 6;
+            const int sh = 4 * (grp & 1);     // low nibbles: elements 0..15, high: 16..31
+            const uint4 ch = pf.ch[k];
+            const uint32_t q0 = (ch.x >> sh) & 0x0F0F0F0Fu, q1 = (ch.y >> sh) & 0x0F0F0F0Fu;
+            const uint32_t q2 = (ch.z >> sh) & 0x0F0F0F0Fu, q3 = (ch.w >> sh) & 0x0F0F0F0Fu;
+            const int slot = (r * 4 + p) * 64 + lane;
+            reinterpret_cast<uint4 *>(st + St::kBH)[slot] =
+                make_uint4(bytes_times(q0, hi), bytes_times(q1, hi), bytes_times(q2, hi), bytes_times(q3, hi));
+            reinterpret_cast<uint4 *>(st + St::kBL)[slot] =
+                make_uint4(bytes_times(q0, lo), bytes_times(q1, lo), bytes_times(q2, lo), bytes_times(q3, lo));
+            reinterpret_cast<uint32_t *>(st + St::kBO)[slot] = mn * 0x01010101u;
+        }
+        if (c == 0 && grp == 0) reinterpret_cast<uint32_t *>(st + St::kM)[trow] = pf.meta.x;
+        reinterpret_cast<uint4 *>(st + St::kA)[(ta * 4 + pa) * 64 + la] = pf.a;
+        if (tid < 16 * CW) {
+            reinterpret_cast<double *>(st + St::kS)[tid] =
+                __builtin_ldexp((double)((pf.scw >> 16) & 0xFFu), (int)(int16_t)(pf.scw & 0xFFFFu));
+            reinterpret_cast<uint32_t *>(st + St::kW)[tid] = pf.scw;
+        }
+    };
+
+    float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    // the block's integer sums on the matrix cores, then its combine into the row sums
+    auto compute = [&](const unsigned char *st) {
+        v4i acc_h = {0, 0, 0, 0}, acc_l = {0, 0, 0, 0}, acc_o = {0, 0, 0, 0};
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            const int slot = (r * 4 + p) * 64 + lane;
+            const v4i A = reinterpret_cast<const v4i *>(st + St::kA)[(c * 4 + p) * 64 + lane];
+            const v4i Bh = reinterpret_cast<const v4i *>(st + St::kBH)[slot];
+            const v4i Bl = reinterpret_cast<const v4i *>(st + St::kBL)[slot];
+            const int bo = reinterpret_cast<const int *>(st + St::kBO)[slot];
+            const v4i Bo = {bo, bo, bo, bo};
+            acc_h = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bh, acc_h, 0, 0, 0);
+            acc_l = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bl, acc_l, 0, 0, 0);
+            acc_o = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bo, acc_o, 0, 0, 0);
+        }
+        const uint32_t dd = reinterpret_cast<const uint32_t *>(st + St::kM)[trow];
+        const float fd = f16_value(dd), fm = f16_value(dd >> 16);
+        const bool near = q4k_near(fd, fm);
+        const double Dd = (double)fd, Dm = (double)fm;
+        const double *S = reinterpret_cast<const double *>(st + St::kS) + 16 * c + 4 * grp;
+        if (__all(near)) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int Cb = 8 * acc_h[i] + acc_l[i];
+                const double X = __builtin_fma((double)Cb, Dd, -((double)acc_o[i] * Dm));
+                const float piece = ftz_c((float)(X * S[i] + 0.0));   // + 0.0: an exact zero is +0
+                y[i] = ftz_c(y[i] + piece);
+            }
+        } else {
+            const uint32_t *W = reinterpret_cast<const uint32_t *>(st + St::kW) + 16 * c + 4 * grp;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int Cb = 8 * acc_h[i] + acc_l[i];
+                float piece;
+                if (near) {
+                    piece = piece_q4k_perblock_near(Cb, acc_o[i], Dd, Dm, S[i]);
+                } else {
+                    const int m = (int)((W[i] >> 16) & 0xFFu);
+                    const int e = (int)(int16_t)(W[i] & 0xFFFFu);
+                    piece = piece_q4k_perblock(Cb, acc_o[i], dd, m, e);
+                }
+                y[i] = fadd_ftz(y[i], piece);
+            }
+        }
+    };
+
+    unsigned char *st0 = lds, *st1 = lds + St::kBytes;
+    Pref<CW> p0, p1;
+    load(p0, 0);
+    if (G > 1) load(p1, 1);
+    stage_write(p0, st0);
+    __syncthreads();
+    for (int b = 0; b < G; b += 2) {
+        // block b is in stage 0; block b+1's loads are in flight in p1
+        if (b + 2 < G) load(p0, b + 2);
+        compute(st0);
+        if (b + 1 < G) stage_write(p1, st1);
+        __syncthreads();
+        if (b + 1 >= G) break;
+        if (b + 3 < G) load(p1, b + 3);
+        compute(st1);
+        if (b + 2 < G) stage_write(p0, st0);
+        __syncthreads();
+    }
+
+    const int64_t row = (int64_t)g * 64 + trow;
+    if (row < rows) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int col = colbase + 16 * c + 4 * grp + i;
+            if (col < ncol) out[(int64_t)col * rows + row] = canon_nan(y[i]);
+        }
+    }
+}
+
+template <int CW>
+int launch_cw(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes, const qg_act_scale *scales,
+              float *out, hipStream_t s)
+{
+    const int64_t groups = (rows + 63) / 64;
+    const dim3 grid((unsigned)groups, (unsigned)((ncol + 16 * CW - 1) / (16 * CW)));
+    const size_t lds = 2 * (size_t)Stage<CW>::kBytes;   // above 64 KiB: gfx950 gives a workgroup up to 160 KiB
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_mfma_q4k<CW>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)attr;   // a refusal shows up as a launch error below
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(scales);
+    hipEvent_t ev0, ev1;
+    take_timing_events(&ev0, &ev1);
+    if (ev0 && ev1)
+        hipExtLaunchKernelGGL(gemm_mfma_q4k<CW>, grid, dim3(256 * CW), lds, s, ev0, ev1, 0,
+                              static_cast<const uint8_t *>(image), (int)rows, G, codes, w, (int)ncol, out);
+    else
+        hipLaunchKernelGGL(gemm_mfma_q4k<CW>, grid, dim3(256 * CW), lds, s, static_cast<const uint8_t *>(image),
+                           (int)rows, G, codes, w, (int)ncol, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemm (matrix cores) launch: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
 template <int I>
-__device__ __forceinline__ uint32_t field(uint32_t y, uint32_t z, uint32_t w)
+__device__ __forceinline__ uint32_t field_s(uint32_t y, uint32_t z, uint32_t w)
 {
     if constexpr (I < 5) return (uint32_t)(((uint64_t)y | ((uint64_t)z << 32)) >> (12 * I)) & 0xFFFu;
     else return (uint32_t)(((uint64_t)z | ((uint64_t)w << 32)) >> (12 * I - 32)) & 0xFFFu;
 }
 
-// grid: x = 64-row group, y = batch of 16*CT activation columns; 4 waves, wave w = rows 16w..16w+15
+// The per-wave form, for fewer columns: each wave computes 16 rows x 16*CT columns over all
+// blocks from its own registers (weights and activation operands loaded per wave, two
+// register stages).  grid: x = 64-row group, y = batch of 16*CT activation columns; 4 waves,
+// wave w = rows 16w..16w+15
 template <int CT>
-__global__ __launch_bounds__(256) void gemm_mfma_q4k(const uint8_t *__restrict__ image, int rows, int G,
+__global__ __launch_bounds__(256) void gemm_mfma_wave(const uint8_t *__restrict__ image, int rows, int G,
                                                      const int8_t *__restrict__ codes,
                                                      const qg_act_scale *__restrict__ scales, int ncol,
                                                      float *__restrict__ out)
@@ -117,14 +336,14 @@ __global__ __launch_bounds__(256) void gemm_mfma_q4k(const uint8_t *__restrict__
     auto compute = [&](const Stage &st, int b) {
         const uint4 meta = st.meta;
         uint32_t f[8];
-        f[0] = field<0>(meta.y, meta.z, meta.w);
-        f[1] = field<1>(meta.y, meta.z, meta.w);
-        f[2] = field<2>(meta.y, meta.z, meta.w);
-        f[3] = field<3>(meta.y, meta.z, meta.w);
-        f[4] = field<4>(meta.y, meta.z, meta.w);
-        f[5] = field<5>(meta.y, meta.z, meta.w);
-        f[6] = field<6>(meta.y, meta.z, meta.w);
-        f[7] = field<7>(meta.y, meta.z, meta.w);
+        f[0] = field_s<0>(meta.y, meta.z, meta.w);
+        f[1] = field_s<1>(meta.y, meta.z, meta.w);
+        f[2] = field_s<2>(meta.y, meta.z, meta.w);
+        f[3] = field_s<3>(meta.y, meta.z, meta.w);
+        f[4] = field_s<4>(meta.y, meta.z, meta.w);
+        f[5] = field_s<5>(meta.y, meta.z, meta.w);
+        f[6] = field_s<6>(meta.y, meta.z, meta.w);
+        f[7] = field_s<7>(meta.y, meta.z, meta.w);
 
         v4i acc_h[CT], acc_l[CT], acc_o[CT];
 #pragma unroll
@@ -214,7 +433,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_q4k(const uint8_t *__restrict__
 }
 
 template <int CT>
-int launch_ct(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes, const qg_act_scale *scales,
+int launch_wave(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes, const qg_act_scale *scales,
               float *out, hipStream_t s)
 {
     const int64_t groups = (rows + 63) / 64;
@@ -223,10 +442,10 @@ int launch_ct(int64_t rows, int G, int64_t ncol, const void *image, const int8_t
     hipEvent_t ev0, ev1;
     take_timing_events(&ev0, &ev1);
     if (ev0 && ev1)
-        hipExtLaunchKernelGGL(gemm_mfma_q4k<CT>, grid, dim3(256), lds, s, ev0, ev1, 0,
+        hipExtLaunchKernelGGL(gemm_mfma_wave<CT>, grid, dim3(256), lds, s, ev0, ev1, 0,
                               static_cast<const uint8_t *>(image), (int)rows, G, codes, scales, (int)ncol, out);
     else
-        hipLaunchKernelGGL(gemm_mfma_q4k<CT>, grid, dim3(256), lds, s, static_cast<const uint8_t *>(image), (int)rows,
+        hipLaunchKernelGGL(gemm_mfma_wave<CT>, grid, dim3(256), lds, s, static_cast<const uint8_t *>(image), (int)rows,
                            G, codes, scales, (int)ncol, out);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemm (matrix cores) launch: %s", hipGetErrorString(e));
@@ -239,11 +458,14 @@ int launch_gemm_mfma(int64_t rows, int64_t cols, int64_t ncol, const void *image
                      const qg_act_scale *scales, float *out, hipStream_t s)
 {
     const int G = (int)(cols / 256);
-    int ct = tuning().mfma_col_tiles;
-    if (ct <= 0) ct = ncol >= 64 ? 2 : 1;
-    if (ct >= 4) return launch_ct<4>(rows, G, ncol, image, codes, scales, out, s);
-    if (ct >= 2) return launch_ct<2>(rows, G, ncol, image, codes, scales, out, s);
-    return launch_ct<1>(rows, G, ncol, image, codes, scales, out, s);
+    // the tuning knob selects the shared-operand form with that many column tiles; by default
+    // it takes 48 columns and more (64 per workgroup), the per-wave form the rest
+    const int cw = tuning().mfma_col_tiles;
+    if (cw >= 4 || (cw <= 0 && ncol >= 48)) return launch_cw<4>(rows, G, ncol, image, codes, scales, out, s);
+    if (cw == 2) return launch_cw<2>(rows, G, ncol, image, codes, scales, out, s);
+    if (cw == 1) return launch_cw<1>(rows, G, ncol, image, codes, scales, out, s);
+    if (ncol >= 32) return launch_wave<2>(rows, G, ncol, image, codes, scales, out, s);
+    return launch_wave<1>(rows, G, ncol, image, codes, scales, out, s);
 }
 
 }  // namespace qg

@@ -204,7 +204,9 @@ int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink
  *   QG_TUNE_MFMA_MIN_COLS number of columns from which qg_gemm_q on a Q4_K PerBlock matrix
  *                         runs on the int8 matrix cores, columns padded to 16 (0 = 8;
  *                         above 65535 = never)
- *   QG_TUNE_MFMA_COL_TILES 16-column tiles per matrix-core workgroup: 1, 2 or 4 (0 = derived) */
+ *   QG_TUNE_MFMA_COL_TILES 1, 2 or 4: the matrix-core GEMM in its shared-operand form with that
+ *                         many 16-column tiles per workgroup; 0 = derived (that form with 4 tiles
+ *                         from 48 columns, below that a per-wave form) */
 enum { QG_TUNE_WAVES_PER_WG = 1, QG_TUNE_MFMA_MIN_COLS = 2, QG_TUNE_MFMA_COL_TILES = 3 };
 int qg_set_tuning(int key, int64_t value);
 

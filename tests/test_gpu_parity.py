@@ -367,7 +367,7 @@ def test_matrix_core_gemm_matches_oracle(qg, ncol):
     want = oracle.gemm(f, c, m, e, 0).reshape(ncol, 130)
     try:
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 1)                # matrix cores for any column count
-        for ct in (1, 2, 4):
+        for ct in (0, 1, 2, 4):                                     # 0: the default form for this count
             qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, ct)
             say("matrix-core gemm", ncol, "column tiles", ct)
             out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
