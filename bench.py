@@ -77,8 +77,11 @@ def measured_traffic(workload: str, kernel: str):
 METRIC = "quantized GEMV weight-stream HBM GB/s (% of peak) and rows/s at 1 GPU"
 
 WORKLOADS = {
-    # name: (format, rows, cols, scaling, columns)
+    # name: (format, rows, cols, scaling, columns); rows a tuple = several matrices (named by
+    # workloads.gen.llama_q4k) sharing one activation row in one launch
     "q4k_ffn_up_14336x4096": ("q4k", 14336, 4096, 0, 1),
+    "q4k_ffn_gate_up_2x14336x4096": ("q4k", (("gate", 14336), ("ffn", 14336)), 4096, 0, 1),
+    "q4k_attn_qkv_6144x4096": ("q4k", (("attn", 4096), ("k", 1024), ("v", 1024)), 4096, 0, 1),
     "q4k_attn_4096x4096": ("q4k", 4096, 4096, 0, 1),
     "q6k_output_128256x4096": ("q6k", 128256, 4096, 0, 1),
     "q4k_sub32_14336x4096": ("q4k", 14336, 4096, 1, 1),
@@ -146,13 +149,16 @@ class Hip:
 
 
 def make_inputs(wl, n_act):
+    """(list of matrices' fields, activation rows)"""
     from workloads import gen
 
     fmt, rows, cols, mode, ncol = wl
-    if fmt == "q4k":
-        fields = gen.q4k_fields(rows, cols, gen.SEED_ATTN_W if rows == 4096 else gen.SEED_FFN_W)
+    if isinstance(rows, tuple):
+        fields = [gen.llama_q4k(name) for name, _ in rows]
+    elif fmt == "q4k":
+        fields = [gen.q4k_fields(rows, cols, gen.SEED_ATTN_W if rows == 4096 else gen.SEED_FFN_W)]
     else:
-        fields, _ = gen.output_q6k()
+        fields = [gen.output_q6k()[0]]
     if ncol > 1:
         xs = [gen.act_normal(ncol, cols, gen.SEED_BATCH_X + ncol + 1000 * k) for k in range(n_act)]
     elif mode == 1:
@@ -164,7 +170,7 @@ def make_inputs(wl, n_act):
     return fields, xs
 
 
-def cpu_baseline(fields, xs, mode, seconds, image_bytes):
+def cpu_baseline(mats, xs, mode, seconds, image_bytes):
     import oracle
 
     try:
@@ -179,20 +185,21 @@ def cpu_baseline(fields, xs, mode, seconds, image_bytes):
     while True:
         x = xs[steps % len(xs)]
         c, m, e, _ = oracle.quantize(x, mode)
-        out = oracle.gemm(fields, c, m, e, mode)
+        out = np.concatenate([oracle.gemm(f, c, m, e, mode).reshape(xs[0].shape[0], -1) for f in mats], axis=1)
         if steps < 2:
             outs.append(out)
         steps += 1
         dt = time.perf_counter() - t0
         if dt >= seconds:
             break
-    rows = fields["rows"] * xs[0].shape[0]
+    total_rows = sum(f["rows"] for f in mats)
+    rows = total_rows * xs[0].shape[0]
     return {
         "value": round(steps * image_bytes / dt / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{steps} whole steps (quantize + all {fields['rows']} rows x {xs[0].shape[0]} column(s)) "
+        "sample": f"{steps} whole steps (quantize + all {total_rows} rows x {xs[0].shape[0]} column(s)) "
                   f"of the same workload with fresh activations, {dt:.1f} s",
         "rows_per_s": round(steps * rows / dt, 1),
     }, outs
@@ -212,25 +219,37 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = WORKLOADS[args.workload]
-    fmt_s, rows, cols, mode, ncol = wl
+    fmt_s, _, cols, mode, ncol = wl
     fmt = qg.FMT_CODES[fmt_s]
     dev = torch.device("cuda:0")
     hip = Hip()
 
     n_act = 64
-    fields, xs = make_inputs(wl, n_act)
-    img_host = qg.pack(fields)
-    image_bytes = img_host.nbytes
+    mats, xs = make_inputs(wl, n_act)
+    nmat = len(mats)
+    mrows = [int(f["rows"]) for f in mats]
+    rows = sum(mrows)
+    hosts = [qg.pack(f) for f in mats]
+    sizes = [h.nbytes for h in hosts]
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    image_bytes = int(offs[-1])
     copies = 1 if args.warm else max(1, int(np.ceil(args.cold_bytes / image_bytes)))
-    base = torch.from_numpy(img_host).to(dev)
-    images = [base] + [base.clone() for _ in range(copies - 1)]
+    # each copy is one buffer holding the matrices back to back (image sizes are multiples of 16)
+    base = torch.from_numpy(np.concatenate(hosts)).to(dev)
+    bufs = [base] + [base.clone() for _ in range(copies - 1)]
+    images = [[b[int(offs[m]):int(offs[m + 1])] for m in range(nmat)] for b in bufs]
     x_dev = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in xs]
     slots = max(copies, 16)
     acts = [qg.alloc_act(ncol, cols, mode, dev) for _ in range(slots)]
     outs = [torch.empty((ncol, rows), dtype=torch.float32, device=dev) for _ in range(slots)]
+    # per-matrix output views (one column): out[0, row offset of matrix m ...]
+    ro = np.concatenate([[0], np.cumsum(mrows)]).astype(np.int64)
+    mouts = [[o.view(-1)[int(ro[m]):int(ro[m + 1])] for m in range(nmat)] for o in outs]
     act_bytes = ncol * (cols + 4 * qg._nsc(mode, cols) + 4 * (cols // 16))
     out_bytes = 4 * ncol * rows
     fused = ncol == 1 and not args.two_launch
+    if nmat > 1 and ncol != 1:
+        raise SystemExit("several matrices are benchmarked with one activation column")
 
     def quantize(i, stream=None):
         a = acts[i % slots]
@@ -238,18 +257,34 @@ def main():
 
     def multiply(i, stream=None):
         a = acts[i % slots]
-        qg.qg_gemm_q(fmt, mode, rows, cols, ncol, images[i % copies], a.codes, a.scales, a.csums,
-                     outs[i % slots], stream)
+        if nmat > 1:
+            qg.qg_gemv_q_multi(fmt, mode, mrows, cols, images[i % copies], a.codes, a.scales, a.csums,
+                               mouts[i % slots], stream)
+        else:
+            qg.qg_gemm_q(fmt, mode, rows, cols, ncol, images[i % copies][0], a.codes, a.scales, a.csums,
+                         outs[i % slots], stream)
 
     def fused_call(i, stream=None):
         a = acts[i % slots]
-        qg.qg_quantize_gemv(fmt, mode, rows, cols, images[i % copies], x_dev[i % n_act], a.codes, a.scales,
-                            a.csums, None, outs[i % slots], stream)
+        if nmat > 1:
+            qg.qg_quantize_gemv_multi(fmt, mode, mrows, cols, images[i % copies], x_dev[i % n_act], a.codes,
+                                      a.scales, a.csums, None, mouts[i % slots], stream)
+        else:
+            qg.qg_quantize_gemv(fmt, mode, rows, cols, images[i % copies][0], x_dev[i % n_act], a.codes, a.scales,
+                                a.csums, None, outs[i % slots], stream)
 
     def two_launch(i, stream=None):
         quantize(i, stream)
         multiply(i, stream)
 
+    if ncol == 1:
+        kernel_label = ("gemv1_kernel<..., SRC_F32> (one-launch quantize + GEMV)" if fused
+                        else "gemv1_kernel<..., SRC_CODES> (GEMV of a quantized row)")
+    elif fmt_s == "q4k" and mode == 0 and ncol >= 8:
+        kernel_label = "gemm_mfma_q4k (matrix cores, shared operands)" if ncol >= 48 else \
+            "gemm_mfma_wave (matrix cores, per wave)"
+    else:
+        kernel_label = "gemv_kernel (several columns)"
     step = fused_call if fused else two_launch
     # the step's dominant kernel: the fused kernel (reads x, writes the quantized row once)
     # or the GEMV/GEMM kernel (reads the quantized row)
@@ -324,7 +359,7 @@ def main():
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def read_same(i, stream=None):
-        qg.qg_stream_read(images[i % copies], image_bytes, 0x9E3779B9, sink, stream)
+        qg.qg_stream_read(bufs[i % copies], image_bytes, 0x9E3779B9, sink, stream)
 
     ceil_us = per_call_us(read_same, args.kernel_launches // 4)[0]
     big = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
@@ -372,13 +407,15 @@ def main():
         "config": {
             "workload": args.workload,
             "format": fmt_s,
-            "rows": rows,
+            "rows": rows if nmat == 1 else mrows,
+            "matrices": nmat,
             "cols": cols,
             "act_scaling": "perblock" if mode == 0 else "sub32",
             "columns": ncol,
             "weights": "cold, rotating over %d copies (%.0f MB)" % (copies, copies * image_bytes / 1e6)
                        if copies > 1 else "warm, one copy (cache-resident)",
-            "step": ("qg_quantize_gemv (one launch)" if fused else "qg_quantize_act + qg_gemm_q")
+            "step": (("qg_quantize_gemv_multi" if nmat > 1 else "qg_quantize_gemv") + " (one launch)" if fused
+                     else "qg_quantize_act + " + ("qg_gemv_q_multi" if nmat > 1 else "qg_gemm_q"))
                     + ", HIP graph replay",
         },
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -393,17 +430,16 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(args.workload, "fused" if fused else "gemv" if ncol == 1 else "gemm"),
-            "kernel": "gemv_fused_kernel (qg_quantize_gemv)" if fused else
-                      ("gemm_mfma_q4k" if ncol >= 8 and fmt_s == "q4k" and mode == 0 else "gemv_kernel") + " (qg_gemm_q)",
+            "kernel": kernel_label,
             "algorithmic_bytes_per_launch": algo_bytes,
         },
     }
     record["measured_ceiling"] = ceiling
     record.update(extra)
     if not args.no_cpu:
-        cb, cpu_outs = cpu_baseline(fields, xs, mode, args.cpu_seconds, image_bytes)
+        cb, cpu_outs = cpu_baseline(mats, xs, mode, args.cpu_seconds, image_bytes)
         record["cpu_baseline"] = cb
-        record["parity_step0"] = bool(np.array_equal(cpu_outs[0].view(np.uint32),
+        record["parity_step0"] = bool(np.array_equal(cpu_outs[0].reshape(-1).view(np.uint32),
                                                      first.reshape(-1).view(np.uint32)))
     print(json.dumps(record), flush=True)
 

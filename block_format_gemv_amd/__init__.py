@@ -25,9 +25,11 @@ OK, E_INVALID, E_SHAPE, E_UNSUPPORTED, E_UNREADABLE, E_NONFINITE, E_RUNTIME = ra
 TUNE_WAVES_PER_WG, TUNE_MFMA_MIN_COLS, TUNE_MFMA_COL_TILES = 1, 2, 3
 BLOCK = 256
 MAX_COLS = 32768
+MAX_MATRICES = 8
 
 EXPORTS = ("qg_reads", "qg_image_bytes", "qg_pack_q4k", "qg_pack_q6k", "qg_quantize_act", "qg_gemv_q",
-           "qg_gemm_q", "qg_quantize_gemv", "qg_block_sums", "qg_stream_read", "qg_set_tuning", "qg_time_next_launch", "qg_last_error", "qg_version")
+           "qg_gemm_q", "qg_quantize_gemv", "qg_quantize_gemv_multi", "qg_gemv_q_multi", "qg_block_sums",
+           "qg_stream_read", "qg_set_tuning", "qg_time_next_launch", "qg_last_error", "qg_version")
 
 
 class QGError(RuntimeError):
@@ -53,6 +55,8 @@ def _load():
     L.qg_quantize_gemv.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     L.qg_block_sums.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
     L.qg_stream_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_uint32, vp, vp]
+    L.qg_quantize_gemv_multi.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.qg_gemv_q_multi.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp]
     L.qg_set_tuning.argtypes = [i32, i64]
     L.qg_time_next_launch.argtypes = [vp, vp]
     L.qg_last_error.restype = ctypes.c_char_p
@@ -172,6 +176,42 @@ def qg_quantize_gemv(fmt, mode, rows, cols, image, x, codes, scales, csums, err_
             _need(out, 4 * rows, "out")
     _check(_lib.qg_quantize_gemv(fmt, mode, rows, cols, _dptr(image), _dptr(x), _dptr(codes), _dptr(scales),
                                  _dptr(csums), _dptr(err_flag), _dptr(out), _stream(stream)))
+
+
+def _multi_args(fmt, mode, rows, cols, images, outs):
+    """Host arrays for the *_multi calls (kept alive by the caller's frame)."""
+    nmat = len(rows)
+    if not (len(images) == len(outs) == nmat):
+        raise QGError(E_INVALID, "rows, images and outs differ in length")
+    if cols > 0 and cols % BLOCK == 0 and fmt in (Q4K, Q6K):
+        for m in range(nmat):
+            if rows[m] > 0:
+                _need(images[m], qg_image_bytes(fmt, rows[m], cols), f"images[{m}]")
+                _need(outs[m], 4 * rows[m], f"outs[{m}]")
+    r = (ctypes.c_int64 * max(nmat, 1))(*[int(v) for v in rows])
+    im = (ctypes.c_void_p * max(nmat, 1))(*[_dptr(t) for t in images])
+    ou = (ctypes.c_void_p * max(nmat, 1))(*[_dptr(t) for t in outs])
+    return nmat, r, im, ou
+
+
+def qg_quantize_gemv_multi(fmt, mode, rows, cols, images, x, codes, scales, csums, err_flag, outs,
+                           stream=None) -> None:
+    """rows: list of ints; images, outs: lists of device tensors (one per matrix)."""
+    nmat, r, im, ou = _multi_args(fmt, mode, rows, cols, images, outs)
+    if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32):
+        _need(x, 4 * cols, "x")
+        _check_act(mode, 1, cols, codes, scales, csums)
+        _need(err_flag, 4, "err_flag")
+    _check(_lib.qg_quantize_gemv_multi(fmt, mode, nmat, r, cols, im, _dptr(x), _dptr(codes), _dptr(scales),
+                                       _dptr(csums), _dptr(err_flag), ou, _stream(stream)))
+
+
+def qg_gemv_q_multi(fmt, mode, rows, cols, images, codes, scales, csums, outs, stream=None) -> None:
+    nmat, r, im, ou = _multi_args(fmt, mode, rows, cols, images, outs)
+    if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32):
+        _check_act(mode, 1, cols, codes, scales, csums)
+    _check(_lib.qg_gemv_q_multi(fmt, mode, nmat, r, cols, im, _dptr(codes), _dptr(scales), _dptr(csums), ou,
+                                _stream(stream)))
 
 
 def qg_block_sums(fmt, rows, cols, image, codes, csum_out, osum_out=None, stream=None) -> None:

@@ -210,6 +210,57 @@ int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *
     return launch_quantize(mode, QG_BLOCK, 1, cols, x, codes, scales, csums, err_flag, s);
 }
 
+static int check_multi(const char *who, int fmt, int mode, int nmat, const int64_t *rows, int64_t cols,
+                       const void *const *images, float *const *outs)
+{
+    int st;
+    if ((st = check_fmt_mode(who, fmt, mode))) return st;
+    if ((st = check_cols(who, cols))) return st;
+    if (nmat < 1 || nmat > QG_MAX_MATRICES)
+        return fail(QG_E_SHAPE, "%s: nmat %d is not in 1..%d", who, nmat, QG_MAX_MATRICES);
+    if (!rows || !images || !outs) return fail(QG_E_INVALID, "%s: rows, images or outs is NULL", who);
+    for (int m = 0; m < nmat; m++) {
+        if (rows[m] < 0 || rows[m] > 0x7fffffff)
+            return fail(QG_E_SHAPE, "%s: rows[%d] = %lld out of range", who, m, (long long)rows[m]);
+        if (rows[m] == 0) continue;
+        if (!images[m] || !aligned(images[m], 16)) return fail(QG_E_INVALID, "%s: images[%d] is NULL or not 16-byte aligned", who, m);
+        if (!outs[m] || !aligned(outs[m], 4)) return fail(QG_E_INVALID, "%s: outs[%d] is NULL or not 4-byte aligned", who, m);
+    }
+    return QG_OK;
+}
+
+int qg_quantize_gemv_multi(int fmt, int mode, int nmat, const int64_t *rows, int64_t cols, const void *const *images,
+                           const float *x, int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag,
+                           float *const *outs, void *stream)
+{
+    const char *who = "qg_quantize_gemv_multi";
+    int st;
+    if ((st = check_multi(who, fmt, mode, nmat, rows, cols, images, outs))) return st;
+    if ((st = check_ptr(who, "x", x, 16))) return st;
+    if ((st = check_act(who, codes, scales, csums))) return st;
+    if (err_flag && !aligned(err_flag, 4)) return fail(QG_E_INVALID, "%s: err_flag is not 4-byte aligned", who);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int64_t total = 0;
+    for (int m = 0; m < nmat; m++) total += rows[m];
+    if (total == 0) return launch_quantize(mode, QG_BLOCK, 1, cols, x, codes, scales, csums, err_flag, s);
+    // the quantized row is written by the launch's first workgroup, which belongs to the
+    // first matrix with rows
+    return launch_gemv_multi(fmt, mode, nmat, rows, cols, images, x, nullptr, nullptr, codes, scales, csums, err_flag,
+                             outs, s);
+}
+
+int qg_gemv_q_multi(int fmt, int mode, int nmat, const int64_t *rows, int64_t cols, const void *const *images,
+                    const int8_t *codes, const qg_act_scale *scales, const int32_t *csums, float *const *outs,
+                    void *stream)
+{
+    const char *who = "qg_gemv_q_multi";
+    int st;
+    if ((st = check_multi(who, fmt, mode, nmat, rows, cols, images, outs))) return st;
+    if ((st = check_act(who, codes, scales, csums))) return st;
+    return launch_gemv_multi(fmt, mode, nmat, rows, cols, images, nullptr, codes, scales, nullptr, nullptr, nullptr,
+                             nullptr, outs, static_cast<hipStream_t>(stream));
+}
+
 int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink, void *stream)
 {
     const char *who = "qg_stream_read";

@@ -578,17 +578,30 @@ __device__ __forceinline__ float piece_one(const TileRegs<FMT> &t, int b, const 
     }
 }
 
+// The matrices of one launch, all multiplied by the same activation row: workgroups
+// gstart[m] .. gstart[m+1]-1 are the 64-row groups of matrix m.
+struct Targets {
+    int nmat;
+    int gstart[QG_MAX_MATRICES + 1];
+    int rows[QG_MAX_MATRICES];
+    const uint8_t *image[QG_MAX_MATRICES];
+    float *out[QG_MAX_MATRICES];
+};
+
 template <int FMT, int MODE, int SRC, int W, bool DB>
-__global__ __launch_bounds__(64 * W) void gemv1_kernel(const uint8_t *image, int rows, int G, ActIO io,
-                                                       float *__restrict__ out)
+__global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, ActIO io)
 {
     extern __shared__ __align__(16) float s_piece[];
     using T = TileRegs<FMT>;
-    const int g = blockIdx.x;
+    int m = 0;                                   // this workgroup's matrix (wave-uniform)
+    while (m + 1 < tg.nmat && (int)blockIdx.x >= tg.gstart[m + 1]) m++;
+    const int g = (int)blockIdx.x - tg.gstart[m];
+    const int rows = tg.rows[m];
+    float *out = tg.out[m];
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const bool emit = g == 0;
-    const uint8_t *gbase = image + (size_t)g * G * T::kBytes;
+    const bool emit = blockIdx.x == 0;           // the first workgroup writes the quantized row out
+    const uint8_t *gbase = tg.image[m] + (size_t)g * G * T::kBytes;
 
     // the first block's activations, then its tile: both loads unconditional (a wave past
     // the last block works on a copy of it and stores nothing), kept in this order
@@ -707,49 +720,70 @@ __global__ __launch_bounds__(256) void block_sums_kernel(const uint8_t *__restri
 }
 
 template <int FMT, int MODE, int SRC, int W, bool DB>
-int launch_one_typed(int64_t rows, int G, const void *image, const ActIO &io, float *out, hipStream_t s)
+int launch_one_typed(const Targets &tg, int G, const ActIO &io, hipStream_t s)
 {
-    const int64_t groups = (rows + 63) / 64;
-    if (groups > 0x7fffffff) return fail(QG_E_SHAPE, "too many rows: %lld", (long long)rows);
+    const int64_t groups = tg.gstart[tg.nmat];
+    if (groups == 0) return QG_OK;
     const size_t lds = (size_t)G * 64 * sizeof(float);
     hipEvent_t ev0, ev1;
     take_timing_events(&ev0, &ev1);
     if (ev0 && ev1)
         hipExtLaunchKernelGGL((gemv1_kernel<FMT, MODE, SRC, W, DB>), dim3((unsigned)groups), dim3(64 * W), lds, s,
-                              ev0, ev1, 0, static_cast<const uint8_t *>(image), (int)rows, G, io, out);
+                              ev0, ev1, 0, tg, G, io);
     else
-        hipLaunchKernelGGL((gemv1_kernel<FMT, MODE, SRC, W, DB>), dim3((unsigned)groups), dim3(64 * W), lds, s,
-                           static_cast<const uint8_t *>(image), (int)rows, G, io, out);
+        hipLaunchKernelGGL((gemv1_kernel<FMT, MODE, SRC, W, DB>), dim3((unsigned)groups), dim3(64 * W), lds, s, tg, G,
+                           io);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemv launch: %s", hipGetErrorString(e));
     return QG_OK;
 }
 
 template <int FMT, int MODE, int SRC>
-int launch_one(int64_t rows, int G, const void *image, const ActIO &io, float *out, hipStream_t s)
+int launch_one(const Targets &tg, int G, const ActIO &io, hipStream_t s)
 {
     // waves per workgroup: the tuning knob if set, else one wave per block up to 16; with
     // more blocks than 16 two tiles per wave (double-buffered), which takes 8-wave groups
     int w = tuning().waves_per_wg;
     if (w <= 0) w = G >= 16 ? 16 : G >= 8 ? 8 : 4;
     if (w > 8 && G > 16) w = 8;
-    if (w >= 16) return launch_one_typed<FMT, MODE, SRC, 16, false>(rows, G, image, io, out, s);
+    if (w >= 16) return launch_one_typed<FMT, MODE, SRC, 16, false>(tg, G, io, s);
     if (w >= 8) {
-        if (G > 8) return launch_one_typed<FMT, MODE, SRC, 8, true>(rows, G, image, io, out, s);
-        return launch_one_typed<FMT, MODE, SRC, 8, false>(rows, G, image, io, out, s);
+        if (G > 8) return launch_one_typed<FMT, MODE, SRC, 8, true>(tg, G, io, s);
+        return launch_one_typed<FMT, MODE, SRC, 8, false>(tg, G, io, s);
     }
-    if (G > 4) return launch_one_typed<FMT, MODE, SRC, 4, true>(rows, G, image, io, out, s);
-    return launch_one_typed<FMT, MODE, SRC, 4, false>(rows, G, image, io, out, s);
+    if (G > 4) return launch_one_typed<FMT, MODE, SRC, 4, true>(tg, G, io, s);
+    return launch_one_typed<FMT, MODE, SRC, 4, false>(tg, G, io, s);
 }
 
 template <int SRC>
-int launch_one_any(int fmt, int mode, int64_t rows, int G, const void *image, const ActIO &io, float *out,
-                   hipStream_t s)
+int launch_one_any(int fmt, int mode, const Targets &tg, int G, const ActIO &io, hipStream_t s)
 {
-    if (fmt == QG_Q4K && mode == QG_PERBLOCK) return launch_one<QG_Q4K, QG_PERBLOCK, SRC>(rows, G, image, io, out, s);
-    if (fmt == QG_Q4K && mode == QG_SUB32) return launch_one<QG_Q4K, QG_SUB32, SRC>(rows, G, image, io, out, s);
-    if (fmt == QG_Q6K && mode == QG_PERBLOCK) return launch_one<QG_Q6K, QG_PERBLOCK, SRC>(rows, G, image, io, out, s);
-    return launch_one<QG_Q6K, QG_SUB32, SRC>(rows, G, image, io, out, s);
+    if (fmt == QG_Q4K && mode == QG_PERBLOCK) return launch_one<QG_Q4K, QG_PERBLOCK, SRC>(tg, G, io, s);
+    if (fmt == QG_Q4K && mode == QG_SUB32) return launch_one<QG_Q4K, QG_SUB32, SRC>(tg, G, io, s);
+    if (fmt == QG_Q6K && mode == QG_PERBLOCK) return launch_one<QG_Q6K, QG_PERBLOCK, SRC>(tg, G, io, s);
+    return launch_one<QG_Q6K, QG_SUB32, SRC>(tg, G, io, s);
+}
+
+// the descriptor of nmat matrices (rows[m] rows each); QG_E_SHAPE if the row groups overflow
+int make_targets(int nmat, const int64_t *rows, const void *const *images, float *const *outs, Targets &tg)
+{
+    tg.nmat = nmat;
+    int64_t groups = 0;
+    for (int m = 0; m < nmat; m++) {
+        tg.gstart[m] = (int)groups;
+        tg.rows[m] = (int)rows[m];
+        tg.image[m] = static_cast<const uint8_t *>(images[m]);
+        tg.out[m] = outs[m];
+        groups += (rows[m] + 63) / 64;
+        if (groups > 0x7fffffff) return fail(QG_E_SHAPE, "too many row groups in one launch");
+    }
+    for (int m = nmat; m <= QG_MAX_MATRICES; m++) tg.gstart[m] = (int)groups;
+    for (int m = nmat; m < QG_MAX_MATRICES; m++) {
+        tg.rows[m] = 0;
+        tg.image[m] = nullptr;
+        tg.out[m] = nullptr;
+    }
+    return QG_OK;
 }
 
 // LDS bytes the kernel needs for NC columns
@@ -815,7 +849,10 @@ int launch_nc(int64_t rows, int G, int64_t ncol, const void *image, const int8_t
     for (int64_t c = 0; c < ncol; c++) {
         const ActIO io{nullptr, codes + c * C, reinterpret_cast<const uint32_t *>(scales + c * nsc), nullptr, nullptr,
                        nullptr, nullptr};
-        const int st = launch_one<FMT, MODE, SRC_CODES>(rows, G, image, io, out + c * rows, s);
+        Targets tg;
+        float *oc = out + c * rows;
+        int st = make_targets(1, &rows, &image, &oc, tg);
+        if (st == QG_OK) st = launch_one<FMT, MODE, SRC_CODES>(tg, G, io, s);
         if (st != QG_OK) return st;
     }
     return QG_OK;
@@ -829,7 +866,27 @@ int launch_gemv_fused(int fmt, int mode, int64_t rows, int64_t cols, const void 
 {
     if (rows == 0) return QG_OK;
     const ActIO io{x, nullptr, nullptr, codes, scales, csums, err_flag};
-    return launch_one_any<SRC_F32>(fmt, mode, rows, (int)(cols / 256), image, io, out, s);
+    Targets tg;
+    const int st = make_targets(1, &rows, &image, &out, tg);
+    if (st != QG_OK) return st;
+    return launch_one_any<SRC_F32>(fmt, mode, tg, (int)(cols / 256), io, s);
+}
+
+int launch_gemv_multi(int fmt, int mode, int nmat, const int64_t *rows, int64_t cols, const void *const *images,
+                      const float *x, const int8_t *codes_in, const qg_act_scale *scales_in, int8_t *codes_out,
+                      qg_act_scale *scales_out, int32_t *csums_out, int32_t *err_flag, float *const *outs,
+                      hipStream_t s)
+{
+    Targets tg;
+    const int st = make_targets(nmat, rows, images, outs, tg);
+    if (st != QG_OK) return st;
+    const int G = (int)(cols / 256);
+    if (x) {
+        const ActIO io{x, nullptr, nullptr, codes_out, scales_out, csums_out, err_flag};
+        return launch_one_any<SRC_F32>(fmt, mode, tg, G, io, s);
+    }
+    const ActIO io{nullptr, codes_in, reinterpret_cast<const uint32_t *>(scales_in), nullptr, nullptr, nullptr, nullptr};
+    return launch_one_any<SRC_CODES>(fmt, mode, tg, G, io, s);
 }
 
 int launch_gemv(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, const void *image,
@@ -840,7 +897,10 @@ int launch_gemv(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, con
     const int G = (int)(cols / 256);
     if (ncol == 1) {
         const ActIO io{nullptr, codes, reinterpret_cast<const uint32_t *>(scales), nullptr, nullptr, nullptr, nullptr};
-        return launch_one_any<SRC_CODES>(fmt, mode, rows, G, image, io, out, s);
+        Targets tg;
+        const int st = make_targets(1, &rows, &image, &out, tg);
+        if (st != QG_OK) return st;
+        return launch_one_any<SRC_CODES>(fmt, mode, tg, G, io, s);
     }
     if (fmt == QG_Q4K && mode == QG_PERBLOCK)
         return launch_nc<QG_Q4K, QG_PERBLOCK>(rows, G, ncol, image, codes, scales, csums, out, s);

@@ -42,6 +42,13 @@ int launch_gemv_fused(int fmt, int mode, int64_t rows, int64_t cols, const void 
                       int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
                       hipStream_t s);
 
+// several matrices, one activation row: from x (quantized on the fly, written to *_out) when x
+// is not null, else from codes_in / scales_in
+int launch_gemv_multi(int fmt, int mode, int nmat, const int64_t *rows, int64_t cols, const void *const *images,
+                      const float *x, const int8_t *codes_in, const qg_act_scale *scales_in, int8_t *codes_out,
+                      qg_act_scale *scales_out, int32_t *csums_out, int32_t *err_flag, float *const *outs,
+                      hipStream_t s);
+
 int launch_gemm_mfma(int64_t rows, int64_t cols, int64_t ncol, const void *image, const int8_t *codes,
                      const qg_act_scale *scales, float *out, hipStream_t s);
 

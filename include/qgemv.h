@@ -71,6 +71,7 @@ typedef enum {
 
 #define QG_BLOCK 256
 #define QG_MAX_COLS 32768
+#define QG_MAX_MATRICES 8     /* matrices per qg_*_multi call */
 
 /* Whether the kernels read matrices of `fmt` under `mode` ("Module numerics", Functions
  * reads).  1 for (Q4K, PerBlock), (Q4K, Sub32), (Q6K, PerBlock), (Q6K, Sub32); else 0. */
@@ -177,6 +178,22 @@ int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *
                      int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
                      void *stream);
 
+/* Several matrices that share one activation row, in one launch (a decode layer's Q, K and V
+ * projections, or its gate and up projections).  The matrices share fmt, mode and cols;
+ *   nmat      1 .. QG_MAX_MATRICES
+ *   rows      host int64 [nmat], each >= 0
+ *   images    host array [nmat] of device images (qg_image_bytes(fmt, rows[m], cols) each)
+ *   outs      host array [nmat] of device f32 outputs (rows[m] each)
+ * qg_quantize_gemv_multi quantizes x as qg_quantize_gemv does (every workgroup the blocks it
+ * needs; the first writes the quantized row to codes / scales / csums); qg_gemv_q_multi
+ * takes an already quantized row.  Every outs[m] is bit for bit the one-matrix call's. */
+int qg_quantize_gemv_multi(int fmt, int mode, int nmat, const int64_t *rows, int64_t cols,
+                           const void *const *images, const float *x, int8_t *codes, qg_act_scale *scales,
+                           int32_t *csums, int32_t *err_flag, float *const *outs, void *stream);
+int qg_gemv_q_multi(int fmt, int mode, int nmat, const int64_t *rows, int64_t cols, const void *const *images,
+                    const int8_t *codes, const qg_act_scale *scales, const int32_t *csums, float *const *outs,
+                    void *stream);
+
 /* Integer sums per (row, sub-block), before any scale ("Module lane", Functions
  * block_sums), for one activation row:
  *   Q4K: csum_out int32 [rows][cols/32] = sum sc_j*q*c over sub-block j,
@@ -210,8 +227,8 @@ int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink
 enum { QG_TUNE_WAVES_PER_WG = 1, QG_TUNE_MFMA_MIN_COLS = 2, QG_TUNE_MFMA_COL_TILES = 3 };
 int qg_set_tuning(int key, int64_t value);
 
-/* Measurement hook: the next qg_gemv_q / qg_gemm_q / qg_quantize_gemv / qg_stream_read call
- * made on this thread launches its (GEMV, GEMM or read) kernel with hipExtLaunchKernelGGL, which records start_event as the kernel begins and
+/* Measurement hook: the next qg_gemv_q / qg_gemm_q / qg_quantize_gemv / qg_*_multi /
+ * qg_stream_read call made on this thread launches its (GEMV, GEMM or read) kernel with hipExtLaunchKernelGGL, which records start_event as the kernel begins and
  * stop_event as it ends (hipEvent_t handles owned by the caller; both NULL cancels).
  * Later launches are not timed.  Changes no output bits. */
 int qg_time_next_launch(void *start_event, void *stop_event);

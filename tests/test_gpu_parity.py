@@ -480,3 +480,59 @@ def test_stream_read_diagnostic(qg):
     qg.qg_stream_read(buf, buf.numel(), 0x1234, sink)
     torch.cuda.synchronize()
     assert int(sink.item()) == 0x1234
+
+
+# --- several matrices sharing one activation row ------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_multi_matrix_launch_matches_single_calls(qg, fmt, mode):
+    """One launch over matrices of ragged row counts (one of them empty) gives every matrix the
+    bits of its own call and of the oracle; the quantized row is the one-matrix call's."""
+    cols = 1280
+    shapes = [130, 64, 0, 5, 300]
+    mats = []
+    for k, rows in enumerate(shapes):
+        f = _adversarial_fields(fmt, max(rows, 1), cols, 700 + 13 * k)
+        if rows == 0:
+            mats.append(None)
+            continue
+        mats.append(Mat(qg, f))
+    x = gen.act_outliers(1, cols, 77) if mode == 0 else gen.act_sub32(1, cols, 77)[0]
+    xd = dev(x.reshape(-1))
+    images = [M.img if M else None for M in mats]
+    outs = [torch.full((max(r, 1),), -7.0, dtype=torch.float32, device=DEV) for r in shapes]
+    act = qg.alloc_act(1, cols, mode)
+    fmt_code = qg.FMT_CODES[fmt]
+    qg.qg_quantize_gemv_multi(fmt_code, mode, shapes, cols, images, xd, act.codes, act.scales, act.csums, None, outs)
+    oc, om, oe, os_ = oracle.quantize(x, mode)
+    m, e = act.scale_fields()
+    assert np.array_equal(act.codes.cpu().numpy(), oc) and np.array_equal(m, om) and np.array_equal(e, oe)
+    assert np.array_equal(act.csums.cpu().numpy(), os_)
+    outs2 = [torch.full((max(r, 1),), -7.0, dtype=torch.float32, device=DEV) for r in shapes]
+    qg.qg_gemv_q_multi(fmt_code, mode, shapes, cols, images, act.codes, act.scales, act.csums, outs2)
+    for k, M in enumerate(mats):
+        if M is None:
+            assert float(outs[k][0].item()) == -7.0 and float(outs2[k][0].item()) == -7.0
+            continue
+        say("multi", fmt, "mode", mode, "matrix", k, M.rows)
+        single, _ = qg.quantize_gemv(M.fmt, M.rows, M.cols, M.img, xd, mode)
+        want = oracle.gemv(M.f, oc, om, oe, mode)
+        assert np.array_equal(bits(outs[k]), bits(single)), k
+        assert np.array_equal(bits(outs2[k]), bits(single)), k
+        assert first_mismatch(outs[k], want) is None, k
+
+
+def test_multi_matrix_gate_up_workload(qg, llama):
+    """The decode layer's gate and up projections (two 14336 x 4096 matrices) in one launch."""
+    up = llama["ffn"]
+    gate = Mat(qg, gen.q4k_fields(14336, 4096, gen.SEED_GATE_W))
+    x = gen.decode_act(3)
+    xd = dev(x.reshape(-1))
+    outs = [torch.empty(14336, dtype=torch.float32, device=DEV) for _ in range(2)]
+    act = qg.alloc_act(1, 4096, 0)
+    qg.qg_quantize_gemv_multi(qg.Q4K, 0, [14336, 14336], 4096, [gate.img, up.img], xd, act.codes, act.scales,
+                              act.csums, None, outs)
+    oc, om, oe, _ = oracle.quantize(x, 0)
+    for M, o in ((gate, outs[0]), (up, outs[1])):
+        assert first_mismatch(o, oracle.gemv(M.f, oc, om, oe, 0)) is None

@@ -181,6 +181,18 @@ def test_validation_refuses_before_any_gpu_work():
     assert L.qg_set_tuning(77, 1) == qg.E_INVALID
     assert L.qg_set_tuning(qg.TUNE_WAVES_PER_WG, 3) == qg.E_INVALID
     assert L.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 3) == qg.E_INVALID
+    rows2 = (ctypes.c_int64 * 2)(8, 8)
+    imgs2 = (ctypes.c_void_p * 2)(0x1000, 0x1000)
+    outs2 = (ctypes.c_void_p * 2)(0x1000, 0x1000)
+    assert L.qg_gemv_q_multi(qg.Q4K, qg.PERBLOCK, 0, rows2, 256, imgs2, fake, fake, fake, outs2, None) == qg.E_SHAPE
+    assert L.qg_gemv_q_multi(qg.Q4K, qg.PERBLOCK, 9, rows2, 256, imgs2, fake, fake, fake, outs2, None) == qg.E_SHAPE
+    imgs_bad = (ctypes.c_void_p * 2)(0x1000, None)
+    assert L.qg_gemv_q_multi(qg.Q4K, qg.PERBLOCK, 2, rows2, 256, imgs_bad, fake, fake, fake, outs2, None) == qg.E_INVALID
+    assert "images[1]" in qg.qg_last_error()
+    assert L.qg_quantize_gemv_multi(qg.Q4K, qg.PERBLOCK, 2, rows2, 300, imgs2, fake, fake, fake, fake, None, outs2,
+                                    None) == qg.E_SHAPE
+    assert L.qg_quantize_gemv_multi(qg.Q4K, qg.PERBLOCK, 2, rows2, 256, imgs2, odd, fake, fake, fake, None, outs2,
+                                    None) == qg.E_INVALID
     # empty work is not an error and launches nothing
     assert L.qg_gemv_q(qg.Q4K, qg.PERBLOCK, 0, 256, None, None, None, None, None, None) == qg.OK
     assert L.qg_quantize_act(qg.Q4K, qg.PERBLOCK, 0, 256, None, None, None, None, None, None) == qg.OK

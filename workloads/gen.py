@@ -31,6 +31,8 @@ BLOCK = 256
 # Seeds, fixed once per role and never reused across roles.
 SEED_TINY_W, SEED_TINY_X = 100, 101
 SEED_ATTN_W, SEED_FFN_W = 110, 111
+SEED_GATE_W = 112                  # the FFN gate projection, beside the up projection (seed 111)
+SEED_K_W, SEED_V_W = 113, 114      # 1024 x 4096 K and V projections (Llama-8B grouped-query shapes)
 SEED_REP_X = 1_000_000          # repetition k of the decode workload uses SEED_REP_X + k
 SEED_OUT_W, SEED_OUT_X = 120, 121
 SEED_SUB32_X = 130              # repetition k uses SEED_SUB32_X + k
@@ -126,11 +128,18 @@ def tiny_q4k():
 
 
 def llama_q4k(which: str):
-    """Llama-8B-shaped Q4_K-style matrices: 'attn' 4096 x 4096 or 'ffn' 14336 x 4096."""
+    """Llama-8B-shaped Q4_K-style matrices: 'attn' 4096 x 4096 (also the Q projection),
+    'ffn' 14336 x 4096 (the up projection), 'gate' 14336 x 4096, 'k' and 'v' 1024 x 4096."""
     if which == "attn":
         return q4k_fields(4096, 4096, SEED_ATTN_W)
     if which == "ffn":
         return q4k_fields(14336, 4096, SEED_FFN_W)
+    if which == "gate":
+        return q4k_fields(14336, 4096, SEED_GATE_W)
+    if which == "k":
+        return q4k_fields(1024, 4096, SEED_K_W)
+    if which == "v":
+        return q4k_fields(1024, 4096, SEED_V_W)
     raise ValueError(which)
 
 
