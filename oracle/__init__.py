@@ -56,6 +56,8 @@ def lib(mutant: int = 0):
     L.or_rne_div.restype = ctypes.c_int64
     L.or_f16_scale.argtypes = [ctypes.c_uint16, vp, vp]
     L.or_set_threads.argtypes = [ctypes.c_int]
+    L.or_argmax.argtypes = [vp, i64]
+    L.or_argmax.restype = ctypes.c_int64
     _libs[mutant] = L
     return L
 
@@ -158,6 +160,12 @@ def least_scale(amax: float, bits: int, mutant: int = 0):
 
 def rne_div(x: float, m: int, e: int, mutant: int = 0) -> int:
     return int(lib(mutant).or_rne_div(float(np.float32(x)), int(m), int(e)))
+
+
+def argmax(x: np.ndarray, mutant: int = 0) -> int:
+    """[numerics] argmax of a binary32 row: first of equals, +0 == -0, NaN passed over, 0 if none."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    return int(lib(mutant).or_argmax(_p(x), x.size))
 
 
 def f16_scale(h: int):

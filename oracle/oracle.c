@@ -44,6 +44,8 @@
  * adds with the default MXCSR: no FTZ/DAZ).  Rows may be spread over OpenMP threads; the
  * arithmetic of each row is the same sequential loop whatever the thread count.
  *
+ * argmax follows "Module numerics", Functions argmax.
+ *
  * OR_MUTANT (0 = none) plants one deliberate mistake; only the oracle's own pin tests build
  * such variants, to show that some pin fails for each.
  */
@@ -576,6 +578,25 @@ int or_sub_sums_q6k(int64_t rows, int64_t cols, const uint8_t *q, const int8_t *
         for (int64_t k = 0; k < cols / 16; k++)
             Cs[r * (cols / 16) + k] = q6k_sub_sum(q + r * cols + k * 16, sc[r * (cols / 16) + k], codes + k * 16);
     return OR_OK;
+}
+
+/* [N] argmax: the index of the largest element, the first of equals (+0 and -0 are equal),
+ * a NaN passed over; 0 when there is none (every element NaN, or none at all).  A plain
+ * left-to-right scan with binary32 comparisons. */
+int64_t or_argmax(const float *x, int64_t n)
+{
+    int64_t best = -1;
+    for (int64_t i = 0; i < n; i++) {
+        if (x[i] != x[i]) continue;                 /* NaN */
+#if OR_MUTANT == 10
+        if (best < 0 || x[i] >= x[best]) best = i;  /* planted: the last of equals */
+#elif OR_MUTANT == 11
+        if (best < 0 || bits_of(x[i]) > bits_of(x[best])) best = i;   /* planted: compares bit patterns */
+#else
+        if (best < 0 || x[i] > x[best]) best = i;
+#endif
+    }
+    return best < 0 ? 0 : best;
 }
 
 int or_mutant(void) { return OR_MUTANT; }

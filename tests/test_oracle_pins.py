@@ -545,6 +545,36 @@ def test_sub32_rows_with_the_window_engaged():
     assert engaged > 0
 
 
+# --- argmax ([numerics] Functions argmax) ---------------------------------------------------
+
+def _argmax_cases():
+    for r in read_table("argmax.txt"):
+        vals = [] if r[1] == "-" else [int(h, 16) for h in r[1:]]
+        yield int(r[0]), np.array(vals, np.uint32).view(np.float32)
+
+
+def test_argmax_hand_cases():
+    for want, x in _argmax_cases():
+        assert oracle.argmax(x) == want, (want, x)
+
+
+def test_argmax_matches_numpy_first_occurrence():
+    """numpy's argmax returns the first of equal maxima and compares -0 == +0; with NaNs it is
+    taken over the non-NaN entries (nanargmax would confuse a NaN with a real -inf).  Rows are
+    drawn from few values so ties and signed zeros are common."""
+    g = np.random.Generator(np.random.PCG64(31))
+    pool = np.array([0.0, -0.0, 1.0, -1.0, 2.5, -2.5, np.inf, -np.inf], np.float32)
+    for _ in range(2000):
+        n = int(g.integers(1, 40))
+        x = g.choice(pool, n)
+        assert oracle.argmax(x) == int(np.argmax(x))
+        y = x.copy()
+        y[g.random(n) < 0.3] = np.nan
+        keep = np.flatnonzero(~np.isnan(y))
+        want = 0 if keep.size == 0 else int(keep[np.argmax(y[keep])])
+        assert oracle.argmax(y) == want
+
+
 # --- planted mistakes --------------------------------------------------------------------
 
 def _quick_pins(mutant: int) -> bool:
@@ -587,6 +617,9 @@ def _quick_pins(mutant: int) -> bool:
         c, m, e, _ = oracle.quantize(xs, oracle.PERBLOCK, mutant=mutant)
         if (int(m[0, 0]), int(e[0, 0])) != (128, 0):
             return False
+        for want, x in _argmax_cases():
+            if oracle.argmax(x, mutant) != want:
+                return False
     except oracle.OracleError:
         return False
     return True
@@ -595,5 +628,5 @@ def _quick_pins(mutant: int) -> bool:
 @pytest.mark.slow
 def test_mutants_are_caught():
     assert _quick_pins(0)
-    for mutant in range(1, 10):
+    for mutant in range(1, 12):
         assert not _quick_pins(mutant), f"oracle mutant {mutant} passes every quick pin"
