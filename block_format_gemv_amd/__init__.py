@@ -28,7 +28,7 @@ MAX_COLS = 32768
 MAX_MATRICES = 8
 
 EXPORTS = ("qg_reads", "qg_image_bytes", "qg_pack_q4k", "qg_pack_q6k", "qg_quantize_act", "qg_gemv_q",
-           "qg_gemm_q", "qg_quantize_gemv", "qg_quantize_gemv_multi", "qg_gemv_q_multi", "qg_block_sums",
+           "qg_gemm_q", "qg_quantize_gemv", "qg_quantize_gemv_argmax", "qg_argmax_index", "qg_quantize_gemv_multi", "qg_gemv_q_multi", "qg_block_sums",
            "qg_stream_read", "qg_set_tuning", "qg_time_next_launch", "qg_last_error", "qg_version")
 
 
@@ -55,6 +55,9 @@ def _load():
     L.qg_quantize_gemv.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     L.qg_block_sums.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
     L.qg_stream_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_uint32, vp, vp]
+    L.qg_quantize_gemv_argmax.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.qg_argmax_index.argtypes = [ctypes.c_uint64]
+    L.qg_argmax_index.restype = ctypes.c_int64
     L.qg_quantize_gemv_multi.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     L.qg_gemv_q_multi.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp]
     L.qg_set_tuning.argtypes = [i32, i64]
@@ -176,6 +179,26 @@ def qg_quantize_gemv(fmt, mode, rows, cols, image, x, codes, scales, csums, err_
             _need(out, 4 * rows, "out")
     _check(_lib.qg_quantize_gemv(fmt, mode, rows, cols, _dptr(image), _dptr(x), _dptr(codes), _dptr(scales),
                                  _dptr(csums), _dptr(err_flag), _dptr(out), _stream(stream)))
+
+
+def qg_quantize_gemv_argmax(fmt, mode, rows, cols, image, x, codes, scales, csums, err_flag, out, argmax_key,
+                            stream=None) -> None:
+    """argmax_key: device int64 [1] holding 0 before the call."""
+    if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32) and fmt in (Q4K, Q6K):
+        _need(x, 4 * cols, "x")
+        _check_act(mode, 1, cols, codes, scales, csums)
+        _need(err_flag, 4, "err_flag")
+        _need(argmax_key, 8, "argmax_key")
+        if rows > 0:
+            _need(image, qg_image_bytes(fmt, rows, cols), "image")
+            _need(out, 4 * rows, "out")
+    _check(_lib.qg_quantize_gemv_argmax(fmt, mode, rows, cols, _dptr(image), _dptr(x), _dptr(codes), _dptr(scales),
+                                        _dptr(csums), _dptr(err_flag), _dptr(out), _dptr(argmax_key),
+                                        _stream(stream)))
+
+
+def qg_argmax_index(key: int) -> int:
+    return int(_lib.qg_argmax_index(ctypes.c_uint64(key & 0xFFFFFFFFFFFFFFFF)))
 
 
 def _multi_args(fmt, mode, rows, cols, images, outs):

@@ -188,11 +188,10 @@ int qg_gemm_q(int fmt, int mode, int64_t rows, int64_t cols, int64_t n, const vo
     return gemm_common("qg_gemm_q", fmt, mode, rows, cols, n, image, codes, scales, csums, out, stream);
 }
 
-int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const float *x,
-                     int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
-                     void *stream)
+static int quantize_gemv_common(const char *who, int fmt, int mode, int64_t rows, int64_t cols, const void *image,
+                                const float *x, int8_t *codes, qg_act_scale *scales, int32_t *csums,
+                                int32_t *err_flag, float *out, uint64_t *argmax_key, void *stream)
 {
-    const char *who = "qg_quantize_gemv";
     int st;
     if ((st = check_fmt_mode(who, fmt, mode))) return st;
     if ((st = check_cols(who, cols))) return st;
@@ -205,10 +204,33 @@ int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *
         if ((st = check_ptr(who, "out", out, 4))) return st;
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (rows > 0) return launch_gemv_fused(fmt, mode, rows, cols, image, x, codes, scales, csums, err_flag, out, s);
+    if (rows > 0)
+        return launch_gemv_fused(fmt, mode, rows, cols, image, x, codes, scales, csums, err_flag, out,
+                                 reinterpret_cast<unsigned long long *>(argmax_key), s);
     // no rows to multiply: only the quantized row
     return launch_quantize(mode, QG_BLOCK, 1, cols, x, codes, scales, csums, err_flag, s);
 }
+
+int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const float *x,
+                     int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
+                     void *stream)
+{
+    return quantize_gemv_common("qg_quantize_gemv", fmt, mode, rows, cols, image, x, codes, scales, csums, err_flag,
+                                out, nullptr, stream);
+}
+
+int qg_quantize_gemv_argmax(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const float *x,
+                            int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
+                            uint64_t *argmax_key, void *stream)
+{
+    const char *who = "qg_quantize_gemv_argmax";
+    int st;
+    if ((st = check_ptr(who, "argmax_key", argmax_key, 8))) return st;
+    return quantize_gemv_common(who, fmt, mode, rows, cols, image, x, codes, scales, csums, err_flag, out, argmax_key,
+                                stream);
+}
+
+int64_t qg_argmax_index(uint64_t key) { return key == 0 ? 0 : (int64_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu)); }
 
 static int check_multi(const char *who, int fmt, int mode, int nmat, const int64_t *rows, int64_t cols,
                        const void *const *images, float *const *outs)

@@ -478,7 +478,21 @@ struct ActIO {
     qg_act_scale *scales_out;
     int32_t *csums_out;
     int32_t *err_flag;            // may be null
+    unsigned long long *argmax;   // may be null: the row's argmax key is folded in here
 };
+
+// argmax of the output row ("Module numerics", Functions argmax) as one 64-bit key per row:
+// the value's bits mapped so that unsigned order is numeric order (+0 and -0 both map to +0's
+// key) in the high word, and ~row in the low word, so the larger key is the larger value and,
+// among equals, the lower row.  A NaN, or a padding row, gives 0: "none".
+__device__ __forceinline__ unsigned long long argmax_key(float y, int64_t row, bool valid)
+{
+    if (!valid || y != y) return 0ull;
+    uint32_t u = __float_as_uint(y);
+    if ((u & 0x7FFFFFFFu) == 0) u = 0;                       // -0 equals +0
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)row);
+}
 
 // Keeps the loads issued above here: a compiler-only barrier (no instruction, no wait) that
 // neither the IR passes nor the scheduler move memory operations across.  (Loads through a
@@ -656,7 +670,18 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
         const int64_t row = (int64_t)g * 64 + lane;
         float y = 0.0f;
         for (int b = 0; b < G; b++) y = fadd_ftz(y, s_piece[(size_t)b * 64 + lane]);
-        if (row < rows) out[row] = canon_nan(y);
+        y = canon_nan(y);
+        if (row < rows) out[row] = y;
+        if (io.argmax) {
+            // the largest key of the group's 64 rows, then one atomic max per workgroup
+            unsigned long long k = argmax_key(y, row, row < rows);
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const unsigned long long o = __shfl_xor(k, off, 64);
+                k = o > k ? o : k;
+            }
+            if (lane == 0 && k != 0ull) atomicMax(io.argmax, k);
+        }
     }
 }
 
@@ -848,7 +873,7 @@ int launch_nc(int64_t rows, int G, int64_t ncol, const void *image, const int8_t
     const int64_t C = (int64_t)G * 256, nsc = MODE == QG_PERBLOCK ? G : (int64_t)G * 8;
     for (int64_t c = 0; c < ncol; c++) {
         const ActIO io{nullptr, codes + c * C, reinterpret_cast<const uint32_t *>(scales + c * nsc), nullptr, nullptr,
-                       nullptr, nullptr};
+                       nullptr, nullptr, nullptr};
         Targets tg;
         float *oc = out + c * rows;
         int st = make_targets(1, &rows, &image, &oc, tg);
@@ -862,10 +887,10 @@ int launch_nc(int64_t rows, int G, int64_t ncol, const void *image, const int8_t
 
 int launch_gemv_fused(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const float *x,
                       int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
-                      hipStream_t s)
+                      unsigned long long *argmax, hipStream_t s)
 {
     if (rows == 0) return QG_OK;
-    const ActIO io{x, nullptr, nullptr, codes, scales, csums, err_flag};
+    const ActIO io{x, nullptr, nullptr, codes, scales, csums, err_flag, argmax};
     Targets tg;
     const int st = make_targets(1, &rows, &image, &out, tg);
     if (st != QG_OK) return st;
@@ -882,10 +907,11 @@ int launch_gemv_multi(int fmt, int mode, int nmat, const int64_t *rows, int64_t 
     if (st != QG_OK) return st;
     const int G = (int)(cols / 256);
     if (x) {
-        const ActIO io{x, nullptr, nullptr, codes_out, scales_out, csums_out, err_flag};
+        const ActIO io{x, nullptr, nullptr, codes_out, scales_out, csums_out, err_flag, nullptr};
         return launch_one_any<SRC_F32>(fmt, mode, tg, G, io, s);
     }
-    const ActIO io{nullptr, codes_in, reinterpret_cast<const uint32_t *>(scales_in), nullptr, nullptr, nullptr, nullptr};
+    const ActIO io{nullptr, codes_in, reinterpret_cast<const uint32_t *>(scales_in), nullptr, nullptr, nullptr, nullptr,
+                   nullptr};
     return launch_one_any<SRC_CODES>(fmt, mode, tg, G, io, s);
 }
 
@@ -896,7 +922,8 @@ int launch_gemv(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, con
     if (rows == 0 || ncol == 0) return QG_OK;
     const int G = (int)(cols / 256);
     if (ncol == 1) {
-        const ActIO io{nullptr, codes, reinterpret_cast<const uint32_t *>(scales), nullptr, nullptr, nullptr, nullptr};
+        const ActIO io{nullptr, codes, reinterpret_cast<const uint32_t *>(scales), nullptr, nullptr, nullptr, nullptr,
+                       nullptr};
         Targets tg;
         const int st = make_targets(1, &rows, &image, &out, tg);
         if (st != QG_OK) return st;

@@ -38,9 +38,10 @@ int launch_gemv(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, con
                 hipStream_t s);
 
 // one activation row: quantize it and run the GEMV in one launch
+// argmax: null, or a 64-bit key word the row's argmax is folded into (atomic max)
 int launch_gemv_fused(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const float *x,
                       int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
-                      hipStream_t s);
+                      unsigned long long *argmax, hipStream_t s);
 
 // several matrices, one activation row: from x (quantized on the fly, written to *_out) when x
 // is not null, else from codes_in / scales_in

@@ -178,6 +178,21 @@ int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *
                      int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
                      void *stream);
 
+/* qg_quantize_gemv plus the argmax of the output row ("Module numerics", Functions argmax:
+ * the index of the largest element, the first of equals, +0 and -0 equal, a NaN passed
+ * over, 0 when there is none): the greedy pick over an output projection's logits.
+ *   argmax_key  device uint64 [1], 8-byte aligned; must hold 0 before the call (the caller
+ *               clears it).  Each workgroup folds its rows into it with an atomic max of a
+ *               key whose order is the value's, then the lower row's; the result is
+ *               independent of workgroup order.  qg_argmax_index decodes it.
+ * out and the quantized row are as qg_quantize_gemv writes them. */
+int qg_quantize_gemv_argmax(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const float *x,
+                            int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
+                            uint64_t *argmax_key, void *stream);
+
+/* The row index an argmax key stands for (host; 0 for the key 0: no row, or every row NaN). */
+int64_t qg_argmax_index(uint64_t key);
+
 /* Several matrices that share one activation row, in one launch (a decode layer's Q, K and V
  * projections, or its gate and up projections).  The matrices share fmt, mode and cols;
  *   nmat      1 .. QG_MAX_MATRICES

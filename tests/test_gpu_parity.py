@@ -536,3 +536,67 @@ def test_multi_matrix_gate_up_workload(qg, llama):
     oc, om, oe, _ = oracle.quantize(x, 0)
     for M, o in ((gate, outs[0]), (up, outs[1])):
         assert first_mismatch(o, oracle.gemv(M.f, oc, om, oe, 0)) is None
+
+
+# --- argmax of the output row --------------------------------------------------------------
+
+def _fused_argmax(qg, M, x: np.ndarray, mode: int):
+    key = torch.zeros(1, dtype=torch.int64, device=DEV)
+    act = qg.alloc_act(1, M.cols, mode)
+    out = torch.empty(M.rows, dtype=torch.float32, device=DEV)
+    qg.qg_quantize_gemv_argmax(M.fmt, mode, M.rows, M.cols, M.img, dev(x.reshape(-1)), act.codes, act.scales,
+                               act.csums, None, out, key)
+    return qg.qg_argmax_index(int(key.item()) & 0xFFFFFFFFFFFFFFFF), out
+
+
+def test_argmax_of_logits_q6k_output(qg):
+    """The 128256-row Q6_K output projection: the fused argmax equals the oracle's argmax of
+    the oracle's logits, and the logits are the plain call's bits."""
+    f, x = gen.output_q6k()
+    M = Mat(qg, f)
+    idx, out = _fused_argmax(qg, M, x, 0)
+    c, m, e, _ = oracle.quantize(x, 0)
+    want = oracle.gemv(f, c, m, e, 0)
+    assert first_mismatch(out, want) is None
+    assert idx == oracle.argmax(want)
+    del M
+    torch.cuda.empty_cache()
+
+
+def test_argmax_ties_nan_and_zeros(qg):
+    """Equal maxima in several workgroups (the first wins), NaN rows passed over, and a matrix
+    whose every row is NaN (index 0)."""
+    cols = 512
+    f = gen.q4k_fields(300, cols, 61)
+    x = gen.act_normal(1, cols, 62)
+    c, m, e, _ = oracle.quantize(x, 0)
+    base = oracle.gemv(f, c, m, e, 0)
+    top = int(np.argmax(base))
+    for r in (7, 100, 299):                                # copies of the top row, above and below it
+        for k in ("q", "sc", "mn", "d", "dmin"):
+            f[k][r] = f[k][top]
+    want = oracle.gemv(f, c, m, e, 0)
+    idx, out = _fused_argmax(qg, Mat(qg, f), x, 0)
+    assert first_mismatch(out, want) is None
+    assert idx == oracle.argmax(want) == min(7, top)
+    # rows of inf - inf (canonical NaN) are passed over; all of them NaN gives 0.  With the
+    # largest scales and activations every piece overflows: block 0 (codes 15) to +inf, block 1
+    # (codes 0, only the offset term) to -inf, so a row is NaN unless its block 1 keeps codes 15.
+    g = gen.q4k_fields(130, cols, 63)
+    g["d"][:] = 0x7BFF
+    g["dmin"][:] = 0x7BFF
+    g["sc"][:] = 63
+    g["mn"][:] = 63
+    g["q"][:, :256] = 15
+    g["q"][:, 256:] = 0
+    xb = np.full((1, cols), np.float32(3.0e38), np.float32)
+    c2, m2, e2, _ = oracle.quantize(xb, 0)
+    for finite_rows in ((70, 71), ()):
+        h = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in g.items()}
+        for r in finite_rows:
+            h["q"][r, 256:] = 15
+        want2 = oracle.gemv(h, c2, m2, e2, 0)
+        assert np.isnan(want2).sum() == h["rows"] - len(finite_rows)
+        idx2, out2 = _fused_argmax(qg, Mat(qg, h), xb, 0)
+        assert first_mismatch(out2, want2) is None
+        assert idx2 == oracle.argmax(want2) == (finite_rows[0] if finite_rows else 0)

@@ -193,6 +193,17 @@ def test_validation_refuses_before_any_gpu_work():
                                     None) == qg.E_SHAPE
     assert L.qg_quantize_gemv_multi(qg.Q4K, qg.PERBLOCK, 2, rows2, 256, imgs2, odd, fake, fake, fake, None, outs2,
                                     None) == qg.E_INVALID
+    assert L.qg_quantize_gemv_argmax(qg.Q4K, qg.PERBLOCK, 8, 256, fake, fake, fake, fake, fake, None, fake, None,
+                                     None) == qg.E_INVALID
+    assert "argmax_key is NULL" in qg.qg_last_error()
     # empty work is not an error and launches nothing
     assert L.qg_gemv_q(qg.Q4K, qg.PERBLOCK, 0, 256, None, None, None, None, None, None) == qg.OK
     assert L.qg_quantize_act(qg.Q4K, qg.PERBLOCK, 0, 256, None, None, None, None, None, None) == qg.OK
+
+
+def test_argmax_key_decoding():
+    """qg_argmax_index: key 0 is "none" (index 0); otherwise the low word is ~row."""
+    assert qg.qg_argmax_index(0) == 0
+    for row in (0, 1, 5, 14335, 128255, 2**31 - 1):
+        key = (0x80000000 << 32) | (0xFFFFFFFF - row)
+        assert qg.qg_argmax_index(key) == row
