@@ -56,6 +56,7 @@ def lib(mutant: int = 0):
     L.or_rne_div.restype = ctypes.c_int64
     L.or_f16_scale.argtypes = [ctypes.c_uint16, vp, vp]
     L.or_set_threads.argtypes = [ctypes.c_int]
+    L.or_gemm_b32.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]
     L.or_argmax.argtypes = [vp, i64]
     L.or_argmax.restype = ctypes.c_int64
     _libs[mutant] = L
@@ -85,6 +86,16 @@ def quantize(x: np.ndarray, mode: int, block: int = 256, mutant: int = 0, check:
     return codes, m, e, s16
 
 
+B32_FMT = {"q8_0": 3, "q4_0": 4}
+
+
+def act_block(fmt: str, mode: int) -> int:
+    """Elements per activation scale: the weight format's own block under PerBlock, 32 under Sub32."""
+    if mode == SUB32:
+        return 32
+    return 32 if fmt in B32_FMT else 256
+
+
 def gemm(fields: dict, codes: np.ndarray, m: np.ndarray, e: np.ndarray, mode: int, mutant: int = 0) -> np.ndarray:
     """out f32 [ncol * rows] with out[c*rows + r] = dot(row r, activation column c)."""
     codes = np.ascontiguousarray(codes, np.int8)
@@ -100,8 +111,12 @@ def gemm(fields: dict, codes: np.ndarray, m: np.ndarray, e: np.ndarray, mode: in
     if fields["fmt"] == "q4k":
         st = L.or_gemm_q4k(mode, rows, cols, ncol, _p(f["q"]), _p(f["sc"]), _p(f["mn"]), _p(f["d"]),
                            _p(f["dmin"]), _p(codes), _p(m), _p(e), _p(out))
-    else:
+    elif fields["fmt"] == "q6k":
         st = L.or_gemm_q6k(mode, rows, cols, ncol, _p(f["q"]), _p(f["sc"]), _p(f["d"]),
+                           _p(codes), _p(m), _p(e), _p(out))
+    else:
+        q = np.ascontiguousarray(f["q"]).view(np.uint8)            # stored bytes (int8 for Q8_0)
+        st = L.or_gemm_b32(B32_FMT[fields["fmt"]], mode, rows, cols, ncol, _p(q), _p(f["d"]),
                            _p(codes), _p(m), _p(e), _p(out))
     if st:
         raise OracleError(st, "gemm")

@@ -138,9 +138,10 @@ def quantize_block(x: np.ndarray, bits: int):
     return m, e, codes
 
 
-def quantize(x: np.ndarray, mode: int):
-    """Row x (1-D f32) -> (codes list, [(m, e)] per activation block)."""
-    blk, bits = (256, 8) if mode == 0 else (32, 4)
+def quantize(x: np.ndarray, mode: int, blk: int = 256):
+    """Row x (1-D f32) -> (codes list, [(m, e)] per activation block).  PerBlock blocks are
+    `blk` elements (the weight format's own block) with 8 bits, Sub32 blocks 32 with 4."""
+    blk, bits = (blk, 8) if mode == 0 else (32, 4)
     codes, scales = [], []
     for b in range(len(x) // blk):
         m, e, c = quantize_block(x[b * blk:(b + 1) * blk], bits)
@@ -170,14 +171,24 @@ def q6k_weights(f: dict, r: int) -> list[Fraction]:
             for i in range(C)]
 
 
-def dot_row(weights: list[Fraction], codes: list[int], scales: list[tuple[int, int]], mode: int) -> np.float32:
-    """Row value: per 256-element block the exact sum(w_i * c_i * s_i), rounded once, the
-    rounded pieces added in order from +0; NaN -> 0x7FC00000."""
-    ablk = 256 if mode == 0 else 32
+def b32_weights(f: dict, r: int) -> list[Fraction]:
+    """Exact weights of row r of a 32-element-block matrix: Q8_0-style w = d*q (int8 q),
+    Q4_0-style w = d*(q - 8)."""
+    off = 0 if f["fmt"] == "q8_0" else 8
+    return [f16_value(int(f["d"][r, i // 32])) * (int(f["q"][r, i]) - off) for i in range(f["cols"])]
+
+
+def dot_row(weights: list[Fraction], codes: list[int], scales: list[tuple[int, int]], mode: int,
+            ablk: int = 256, piece: int = 256) -> np.float32:
+    """Row value: per piece (`piece` elements: the weight block under PerBlock, the 256-element
+    group under Sub32) the exact sum(w_i * c_i * s_i), rounded once, the rounded pieces added
+    in order from +0; NaN -> 0x7FC00000.  Activation scales cover `ablk` elements."""
+    if mode != 0:
+        ablk = 32
     y = np.float32(0.0)
-    for b in range(len(weights) // 256):
+    for b in range(len(weights) // piece):
         X = F0
-        for i in range(b * 256, (b + 1) * 256):
+        for i in range(b * piece, (b + 1) * piece):
             m, e = scales[i // ablk]
             X += weights[i] * codes[i] * m * Fraction(2) ** e
         y = fadd(y, round_f32(X))
@@ -188,6 +199,10 @@ def dot_row(weights: list[Fraction], codes: list[int], scales: list[tuple[int, i
 
 def gemv(f: dict, x: np.ndarray, mode: int) -> np.ndarray:
     """All rows of a tiny matrix against one f32 activation row."""
-    codes, scales = quantize(np.asarray(x, np.float32).reshape(-1), mode)
-    wfun = q4k_weights if f["fmt"] == "q4k" else q6k_weights
-    return np.array([dot_row(wfun(f, r), codes, scales, mode) for r in range(f["rows"])], dtype=np.float32)
+    b32 = f["fmt"] in ("q8_0", "q4_0")
+    blk = 32 if b32 else 256
+    codes, scales = quantize(np.asarray(x, np.float32).reshape(-1), mode, blk)
+    wfun = {"q4k": q4k_weights, "q6k": q6k_weights}.get(f["fmt"], b32_weights)
+    piece = 32 if (b32 and mode == 0) else 256
+    return np.array([dot_row(wfun(f, r), codes, scales, mode, blk, piece) for r in range(f["rows"])],
+                    dtype=np.float32)

@@ -44,7 +44,9 @@
  * adds with the default MXCSR: no FTZ/DAZ).  Rows may be spread over OpenMP threads; the
  * arithmetic of each row is the same sequential loop whatever the thread count.
  *
- * argmax follows "Module numerics", Functions argmax.
+ * argmax follows "Module numerics", Functions argmax.  The 32-element-block formats (Q8_0- and
+ * Q4_0-style, b32_row) follow the module description's "the matrix format's own block, 32 or
+ * 256 elements" under PerBlock, and its 256-element groups under Sub32.
  *
  * OR_MUTANT (0 = none) plants one deliberate mistake; only the oracle's own pin tests build
  * such variants, to show that some pin fails for each.
@@ -510,6 +512,80 @@ static int q6k_row(int mode, int64_t cols, const uint8_t *q, const int8_t *sc, c
     }
     *out = canon_nan(y);
     return OR_OK;
+}
+
+/* Formats with 32-element weight blocks and one binary16 scale per block ([N] module
+ * description: "the matrix format's own block, 32 or 256 elements"): Q8_0-style (fmt 3), an
+ * int8 code per weight, w = d*q; Q4_0-style (fmt 4), a 4-bit code, w = d*(q - 8).  q holds
+ * the stored bytes: int8 two's complement for Q8_0, 0..15 for Q4_0.  The integer sum of one
+ * 32-element block against 32 activation codes, element by element. */
+static int64_t b32_sum(int fmt, const uint8_t *q, const int8_t *c)
+{
+    int64_t C = 0;
+    for (int i = 0; i < 32; i++) {
+#if OR_MUTANT == 12
+        int64_t w = fmt == 3 ? (int64_t)q[i] : (int64_t)q[i] - 8;          /* MUTANT: Q8_0 read unsigned */
+#elif OR_MUTANT == 13
+        int64_t w = fmt == 3 ? (int64_t)(int8_t)q[i] : (int64_t)q[i];      /* MUTANT: Q4_0 offset dropped */
+#else
+        int64_t w = fmt == 3 ? (int64_t)(int8_t)q[i] : (int64_t)q[i] - 8;
+#endif
+        C += w * c[i];
+    }
+    return C;
+}
+
+/* One row of a 32-element-block matrix.  mode 0 (PerBlock over the format's own 32-element
+ * block, 8-bit significand): per block the single term m*2^e * d * C_b, rounded once.  mode 1
+ * (Sub32, 4-bit significand): per 256-element group the eight terms of its blocks, each
+ * under its own activation and weight scale, summed exactly and rounded once.  The pieces
+ * are then added in order. */
+static int b32_row(int fmt, int mode, int64_t cols, const uint8_t *q, const uint16_t *d, const int8_t *c,
+                   const uint8_t *sm, const int16_t *se, float *out)
+{
+    if (fmt == 4)
+        for (int64_t i = 0; i < cols; i++) if (q[i] > 15) return OR_E_RANGE;
+    int64_t nb = cols / 32;
+    float y = 0.0f;
+    const int per = mode == 0 ? 1 : 8;        /* blocks per piece */
+    for (int64_t b0 = 0; b0 < nb; b0 += per) {
+        term_t t[8];
+        for (int j = 0; j < per; j++) {
+            int64_t b = b0 + j;
+            int64_t sd; int ed;
+            if (f16_scale(d[b], &sd, &ed)) return OR_E_UNREADABLE;
+            t[j].v = (i128)sm[b] * sd * b32_sum(fmt, q + b * 32, c + b * 32);
+            t[j].e = se[b] + ed;
+        }
+        float p;
+        int st = exact_sum(t, per, &p);
+        if (st) return st;
+        y = fadd(y, p);
+    }
+    *out = canon_nan(y);
+    return OR_OK;
+}
+
+/* [N] dot, batched, for the 32-element-block formats: q [rows][cols], d [rows][cols/32],
+ * activation scales [ncol][cols/32] (PerBlock over 32 elements, or Sub32). */
+int or_gemm_b32(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, const uint8_t *q, const uint16_t *d,
+                const int8_t *codes, const uint8_t *sm, const int16_t *se, float *out)
+{
+    if ((fmt != 3 && fmt != 4) || (mode != 0 && mode != 1) || cols % OR_BLOCK) return OR_E_SHAPE;
+    int status = OR_OK;
+    const int64_t nsc = cols / 32;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(g_threads) if (g_threads > 1)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t k = 0; k < ncol; k++) {
+            int st = b32_row(fmt, mode, cols, q + r * cols, d + r * (cols / 32), codes + k * cols, sm + k * nsc,
+                             se + k * nsc, &out[k * rows + r]);
+            if (st) {
+#pragma omp critical
+                status = st;
+            }
+        }
+    }
+    return status;
 }
 
 /* [N] dot, batched: out[col * rows + r] = dot(row r, activation row col).

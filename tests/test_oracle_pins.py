@@ -545,6 +545,93 @@ def test_sub32_rows_with_the_window_engaged():
     assert engaged > 0
 
 
+# --- 32-element weight blocks (Q8_0- and Q4_0-style) ----------------------------------------
+
+def _adversarial_b32(fmt, seed, rows, cols):
+    f = gen.q8_0_fields(rows, cols, seed) if fmt == "q8_0" else gen.q4_0_fields(rows, cols, seed)
+    g = np.random.Generator(np.random.PCG64(seed + 1))
+    choices = np.array([0x0000, 0x0001, 0x0003, 0x03FF, 0x0400, 0x1400, 0x3C00, 0x7BFF, 0x8001, 0xFBFF], np.uint16)
+    pick = g.random(f["d"].shape) < 0.4
+    f["d"][pick] = g.choice(choices, size=int(pick.sum()))
+    hi = 127 if fmt == "q8_0" else 15
+    lo = -128 if fmt == "q8_0" else 0
+    f["q"][g.random(f["q"].shape) < 0.05] = hi
+    f["q"][g.random(f["q"].shape) < 0.05] = lo
+    return f
+
+
+def _b32_x(seed, cols, mode):
+    """Adversarial activations with PerBlock blocks of 32 elements (the format's own block)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal(cols).astype(np.float32)
+    lo_k, hi_k = (-120, 100) if mode == oracle.PERBLOCK else (-20, 20)
+    for b in range(cols // 32):
+        kind = g.integers(0, 7)
+        sl = slice(b * 32, (b + 1) * 32)
+        if kind == 0:
+            x[sl] = 0.0
+        elif kind == 1:
+            x[sl] *= np.float32(2.0 ** lo_k)
+        elif kind == 2:
+            x[sl] *= np.float32(2.0 ** hi_k)
+        elif kind == 3:
+            x[b * 32 + 1] = np.nan
+        elif kind == 4:
+            x[sl] = np.round(x[sl] * 4) / 4
+    return x
+
+
+def _b32_quant(fmt, x, mode, mutant=0):
+    return oracle.quantize(np.asarray(x, np.float32).reshape(1, -1), mode, block=oracle.act_block(fmt, mode),
+                           mutant=mutant)
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_b32_closed_form(fmt, mode):
+    """All weights d*1 with d = 2^-10 and x = 127*128*2^-14 everywhere: codes 127 under
+    s = 2^-7 (PerBlock over 32: m = 128, e = -14; Sub32: m = 8, e = -10), so every 32-block
+    is 2^-7 * 2^-10 * 32 * 127 and a 256-element row 8 of them: 127/512 exactly."""
+    f = gen.q8_0_fields(2, 512, 5) if fmt == "q8_0" else gen.q4_0_fields(2, 512, 5)
+    f["q"][:] = 1 if fmt == "q8_0" else 9
+    f["d"][:] = 0x1400
+    x = np.full(512, np.float32(0.9921875), np.float32)
+    c, m, e, _ = _b32_quant(fmt, x, mode)
+    assert (c == 127).all()
+    assert (m == (128 if mode == 0 else 8)).all() and (e == (-14 if mode == 0 else -10)).all()
+    out = oracle.gemv(f, c, m, e, mode)
+    assert (out == np.float32(254 / 512)).all()
+    if fmt == "q4_0":                                        # codes 8 are the value 0
+        f["q"][:] = 8
+        assert (oracle.gemv(f, c, m, e, mode) == 0).all()
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_q4_0_equals_q8_0_shifted(mode):
+    """A Q4_0-style code q is the value q - 8: the same matrix stored as Q8_0 codes q - 8 gives
+    the same bits (two code paths of the oracle)."""
+    f4 = _adversarial_b32("q4_0", 41, 37, 1024)
+    f8 = {"fmt": "q8_0", "rows": 37, "cols": 1024, "q": (f4["q"].astype(np.int16) - 8).astype(np.int8),
+          "d": f4["d"].copy()}
+    x = _b32_x(42, 1024, mode)
+    c, m, e, _ = _b32_quant("q4_0", x, mode)
+    assert np.array_equal(oracle.gemv(f4, c, m, e, mode).view(np.uint32), oracle.gemv(f8, c, m, e, mode).view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_b32_fraction_brute_force(fmt, mode):
+    """Tiny adversarial rows against the exact-rational reference (subnormal, zero, huge and
+    negative binary16 scales; tiny, huge, NaN, all-zero and tie-laden activation blocks)."""
+    for seed in (1, 2, 3):
+        f = _adversarial_b32(fmt, 500 + seed, 4, 512)
+        x = _b32_x(600 + seed, 512, mode)
+        c, m, e, _ = _b32_quant(fmt, x, mode)
+        got = oracle.gemv(f, c, m, e, mode)
+        want = exact.gemv(f, x, mode)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (fmt, mode, seed)
+
+
 # --- argmax ([numerics] Functions argmax) ---------------------------------------------------
 
 def _argmax_cases():
@@ -620,6 +707,13 @@ def _quick_pins(mutant: int) -> bool:
         for want, x in _argmax_cases():
             if oracle.argmax(x, mutant) != want:
                 return False
+        for fmt in ("q8_0", "q4_0"):
+            f = _adversarial_b32(fmt, 800, 3, 256)
+            x = _b32_x(801, 256, oracle.PERBLOCK)
+            c, m, e, _ = _b32_quant(fmt, x, oracle.PERBLOCK, mutant)
+            got = oracle.gemv(f, c, m, e, oracle.PERBLOCK, mutant=mutant)
+            if not np.array_equal(got.view(np.uint32), exact.gemv(f, x, oracle.PERBLOCK).view(np.uint32)):
+                return False
     except oracle.OracleError:
         return False
     return True
@@ -628,5 +722,5 @@ def _quick_pins(mutant: int) -> bool:
 @pytest.mark.slow
 def test_mutants_are_caught():
     assert _quick_pins(0)
-    for mutant in range(1, 12):
+    for mutant in range(1, 14):
         assert not _quick_pins(mutant), f"oracle mutant {mutant} passes every quick pin"

@@ -33,6 +33,7 @@ SEED_TINY_W, SEED_TINY_X = 100, 101
 SEED_ATTN_W, SEED_FFN_W = 110, 111
 SEED_GATE_W = 112                  # the FFN gate projection, beside the up projection (seed 111)
 SEED_K_W, SEED_V_W = 113, 114      # 1024 x 4096 K and V projections (Llama-8B grouped-query shapes)
+SEED_Q8_W, SEED_Q4_0_W = 150, 151  # 14336 x 4096 Q8_0-style and Q4_0-style matrices
 SEED_REP_X = 1_000_000          # repetition k of the decode workload uses SEED_REP_X + k
 SEED_OUT_W, SEED_OUT_X = 120, 121
 SEED_SUB32_X = 130              # repetition k uses SEED_SUB32_X + k
@@ -68,6 +69,26 @@ def q6k_fields(rows: int, cols: int, seed: int, scale_exp: int = -10) -> dict:
     sc = g.integers(-128, 128, size=(rows, cols // 16), dtype=np.int8)
     d = f16_bits_of(np.abs(g.standard_normal((rows, cols // BLOCK))) * 2.0 ** scale_exp)
     return {"fmt": "q6k", "rows": rows, "cols": cols, "q": q, "sc": sc, "d": d}
+
+
+def q8_0_fields(rows: int, cols: int, seed: int, scale_exp: int = -8) -> dict:
+    """Q8_0-style matrix (32-element blocks): q ~ U{-128..127} int8, one d = f16(|N(0,1)| * 2^scale_exp)
+    per 32 weights."""
+    assert cols % BLOCK == 0
+    g = _rng(seed)
+    q = g.integers(-128, 128, size=(rows, cols), dtype=np.int8)
+    d = f16_bits_of(np.abs(g.standard_normal((rows, cols // 32))) * 2.0 ** scale_exp)
+    return {"fmt": "q8_0", "rows": rows, "cols": cols, "q": q, "d": d}
+
+
+def q4_0_fields(rows: int, cols: int, seed: int, scale_exp: int = -8) -> dict:
+    """Q4_0-style matrix (32-element blocks): q ~ U{0..15} (value q - 8), one d = f16(|N(0,1)| *
+    2^scale_exp) per 32 weights."""
+    assert cols % BLOCK == 0
+    g = _rng(seed)
+    q = g.integers(0, 16, size=(rows, cols), dtype=np.uint8)
+    d = f16_bits_of(np.abs(g.standard_normal((rows, cols // 32))) * 2.0 ** scale_exp)
+    return {"fmt": "q4_0", "rows": rows, "cols": cols, "q": q, "d": d}
 
 
 def slice_rows(fields: dict, idx) -> dict:
