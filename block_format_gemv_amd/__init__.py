@@ -19,7 +19,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqgemv.so")
 
-Q4K, Q6K = 1, 2
+Q4K, Q6K, Q8_0, Q4_0 = 1, 2, 3, 4
+FORMATS = (Q4K, Q6K, Q8_0, Q4_0)
 PERBLOCK, SUB32 = 0, 1
 OK, E_INVALID, E_SHAPE, E_UNSUPPORTED, E_UNREADABLE, E_NONFINITE, E_RUNTIME = range(7)
 TUNE_WAVES_PER_WG, TUNE_MFMA_MIN_COLS, TUNE_MFMA_COL_TILES = 1, 2, 3
@@ -27,9 +28,10 @@ BLOCK = 256
 MAX_COLS = 32768
 MAX_MATRICES = 8
 
-EXPORTS = ("qg_reads", "qg_image_bytes", "qg_pack_q4k", "qg_pack_q6k", "qg_quantize_act", "qg_gemv_q",
-           "qg_gemm_q", "qg_quantize_gemv", "qg_quantize_gemv_argmax", "qg_argmax_index", "qg_quantize_gemv_multi", "qg_gemv_q_multi", "qg_block_sums",
-           "qg_stream_read", "qg_set_tuning", "qg_time_next_launch", "qg_last_error", "qg_version")
+EXPORTS = ("qg_reads", "qg_image_bytes", "qg_pack_q4k", "qg_pack_q6k", "qg_pack_b32", "qg_quantize_act",
+           "qg_gemv_q", "qg_gemm_q", "qg_quantize_gemv", "qg_quantize_gemv_argmax", "qg_argmax_index",
+           "qg_quantize_gemv_multi", "qg_gemv_q_multi", "qg_block_sums", "qg_stream_read", "qg_set_tuning",
+           "qg_time_next_launch", "qg_last_error", "qg_version")
 
 
 class QGError(RuntimeError):
@@ -122,6 +124,10 @@ def qg_pack_q6k(rows, cols, q, sc, d, image) -> None:
     _check(_lib.qg_pack_q6k(rows, cols, _hptr(q), _hptr(sc), _hptr(d), _hptr(image)))
 
 
+def qg_pack_b32(fmt, rows, cols, q, d, image) -> None:
+    _check(_lib.qg_pack_b32(fmt, rows, cols, _hptr(q), _hptr(d), _hptr(image)))
+
+
 def _need(t, nbytes: int, name: str) -> None:
     """Refuse a device buffer smaller than the call will touch (the C ABI cannot see sizes)."""
     if t is None:
@@ -131,29 +137,34 @@ def _need(t, nbytes: int, name: str) -> None:
         raise QGError(E_SHAPE, f"{name} holds {have} bytes, the call needs {nbytes}")
 
 
-def _nsc(mode: int, cols: int) -> int:
-    return cols // (BLOCK if mode == PERBLOCK else 32)
+def act_block(fmt: int, mode: int) -> int:
+    """Elements per activation scale: 32 under Sub32 or for a 32-element-block format, else 256."""
+    return 32 if mode == SUB32 or fmt in (Q8_0, Q4_0) else BLOCK
 
 
-def _check_act(mode, n, cols, codes, scales, csums):
+def _nsc(fmt: int, mode: int, cols: int) -> int:
+    return cols // act_block(fmt, mode)
+
+
+def _check_act(fmt, mode, n, cols, codes, scales, csums):
     _need(codes, n * cols, "codes")
-    _need(scales, 4 * n * _nsc(mode, cols), "scales")
+    _need(scales, 4 * n * _nsc(fmt, mode, cols), "scales")
     _need(csums, 4 * n * (cols // 16), "csums")
 
 
 def qg_quantize_act(fmt, mode, n, cols, x, codes, scales, csums, err_flag=None, stream=None) -> None:
     if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32):
         _need(x, 4 * n * cols, "x")
-        _check_act(mode, n, cols, codes, scales, csums)
+        _check_act(fmt, mode, n, cols, codes, scales, csums)
         _need(err_flag, 4, "err_flag")
     _check(_lib.qg_quantize_act(fmt, mode, n, cols, _dptr(x), _dptr(codes), _dptr(scales), _dptr(csums),
                                 _dptr(err_flag), _stream(stream)))
 
 
 def _check_gemm(fmt, mode, rows, cols, n, image, codes, scales, csums, out):
-    if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32) and fmt in (Q4K, Q6K) and rows > 0:
+    if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32) and fmt in FORMATS and rows > 0:
         _need(image, qg_image_bytes(fmt, rows, cols), "image")
-        _check_act(mode, n, cols, codes, scales, csums)
+        _check_act(fmt, mode, n, cols, codes, scales, csums)
         _need(out, 4 * n * rows, "out")
 
 
@@ -170,9 +181,9 @@ def qg_gemm_q(fmt, mode, rows, cols, n, image, codes, scales, csums, out, stream
 
 
 def qg_quantize_gemv(fmt, mode, rows, cols, image, x, codes, scales, csums, err_flag, out, stream=None) -> None:
-    if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32) and fmt in (Q4K, Q6K):
+    if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32) and fmt in FORMATS:
         _need(x, 4 * cols, "x")
-        _check_act(mode, 1, cols, codes, scales, csums)
+        _check_act(fmt, mode, 1, cols, codes, scales, csums)
         _need(err_flag, 4, "err_flag")
         if rows > 0:
             _need(image, qg_image_bytes(fmt, rows, cols), "image")
@@ -184,9 +195,9 @@ def qg_quantize_gemv(fmt, mode, rows, cols, image, x, codes, scales, csums, err_
 def qg_quantize_gemv_argmax(fmt, mode, rows, cols, image, x, codes, scales, csums, err_flag, out, argmax_key,
                             stream=None) -> None:
     """argmax_key: device int64 [1] holding 0 before the call."""
-    if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32) and fmt in (Q4K, Q6K):
+    if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32) and fmt in FORMATS:
         _need(x, 4 * cols, "x")
-        _check_act(mode, 1, cols, codes, scales, csums)
+        _check_act(fmt, mode, 1, cols, codes, scales, csums)
         _need(err_flag, 4, "err_flag")
         _need(argmax_key, 8, "argmax_key")
         if rows > 0:
@@ -206,7 +217,7 @@ def _multi_args(fmt, mode, rows, cols, images, outs):
     nmat = len(rows)
     if not (len(images) == len(outs) == nmat):
         raise QGError(E_INVALID, "rows, images and outs differ in length")
-    if cols > 0 and cols % BLOCK == 0 and fmt in (Q4K, Q6K):
+    if cols > 0 and cols % BLOCK == 0 and fmt in FORMATS:
         for m in range(nmat):
             if rows[m] > 0:
                 _need(images[m], qg_image_bytes(fmt, rows[m], cols), f"images[{m}]")
@@ -223,7 +234,7 @@ def qg_quantize_gemv_multi(fmt, mode, rows, cols, images, x, codes, scales, csum
     nmat, r, im, ou = _multi_args(fmt, mode, rows, cols, images, outs)
     if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32):
         _need(x, 4 * cols, "x")
-        _check_act(mode, 1, cols, codes, scales, csums)
+        _check_act(fmt, mode, 1, cols, codes, scales, csums)
         _need(err_flag, 4, "err_flag")
     _check(_lib.qg_quantize_gemv_multi(fmt, mode, nmat, r, cols, im, _dptr(x), _dptr(codes), _dptr(scales),
                                        _dptr(csums), _dptr(err_flag), ou, _stream(stream)))
@@ -232,7 +243,7 @@ def qg_quantize_gemv_multi(fmt, mode, rows, cols, images, x, codes, scales, csum
 def qg_gemv_q_multi(fmt, mode, rows, cols, images, codes, scales, csums, outs, stream=None) -> None:
     nmat, r, im, ou = _multi_args(fmt, mode, rows, cols, images, outs)
     if cols > 0 and cols % BLOCK == 0 and mode in (PERBLOCK, SUB32):
-        _check_act(mode, 1, cols, codes, scales, csums)
+        _check_act(fmt, mode, 1, cols, codes, scales, csums)
     _check(_lib.qg_gemv_q_multi(fmt, mode, nmat, r, cols, im, _dptr(codes), _dptr(scales), _dptr(csums), ou,
                                 _stream(stream)))
 
@@ -276,7 +287,7 @@ def qg_version() -> int:
 
 # --- convenience wrappers ------------------------------------------------------------------
 
-FMT_CODES = {"q4k": Q4K, "q6k": Q6K}
+FMT_CODES = {"q4k": Q4K, "q6k": Q6K, "q8_0": Q8_0, "q4_0": Q4_0}
 
 
 def pack(fields: dict) -> np.ndarray:
@@ -289,9 +300,12 @@ def pack(fields: dict) -> np.ndarray:
         qg_pack_q4k(rows, cols, c["q"].astype(np.uint8, copy=False), c["sc"].astype(np.uint8, copy=False),
                     c["mn"].astype(np.uint8, copy=False), c["d"].astype(np.uint16, copy=False),
                     c["dmin"].astype(np.uint16, copy=False), img)
-    else:
+    elif fmt == Q6K:
         qg_pack_q6k(rows, cols, c["q"].astype(np.uint8, copy=False), c["sc"].astype(np.int8, copy=False),
                     c["d"].astype(np.uint16, copy=False), img)
+    else:
+        q = c["q"].astype(np.int8 if fmt == Q8_0 else np.uint8, copy=False)
+        qg_pack_b32(fmt, rows, cols, q, c["d"].astype(np.uint16, copy=False), img)
     return img
 
 
@@ -313,9 +327,9 @@ class Act:
         return raw[..., 2].copy(), e
 
 
-def alloc_act(n: int, cols: int, mode: int, device="cuda"):
+def alloc_act(n: int, cols: int, mode: int, device="cuda", fmt: int = Q4K):
     import torch
-    nsc = cols // (BLOCK if mode == PERBLOCK else 32)
+    nsc = _nsc(fmt, mode, cols)
     codes = torch.empty((n, cols), dtype=torch.int8, device=device)
     scales = torch.empty((n, nsc), dtype=torch.int32, device=device)
     csums = torch.empty((n, cols // 16), dtype=torch.int32, device=device)
@@ -327,7 +341,7 @@ def quantize_act(x, mode: int, fmt: int = Q4K, err_flag=None, stream=None, out: 
     if x.dim() == 1:
         x = x.unsqueeze(0)
     n, cols = x.shape
-    a = out if out is not None else alloc_act(n, cols, mode, x.device)
+    a = out if out is not None else alloc_act(n, cols, mode, x.device, fmt)
     qg_quantize_act(fmt, mode, n, cols, x, a.codes, a.scales, a.csums, err_flag, stream)
     return a
 
@@ -345,7 +359,7 @@ def quantize_gemv(fmt: int, rows: int, cols: int, image, x, mode: int, act: Act 
     """One f32 activation row x [C] on the GPU: quantize and multiply in one call.
     Returns (out [rows], the Act holding the quantized row)."""
     import torch
-    a = act if act is not None else alloc_act(1, cols, mode, x.device)
+    a = act if act is not None else alloc_act(1, cols, mode, x.device, fmt)
     if out is None:
         out = torch.empty(rows, dtype=torch.float32, device=x.device)
     qg_quantize_gemv(fmt, mode, rows, cols, image, x, a.codes, a.scales, a.csums, err_flag, out, stream)

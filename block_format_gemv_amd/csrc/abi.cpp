@@ -65,7 +65,7 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int check_fmt_mode(const char *who, int fmt, int mode)
 {
-    if (fmt != QG_Q4K && fmt != QG_Q6K) return fail(QG_E_INVALID, "%s: unknown format %d", who, fmt);
+    if (fmt < QG_Q4K || fmt > QG_Q4_0) return fail(QG_E_INVALID, "%s: unknown format %d", who, fmt);
     if (mode != QG_PERBLOCK && mode != QG_SUB32) return fail(QG_E_INVALID, "%s: unknown scaling %d", who, mode);
     if (!qg_reads(fmt, mode)) return fail(QG_E_UNSUPPORTED, "%s: format %d is not read under scaling %d", who, fmt, mode);
     return QG_OK;
@@ -105,7 +105,7 @@ const char *qg_last_error(void) { return g_reason; }
 
 int qg_reads(int fmt, int mode)
 {
-    const bool f = fmt == QG_Q4K || fmt == QG_Q6K;
+    const bool f = fmt == QG_Q4K || fmt == QG_Q6K || fmt == QG_Q8_0 || fmt == QG_Q4_0;
     const bool m = mode == QG_PERBLOCK || mode == QG_SUB32;
     return f && m ? 1 : 0;
 }
@@ -153,7 +153,7 @@ int qg_quantize_act(int fmt, int mode, int64_t n, int64_t cols, const float *x, 
     if ((st = check_ptr(who, "x", x, 16))) return st;
     if ((st = check_act(who, codes, scales, csums))) return st;
     if (err_flag && !aligned(err_flag, 4)) return fail(QG_E_INVALID, "%s: err_flag is not 4-byte aligned", who);
-    return launch_quantize(mode, QG_BLOCK, n, cols, x, codes, scales, csums, err_flag,
+    return launch_quantize(mode, act_block(fmt, mode), n, cols, x, codes, scales, csums, err_flag,
                            static_cast<hipStream_t>(stream));
 }
 
@@ -208,7 +208,7 @@ static int quantize_gemv_common(const char *who, int fmt, int mode, int64_t rows
         return launch_gemv_fused(fmt, mode, rows, cols, image, x, codes, scales, csums, err_flag, out,
                                  reinterpret_cast<unsigned long long *>(argmax_key), s);
     // no rows to multiply: only the quantized row
-    return launch_quantize(mode, QG_BLOCK, 1, cols, x, codes, scales, csums, err_flag, s);
+    return launch_quantize(mode, act_block(fmt, mode), 1, cols, x, codes, scales, csums, err_flag, s);
 }
 
 int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *image, const float *x,
@@ -264,7 +264,7 @@ int qg_quantize_gemv_multi(int fmt, int mode, int nmat, const int64_t *rows, int
     const hipStream_t s = static_cast<hipStream_t>(stream);
     int64_t total = 0;
     for (int m = 0; m < nmat; m++) total += rows[m];
-    if (total == 0) return launch_quantize(mode, QG_BLOCK, 1, cols, x, codes, scales, csums, err_flag, s);
+    if (total == 0) return launch_quantize(mode, act_block(fmt, mode), 1, cols, x, codes, scales, csums, err_flag, s);
     // the quantized row is written by the launch's first workgroup, which belongs to the
     // first matrix with rows
     return launch_gemv_multi(fmt, mode, nmat, rows, cols, images, x, nullptr, nullptr, codes, scales, csums, err_flag,
@@ -298,7 +298,8 @@ int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const 
 {
     const char *who = "qg_block_sums";
     int st;
-    if (fmt != QG_Q4K && fmt != QG_Q6K) return fail(QG_E_INVALID, "%s: unknown format %d", who, fmt);
+    if (fmt < QG_Q4K || fmt > QG_Q4_0) return fail(QG_E_INVALID, "%s: unknown format %d", who, fmt);
+    if (is_b32(fmt)) return fail(QG_E_UNSUPPORTED, "%s: no sub-block sums view for format %d", who, fmt);
     if ((st = check_cols(who, cols))) return st;
     if (rows < 0 || rows > 0x7fffffff) return fail(QG_E_SHAPE, "%s: rows %lld out of range", who, (long long)rows);
     if (rows == 0) return QG_OK;

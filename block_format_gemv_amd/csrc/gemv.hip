@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "qg_device.hpp"
 #include "qg_internal.hpp"
 
@@ -271,6 +273,34 @@ struct TileRegs<QG_Q6K> {
     }
 };
 
+// The 32-element-block formats: eight blocks per tile, their eight binary16 scales in one
+// 16-byte load per lane.
+template <>
+struct TileRegs<QG_Q8_0> {
+    static constexpr int kBytes = kTileBytesQ8_0;
+    uint4 w[16];    // int8 codes of elements 16i .. 16i+15
+    uint4 d;        // binary16 bits of the eight blocks' scales
+    __device__ __forceinline__ void load(const uint8_t *tile, int lane)
+    {
+#pragma unroll
+        for (int i = 0; i < 16; i++) w[i] = ld_stream(tile + 1024 * i + 16 * lane);
+        d = ld_stream(tile + 16384 + 16 * lane);
+    }
+};
+
+template <>
+struct TileRegs<QG_Q4_0> {
+    static constexpr int kBytes = kTileBytesQ4_0;
+    uint4 w[8];     // block i's 32 codes, nibble-split as in the Q4_K-style tile
+    uint4 d;        // binary16 bits of the eight blocks' scales
+    __device__ __forceinline__ void load(const uint8_t *tile, int lane)
+    {
+#pragma unroll
+        for (int i = 0; i < 8; i++) w[i] = ld_stream(tile + 1024 * i + 16 * lane);
+        d = ld_stream(tile + 8192 + 16 * lane);
+    }
+};
+
 // ---------------------------------------------------------------------------------------
 // The piece of one (row, block) pair for one activation column.
 
@@ -353,6 +383,65 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q6K> &T, int b, co
             e[j] = s.e + d.ex;
         }
         return exact_sum<8>(v, e);
+    }
+}
+
+// The eight integer block sums C_j of a 32-element-block tile (w = d*q for Q8_0, d*(q - 8)
+// for Q4_0) against the activation block's codes.  |C_j| <= 32 * 128 * 127 < 2^19.
+__device__ __forceinline__ void b32_sums(const TileRegs<QG_Q8_0> &T, const ActWaveCodes &act, int (&C)[8])
+{
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        int P = 0;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const uint4 w = T.w[2 * j + h];
+            const int c = 8 * j + 4 * h;
+            P = sdot4(w.x, act.c[c], P);
+            P = sdot4(w.y, act.c[c + 1], P);
+            P = sdot4(w.z, act.c[c + 2], P);
+            P = sdot4(w.w, act.c[c + 3], P);
+        }
+        C[j] = P;
+    }
+}
+
+__device__ __forceinline__ void b32_sums(const TileRegs<QG_Q4_0> &T, const ActPlanes &act, int (&C)[8])
+{
+    // (q - 8) . a = q . a - 8 * sum(a)
+#pragma unroll
+    for (int j = 0; j < 8; j++) C[j] = q4k_sub(T.w[j], 0, j, act) - 8 * act.sum32(0, j);
+}
+
+// The pieces of one tile row: PerBlock, one per 32-element block, R32(m_j*2^e_j * d_j * C_j)
+// (|C_j| < 2^19, d_j and m_j of 11 and 8 significant bits: the products are exact in f64 and
+// the conversion is the one rounding); Sub32, one per tile, the eight terms summed exactly.
+template <int MODE, int FMT, class Act>
+__device__ __forceinline__ void b32_pieces(const TileRegs<FMT> &T, const Act &act,
+                                           float (&p)[MODE == QG_PERBLOCK ? 8 : 1])
+{
+    int C[8];
+    b32_sums(T, act, C);
+    const uint32_t dw[4] = {T.d.x, T.d.y, T.d.z, T.d.w};
+    if constexpr (MODE == QG_PERBLOCK) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const qg_act_scale s = act.scale(0, j, 8);
+            const double S = __builtin_ldexp((double)s.m, s.e);
+            const double D = (double)f16_value(dw[j >> 1] >> (16 * (j & 1)));
+            p[j] = r32_exact_double((double)C[j] * D * S);
+        }
+    } else {
+        long long v[8];
+        int e[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const F16Scale d = f16_scale((dw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+            const qg_act_scale s = act.scale(0, j, 8);
+            v[j] = (long long)(d.sig * (int)s.m) * C[j];
+            e[j] = s.e + d.ex;
+        }
+        p[0] = exact_sum<8>(v, e);
     }
 }
 
@@ -516,7 +605,8 @@ struct ActRaw<SRC_CODES> {
     uint32_t scale;               // the qg_act_scale word of the lane's activation block
 };
 
-template <int SRC, int MODE>
+// GL = lanes per activation block (64: one scale per 256 elements; 8: one per 32)
+template <int SRC, int GL>
 __device__ __forceinline__ ActRaw<SRC> load_act(const ActIO &io, int b, int lane)
 {
     ActRaw<SRC> r;
@@ -524,18 +614,17 @@ __device__ __forceinline__ ActRaw<SRC> load_act(const ActIO &io, int b, int lane
         r.v = *reinterpret_cast<const float4 *>(io.x + (size_t)b * 256 + 4 * lane);
     } else {
         r.packed = reinterpret_cast<const uint32_t *>(io.codes_in + (size_t)b * 256)[lane];
-        r.scale = io.scales_in[MODE == QG_PERBLOCK ? (size_t)b : (size_t)b * 8 + (lane >> 3)];
+        r.scale = io.scales_in[GL == 64 ? (size_t)b : (size_t)b * 8 + (lane >> 3)];
     }
     return r;
 }
 
 // Quantizes one block; workgroup 0 (emit) writes block b < G out.
-template <int MODE>
+template <int BITS, int GROUP_LANES>
 __device__ __forceinline__ ActWave quantize_block_in_wave(float4 v, int b, int G, int lane, bool emit,
                                                           const ActIO &io)
 {
-    constexpr int GROUP_LANES = MODE == QG_PERBLOCK ? 64 : 8;
-    const QuantLane q = quantize_lane<MODE>(v);
+    const QuantLane q = quantize_lane<BITS, GROUP_LANES>(v);
     ActWave a;
     a.packed = q.packed;
     a.s16 = quad_sum(q.sum4);                  // sums of 16 consecutive codes = 4 lanes
@@ -560,11 +649,11 @@ __device__ __forceinline__ ActWave quantize_block_in_wave(float4 v, int b, int G
     return a;
 }
 
-template <int SRC, int MODE>
+template <int SRC, int BITS, int GL>
 __device__ __forceinline__ ActWave ready_act(const ActRaw<SRC> &r, int b, int G, int lane, bool emit, const ActIO &io)
 {
     if constexpr (SRC == SRC_F32) {
-        return quantize_block_in_wave<MODE>(r.v, b, G, lane, emit, io);
+        return quantize_block_in_wave<BITS, GL>(r.v, b, G, lane, emit, io);
     } else {
         ActWave a;
         a.packed = r.packed;
@@ -607,6 +696,7 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
 {
     extern __shared__ __align__(16) float s_piece[];
     using T = TileRegs<FMT>;
+    constexpr int BITS = ActKind<FMT, MODE>::kBits, GL = ActKind<FMT, MODE>::kLanes;
     int m = 0;                                   // this workgroup's matrix (wave-uniform)
     while (m + 1 < tg.nmat && (int)blockIdx.x >= tg.gstart[m + 1]) m++;
     const int g = (int)blockIdx.x - tg.gstart[m];
@@ -620,13 +710,13 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
     // the first block's activations, then its tile: both loads unconditional (a wave past
     // the last block works on a copy of it and stores nothing), kept in this order
     const int bf = min(wid, G - 1);
-    ActRaw<SRC> r0 = load_act<SRC, MODE>(io, bf, lane);
+    ActRaw<SRC> r0 = load_act<SRC, GL>(io, bf, lane);
     __builtin_amdgcn_sched_barrier(0);
     T t0;
     [[maybe_unused]] T t1;
     t0.load(gbase + (size_t)bf * T::kBytes, lane);
     load_fence();
-    ActWave a0 = ready_act<SRC, MODE>(r0, wid, G, lane, emit, io);
+    ActWave a0 = ready_act<SRC, BITS, GL>(r0, wid, G, lane, emit, io);
 
     // Every use of the first tile is unconditional too, so the compiler cannot sink its loads
     // below the wait for the activation load.
@@ -638,24 +728,24 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
             const int b1 = b + W;
             ActRaw<SRC> r1;
             if (b1 < G) {
-                r1 = load_act<SRC, MODE>(io, b1, lane);
+                r1 = load_act<SRC, GL>(io, b1, lane);
                 __builtin_amdgcn_sched_barrier(0);
                 t1.load(gbase + (size_t)b1 * T::kBytes, lane);
                 load_fence();
             }
             s_piece[(size_t)b * 64 + lane] = piece_one<FMT, MODE>(t0, b, a0);
             if (b1 >= G) break;
-            const ActWave a1 = ready_act<SRC, MODE>(r1, b1, G, lane, emit, io);
+            const ActWave a1 = ready_act<SRC, BITS, GL>(r1, b1, G, lane, emit, io);
             const int b2 = b + 2 * W;
             if (b2 < G) {
-                r0 = load_act<SRC, MODE>(io, b2, lane);
+                r0 = load_act<SRC, GL>(io, b2, lane);
                 __builtin_amdgcn_sched_barrier(0);
                 t0.load(gbase + (size_t)b2 * T::kBytes, lane);
                 load_fence();
             }
             s_piece[(size_t)b1 * 64 + lane] = piece_one<FMT, MODE>(t1, b1, a1);
             if (b2 >= G) break;
-            a0 = ready_act<SRC, MODE>(r0, b2, G, lane, emit, io);
+            a0 = ready_act<SRC, BITS, GL>(r0, b2, G, lane, emit, io);
             b = b2;
         } while (true);
     } else {
@@ -674,6 +764,101 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
         if (row < rows) out[row] = y;
         if (io.argmax) {
             // the largest key of the group's 64 rows, then one atomic max per workgroup
+            unsigned long long k = argmax_key(y, row, row < rows);
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const unsigned long long o = __shfl_xor(k, off, 64);
+                k = o > k ? o : k;
+            }
+            if (lane == 0 && k != 0ull) atomicMax(io.argmax, k);
+        }
+    }
+}
+
+// One activation column over a 32-element-block format.  A row has up to eight pieces per
+// tile (PerBlock), too many to park all of a long row's in LDS, so the workgroup goes through
+// its blocks in rounds of W (wave w takes block rW + w of round r): each round's pieces go to
+// one of two LDS slots, and after the round's barrier the first wave adds them to its rows'
+// running sums, in block order, while the others start the next round.  The next barrier
+// falls after that fold, so a slot is written again only once it has been read.
+template <int FMT, int MODE, int SRC, int W>
+__global__ __launch_bounds__(64 * W) void gemv1_b32_kernel(const Targets tg, int G, ActIO io)
+{
+    constexpr int PPT = MODE == QG_PERBLOCK ? 8 : 1;      // pieces per tile row
+    constexpr int BITS = ActKind<FMT, MODE>::kBits, GL = ActKind<FMT, MODE>::kLanes;
+    __shared__ __align__(16) float s_ring[2][W * PPT * 64];
+    using T = TileRegs<FMT>;
+    using A = typename std::conditional<FMT == QG_Q4_0, ActPlanes, ActWaveCodes>::type;
+    int m = 0;
+    while (m + 1 < tg.nmat && (int)blockIdx.x >= tg.gstart[m + 1]) m++;
+    const int g = (int)blockIdx.x - tg.gstart[m];
+    const int rows = tg.rows[m];
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool emit = blockIdx.x == 0;
+    const uint8_t *gbase = tg.image[m] + (size_t)g * G * T::kBytes;
+    const int R = (G + W - 1) / W;                         // rounds; every wave goes through all
+
+    float y = 0.0f;                                        // first wave: its row's running sum
+    auto round = [&](const T &t, const ActWave &a, int r, int b) {
+        float p[PPT];
+        {
+            const A act(a);
+            __builtin_amdgcn_sched_barrier(0);
+            b32_pieces<MODE>(t, act, p);
+        }
+        float *slot = s_ring[r & 1];
+        if (b < G) {
+#pragma unroll
+            for (int j = 0; j < PPT; j++) slot[(wid * PPT + j) * 64 + lane] = p[j];
+        }
+        __syncthreads();
+        if (wid == 0) {
+            const int nb = min(W, G - r * W);
+            for (int k = 0; k < nb * PPT; k++) y = fadd_ftz(y, slot[k * 64 + lane]);
+        }
+    };
+
+    // a block past the end (last round) is worked on as a copy of the last block and dropped
+    int b = wid;
+    ActRaw<SRC> r0 = load_act<SRC, GL>(io, min(b, G - 1), lane);
+    __builtin_amdgcn_sched_barrier(0);
+    T t0;
+    T t1;
+    t0.load(gbase + (size_t)min(b, G - 1) * T::kBytes, lane);
+    load_fence();
+    ActWave a0 = ready_act<SRC, BITS, GL>(r0, b, G, lane, emit, io);
+    int r = 0;
+    do {
+        const int b1 = b + W;
+        ActRaw<SRC> r1;
+        if (r + 1 < R) {
+            r1 = load_act<SRC, GL>(io, min(b1, G - 1), lane);
+            __builtin_amdgcn_sched_barrier(0);
+            t1.load(gbase + (size_t)min(b1, G - 1) * T::kBytes, lane);
+            load_fence();
+        }
+        round(t0, a0, r, b);
+        if (++r >= R) break;
+        const ActWave a1 = ready_act<SRC, BITS, GL>(r1, b1, G, lane, emit, io);
+        const int b2 = b1 + W;
+        if (r + 1 < R) {
+            r0 = load_act<SRC, GL>(io, min(b2, G - 1), lane);
+            __builtin_amdgcn_sched_barrier(0);
+            t0.load(gbase + (size_t)min(b2, G - 1) * T::kBytes, lane);
+            load_fence();
+        }
+        round(t1, a1, r, b1);
+        if (++r >= R) break;
+        a0 = ready_act<SRC, BITS, GL>(r0, b2, G, lane, emit, io);
+        b = b2;
+    } while (true);
+
+    if (wid == 0) {
+        const int64_t row = (int64_t)g * 64 + lane;
+        y = canon_nan(y);
+        if (row < rows) tg.out[m][row] = y;
+        if (io.argmax) {
             unsigned long long k = argmax_key(y, row, row < rows);
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) {
@@ -780,9 +965,41 @@ int launch_one(const Targets &tg, int G, const ActIO &io, hipStream_t s)
     return launch_one_typed<FMT, MODE, SRC, 4, false>(tg, G, io, s);
 }
 
+template <int FMT, int MODE, int SRC, int W>
+int launch_b32_typed(const Targets &tg, int G, const ActIO &io, hipStream_t s)
+{
+    const int64_t groups = tg.gstart[tg.nmat];
+    if (groups == 0) return QG_OK;
+    hipEvent_t ev0, ev1;
+    take_timing_events(&ev0, &ev1);
+    if (ev0 && ev1)
+        hipExtLaunchKernelGGL((gemv1_b32_kernel<FMT, MODE, SRC, W>), dim3((unsigned)groups), dim3(64 * W), 0, s, ev0,
+                              ev1, 0, tg, G, io);
+    else
+        hipLaunchKernelGGL((gemv1_b32_kernel<FMT, MODE, SRC, W>), dim3((unsigned)groups), dim3(64 * W), 0, s, tg, G,
+                           io);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemv launch: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+template <int FMT, int MODE, int SRC>
+int launch_b32(const Targets &tg, int G, const ActIO &io, hipStream_t s)
+{
+    // 8 waves a workgroup (the tuning knob may ask for 4; 16 is taken as 8), 4 for short rows
+    int w = tuning().waves_per_wg;
+    if (w <= 0) w = G >= 8 ? 8 : 4;
+    if (w >= 8) return launch_b32_typed<FMT, MODE, SRC, 8>(tg, G, io, s);
+    return launch_b32_typed<FMT, MODE, SRC, 4>(tg, G, io, s);
+}
+
 template <int SRC>
 int launch_one_any(int fmt, int mode, const Targets &tg, int G, const ActIO &io, hipStream_t s)
 {
+    if (fmt == QG_Q8_0 && mode == QG_PERBLOCK) return launch_b32<QG_Q8_0, QG_PERBLOCK, SRC>(tg, G, io, s);
+    if (fmt == QG_Q8_0 && mode == QG_SUB32) return launch_b32<QG_Q8_0, QG_SUB32, SRC>(tg, G, io, s);
+    if (fmt == QG_Q4_0 && mode == QG_PERBLOCK) return launch_b32<QG_Q4_0, QG_PERBLOCK, SRC>(tg, G, io, s);
+    if (fmt == QG_Q4_0 && mode == QG_SUB32) return launch_b32<QG_Q4_0, QG_SUB32, SRC>(tg, G, io, s);
     if (fmt == QG_Q4K && mode == QG_PERBLOCK) return launch_one<QG_Q4K, QG_PERBLOCK, SRC>(tg, G, io, s);
     if (fmt == QG_Q4K && mode == QG_SUB32) return launch_one<QG_Q4K, QG_SUB32, SRC>(tg, G, io, s);
     if (fmt == QG_Q6K && mode == QG_PERBLOCK) return launch_one<QG_Q6K, QG_PERBLOCK, SRC>(tg, G, io, s);
@@ -921,13 +1138,19 @@ int launch_gemv(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, con
 {
     if (rows == 0 || ncol == 0) return QG_OK;
     const int G = (int)(cols / 256);
-    if (ncol == 1) {
-        const ActIO io{nullptr, codes, reinterpret_cast<const uint32_t *>(scales), nullptr, nullptr, nullptr, nullptr,
-                       nullptr};
-        Targets tg;
-        const int st = make_targets(1, &rows, &image, &out, tg);
-        if (st != QG_OK) return st;
-        return launch_one_any<SRC_CODES>(fmt, mode, tg, G, io, s);
+    if (ncol == 1 || is_b32(fmt)) {
+        // one launch per column (the 32-element-block formats have no several-column kernel)
+        const int64_t nsc = act_block(fmt, mode) == 256 ? G : (int64_t)G * 8;
+        for (int64_t c = 0; c < ncol; c++) {
+            const ActIO io{nullptr, codes + c * cols, reinterpret_cast<const uint32_t *>(scales + c * nsc), nullptr,
+                           nullptr, nullptr, nullptr, nullptr};
+            Targets tg;
+            float *oc = out + c * rows;
+            int st = make_targets(1, &rows, &image, &oc, tg);
+            if (st == QG_OK) st = launch_one_any<SRC_CODES>(fmt, mode, tg, G, io, s);
+            if (st != QG_OK) return st;
+        }
+        return QG_OK;
     }
     if (fmt == QG_Q4K && mode == QG_PERBLOCK)
         return launch_nc<QG_Q4K, QG_PERBLOCK>(rows, G, ncol, image, codes, scales, csums, out, s);

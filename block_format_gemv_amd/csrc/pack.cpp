@@ -24,10 +24,12 @@ using namespace qg;
 
 extern "C" size_t qg_image_bytes(int fmt, int64_t rows, int64_t cols)
 {
-    if ((fmt != QG_Q4K && fmt != QG_Q6K) || rows < 0 || cols <= 0 || cols % QG_BLOCK) return 0;
+    if ((fmt < QG_Q4K || fmt > QG_Q4_0) || rows < 0 || cols <= 0 || cols % QG_BLOCK) return 0;
     const int64_t groups = (rows + kTileRows - 1) / kTileRows;
     const int64_t tiles = groups * (cols / QG_BLOCK);
-    return (size_t)tiles * (size_t)(fmt == QG_Q4K ? kTileBytesQ4K : kTileBytesQ6K);
+    const int tb = fmt == QG_Q4K ? kTileBytesQ4K : fmt == QG_Q6K ? kTileBytesQ6K : fmt == QG_Q8_0 ? kTileBytesQ8_0
+                                                                                                 : kTileBytesQ4_0;
+    return (size_t)tiles * (size_t)tb;
 }
 
 extern "C" int qg_pack_q4k(int64_t rows, int64_t cols, const uint8_t *q, const uint8_t *sc, const uint8_t *mn,
@@ -128,6 +130,52 @@ extern "C" int qg_pack_q6k(int64_t rows, int64_t cols, const uint8_t *q, const i
         const uint16_t dv = d[r * G + b];
         tile[13312 + 2 * l] = (uint8_t)(dv & 0xFF);
         tile[13312 + 2 * l + 1] = (uint8_t)(dv >> 8);
+    }
+    return QG_OK;
+}
+
+extern "C" int qg_pack_b32(int fmt, int64_t rows, int64_t cols, const void *q_host, const uint16_t *d_host,
+                           void *image_host)
+{
+    if (fmt != QG_Q8_0 && fmt != QG_Q4_0) return fail(QG_E_INVALID, "qg_pack_b32: format %d has no 32-element blocks", fmt);
+    if (rows < 0 || cols <= 0 || cols % QG_BLOCK)
+        return fail(QG_E_SHAPE, "qg_pack_b32: cols %lld is not a positive multiple of 256", (long long)cols);
+    if (rows > 0 && (!q_host || !d_host || !image_host)) return fail(QG_E_INVALID, "qg_pack_b32: null pointer");
+    const uint8_t *q = static_cast<const uint8_t *>(q_host);
+    const int64_t G = cols / QG_BLOCK, nb = cols / 32;
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t j = 0; j < nb; j++)
+            if (f16_unreadable(d_host[r * nb + j]))
+                return fail(QG_E_UNREADABLE, "qg_pack_b32: row %lld block %lld has an inf/NaN scale", (long long)r,
+                            (long long)j);
+        if (fmt == QG_Q4_0)
+            for (int64_t i = 0; i < cols; i++)
+                if (q[r * cols + i] > 15)
+                    return fail(QG_E_INVALID, "qg_pack_b32: code %u at row %lld col %lld exceeds 15", q[r * cols + i],
+                                (long long)r, (long long)i);
+    }
+    const int tb = fmt == QG_Q8_0 ? kTileBytesQ8_0 : kTileBytesQ4_0;
+    const int doff = fmt == QG_Q8_0 ? 16384 : 8192;
+    uint8_t *img = static_cast<uint8_t *>(image_host);
+    memset(img, 0, qg_image_bytes(fmt, rows, cols));
+    for (int64_t r = 0; r < rows; r++) for (int64_t b = 0; b < G; b++) {
+        uint8_t *tile = img + ((r / kTileRows) * G + b) * tb;
+        const int l = (int)(r % kTileRows);
+        const uint8_t *qb = q + r * cols + b * QG_BLOCK;
+        if (fmt == QG_Q8_0) {
+            for (int i = 0; i < 16; i++) memcpy(tile + 1024 * i + 16 * l, qb + 16 * i, 16);
+        } else {
+            for (int i = 0; i < 8; i++) {
+                uint8_t *dst = tile + 1024 * i + 16 * l;
+                for (int k = 0; k < 16; k++) dst[k] = (uint8_t)(qb[32 * i + k] | (qb[32 * i + 16 + k] << 4));
+            }
+        }
+        uint8_t *dd = tile + doff + 16 * l;
+        for (int j = 0; j < 8; j++) {
+            const uint16_t dv = d_host[r * nb + b * 8 + j];
+            dd[2 * j] = (uint8_t)(dv & 0xFF);
+            dd[2 * j + 1] = (uint8_t)(dv >> 8);
+        }
     }
     return QG_OK;
 }

@@ -186,8 +186,8 @@ __device__ __forceinline__ float exact_sum(const long long (&v)[N], const int (&
 // ---------------------------------------------------------------------------------------
 // Activation quantization of 256 consecutive elements by one wave, four per lane (lane l
 // holds elements 4l..4l+3) ("Module numerics": Functions absmax, wide_scale, block_scale,
-// rne_div, quantize, quantize_blocks).  One PerBlock block spans the wave; a Sub32 block
-// spans eight lanes.
+// rne_div, quantize, quantize_blocks).  A block of 256 elements spans the wave, one of 32
+// spans eight lanes: BITS significant bits (8 PerBlock, 4 Sub32) over GL lanes (64 or 8).
 //
 // The scale comes from amax/127 in f64: the quotient is within 2^-53 of amax/127, and the
 // nearest grid point of `bits` significant bits lies at least 2^-25 of it away unless it
@@ -240,10 +240,17 @@ struct QuantLane {
     int inf;           // the lane's activation block holds an infinity
 };
 
-template <int MODE>
+// significand bits and lanes per activation block of a (format, scaling)
+template <int FMT, int MODE>
+struct ActKind {
+    static constexpr int kBits = MODE == QG_PERBLOCK ? 8 : 4;
+    static constexpr int kLanes = (MODE == QG_SUB32 || FMT == QG_Q8_0 || FMT == QG_Q4_0) ? 8 : 64;
+};
+
+template <int BITS, int GL>
 __device__ __forceinline__ QuantLane quantize_lane(float4 v4)
 {
-    constexpr int BITS = MODE == QG_PERBLOCK ? 8 : 4;
+    static_assert(GL == 8 || GL == 64, "activation blocks of 32 or 256 elements");
     const float v[4] = {ftz(v4.x), ftz(v4.y), ftz(v4.z), ftz(v4.w)};
     // largest magnitude, NaN passed over; non-negative floats order as integers, and an
     // infinity is the largest value left
@@ -256,8 +263,8 @@ __device__ __forceinline__ QuantLane quantize_lane(float4 v4)
     auto umax = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
     amax_bits = umax(amax_bits, (uint32_t)dpp<kDppQuadSwap1>((int)amax_bits));
     amax_bits = umax(amax_bits, (uint32_t)dpp<kDppQuadSwap2>((int)amax_bits));
-    amax_bits = umax(amax_bits, (uint32_t)dpp<kDppHalfMirror>((int)amax_bits));   // 8 lanes: a Sub32 block
-    if constexpr (MODE == QG_PERBLOCK) {
+    amax_bits = umax(amax_bits, (uint32_t)dpp<kDppHalfMirror>((int)amax_bits));   // 8 lanes: 32 elements
+    if constexpr (GL == 64) {
         amax_bits = umax(amax_bits, (uint32_t)dpp<kDppRowMirror>((int)amax_bits));  // 16 lanes
         const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)amax_bits, 0);
         const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)amax_bits, 16);

@@ -12,6 +12,13 @@ namespace qg {
 constexpr int kTileRows = 64;     // rows per tile (one 256-element block each)
 constexpr int kTileBytesQ4K = 64 * 144;   // 9216
 constexpr int kTileBytesQ6K = 64 * 210;   // 13440
+constexpr int kTileBytesQ8_0 = 64 * 272;  // 17408
+constexpr int kTileBytesQ4_0 = 64 * 144;  // 9216
+
+// formats with 32-element weight blocks (PerBlock activation blocks of 32 too)
+constexpr bool is_b32(int fmt) { return fmt == QG_Q8_0 || fmt == QG_Q4_0; }
+// elements per activation scale for (format, scaling)
+constexpr int act_block(int fmt, int mode) { return (mode == QG_SUB32 || is_b32(fmt)) ? 32 : 256; }
 
 // per-thread failure reason
 int fail(int status, const char *fmt, ...);
@@ -30,6 +37,7 @@ int device_cu_count();   // compute units of the current device
 void take_timing_events(hipEvent_t *start, hipEvent_t *stop);
 
 // kernel launchers (return QG_OK or a failure already reported through fail())
+// block: elements per activation scale (act_block)
 int launch_quantize(int mode, int block, int64_t n, int64_t cols, const float *x, int8_t *codes,
                     qg_act_scale *scales, int32_t *csums, int32_t *err_flag, hipStream_t s);
 

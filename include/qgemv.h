@@ -38,15 +38,17 @@
 extern "C" {
 #endif
 
-/* Weight block formats.  Both use 256-element blocks. */
+/* Weight block formats.  The first two use 256-element blocks, the last two 32-element ones. */
 typedef enum {
     QG_Q4K = 1,   /* 4-bit codes, 8 sub-blocks of 32 with 6-bit scale and offset, f16 d, dmin */
-    QG_Q6K = 2    /* 6-bit codes offset by -32, 16 sub-blocks of 16 with int8 scales, f16 d */
+    QG_Q6K = 2,   /* 6-bit codes offset by -32, 16 sub-blocks of 16 with int8 scales, f16 d */
+    QG_Q8_0 = 3,  /* 32-element blocks: int8 codes, one f16 d per block (w = d*q) */
+    QG_Q4_0 = 4   /* 32-element blocks: 4-bit codes offset by -8, one f16 d per block (w = d*(q-8)) */
 } qg_format;
 
 /* How an activation row is scaled ("Module numerics", Enums ActScaling). */
 typedef enum {
-    QG_PERBLOCK = 0,  /* one scale per 256-element weight block, m in 128..255 */
+    QG_PERBLOCK = 0,  /* one scale per weight block (256 or 32 elements), m in 128..255 */
     QG_SUB32 = 1      /* one scale per 32 elements, m in 8..15; a 256-group rounds once */
 } qg_act_scaling;
 
@@ -74,7 +76,7 @@ typedef enum {
 #define QG_MAX_MATRICES 8     /* matrices per qg_*_multi call */
 
 /* Whether the kernels read matrices of `fmt` under `mode` ("Module numerics", Functions
- * reads).  1 for (Q4K, PerBlock), (Q4K, Sub32), (Q6K, PerBlock), (Q6K, Sub32); else 0. */
+ * reads).  1 for each of the four formats under PerBlock and Sub32; else 0. */
 int qg_reads(int fmt, int mode);
 
 /*
@@ -103,10 +105,21 @@ int qg_reads(int fmt, int mode);
  *       0-1, 2-3, 4-5, 6-7.
  *   scales at byte 12288, 16 bytes per lane: sub-block k's int8 scale in byte k.
  *   d at byte 13312, 2 bytes per lane: binary16 bits.
+ *
+ * The 32-element-block formats keep the same tiles of 64 rows x 256 elements (eight of
+ * their blocks):
+ * Q8_0-style tile, 17408 bytes (= 64 x 272):
+ *   chunk i (i = 0..15) at byte 1024*i, 16 bytes per lane: the int8 codes of elements
+ *       16i .. 16i+15 of the tile.
+ *   d at byte 16384, 16 bytes per lane: the binary16 bits of the eight blocks' scales.
+ * Q4_0-style tile, 9216 bytes (= 64 x 144):
+ *   chunk i (i = 0..7) at byte 1024*i: block i's 32 codes, nibble-split as in the Q4_K-style
+ *       tile (byte k: element 32i+k low, 32i+16+k high).
+ *   d at byte 8192, 16 bytes per lane: the binary16 bits of the eight blocks' scales.
  */
 
-/* Bytes of the image of an R x C matrix: ceil(R/64) * (C/256) * 64 * (144 or 210).
- * 0 for a bad format or shape. */
+/* Bytes of the image of an R x C matrix: ceil(R/64) * (C/256) * 64 * (144, 210, 272 or 144
+ * for Q4_K, Q6_K, Q8_0, Q4_0).  0 for a bad format or shape. */
 size_t qg_image_bytes(int fmt, int64_t rows, int64_t cols);
 
 /* Pack Q4_K-style logical fields (host memory, row-major) into an image (host memory,
@@ -133,11 +146,22 @@ int qg_pack_q4k(int64_t rows, int64_t cols, const uint8_t *q_host, const uint8_t
 int qg_pack_q6k(int64_t rows, int64_t cols, const uint8_t *q_host, const int8_t *sc_host,
                 const uint16_t *d_host, void *image_host);
 
+/* Pack a matrix with 32-element blocks ("Module numerics", module description: the matrix
+ * format's own block, 32 or 256 elements) into an image (host memory):
+ *   fmt  QG_Q8_0: q int8 [rows][cols] codes, w = d*q
+ *        QG_Q4_0: q uint8 [rows][cols] codes 0..15, w = d*(q - 8)
+ *   q    [rows][cols] as above (passed as bytes)
+ *   d    uint16 [rows][cols/32]  binary16 bits of each block's scale
+ * Errors as qg_pack_q4k (the reason of QG_E_UNREADABLE names the row and 32-element block). */
+int qg_pack_b32(int fmt, int64_t rows, int64_t cols, const void *q_host, const uint16_t *d_host,
+                void *image_host);
+
 /* Quantize n activation rows ("Module numerics", Functions quantize_blocks (PerBlock) and
  * quantize (Sub32), absmax, wide_scale, block_scale, rne_div):
  *   x       f32 [n][cols]                       device
  *   codes   int8 [n][cols]                      device, out: rne(x / s), |code| <= 127
- *   scales  qg_act_scale [n][cols/B]            device, out; B = 256 (PerBlock) or 32 (Sub32)
+ *   scales  qg_act_scale [n][cols/B]            device, out; B = 32 under Sub32; under PerBlock
+ *                                                the weight format's block (256 or 32)
  *   csums   int32 [n][cols/16]                  device, out: sum of the codes of each run of
  *                                                16 elements (the activation-side unit sums
  *                                                of "Module lane")
@@ -146,7 +170,8 @@ int qg_pack_q6k(int64_t rows, int64_t cols, const uint8_t *q_host, const int8_t 
  *                                                before the call).  May be NULL.
  * Each element is read with denormals as zero; the scale is the least m*2^e with
  * 127*m*2^e >= the block's largest magnitude (NaN passed over); a NaN element gets code 0.
- * fmt selects the PerBlock block (256 for both formats). */
+ * fmt selects the PerBlock block: the weight format's own (256 for Q4_K and Q6_K, 32 for
+ * Q8_0 and Q4_0), so scales are [n][cols/32] whenever mode is Sub32 or fmt is Q8_0 / Q4_0. */
 int qg_quantize_act(int fmt, int mode, int64_t n, int64_t cols, const float *x, int8_t *codes,
                     qg_act_scale *scales, int32_t *csums, int32_t *err_flag, void *stream);
 
@@ -215,7 +240,8 @@ int qg_gemv_q_multi(int fmt, int mode, int nmat, const int64_t *rows, int64_t co
  *        osum_out int32 [rows][cols/32] = sum mn_j*c.
  *   Q6K: csum_out int32 [rows][cols/16] = sum sc_k*(q-32)*c over sub-block k; osum_out is
  *        not written (may be NULL).
- * A debugging view of the kernels' integer stage. */
+ * A debugging view of the kernels' integer stage; Q4_K and Q6_K only (QG_E_UNSUPPORTED
+ * otherwise). */
 int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
                   int32_t *csum_out, int32_t *osum_out, void *stream);
 

@@ -80,6 +80,58 @@ def unpack_q6k(img: np.ndarray, rows: int, cols: int) -> dict:
     return {"q": q, "sc": scs, "d": dd}
 
 
+def unpack_b32(img: np.ndarray, fmt: int, rows: int, cols: int) -> dict:
+    """Q8_0-style: sixteen chunks of 16 int8 codes (elements 16i..16i+15) then the eight f16
+    scales; Q4_0-style: eight nibble-split chunks (one 32-element block each) then the scales."""
+    tb = 17408 if fmt == qg.Q8_0 else 9216
+    t, G, groups = _tiles(img, rows, cols, tb)
+    if fmt == qg.Q8_0:
+        codes = t[..., :16384].reshape(groups, G, 16, 64, 16).transpose(0, 1, 3, 2, 4).reshape(groups, G, 64, 256)
+        dpart = t[..., 16384:]
+    else:
+        ch = t[..., :8192].reshape(groups, G, 8, 64, 16)
+        codes = np.concatenate([ch & 15, ch >> 4], axis=4).transpose(0, 1, 3, 2, 4).reshape(groups, G, 64, 256)
+        dpart = t[..., 8192:]
+    q = codes.transpose(0, 2, 1, 3).reshape(groups * 64, cols)[:rows]
+    if fmt == qg.Q8_0:
+        q = q.view(np.int8)
+    dp = dpart.reshape(groups, G, 64, 8, 2).astype(np.uint16)
+    d = (dp[..., 0] | (dp[..., 1] << 8)).transpose(0, 2, 1, 3).reshape(groups * 64, G * 8)[:rows]
+    return {"q": q, "d": d}
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("rows,cols", [(1, 256), (5, 768), (64, 1024), (70, 512)])
+def test_b32_pack_roundtrip(fmt, rows, cols):
+    f = (gen.q8_0_fields if fmt == "q8_0" else gen.q4_0_fields)(rows, cols, rows * 13 + cols)
+    code = qg.FMT_CODES[fmt]
+    img = qg.pack(f)
+    assert img.nbytes == qg.qg_image_bytes(code, rows, cols)
+    u = unpack_b32(img, code, rows, cols)
+    assert np.array_equal(u["q"], f["q"]) and np.array_equal(u["d"], f["d"])
+    if rows % 64:
+        t, G, groups = _tiles(img, rows, cols, 17408 if code == qg.Q8_0 else 9216)
+        lanes = np.arange(64) >= rows % 64
+        assert not t[-1].reshape(G, -1, 64, 16)[:, :, lanes].any()
+
+
+def test_b32_pack_refusals():
+    f = gen.q4_0_fields(3, 256, 5)
+    f["q"][2, 200] = 16
+    with pytest.raises(qg.QGError) as ei:
+        qg.pack(f)
+    assert ei.value.status == qg.E_INVALID
+    f = gen.q8_0_fields(3, 512, 5)
+    f["d"][1, 9] = 0x7C00                                        # +inf
+    with pytest.raises(qg.QGError) as ei:
+        qg.pack(f)
+    assert ei.value.status == qg.E_UNREADABLE and "row 1" in ei.value.reason
+    img = np.zeros(qg.qg_image_bytes(qg.Q8_0, 3, 512), np.uint8)
+    with pytest.raises(qg.QGError) as ei:
+        qg.qg_pack_b32(qg.Q4K, 3, 512, f["q"], f["d"], img)
+    assert ei.value.status == qg.E_INVALID
+
+
 @pytest.mark.parametrize("rows,cols", [(1, 256), (5, 768), (64, 1024), (3, 2048), (37, 4096), (130, 1280)])
 def test_q4k_pack_roundtrip(rows, cols):
     f = gen.q4k_fields(rows, cols, rows * 7 + cols)
@@ -140,8 +192,10 @@ def test_image_bytes_and_reads():
     assert qg.qg_image_bytes(qg.Q6K, 128256, 4096) == 430_940_160
     assert qg.qg_image_bytes(qg.Q4K, 256, 1024) == 147_456
     assert qg.qg_image_bytes(qg.Q4K, 4, 100) == 0
-    assert qg.qg_image_bytes(3, 4, 256) == 0
-    for fmt in (qg.Q4K, qg.Q6K):
+    assert qg.qg_image_bytes(qg.Q8_0, 14336, 4096) == 14336 // 64 * 16 * 17408
+    assert qg.qg_image_bytes(qg.Q4_0, 65, 512) == 2 * 2 * 9216
+    assert qg.qg_image_bytes(5, 4, 256) == 0 and qg.qg_image_bytes(0, 4, 256) == 0
+    for fmt in qg.FORMATS:
         for mode in (qg.PERBLOCK, qg.SUB32):
             assert qg.qg_reads(fmt, mode)
     assert not qg.qg_reads(0, 0) and not qg.qg_reads(qg.Q4K, 7)
