@@ -84,6 +84,8 @@ WORKLOADS = {
     "q4k_attn_qkv_6144x4096": ("q4k", (("attn", 4096), ("k", 1024), ("v", 1024)), 4096, 0, 1),
     "q4k_attn_4096x4096": ("q4k", 4096, 4096, 0, 1),
     "q6k_output_128256x4096": ("q6k", 128256, 4096, 0, 1),
+    "q8_0_ffn_up_14336x4096": ("q8_0", 14336, 4096, 0, 1),
+    "q4_0_ffn_up_14336x4096": ("q4_0", 14336, 4096, 0, 1),
     "q4k_sub32_14336x4096": ("q4k", 14336, 4096, 1, 1),
     "q4k_gemm_n2_14336x4096": ("q4k", 14336, 4096, 0, 2),
     "q4k_gemm_n8_14336x4096": ("q4k", 14336, 4096, 0, 8),
@@ -157,6 +159,10 @@ def make_inputs(wl, n_act):
         fields = [gen.llama_q4k(name) for name, _ in rows]
     elif fmt == "q4k":
         fields = [gen.q4k_fields(rows, cols, gen.SEED_ATTN_W if rows == 4096 else gen.SEED_FFN_W)]
+    elif fmt == "q8_0":
+        fields = [gen.q8_0_fields(rows, cols, gen.SEED_Q8_W)]
+    elif fmt == "q4_0":
+        fields = [gen.q4_0_fields(rows, cols, gen.SEED_Q4_0_W)]
     else:
         fields = [gen.output_q6k()[0]]
     if ncol > 1:
@@ -184,7 +190,7 @@ def cpu_baseline(mats, xs, mode, seconds, image_bytes):
     outs = []
     while True:
         x = xs[steps % len(xs)]
-        c, m, e, _ = oracle.quantize(x, mode)
+        c, m, e, _ = oracle.quantize(x, mode, block=oracle.act_block(mats[0]["fmt"], mode))
         out = np.concatenate([oracle.gemm(f, c, m, e, mode).reshape(xs[0].shape[0], -1) for f in mats], axis=1)
         if steps < 2:
             outs.append(out)
@@ -240,12 +246,12 @@ def main():
     images = [[b[int(offs[m]):int(offs[m + 1])] for m in range(nmat)] for b in bufs]
     x_dev = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in xs]
     slots = max(copies, 16)
-    acts = [qg.alloc_act(ncol, cols, mode, dev) for _ in range(slots)]
+    acts = [qg.alloc_act(ncol, cols, mode, dev, fmt) for _ in range(slots)]
     outs = [torch.empty((ncol, rows), dtype=torch.float32, device=dev) for _ in range(slots)]
     # per-matrix output views (one column): out[0, row offset of matrix m ...]
     ro = np.concatenate([[0], np.cumsum(mrows)]).astype(np.int64)
     mouts = [[o.view(-1)[int(ro[m]):int(ro[m + 1])] for m in range(nmat)] for o in outs]
-    act_bytes = ncol * (cols + 4 * qg._nsc(mode, cols) + 4 * (cols // 16))
+    act_bytes = ncol * (cols + 4 * qg._nsc(fmt, mode, cols) + 4 * (cols // 16))
     out_bytes = 4 * ncol * rows
     fused = ncol == 1 and not args.two_launch
     if nmat > 1 and ncol != 1:
@@ -277,7 +283,10 @@ def main():
         quantize(i, stream)
         multiply(i, stream)
 
-    if ncol == 1:
+    if ncol == 1 and fmt_s in ("q8_0", "q4_0"):
+        kernel_label = ("gemv1_b32_kernel<..., SRC_F32> (one-launch quantize + GEMV)" if fused
+                        else "gemv1_b32_kernel<..., SRC_CODES> (GEMV of a quantized row)")
+    elif ncol == 1:
         kernel_label = ("gemv1_kernel<..., SRC_F32> (one-launch quantize + GEMV)" if fused
                         else "gemv1_kernel<..., SRC_CODES> (GEMV of a quantized row)")
     elif fmt_s == "q4k" and mode == 0 and ncol >= 8:

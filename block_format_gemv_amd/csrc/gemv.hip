@@ -482,9 +482,7 @@ __device__ __forceinline__ void group_pieces_and_rows(const uint8_t *gbase, int 
         const int64_t row = row0 + lane;
 #pragma unroll
         for (int c = 0; c < NC; c++) {
-            float y = 0.0f;
-            const float *pc = s_piece + (size_t)c * G * 64 + lane;
-            for (int b = 0; b < G; b++) y = fadd_ftz(y, pc[(size_t)b * 64]);
+            const float y = fold_ftz(0.0f, s_piece + (size_t)c * G * 64 + lane, G, 64);
             if (row < rows && col0 + c < ncol) out[(int64_t)(col0 + c) * rows + row] = canon_nan(y);
         }
     }
@@ -758,9 +756,7 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
     // the first wave adds each row's pieces in block order, one row per lane
     if (wid == 0) {
         const int64_t row = (int64_t)g * 64 + lane;
-        float y = 0.0f;
-        for (int b = 0; b < G; b++) y = fadd_ftz(y, s_piece[(size_t)b * 64 + lane]);
-        y = canon_nan(y);
+        float y = canon_nan(fold_ftz(0.0f, s_piece + lane, G, 64));
         if (row < rows) out[row] = y;
         if (io.argmax) {
             // the largest key of the group's 64 rows, then one atomic max per workgroup
@@ -780,13 +776,16 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
 // its blocks in rounds of W (wave w takes block rW + w of round r): each round's pieces go to
 // one of two LDS slots, and after the round's barrier the first wave adds them to its rows'
 // running sums, in block order, while the others start the next round.  The next barrier
-// falls after that fold, so a slot is written again only once it has been read.
-template <int FMT, int MODE, int SRC, int W>
+// falls after that fold, so a slot is written again only once it has been read.  Without DB
+// there is one round (G <= W) and one slot.  Beside its pieces each wave parks, per row,
+// whether one of them is tiny (tiny_piece); a round without one is added with plain adds.
+template <int FMT, int MODE, int SRC, int W, bool DB>
 __global__ __launch_bounds__(64 * W) void gemv1_b32_kernel(const Targets tg, int G, ActIO io)
 {
     constexpr int PPT = MODE == QG_PERBLOCK ? 8 : 1;      // pieces per tile row
+    constexpr int SLOT = W * PPT * 64 + W * 64;           // words per slot: pieces, then tiny flags
     constexpr int BITS = ActKind<FMT, MODE>::kBits, GL = ActKind<FMT, MODE>::kLanes;
-    __shared__ __align__(16) float s_ring[2][W * PPT * 64];
+    extern __shared__ __align__(16) float s_ring[];
     using T = TileRegs<FMT>;
     using A = typename std::conditional<FMT == QG_Q4_0, ActPlanes, ActWaveCodes>::type;
     int m = 0;
@@ -807,15 +806,23 @@ __global__ __launch_bounds__(64 * W) void gemv1_b32_kernel(const Targets tg, int
             __builtin_amdgcn_sched_barrier(0);
             b32_pieces<MODE>(t, act, p);
         }
-        float *slot = s_ring[r & 1];
+        float *slot = s_ring + (DB ? (r & 1) * SLOT : 0);
+        int *tiny = reinterpret_cast<int *>(slot + W * PPT * 64);
         if (b < G) {
+            bool t = false;
 #pragma unroll
-            for (int j = 0; j < PPT; j++) slot[(wid * PPT + j) * 64 + lane] = p[j];
+            for (int j = 0; j < PPT; j++) {
+                slot[(wid * PPT + j) * 64 + lane] = p[j];
+                t |= tiny_piece(p[j]);
+            }
+            tiny[wid * 64 + lane] = t;
         }
         __syncthreads();
         if (wid == 0) {
             const int nb = min(W, G - r * W);
-            for (int k = 0; k < nb * PPT; k++) y = fadd_ftz(y, slot[k * 64 + lane]);
+            int t = 0;
+            for (int w = 0; w < nb; w++) t |= tiny[w * 64 + lane];
+            y = fold_flagged(y, slot + lane, nb * PPT, 64, t != 0);
         }
     };
 
@@ -824,12 +831,14 @@ __global__ __launch_bounds__(64 * W) void gemv1_b32_kernel(const Targets tg, int
     ActRaw<SRC> r0 = load_act<SRC, GL>(io, min(b, G - 1), lane);
     __builtin_amdgcn_sched_barrier(0);
     T t0;
-    T t1;
+    [[maybe_unused]] T t1;
     t0.load(gbase + (size_t)min(b, G - 1) * T::kBytes, lane);
     load_fence();
     ActWave a0 = ready_act<SRC, BITS, GL>(r0, b, G, lane, emit, io);
     int r = 0;
-    do {
+    if constexpr (!DB) {
+        round(t0, a0, 0, b);
+    } else do {
         const int b1 = b + W;
         ActRaw<SRC> r1;
         if (r + 1 < R) {
@@ -965,19 +974,21 @@ int launch_one(const Targets &tg, int G, const ActIO &io, hipStream_t s)
     return launch_one_typed<FMT, MODE, SRC, 4, false>(tg, G, io, s);
 }
 
-template <int FMT, int MODE, int SRC, int W>
+template <int FMT, int MODE, int SRC, int W, bool DB>
 int launch_b32_typed(const Targets &tg, int G, const ActIO &io, hipStream_t s)
 {
     const int64_t groups = tg.gstart[tg.nmat];
     if (groups == 0) return QG_OK;
+    if (!DB && G > W) return fail(QG_E_RUNTIME, "gemv: %d blocks do not fit one round of %d waves", G, W);
+    const size_t lds = (DB ? 2 : 1) * (size_t)W * ((MODE == QG_PERBLOCK ? 8 : 1) + 1) * 64 * sizeof(float);
     hipEvent_t ev0, ev1;
     take_timing_events(&ev0, &ev1);
     if (ev0 && ev1)
-        hipExtLaunchKernelGGL((gemv1_b32_kernel<FMT, MODE, SRC, W>), dim3((unsigned)groups), dim3(64 * W), 0, s, ev0,
-                              ev1, 0, tg, G, io);
+        hipExtLaunchKernelGGL((gemv1_b32_kernel<FMT, MODE, SRC, W, DB>), dim3((unsigned)groups), dim3(64 * W), lds, s,
+                              ev0, ev1, 0, tg, G, io);
     else
-        hipLaunchKernelGGL((gemv1_b32_kernel<FMT, MODE, SRC, W>), dim3((unsigned)groups), dim3(64 * W), 0, s, tg, G,
-                           io);
+        hipLaunchKernelGGL((gemv1_b32_kernel<FMT, MODE, SRC, W, DB>), dim3((unsigned)groups), dim3(64 * W), lds, s,
+                           tg, G, io);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemv launch: %s", hipGetErrorString(e));
     return QG_OK;
@@ -986,11 +997,17 @@ int launch_b32_typed(const Targets &tg, int G, const ActIO &io, hipStream_t s)
 template <int FMT, int MODE, int SRC>
 int launch_b32(const Targets &tg, int G, const ActIO &io, hipStream_t s)
 {
-    // 8 waves a workgroup (the tuning knob may ask for 4; 16 is taken as 8), 4 for short rows
+    // waves per workgroup: the tuning knob if set, else one wave per block up to 16; more
+    // blocks than waves go in rounds of 8 (or 4) with the next round's tiles in flight
     int w = tuning().waves_per_wg;
-    if (w <= 0) w = G >= 8 ? 8 : 4;
-    if (w >= 8) return launch_b32_typed<FMT, MODE, SRC, 8>(tg, G, io, s);
-    return launch_b32_typed<FMT, MODE, SRC, 4>(tg, G, io, s);
+    if (w <= 0) w = G <= 4 ? 4 : G <= 8 ? 8 : G <= 16 ? 16 : 8;
+    if (w >= 16 && G <= 16) return launch_b32_typed<FMT, MODE, SRC, 16, false>(tg, G, io, s);
+    if (w >= 8) {
+        if (G <= 8) return launch_b32_typed<FMT, MODE, SRC, 8, false>(tg, G, io, s);
+        return launch_b32_typed<FMT, MODE, SRC, 8, true>(tg, G, io, s);
+    }
+    if (G <= 4) return launch_b32_typed<FMT, MODE, SRC, 4, false>(tg, G, io, s);
+    return launch_b32_typed<FMT, MODE, SRC, 4, true>(tg, G, io, s);
 }
 
 template <int SRC>

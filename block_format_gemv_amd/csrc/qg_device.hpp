@@ -52,6 +52,91 @@ __device__ __forceinline__ float ftz(float x)
 // in-order row accumulation: binary32 add (nearest even), result flushed
 __device__ __forceinline__ float fadd_ftz(float acc, float piece) { return ftz(acc + piece); }
 
+// acc plus n pieces p[0], p[stride], ... in that order, each add flushed as fadd_ftz.  The
+// pieces and the running sum are zero or normal, and such a sum lands in the subnormal range
+// only when it is exact, so plain adds give the same partial sums unless one of them is
+// subnormal.  The pieces are read in batches of eight, the next batch's reads issued before
+// this batch's adds, so the dependent chain is one add per piece.  CHECK keeps the least
+// binary exponent of the partial sums beside the chain (frexp: a subnormal has exponent
+// <= -126, a zero 0) so that a lane where one was subnormal can run again with the flush.
+__device__ __forceinline__ void fold_read8(float (&a)[8], const float *p, int k, int stride)
+{
+#pragma unroll
+    for (int j = 0; j < 8; j++) a[j] = p[(size_t)(k + j) * stride];
+}
+
+template <bool CHECK>
+__device__ __forceinline__ void fold_add8(float &y, int &lo, const float (&a)[8])
+{
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        y = y + a[j];
+        if constexpr (CHECK) lo = min(lo, __builtin_amdgcn_frexp_expf(y));
+    }
+}
+
+template <bool CHECK>
+__device__ __forceinline__ float fold_chain(float y, int &lo, const float *p, int n, int stride)
+{
+    const int n8 = n & ~7;
+    int k = 0;
+    if (n8 > 0) {
+        // batches k (in a) and k + 8 (in b) alternate
+        float a[8], b[8];
+        fold_read8(a, p, 0, stride);
+        do {
+            const bool b_next = k + 8 < n8;
+            if (b_next) fold_read8(b, p, k + 8, stride);
+            fold_add8<CHECK>(y, lo, a);
+            k += 8;
+            if (!b_next) break;
+            const bool a_next = k + 8 < n8;
+            if (a_next) fold_read8(a, p, k + 8, stride);
+            fold_add8<CHECK>(y, lo, b);
+            k += 8;
+            if (!a_next) break;
+        } while (true);
+    }
+    for (; k < n; k++) {
+        y = y + p[(size_t)k * stride];
+        if constexpr (CHECK) lo = min(lo, __builtin_amdgcn_frexp_expf(y));
+    }
+    return y;
+}
+
+__device__ __forceinline__ float fold_flushed(float y, const float *p, int n, int stride)
+{
+    for (int i = 0; i < n; i++) y = fadd_ftz(y, p[(size_t)i * stride]);
+    return y;
+}
+
+__device__ __forceinline__ float fold_ftz(float acc, const float *p, int n, int stride)
+{
+    int lo = 0;
+    const float y = fold_chain<true>(acc, lo, p, n, stride);
+    return lo <= -126 ? fold_flushed(acc, p, n, stride) : y;
+}
+
+// Whether a piece may let a partial sum of the row become subnormal: nonzero and below 2^-102
+// in magnitude.  A nonzero piece of at least 2^-102 has an ulp of at least 2^-125; when every
+// nonzero piece of a row is one, every partial sum is a multiple of the least such ulp (an add
+// rounds to a grid at least that coarse or is exact), so a nonzero partial sum is at least
+// 2^-125 and the row's adds need no flush at all.
+__device__ __forceinline__ bool tiny_piece(float p)
+{
+    const uint32_t u = __float_as_uint(p) & 0x7FFFFFFFu;
+    return u - 1u < 0x0C7FFFFFu;
+}
+
+// acc plus the pieces as fold_ftz, for a row whose producers have flagged whether any of its
+// pieces is tiny (tiny_piece): plain adds unless one is.
+__device__ __forceinline__ float fold_flagged(float acc, const float *p, int n, int stride, bool tiny)
+{
+    if (tiny) return fold_flushed(acc, p, n, stride);
+    int lo = 0;
+    return fold_chain<false>(acc, lo, p, n, stride);
+}
+
 __device__ __forceinline__ float canon_nan(float y)
 {
     return (y != y) ? __uint_as_float(0x7FC00000u) : y;

@@ -237,3 +237,57 @@ def test_full_size_matrix(qg, fmt, seed):
         want = oracle.gemv(f, oc, om, oe, 0)
         assert first_mismatch(out, want) is None, (k, first_mismatch(out, want))
         assert np.array_equal(bits(qg.gemv(M.fmt, M.rows, M.cols, M.img, act)), bits(out))
+
+
+def _subnormal_partial_row(fmt, cols, at):
+    """A row whose pieces (one per 32-element block, PerBlock) are normal but tiny (about
+    2^-120) and cancel so that partial sums of the row are subnormal: blocks at+0 and at+1 give
+    +p and -p' with p' - p one binary16 step of d, and block at+2 a piece the flushed and the
+    unflushed running sums treat differently.  Activations are all 2^-110, so every block has
+    the same codes and scale."""
+    nb = cols // 32
+    if fmt == "q8_0":
+        q = np.ones(cols, np.int8)
+        plus, minus = 1, -1
+    else:
+        q = np.full(cols, 9, np.uint8)
+        plus, minus = 9, 7
+    d = np.full(nb, 0x0400, np.uint16)                      # 2^-14
+    q[32 * (at + 1):32 * (at + 2)] = minus
+    q[32 * at:32 * (at + 1)] = plus
+    d[at] = 0x0800                                          # 2^-13
+    d[at + 1] = 0x0801                                      # 2^-13 (1 + 2^-10)
+    d[at + 2] = 0x0001                                      # 2^-24
+    return q, d
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_subnormal_partial_sums_are_flushed(qg, fmt):
+    """Rows whose running sum passes through the subnormal range: every partial sum is flushed
+    as in the oracle (the producers flag the tiny pieces and the row is added with the flush);
+    one round (256 columns) and several rounds (8192 columns, pattern in a later round)."""
+    for cols, at in ((256, 0), (8192, 130), (8192, 0)):
+        rows = 70
+        f = fields(fmt, rows, cols, 60 + at, adversarial=False)
+        f["d"][:] = 0x0400
+        for r in (0, 5, 69):
+            q, d = _subnormal_partial_row(fmt, cols, at)
+            f["q"][r], f["d"][r] = q, d
+        M = Mat(qg, f)
+        x = np.full((1, cols), np.float32(2.0 ** -110))
+        say("b32 subnormal partial sums", fmt, cols, at)
+        out, act = qg.quantize_gemv(M.fmt, rows, cols, M.img, dev(x.reshape(-1)), 0)
+        oc, om, oe, _ = oracle_act(fmt, x, 0)
+        want = oracle.gemv(f, oc, om, oe, 0)
+        assert first_mismatch(out, want) is None, (cols, at, first_mismatch(out, want))
+        # the case is a real one: adding the same pieces without the flush gives other bits
+        code = int(oc[0, 0])
+        s = float(om[0, 0]) * 2.0 ** int(oe[0, 0])
+        w = np.float32(0)
+        q0, d0 = f["q"][0], f["d"][0]
+        for j in range(cols // 32):
+            wq = q0[32 * j:32 * j + 32].astype(np.int64) - (0 if fmt == "q8_0" else 8)
+            C = int(wq.sum()) * code
+            p = np.float32(C * float(np.uint16(d0[j]).view(np.float16)) * s)
+            w = np.float32(w + p)
+        assert w.view(np.uint32) != bits(want)[0], "the row does not reach a subnormal partial sum"
