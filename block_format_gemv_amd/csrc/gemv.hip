@@ -689,21 +689,69 @@ struct Targets {
     float *out[QG_MAX_MATRICES];
 };
 
+// This workgroup's matrix: the last one whose first group is at or before blockIdx.x (an
+// empty matrix starts where the next one does; past nmat the starts equal the total).  Every
+// index is a compile-time constant, so the descriptor's fields come in one batch of scalar
+// loads rather than through loads that wait on each other.
+struct Picked {
+    const uint8_t *image;
+    float *out;
+    int rows, g;
+};
+
+// A value as an opaque scalar register: the selects below then choose between values, and the
+// compiler cannot turn them back into one load through a computed index.
+template <class V>
+__device__ __forceinline__ V opaque_sgpr(V v)
+{
+    asm("" : "+s"(v));
+    return v;
+}
+
+// The same for a pointer into global memory; it comes back as a global-address-space pointer
+// seen through a generic one, so accesses through it stay global (not flat) loads and stores.
+template <class P>
+__device__ __forceinline__ P *opaque_global(P *p)
+{
+    uint64_t v = opaque_sgpr((uint64_t)(uintptr_t)p);
+    auto *g = (__attribute__((address_space(1))) P *)(uintptr_t)v;
+    return (P *)g;
+}
+
+__device__ __forceinline__ Picked pick_matrix(const Targets &tg)
+{
+    const int bx = (int)blockIdx.x;
+    Picked p{opaque_global(tg.image[0]), opaque_global(tg.out[0]), opaque_sgpr(tg.rows[0]), bx};
+    if (tg.nmat == 1) return p;
+#pragma unroll
+    for (int k = 1; k < QG_MAX_MATRICES; k++) {
+        const int start = opaque_sgpr(tg.gstart[k]);
+        const uint8_t *image = opaque_global(tg.image[k]);
+        float *out = opaque_global(tg.out[k]);
+        const int rows = opaque_sgpr(tg.rows[k]);
+        const bool here = bx >= start;
+        p.image = here ? image : p.image;
+        p.out = here ? out : p.out;
+        p.rows = here ? rows : p.rows;
+        p.g = here ? bx - start : p.g;
+    }
+    return p;
+}
+
 template <int FMT, int MODE, int SRC, int W, bool DB>
 __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, ActIO io)
 {
     extern __shared__ __align__(16) float s_piece[];
     using T = TileRegs<FMT>;
     constexpr int BITS = ActKind<FMT, MODE>::kBits, GL = ActKind<FMT, MODE>::kLanes;
-    int m = 0;                                   // this workgroup's matrix (wave-uniform)
-    while (m + 1 < tg.nmat && (int)blockIdx.x >= tg.gstart[m + 1]) m++;
-    const int g = (int)blockIdx.x - tg.gstart[m];
-    const int rows = tg.rows[m];
-    float *out = tg.out[m];
+    const Picked pm = pick_matrix(tg);           // this workgroup's matrix (wave-uniform)
+    const int g = pm.g;
+    const int rows = pm.rows;
+    float *out = pm.out;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool emit = blockIdx.x == 0;           // the first workgroup writes the quantized row out
-    const uint8_t *gbase = tg.image[m] + (size_t)g * G * T::kBytes;
+    const uint8_t *gbase = pm.image + (size_t)g * G * T::kBytes;
 
     // the first block's activations, then its tile: both loads unconditional (a wave past
     // the last block works on a copy of it and stores nothing), kept in this order
@@ -788,14 +836,13 @@ __global__ __launch_bounds__(64 * W) void gemv1_b32_kernel(const Targets tg, int
     extern __shared__ __align__(16) float s_ring[];
     using T = TileRegs<FMT>;
     using A = typename std::conditional<FMT == QG_Q4_0, ActPlanes, ActWaveCodes>::type;
-    int m = 0;
-    while (m + 1 < tg.nmat && (int)blockIdx.x >= tg.gstart[m + 1]) m++;
-    const int g = (int)blockIdx.x - tg.gstart[m];
-    const int rows = tg.rows[m];
+    const Picked pm = pick_matrix(tg);
+    const int g = pm.g;
+    const int rows = pm.rows;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool emit = blockIdx.x == 0;
-    const uint8_t *gbase = tg.image[m] + (size_t)g * G * T::kBytes;
+    const uint8_t *gbase = pm.image + (size_t)g * G * T::kBytes;
     const int R = (G + W - 1) / W;                         // rounds; every wave goes through all
 
     float y = 0.0f;                                        // first wave: its row's running sum
@@ -866,7 +913,7 @@ __global__ __launch_bounds__(64 * W) void gemv1_b32_kernel(const Targets tg, int
     if (wid == 0) {
         const int64_t row = (int64_t)g * 64 + lane;
         y = canon_nan(y);
-        if (row < rows) tg.out[m][row] = y;
+        if (row < rows) pm.out[row] = y;
         if (io.argmax) {
             unsigned long long k = argmax_key(y, row, row < rows);
 #pragma unroll
