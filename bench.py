@@ -295,7 +295,7 @@ def main():
                         else "gemv1_kernel<..., SRC_CODES> (GEMV of a quantized row)")
     elif fmt_s == "q4k" and mode == 0 and ncol >= 8:
         kernel_label = "gemm_mfma_q4k (matrix cores, shared operands)" if ncol >= 48 else \
-            "gemm_mfma_wave (matrix cores, per wave)"
+            "gemm_ring_q4k (matrix cores, LDS-DMA ring)"
     else:
         kernel_label = "gemv_kernel (several columns)"
     step = fused_call if fused else two_launch

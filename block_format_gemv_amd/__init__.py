@@ -23,7 +23,7 @@ Q4K, Q6K, Q8_0, Q4_0 = 1, 2, 3, 4
 FORMATS = (Q4K, Q6K, Q8_0, Q4_0)
 PERBLOCK, SUB32 = 0, 1
 OK, E_INVALID, E_SHAPE, E_UNSUPPORTED, E_UNREADABLE, E_NONFINITE, E_RUNTIME = range(7)
-TUNE_WAVES_PER_WG, TUNE_MFMA_MIN_COLS, TUNE_MFMA_COL_TILES = 1, 2, 3
+TUNE_WAVES_PER_WG, TUNE_MFMA_MIN_COLS, TUNE_MFMA_COL_TILES, TUNE_MFMA_FORM, TUNE_MFMA_RING_WAVES = 1, 2, 3, 4, 5
 BLOCK = 256
 MAX_COLS = 32768
 MAX_MATRICES = 8
@@ -51,6 +51,7 @@ def _load():
     L.qg_image_bytes.restype = ctypes.c_size_t
     L.qg_pack_q4k.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp]
     L.qg_pack_q6k.argtypes = [i64, i64, vp, vp, vp, vp]
+    L.qg_pack_b32.argtypes = [i32, i64, i64, vp, vp, vp]
     L.qg_quantize_act.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp]
     L.qg_gemv_q.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp]
     L.qg_gemm_q.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]

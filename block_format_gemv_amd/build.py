@@ -35,13 +35,18 @@ DEVICE = [f"--offload-arch={ARCH}", "-fno-gpu-rdc",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# per-source device flags: the matrix-core GEMM keeps its MFMA accumulators in ordinary VGPRs
+# (no copies out of AGPRs before the epilogue reads them)
+EXTRA = {"gemm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, *DEVICE, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *DEVICE, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

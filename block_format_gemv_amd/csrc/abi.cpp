@@ -18,7 +18,7 @@ namespace qg {
 namespace {
 thread_local char g_reason[512] = "";
 thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
-Tuning g_tuning = {0, 0, 0};
+Tuning g_tuning = {0, 0, 0, 0, 0};
 
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices];
@@ -126,6 +126,15 @@ int qg_set_tuning(int key, int64_t value)
         if (value != 0 && value != 1 && value != 2 && value != 4)
             return fail(QG_E_INVALID, "qg_set_tuning: column tiles must be 0, 1, 2 or 4");
         g_tuning.mfma_col_tiles = (int)value;
+        return QG_OK;
+    case QG_TUNE_MFMA_FORM:
+        if (value > 3) return fail(QG_E_INVALID, "qg_set_tuning: form must be 0, 1, 2 or 3");
+        g_tuning.mfma_form = (int)value;
+        return QG_OK;
+    case QG_TUNE_MFMA_RING_WAVES:
+        if (value != 0 && value != 1 && value != 2 && value != 4)
+            return fail(QG_E_INVALID, "qg_set_tuning: ring waves per row quarter must be 0, 1, 2 or 4");
+        g_tuning.mfma_ring_waves = (int)value;
         return QG_OK;
     default:
         return fail(QG_E_INVALID, "qg_set_tuning: unknown key %d", key);

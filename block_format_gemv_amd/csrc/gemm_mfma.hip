@@ -32,6 +32,8 @@ namespace qg {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxLds = 160 * 1024;   // LDS a gfx950 workgroup may use
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 // each byte of q (at most 15) times k (at most 7): the products stay below 128, so the two
@@ -452,19 +454,325 @@ int launch_wave(int64_t rows, int G, int64_t ncol, const void *image, const int8
     return QG_OK;
 }
 
+// ---------------------------------------------------------------------------------------
+// The ring form.  A workgroup owns one 64-row group and 16*CT columns; with WH waves per row
+// quarter, wave w computes rows 16(w%4)..+15 against column tiles (w/4)*CT/WH .. +CT/WH-1,
+// from an LDS ring of D+1 slots.  Each slot holds one block:
+// the weight tile as it lies in the image, then the activation operands already in the order
+// the matrix cores read them (operand (ct, p) = 1 KiB: lane l <- column 16ct + l%16, bytes
+// 64p + 16(l/16) of the block).  The slots are filled by LDS-DMA loads (global_load_lds:
+// lane l's bytes land at the wave-uniform LDS base + size * l) issued D blocks ahead, so the
+// weight stream stays in flight without holding registers.  They are issued from inline
+// asm: the compiler would otherwise wait for every outstanding one before each LDS read.
+// The kernel waits for its own (s_waitcnt vmcnt with the exact count of younger loads) and
+// a barrier then covers every wave's.
+//
+// The epilogue adds each block's pieces into the row sums with plain binary32 adds while no
+// piece of the wave's rows is tiny (tiny_piece); a lane that meets one takes the exact
+// combine and the flushed add from then on, and with it its wave.
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// 16 bytes per lane from global memory to LDS (base + 16 * lane, base wave-uniform); M0 is
+// saved and restored, and the load waits one instruction after M0 is written
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base)
+{
+    uint32_t t;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(t)
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+// wait until at most N vector-memory loads of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int CT, int D, int WH>
+struct Ring {
+    static constexpr int kWaves = 4 * WH;
+    static constexpr int kA = kTileBytesQ4K;                // activation operands after the tile
+    static constexpr int kSlot = kTileBytesQ4K + CT * 4 * 1024;
+    static constexpr int kSlots = D + 1;                   // the block being computed + D in flight
+    static constexpr int kRing = kSlots * kSlot;
+    // DMA loads per block: the tile's 9 chunks and 4*CT activation operands, dealt out to the
+    // waves in turn; every wave issues kDma (the last ones repeat chunk 8, so that every wave
+    // issues the same count and can wait for an exact one)
+    static constexpr int kLoads = 9 + 4 * CT;
+    static constexpr int kDma = (kLoads + kWaves - 1) / kWaves;
+};
+
+// PerBlock Q4_K-style piece from the activation scale as the exact double S = m*2^e:
+// R32(S * (d*C - dmin*O)), the same value as piece_q4k_perblock
+__device__ __forceinline__ float piece_q4k_perblock_s(int C, int O, uint32_t d_dmin, double S)
+{
+    const F16Scale d = f16_scale(d_dmin & 0xFFFFu);
+    const F16Scale dm = f16_scale(d_dmin >> 16);
+    const double a = __builtin_ldexp((double)C * (double)d.sig * S, d.ex);
+    const double b = __builtin_ldexp(-(double)O * (double)dm.sig * S, dm.ex);
+    return r32_sum2(a, b);
+}
+
+// grid: x = 64-row group, y = batch of 16*CT activation columns; 4*WH waves
+template <int CT, int D, int WH>
+__global__ __launch_bounds__(256 * WH) void gemm_ring_q4k(const uint8_t *__restrict__ image, int rows, int G,
+                                                          const int8_t *__restrict__ codes,
+                                                          const uint32_t *__restrict__ scw, int ncol,
+                                                          float *__restrict__ out)
+{
+    static_assert(D >= 2 && D <= 4, "ring depth");
+    static_assert(CT % WH == 0, "whole column tiles per wave");
+    using Rg = Ring<CT, D, WH>;
+    constexpr int NC = 16 * CT;
+    constexpr int NW = Rg::kWaves;
+    constexpr int CTW = CT / WH;                       // column tiles per wave
+    constexpr int K = Rg::kDma;
+    extern __shared__ __align__(16) unsigned char lds[];
+    double *s_S = reinterpret_cast<double *>(lds + Rg::kRing);     // [G][NC] activation scales m*2^e
+    const int C = G * 256;
+    const int g = blockIdx.x;
+    const int colbase = blockIdx.y * NC;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, grp = lane >> 4;
+    const int trow = 16 * (wid & 3) + n;               // row within the 64-row group
+    const int ct0 = (wid >> 2) * CTW;                  // this wave's first column tile
+    const uint8_t *gbase = image + (size_t)g * G * kTileBytesQ4K;
+
+    // the scale table first: its loads are waited for by the compiler, which would also wait
+    // for any DMA issued before them
+    for (int i = threadIdx.x; i < G * NC; i += 64 * NW) {
+        const int b = i / NC, col = colbase + i % NC;
+        const uint32_t w = col < ncol ? scw[(size_t)col * G + b] : 0u;
+        s_S[i] = __builtin_ldexp((double)((w >> 16) & 0xFFu), (int)(int16_t)(w & 0xFFFFu));
+    }
+
+    auto issue = [&](int b) {
+        unsigned char *slot = lds + (b % Rg::kSlots) * Rg::kSlot;
+        const uint8_t *tile = gbase + (size_t)b * kTileBytesQ4K;
+#pragma unroll
+        for (int j = 0; j < K; j++) {
+            const int i = wid + NW * j;                 // this wave's j-th load of the block
+            if (i < 9 || i >= Rg::kLoads) {
+                const int ch = min(i, 8);
+                dma16(tile + 1024 * ch + 16 * lane, lds_offset(slot + 1024 * ch));
+            } else {
+                const int k = i - 9;                    // operand (ct, p) = (k / 4, k % 4)
+                const int col = min(colbase + 16 * (k >> 2) + n, ncol - 1);
+                dma16(codes + (size_t)col * C + (size_t)b * 256 + 64 * (k & 3) + 16 * grp,
+                      lds_offset(slot + Rg::kA + 1024 * k));
+            }
+        }
+    };
+    // own loads of the block after the one waited for still outstanding: nb blocks' worth
+    // (nb < D; an exact count, so that the wait ends as soon as that block has landed)
+    auto wait_blocks_after = [&](int nb) {
+        if (nb >= 3) wait_vm<3 * K>();
+        else if (nb == 2) wait_vm<2 * K>();
+        else if (nb == 1) wait_vm<K>();
+        else wait_vm<0>();
+    };
+
+    const int pre = min(D, G);
+    for (int b = 0; b < pre; b++) issue(b);
+    wait_blocks_after(pre - 1);
+    __syncthreads();
+
+    float y[CTW][4];
+#pragma unroll
+    for (int ct = 0; ct < CTW; ct++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) y[ct][i] = 0.0f;
+    bool tainted = false;     // this lane's row has met a tiny piece
+
+    for (int b = 0; b < G; b++) {
+        if (b + D < G) issue(b + D);
+        const unsigned char *slot = lds + (b % Rg::kSlots) * Rg::kSlot;
+        const uint4 meta = *reinterpret_cast<const uint4 *>(slot + 8192 + 16 * trow);
+        uint32_t f[8];
+        f[0] = field_s<0>(meta.y, meta.z, meta.w);
+        f[1] = field_s<1>(meta.y, meta.z, meta.w);
+        f[2] = field_s<2>(meta.y, meta.z, meta.w);
+        f[3] = field_s<3>(meta.y, meta.z, meta.w);
+        f[4] = field_s<4>(meta.y, meta.z, meta.w);
+        f[5] = field_s<5>(meta.y, meta.z, meta.w);
+        f[6] = field_s<6>(meta.y, meta.z, meta.w);
+        f[7] = field_s<7>(meta.y, meta.z, meta.w);
+
+        v4i acc_h[CTW], acc_l[CTW], acc_o[CTW];
+#pragma unroll
+        for (int ct = 0; ct < CTW; ct++) acc_h[ct] = acc_l[ct] = acc_o[ct] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            // this lane's K group lies in sub-block 2p + grp/2, in the low or high nibbles
+            const uint32_t fsel = 0u - (uint32_t)(grp >> 1);
+            const uint32_t fj = f[2 * p] ^ ((f[2 * p] ^ f[2 * p + 1]) & fsel);
+            const uint32_t sc = fj & 63u, hi = sc >> 3, lo = sc & 7u, mn = fj >> 6;
+            const uint4 ch = *reinterpret_cast<const uint4 *>(slot + 1024 * (2 * p + (grp >> 1)) + 16 * trow);
+            const int sh = 4 * (grp & 1);
+            const uint32_t q0 = (ch.x >> sh) & 0x0F0F0F0Fu, q1 = (ch.y >> sh) & 0x0F0F0F0Fu;
+            const uint32_t q2 = (ch.z >> sh) & 0x0F0F0F0Fu, q3 = (ch.w >> sh) & 0x0F0F0F0Fu;
+            const v4i Bh = {bytes_times(q0, hi), bytes_times(q1, hi), bytes_times(q2, hi), bytes_times(q3, hi)};
+            const v4i Bl = {bytes_times(q0, lo), bytes_times(q1, lo), bytes_times(q2, lo), bytes_times(q3, lo)};
+            const int mrep = (int)(mn * 0x01010101u);
+            const v4i Bo = {mrep, mrep, mrep, mrep};
+#pragma unroll
+            for (int ct = 0; ct < CTW; ct++) {
+                const v4i A = *reinterpret_cast<const v4i *>(slot + Rg::kA + 1024 * (4 * (ct0 + ct) + p) + 16 * lane);
+                acc_h[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bh, acc_h[ct], 0, 0, 0);
+                acc_l[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bl, acc_l[ct], 0, 0, 0);
+                acc_o[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bo, acc_o[ct], 0, 0, 0);
+            }
+        }
+
+        // combine each (row, column) of the block once, then add it into the row's sum
+        const float fd = f16_value(meta.x), fm = f16_value(meta.x >> 16);
+        const bool near = q4k_near(fd, fm);
+        const double Dd = (double)fd, Dm = (double)fm;
+        const double *S = s_S + (size_t)b * NC + 16 * ct0 + 4 * grp;
+        bool fast = false;
+        if (__all(near) && !__any(tainted)) {
+            float pc[CTW][4];
+            int lo = 0;
+#pragma unroll
+            for (int ct = 0; ct < CTW; ct++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int Cb = 8 * acc_h[ct][i] + acc_l[ct][i];
+                    const double X = __builtin_fma((double)Cb, Dd, -((double)acc_o[ct][i] * Dm));
+                    pc[ct][i] = (float)(X * S[16 * ct + i]);
+                    lo = min(lo, __builtin_amdgcn_frexp_expf(pc[ct][i]));
+                }
+            if (!__any(lo <= -102)) {
+                // no tiny piece: every piece is zero or normal, and no partial sum can be
+                // subnormal (nor -0), so plain adds give the flushed adds' bits
+                fast = true;
+#pragma unroll
+                for (int ct = 0; ct < CTW; ct++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) y[ct][i] = y[ct][i] + pc[ct][i];
+            }
+        }
+        if (!fast) {
+#pragma unroll
+            for (int ct = 0; ct < CTW; ct++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int Cb = 8 * acc_h[ct][i] + acc_l[ct][i];
+                    const int Ob = acc_o[ct][i];
+                    const float piece = near ? piece_q4k_perblock_near(Cb, Ob, Dd, Dm, S[16 * ct + i])
+                                             : piece_q4k_perblock_s(Cb, Ob, meta.x, S[16 * ct + i]);
+                    tainted |= tiny_piece(piece);
+                    y[ct][i] = fadd_ftz(y[ct][i], piece);
+                }
+        }
+
+        if (b + 1 < G) wait_blocks_after(min(b + D, G - 1) - (b + 1));
+        __syncthreads();
+    }
+
+    const int64_t row = (int64_t)g * 64 + trow;
+    if (row < rows) {
+#pragma unroll
+        for (int ct = 0; ct < CTW; ct++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int col = colbase + 16 * (ct0 + ct) + 4 * grp + i;
+                if (col < ncol) out[(int64_t)col * rows + row] = canon_nan(y[ct][i]);
+            }
+    }
+}
+
+template <int CT, int D>
+size_t ring_lds(int G)
+{
+    return (size_t)Ring<CT, D, 1>::kRing + (size_t)G * 16 * CT * sizeof(double);
+}
+
+template <int CT, int D, int WH>
+int launch_ring_typed(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
+                      const qg_act_scale *scales, float *out, hipStream_t s)
+{
+    const int64_t groups = (rows + 63) / 64;
+    const dim3 grid((unsigned)groups, (unsigned)((ncol + 16 * CT - 1) / (16 * CT)));
+    const size_t lds = ring_lds<CT, D>(G);
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_ring_q4k<CT, D, WH>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    (void)attr;   // a refusal shows up as a launch error below
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(scales);
+    hipEvent_t ev0, ev1;
+    take_timing_events(&ev0, &ev1);
+    if (ev0 && ev1)
+        hipExtLaunchKernelGGL((gemm_ring_q4k<CT, D, WH>), grid, dim3(256 * WH), lds, s, ev0, ev1, 0,
+                              static_cast<const uint8_t *>(image), (int)rows, G, codes, w, (int)ncol, out);
+    else
+        hipLaunchKernelGGL((gemm_ring_q4k<CT, D, WH>), grid, dim3(256 * WH), lds, s, static_cast<const uint8_t *>(image),
+                           (int)rows, G, codes, w, (int)ncol, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemm (matrix cores, ring) launch: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+// the deepest ring that fits the LDS of a workgroup, or QG_E_UNSUPPORTED
+template <int CT, int WH>
+int launch_ring_d(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
+                  const qg_act_scale *scales, float *out, hipStream_t s)
+{
+    if (ring_lds<CT, 4>(G) <= (size_t)kMaxLds)
+        return launch_ring_typed<CT, 4, WH>(rows, G, ncol, image, codes, scales, out, s);
+    if (ring_lds<CT, 3>(G) <= (size_t)kMaxLds)
+        return launch_ring_typed<CT, 3, WH>(rows, G, ncol, image, codes, scales, out, s);
+    if (ring_lds<CT, 2>(G) <= (size_t)kMaxLds)
+        return launch_ring_typed<CT, 2, WH>(rows, G, ncol, image, codes, scales, out, s);
+    return QG_E_UNSUPPORTED;
+}
+
+// waves per row quarter: the tuning knob's value where it divides the column tiles, else 1
+template <int CT>
+int launch_ring(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
+                const qg_act_scale *scales, float *out, hipStream_t s)
+{
+    const int wh = tuning().mfma_ring_waves;
+    if constexpr (CT >= 4)
+        if (wh == 4) return launch_ring_d<CT, 4>(rows, G, ncol, image, codes, scales, out, s);
+    if constexpr (CT >= 2)
+        if (wh == 2) return launch_ring_d<CT, 2>(rows, G, ncol, image, codes, scales, out, s);
+    return launch_ring_d<CT, 1>(rows, G, ncol, image, codes, scales, out, s);
+}
+
 }  // namespace
 
 int launch_gemm_mfma(int64_t rows, int64_t cols, int64_t ncol, const void *image, const int8_t *codes,
                      const qg_act_scale *scales, float *out, hipStream_t s)
 {
     const int G = (int)(cols / 256);
-    // the tuning knob selects the shared-operand form with that many column tiles; by default
-    // it takes 48 columns and more (64 per workgroup), the per-wave form the rest
-    const int cw = tuning().mfma_col_tiles;
-    if (cw >= 4 || (cw <= 0 && ncol >= 48)) return launch_cw<4>(rows, G, ncol, image, codes, scales, out, s);
-    if (cw == 2) return launch_cw<2>(rows, G, ncol, image, codes, scales, out, s);
-    if (cw == 1) return launch_cw<1>(rows, G, ncol, image, codes, scales, out, s);
-    if (ncol >= 32) return launch_wave<2>(rows, G, ncol, image, codes, scales, out, s);
+    const int form = tuning().mfma_form;
+    int tiles = tuning().mfma_col_tiles;
+    // derived (measured on the 14336 x 4096 matrix): below 48 columns the ring with one column
+    // tile, from 48 the shared-operand form with four
+    if (form == 1 || (form == 0 && ncol < 48)) {
+        const int ct = tiles > 0 ? tiles : form == 0 ? 1 : ncol >= 48 ? 4 : ncol >= 24 ? 2 : 1;
+        int st = QG_E_UNSUPPORTED;
+        if (ct == 4) st = launch_ring<4>(rows, G, ncol, image, codes, scales, out, s);
+        else if (ct == 2) st = launch_ring<2>(rows, G, ncol, image, codes, scales, out, s);
+        else st = launch_ring<1>(rows, G, ncol, image, codes, scales, out, s);
+        if (st != QG_E_UNSUPPORTED) return st;
+        if (form == 1) return fail(QG_E_UNSUPPORTED, "gemm: rows of %d blocks do not fit the ring's LDS", G);
+    }
+    if (form == 2 || (form == 0 && ncol >= 48)) {
+        // shared operands: 4 column tiles (64 columns per workgroup) unless asked otherwise
+        if (tiles == 1) return launch_cw<1>(rows, G, ncol, image, codes, scales, out, s);
+        if (tiles == 2) return launch_cw<2>(rows, G, ncol, image, codes, scales, out, s);
+        return launch_cw<4>(rows, G, ncol, image, codes, scales, out, s);
+    }
+    if (tiles == 2 || (tiles == 0 && ncol >= 32)) return launch_wave<2>(rows, G, ncol, image, codes, scales, out, s);
     return launch_wave<1>(rows, G, ncol, image, codes, scales, out, s);
 }
 

@@ -262,10 +262,23 @@ int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink
  *   QG_TUNE_MFMA_MIN_COLS number of columns from which qg_gemm_q on a Q4_K PerBlock matrix
  *                         runs on the int8 matrix cores, columns padded to 16 (0 = 8;
  *                         above 65535 = never)
- *   QG_TUNE_MFMA_COL_TILES 1, 2 or 4: the matrix-core GEMM in its shared-operand form with that
- *                         many 16-column tiles per workgroup; 0 = derived (that form with 4 tiles
- *                         from 48 columns, below that a per-wave form) */
-enum { QG_TUNE_WAVES_PER_WG = 1, QG_TUNE_MFMA_MIN_COLS = 2, QG_TUNE_MFMA_COL_TILES = 3 };
+ *   QG_TUNE_MFMA_FORM     the matrix-core GEMM's form: 1 = LDS ring (tiles and activation operands
+ *                         staged by LDS-DMA loads several blocks ahead), 2 = shared operands
+ *                         (weight operands built once per workgroup in LDS), 3 = per wave
+ *                         (operands in each wave's registers); 0 = derived (the ring where its
+ *                         LDS fits, else shared operands from 48 columns, else per wave)
+ *   QG_TUNE_MFMA_COL_TILES 1, 2 or 4: 16-column tiles per workgroup of the ring and shared-operand
+ *                         forms (the per-wave form takes 1 or 2); 0 = derived from the columns
+ *   QG_TUNE_MFMA_RING_WAVES 1, 2 or 4 waves per 16-row quarter in the ring form, each taking an
+ *                         equal share of the column tiles (a value that does not divide them
+ *                         is taken as 1); 0 = derived */
+enum {
+    QG_TUNE_WAVES_PER_WG = 1,
+    QG_TUNE_MFMA_MIN_COLS = 2,
+    QG_TUNE_MFMA_COL_TILES = 3,
+    QG_TUNE_MFMA_FORM = 4,
+    QG_TUNE_MFMA_RING_WAVES = 5
+};
 int qg_set_tuning(int key, int64_t value);
 
 /* Measurement hook: the next qg_gemv_q / qg_gemm_q / qg_quantize_gemv / qg_*_multi /

@@ -367,16 +367,76 @@ def test_matrix_core_gemm_matches_oracle(qg, ncol):
     want = oracle.gemm(f, c, m, e, 0).reshape(ncol, 130)
     try:
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 1)                # matrix cores for any column count
-        for ct in (0, 1, 2, 4):                                     # 0: the default form for this count
-            qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, ct)
-            say("matrix-core gemm", ncol, "column tiles", ct)
-            out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
-            assert first_mismatch(out, want) is None, (ncol, ct, first_mismatch(out, want))
+        for form, wh in ((0, 0), (1, 1), (1, 2), (1, 4), (2, 0), (3, 0)):   # derived, ring, shared, per wave
+            qg.qg_set_tuning(qg.TUNE_MFMA_FORM, form)
+            qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, wh)
+            for ct in (0, 1, 2, 4):                                 # 0: derived from the column count
+                qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, ct)
+                say("matrix-core gemm", ncol, "form", form, "ring waves", wh, "column tiles", ct)
+                out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+                assert first_mismatch(out, want) is None, (ncol, form, wh, ct, first_mismatch(out, want))
+        qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 0)
+        qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, 0)
+        qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 65536)          # force the vector-ALU kernel
         out_valu = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
         assert first_mismatch(out_valu, want) is None
     finally:
+        qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 0)
+        qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 0)
+        qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 0)
+
+
+def _subnormal_partial_q4k(f, r):
+    """Row r of a Q4_K-style matrix (at least 3 blocks) whose PerBlock pieces, under an
+    activation block of all 2^-112 (codes 126, scale 130 * 2^-126), are 16380*k*2^-142 with
+    k = 800, -801, 8 in blocks 0, 1, 2: normal, but the first two cancel to a subnormal
+    partial sum, which the flush turns into -0 before block 2 is added."""
+    f["q"][r, :768] = 1
+    f["q"][r, 256:512] = 0
+    f["sc"][r, :24] = 1
+    f["sc"][r, 8:16] = 0
+    f["mn"][r, :24] = 0
+    f["mn"][r, 8:16] = 1
+    f["d"][r, :3] = [800, 0, 8]                     # binary16 subnormals k * 2^-24
+    f["dmin"][r, :3] = [0, 801, 0]
+
+
+def test_subnormal_partial_sums_gemv_and_gemm(qg):
+    """Rows whose running sum passes through the subnormal range, through the GEMV and every
+    GEMM form: all must give the oracle's bits, which differ from unflushed adds."""
+    rows, cols, ncol = 70, 768, 64
+    f = gen.q4k_fields(rows, cols, 77)
+    for r in (0, 5, 69):
+        _subnormal_partial_q4k(f, r)
+    M = Mat(qg, f)
+    xs = gen.act_outliers(ncol, cols, 78)
+    xs[0, :] = np.float32(2.0 ** -112)
+    xs[ncol - 1, :] = np.float32(2.0 ** -112)
+    act, c, m, e, _ = gpu_quant(qg, xs, 0)
+    assert int(c[0, 0]) == 126 and int(m[0, 0]) == 130 and int(e[0, 0]) == -126
+    want = oracle.gemm(f, c, m, e, 0).reshape(ncol, rows)
+    # unflushed adds of the three pieces (exact binary32 values) give other bits
+    unit = np.float32(16380.0 * 2.0 ** -142)
+    plain = np.float32(np.float32(np.float32(0) + np.float32(800 * unit)) + np.float32(-801 * unit))
+    plain = np.float32(plain + np.float32(8 * unit))
+    assert plain.view(np.uint32) != bits(want[0])[0]
+    assert bits(want[0])[0] == np.float32(8 * unit).view(np.uint32)
+    one = qg.alloc_act(1, cols, 0)
+    one.codes.copy_(act.codes[0:1]); one.scales.copy_(act.scales[0:1]); one.csums.copy_(act.csums[0:1])
+    assert first_mismatch(run_gemv(qg, M, one), want[0]) is None
+    try:
+        qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 1)
+        for form, wh in ((1, 1), (1, 2), (1, 4), (2, 0), (3, 0)):
+            qg.qg_set_tuning(qg.TUNE_MFMA_FORM, form)
+            qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, wh)
+            say("subnormal partial sums, gemm form", form, "ring waves", wh)
+            out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+            assert first_mismatch(out, want) is None, (form, wh, first_mismatch(out, want))
+    finally:
+        qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 0)
+        qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 0)
 
 
