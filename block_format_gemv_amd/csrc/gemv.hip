@@ -330,22 +330,17 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q4K> &T, int b, co
             return piece_q4k_perblock_near(Cb, Ob, (double)fd, (double)fm, __builtin_ldexp((double)s.m, s.e));
         return piece_q4k_perblock(Cb, Ob, T.meta.x, s.m, s.e);
     } else {
-        const F16Scale d = f16_scale(T.meta.x & 0xFFFFu);
-        const F16Scale dm = f16_scale(T.meta.x >> 16);
-        long long v[16];
-        int e[16];
+        int Cj[8], Oj[8], m[8], e[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const int P = q4k_sub(T.w[i], b, i, act);
-            const int Cj = __mul24((int)(f[i] & 63u), P);
-            const int Oj = __mul24((int)(f[i] >> 6), act.sum32(b, i));
+            Cj[i] = __mul24((int)(f[i] & 63u), P);
+            Oj[i] = __mul24((int)(f[i] >> 6), act.sum32(b, i));
             const qg_act_scale s = act.scale(b, i, 8);
-            v[2 * i] = (long long)(d.sig * (int)s.m) * Cj;
-            e[2 * i] = s.e + d.ex;
-            v[2 * i + 1] = -(long long)(dm.sig * (int)s.m) * Oj;
-            e[2 * i + 1] = s.e + dm.ex;
+            m[i] = s.m;
+            e[i] = s.e;
         }
-        return exact_sum<16>(v, e);
+        return piece_q4k_sub32(Cj, Oj, m, e, T.meta.x);
     }
 }
 
@@ -373,16 +368,18 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q6K> &T, int b, co
         const qg_act_scale s = act.scale(b, 0, 1);
         return piece_q6k_perblock(Cb, T.d, s.m, s.e);
     } else {
-        const F16Scale d = f16_scale(T.d);
-        long long v[8];
-        int e[8];
+        long long C[8];
+        uint32_t db[8];
+        int m[8], e[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const qg_act_scale s = act.scale(b, j, 8);
-            v[j] = (long long)(d.sig * (int)s.m) * (long long)(Ck[2 * j] + Ck[2 * j + 1]);
-            e[j] = s.e + d.ex;
+            C[j] = (long long)(Ck[2 * j] + Ck[2 * j + 1]);
+            db[j] = T.d;
+            m[j] = s.m;
+            e[j] = s.e;
         }
-        return exact_sum<8>(v, e);
+        return piece_sub32_scaled(C, db, m, e);
     }
 }
 
@@ -432,16 +429,18 @@ __device__ __forceinline__ void b32_pieces(const TileRegs<FMT> &T, const Act &ac
             p[j] = r32_exact_double((double)C[j] * D * S);
         }
     } else {
-        long long v[8];
-        int e[8];
+        long long Cl[8];
+        uint32_t db[8];
+        int m[8], e[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-            const F16Scale d = f16_scale((dw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
             const qg_act_scale s = act.scale(0, j, 8);
-            v[j] = (long long)(d.sig * (int)s.m) * C[j];
-            e[j] = s.e + d.ex;
+            Cl[j] = C[j];
+            db[j] = (dw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+            m[j] = s.m;
+            e[j] = s.e;
         }
-        p[0] = exact_sum<8>(v, e);
+        p[0] = piece_sub32_scaled(Cl, db, m, e);
     }
 }
 

@@ -430,4 +430,94 @@ __device__ __forceinline__ float piece_q6k_perblock(int C, uint32_t dbits, int m
     return r32_exact_double(__builtin_ldexp((double)C * (double)(d.sig * m), d.ex + e));
 }
 
+// The exact sum of eight doubles T[j] (each exact, every one a multiple of 2^low) rounded once
+// to binary32, as hi + lo: hi the rounded running sum, lo the sum of TwoSum's exact errors.
+// Each error is a multiple of 2^low below 2^(top - 53), top bounding every partial sum
+// (2^top > 8 * max |T|), so lo is exact while top - low <= 103, and then hi + lo is the sum and
+// r32_sum2 rounds it once.  Returns false (out untouched) when the bound does not hold.
+__device__ __forceinline__ bool sum8_pair(const double (&T)[8], int low, float &out)
+{
+    double hi = 0.0, lo = 0.0, amax = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const double a = hi, b = T[j];
+        hi = a + b;
+        const double bv = hi - a;
+        lo += (a - (hi - bv)) + (b - bv);
+        amax = __builtin_fmax(amax, __builtin_fabs(b));
+    }
+    int k;
+    (void)__builtin_frexp(amax, &k);                // amax < 2^k
+    if (amax != 0.0 && k + 3 - low > 103) return false;
+    out = r32_sum2(hi, lo);
+    return true;
+}
+
+// Sub32, Q4_K-style: R32(sum_j m_j 2^e_j (d*C_j - dmin*O_j)), the sixteen terms of exact_sum.
+// When the block scales are near (q4k_near), X_j = d*C_j - dmin*O_j is exact in one fma (|C_j|
+// < 2^22, |O_j| < 2^18) and T_j = X_j * m_j 2^e_j too (m_j has 4 significant bits); with the sum
+// window not engaged the eight T_j are summed by sum8_pair.  Otherwise the 128-bit sum.
+__device__ __forceinline__ float piece_q4k_sub32(const int (&C)[8], const int (&O)[8], const int (&m)[8],
+                                                 const int (&e)[8], uint32_t d_dmin)
+{
+    const F16Scale d = f16_scale(d_dmin & 0xFFFFu);
+    const F16Scale dm = f16_scale(d_dmin >> 16);
+    int emin = e[0], emax = e[0];
+#pragma unroll
+    for (int j = 1; j < 8; j++) {
+        emin = e[j] < emin ? e[j] : emin;
+        emax = e[j] > emax ? e[j] : emax;
+    }
+    const int dlo = d.ex < dm.ex ? d.ex : dm.ex, dhi = d.ex < dm.ex ? dm.ex : d.ex;
+    const float fd = f16_value(d_dmin), fm = f16_value(d_dmin >> 16);
+    if (q4k_near(fd, fm) && (emax - emin) + (dhi - dlo) <= kSumWindow) {
+        double T[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const double X = __builtin_fma((double)C[j], (double)fd, -((double)O[j] * (double)fm));
+            T[j] = X * __builtin_ldexp((double)m[j], e[j]);
+        }
+        float r;
+        if (sum8_pair(T, emin + dlo, r)) return r;
+    }
+    long long v[16];
+    int ex[16];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        v[2 * j] = (long long)(d.sig * m[j]) * C[j];
+        ex[2 * j] = e[j] + d.ex;
+        v[2 * j + 1] = -(long long)(dm.sig * m[j]) * O[j];
+        ex[2 * j + 1] = e[j] + dm.ex;
+    }
+    return exact_sum<16>(v, ex);
+}
+
+// Sub32 with one weight scale per term (Q6_K-style: d shared, C_j the pair of 16-element sums
+// of sub-block j; the 32-element-block formats: d_j per block): R32(sum_j m_j 2^e_j d_j C_j),
+// eight terms of at most 2^11 * 2^4 * 2^28 in magnitude, each exact as a double; summed by
+// sum8_pair when the window is not engaged, else by the 128-bit sum.
+__device__ __forceinline__ float piece_sub32_scaled(const long long (&C)[8], const uint32_t (&dbits)[8],
+                                                    const int (&m)[8], const int (&e)[8])
+{
+    long long v[8];
+    int ex[8];
+    int emin, emax;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const F16Scale d = f16_scale(dbits[j]);
+        v[j] = (long long)(d.sig * m[j]) * C[j];
+        ex[j] = e[j] + d.ex;
+        emin = j == 0 || ex[j] < emin ? ex[j] : emin;
+        emax = j == 0 || ex[j] > emax ? ex[j] : emax;
+    }
+    if (emax - emin <= kSumWindow) {
+        double T[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) T[j] = __builtin_ldexp((double)v[j], ex[j]);
+        float r;
+        if (sum8_pair(T, emin, r)) return r;
+    }
+    return exact_sum<8>(v, ex);
+}
+
 }  // namespace qg
