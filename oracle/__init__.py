@@ -58,6 +58,12 @@ def lib(mutant: int = 0):
     L.or_set_threads.argtypes = [ctypes.c_int]
     L.or_gemm_b32.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]
     L.or_argmax.argtypes = [vp, i64]
+    L.or_f16_rne.argtypes = [ctypes.c_float]
+    L.or_f16_rne.restype = ctypes.c_uint16
+    L.or_kv_cache_rows.argtypes = [i64, i64, vp, vp, vp]
+    L.or_kv_quantize_heads.argtypes = [i32, i64, i64, vp, vp, vp, vp]
+    L.or_kv_scores.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.or_kv_weighted.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp]
     L.or_argmax.restype = ctypes.c_int64
     _libs[mutant] = L
     return L
@@ -190,3 +196,77 @@ def f16_scale(h: int):
     if st:
         raise OracleError(st, "f16_scale")
     return int(sig[0]), int(ex[0])
+
+
+# --- int8 KV cache ([numerics] cache_row, quantize_head, int8_score, weighted_int8) ----------
+
+VALUE_BLOCK = 32
+
+
+def f16_rne(x: float, mutant: int = 0) -> int:
+    """binary32 -> binary16 bits, nearest even, subnormals kept, past the top infinite."""
+    return int(lib(mutant).or_f16_rne(float(np.float32(x))))
+
+
+def kv_cache_rows(x: np.ndarray, mutant: int = 0):
+    """Rows x f32 [n, hd] -> (scales uint16 [n] (binary16 bits), codes int8 [n, hd])."""
+    x = np.ascontiguousarray(x, np.float32)
+    if x.ndim == 1:
+        x = x[None]
+    n, hd = x.shape
+    scales = np.zeros(n, np.uint16)
+    codes = np.zeros((n, hd), np.int8)
+    st = lib(mutant).or_kv_cache_rows(n, hd, _p(x), _p(scales), _p(codes))
+    if st:
+        raise OracleError(st, "kv_cache_rows")
+    return scales, codes
+
+
+def kv_quantize_heads(q: np.ndarray, mode: int, mutant: int = 0, check: bool = True):
+    """Query heads f32 [nh, hd] -> (codes int8 [nh, hd], m uint8 [nh, nb], e int16 [nh, nb])."""
+    q = np.ascontiguousarray(q, np.float32)
+    if q.ndim == 1:
+        q = q[None]
+    nh, hd = q.shape
+    nb = 1 if mode == PERBLOCK else hd // 32
+    codes = np.zeros((nh, hd), np.int8)
+    m = np.zeros((nh, nb), np.uint8)
+    e = np.zeros((nh, nb), np.int16)
+    st = lib(mutant).or_kv_quantize_heads(mode, nh, hd, _p(q), _p(codes), _p(m), _p(e))
+    if st and check:
+        raise OracleError(st, "kv_quantize_heads")
+    return codes, m, e
+
+
+def kv_scores(mode: int, qc, qm, qe, kscales, kcodes, mutant: int = 0) -> np.ndarray:
+    """int8_score of every query head against every key row of its KV head.
+    qc int8 [nh, hd]; qm, qe [nh, nb]; kscales uint16 [nkv, npos]; kcodes int8 [nkv, npos, hd].
+    -> f32 [nh, npos]."""
+    qc = np.ascontiguousarray(qc, np.int8)
+    qm = np.ascontiguousarray(qm, np.uint8)
+    qe = np.ascontiguousarray(qe, np.int16)
+    ks = np.ascontiguousarray(kscales, np.uint16)
+    kc = np.ascontiguousarray(kcodes, np.int8)
+    nh, hd = qc.shape
+    nkv, npos = ks.shape
+    out = np.zeros((nh, npos), np.float32)
+    st = lib(mutant).or_kv_scores(mode, nh, nkv, npos, hd, _p(qc), _p(qm), _p(qe), _p(ks), _p(kc), _p(out))
+    if st:
+        raise OracleError(st, "kv_scores")
+    return out
+
+
+def kv_weighted(probs, vscales, vcodes, mutant: int = 0) -> np.ndarray:
+    """weighted_int8 per head: probs f32 [nh, npos]; vscales uint16 [nkv, npos];
+    vcodes int8 [nkv, npos, hd] -> f32 [nh, hd]."""
+    p = np.ascontiguousarray(probs, np.float32)
+    vs = np.ascontiguousarray(vscales, np.uint16)
+    vc = np.ascontiguousarray(vcodes, np.int8)
+    nh, npos = p.shape
+    nkv = vs.shape[0]
+    hd = vc.shape[2]
+    out = np.zeros((nh, hd), np.float32)
+    st = lib(mutant).or_kv_weighted(nh, nkv, npos, hd, _p(p), _p(vs), _p(vc), _p(out))
+    if st:
+        raise OracleError(st, "kv_weighted")
+    return out

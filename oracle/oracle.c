@@ -675,6 +675,242 @@ int64_t or_argmax(const float *x, int64_t n)
     return best < 0 ? 0 : best;
 }
 
+/* ------------------------------------------------------------------------------------- */
+/* int8 KV cache ([N] Functions cache_row, int8_codes, quantize_head, int8_score,           */
+/* weighted_int8, attend_int8; Constants INV_127, VALUE_BLOCK).                            */
+/*                                                                                         */
+/* Readings (the pages leave these open):                                                  */
+/*   K1 cache_row's scale is the binary16 (nearest even, subnormals kept, past the top       */
+/*      infinite) of amax * INV_127 formed in binary32, INV_127 = 1/127 rounded to binary32, */
+/*      amax as absmax (a denormal read as 0, a NaN passed over).                           */
+/*   K2 int8_codes: inv = 1 / (the scale as binary32), a binary32 division; a code is the   */
+/*      binary32 product x * inv to the nearest integer (ties to even), clamped to           */
+/*      [-127, 127]; a NaN product gives 0; an infinite inv (a zero scale) gives all zeros.  */
+/*   K3 quantize_head: PerBlock, the whole head one block under the 8-bit wide scale;       */
+/*      Sub32, per 32 elements under the 4-bit block scale.  The head is a whole number of  */
+/*      32-element groups.                                                                  */
+/*   K4 int8_score: over the query's blocks b, m_b 2^e_b * (sum of c_i k_i) * d_k summed     */
+/*      exactly (exact_sum, window included) and rounded once; a key whose scale is not     */
+/*      finite scores the canonical NaN.                                                    */
+/*   K5 weighted_int8: w_j = p_j * d_j in binary32 (d_j the value row's scale); per block   */
+/*      of VALUE_BLOCK = 32 positions (the last one possibly shorter) the least power of two */
+/*      2^E with 127 * 2^E >= absmax of the w_j (E = 0 for an all-zero block); codes        */
+/*      u_j = rne(w_j / 2^E), exact (a NaN gives 0); per value element the piece            */
+/*      R32(2^E * sum_j u_j v_j), the pieces added in block order (fadd).  A block holding   */
+/*      an infinite w_j, or a value row whose scale is not finite, gives NaN pieces.         */
+/* -------------------------------------------------------------------------------------- */
+
+#define OR_VALUE_BLOCK 32
+
+static int bitlen_u64(uint64_t v)
+{
+    int n = 0;
+    while (v) { v >>= 1; n++; }
+    return n;
+}
+
+/* [K1] binary32 -> binary16 bits: nearest even on the binary16 grid (subnormals kept: a
+ * spacing of 2^-24 below 2^-14), past the largest finite value infinite, NaN -> 0x7E00. */
+uint16_t or_f16_rne(float x)
+{
+    uint32_t u = bits_of(x);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    if (isnan(x)) return 0x7E00;
+    if (isinf(x)) return sign | 0x7C00;
+    if (x == 0.0f) return sign;
+    int64_t X; int a;
+    f32_split(fabsf(x), &X, &a);                        /* |x| = X * 2^a */
+    int L = bitlen_u64((uint64_t)X) - 1 + a;            /* 2^L <= |x| < 2^(L+1) */
+    int s = L - 10;                                     /* the grid spacing there */
+    if (s < -24) s = -24;
+    int k = a - s;
+    uint64_t q;
+    if (k >= 0) {
+        q = (uint64_t)X << k;                           /* exact: |x| on the grid already */
+    } else {
+        int sh = -k;
+        if (sh > 62) q = 0;
+        else {
+            uint64_t num = (uint64_t)X;
+            q = num >> sh;
+            uint64_t rem = num - (q << sh), half = 1ull << (sh - 1);
+#if OR_MUTANT == 14
+            if (rem >= half) q++;                       /* MUTANT: ties away from zero */
+#else
+            if (rem > half || (rem == half && (q & 1))) q++;
+#endif
+        }
+    }
+    if (q == 2048) { q = 1024; s += 1; }                /* rounded up to the next binade */
+    if (s == -24 && q < 1024) return sign | (uint16_t)q;   /* subnormal (or zero) */
+    int Eb = s + 25;                                    /* value (q / 1024) * 2^(s + 10) */
+    if (Eb >= 31) return sign | 0x7C00;
+    return sign | (uint16_t)(Eb << 10) | (uint16_t)(q - 1024);
+}
+
+/* binary16 bits -> binary32 value (exact) */
+static float f16_to_f32(uint16_t h)
+{
+    int s = h >> 15, E = (h >> 10) & 31, M = h & 1023;
+    float v;
+    if (E == 31) v = M ? NAN : INFINITY;
+    else if (E == 0) v = ldexpf((float)M, -24);
+    else v = ldexpf((float)(M | 1024), E - 25);
+    return s ? -v : v;
+}
+
+/* [N] cache_row, K1, K2: n rows of hd elements -> scales (binary16 bits) [n], codes [n][hd]. */
+int or_kv_cache_rows(int64_t n, int64_t hd, const float *x, uint16_t *scales, int8_t *codes)
+{
+    if (n < 0 || hd <= 0) return OR_E_SHAPE;
+    const float inv127 = 1.0f / 127.0f;
+    for (int64_t r = 0; r < n; r++) {
+        const float *xr = x + r * hd;
+        float amax = absmax(xr, hd);
+        uint16_t h = or_f16_rne(amax * inv127);
+        scales[r] = h;
+        float inv = 1.0f / f16_to_f32(h);
+        for (int64_t i = 0; i < hd; i++) {
+            int c = 0;
+            if (!isinf(inv)) {
+                float p = xr[i] * inv;
+                if (!isnan(p)) {
+#if OR_MUTANT == 15
+                    float rr = truncf(p);               /* MUTANT: toward zero */
+#else
+                    float rr = rintf(p);                /* nearest integer, ties to even */
+#endif
+                    if (rr > 127.0f) rr = 127.0f;
+                    if (rr < -127.0f) rr = -127.0f;
+                    c = (int)rr;
+                }
+            }
+            codes[r * hd + i] = (int8_t)c;
+        }
+    }
+    return OR_OK;
+}
+
+/* [N] quantize_head, K3: nh heads of hd elements -> codes [nh][hd], m, e [nh][hd / B]
+ * (B = hd under PerBlock, 32 under Sub32).  OR_E_NONFINITE when a block holds +-inf (its
+ * m = 0 and codes 0, as the activation quantizer). */
+int or_kv_quantize_heads(int mode, int64_t nh, int64_t hd, const float *q, int8_t *codes, uint8_t *sm, int16_t *se)
+{
+    if ((mode != 0 && mode != 1) || nh < 0 || hd <= 0 || hd % 32) return OR_E_SHAPE;
+    const int64_t B = mode == 0 ? hd : 32;
+    const int lo = mode == 0 ? 128 : 8;
+    const int64_t nb = hd / B;
+    int status = OR_OK;
+    for (int64_t h = 0; h < nh; h++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const float *xb = q + h * hd + b * B;
+            float amax = absmax(xb, B);
+            int m, e;
+            if (isinf(amax)) { status = OR_E_NONFINITE; m = 0; e = 0; }
+            else if (amax == 0.0f) { m = lo; e = 0; }
+            else least_scale(amax, lo, &m, &e);
+            sm[h * nb + b] = (uint8_t)m;
+            se[h * nb + b] = (int16_t)e;
+            for (int64_t i = 0; i < B; i++) {
+                float v = or_ftz(xb[i]);
+                int64_t c = 0;
+                if (m != 0 && !isnan(v)) c = rne_div(v, m, e);
+                if (c > 127 || c < -127) return OR_E_INTERNAL;
+                codes[h * hd + b * B + i] = (int8_t)c;
+            }
+        }
+    }
+    return status;
+}
+
+/* [N] int8_score, K4, for every query head h against every cached key row j of its KV head
+ * (h / (nh / nkv)): out[h * npos + j].  Keys: scales [nkv][npos], codes [nkv][npos][hd]. */
+int or_kv_scores(int mode, int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const int8_t *qc, const uint8_t *qm,
+                 const int16_t *qe, const uint16_t *ks, const int8_t *kc, float *out)
+{
+    if ((mode != 0 && mode != 1) || hd <= 0 || hd % 32 || nkv <= 0 || nh % nkv) return OR_E_SHAPE;
+    const int64_t B = mode == 0 ? hd : 32, nb = hd / B, grp = nh / nkv;
+    if (nb > 32) return OR_E_SHAPE;
+    int status = OR_OK;
+#pragma omp parallel for schedule(static) num_threads(g_threads) if (g_threads > 1)
+    for (int64_t h = 0; h < nh; h++) {
+        const int64_t kv = h / grp;
+        for (int64_t j = 0; j < npos; j++) {
+            const int8_t *k = kc + (kv * npos + j) * hd;
+            int64_t sig; int ex;
+            if (f16_scale(ks[kv * npos + j], &sig, &ex)) { out[h * npos + j] = canon_nan(NAN); continue; }
+            term_t t[32];
+            for (int64_t b = 0; b < nb; b++) {
+                int64_t P = 0;
+                for (int64_t i = 0; i < B; i++) P += (int64_t)qc[h * hd + b * B + i] * k[b * B + i];
+                t[b].v = (i128)qm[h * nb + b] * sig * P;
+                t[b].e = qe[h * nb + b] + ex;
+            }
+            float y;
+            int st = exact_sum(t, (int)nb, &y);
+            if (st) {
+#pragma omp critical
+                status = st;
+            }
+            out[h * npos + j] = canon_nan(y);
+        }
+    }
+    return status;
+}
+
+/* [N] weighted_int8, K5, for every head h over its KV head's cached value rows:
+ * out[h * hd + e] from probs [nh][npos], values: scales [nkv][npos], codes [nkv][npos][hd]. */
+int or_kv_weighted(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs, const uint16_t *vs,
+                   const int8_t *vc, float *out)
+{
+    if (hd <= 0 || nkv <= 0 || nh % nkv || npos < 0) return OR_E_SHAPE;
+    const int64_t grp = nh / nkv;
+#pragma omp parallel for schedule(static) num_threads(g_threads) if (g_threads > 1)
+    for (int64_t h = 0; h < nh; h++) {
+        const int64_t kv = h / grp;
+        float *y = out + h * hd;
+        for (int64_t e = 0; e < hd; e++) y[e] = 0.0f;
+#if OR_MUTANT == 17
+        for (int64_t j0 = (npos - 1) / OR_VALUE_BLOCK * OR_VALUE_BLOCK; j0 >= 0; j0 -= OR_VALUE_BLOCK) {   /* MUTANT: last block first */
+#else
+        for (int64_t j0 = 0; j0 < npos; j0 += OR_VALUE_BLOCK) {
+#endif
+            const int64_t nj = npos - j0 < OR_VALUE_BLOCK ? npos - j0 : OR_VALUE_BLOCK;
+            float w[OR_VALUE_BLOCK];
+            int bad = 0;
+            for (int64_t j = 0; j < nj; j++) {
+                const uint16_t s = vs[kv * npos + j0 + j];
+                if (((s >> 10) & 31) == 31) bad = 1;
+                w[j] = probs[h * npos + j0 + j] * f16_to_f32(s);
+            }
+            float amax = absmax(w, nj);
+            if (isinf(amax)) bad = 1;
+            int E = 0, m = 1;
+            if (!bad && amax > 0.0f) least_scale(amax, 1, &m, &E);   /* m = 1: a power of two */
+#if OR_MUTANT == 16
+            E += 1;                                     /* MUTANT: not the least power of two */
+#endif
+            int64_t u[OR_VALUE_BLOCK];
+            for (int64_t j = 0; j < nj; j++) {
+                const float v = or_ftz(w[j]);
+                u[j] = (bad || isnan(v)) ? 0 : rne_div(v, 1, E);
+            }
+            for (int64_t e = 0; e < hd; e++) {
+                float piece;
+                if (bad) piece = NAN;
+                else {
+                    int64_t T = 0;
+                    for (int64_t j = 0; j < nj; j++) T += u[j] * vc[(kv * npos + j0 + j) * hd + e];
+                    piece = or_r32((i128)T, E);
+                }
+                y[e] = fadd(y[e], piece);
+            }
+        }
+        for (int64_t e = 0; e < hd; e++) y[e] = canon_nan(y[e]);
+    }
+    return OR_OK;
+}
+
 int or_mutant(void) { return OR_MUTANT; }
 int or_coef_bound(void) { return OR_COEF_BOUND; }
 int or_sum_window(void) { return OR_SUM_WINDOW; }
