@@ -31,7 +31,10 @@ MAX_MATRICES = 8
 EXPORTS = ("qg_reads", "qg_image_bytes", "qg_pack_q4k", "qg_pack_q6k", "qg_pack_b32", "qg_quantize_act",
            "qg_gemv_q", "qg_gemm_q", "qg_quantize_gemv", "qg_quantize_gemv_argmax", "qg_argmax_index",
            "qg_quantize_gemv_multi", "qg_gemv_q_multi", "qg_block_sums", "qg_stream_read", "qg_set_tuning",
-           "qg_time_next_launch", "qg_last_error", "qg_version")
+           "qg_time_next_launch", "qg_last_error", "qg_version", "qg_kv_cache_rows", "qg_kv_quantize_heads",
+           "qg_kv_scores", "qg_kv_weighted")
+VALUE_BLOCK = 32
+KV_HEAD_SIZES = (32, 64, 128, 256)
 
 
 class QGError(RuntimeError):
@@ -64,6 +67,10 @@ def _load():
     L.qg_quantize_gemv_multi.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     L.qg_gemv_q_multi.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp]
     L.qg_set_tuning.argtypes = [i32, i64]
+    L.qg_kv_cache_rows.argtypes = [i64, i64, vp, vp, vp, vp]
+    L.qg_kv_quantize_heads.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
+    L.qg_kv_scores.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.qg_kv_weighted.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp]
     L.qg_time_next_launch.argtypes = [vp, vp]
     L.qg_last_error.restype = ctypes.c_char_p
     return L
@@ -259,6 +266,50 @@ def qg_block_sums(fmt, rows, cols, image, codes, csum_out, osum_out=None, stream
             _need(osum_out, 4 * rows * (cols // 32), "osum_out")
     _check(_lib.qg_block_sums(fmt, rows, cols, _dptr(image), _dptr(codes), _dptr(csum_out), _dptr(osum_out),
                               _stream(stream)))
+
+
+def _kv_shape_ok(nh, nkv, npos, hd) -> bool:
+    return hd in KV_HEAD_SIZES and nkv >= 1 and nh >= 0 and nh % nkv == 0 and npos >= 0
+
+
+def qg_kv_cache_rows(n, hd, x, scales, codes, stream=None) -> None:
+    if hd in KV_HEAD_SIZES and n > 0:
+        _need(x, 4 * n * hd, "x")
+        _need(scales, 2 * n, "scales")
+        _need(codes, n * hd, "codes")
+    _check(_lib.qg_kv_cache_rows(n, hd, _dptr(x), _dptr(scales), _dptr(codes), _stream(stream)))
+
+
+def qg_kv_quantize_heads(mode, nh, hd, q, codes, scales, err_flag=None, stream=None) -> None:
+    if hd in KV_HEAD_SIZES and nh > 0 and mode in (PERBLOCK, SUB32):
+        _need(q, 4 * nh * hd, "q")
+        _need(codes, nh * hd, "codes")
+        _need(scales, 4 * nh * (1 if mode == PERBLOCK else hd // 32), "scales")
+        _need(err_flag, 4, "err_flag")
+    _check(_lib.qg_kv_quantize_heads(mode, nh, hd, _dptr(q), _dptr(codes), _dptr(scales), _dptr(err_flag),
+                                     _stream(stream)))
+
+
+def qg_kv_scores(mode, nh, nkv, npos, hd, qcodes, qscales, kscales, kcodes, out, stream=None) -> None:
+    if _kv_shape_ok(nh, nkv, npos, hd) and nh > 0 and npos > 0 and mode in (PERBLOCK, SUB32):
+        _need(qcodes, nh * hd, "qcodes")
+        _need(qscales, 4 * nh * (1 if mode == PERBLOCK else hd // 32), "qscales")
+        _need(kscales, 2 * nkv * npos, "kscales")
+        _need(kcodes, nkv * npos * hd, "kcodes")
+        _need(out, 4 * nh * npos, "out")
+    _check(_lib.qg_kv_scores(mode, nh, nkv, npos, hd, _dptr(qcodes), _dptr(qscales), _dptr(kscales), _dptr(kcodes),
+                             _dptr(out), _stream(stream)))
+
+
+def qg_kv_weighted(nh, nkv, npos, hd, probs, vscales, vcodes, out, stream=None) -> None:
+    if _kv_shape_ok(nh, nkv, npos, hd) and nh > 0:
+        _need(out, 4 * nh * hd, "out")
+        if npos > 0:
+            _need(probs, 4 * nh * npos, "probs")
+            _need(vscales, 2 * nkv * npos, "vscales")
+            _need(vcodes, nkv * npos * hd, "vcodes")
+    _check(_lib.qg_kv_weighted(nh, nkv, npos, hd, _dptr(probs), _dptr(vscales), _dptr(vcodes), _dptr(out),
+                               _stream(stream)))
 
 
 def qg_stream_read(buf, nbytes: int, magic: int, sink, stream=None) -> None:

@@ -86,6 +86,19 @@ int check_ptr(const char *who, const char *name, const void *p, uintptr_t align)
     return QG_OK;
 }
 
+// head size and head counts of the KV-cache calls
+int check_kv(const char *who, int64_t nh, int64_t nkv, int64_t npos, int64_t hd)
+{
+    if (hd != 32 && hd != 64 && hd != 128 && hd != 256)
+        return fail(QG_E_SHAPE, "%s: head size %lld is not 32, 64, 128 or 256", who, (long long)hd);
+    if (nkv < 1 || nh < 0 || nh % nkv)
+        return fail(QG_E_SHAPE, "%s: %lld heads do not share %lld KV heads evenly", who, (long long)nh, (long long)nkv);
+    if (nh > 65535) return fail(QG_E_SHAPE, "%s: %lld heads exceed 65535", who, (long long)nh);
+    if (npos < 0 || npos > ((int64_t)1 << 31) / hd)
+        return fail(QG_E_SHAPE, "%s: %lld positions out of range", who, (long long)npos);
+    return QG_OK;
+}
+
 int check_act(const char *who, const int8_t *codes, const qg_act_scale *scales, const int32_t *csums)
 {
     int st;
@@ -300,6 +313,67 @@ int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink
     if ((st = check_ptr(who, "buf", buf, 16))) return st;
     if ((st = check_ptr(who, "sink", sink, 4))) return st;
     return launch_stream_read(buf, bytes, magic, sink, static_cast<hipStream_t>(stream));
+}
+
+int qg_kv_cache_rows(int64_t n, int64_t hd, const float *x, uint16_t *scales, int8_t *codes, void *stream)
+{
+    const char *who = "qg_kv_cache_rows";
+    int st;
+    if ((st = check_kv(who, 0, 1, 0, hd))) return st;
+    if (n < 0 || n > 0x7fffffffLL * 4) return fail(QG_E_SHAPE, "%s: %lld rows out of range", who, (long long)n);
+    if (n == 0) return QG_OK;
+    if ((st = check_ptr(who, "x", x, 4))) return st;
+    if ((st = check_ptr(who, "scales", scales, 2))) return st;
+    if ((st = check_ptr(who, "codes", codes, 4))) return st;
+    return launch_kv_cache_rows(n, hd, x, scales, codes, static_cast<hipStream_t>(stream));
+}
+
+int qg_kv_quantize_heads(int mode, int64_t nh, int64_t hd, const float *q, int8_t *codes, qg_act_scale *scales,
+                         int32_t *err_flag, void *stream)
+{
+    const char *who = "qg_kv_quantize_heads";
+    int st;
+    if (mode != QG_PERBLOCK && mode != QG_SUB32) return fail(QG_E_INVALID, "%s: unknown scaling %d", who, mode);
+    if ((st = check_kv(who, nh, 1, 0, hd))) return st;
+    if (nh == 0) return QG_OK;
+    if ((st = check_ptr(who, "q", q, 16))) return st;
+    if ((st = check_ptr(who, "codes", codes, 4))) return st;
+    if ((st = check_ptr(who, "scales", scales, 4))) return st;
+    if (err_flag && (st = check_ptr(who, "err_flag", err_flag, 4))) return st;
+    return launch_kv_quantize_heads(mode, nh, hd, q, codes, scales, err_flag, static_cast<hipStream_t>(stream));
+}
+
+int qg_kv_scores(int mode, int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const int8_t *qcodes,
+                 const qg_act_scale *qscales, const uint16_t *kscales, const int8_t *kcodes, float *out, void *stream)
+{
+    const char *who = "qg_kv_scores";
+    int st;
+    if (mode != QG_PERBLOCK && mode != QG_SUB32) return fail(QG_E_INVALID, "%s: unknown scaling %d", who, mode);
+    if ((st = check_kv(who, nh, nkv, npos, hd))) return st;
+    if (nh == 0 || npos == 0) return QG_OK;
+    if ((st = check_ptr(who, "qcodes", qcodes, 4))) return st;
+    if ((st = check_ptr(who, "qscales", qscales, 4))) return st;
+    if ((st = check_ptr(who, "kscales", kscales, 2))) return st;
+    if ((st = check_ptr(who, "kcodes", kcodes, 16))) return st;
+    if ((st = check_ptr(who, "out", out, 4))) return st;
+    return launch_kv_scores(mode, nh, nkv, npos, hd, qcodes, qscales, kscales, kcodes, out,
+                            static_cast<hipStream_t>(stream));
+}
+
+int qg_kv_weighted(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs, const uint16_t *vscales,
+                   const int8_t *vcodes, float *out, void *stream)
+{
+    const char *who = "qg_kv_weighted";
+    int st;
+    if ((st = check_kv(who, nh, nkv, npos, hd))) return st;
+    if (nh == 0) return QG_OK;
+    if ((st = check_ptr(who, "out", out, 4))) return st;
+    if (npos > 0) {
+        if ((st = check_ptr(who, "probs", probs, 4))) return st;
+        if ((st = check_ptr(who, "vscales", vscales, 2))) return st;
+        if ((st = check_ptr(who, "vcodes", vcodes, 4))) return st;
+    }
+    return launch_kv_weighted(nh, nkv, npos, hd, probs, vscales, vcodes, out, static_cast<hipStream_t>(stream));
 }
 
 int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,

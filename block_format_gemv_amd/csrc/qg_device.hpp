@@ -335,7 +335,7 @@ struct ActKind {
 template <int BITS, int GL>
 __device__ __forceinline__ QuantLane quantize_lane(float4 v4)
 {
-    static_assert(GL == 8 || GL == 64, "activation blocks of 32 or 256 elements");
+    static_assert(GL == 8 || GL == 16 || GL == 32 || GL == 64, "activation blocks of 32 to 256 elements");
     const float v[4] = {ftz(v4.x), ftz(v4.y), ftz(v4.z), ftz(v4.w)};
     // largest magnitude, NaN passed over; non-negative floats order as integers, and an
     // infinity is the largest value left
@@ -349,13 +349,17 @@ __device__ __forceinline__ QuantLane quantize_lane(float4 v4)
     amax_bits = umax(amax_bits, (uint32_t)dpp<kDppQuadSwap1>((int)amax_bits));
     amax_bits = umax(amax_bits, (uint32_t)dpp<kDppQuadSwap2>((int)amax_bits));
     amax_bits = umax(amax_bits, (uint32_t)dpp<kDppHalfMirror>((int)amax_bits));   // 8 lanes: 32 elements
-    if constexpr (GL == 64) {
-        amax_bits = umax(amax_bits, (uint32_t)dpp<kDppRowMirror>((int)amax_bits));  // 16 lanes
+    if constexpr (GL >= 16)
+        amax_bits = umax(amax_bits, (uint32_t)dpp<kDppRowMirror>((int)amax_bits));  // 16 lanes: 64 elements
+    if constexpr (GL >= 32) {
         const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)amax_bits, 0);
         const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)amax_bits, 16);
         const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)amax_bits, 32);
         const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)amax_bits, 48);
-        amax_bits = umax(umax(r0, r1), umax(r2, r3));                              // the wave
+        if constexpr (GL == 64)
+            amax_bits = umax(umax(r0, r1), umax(r2, r3));                          // the wave
+        else
+            amax_bits = (threadIdx.x & 32) ? umax(r2, r3) : umax(r0, r1);          // half waves
     }
     QuantLane q;
     q.inf = amax_bits == 0x7F800000u;

@@ -234,6 +234,62 @@ int qg_gemv_q_multi(int fmt, int mode, int nmat, const int64_t *rows, int64_t co
                     const int8_t *codes, const qg_act_scale *scales, const int32_t *csums, float *const *outs,
                     void *stream);
 
+/*
+ * int8 KV cache ------------------------------------------------------------------------
+ *
+ * Attention over cached int8 rows on the same exact machinery ("Module numerics", Functions
+ * cache_row, int8_codes, quantize_head, int8_score, weighted_int8, attend_int8; Constants
+ * INV_127, VALUE_BLOCK).  The softmax between the scores and the weighted sum is the caller's.
+ * Head sizes hd are 32, 64, 128 or 256.  nh query heads share nkv KV heads evenly: query head
+ * h reads KV head h / (nh / nkv).  A KV cache of one KV head is npos rows: scales uint16 [npos]
+ * (binary16 bits) and codes int8 [npos][hd]; the calls take [nkv][npos] and [nkv][npos][hd].
+ * All buffers are device memory; QG_E_SHAPE for a bad head size, head counts that do not
+ * divide, or sizes out of range; QG_E_INVALID for a bad pointer or enum.
+ */
+#define QG_VALUE_BLOCK 32   /* positions per block of the weighted sum */
+
+/* Cache n rows x f32 [n][hd] (cache_row): per row the binary16 scale of amax * (1/127), amax
+ * the largest magnitude (a denormal read as 0, a NaN passed over) and the product formed in
+ * binary32, rounded to nearest even with subnormals kept (past the top it is infinite); the
+ * codes are each x times the scale's binary32 reciprocal, to the nearest integer (ties to
+ * even), within +-127 (a NaN product 0; all zero when the scale is zero).
+ *   scales  uint16 [n]       out
+ *   codes   int8 [n][hd]     out (4-byte aligned) */
+int qg_kv_cache_rows(int64_t n, int64_t hd, const float *x, uint16_t *scales, int8_t *codes, void *stream);
+
+/* Quantize nh query heads q f32 [nh][hd] (16-byte aligned) as the array reads them
+ * (quantize_head): PerBlock, the whole head one block under an 8-bit significand scale;
+ * Sub32, 32-element blocks under 4-bit ones; the rules of qg_quantize_act.
+ *   codes   int8 [nh][hd]                       out
+ *   scales  qg_act_scale [nh][1] (PerBlock) or [nh][hd/32] (Sub32)   out
+ *   err_flag int32 [1] or NULL: set to 1 when a block holds +-inf (never cleared). */
+int qg_kv_quantize_heads(int mode, int64_t nh, int64_t hd, const float *q, int8_t *codes, qg_act_scale *scales,
+                         int32_t *err_flag, void *stream);
+
+/* Scores (int8_score) of every query head against every cached key row of its KV head:
+ * out[h][j] = R32(sum over the query's blocks b of m_b 2^e_b * (sum_i c_i k_ji) * d_j), the
+ * terms summed exactly and rounded once (ftz); a key whose scale is not finite scores NaN
+ * (0x7FC00000).  No softmax scale is applied.
+ *   qcodes, qscales  one quantized head per query head, as qg_kv_quantize_heads writes them
+ *   kscales uint16 [nkv][npos], kcodes int8 [nkv][npos][hd] (16-byte aligned)
+ *   out     f32 [nh][npos] */
+int qg_kv_scores(int mode, int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const int8_t *qcodes,
+                 const qg_act_scale *qscales, const uint16_t *kscales, const int8_t *kcodes, float *out,
+                 void *stream);
+
+/* The weighted sum (weighted_int8) of every query head over its KV head's cached value rows:
+ * w_j = p_j * d_j in binary32; per block of QG_VALUE_BLOCK positions (the last one possibly
+ * shorter) the least power of two 2^E with 127 * 2^E >= the block's largest |w_j| (a denormal
+ * read as 0, a NaN passed over; E = 0 for an all-zero block) and codes u_j = rne(w_j / 2^E);
+ * per value element e the piece R32(2^E * sum_j u_j v_je); out[h][e] adds the pieces in block
+ * order (binary32, each sum flushed; NaN -> 0x7FC00000).  A block holding an infinite w_j or a
+ * value row whose scale is not finite gives NaN.  npos = 0 gives zeros.
+ *   probs   f32 [nh][npos]
+ *   vscales uint16 [nkv][npos], vcodes int8 [nkv][npos][hd]
+ *   out     f32 [nh][hd] */
+int qg_kv_weighted(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs, const uint16_t *vscales,
+                   const int8_t *vcodes, float *out, void *stream);
+
 /* Integer sums per (row, sub-block), before any scale ("Module lane", Functions
  * block_sums), for one activation row:
  *   Q4K: csum_out int32 [rows][cols/32] = sum sc_j*q*c over sub-block j,

@@ -255,6 +255,52 @@ def test_validation_refuses_before_any_gpu_work():
     assert L.qg_quantize_act(qg.Q4K, qg.PERBLOCK, 0, 256, None, None, None, None, None, None) == qg.OK
 
 
+def test_kv_validation_refuses_before_any_gpu_work():
+    """The int8 KV cache entry points refuse bad head sizes, uneven grouped heads, bad
+    scalings, null and misaligned pointers before any GPU work, and launch nothing for empty
+    work (every call below returns here, where there is no GPU)."""
+    L = qg.lib()
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1002)
+    assert L.qg_kv_cache_rows(4, 48, fake, fake, fake, None) == qg.E_SHAPE
+    assert "head size" in qg.qg_last_error()
+    assert L.qg_kv_cache_rows(-1, 64, fake, fake, fake, None) == qg.E_SHAPE
+    assert L.qg_kv_cache_rows(4, 64, None, fake, fake, None) == qg.E_INVALID
+    assert L.qg_kv_cache_rows(4, 64, fake, fake, odd, None) == qg.E_INVALID
+    assert L.qg_kv_cache_rows(0, 64, None, None, None, None) == qg.OK
+    assert L.qg_kv_quantize_heads(2, 4, 64, fake, fake, fake, None, None) == qg.E_INVALID
+    assert L.qg_kv_quantize_heads(qg.SUB32, 4, 96, fake, fake, fake, None, None) == qg.E_SHAPE
+    assert L.qg_kv_quantize_heads(qg.SUB32, 4, 64, odd, fake, fake, None, None) == qg.E_INVALID
+    assert L.qg_kv_quantize_heads(qg.PERBLOCK, 4, 64, fake, fake, None, None, None) == qg.E_INVALID
+    assert L.qg_kv_quantize_heads(qg.PERBLOCK, 70000, 64, fake, fake, fake, None, None) == qg.E_SHAPE
+    assert L.qg_kv_quantize_heads(qg.PERBLOCK, 0, 64, None, None, None, None, None) == qg.OK
+    assert L.qg_kv_scores(qg.PERBLOCK, 6, 4, 10, 64, fake, fake, fake, fake, fake, None) == qg.E_SHAPE
+    assert "KV heads" in qg.qg_last_error()
+    assert L.qg_kv_scores(qg.PERBLOCK, 8, 0, 10, 64, fake, fake, fake, fake, fake, None) == qg.E_SHAPE
+    assert L.qg_kv_scores(qg.SUB32, 8, 2, -1, 64, fake, fake, fake, fake, fake, None) == qg.E_SHAPE
+    assert L.qg_kv_scores(qg.SUB32, 8, 2, 1 << 26, 64, fake, fake, fake, fake, fake, None) == qg.E_SHAPE
+    assert L.qg_kv_scores(qg.SUB32, 8, 2, 10, 64, fake, fake, fake, odd, fake, None) == qg.E_INVALID
+    assert L.qg_kv_scores(3, 8, 2, 10, 64, fake, fake, fake, fake, fake, None) == qg.E_INVALID
+    assert L.qg_kv_scores(qg.SUB32, 8, 2, 0, 64, None, None, None, None, None, None) == qg.OK
+    assert L.qg_kv_weighted(8, 3, 10, 64, fake, fake, fake, fake, None) == qg.E_SHAPE
+    assert L.qg_kv_weighted(8, 2, 10, 64, fake, fake, fake, None, None) == qg.E_INVALID
+    assert L.qg_kv_weighted(8, 2, 10, 64, fake, odd, ctypes.c_void_p(0x1001), fake, None) == qg.E_INVALID
+    assert L.qg_kv_weighted(0, 2, 10, 64, None, None, None, None, None) == qg.OK
+
+
+def test_kv_binding_refuses_short_buffers():
+    """The binding checks buffer sizes the C ABI cannot see."""
+    import torch
+    x = torch.zeros(4 * 64 - 1, dtype=torch.float32)
+    with pytest.raises(qg.QGError) as ei:
+        qg.qg_kv_cache_rows(4, 64, x, torch.zeros(4, dtype=torch.int16), torch.zeros(256, dtype=torch.int8))
+    assert ei.value.status == qg.E_SHAPE
+    with pytest.raises(qg.QGError):
+        qg.qg_kv_scores(qg.SUB32, 4, 2, 8, 64, torch.zeros(256, dtype=torch.int8),
+                        torch.zeros(4, dtype=torch.int32), torch.zeros(16, dtype=torch.int16),
+                        torch.zeros(1024, dtype=torch.int8), torch.zeros(32, dtype=torch.float32))
+
+
 def test_argmax_key_decoding():
     """qg_argmax_index: key 0 is "none" (index 0); otherwise the low word is ~row."""
     assert qg.qg_argmax_index(0) == 0

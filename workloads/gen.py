@@ -38,6 +38,7 @@ SEED_REP_X = 1_000_000          # repetition k of the decode workload uses SEED_
 SEED_OUT_W, SEED_OUT_X = 120, 121
 SEED_SUB32_X = 130              # repetition k uses SEED_SUB32_X + k
 SEED_BATCH_X = 140              # batch of N columns uses SEED_BATCH_X + N
+SEED_KV = 160                   # decode attention over a cached context: keys, values, query, weights
 
 
 def _rng(seed: int) -> np.random.Generator:
@@ -180,3 +181,36 @@ def sub32_act(rep: int, cols: int = 4096):
 
 def batch_act(n: int, cols: int = 4096) -> np.ndarray:
     return act_normal(n, cols, SEED_BATCH_X + n)
+
+
+# --- attention over an int8 KV cache -----------------------------------------------------
+
+def kv_rows(n: int, hd: int, seed: int) -> np.ndarray:
+    """n cached key or value rows of hd elements, float32: N(0,1) times a per-row magnitude
+    2^u with u uniform in [-3, 3] (rows of one context differ in size)."""
+    g = _rng(seed)
+    x = g.standard_normal((n, hd))
+    x *= np.exp2(g.uniform(-3.0, 3.0, size=(n, 1)))
+    return x.astype(np.float32)
+
+
+def attn_weights(nh: int, npos: int, seed: int) -> np.ndarray:
+    """Per-head attention weights over npos positions, float32, each row positive and summing
+    to about 1: exp of N(0, 2^2) draws, normalised in float64 (a peaked, uneven mix)."""
+    g = _rng(seed)
+    z = g.standard_normal((nh, npos)) * 2.0
+    w = np.exp(z - z.max(axis=1, keepdims=True)) if npos else z
+    if npos:
+        w /= w.sum(axis=1, keepdims=True)
+    return w.astype(np.float32)
+
+
+def kv_decode(nh: int = 32, nkv: int = 8, npos: int = 4096, hd: int = 128, seed: int = SEED_KV):
+    """One decode step's attention inputs (Llama-8B grouped-query shapes by default): the
+    context's keys and values f32 [nkv, npos, hd], the query f32 [nh, hd] and the weights
+    f32 [nh, npos]."""
+    keys = kv_rows(nkv * npos, hd, seed).reshape(nkv, npos, hd)
+    vals = kv_rows(nkv * npos, hd, seed + 1).reshape(nkv, npos, hd)
+    query = act_normal(nh, hd, seed + 2)
+    weights = attn_weights(nh, npos, seed + 3)
+    return keys, vals, query, weights
