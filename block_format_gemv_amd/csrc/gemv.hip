@@ -247,11 +247,17 @@ struct TileRegs<QG_Q4K> {
     static constexpr int kBytes = kTileBytesQ4K;
     uint4 w[8];     // code chunks (sub-blocks 0..7)
     uint4 meta;     // d | dmin << 16, then the 96-bit sc/mn field string
+    // Issued in the order they are used (the meta chunk, then sub-blocks 0..7), each kept
+    // in place, so a wave waits for one chunk at a time and starts on the first while the
+    // rest are in flight.
     __device__ __forceinline__ void load(const uint8_t *tile, int lane)
     {
-#pragma unroll
-        for (int i = 0; i < 8; i++) w[i] = ld_stream(tile + 1024 * i + 16 * lane);
         meta = ld_stream(tile + 8192 + 16 * lane);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            __builtin_amdgcn_sched_barrier(0);
+            w[i] = ld_stream(tile + 1024 * i + 16 * lane);
+        }
     }
 };
 
@@ -317,17 +323,25 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q4K> &T, int b, co
     f[6] = q4k_field<6>(T.meta.y, T.meta.z, T.meta.w);
     f[7] = q4k_field<7>(T.meta.y, T.meta.z, T.meta.w);
     if constexpr (MODE == QG_PERBLOCK) {
+        // Everything that needs the meta chunk alone (it arrives first) is done before the
+        // code chunks are waited for: the offset sum, the block scales and their product
+        // with it (exact, as in piece_q4k_perblock_near).
         int Cb = 0, Ob = 0;
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int P = q4k_sub(T.w[i], b, i, act);
-            Cb += __mul24((int)(f[i] & 63u), P);
-            Ob += __mul24((int)(f[i] >> 6), act.sum32(b, i));
-        }
+        for (int i = 0; i < 8; i++) Ob += __mul24((int)(f[i] >> 6), act.sum32(b, i));
         const qg_act_scale s = act.scale(b, 0, 1);
         const float fd = f16_value(T.meta.x), fm = f16_value(T.meta.x >> 16);
-        if (__all(q4k_near(fd, fm)))
-            return piece_q4k_perblock_near(Cb, Ob, (double)fd, (double)fm, __builtin_ldexp((double)s.m, s.e));
+        const bool near = __all(q4k_near(fd, fm));
+        const double Dd = (double)fd, S = __builtin_ldexp((double)s.m, s.e);
+        const double nOD = -((double)Ob * (double)fm);
+        // sub-block by sub-block in load order: each waits for its own chunk only
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int P = q4k_sub(T.w[i], b, i, act);
+            Cb += __mul24((int)(f[i] & 63u), P);
+        }
+        if (near) return r32_exact_double(__builtin_fma((double)Cb, Dd, nOD) * S);
         return piece_q4k_perblock(Cb, Ob, T.meta.x, s.m, s.e);
     } else {
         int Cj[8], Oj[8], m[8], e[8];
@@ -737,12 +751,52 @@ __device__ __forceinline__ Picked pick_matrix(const Targets &tg)
     return p;
 }
 
+// A piece is R32 of an exact value X that is an integer multiple of 2^(e + eps): e an
+// activation scale exponent of its block and eps >= -24 the exponent of the least place of a
+// binary16 block scale.  With every such e >= -78 a nonzero X is at least 2^-102, and so is
+// its rounding: no piece of the block is tiny (tiny_piece), whatever the weights.
+constexpr int kNoTinyExp = -78;
+
+// whether any of the W flag bytes is set (wave-uniform)
+template <int W>
+__device__ __forceinline__ bool any_flag(const unsigned char *f)
+{
+    uint32_t v;
+    if constexpr (W == 16) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(f);
+        v = q.x | q.y | q.z | q.w;
+    } else if constexpr (W == 8) {
+        const uint2 q = *reinterpret_cast<const uint2 *>(f);
+        v = q.x | q.y;
+    } else {
+        v = *reinterpret_cast<const uint32_t *>(f);
+    }
+    return __builtin_amdgcn_readfirstlane((int)v) != 0;
+}
+
+// +0 plus the N pieces p[0], p[stride], ... in order with plain binary32 adds (all reads
+// issued first).  Equal to the flushed fold when no piece is tiny: see fold_chain.
+template <int N>
+__device__ __forceinline__ float fold_fixed(const float *p, int stride)
+{
+    float a[N];
+#pragma unroll
+    for (int k = 0; k < N; k++) a[k] = p[(size_t)k * stride];
+    float y = 0.0f;
+#pragma unroll
+    for (int k = 0; k < N; k++) y = y + a[k];
+    return y;
+}
+
 template <int FMT, int MODE, int SRC, int W, bool DB>
 __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, ActIO io)
 {
     extern __shared__ __align__(16) float s_piece[];
     using T = TileRegs<FMT>;
     constexpr int BITS = ActKind<FMT, MODE>::kBits, GL = ActKind<FMT, MODE>::kLanes;
+    // pieces: G per row with DB, else W (one per wave); then one flag byte per wave
+    unsigned char *s_small = reinterpret_cast<unsigned char *>(s_piece + (size_t)(DB ? G : W) * 64);
+    bool small = false;                          // a block of this wave may give a tiny piece
     const Picked pm = pick_matrix(tg);           // this workgroup's matrix (wave-uniform)
     const int g = pm.g;
     const int rows = pm.rows;
@@ -756,6 +810,12 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
     // the last block works on a copy of it and stores nothing), kept in this order
     const int bf = min(wid, G - 1);
     ActRaw<SRC> r0 = load_act<SRC, GL>(io, bf, lane);
+    // Every wave's activation load is issued before any wave's tile loads (a barrier that
+    // waits for no memory): a compute unit hands back vector loads in issue order, so an
+    // activation load queued behind other waves' tiles would arrive with them, and that
+    // wave's activation work would land at the end of the weight stream.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     T t0;
     [[maybe_unused]] T t1;
@@ -779,6 +839,7 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
                 load_fence();
             }
             s_piece[(size_t)b * 64 + lane] = piece_one<FMT, MODE>(t0, b, a0);
+            small |= __ballot(a0.e < kNoTinyExp) != 0;
             if (b1 >= G) break;
             const ActWave a1 = ready_act<SRC, BITS, GL>(r1, b1, G, lane, emit, io);
             const int b2 = b + 2 * W;
@@ -789,21 +850,29 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
                 load_fence();
             }
             s_piece[(size_t)b1 * 64 + lane] = piece_one<FMT, MODE>(t1, b1, a1);
+            small |= __ballot(a1.e < kNoTinyExp) != 0;
             if (b2 >= G) break;
             a0 = ready_act<SRC, BITS, GL>(r0, b2, G, lane, emit, io);
             b = b2;
         } while (true);
     } else {
-        // at most one block per wave; a wave past the last block computes a copy and drops it
+        // at most one block per wave; a wave past the last block computes a copy and parks +0
         const float p = piece_one<FMT, MODE>(t0, bf, a0);
-        if (wid < G) s_piece[(size_t)wid * 64 + lane] = p;
+        s_piece[(size_t)wid * 64 + lane] = wid < G ? p : 0.0f;
+        small |= __ballot(a0.e < kNoTinyExp) != 0;
     }
+    if (lane == 0) s_small[wid] = small ? 1 : 0;
     __syncthreads();
 
-    // the first wave adds each row's pieces in block order, one row per lane
+    // the first wave adds each row's pieces in block order, one row per lane: plain adds
+    // unless a block's activation exponent allows a tiny piece (then the flushed chain)
     if (wid == 0) {
         const int64_t row = (int64_t)g * 64 + lane;
-        float y = canon_nan(fold_ftz(0.0f, s_piece + lane, G, 64));
+        float y;
+        if (any_flag<W>(s_small)) y = fold_flushed(0.0f, s_piece + lane, G, 64);
+        else if constexpr (DB) y = fold_chain_plain(0.0f, s_piece + lane, G, 64);
+        else y = fold_fixed<W>(s_piece + lane, 64);   // G <= W; the pieces past G are +0
+        y = canon_nan(y);
         if (row < rows) out[row] = y;
         if (io.argmax) {
             // the largest key of the group's 64 rows, then one atomic max per workgroup
@@ -989,7 +1058,8 @@ int launch_one_typed(const Targets &tg, int G, const ActIO &io, hipStream_t s)
 {
     const int64_t groups = tg.gstart[tg.nmat];
     if (groups == 0) return QG_OK;
-    const size_t lds = (size_t)G * 64 * sizeof(float);
+    if (!DB && G > W) return fail(QG_E_RUNTIME, "gemv: %d blocks do not fit %d waves", G, W);
+    const size_t lds = (size_t)(DB ? G : W) * 64 * sizeof(float) + 16;
     hipEvent_t ev0, ev1;
     take_timing_events(&ev0, &ev1);
     if (ev0 && ev1)

@@ -104,6 +104,13 @@ __device__ __forceinline__ float fold_chain(float y, int &lo, const float *p, in
     return y;
 }
 
+// acc plus the pieces with plain adds, for a row none of whose pieces is tiny
+__device__ __forceinline__ float fold_chain_plain(float acc, const float *p, int n, int stride)
+{
+    int lo = 0;
+    return fold_chain<false>(acc, lo, p, n, stride);
+}
+
 __device__ __forceinline__ float fold_flushed(float y, const float *p, int n, int stride)
 {
     for (int i = 0; i < n; i++) y = fadd_ftz(y, p[(size_t)i * stride]);
@@ -274,24 +281,38 @@ __device__ __forceinline__ float exact_sum(const long long (&v)[N], const int (&
 // rne_div, quantize, quantize_blocks).  A block of 256 elements spans the wave, one of 32
 // spans eight lanes: BITS significant bits (8 PerBlock, 4 Sub32) over GL lanes (64 or 8).
 //
-// The scale comes from amax/127 in f64: the quotient is within 2^-53 of amax/127, and the
-// nearest grid point of `bits` significant bits lies at least 2^-25 of it away unless it
-// equals it, so rounding the f64 quotient up to `bits` significant bits gives the least
-// admissible scale.  Codes are rint(x / s) in f64: |x/s| <= 127, and an f64 quotient that
-// is not a half-integer cannot round onto one, so ties are exactly the true ties and go
-// to even.
+// The scale: t = amax * (1/127) in f64 is within 2^-52 (relative) of amax/127, while a grid
+// point of BITS significant bits lies at least 2^-24 (relative) from amax/127 unless it
+// equals it (amax has 24 significant bits).  So the least grid point at or above t is the
+// least admissible scale, except when amax/127 is itself a grid point and t lies above it;
+// then the grid point below the candidate is admissible, which the exact test
+// 127*m*2^e >= amax (in f64) finds.
+//
+// The codes: q = x/s has |q| <= 127.5, and a q that is not a half-integer lies more than
+// 2^-26 from every half-integer (x = X*2^k with |X| < 2^24, s = m*2^e: near a half-integer
+// the gap is a nonzero multiple of 1/(2m*2^(e-k)) with 2m*2^(e-k) < 4|X|).  In binary32,
+// t = (x*2^-e) * fl(1/m) is within 2^-16 of q (x*2^-e exact or below 2^-100; two roundings
+// of 2^-24 relative), so rint(t) is q rounded to nearest unless t lies within 2^-14 of a
+// half-integer.  Such elements (a few per thousand) are coded from the correctly rounded f64
+// quotient instead: an f64 quotient that is not a half-integer cannot round onto one, so its
+// ties are exactly the true ties and go to even.
 
 // least m*2^e (m with BITS significant bits) not below amax/127, amax finite and > 0
 template <int BITS>
 __device__ __forceinline__ void least_scale(float amax, int &m, int &e)
 {
-    const double t = (double)amax / 127.0;
+    const double t = (double)amax * (1.0 / 127.0);
     int k;
     const double f = __builtin_frexp(t, &k);                // t = f * 2^k, f in [0.5, 1)
-    double mm = __builtin_ceil(__builtin_ldexp(f, BITS));   // in [2^(BITS-1), 2^BITS]
+    int mm = (int)__builtin_ceil(__builtin_ldexp(f, BITS)); // in [2^(BITS-1), 2^BITS]
     int ee = k - BITS;
-    if (mm == (double)(1 << BITS)) { mm = (double)(1 << (BITS - 1)); ee += 1; }
-    m = (int)mm;
+    if (mm == (1 << BITS)) { mm = 1 << (BITS - 1); ee += 1; }
+    // the grid point below the candidate, taken when it is admissible (127 * 255 < 2^15:
+    // the product and the comparison are exact)
+    int pm = mm - 1, pe = ee;
+    if (pm < (1 << (BITS - 1))) { pm = (1 << BITS) - 1; pe = ee - 1; }
+    if (__builtin_ldexp(127.0 * (double)pm, pe) >= (double)amax) { mm = pm; ee = pe; }
+    m = mm;
     e = ee;
 }
 
@@ -373,11 +394,18 @@ __device__ __forceinline__ QuantLane quantize_lane(float4 v4)
     q.packed = 0;
     q.sum4 = 0;
     if (q.m != 0) {
-        const double s = __builtin_ldexp((double)q.m, q.e);
+        const float rm = 1.0f / (float)q.m;                 // correctly rounded
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             int c = 0;
-            if (v[i] == v[i]) c = (int)__builtin_rint((double)v[i] / s);
+            if (v[i] == v[i]) {
+                const float t = __builtin_ldexpf(v[i], -q.e) * rm;
+                const float r = __builtin_rintf(t);
+                c = (int)r;
+                // t - r is exact (|t - r| <= 1/2 and r is 0 or within a factor 2 of t)
+                if (__builtin_fabsf(__builtin_fabsf(t - r) - 0.5f) < 0x1p-14f)
+                    c = (int)__builtin_rint((double)v[i] / __builtin_ldexp((double)q.m, q.e));
+            }
             q.sum4 += c;
             q.packed |= ((uint32_t)c & 0xFFu) << (8 * i);
         }

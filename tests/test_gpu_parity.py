@@ -108,6 +108,49 @@ def test_quantize_matches_oracle(qg, mode):
         assert np.array_equal(s, os_), name
 
 
+def _tie_rows(mode: int, nblocks: int, seed: int) -> np.ndarray:
+    """Activation rows built on the quantizer's grid: per activation block a scale s = m*2^e,
+    an element at exactly 127*s (the least-scale boundary) or one binary32 step either side
+    of it, and the other elements at exact half-integer multiples of s (ties), one step
+    either side of a tie, or exact multiples of s.  Every value is exact in binary32."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    blk, lo, hi = (256, 128, 256) if mode == 0 else (32, 8, 16)
+    x = np.empty((nblocks, blk), np.float32)
+    for b in range(nblocks):
+        m = int(g.integers(lo, hi))
+        e = int(g.integers(-118, 100))
+        n = g.integers(-127, 127, blk)
+        kind = g.integers(0, 4, blk)
+        half = np.ldexp((2.0 * n + 1.0) * m, e - 1).astype(np.float32)        # (n + 1/2) * s
+        v = np.where(kind == 0, half, np.where(kind == 1, np.nextafter(half, np.float32(np.inf)),
+                     np.where(kind == 2, np.nextafter(half, np.float32(-np.inf)),
+                              np.ldexp(float(m) * n, e).astype(np.float32))))
+        top = np.float32(np.ldexp(127.0 * m, e))
+        top = [top, np.nextafter(top, np.float32(np.inf)), np.nextafter(top, np.float32(0))][b % 3]
+        v[int(g.integers(0, blk))] = top if b % 2 else -top
+        x[b] = v.astype(np.float32)
+    return x.reshape(-1, 1024)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_quantize_ties_and_grid_boundaries(qg, mode):
+    """Codes of exact ties (to even) and of values one binary32 step from a tie, and the
+    least scale when the block's largest magnitude is exactly 127*m*2^e or one step off it:
+    the quantizer, the one-launch quantize + GEMV and the oracle agree bit for bit."""
+    x = _tie_rows(mode, 4096 if mode == 0 else 8192, 77 + mode)
+    say("quantize ties", x.shape, "mode", mode)
+    _, c, m, e, s = gpu_quant(qg, x, mode)
+    oc, om, oe, os_ = oracle.quantize(x, mode)
+    assert np.array_equal(m, om) and np.array_equal(e, oe)
+    assert np.array_equal(c, oc) and np.array_equal(s, os_)
+    f = gen.q4k_fields(64, 1024, 5)
+    M = Mat(qg, f)
+    for r in range(0, x.shape[0], 97):
+        out, fc, fm, fe, fs = _fused(qg, M, x[r:r + 1], mode)
+        assert np.array_equal(fc, oc[r:r + 1]) and np.array_equal(fm, om[r:r + 1]) and np.array_equal(fe, oe[r:r + 1])
+        assert first_mismatch(out, oracle.gemv(f, oc[r:r + 1], om[r:r + 1], oe[r:r + 1], mode)) is None, r
+
+
 def test_quantize_infinity_raises_the_flag(qg):
     x = gen.act_normal(2, 1024, 4)
     x[1, 600] = np.inf
@@ -438,6 +481,31 @@ def test_subnormal_partial_sums_gemv_and_gemm(qg):
         qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 0)
+
+
+@pytest.mark.parametrize("cols", [4096, 8192])
+def test_subnormal_partial_sums_wide_rows(qg, cols):
+    """The same cancelling rows at 16 blocks (one wave per block) and 32 blocks (two tiles
+    per wave), their later blocks zero: the quantized-row GEMV and the one-launch step give
+    the oracle's bits, 8 units where unflushed adds would give 7."""
+    rows = 70
+    f = gen.q4k_fields(rows, cols, 79)
+    for r in (0, 5, 69):
+        _subnormal_partial_q4k(f, r)
+        f["q"][r, 768:] = 0
+        f["mn"][r, 24:] = 0
+    M = Mat(qg, f)
+    x = np.full((1, cols), np.float32(2.0 ** -112), np.float32)
+    c, m, e, _ = oracle.quantize(x, 0)
+    want = oracle.gemv(f, c, m, e, 0)
+    unit = np.float32(16380.0 * 2.0 ** -142)
+    assert bits(want)[0] == np.float32(8 * unit).view(np.uint32)
+    act, gc, gm, ge, _ = gpu_quant(qg, x, 0)
+    assert np.array_equal(gc, c)
+    say("subnormal partial sums, wide rows", cols)
+    assert first_mismatch(run_gemv(qg, M, act), want) is None
+    out, *_ = _fused(qg, M, x, 0)
+    assert first_mismatch(out, want) is None
 
 
 # --- quantize + GEMV in one launch ------------------------------------------------------------
