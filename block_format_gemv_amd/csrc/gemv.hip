@@ -31,6 +31,19 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c)
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
+// A piece is R32 of an exact value X that is an integer multiple of 2^(e + eps): e an
+// activation scale exponent of its block and eps >= -24 the exponent of the least place of a
+// binary16 block scale.  With every such e >= -78 a nonzero X is at least 2^-102, and so is
+// its rounding: no piece of the block is tiny (tiny_piece), whatever the weights.
+constexpr int kNoTinyExp = -78;
+
+// a * b + c with a and b taken as signed 24-bit integers (exact when |a|, |b| < 2^23 and the
+// result fits 32 bits): the target's 24-bit multiply, which reads the low 24 bits of each
+// operand as they are (__mul24 would first mask b to 24 bits with two shifts).  A compiler
+// intrinsic rather than inline assembly, so the instruction takes part in hazard checking.
+extern "C" __device__ int qg_llvm_mul_i24(int, int) __asm("llvm.amdgcn.mul.i24");
+__device__ __forceinline__ int mad_i24(int a, int b, int c) { return qg_llvm_mul_i24(a, b) + c; }
+
 // ---------------------------------------------------------------------------------------
 // Activation sources.  Each hands out wave-uniform values: codes16(b, i) = codes 16i..16i+15
 // of block b, sum32 / sum16 = code sums of a 32- / 16-element run, scale(b, j, per_block).
@@ -335,13 +348,20 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q4K> &T, int b, co
         const double Dd = (double)fd, S = __builtin_ldexp((double)s.m, s.e);
         const double nOD = -((double)Ob * (double)fm);
         // sub-block by sub-block in load order: each waits for its own chunk only
+        // (|P| < 2^16, sc < 64: |Cb| < 2^25)
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             __builtin_amdgcn_sched_barrier(0);
             const int P = q4k_sub(T.w[i], b, i, act);
-            Cb += __mul24((int)(f[i] & 63u), P);
+            Cb = mad_i24((int)(f[i] & 63u), P, Cb);
         }
-        if (near) return r32_exact_double(__builtin_fma((double)Cb, Dd, nOD) * S);
+        if (near) {
+            const double X = __builtin_fma((double)Cb, Dd, nOD) * S;
+            // an activation exponent >= kNoTinyExp: X is 0 or at least 2^-102, so the
+            // conversion needs no flush, and adding +0 turns an exact -0 into +0
+            if (s.e >= kNoTinyExp) return (float)X + 0.0f;
+            return r32_exact_double(X);
+        }
         return piece_q4k_perblock(Cb, Ob, T.meta.x, s.m, s.e);
     } else {
         int Cj[8], Oj[8], m[8], e[8];
@@ -750,12 +770,6 @@ __device__ __forceinline__ Picked pick_matrix(const Targets &tg)
     }
     return p;
 }
-
-// A piece is R32 of an exact value X that is an integer multiple of 2^(e + eps): e an
-// activation scale exponent of its block and eps >= -24 the exponent of the least place of a
-// binary16 block scale.  With every such e >= -78 a nonzero X is at least 2^-102, and so is
-// its rounding: no piece of the block is tiny (tiny_piece), whatever the weights.
-constexpr int kNoTinyExp = -78;
 
 // whether any of the W flag bytes is set (wave-uniform)
 template <int W>

@@ -281,39 +281,37 @@ __device__ __forceinline__ float exact_sum(const long long (&v)[N], const int (&
 // rne_div, quantize, quantize_blocks).  A block of 256 elements spans the wave, one of 32
 // spans eight lanes: BITS significant bits (8 PerBlock, 4 Sub32) over GL lanes (64 or 8).
 //
-// The scale: t = amax * (1/127) in f64 is within 2^-52 (relative) of amax/127, while a grid
-// point of BITS significant bits lies at least 2^-24 (relative) from amax/127 unless it
-// equals it (amax has 24 significant bits).  So the least grid point at or above t is the
-// least admissible scale, except when amax/127 is itself a grid point and t lies above it;
-// then the grid point below the candidate is admissible, which the exact test
-// 127*m*2^e >= amax (in f64) finds.
+// The scale: exact integer arithmetic on amax's significand (least_scale).
 //
 // The codes: q = x/s has |q| <= 127.5, and a q that is not a half-integer lies more than
 // 2^-26 from every half-integer (x = X*2^k with |X| < 2^24, s = m*2^e: near a half-integer
 // the gap is a nonzero multiple of 1/(2m*2^(e-k)) with 2m*2^(e-k) < 4|X|).  In binary32,
-// t = (x*2^-e) * fl(1/m) is within 2^-16 of q (x*2^-e exact or below 2^-100; two roundings
-// of 2^-24 relative), so rint(t) is q rounded to nearest unless t lies within 2^-14 of a
-// half-integer.  Such elements (a few per thousand) are coded from the correctly rounded f64
-// quotient instead: an f64 quotient that is not a half-integer cannot round onto one, so its
-// ties are exactly the true ties and go to even.
+// t = (x*2^-e) * rcp(m) is within 2^-15 of q (x*2^-e exact or below 2^-100; v_rcp_f32 within
+// one ulp, 2^-23 relative, and one rounding of 2^-24), so rint(t) is q rounded to nearest
+// unless t lies within 2^-13 of a half-integer.  Such elements (a few per ten thousand) are
+// coded from the correctly rounded f64 quotient instead: an f64 quotient that is not a
+// half-integer cannot round onto one, so its ties are exactly the true ties and go to even.
 
-// least m*2^e (m with BITS significant bits) not below amax/127, amax finite and > 0
+// least m*2^e (m with BITS significant bits) not below amax/127, amax a normal binary32 > 0
+// (finite).  With amax = A*2^(E-150), A the 24-bit significand: scales m*2^(E-150+j) with
+// 127*m*2^j >= A.  At j = J0 every admissible grid point lies above every grid point of a
+// lower exponent (127*(2^BITS - 1)*2^(J0-1) < 2^23 <= A), so m = ceil(A / (127*2^J0)) is
+// the least one when it has BITS bits; otherwise no grid point of exponent J0 is admissible
+// and m = ceil(A / (127*2^(J0+1))) (at least 2^(BITS-1)) at J0 + 1 is.  Integer arithmetic
+// only (uniform operands stay scalar).
 template <int BITS>
 __device__ __forceinline__ void least_scale(float amax, int &m, int &e)
 {
-    const double t = (double)amax * (1.0 / 127.0);
-    int k;
-    const double f = __builtin_frexp(t, &k);                // t = f * 2^k, f in [0.5, 1)
-    int mm = (int)__builtin_ceil(__builtin_ldexp(f, BITS)); // in [2^(BITS-1), 2^BITS]
-    int ee = k - BITS;
-    if (mm == (1 << BITS)) { mm = 1 << (BITS - 1); ee += 1; }
-    // the grid point below the candidate, taken when it is admissible (127 * 255 < 2^15:
-    // the product and the comparison are exact)
-    int pm = mm - 1, pe = ee;
-    if (pm < (1 << (BITS - 1))) { pm = (1 << BITS) - 1; pe = ee - 1; }
-    if (__builtin_ldexp(127.0 * (double)pm, pe) >= (double)amax) { mm = pm; ee = pe; }
-    m = mm;
-    e = ee;
+    constexpr int J0 = BITS == 1 ? 17 : 17 - BITS;
+    constexpr uint32_t D0 = 127u << J0, D1 = 127u << (J0 + 1);
+    const uint32_t u = __float_as_uint(amax);
+    const uint32_t A = (u & 0x7FFFFFu) | 0x800000u;
+    const int E = (int)(u >> 23);
+    uint32_t mm = (A + D0 - 1) / D0;
+    int j = J0;
+    if (mm >= (1u << BITS)) { mm = (A + D1 - 1) / D1; j = J0 + 1; }
+    m = (int)mm;
+    e = E - 150 + j;
 }
 
 // Lane exchanges within rows of 16 lanes through DPP (every source lane is valid)
@@ -357,14 +355,16 @@ template <int BITS, int GL>
 __device__ __forceinline__ QuantLane quantize_lane(float4 v4)
 {
     static_assert(GL == 8 || GL == 16 || GL == 32 || GL == 64, "activation blocks of 32 to 256 elements");
-    const float v[4] = {ftz(v4.x), ftz(v4.y), ftz(v4.z), ftz(v4.w)};
-    // largest magnitude, NaN passed over; non-negative floats order as integers, and an
-    // infinity is the largest value left
+    // a denormal reads as 0 and so does a NaN (passed over by absmax, code 0): one class test
+    // (quiet and signalling NaN, negative and positive denormal)
+    const float raw[4] = {v4.x, v4.y, v4.z, v4.w};
+    float v[4];
     uint32_t amax_bits = 0;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const uint32_t a = __float_as_uint(v[i]) & 0x7FFFFFFFu;
-        if (a <= 0x7F800000u && a > amax_bits) amax_bits = a;
+        v[i] = __builtin_amdgcn_classf(raw[i], 0x93) ? 0.0f : raw[i];
+        const uint32_t a = __float_as_uint(v[i]) & 0x7FFFFFFFu;   // non-negative floats order as integers
+        amax_bits = a > amax_bits ? a : amax_bits;
     }
     auto umax = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
     amax_bits = umax(amax_bits, (uint32_t)dpp<kDppQuadSwap1>((int)amax_bits));
@@ -394,20 +394,31 @@ __device__ __forceinline__ QuantLane quantize_lane(float4 v4)
     q.packed = 0;
     q.sum4 = 0;
     if (q.m != 0) {
-        const float rm = 1.0f / (float)q.m;                 // correctly rounded
+        // t = (x * 2^-e) * rcp(m); v_rcp_f32 is within one ulp of 1/m (see the comment above)
+        const float rm = __builtin_amdgcn_rcpf((float)q.m);
+        float t[4], r[4];
+        bool near = false;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            int c = 0;
-            if (v[i] == v[i]) {
-                const float t = __builtin_ldexpf(v[i], -q.e) * rm;
-                const float r = __builtin_rintf(t);
-                c = (int)r;
-                // t - r is exact (|t - r| <= 1/2 and r is 0 or within a factor 2 of t)
-                if (__builtin_fabsf(__builtin_fabsf(t - r) - 0.5f) < 0x1p-14f)
-                    c = (int)__builtin_rint((double)v[i] / __builtin_ldexp((double)q.m, q.e));
-            }
-            q.sum4 += c;
-            q.packed |= ((uint32_t)c & 0xFFu) << (8 * i);
+            t[i] = __builtin_ldexpf(v[i], -q.e) * rm;
+            r[i] = __builtin_rintf(t[i]);
+            // t - r is exact (|t - r| <= 1/2 and r is 0 or within a factor 2 of t)
+            near |= __builtin_fabsf(__builtin_fabsf(t[i] - r[i]) - 0.5f) < 0x1p-13f;
+        }
+        int c[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) c[i] = (int)r[i];
+        if (near) {
+            const double s = __builtin_ldexp((double)q.m, q.e);
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                if (__builtin_fabsf(__builtin_fabsf(t[i] - r[i]) - 0.5f) < 0x1p-13f)
+                    c[i] = (int)__builtin_rint((double)v[i] / s);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            q.sum4 += c[i];
+            q.packed |= ((uint32_t)c[i] & 0xFFu) << (8 * i);
         }
     }
     return q;
