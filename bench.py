@@ -94,7 +94,11 @@ WORKLOADS = {
     "q4k_gemm_n2_14336x4096": ("q4k", 14336, 4096, 0, 2),
     "q4k_gemm_n8_14336x4096": ("q4k", 14336, 4096, 0, 8),
     "q4k_gemm_n64_14336x4096": ("q4k", 14336, 4096, 0, 64),
+    # int8 KV cache (attention of one decode step): ("kv", query heads, KV heads, positions,
+    # head size, query scaling)
+    "kv_decode_32h_8kv_4096pos_128hd": ("kv", 32, 8, 4096, 128, 0),
 }
+KV_METRIC = "int8 KV-cache attention stream GB/s at 1 GPU"
 DEFAULT = "q4k_ffn_up_14336x4096"
 
 
@@ -229,6 +233,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = WORKLOADS[args.workload]
+    if wl[0] == "kv":
+        kv_main(args, wl, torch, qg, Hip())
+        return
     fmt_s, _, cols, mode, ncol = wl
     fmt = qg.FMT_CODES[fmt_s]
     dev = torch.device("cuda:0")
@@ -454,6 +461,181 @@ def main():
         record["cpu_baseline"] = cb
         record["parity_step0"] = bool(np.array_equal(cpu_outs[0].reshape(-1).view(np.uint32),
                                                      first.reshape(-1).view(np.uint32)))
+    print(json.dumps(record), flush=True)
+
+
+def kv_main(args, wl, torch, qg, hip):
+    """One decode step of attention over an int8 KV cache: the step appends the new
+    position's key and value rows to the cache (qg_kv_cache_rows), quantizes the query heads
+    (qg_kv_quantize_heads), scores them against every cached key (qg_kv_scores) and forms the
+    weighted sum of the cached values (qg_kv_weighted) with given attention weights (the
+    softmax between the two is the caller's and is not timed).  The caches rotate over copies
+    of at least --cold-bytes, like the GEMV's weights."""
+    from workloads import gen
+
+    _, nh, nkv, npos, hd, mode = wl
+    dev = torch.device("cuda:0")
+    keys, vals, query, weights = gen.kv_decode(nh, nkv, npos, hd)
+    rows = nkv * npos
+    ks = torch.zeros(rows, dtype=torch.int16, device=dev)
+    kc = torch.zeros((rows, hd), dtype=torch.int8, device=dev)
+    vs = torch.zeros(rows, dtype=torch.int16, device=dev)
+    vc = torch.zeros((rows, hd), dtype=torch.int8, device=dev)
+    qg.qg_kv_cache_rows(rows, hd, torch.from_numpy(keys.reshape(-1, hd)).to(dev), ks, kc)
+    qg.qg_kv_cache_rows(rows, hd, torch.from_numpy(vals.reshape(-1, hd)).to(dev), vs, vc)
+    cache_bytes = 2 * (rows * hd + 2 * rows)
+    copies = 1 if args.warm else max(1, int(np.ceil(args.cold_bytes / cache_bytes)))
+    caches = [(ks, kc, vs, vc)] + [(ks.clone(), kc.clone(), vs.clone(), vc.clone()) for _ in range(copies - 1)]
+    n_q = 64
+    qs = [torch.from_numpy(gen.act_normal(nh, hd, gen.SEED_KV + 10 + k)).to(dev) for k in range(n_q)]
+    new_rows = [torch.from_numpy(gen.kv_rows(2 * nkv, hd, gen.SEED_KV + 200 + k)).to(dev) for k in range(n_q)]
+    probs = torch.from_numpy(weights).to(dev)
+    nb = 1 if mode == qg.PERBLOCK else hd // 32
+    slots = 16
+    new_s = [torch.zeros(2 * nkv, dtype=torch.int16, device=dev) for _ in range(slots)]
+    new_c = [torch.zeros((2 * nkv, hd), dtype=torch.int8, device=dev) for _ in range(slots)]
+    qc = [torch.zeros((nh, hd), dtype=torch.int8, device=dev) for _ in range(slots)]
+    qsc = [torch.zeros((nh, nb), dtype=torch.int32, device=dev) for _ in range(slots)]
+    sc = [torch.zeros((nh, npos), dtype=torch.float32, device=dev) for _ in range(slots)]
+    out = [torch.zeros((nh, hd), dtype=torch.float32, device=dev) for _ in range(slots)]
+
+    def append(i, stream=None):
+        qg.qg_kv_cache_rows(2 * nkv, hd, new_rows[i % n_q], new_s[i % slots], new_c[i % slots], stream)
+
+    def quant(i, stream=None):
+        qg.qg_kv_quantize_heads(mode, nh, hd, qs[i % n_q], qc[i % slots], qsc[i % slots], None, stream)
+
+    def scores(i, stream=None):
+        k = caches[i % copies]
+        qg.qg_kv_scores(mode, nh, nkv, npos, hd, qc[i % slots], qsc[i % slots], k[0], k[1], sc[i % slots], stream)
+
+    def weighted(i, stream=None):
+        k = caches[i % copies]
+        qg.qg_kv_weighted(nh, nkv, npos, hd, probs, k[2], k[3], out[i % slots], stream)
+
+    def step(i, stream=None):
+        append(i, stream)
+        quant(i, stream)
+        scores(i, stream)
+        weighted(i, stream)
+
+    # algorithmic bytes: every cached code and scale read once (per KV head), the weights,
+    # the query, the scores written once, the output; the append's rows in and out
+    b_scores = rows * hd + 2 * rows + nh * hd * 4 + nh * npos * 4
+    b_weighted = nh * npos * 4 + rows * hd + 2 * rows + nh * hd * 4
+    b_step = b_scores + b_weighted + 2 * nkv * hd * (4 + 1) + 2 * 2 * nkv + nh * hd * (4 + 1)
+    gsteps = slots
+    s = torch.cuda.Stream()
+
+    def graph_of(fn, nsteps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(nsteps):
+                fn(i)
+        return g
+
+    def replay_ms(graphs):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            torch.cuda.synchronize()
+            t0.record(s)
+            for g in graphs:
+                g.replay()
+            t1.record(s)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
+    def per_call_us(fn, launches):
+        g = graph_of(fn, gsteps)
+        for _ in range(4):
+            g.replay()
+        reps = max(1, launches // gsteps)
+        return replay_ms([g] * reps) * 1e3 / (reps * gsteps)
+
+    torch.cuda.synchronize()
+    step(0)
+    torch.cuda.synchronize()
+    first_sc = sc[0].cpu().numpy().copy()
+    first_out = out[0].cpu().numpy().copy()
+    full = graph_of(step, gsteps)
+    rest = args.steps % gsteps
+    tail = graph_of(step, rest) if rest else None
+    for _ in range(max(1, -(-args.warmup // gsteps))):
+        full.replay()
+    torch.cuda.synchronize()
+    ms_total = replay_ms([full] * (args.steps // gsteps) + ([tail] if tail is not None else []))
+    ms_per_step = ms_total / args.steps
+    us_scores = per_call_us(scores, args.kernel_launches)
+    us_weighted = per_call_us(weighted, args.kernel_launches)
+    us_quant = per_call_us(quant, args.kernel_launches // 4)
+    us_append = per_call_us(append, args.kernel_launches // 4)
+    dom = ("kv_scores_kernel", us_scores, b_scores) if us_scores >= us_weighted else \
+        ("kv_weighted_kernel", us_weighted, b_weighted)
+    achieved = dom[2] / (dom[1] * 1e-6) / 1e9
+    value = b_step / (ms_per_step * 1e-3) / 1e9
+    record = {
+        "metric": KV_METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "query_heads": nh, "kv_heads": nkv, "positions": npos, "head_size": hd,
+            "query_scaling": "perblock" if mode == 0 else "sub32",
+            "cache": "cold, rotating over %d copies (%.0f MB)" % (copies, copies * cache_bytes / 1e6)
+                     if copies > 1 else "warm, one copy (cache-resident)",
+            "step": "qg_kv_cache_rows + qg_kv_quantize_heads + qg_kv_scores + qg_kv_weighted, HIP graph replay",
+        },
+        "algorithmic_bytes_per_step": b_step,
+        "kernels_us": {"kv_scores": round(us_scores, 3), "kv_weighted": round(us_weighted, 3),
+                       "kv_quantize_heads": round(us_quant, 3), "kv_cache_rows": round(us_append, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom[0],
+                     "algorithmic_bytes_per_launch": dom[2]},
+    }
+    if not args.no_cpu:
+        import oracle
+
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count() or 1
+        threads = max(1, min(16, cores))
+        oracle.set_threads(threads)
+        kh, kcc = oracle.kv_cache_rows(keys.reshape(-1, hd))
+        vh, vcc = oracle.kv_cache_rows(vals.reshape(-1, hd))
+        kh, kcc = kh.reshape(nkv, npos), kcc.reshape(nkv, npos, hd)
+        vh, vcc = vh.reshape(nkv, npos), vcc.reshape(nkv, npos, hd)
+        q0 = qs[0].cpu().numpy()
+        t0 = time.perf_counter()
+        steps = 0
+        while True:
+            qn = qs[steps % n_q].cpu().numpy() if steps else q0
+            oracle.kv_cache_rows(new_rows[steps % n_q].cpu().numpy())
+            c, m_, e_ = oracle.kv_quantize_heads(qn, mode)
+            sc_o = oracle.kv_scores(mode, c, m_, e_, kh, kcc)
+            out_o = oracle.kv_weighted(weights, vh, vcc)
+            if steps == 0:
+                parity = bool(np.array_equal(sc_o.view(np.uint32), first_sc.view(np.uint32))
+                              and np.array_equal(out_o.view(np.uint32), first_out.view(np.uint32)))
+            steps += 1
+            dt = time.perf_counter() - t0
+            if dt >= args.cpu_seconds:
+                break
+        record["cpu_baseline"] = {"value": round(steps * b_step / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": f"{steps} whole steps (append, quantize, all scores, weighted sum) of "
+                                            f"the same workload, {dt:.1f} s"}
+        record["parity_step0"] = parity
     print(json.dumps(record), flush=True)
 
 

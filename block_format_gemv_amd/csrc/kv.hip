@@ -177,27 +177,31 @@ __global__ __launch_bounds__(256) void kv_scores_kernel(int nh, int grp, int64_t
 }
 
 // ---------------------------------------------------------------------------------------
-// weighted sum: one workgroup of W waves per head.  A wave covers BPW = 256 / HD blocks of
-// 32 positions at a time, HD / 4 lanes per block, each lane four consecutive value elements.
-// The rounds' pieces go to LDS ([block of the round][HD]) and after the round's barrier the
-// first HD / 64 waves add them in block order, one element per lane.
+// weighted sum: one workgroup of W waves per (head, group of EG value elements).  A wave
+// covers BPW = 256 / EG blocks of 32 positions at a time, EG / 4 lanes per block, each lane
+// four consecutive value elements; a round of W * BPW blocks (a 4096-position context at
+// EG = 16 and W = 8: every block in one round, all its loads in flight together).  The
+// round's pieces go to LDS ([block of the round][EG]) and after the round's barrier the
+// first EG lanes add them in block order, one element per lane.
 
-template <int HD, int W>
+template <int HD, int EG, int W>
 __global__ __launch_bounds__(64 * W) void kv_weighted_kernel(int grp, int64_t npos, const float *__restrict__ probs,
                                                              const uint16_t *__restrict__ vscales,
                                                              const int8_t *__restrict__ vcodes,
                                                              float *__restrict__ out)
 {
-    constexpr int LPB = HD / 4;                // lanes per block
+    static_assert(EG % 4 == 0 && EG <= HD && HD % EG == 0 && EG <= 64, "element groups");
+    constexpr int LPB = EG / 4;                // lanes per block
     constexpr int BPW = 64 / LPB;              // blocks per wave
     constexpr int RB = W * BPW;                // blocks per round
-    __shared__ float s_piece[RB * HD];
+    __shared__ float s_piece[RB * EG];
     const int h = blockIdx.x;
     const int kv = h / grp;
+    const int eg0 = (int)blockIdx.y * EG;      // this workgroup's first value element
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
     const int sub = lane / LPB;                // this lane's block within the wave
-    const int el = 4 * (lane % LPB);           // its first value element
+    const int el = eg0 + 4 * (lane % LPB);     // its first value element
     const int64_t nblk = (npos + kValueBlock - 1) / kValueBlock;
     const float *ph = probs + (size_t)h * npos;
     const uint16_t *vs = vscales + (size_t)kv * npos;
@@ -259,15 +263,15 @@ __global__ __launch_bounds__(64 * W) void kv_weighted_kernel(int grp, int64_t np
                                : r32_exact_double(__builtin_ldexp((double)T[e], E));
         }
 #pragma unroll
-        for (int e = 0; e < 4; e++) s_piece[kb * HD + el + e] = piece[e];
+        for (int e = 0; e < 4; e++) s_piece[kb * EG + (el - eg0) + e] = piece[e];
         __syncthreads();
-        if (threadIdx.x < HD) {
+        if (threadIdx.x < EG) {
             const int64_t nb = nblk - r * RB < RB ? nblk - r * RB : RB;
-            y = fold_ftz(y, s_piece + threadIdx.x, (int)nb, HD);
+            y = fold_ftz(y, s_piece + threadIdx.x, (int)nb, EG);
         }
         __syncthreads();
     }
-    if (threadIdx.x < HD) out[(size_t)h * HD + threadIdx.x] = canon_nan(y);
+    if (threadIdx.x < EG) out[(size_t)h * HD + eg0 + threadIdx.x] = canon_nan(y);
 }
 
 }  // namespace
@@ -326,11 +330,13 @@ void weighted_typed(int nh, int grp, int64_t npos, const float *p, const uint16_
 {
     hipEvent_t ev0, ev1;
     take_timing_events(&ev0, &ev1);
+    constexpr int EG = 16, W = 8;
+    const dim3 grid((unsigned)nh, (unsigned)(HD / EG));
     if (ev0 && ev1)
-        hipExtLaunchKernelGGL((kv_weighted_kernel<HD, 8>), dim3((unsigned)nh), dim3(512), 0, s, ev0, ev1, 0, grp, npos,
-                              p, vs, vc, out);
+        hipExtLaunchKernelGGL((kv_weighted_kernel<HD, EG, W>), grid, dim3(64 * W), 0, s, ev0, ev1, 0, grp, npos, p,
+                              vs, vc, out);
     else
-        hipLaunchKernelGGL((kv_weighted_kernel<HD, 8>), dim3((unsigned)nh), dim3(512), 0, s, grp, npos, p, vs, vc, out);
+        hipLaunchKernelGGL((kv_weighted_kernel<HD, EG, W>), grid, dim3(64 * W), 0, s, grp, npos, p, vs, vc, out);
 }
 }  // namespace
 
