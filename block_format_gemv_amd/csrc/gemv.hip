@@ -42,6 +42,7 @@ constexpr int kNoTinyExp = -78;
 // operand as they are (__mul24 would first mask b to 24 bits with two shifts).  A compiler
 // intrinsic rather than inline assembly, so the instruction takes part in hazard checking.
 extern "C" __device__ int qg_llvm_mul_i24(int, int) __asm("llvm.amdgcn.mul.i24");
+__device__ __forceinline__ int mul_i24(int a, int b) { return qg_llvm_mul_i24(a, b); }
 __device__ __forceinline__ int mad_i24(int a, int b, int c) { return qg_llvm_mul_i24(a, b) + c; }
 
 // ---------------------------------------------------------------------------------------
@@ -341,7 +342,7 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q4K> &T, int b, co
         // with it (exact, as in piece_q4k_perblock_near).
         int Cb = 0, Ob = 0;
 #pragma unroll
-        for (int i = 0; i < 8; i++) Ob += __mul24((int)(f[i] >> 6), act.sum32(b, i));
+        for (int i = 0; i < 8; i++) Ob = mad_i24((int)(f[i] >> 6), act.sum32(b, i), Ob);
         const qg_act_scale s = act.scale(b, 0, 1);
         const float fd = f16_value(T.meta.x), fm = f16_value(T.meta.x >> 16);
         const bool near = __all(q4k_near(fd, fm));
@@ -368,8 +369,8 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q4K> &T, int b, co
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const int P = q4k_sub(T.w[i], b, i, act);
-            Cj[i] = __mul24((int)(f[i] & 63u), P);
-            Oj[i] = __mul24((int)(f[i] >> 6), act.sum32(b, i));
+            Cj[i] = mul_i24((int)(f[i] & 63u), P);
+            Oj[i] = mul_i24((int)(f[i] >> 6), act.sum32(b, i));
             const qg_act_scale s = act.scale(b, i, 8);
             m[i] = s.m;
             e[i] = s.e;
@@ -392,8 +393,9 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q6K> &T, int b, co
         // (q - 32) . a = q . a - 32 * sum(a)
         const int s0 = (int)(int8_t)(sw[(2 * i) >> 2] >> (8 * ((2 * i) & 3)));
         const int s1 = (int)(int8_t)(sw[(2 * i + 1) >> 2] >> (8 * ((2 * i + 1) & 3)));
-        Ck[2 * i] = __mul24(s0, P0 - 32 * act.sum16(b, 2 * i));
-        Ck[2 * i + 1] = __mul24(s1, P1 - 32 * act.sum16(b, 2 * i + 1));
+        // |P - 32 * sum| < 2^18, |s| <= 128
+        Ck[2 * i] = mul_i24(s0, P0 - 32 * act.sum16(b, 2 * i));
+        Ck[2 * i + 1] = mul_i24(s1, P1 - 32 * act.sum16(b, 2 * i + 1));
     }
     if constexpr (MODE == QG_PERBLOCK) {
         int Cb = 0;

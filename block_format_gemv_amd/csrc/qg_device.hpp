@@ -500,6 +500,15 @@ __device__ __forceinline__ bool sum8_pair(const double (&T)[8], int low, float &
 // When the block scales are near (q4k_near), X_j = d*C_j - dmin*O_j is exact in one fma (|C_j|
 // < 2^22, |O_j| < 2^18) and T_j = X_j * m_j 2^e_j too (m_j has 4 significant bits); with the sum
 // window not engaged the eight T_j are summed by sum8_pair.  Otherwise the 128-bit sum.
+//
+// First, when the group's activation exponents span at most 16 places: with F_j = m_j *
+// 2^(e_j - emin) (below 2^20; the activation scales are the same for every row of a tile),
+// IC = sum F_j C_j (< 2^45) and IO = sum F_j O_j (< 2^41) are exact integer sums in f64, and the
+// piece is R32(2^emin * (d*IC - dmin*IO)).  d*IC is split exactly into p1 + e1 (its rounded
+// product and the fma residual), dmin*IO is exact (< 2^52), TwoSum gives p1 - dmin*IO = s + t
+// exactly, and u = t + e1 is exact: both are multiples of the lesser least place of d and
+// dmin, below 2^6 times the greater (the block scales are near, so their exponents differ by
+// at most 12).  Then r32_sum2 rounds 2^emin * (s + u) once.
 __device__ __forceinline__ float piece_q4k_sub32(const int (&C)[8], const int (&O)[8], const int (&m)[8],
                                                  const int (&e)[8], uint32_t d_dmin)
 {
@@ -513,7 +522,27 @@ __device__ __forceinline__ float piece_q4k_sub32(const int (&C)[8], const int (&
     }
     const int dlo = d.ex < dm.ex ? d.ex : dm.ex, dhi = d.ex < dm.ex ? dm.ex : d.ex;
     const float fd = f16_value(d_dmin), fm = f16_value(d_dmin >> 16);
-    if (q4k_near(fd, fm) && (emax - emin) + (dhi - dlo) <= kSumWindow) {
+    const bool near = q4k_near(fd, fm) && (emax - emin) + (dhi - dlo) <= kSumWindow;
+    if (near && emax - emin <= 16) {
+        double IC = 0.0, IO = 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const double F = __builtin_ldexp((double)m[j], e[j] - emin);
+            IC = __builtin_fma(F, (double)C[j], IC);
+            IO = __builtin_fma(F, (double)O[j], IO);
+        }
+        const double Dd = (double)fd;
+        const double p1 = IC * Dd;
+        const double e1 = __builtin_fma(IC, Dd, -p1);
+        const double p2 = -(IO * (double)fm);
+        const double s = p1 + p2;
+        const double bv = s - p1;
+        const double av = s - bv;
+        const double t = (p1 - av) + (p2 - bv);
+        const double u = t + e1;
+        return r32_sum2(__builtin_ldexp(s, emin), __builtin_ldexp(u, emin));
+    }
+    if (near) {
         double T[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {

@@ -483,6 +483,29 @@ def test_subnormal_partial_sums_gemv_and_gemm(qg):
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 0)
 
 
+@pytest.mark.parametrize("span", [15, 16, 17, 20])
+def test_sub32_exponent_spans(qg, span):
+    """Sub32 groups whose activation exponents span 15 to 20 places (the factored exact sum
+    takes up to 16, wider groups take the pairwise one): the quantized-row GEMV and the
+    one-launch step give the oracle's bits, on near and far block-scale pairs."""
+    rows, cols = 200, 4096
+    f = _adversarial_fields("q4k", rows, cols, 300 + span)
+    M = Mat(qg, f)
+    x, t = gen.act_sub32(2, cols, 310 + span, e_lo=-12, e_hi=-12 + span)
+    g8 = t.reshape(2, -1, 8)
+    assert (g8.max(axis=2) - g8.min(axis=2)).max() == span
+    say("sub32 exponent span", span)
+    for k in range(2):
+        c, m, e, _ = oracle.quantize(x[k:k + 1], 1)
+        assert np.array_equal(e.reshape(-1), t[k])
+        want = oracle.gemv(f, c, m, e, 1)
+        act, gc, gm, ge, _ = gpu_quant(qg, x[k:k + 1], 1)
+        assert np.array_equal(gc, c) and np.array_equal(ge, e)
+        assert first_mismatch(run_gemv(qg, M, act), want) is None, (span, k)
+        out, *_ = _fused(qg, M, x[k:k + 1], 1)
+        assert first_mismatch(out, want) is None, (span, k)
+
+
 @pytest.mark.parametrize("cols", [4096, 8192])
 def test_subnormal_partial_sums_wide_rows(qg, cols):
     """The same cancelling rows at 16 blocks (one wave per block) and 32 blocks (two tiles
