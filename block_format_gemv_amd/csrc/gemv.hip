@@ -826,12 +826,12 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
     // the last block works on a copy of it and stores nothing), kept in this order
     const int bf = min(wid, G - 1);
     ActRaw<SRC> r0 = load_act<SRC, GL>(io, bf, lane);
-    // Every wave's activation load is issued before any wave's tile loads (a barrier that
-    // waits for no memory): a compute unit hands back vector loads in issue order, so an
-    // activation load queued behind other waves' tiles would arrive with them, and that
-    // wave's activation work would land at the end of the weight stream.
+    // Quantizing in the wave: every wave's activation load is issued before any wave's tile
+    // loads (a barrier that waits for no memory), so the quantizing work starts ahead of the
+    // weight stream (measured: 0.2 us of a 7.2 us launch; without quantizing it costs more
+    // than it gains).
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
+    if constexpr (SRC == SRC_F32) __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     T t0;
     [[maybe_unused]] T t1;
