@@ -119,6 +119,9 @@ def parse():
     p.add_argument("--kernel-launches", type=int, default=1600)
     p.add_argument("--two-launch", action="store_true",
                    help="time the step as qg_quantize_act + qg_gemv_q instead of qg_quantize_gemv")
+    p.add_argument("--tune", action="append", default=[], metavar="KEY=VALUE",
+                   help="a speed-only tuning knob (qg_set_tuning): waves_per_wg, mfma_min_cols, mfma_col_tiles, "
+                        "mfma_form, mfma_ring_waves, cols_kernel; output bits do not depend on them")
     p.add_argument("--copy-probe", type=float, default=0,
                    help="only run 20 device-to-device copies of this many bytes (counter calibration) and exit")
     return p.parse_args()
@@ -236,6 +239,11 @@ def main():
     import block_format_gemv_amd as qg
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    tuned = {}
+    for kv in args.tune:
+        key, _, val = kv.partition("=")
+        qg.qg_set_tuning(getattr(qg, "TUNE_" + key.upper()), int(val))
+        tuned[key] = int(val)
     wl = WORKLOADS[args.workload]
     if wl[0] == "kv":
         kv_main(args, wl, torch, qg, Hip())
@@ -304,11 +312,13 @@ def main():
     elif ncol == 1:
         kernel_label = ("gemv1_kernel<..., SRC_F32> (one-launch quantize + GEMV)" if fused
                         else "gemv1_kernel<..., SRC_CODES> (GEMV of a quantized row)")
-    elif fmt_s == "q4k" and mode == 0 and ncol >= 8:
+    elif fmt_s == "q4k" and mode == 0 and ncol >= (tuned.get("mfma_min_cols") or 9):
         kernel_label = "gemm_mfma_q4k (matrix cores, shared operands)" if ncol >= 48 else \
             "gemm_ring_q4k (matrix cores, LDS-DMA ring)"
+    elif cols <= 16 * 256 and not tuned.get("cols_kernel") and fmt_s in ("q4k", "q6k"):
+        kernel_label = "gemv1_cols_kernel (one-column machinery, up to 8 columns a wave)"
     else:
-        kernel_label = "gemv_kernel (several columns)"
+        kernel_label = "gemv_kernel (several columns staged in LDS)"
     step = fused_call if fused else two_launch
     # the step's dominant kernel: the fused kernel (reads x, writes the quantized row once)
     # or the GEMV/GEMM kernel (reads the quantized row)
@@ -438,6 +448,7 @@ def main():
             "columns": ncol,
             "weights": "cold, rotating over %d copies (%.0f MB)" % (copies, copies * image_bytes / 1e6)
                        if copies > 1 else "warm, one copy (cache-resident)",
+            **({"tuning": tuned} if tuned else {}),
             "step": (("qg_quantize_gemv_multi" if nmat > 1 else "qg_quantize_gemv") + " (one launch)" if fused
                      else "qg_quantize_act + " + ("qg_gemv_q_multi" if nmat > 1 else "qg_gemm_q"))
                     + ", HIP graph replay",

@@ -149,6 +149,10 @@ int qg_set_tuning(int key, int64_t value)
             return fail(QG_E_INVALID, "qg_set_tuning: ring waves per row quarter must be 0, 1, 2 or 4");
         g_tuning.mfma_ring_waves = (int)value;
         return QG_OK;
+    case QG_TUNE_COLS_KERNEL:
+        if (value > 1) return fail(QG_E_INVALID, "qg_set_tuning: the several-column kernel choice must be 0 or 1");
+        g_tuning.cols_off = (int)value;
+        return QG_OK;
     default:
         return fail(QG_E_INVALID, "qg_set_tuning: unknown key %d", key);
     }
@@ -192,7 +196,7 @@ static int gemm_common(const char *who, int fmt, int mode, int64_t rows, int64_t
     if ((st = check_ptr(who, "image", image, 16))) return st;
     if ((st = check_act(who, codes, scales, csums))) return st;
     if ((st = check_ptr(who, "out", out, 4))) return st;
-    const int min_cols = g_tuning.mfma_min_cols > 0 ? g_tuning.mfma_min_cols : 8;
+    const int min_cols = g_tuning.mfma_min_cols > 0 ? g_tuning.mfma_min_cols : 9;
     if (fmt == QG_Q4K && mode == QG_PERBLOCK && n >= min_cols)
         return launch_gemm_mfma(rows, cols, n, image, codes, scales, out, static_cast<hipStream_t>(stream));
     return launch_gemv(fmt, mode, rows, cols, n, image, codes, scales, csums, out, static_cast<hipStream_t>(stream));

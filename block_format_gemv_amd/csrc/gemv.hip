@@ -903,6 +903,73 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
     }
 }
 
+// Several activation columns on the one-column machinery (a quantized activation matrix, at
+// most 16 blocks per row): each wave keeps its tile in registers and forms its block's piece
+// for NC columns in turn, each column's codes read out into scalar registers as in the
+// one-column kernel; the columns' activation loads are issued ahead of the tile.  Column c0 +
+// c of the launch is blockIdx.y * NC + c; columns past ncol are worked on as copies of the
+// last and dropped.  The first wave adds each row's pieces in block order per column.
+struct ActCols {
+    const int8_t *codes;          // column c's codes at codes + c * cstride
+    const uint32_t *scales;       // its qg_act_scale words at scales + c * sstride
+    int64_t cstride, sstride;
+};
+
+template <int FMT, int MODE, int NC>
+__global__ __launch_bounds__(64 * 16) void gemv1_cols_kernel(const uint8_t *image, int rows, int G, ActCols ac,
+                                                            int ncol, float *__restrict__ out)
+{
+    constexpr int W = 16;
+    extern __shared__ __align__(16) float s_piece[];   // [NC][W][64] pieces, then W flag bytes
+    unsigned char *s_small = reinterpret_cast<unsigned char *>(s_piece + (size_t)NC * W * 64);
+    using T = TileRegs<FMT>;
+    constexpr int BITS = ActKind<FMT, MODE>::kBits, GL = ActKind<FMT, MODE>::kLanes;
+    const int g = (int)blockIdx.x;
+    const int c0 = (int)blockIdx.y * NC;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int bf = min(wid, G - 1);
+    const uint8_t *gbase = image + (size_t)g * G * T::kBytes;
+    const ActIO none{};
+
+    ActRaw<SRC_CODES> r[NC];
+#pragma unroll
+    for (int c = 0; c < NC; c++) {
+        const int64_t cc = min(c0 + c, ncol - 1);
+        ActIO io{};
+        io.codes_in = ac.codes + cc * ac.cstride;
+        io.scales_in = ac.scales + cc * ac.sstride;
+        r[c] = load_act<SRC_CODES, GL>(io, bf, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    T t0;
+    t0.load(gbase + (size_t)bf * T::kBytes, lane);
+    load_fence();
+    bool small = false;
+#pragma unroll
+    for (int c = 0; c < NC; c++) {
+        __builtin_amdgcn_sched_barrier(0);
+        const ActWave a = ready_act<SRC_CODES, BITS, GL>(r[c], bf, G, lane, false, none);
+        const float p = piece_one<FMT, MODE>(t0, bf, a);
+        s_piece[((size_t)c * W + wid) * 64 + lane] = wid < G ? p : 0.0f;
+        small |= __ballot(a.e < kNoTinyExp) != 0;
+    }
+    if (lane == 0) s_small[wid] = small ? 1 : 0;
+    __syncthreads();
+
+    if (wid == 0) {
+        const int64_t row = (int64_t)g * 64 + lane;
+        const bool flushed = any_flag<W>(s_small);
+#pragma unroll
+        for (int c = 0; c < NC; c++) {
+            if (c0 + c >= ncol) break;
+            const float *pc = s_piece + (size_t)c * W * 64 + lane;
+            const float y = flushed ? fold_flushed(0.0f, pc, G, 64) : fold_fixed<W>(pc, 64);
+            if (row < rows) out[(int64_t)(c0 + c) * rows + row] = canon_nan(y);
+        }
+    }
+}
+
 // One activation column over a 32-element-block format.  A row has up to eight pieces per
 // tile (PerBlock), too many to park all of a long row's in LDS, so the workgroup goes through
 // its blocks in rounds of W (wave w takes block rW + w of round r): each round's pieces go to
@@ -1281,12 +1348,54 @@ int launch_gemv_multi(int fmt, int mode, int nmat, const int64_t *rows, int64_t 
     return launch_one_any<SRC_CODES>(fmt, mode, tg, G, io, s);
 }
 
+template <int FMT, int MODE, int NC>
+int launch_cols_typed(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
+                      const qg_act_scale *scales, float *out, hipStream_t s)
+{
+    const int64_t groups = (rows + 63) / 64;
+    const int64_t batches = (ncol + NC - 1) / NC;
+    const int64_t nsc = act_block(FMT, MODE) == 256 ? G : (int64_t)G * 8;
+    const ActCols ac{codes, reinterpret_cast<const uint32_t *>(scales), (int64_t)G * 256, nsc};
+    const size_t lds = (size_t)NC * 16 * 64 * sizeof(float) + 16;
+    const dim3 grid((unsigned)groups, (unsigned)batches);
+    hipEvent_t ev0, ev1;
+    take_timing_events(&ev0, &ev1);
+    if (ev0 && ev1)
+        hipExtLaunchKernelGGL((gemv1_cols_kernel<FMT, MODE, NC>), grid, dim3(1024), lds, s, ev0, ev1, 0,
+                              static_cast<const uint8_t *>(image), (int)rows, G, ac, (int)ncol, out);
+    else
+        hipLaunchKernelGGL((gemv1_cols_kernel<FMT, MODE, NC>), grid, dim3(1024), lds, s,
+                           static_cast<const uint8_t *>(image), (int)rows, G, ac, (int)ncol, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemv launch: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+template <int FMT, int MODE>
+int launch_cols(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
+                const qg_act_scale *scales, float *out, hipStream_t s)
+{
+    if (ncol <= 2) return launch_cols_typed<FMT, MODE, 2>(rows, G, ncol, image, codes, scales, out, s);
+    if (ncol <= 4) return launch_cols_typed<FMT, MODE, 4>(rows, G, ncol, image, codes, scales, out, s);
+    return launch_cols_typed<FMT, MODE, 8>(rows, G, ncol, image, codes, scales, out, s);
+}
+
 int launch_gemv(int fmt, int mode, int64_t rows, int64_t cols, int64_t ncol, const void *image,
                 const int8_t *codes, const qg_act_scale *scales, const int32_t *csums, float *out,
                 hipStream_t s)
 {
     if (rows == 0 || ncol == 0) return QG_OK;
     const int G = (int)(cols / 256);
+    if (ncol > 1 && !is_b32(fmt) && G <= 16 && tuning().cols_off == 0) {
+        // several columns, at most 16 blocks per row: the one-column machinery, NC columns a wave
+        if (fmt == QG_Q4K && mode == QG_PERBLOCK)
+            return launch_cols<QG_Q4K, QG_PERBLOCK>(rows, G, ncol, image, codes, scales, out, s);
+        if (fmt == QG_Q4K && mode == QG_SUB32)
+            return launch_cols<QG_Q4K, QG_SUB32>(rows, G, ncol, image, codes, scales, out, s);
+        if (fmt == QG_Q6K && mode == QG_PERBLOCK)
+            return launch_cols<QG_Q6K, QG_PERBLOCK>(rows, G, ncol, image, codes, scales, out, s);
+        return launch_cols<QG_Q6K, QG_SUB32>(rows, G, ncol, image, codes, scales, out, s);
+    }
     if (ncol == 1 || is_b32(fmt)) {
         // one launch per column (the 32-element-block formats have no several-column kernel)
         const int64_t nsc = act_block(fmt, mode) == 256 ? G : (int64_t)G * 8;

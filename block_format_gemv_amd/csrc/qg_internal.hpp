@@ -29,6 +29,7 @@ struct Tuning {
     int mfma_col_tiles;   // matrix-core GEMM: 1, 2 or 4 column tiles per workgroup; 0 = derived
     int mfma_form;        // matrix-core GEMM: 1 ring, 2 shared operands, 3 per wave; 0 = derived
     int mfma_ring_waves;  // ring form: waves per 16-row quarter (1, 2 or 4); 0 = derived
+    int cols_off;         // 1: several columns take the LDS-staged kernel, not the one-column machinery
 };
 const Tuning &tuning();
 

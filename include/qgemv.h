@@ -316,7 +316,7 @@ int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink
  *                         4, 8 or 16 (0 = one wave per block, at most 16).  16 applies
  *                         only to a single column of at most 16 blocks; otherwise 8 is used
  *   QG_TUNE_MFMA_MIN_COLS number of columns from which qg_gemm_q on a Q4_K PerBlock matrix
- *                         runs on the int8 matrix cores, columns padded to 16 (0 = 8;
+ *                         runs on the int8 matrix cores, columns padded to 16 (0 = 9;
  *                         above 65535 = never)
  *   QG_TUNE_MFMA_FORM     the matrix-core GEMM's form: 1 = LDS ring (tiles and activation operands
  *                         staged by LDS-DMA loads several blocks ahead), 2 = shared operands
@@ -327,13 +327,17 @@ int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink
  *                         forms (the per-wave form takes 1 or 2); 0 = derived from the columns
  *   QG_TUNE_MFMA_RING_WAVES 1, 2 or 4 waves per 16-row quarter in the ring form, each taking an
  *                         equal share of the column tiles (a value that does not divide them
- *                         is taken as 1); 0 = derived */
+ *                         is taken as 1); 0 = derived
+ *   QG_TUNE_COLS_KERNEL   several columns below the matrix-core threshold (Q4_K/Q6_K, at most 16
+ *                         blocks per row): 0 = the one-column kernel's machinery, NC columns per
+ *                         wave (default); 1 = the kernel that stages the columns in LDS */
 enum {
     QG_TUNE_WAVES_PER_WG = 1,
     QG_TUNE_MFMA_MIN_COLS = 2,
     QG_TUNE_MFMA_COL_TILES = 3,
     QG_TUNE_MFMA_FORM = 4,
-    QG_TUNE_MFMA_RING_WAVES = 5
+    QG_TUNE_MFMA_RING_WAVES = 5,
+    QG_TUNE_COLS_KERNEL = 6
 };
 int qg_set_tuning(int key, int64_t value);
 

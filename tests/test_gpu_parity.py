@@ -33,6 +33,7 @@ def qg():
     q.qg_set_tuning(q.TUNE_WAVES_PER_WG, 0)
     q.qg_set_tuning(q.TUNE_MFMA_MIN_COLS, 0)
     q.qg_set_tuning(q.TUNE_MFMA_COL_TILES, 0)
+    q.qg_set_tuning(q.TUNE_COLS_KERNEL, 0)
     oracle.set_threads(8)
     return q
 
@@ -392,6 +393,33 @@ def test_batched_columns(qg, llama, n):
             one.scales.copy_(act.scales[k:k + 1])
             one.csums.copy_(act.csums[k:k + 1])
             assert np.array_equal(bits(run_gemv(qg, M, one)), bits(out[k]))
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_several_columns_one_column_machinery(qg, fmt, mode):
+    """Several activation columns below the matrix-core threshold (2 to 13 columns, batches of
+    2, 4 and 8 per workgroup, ragged rows, 1 to 16 blocks per row): the oracle's bits, and the
+    same bits as the kernel that stages the columns in LDS."""
+    try:
+        qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 65536)
+        for rows, cols, n in ((70, 4096, 2), (130, 3072, 3), (64, 1024, 4), (9, 256, 5), (200, 4096, 8),
+                              (65, 2048, 9), (33, 4096, 13)):
+            say("several columns", fmt, "mode", mode, "shape", rows, cols, "n", n)
+            f = _adversarial_fields(fmt, rows, cols, rows + 7 * cols + n)
+            M = Mat(qg, f)
+            xs = gen.act_outliers(n, cols, rows + n) if mode == 0 else gen.act_sub32(n, cols, rows + n)[0]
+            act, c, m, e, _ = gpu_quant(qg, xs, mode)
+            qg.qg_set_tuning(qg.TUNE_COLS_KERNEL, 0)
+            out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+            want = oracle.gemm(f, c, m, e, mode).reshape(n, rows)
+            assert first_mismatch(out, want) is None, (rows, cols, n, first_mismatch(out, want))
+            qg.qg_set_tuning(qg.TUNE_COLS_KERNEL, 1)
+            staged = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+            assert np.array_equal(bits(staged), bits(out)), (rows, cols, n)
+    finally:
+        qg.qg_set_tuning(qg.TUNE_COLS_KERNEL, 0)
+        qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 0)
 
 
 # --- batched columns on the int8 matrix cores -----------------------------------------------
