@@ -300,11 +300,15 @@ struct TileRegs<QG_Q8_0> {
     static constexpr int kBytes = kTileBytesQ8_0;
     uint4 w[16];    // int8 codes of elements 16i .. 16i+15
     uint4 d;        // binary16 bits of the eight blocks' scales
+    // the scales first, then the code chunks in the order they are used (as the Q4_K tile)
     __device__ __forceinline__ void load(const uint8_t *tile, int lane)
     {
-#pragma unroll
-        for (int i = 0; i < 16; i++) w[i] = ld_stream(tile + 1024 * i + 16 * lane);
         d = ld_stream(tile + 16384 + 16 * lane);
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            __builtin_amdgcn_sched_barrier(0);
+            w[i] = ld_stream(tile + 1024 * i + 16 * lane);
+        }
     }
 };
 
@@ -315,9 +319,12 @@ struct TileRegs<QG_Q4_0> {
     uint4 d;        // binary16 bits of the eight blocks' scales
     __device__ __forceinline__ void load(const uint8_t *tile, int lane)
     {
-#pragma unroll
-        for (int i = 0; i < 8; i++) w[i] = ld_stream(tile + 1024 * i + 16 * lane);
         d = ld_stream(tile + 8192 + 16 * lane);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            __builtin_amdgcn_sched_barrier(0);
+            w[i] = ld_stream(tile + 1024 * i + 16 * lane);
+        }
     }
 };
 
@@ -419,31 +426,27 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q6K> &T, int b, co
     }
 }
 
-// The eight integer block sums C_j of a 32-element-block tile (w = d*q for Q8_0, d*(q - 8)
-// for Q4_0) against the activation block's codes.  |C_j| <= 32 * 128 * 127 < 2^19.
-__device__ __forceinline__ void b32_sums(const TileRegs<QG_Q8_0> &T, const ActWaveCodes &act, int (&C)[8])
+// The integer block sum C_j of block j of a 32-element-block tile (w = d*q for Q8_0,
+// d*(q - 8) for Q4_0) against the activation block's codes.  |C_j| <= 32 * 128 * 127 < 2^19.
+__device__ __forceinline__ int b32_sum(const TileRegs<QG_Q8_0> &T, const ActWaveCodes &act, int j)
 {
+    int P = 0;
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        int P = 0;
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const uint4 w = T.w[2 * j + h];
-            const int c = 8 * j + 4 * h;
-            P = sdot4(w.x, act.c[c], P);
-            P = sdot4(w.y, act.c[c + 1], P);
-            P = sdot4(w.z, act.c[c + 2], P);
-            P = sdot4(w.w, act.c[c + 3], P);
-        }
-        C[j] = P;
+    for (int h = 0; h < 2; h++) {
+        const uint4 w = T.w[2 * j + h];
+        const int c = 8 * j + 4 * h;
+        P = sdot4(w.x, act.c[c], P);
+        P = sdot4(w.y, act.c[c + 1], P);
+        P = sdot4(w.z, act.c[c + 2], P);
+        P = sdot4(w.w, act.c[c + 3], P);
     }
+    return P;
 }
 
-__device__ __forceinline__ void b32_sums(const TileRegs<QG_Q4_0> &T, const ActPlanes &act, int (&C)[8])
+// (q - 8) . a = q . a - 8 * sum(a)
+__device__ __forceinline__ int b32_sum(const TileRegs<QG_Q4_0> &T, const ActPlanes &act, int j)
 {
-    // (q - 8) . a = q . a - 8 * sum(a)
-#pragma unroll
-    for (int j = 0; j < 8; j++) C[j] = q4k_sub(T.w[j], 0, j, act) - 8 * act.sum32(0, j);
+    return q4k_sub(T.w[j], 0, j, act) - 8 * act.sum32(0, j);
 }
 
 // The pieces of one tile row: PerBlock, one per 32-element block, R32(m_j*2^e_j * d_j * C_j)
@@ -454,17 +457,23 @@ __device__ __forceinline__ void b32_pieces(const TileRegs<FMT> &T, const Act &ac
                                            float (&p)[MODE == QG_PERBLOCK ? 8 : 1])
 {
     int C[8];
-    b32_sums(T, act, C);
     const uint32_t dw[4] = {T.d.x, T.d.y, T.d.z, T.d.w};
     if constexpr (MODE == QG_PERBLOCK) {
+        // block by block in load order, each waiting for its own code chunks; with the block's
+        // activation exponent >= kNoTinyExp the piece cannot be tiny (no flush, +0 for -0)
 #pragma unroll
         for (int j = 0; j < 8; j++) {
+            __builtin_amdgcn_sched_barrier(0);
+            C[j] = b32_sum(T, act, j);
             const qg_act_scale s = act.scale(0, j, 8);
             const double S = __builtin_ldexp((double)s.m, s.e);
             const double D = (double)f16_value(dw[j >> 1] >> (16 * (j & 1)));
-            p[j] = r32_exact_double((double)C[j] * D * S);
+            const double X = (double)C[j] * D * S;
+            p[j] = s.e >= kNoTinyExp ? (float)X + 0.0f : r32_exact_double(X);
         }
     } else {
+#pragma unroll
+        for (int j = 0; j < 8; j++) C[j] = b32_sum(T, act, j);
         long long Cl[8];
         uint32_t db[8];
         int m[8], e[8];
@@ -976,8 +985,9 @@ __global__ __launch_bounds__(64 * 16) void gemv1_cols_kernel(const uint8_t *imag
 // one of two LDS slots, and after the round's barrier the first wave adds them to its rows'
 // running sums, in block order, while the others start the next round.  The next barrier
 // falls after that fold, so a slot is written again only once it has been read.  Without DB
-// there is one round (G <= W) and one slot.  Beside its pieces each wave parks, per row,
-// whether one of them is tiny (tiny_piece); a round without one is added with plain adds.
+// there is one round (G <= W) and one slot.  Beside its pieces each wave parks a flag byte:
+// whether an activation exponent of its tile allows a tiny piece (kNoTinyExp); a round
+// without one is added with plain adds.
 template <int FMT, int MODE, int SRC, int W, bool DB>
 __global__ __launch_bounds__(64 * W) void gemv1_b32_kernel(const Targets tg, int G, ActIO io)
 {
@@ -1005,22 +1015,17 @@ __global__ __launch_bounds__(64 * W) void gemv1_b32_kernel(const Targets tg, int
             b32_pieces<MODE>(t, act, p);
         }
         float *slot = s_ring + (DB ? (r & 1) * SLOT : 0);
-        int *tiny = reinterpret_cast<int *>(slot + W * PPT * 64);
+        unsigned char *small = reinterpret_cast<unsigned char *>(slot + W * PPT * 64);
+        const bool sm = __ballot(a.e < kNoTinyExp) != 0;   // a block of the tile may give a tiny piece
         if (b < G) {
-            bool t = false;
 #pragma unroll
-            for (int j = 0; j < PPT; j++) {
-                slot[(wid * PPT + j) * 64 + lane] = p[j];
-                t |= tiny_piece(p[j]);
-            }
-            tiny[wid * 64 + lane] = t;
+            for (int j = 0; j < PPT; j++) slot[(wid * PPT + j) * 64 + lane] = p[j];
         }
+        if (lane == 0) small[wid] = b < G && sm ? 1 : 0;
         __syncthreads();
         if (wid == 0) {
             const int nb = min(W, G - r * W);
-            int t = 0;
-            for (int w = 0; w < nb; w++) t |= tiny[w * 64 + lane];
-            y = fold_flagged(y, slot + lane, nb * PPT, 64, t != 0);
+            y = fold_flagged(y, slot + lane, nb * PPT, 64, any_flag<W>(small));
         }
     };
 
