@@ -215,29 +215,57 @@ __global__ __launch_bounds__(64 * W) void kv_weighted_kernel(int grp, int64_t np
         if (blk < nblk) {
             const int64_t j0 = blk * kValueBlock;
             const int nj = (int)(npos - j0 < kValueBlock ? npos - j0 : kValueBlock);
-            // every lane of the block computes the block's codes (32 positions, one per step)
-            int u[kValueBlock];
+            // the block's codes, each of its LPB lanes coding PPL = 32 / LPB consecutive positions:
+            // absmax and the flags reduced over the block's lanes, the packed codes (four
+            // positions a dword) handed to every lane of the block
+            constexpr int PPL = kValueBlock / LPB;
+            const int q = lane % LPB;
             uint32_t amax = 0;
-            bool bad = false;
-            float w[kValueBlock];
+            int bad = 0;
+            float w[PPL];
 #pragma unroll
-            for (int j = 0; j < kValueBlock; j++) {
-                w[j] = 0.0f;
+            for (int i = 0; i < PPL; i++) {
+                const int j = q * PPL + i;
+                w[i] = 0.0f;
                 if (j < nj) {
                     const uint32_t sb = vs[j0 + j];
                     bad |= ((sb >> 10) & 31u) == 31u;
-                    w[j] = ph[j0 + j] * half_bits_value(sb);            // binary32 product
-                    const uint32_t a = __float_as_uint(ftz(w[j])) & 0x7FFFFFFFu;
+                    w[i] = ph[j0 + j] * half_bits_value(sb);            // binary32 product
+                    const uint32_t a = __float_as_uint(ftz(w[i])) & 0x7FFFFFFFu;
                     if (a <= 0x7F800000u && a > amax) amax = a;
                 }
             }
-            bad |= amax == 0x7F800000u;
+            static_assert(LPB == 4, "the block's lanes are one quad");
+            amax = max(amax, (uint32_t)dpp<kDppQuadSwap1>((int)amax));
+            amax = max(amax, (uint32_t)dpp<kDppQuadSwap2>((int)amax));
+            bad |= dpp<kDppQuadSwap1>(bad);
+            bad |= dpp<kDppQuadSwap2>(bad);
+            const bool badb = bad != 0 || amax == 0x7F800000u;
             int E = 0, m1 = 1;
-            if (!bad && amax != 0) least_scale<1>(__uint_as_float(amax), m1, E);
+            if (!badb && amax != 0) least_scale<1>(__uint_as_float(amax), m1, E);
+            uint32_t mine[PPL / 4];
 #pragma unroll
-            for (int j = 0; j < kValueBlock; j++) {
-                const float f = ftz(w[j]);
-                u[j] = (bad || f != f) ? 0 : (int)__builtin_rint(__builtin_ldexp((double)f, -E));
+            for (int k = 0; k < PPL / 4; k++) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    const float f = ftz(w[4 * k + t]);
+                    const int u = (badb || f != f) ? 0 : (int)__builtin_rint(__builtin_ldexp((double)f, -E));
+                    word |= ((uint32_t)u & 255u) << (8 * t);
+                }
+                mine[k] = word;
+            }
+            // dword d (positions 4d .. 4d+3) is held by the block's lane d / (PPL / 4)
+            uint32_t codes4[kValueBlock / 4];
+#pragma unroll
+            for (int d = 0; d < kValueBlock / 4; d++) {
+                constexpr int K = PPL / 4;
+                const int src = d / K;
+                const int ctrl = src | (src << 2) | (src << 4) | (src << 6);   // quad_perm [src x4]
+                const uint32_t v = mine[d % K];
+                codes4[d] = (uint32_t)(ctrl == 0x00 ? dpp<0x00>((int)v)
+                                     : ctrl == 0x55 ? dpp<0x55>((int)v)
+                                     : ctrl == 0xAA ? dpp<0xAA>((int)v) : dpp<0xFF>((int)v));
             }
             // value element sums: rows j..j+3 of the lane's four elements, transposed to per
             // element dwords of four positions, against four codes at a time
@@ -248,8 +276,7 @@ __global__ __launch_bounds__(64 * W) void kv_weighted_kernel(int grp, int64_t np
 #pragma unroll
                 for (int t = 0; t < 4; t++)
                     r4[t] = j + t < nj ? *reinterpret_cast<const uint32_t *>(vc + (size_t)(j0 + j + t) * HD + el) : 0u;
-                const uint32_t uu = (uint32_t)(u[j] & 255) | ((uint32_t)(u[j + 1] & 255) << 8) |
-                                    ((uint32_t)(u[j + 2] & 255) << 16) | ((uint32_t)(u[j + 3] & 255) << 24);
+                const uint32_t uu = codes4[j / 4];
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const uint32_t col = ((r4[0] >> (8 * e)) & 255u) | (((r4[1] >> (8 * e)) & 255u) << 8) |
@@ -259,7 +286,7 @@ __global__ __launch_bounds__(64 * W) void kv_weighted_kernel(int grp, int64_t np
             }
 #pragma unroll
             for (int e = 0; e < 4; e++)
-                piece[e] = bad ? __uint_as_float(0x7FC00000u)
+                piece[e] = badb ? __uint_as_float(0x7FC00000u)
                                : r32_exact_double(__builtin_ldexp((double)T[e], E));
         }
 #pragma unroll
