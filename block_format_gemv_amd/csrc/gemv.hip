@@ -31,12 +31,6 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c)
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
-// A piece is R32 of an exact value X that is an integer multiple of 2^(e + eps): e an
-// activation scale exponent of its block and eps >= -24 the exponent of the least place of a
-// binary16 block scale.  With every such e >= -78 a nonzero X is at least 2^-102, and so is
-// its rounding: no piece of the block is tiny (tiny_piece), whatever the weights.
-constexpr int kNoTinyExp = -78;
-
 // a * b + c with a and b taken as signed 24-bit integers (exact when |a|, |b| < 2^23 and the
 // result fits 32 bits): the target's 24-bit multiply, which reads the low 24 bits of each
 // operand as they are (__mul24 would first mask b to 24 bits with two shifts).  A compiler
@@ -282,14 +276,21 @@ struct TileRegs<QG_Q6K> {
     uint4 H[4];     // high 2 bits
     uint4 sc;       // sixteen int8 sub-block scales
     uint32_t d;     // binary16 bits of the block scale
+    // the scales first, then each pair of sub-blocks' low and high bits in the order they are
+    // used (L0 H0 L1 L2 H1 L3 ...), each kept in place so a pair waits for its own chunks only
     __device__ __forceinline__ void load(const uint8_t *tile, int lane)
     {
-#pragma unroll
-        for (int i = 0; i < 8; i++) L[i] = ld_stream(tile + 1024 * i + 16 * lane);
-#pragma unroll
-        for (int h = 0; h < 4; h++) H[h] = ld_stream(tile + 8192 + 1024 * h + 16 * lane);
-        sc = ld_stream(tile + 12288 + 16 * lane);
         d = *reinterpret_cast<const uint16_t *>(tile + 13312 + 2 * lane);
+        sc = ld_stream(tile + 12288 + 16 * lane);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            __builtin_amdgcn_sched_barrier(0);
+            L[i] = ld_stream(tile + 1024 * i + 16 * lane);
+            if ((i & 1) == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                H[i >> 1] = ld_stream(tile + 8192 + 1024 * (i >> 1) + 16 * lane);
+            }
+        }
     }
 };
 
@@ -391,8 +392,10 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q6K> &T, int b, co
 {
     const uint32_t sw[4] = {T.sc.x, T.sc.y, T.sc.z, T.sc.w};
     int Ck[16];
+    // sub-block pairs in load order, each waiting for its own chunks
 #pragma unroll
     for (int i = 0; i < 8; i++) {
+        __builtin_amdgcn_sched_barrier(0);
         int P0, P1;
         const uint4 a0 = act.codes16(b, 2 * i), a1 = act.codes16(b, 2 * i + 1);
         if (i & 1) q6k_sub_dots<1>(T.L[i], T.H[i >> 1], a0, a1, P0, P1);

@@ -124,6 +124,12 @@ __device__ __forceinline__ float fold_ftz(float acc, const float *p, int n, int 
     return lo <= -126 ? fold_flushed(acc, p, n, stride) : y;
 }
 
+// A piece is R32 of an exact value X that is an integer multiple of 2^(e + eps): e an
+// activation scale exponent of its block and eps >= -24 the exponent of the least place of a
+// binary16 block scale.  With every such e >= -78 a nonzero X is at least 2^-102, and so is
+// its rounding: no piece of the block is tiny (tiny_piece), whatever the weights.
+constexpr int kNoTinyExp = -78;
+
 // Whether a piece may let a partial sum of the row become subnormal: nonzero and below 2^-102
 // in magnitude.  A nonzero piece of at least 2^-102 has an ulp of at least 2^-125; when every
 // nonzero piece of a row is one, every partial sum is a multiple of the least such ulp (an add
@@ -470,7 +476,11 @@ __device__ __forceinline__ bool q4k_near(float fd, float fm)
 __device__ __forceinline__ float piece_q6k_perblock(int C, uint32_t dbits, int m, int e)
 {
     const F16Scale d = f16_scale(dbits);
-    return r32_exact_double(__builtin_ldexp((double)C * (double)(d.sig * m), d.ex + e));
+    const double X = __builtin_ldexp((double)C * (double)(d.sig * m), d.ex + e);
+    // e >= kNoTinyExp: X is 0 or at least 2^-102, so the conversion needs no flush, and adding
+    // +0 turns an exact -0 into +0
+    if (e >= kNoTinyExp) return (float)X + 0.0f;
+    return r32_exact_double(X);
 }
 
 // The exact sum of eight doubles T[j] (each exact, every one a multiple of 2^low) rounded once
