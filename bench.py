@@ -54,16 +54,16 @@ KERNEL_SOURCES = ("block_format_gemv_amd/csrc/gemv.hip", "block_format_gemv_amd/
                   "block_format_gemv_amd/csrc/qg_internal.hpp")
 MEASURED_TRAFFIC = {
     # (workload, dominant kernel): medians per dispatch, kernel sources hash
-    ("q4k_ffn_up_14336x4096", "fused"): {"kernel_sha": "0097a32191efe00b", "fetch_kib": 16247.0, "write_kib": 61.0625},
-    ("q4k_ffn_up_14336x4096", "gemv"): {"kernel_sha": "0097a32191efe00b", "fetch_kib": 16185.0, "write_kib": 56.0},
-    ("q4k_sub32_14336x4096", "fused"): {"kernel_sha": "0097a32191efe00b", "fetch_kib": 16287.5, "write_kib": 61.5},
-    ("q4k_sub32_14336x4096", "gemv"): {"kernel_sha": "0097a32191efe00b", "fetch_kib": 16234.5, "write_kib": 56.0},
-    ("q6k_output_128256x4096", "fused"): {"kernel_sha": "0097a32191efe00b", "fetch_kib": 210543.5, "write_kib": 506.0625},
-    ("q6k_output_128256x4096", "gemv"): {"kernel_sha": "0097a32191efe00b", "fetch_kib": 210486.0, "write_kib": 501.0},
-    ("q8_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "0097a32191efe00b", "fetch_kib": 30582.5, "write_kib": 61.5},
-    ("q8_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "0097a32191efe00b", "fetch_kib": 30527.5, "write_kib": 56.0},
-    ("q4_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "0097a32191efe00b", "fetch_kib": 16253.5, "write_kib": 61.5},
-    ("q4_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "0097a32191efe00b", "fetch_kib": 16197.0, "write_kib": 56.0},
+    ("q4k_ffn_up_14336x4096", "fused"): {"kernel_sha": "11305c7cbb049469", "fetch_kib": 16242.5, "write_kib": 61.0625},
+    ("q4k_ffn_up_14336x4096", "gemv"): {"kernel_sha": "11305c7cbb049469", "fetch_kib": 16189.5, "write_kib": 56.0},
+    ("q4k_sub32_14336x4096", "fused"): {"kernel_sha": "11305c7cbb049469", "fetch_kib": 16286.0, "write_kib": 61.5},
+    ("q4k_sub32_14336x4096", "gemv"): {"kernel_sha": "11305c7cbb049469", "fetch_kib": 16238.5, "write_kib": 56.0},
+    ("q6k_output_128256x4096", "fused"): {"kernel_sha": "11305c7cbb049469", "fetch_kib": 210544.5, "write_kib": 506.0625},
+    ("q6k_output_128256x4096", "gemv"): {"kernel_sha": "11305c7cbb049469", "fetch_kib": 210485.0, "write_kib": 501.0},
+    ("q8_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "11305c7cbb049469", "fetch_kib": 30578.5, "write_kib": 61.5},
+    ("q8_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "11305c7cbb049469", "fetch_kib": 30527.0, "write_kib": 56.0},
+    ("q4_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "11305c7cbb049469", "fetch_kib": 16252.0, "write_kib": 61.5},
+    ("q4_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "11305c7cbb049469", "fetch_kib": 16195.5, "write_kib": 56.0},
 }
 
 
