@@ -66,22 +66,45 @@ MEASURED_TRAFFIC = {
     ("q4_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "11305c7cbb049469", "fetch_kib": 16195.5, "write_kib": 56.0},
 }
 
+# The batched GEMM kernels (several columns): HBM traffic as above, and for the int8
+# matrix-core kernel its matrix-core use, from rocprofv3 --pmc passes:
+# SQ_INSTS_VALU_MFMA_MOPS_I8 (int8 matrix operations / 512 over the chip) and MfmaUtil (the
+# matrix units' busy cycles over the dispatch's active cycles times the SIMDs); medians per
+# dispatch, reported only while the sources (the GEMV kernels, which hold the several-column
+# kernel, and the matrix-core kernels) still hash to the value they were taken on.
+GEMM_SOURCES = KERNEL_SOURCES + ("block_format_gemv_amd/csrc/gemm_mfma.hip",)
+MFMA_PEAK_TOPS = 5000.0     # dense int8 matrix-core peak of the part, TOP/s
+MEASURED_GEMM = {
+    "q4k_gemm_n2_14336x4096": {"kernel_sha": "445f4154bbb6216a", "fetch_kib": 16217.5, "write_kib": 112.0},
+    "q4k_gemm_n8_14336x4096": {"kernel_sha": "445f4154bbb6216a", "fetch_kib": 16447.5, "write_kib": 448.0},
+    "q4k_gemm_n64_14336x4096": {"kernel_sha": "445f4154bbb6216a", "fetch_kib": 17238.5, "write_kib": 3584.0, "mops_i8": 44040192.0, "mfma_util_pct": 11.02},
+}
 
-def kernel_sha() -> str:
+
+def kernel_sha(sources=KERNEL_SOURCES) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for src in KERNEL_SOURCES:
+    for src in sources:
         with open(os.path.join(ROOT, src), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, kernel: str):
-    t = MEASURED_TRAFFIC.get((workload, kernel))
-    if not t or t["kernel_sha"] != kernel_sha():
+    t = MEASURED_GEMM.get(workload) if kernel == "gemm" else MEASURED_TRAFFIC.get((workload, kernel))
+    if not t or t["kernel_sha"] != kernel_sha(GEMM_SOURCES if kernel == "gemm" else KERNEL_SOURCES):
         return None
     return round(t["fetch_kib"] * 1024 * FETCH_FACTOR + t["write_kib"] * 1024 * WRITE_FACTOR)
+
+
+def measured_mfma(workload: str):
+    t = MEASURED_GEMM.get(workload)
+    if not t or "mops_i8" not in t or t["kernel_sha"] != kernel_sha(GEMM_SOURCES):
+        return None
+    return {"int8_ops_per_launch": t["mops_i8"] * 512, "mfma_util_pct": t["mfma_util_pct"]}
+
+
 METRIC = "quantized GEMV weight-stream HBM GB/s (% of peak) and rows/s at 1 GPU"
 
 WORKLOADS = {
@@ -469,6 +492,23 @@ def main():
             "algorithmic_bytes_per_launch": algo_bytes,
         },
     }
+    if "matrix cores" in kernel_label:
+        # the int8 matrix-core roofline: the dense contraction is 2*rows*cols*columns operations;
+        # the kernels issue three int8 products per weight (the sub-scale split into its high and
+        # low 3 bits, and the offset) over columns padded to 16
+        useful = 2.0 * rows * cols * ncol
+        issued = 3 * 2.0 * rows * cols * (-(-ncol // 16) * 16)
+        mm = measured_mfma(args.workload)
+        record["roofline_matrix_cores"] = {
+            "bound": "mfma",
+            "achieved": round(useful / (k_us * 1e-6) / 1e12, 2),
+            "peak": MFMA_PEAK_TOPS,
+            "unit": "TOP/s",
+            "frac": round(useful / (k_us * 1e-6) / 1e12 / MFMA_PEAK_TOPS, 4),
+            "issued_ops_per_launch": issued,
+            "issued_frac": round(issued / (k_us * 1e-6) / 1e12 / MFMA_PEAK_TOPS, 4),
+            "counters": mm,
+        }
     record["measured_ceiling"] = ceiling
     record.update(extra)
     if not args.no_cpu:
