@@ -75,9 +75,9 @@ MEASURED_TRAFFIC = {
 GEMM_SOURCES = KERNEL_SOURCES + ("block_format_gemv_amd/csrc/gemm_mfma.hip",)
 MFMA_PEAK_TOPS = 5000.0     # dense int8 matrix-core peak of the part, TOP/s
 MEASURED_GEMM = {
-    "q4k_gemm_n2_14336x4096": {"kernel_sha": "445f4154bbb6216a", "fetch_kib": 16217.5, "write_kib": 112.0},
-    "q4k_gemm_n8_14336x4096": {"kernel_sha": "445f4154bbb6216a", "fetch_kib": 16447.5, "write_kib": 448.0},
-    "q4k_gemm_n64_14336x4096": {"kernel_sha": "445f4154bbb6216a", "fetch_kib": 17238.5, "write_kib": 3584.0, "mops_i8": 44040192.0, "mfma_util_pct": 11.02},
+    "q4k_gemm_n2_14336x4096": {"kernel_sha": "55aafe9f16a21293", "fetch_kib": 16217.5, "write_kib": 112.0},
+    "q4k_gemm_n8_14336x4096": {"kernel_sha": "55aafe9f16a21293", "fetch_kib": 16447.5, "write_kib": 448.0},
+    "q4k_gemm_n64_14336x4096": {"kernel_sha": "55aafe9f16a21293", "fetch_kib": 17238.5, "write_kib": 3584.0, "mops_i8": 44040192.0, "mfma_util_pct": 10.85},
 }
 
 
@@ -121,6 +121,9 @@ WORKLOADS = {
     "q4k_gemm_n2_14336x4096": ("q4k", 14336, 4096, 0, 2),
     "q4k_gemm_n8_14336x4096": ("q4k", 14336, 4096, 0, 8),
     "q4k_gemm_n64_14336x4096": ("q4k", 14336, 4096, 0, 64),
+    "q4k_gemm_n64_4096x4096": ("q4k", 4096, 4096, 0, 64),
+    "q4k_gemm_n8_4096x4096": ("q4k", 4096, 4096, 0, 8),
+    "q4k_gemm_n2_4096x4096": ("q4k", 4096, 4096, 0, 2),
     # int8 KV cache (attention of one decode step): ("kv", query heads, KV heads, positions,
     # head size, query scaling)
     "kv_decode_32h_8kv_4096pos_128hd": ("kv", 32, 8, 4096, 128, 0),

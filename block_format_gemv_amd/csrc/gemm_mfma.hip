@@ -155,8 +155,9 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
 
     float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
-    // the block's integer sums on the matrix cores, then its combine into the row sums
-    auto compute = [&](const unsigned char *st) {
+    // the block's integer sums on the matrix cores, then its combine into the row sums; CLEAN:
+    // every activation scale of the workgroup's columns has an exponent of at least kNoTinyExp
+    auto compute = [&](const unsigned char *st, bool CLEAN) {
         v4i acc_h = {0, 0, 0, 0}, acc_l = {0, 0, 0, 0}, acc_o = {0, 0, 0, 0};
 #pragma unroll
         for (int p = 0; p < 4; p++) {
@@ -175,7 +176,17 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
         const bool near = q4k_near(fd, fm);
         const double Dd = (double)fd, Dm = (double)fm;
         const double *S = reinterpret_cast<const double *>(st + St::kS) + 16 * c + 4 * grp;
-        if (__all(near)) {
+        if (CLEAN && __all(near)) {
+            // no piece is tiny: every nonzero one is normal, no partial sum is subnormal or -0,
+            // and an exact zero adds as +0 would, so plain conversions and adds give the
+            // flushed ones' bits
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int Cb = 8 * acc_h[i] + acc_l[i];
+                const double X = __builtin_fma((double)Cb, Dd, -((double)acc_o[i] * Dm));
+                y[i] = y[i] + (float)(X * S[i]);
+            }
+        } else if (__all(near)) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int Cb = 8 * acc_h[i] + acc_l[i];
@@ -201,21 +212,31 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
         }
     };
 
+    bool ok = true;
+    for (int i = tid; i < 16 * CW * G; i += 256 * CW) {
+        const int col = min(colbase + i % (16 * CW), ncol - 1);
+        ok = ok && (int)(int16_t)(scw[(size_t)col * G + i / (16 * CW)] & 0xFFFFu) >= kNoTinyExp;
+    }
+    const bool clean = __syncthreads_and(ok);
+
     unsigned char *st0 = lds, *st1 = lds + St::kBytes;
     Pref<CW> p0, p1;
+    // The loads run unconditionally (past the last block they repeat it): with every path
+    // issuing the same loads, the compiler's wait before a stage is written counts exactly
+    // the younger loads still in flight instead of waiting for all of them.
     load(p0, 0);
-    if (G > 1) load(p1, 1);
+    load(p1, min(1, G - 1));
     stage_write(p0, st0);
     __syncthreads();
     for (int b = 0; b < G; b += 2) {
         // block b is in stage 0; block b+1's loads are in flight in p1
-        if (b + 2 < G) load(p0, b + 2);
-        compute(st0);
+        load(p0, min(b + 2, G - 1));
+        compute(st0, clean);
         if (b + 1 < G) stage_write(p1, st1);
         __syncthreads();
         if (b + 1 >= G) break;
-        if (b + 3 < G) load(p1, b + 3);
-        compute(st1);
+        load(p1, min(b + 3, G - 1));
+        compute(st1, clean);
         if (b + 2 < G) stage_write(p0, st0);
         __syncthreads();
     }

@@ -474,35 +474,39 @@ def _subnormal_partial_q4k(f, r):
     f["dmin"][r, :3] = [0, 801, 0]
 
 
-def test_subnormal_partial_sums_gemv_and_gemm(qg):
+@pytest.mark.parametrize("ncol,tiny", [(64, (0, 63)), (100, (70,))])
+def test_subnormal_partial_sums_gemv_and_gemm(qg, ncol, tiny):
     """Rows whose running sum passes through the subnormal range, through the GEMV and every
-    GEMM form: all must give the oracle's bits, which differ from unflushed adds."""
-    rows, cols, ncol = 70, 768, 64
+    GEMM form: all must give the oracle's bits, which differ from unflushed adds.  With 100
+    columns the tiny activation row lies in the second batch of 64 only, so the first batch
+    takes the matrix-core kernel's plain-add combine and the second its flushed one."""
+    rows, cols = 70, 768
     f = gen.q4k_fields(rows, cols, 77)
     for r in (0, 5, 69):
         _subnormal_partial_q4k(f, r)
     M = Mat(qg, f)
     xs = gen.act_outliers(ncol, cols, 78)
-    xs[0, :] = np.float32(2.0 ** -112)
-    xs[ncol - 1, :] = np.float32(2.0 ** -112)
+    for t in tiny:
+        xs[t, :] = np.float32(2.0 ** -112)
     act, c, m, e, _ = gpu_quant(qg, xs, 0)
-    assert int(c[0, 0]) == 126 and int(m[0, 0]) == 130 and int(e[0, 0]) == -126
+    t0 = tiny[0]
+    assert int(c[t0, 0]) == 126 and int(m[t0, 0]) == 130 and int(e[t0, 0]) == -126
     want = oracle.gemm(f, c, m, e, 0).reshape(ncol, rows)
     # unflushed adds of the three pieces (exact binary32 values) give other bits
     unit = np.float32(16380.0 * 2.0 ** -142)
     plain = np.float32(np.float32(np.float32(0) + np.float32(800 * unit)) + np.float32(-801 * unit))
     plain = np.float32(plain + np.float32(8 * unit))
-    assert plain.view(np.uint32) != bits(want[0])[0]
-    assert bits(want[0])[0] == np.float32(8 * unit).view(np.uint32)
+    assert plain.view(np.uint32) != bits(want[t0])[0]
+    assert bits(want[t0])[0] == np.float32(8 * unit).view(np.uint32)
     one = qg.alloc_act(1, cols, 0)
-    one.codes.copy_(act.codes[0:1]); one.scales.copy_(act.scales[0:1]); one.csums.copy_(act.csums[0:1])
-    assert first_mismatch(run_gemv(qg, M, one), want[0]) is None
+    one.codes.copy_(act.codes[t0:t0 + 1]); one.scales.copy_(act.scales[t0:t0 + 1]); one.csums.copy_(act.csums[t0:t0 + 1])
+    assert first_mismatch(run_gemv(qg, M, one), want[t0]) is None
     try:
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 1)
         for form, wh in ((1, 1), (1, 2), (1, 4), (2, 0), (3, 0)):
             qg.qg_set_tuning(qg.TUNE_MFMA_FORM, form)
             qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, wh)
-            say("subnormal partial sums, gemm form", form, "ring waves", wh)
+            say("subnormal partial sums, gemm form", form, "ring waves", wh, "columns", ncol)
             out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
             assert first_mismatch(out, want) is None, (form, wh, first_mismatch(out, want))
     finally:
