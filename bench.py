@@ -147,7 +147,7 @@ def parse():
                    help="time the step as qg_quantize_act + qg_gemv_q instead of qg_quantize_gemv")
     p.add_argument("--tune", action="append", default=[], metavar="KEY=VALUE",
                    help="a speed-only tuning knob (qg_set_tuning): waves_per_wg, mfma_min_cols, mfma_col_tiles, "
-                        "mfma_form, mfma_ring_waves, cols_kernel; output bits do not depend on them")
+                        "mfma_form, mfma_ring_waves, cols_kernel, mfma_tables; output bits do not depend on them")
     p.add_argument("--copy-probe", type=float, default=0,
                    help="only run 20 device-to-device copies of this many bytes (counter calibration) and exit")
     return p.parse_args()

@@ -153,6 +153,10 @@ int qg_set_tuning(int key, int64_t value)
         if (value > 1) return fail(QG_E_INVALID, "qg_set_tuning: the several-column kernel choice must be 0 or 1");
         g_tuning.cols_off = (int)value;
         return QG_OK;
+    case QG_TUNE_MFMA_TABLES:
+        if (value > 1) return fail(QG_E_INVALID, "qg_set_tuning: the scale tables choice must be 0 or 1");
+        g_tuning.mfma_pre_off = (int)value;
+        return QG_OK;
     default:
         return fail(QG_E_INVALID, "qg_set_tuning: unknown key %d", key);
     }

@@ -86,8 +86,11 @@ __device__ __forceinline__ float ftz_c(float x)
     return sub ? __uint_as_float(__float_as_uint(x) & 0x80000000u) : x;
 }
 
-// grid: x = 64-row group, y = batch of 16*CW activation columns
-template <int CW>
+// grid: x = 64-row group, y = batch of 16*CW activation columns.  PRE: the block scales and
+// sub-block fields of the group's rows and the activation scales of its columns, for every
+// block, are read into LDS tables once at the start (when they fit), so that a block's loads
+// are only its code chunks and activation codes: fewer vector-memory instructions per block.
+template <int CW, bool PRE>
 __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, int rows, int G,
                                                           const int8_t *__restrict__ codes,
                                                           const uint32_t *__restrict__ scw, int ncol,
@@ -113,6 +116,11 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
     const int8_t *abase = codes + (size_t)acol * C + 64 * pa + 16 * (la >> 4);
     const int scol = min(colbase + min(tid, 16 * CW - 1), ncol - 1);   // every thread loads one (in bounds)
     const uint8_t *gbase = image + (size_t)g * G * kTileBytesQ4K;
+    // PRE tables after the two stages: uint4 [G][64] row metas, double [G][16*CW] activation
+    // scales m*2^e, uint32 [G][16*CW] qg_act_scale words
+    uint4 *t_meta = reinterpret_cast<uint4 *>(lds + 2 * St::kBytes);
+    double *t_S = reinterpret_cast<double *>(lds + 2 * St::kBytes + (size_t)G * 64 * 16);
+    uint32_t *t_W = reinterpret_cast<uint32_t *>(t_S + (size_t)G * 16 * CW);
 
     auto load = [&](Pref<CW> &pf, int b) {
         const uint8_t *tile = gbase + (size_t)b * kTileBytesQ4K;
@@ -121,17 +129,18 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
             const int p = c + k * CW;
             pf.ch[k] = ld16(tile + 1024 * (2 * p + (grp >> 1)) + 16 * trow);
         }
-        pf.meta = ld16(tile + 8192 + 16 * trow);
+        if constexpr (!PRE) pf.meta = ld16(tile + 8192 + 16 * trow);
         pf.a = ld16(abase + (size_t)b * 256);
-        pf.scw = scw[(size_t)scol * G + b];
+        if constexpr (!PRE) pf.scw = scw[(size_t)scol * G + b];
     };
 
     // prepare this wave's weight steps and this thread's activation share into stage st
-    auto stage_write = [&](const Pref<CW> &pf, unsigned char *st) {
+    auto stage_write = [&](const Pref<CW> &pf, unsigned char *st, int b) {
+        const uint4 meta = PRE ? t_meta[(size_t)b * 64 + trow] : pf.meta;
 #pragma unroll
         for (int k = 0; k < 4 / CW; k++) {
             const int p = c + k * CW;
-            const uint32_t f = field_at(pf.meta.y, pf.meta.z, pf.meta.w, 2 * p + (grp >> 1));
+            const uint32_t f = field_at(meta.y, meta.z, meta.w, 2 * p + (grp >> 1));
             const uint32_t sc = f & 63u, hi = sc >> 3, lo = sc & 7u, mn = f >> 6;
             const int sh = 4 * (grp & 1);     // low nibbles: elements 0..15, high: 16..31
             const uint4 ch = pf.ch[k];
@@ -144,8 +153,9 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
                 make_uint4(bytes_times(q0, lo), bytes_times(q1, lo), bytes_times(q2, lo), bytes_times(q3, lo));
             reinterpret_cast<uint32_t *>(st + St::kBO)[slot] = mn * 0x01010101u;
         }
-        if (c == 0 && grp == 0) reinterpret_cast<uint32_t *>(st + St::kM)[trow] = pf.meta.x;
         reinterpret_cast<uint4 *>(st + St::kA)[(ta * 4 + pa) * 64 + la] = pf.a;
+        if (PRE) return;
+        if (c == 0 && grp == 0) reinterpret_cast<uint32_t *>(st + St::kM)[trow] = pf.meta.x;
         if (tid < 16 * CW) {
             reinterpret_cast<double *>(st + St::kS)[tid] =
                 __builtin_ldexp((double)((pf.scw >> 16) & 0xFFu), (int)(int16_t)(pf.scw & 0xFFFFu));
@@ -157,7 +167,7 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
 
     // the block's integer sums on the matrix cores, then its combine into the row sums; CLEAN:
     // every activation scale of the workgroup's columns has an exponent of at least kNoTinyExp
-    auto compute = [&](const unsigned char *st, bool CLEAN) {
+    auto compute = [&](const unsigned char *st, int b, bool CLEAN) {
         v4i acc_h = {0, 0, 0, 0}, acc_l = {0, 0, 0, 0}, acc_o = {0, 0, 0, 0};
 #pragma unroll
         for (int p = 0; p < 4; p++) {
@@ -171,11 +181,11 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
             acc_l = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bl, acc_l, 0, 0, 0);
             acc_o = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bo, acc_o, 0, 0, 0);
         }
-        const uint32_t dd = reinterpret_cast<const uint32_t *>(st + St::kM)[trow];
+        const uint32_t dd = PRE ? t_meta[(size_t)b * 64 + trow].x : reinterpret_cast<const uint32_t *>(st + St::kM)[trow];
         const float fd = f16_value(dd), fm = f16_value(dd >> 16);
         const bool near = q4k_near(fd, fm);
         const double Dd = (double)fd, Dm = (double)fm;
-        const double *S = reinterpret_cast<const double *>(st + St::kS) + 16 * c + 4 * grp;
+        const double *S = (PRE ? t_S + (size_t)b * 16 * CW : reinterpret_cast<const double *>(st + St::kS)) + 16 * c + 4 * grp;
         if (CLEAN && __all(near)) {
             // no piece is tiny: every nonzero one is normal, no partial sum is subnormal or -0,
             // and an exact zero adds as +0 would, so plain conversions and adds give the
@@ -195,7 +205,7 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
                 y[i] = ftz_c(y[i] + piece);
             }
         } else {
-            const uint32_t *W = reinterpret_cast<const uint32_t *>(st + St::kW) + 16 * c + 4 * grp;
+            const uint32_t *W = (PRE ? t_W + (size_t)b * 16 * CW : reinterpret_cast<const uint32_t *>(st + St::kW)) + 16 * c + 4 * grp;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int Cb = 8 * acc_h[i] + acc_l[i];
@@ -215,8 +225,16 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
     bool ok = true;
     for (int i = tid; i < 16 * CW * G; i += 256 * CW) {
         const int col = min(colbase + i % (16 * CW), ncol - 1);
-        ok = ok && (int)(int16_t)(scw[(size_t)col * G + i / (16 * CW)] & 0xFFFFu) >= kNoTinyExp;
+        const uint32_t w = scw[(size_t)col * G + i / (16 * CW)];
+        ok = ok && (int)(int16_t)(w & 0xFFFFu) >= kNoTinyExp;
+        if constexpr (PRE) {
+            t_S[i] = __builtin_ldexp((double)((w >> 16) & 0xFFu), (int)(int16_t)(w & 0xFFFFu));
+            t_W[i] = w;
+        }
     }
+    if constexpr (PRE)
+        for (int i = tid; i < 64 * G; i += 256 * CW)
+            t_meta[i] = ld16(gbase + (size_t)(i / 64) * kTileBytesQ4K + 8192 + 16 * (i % 64));
     const bool clean = __syncthreads_and(ok);
 
     unsigned char *st0 = lds, *st1 = lds + St::kBytes;
@@ -226,18 +244,18 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
     // the younger loads still in flight instead of waiting for all of them.
     load(p0, 0);
     load(p1, min(1, G - 1));
-    stage_write(p0, st0);
+    stage_write(p0, st0, 0);
     __syncthreads();
     for (int b = 0; b < G; b += 2) {
         // block b is in stage 0; block b+1's loads are in flight in p1
         load(p0, min(b + 2, G - 1));
-        compute(st0, clean);
-        if (b + 1 < G) stage_write(p1, st1);
+        compute(st0, b, clean);
+        if (b + 1 < G) stage_write(p1, st1, b + 1);
         __syncthreads();
         if (b + 1 >= G) break;
         load(p1, min(b + 3, G - 1));
-        compute(st1, clean);
-        if (b + 2 < G) stage_write(p0, st0);
+        compute(st1, b + 1, clean);
+        if (b + 2 < G) stage_write(p0, st0, b + 2);
         __syncthreads();
     }
 
@@ -251,28 +269,54 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
     }
 }
 
-template <int CW>
-int launch_cw(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes, const qg_act_scale *scales,
-              float *out, hipStream_t s)
+// the LDS a kernel has beside its dynamic share (its own static LDS: the workgroup vote)
+template <int CW, bool PRE>
+size_t cw_static_lds()
+{
+    static const size_t fixed = [] {
+        hipFuncAttributes a{};
+        return hipFuncGetAttributes(&a, reinterpret_cast<const void *>(gemm_mfma_q4k<CW, PRE>)) == hipSuccess
+                   ? a.sharedSizeBytes
+                   : (size_t)kMaxLds;
+    }();
+    return fixed;
+}
+
+template <int CW, bool PRE>
+int launch_cw_typed(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
+                    const qg_act_scale *scales, float *out, hipStream_t s, size_t lds)
 {
     const int64_t groups = (rows + 63) / 64;
     const dim3 grid((unsigned)groups, (unsigned)((ncol + 16 * CW - 1) / (16 * CW)));
-    const size_t lds = 2 * (size_t)Stage<CW>::kBytes;   // above 64 KiB: gfx950 gives a workgroup up to 160 KiB
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_mfma_q4k<CW>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_mfma_q4k<CW, PRE>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kMaxLds - cw_static_lds<CW, PRE>()));
     (void)attr;   // a refusal shows up as a launch error below
     const uint32_t *w = reinterpret_cast<const uint32_t *>(scales);
     hipEvent_t ev0, ev1;
     take_timing_events(&ev0, &ev1);
     if (ev0 && ev1)
-        hipExtLaunchKernelGGL(gemm_mfma_q4k<CW>, grid, dim3(256 * CW), lds, s, ev0, ev1, 0,
+        hipExtLaunchKernelGGL((gemm_mfma_q4k<CW, PRE>), grid, dim3(256 * CW), lds, s, ev0, ev1, 0,
                               static_cast<const uint8_t *>(image), (int)rows, G, codes, w, (int)ncol, out);
     else
-        hipLaunchKernelGGL(gemm_mfma_q4k<CW>, grid, dim3(256 * CW), lds, s, static_cast<const uint8_t *>(image),
+        hipLaunchKernelGGL((gemm_mfma_q4k<CW, PRE>), grid, dim3(256 * CW), lds, s, static_cast<const uint8_t *>(image),
                            (int)rows, G, codes, w, (int)ncol, out);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemm (matrix cores) launch: %s", hipGetErrorString(e));
     return QG_OK;
+}
+
+// two operand stages (above 64 KiB: gfx950 gives a workgroup up to 160 KiB), with the
+// per-block tables after them where those fit
+template <int CW>
+int launch_cw(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes, const qg_act_scale *scales,
+              float *out, hipStream_t s)
+{
+    const size_t stages = 2 * (size_t)Stage<CW>::kBytes;
+    const size_t tables = (size_t)G * (64 * 16 + 16 * CW * (8 + 4));
+    if (tuning().mfma_pre_off == 0 && stages + tables + cw_static_lds<CW, true>() <= (size_t)kMaxLds)
+        return launch_cw_typed<CW, true>(rows, G, ncol, image, codes, scales, out, s, stages + tables);
+    return launch_cw_typed<CW, false>(rows, G, ncol, image, codes, scales, out, s, stages);
 }
 
 template <int I>

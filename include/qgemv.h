@@ -330,14 +330,18 @@ int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink
  *                         is taken as 1); 0 = derived
  *   QG_TUNE_COLS_KERNEL   several columns below the matrix-core threshold (Q4_K/Q6_K, at most 16
  *                         blocks per row): 0 = the one-column kernel's machinery, NC columns per
- *                         wave (default); 1 = the kernel that stages the columns in LDS */
+ *                         wave (default); 1 = the kernel that stages the columns in LDS
+ *   QG_TUNE_MFMA_TABLES   the shared-operand form: 0 = read every block's block scales, sub-block
+ *                         fields and activation scales into LDS tables at the start where they
+ *                         fit (default); 1 = load them with each block */
 enum {
     QG_TUNE_WAVES_PER_WG = 1,
     QG_TUNE_MFMA_MIN_COLS = 2,
     QG_TUNE_MFMA_COL_TILES = 3,
     QG_TUNE_MFMA_FORM = 4,
     QG_TUNE_MFMA_RING_WAVES = 5,
-    QG_TUNE_COLS_KERNEL = 6
+    QG_TUNE_COLS_KERNEL = 6,
+    QG_TUNE_MFMA_TABLES = 7
 };
 int qg_set_tuning(int key, int64_t value);
 

@@ -34,6 +34,7 @@ def qg():
     q.qg_set_tuning(q.TUNE_MFMA_MIN_COLS, 0)
     q.qg_set_tuning(q.TUNE_MFMA_COL_TILES, 0)
     q.qg_set_tuning(q.TUNE_COLS_KERNEL, 0)
+    q.qg_set_tuning(q.TUNE_MFMA_TABLES, 0)
     oracle.set_threads(8)
     return q
 
@@ -443,9 +444,12 @@ def test_matrix_core_gemm_matches_oracle(qg, ncol):
             qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, wh)
             for ct in (0, 1, 2, 4):                                 # 0: derived from the column count
                 qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, ct)
-                say("matrix-core gemm", ncol, "form", form, "ring waves", wh, "column tiles", ct)
-                out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
-                assert first_mismatch(out, want) is None, (ncol, form, wh, ct, first_mismatch(out, want))
+                for tab in ((0, 1) if form == 2 else (0,)):         # shared operands: scale tables or not
+                    qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, tab)
+                    say("matrix-core gemm", ncol, "form", form, "ring waves", wh, "column tiles", ct, "tables off", tab)
+                    out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+                    assert first_mismatch(out, want) is None, (ncol, form, wh, ct, tab, first_mismatch(out, want))
+                qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 0)
@@ -503,15 +507,17 @@ def test_subnormal_partial_sums_gemv_and_gemm(qg, ncol, tiny):
     assert first_mismatch(run_gemv(qg, M, one), want[t0]) is None
     try:
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 1)
-        for form, wh in ((1, 1), (1, 2), (1, 4), (2, 0), (3, 0)):
+        for form, wh, tab in ((1, 1, 0), (1, 2, 0), (1, 4, 0), (2, 0, 0), (2, 0, 1), (3, 0, 0)):
             qg.qg_set_tuning(qg.TUNE_MFMA_FORM, form)
             qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, wh)
-            say("subnormal partial sums, gemm form", form, "ring waves", wh, "columns", ncol)
+            qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, tab)
+            say("subnormal partial sums, gemm form", form, "ring waves", wh, "tables off", tab, "columns", ncol)
             out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
-            assert first_mismatch(out, want) is None, (form, wh, first_mismatch(out, want))
+            assert first_mismatch(out, want) is None, (form, wh, tab, first_mismatch(out, want))
     finally:
         qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, 0)
+        qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 0)
 
 
