@@ -90,14 +90,15 @@ __device__ __forceinline__ float ftz_c(float x)
 // sub-block fields of the group's rows and the activation scales of its columns, for every
 // block, are read into LDS tables once at the start (when they fit), so that a block's loads
 // are only its code chunks and activation codes: fewer vector-memory instructions per block.
-template <int CW, bool PRE>
-__global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, int rows, int G,
+template <int CW, bool PRE, int GT = 0>
+__global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, int rows, int G_arg,
                                                           const int8_t *__restrict__ codes,
                                                           const uint32_t *__restrict__ scw, int ncol,
                                                           float *__restrict__ out)
 {
     using St = Stage<CW>;
     extern __shared__ __align__(16) unsigned char lds[];
+    const int G = GT ? GT : G_arg;   // GT: a block count known when compiling (the loop unrolls)
     const int C = G * 256;
     const int g = blockIdx.x;
     const int colbase = blockIdx.y * 16 * CW;
@@ -238,10 +239,45 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
     const bool clean = __syncthreads_and(ok);
 
     unsigned char *st0 = lds, *st1 = lds + St::kBytes;
-    Pref<CW> p0, p1;
     // The loads run unconditionally (past the last block they repeat it): with every path
     // issuing the same loads, the compiler's wait before a stage is written counts exactly
     // the younger loads still in flight instead of waiting for all of them.
+    if constexpr (PRE) {
+        // a block's loads are its code chunks and activation codes only: three register
+        // buffers (block k in p[k % 3]); the buffer a step stages takes the loads of the block
+        // three steps later
+        Pref<CW> p0, p1, p2;
+        load(p0, 0);
+        load(p1, min(1, G - 1));
+        load(p2, min(2, G - 1));
+        stage_write(p0, st0, 0);
+        load(p0, min(3, G - 1));
+        __syncthreads();
+        auto step = [&](int b, Pref<CW> &ps) {
+            compute((b & 1) ? st1 : st0, b, clean);
+            if (b + 1 < G) stage_write(ps, (b & 1) ? st0 : st1, b + 1);
+            load(ps, min(b + 4, G - 1));
+            __syncthreads();
+        };
+        auto three = [&](int b) {
+            step(b, p1);
+            if (b + 1 >= G) return false;
+            step(b + 1, p2);
+            if (b + 2 >= G) return false;
+            step(b + 2, p0);
+            return true;
+        };
+        if constexpr (GT > 0) {
+            // straight-line code: the compiler's waits count the loads in flight exactly
+#pragma unroll
+            for (int b = 0; b < GT; b += 3)
+                if (!three(b)) break;
+        } else {
+            for (int b = 0; b < G; b += 3)
+                if (!three(b)) break;
+        }
+    } else {
+    Pref<CW> p0, p1;
     load(p0, 0);
     load(p1, min(1, G - 1));
     stage_write(p0, st0, 0);
@@ -258,6 +294,7 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
         if (b + 2 < G) stage_write(p0, st0, b + 2);
         __syncthreads();
     }
+    }
 
     const int64_t row = (int64_t)g * 64 + trow;
     if (row < rows) {
@@ -270,36 +307,36 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
 }
 
 // the LDS a kernel has beside its dynamic share (its own static LDS: the workgroup vote)
-template <int CW, bool PRE>
+template <int CW, bool PRE, int GT = 0>
 size_t cw_static_lds()
 {
     static const size_t fixed = [] {
         hipFuncAttributes a{};
-        return hipFuncGetAttributes(&a, reinterpret_cast<const void *>(gemm_mfma_q4k<CW, PRE>)) == hipSuccess
+        return hipFuncGetAttributes(&a, reinterpret_cast<const void *>(gemm_mfma_q4k<CW, PRE, GT>)) == hipSuccess
                    ? a.sharedSizeBytes
                    : (size_t)kMaxLds;
     }();
     return fixed;
 }
 
-template <int CW, bool PRE>
+template <int CW, bool PRE, int GT = 0>
 int launch_cw_typed(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
                     const qg_act_scale *scales, float *out, hipStream_t s, size_t lds)
 {
     const int64_t groups = (rows + 63) / 64;
     const dim3 grid((unsigned)groups, (unsigned)((ncol + 16 * CW - 1) / (16 * CW)));
     static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_mfma_q4k<CW, PRE>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kMaxLds - cw_static_lds<CW, PRE>()));
+        hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_mfma_q4k<CW, PRE, GT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kMaxLds - cw_static_lds<CW, PRE, GT>()));
     (void)attr;   // a refusal shows up as a launch error below
     const uint32_t *w = reinterpret_cast<const uint32_t *>(scales);
     hipEvent_t ev0, ev1;
     take_timing_events(&ev0, &ev1);
     if (ev0 && ev1)
-        hipExtLaunchKernelGGL((gemm_mfma_q4k<CW, PRE>), grid, dim3(256 * CW), lds, s, ev0, ev1, 0,
+        hipExtLaunchKernelGGL((gemm_mfma_q4k<CW, PRE, GT>), grid, dim3(256 * CW), lds, s, ev0, ev1, 0,
                               static_cast<const uint8_t *>(image), (int)rows, G, codes, w, (int)ncol, out);
     else
-        hipLaunchKernelGGL((gemm_mfma_q4k<CW, PRE>), grid, dim3(256 * CW), lds, s, static_cast<const uint8_t *>(image),
+        hipLaunchKernelGGL((gemm_mfma_q4k<CW, PRE, GT>), grid, dim3(256 * CW), lds, s, static_cast<const uint8_t *>(image),
                            (int)rows, G, codes, w, (int)ncol, out);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemm (matrix cores) launch: %s", hipGetErrorString(e));
@@ -314,8 +351,10 @@ int launch_cw(int64_t rows, int G, int64_t ncol, const void *image, const int8_t
 {
     const size_t stages = 2 * (size_t)Stage<CW>::kBytes;
     const size_t tables = (size_t)G * (64 * 16 + 16 * CW * (8 + 4));
-    if (tuning().mfma_pre_off == 0 && stages + tables + cw_static_lds<CW, true>() <= (size_t)kMaxLds)
+    if (tuning().mfma_pre_off == 0 && stages + tables + cw_static_lds<CW, true>() <= (size_t)kMaxLds) {
+        if (G == 16) return launch_cw_typed<CW, true, 16>(rows, G, ncol, image, codes, scales, out, s, stages + tables);
         return launch_cw_typed<CW, true>(rows, G, ncol, image, codes, scales, out, s, stages + tables);
+    }
     return launch_cw_typed<CW, false>(rows, G, ncol, image, codes, scales, out, s, stages);
 }
 
