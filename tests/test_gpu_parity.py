@@ -463,6 +463,33 @@ def test_matrix_core_gemm_matches_oracle(qg, ncol):
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 0)
 
 
+@pytest.mark.parametrize("ncol", [64, 100])
+def test_matrix_core_gemm_16_blocks(qg, ncol):
+    """Rows of 16 blocks take the shared-operand kernel whose block loop is unrolled when
+    compiled: ragged rows and columns, block scales that take both the near-exponent and the
+    general combine, and (in the second run) a row of tiny activations, which makes its batch
+    of 64 columns take the flushed combine; with and without the scale tables."""
+    rows, cols = 130, 4096
+    f = _adversarial_fields("q4k", rows, cols, 4400 + ncol)
+    for r in (1, 66):
+        _subnormal_partial_q4k(f, r)
+    M = Mat(qg, f)
+    for tiny in (False, True):
+        xs = gen.act_outliers(ncol, cols, 4401 + ncol)
+        if tiny:
+            xs[ncol - 3, :] = np.float32(2.0 ** -112)
+        act, c, m, e, _ = gpu_quant(qg, xs, 0)
+        want = oracle.gemm(f, c, m, e, 0).reshape(ncol, rows)
+        try:
+            for tab in (0, 1):
+                qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, tab)
+                say("matrix-core gemm, 16 blocks", ncol, "tiny row", tiny, "tables off", tab)
+                out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+                assert first_mismatch(out, want) is None, (ncol, tiny, tab, first_mismatch(out, want))
+        finally:
+            qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, 0)
+
+
 def _subnormal_partial_q4k(f, r):
     """Row r of a Q4_K-style matrix (at least 3 blocks) whose PerBlock pieces, under an
     activation block of all 2^-112 (codes 126, scale 130 * 2^-126), are 16380*k*2^-142 with
