@@ -120,6 +120,8 @@ WORKLOADS = {
     "q4k_sub32_14336x4096": ("q4k", 14336, 4096, 1, 1),
     "q4k_gemm_n2_14336x4096": ("q4k", 14336, 4096, 0, 2),
     "q4k_gemm_n8_14336x4096": ("q4k", 14336, 4096, 0, 8),
+    "q4k_gemm_n16_14336x4096": ("q4k", 14336, 4096, 0, 16),
+    "q4k_gemm_n32_14336x4096": ("q4k", 14336, 4096, 0, 32),
     "q4k_gemm_n64_14336x4096": ("q4k", 14336, 4096, 0, 64),
     "q4k_gemm_n64_4096x4096": ("q4k", 4096, 4096, 0, 64),
     "q4k_gemm_n8_4096x4096": ("q4k", 4096, 4096, 0, 8),
@@ -339,7 +341,7 @@ def main():
         kernel_label = ("gemv1_kernel<..., SRC_F32> (one-launch quantize + GEMV)" if fused
                         else "gemv1_kernel<..., SRC_CODES> (GEMV of a quantized row)")
     elif fmt_s == "q4k" and mode == 0 and ncol >= (tuned.get("mfma_min_cols") or 9):
-        kernel_label = "gemm_mfma_q4k (matrix cores, shared operands)" if ncol >= 48 else \
+        kernel_label = "gemm_mfma_q4k (matrix cores, shared operands)" if ncol > 16 else \
             "gemm_ring_q4k (matrix cores, LDS-DMA ring)"
     elif cols <= 16 * 256 and not tuned.get("cols_kernel") and fmt_s in ("q4k", "q6k"):
         kernel_label = "gemv1_cols_kernel (one-column machinery, up to 8 columns a wave)"

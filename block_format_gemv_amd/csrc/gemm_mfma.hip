@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
     double *t_S = reinterpret_cast<double *>(lds + 2 * St::kBytes + (size_t)G * 64 * 16);
     uint32_t *t_W = reinterpret_cast<uint32_t *>(t_S + (size_t)G * 16 * CW);
 
-    auto load = [&](Pref<CW> &pf, int b) {
+    auto load = [&](Pref<CW> &pf, int b) __attribute__((always_inline)) {
         const uint8_t *tile = gbase + (size_t)b * kTileBytesQ4K;
 #pragma unroll
         for (int k = 0; k < 4 / CW; k++) {
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
     };
 
     // prepare this wave's weight steps and this thread's activation share into stage st
-    auto stage_write = [&](const Pref<CW> &pf, unsigned char *st, int b) {
+    auto stage_write = [&](const Pref<CW> &pf, unsigned char *st, int b) __attribute__((always_inline)) {
         const uint4 meta = PRE ? t_meta[(size_t)b * 64 + trow] : pf.meta;
 #pragma unroll
         for (int k = 0; k < 4 / CW; k++) {
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
 
     // the block's integer sums on the matrix cores, then its combine into the row sums; CLEAN:
     // every activation scale of the workgroup's columns has an exponent of at least kNoTinyExp
-    auto compute = [&](const unsigned char *st, int b, bool CLEAN) {
+    auto compute = [&](const unsigned char *st, int b, bool CLEAN) __attribute__((always_inline)) {
         v4i acc_h = {0, 0, 0, 0}, acc_l = {0, 0, 0, 0}, acc_o = {0, 0, 0, 0};
 #pragma unroll
         for (int p = 0; p < 4; p++) {
@@ -253,13 +253,13 @@ __global__ __launch_bounds__(256 * CW) void gemm_mfma_q4k(const uint8_t *image, 
         stage_write(p0, st0, 0);
         load(p0, min(3, G - 1));
         __syncthreads();
-        auto step = [&](int b, Pref<CW> &ps) {
+        auto step = [&](int b, Pref<CW> &ps) __attribute__((always_inline)) {
             compute((b & 1) ? st1 : st0, b, clean);
             if (b + 1 < G) stage_write(ps, (b & 1) ? st0 : st1, b + 1);
             load(ps, min(b + 4, G - 1));
             __syncthreads();
         };
-        auto three = [&](int b) {
+        auto three = [&](int b) __attribute__((always_inline)) {
             step(b, p1);
             if (b + 1 >= G) return false;
             step(b + 1, p2);
@@ -859,9 +859,10 @@ int launch_gemm_mfma(int64_t rows, int64_t cols, int64_t ncol, const void *image
     const int G = (int)(cols / 256);
     const int form = tuning().mfma_form;
     int tiles = tuning().mfma_col_tiles;
-    // derived (measured on the 14336 x 4096 matrix): below 48 columns the ring with one column
-    // tile, from 48 the shared-operand form with four
-    if (form == 1 || (form == 0 && ncol < 48)) {
+    // derived (measured on the 14336 x 4096 matrix): up to 16 columns the ring with one column
+    // tile, up to 32 the shared-operand form with two, beyond that the shared-operand form
+    // with four
+    if (form == 1 || (form == 0 && ncol <= 16)) {
         const int ct = tiles > 0 ? tiles : form == 0 ? 1 : ncol >= 48 ? 4 : ncol >= 24 ? 2 : 1;
         int st = QG_E_UNSUPPORTED;
         if (ct == 4) st = launch_ring<4>(rows, G, ncol, image, codes, scales, out, s);
@@ -870,10 +871,10 @@ int launch_gemm_mfma(int64_t rows, int64_t cols, int64_t ncol, const void *image
         if (st != QG_E_UNSUPPORTED) return st;
         if (form == 1) return fail(QG_E_UNSUPPORTED, "gemm: rows of %d blocks do not fit the ring's LDS", G);
     }
-    if (form == 2 || (form == 0 && ncol >= 48)) {
-        // shared operands: 4 column tiles (64 columns per workgroup) unless asked otherwise
+    if (form == 2 || (form == 0 && ncol > 16)) {
+        // shared operands: 2 column tiles up to 32 columns, else 4, unless asked otherwise
         if (tiles == 1) return launch_cw<1>(rows, G, ncol, image, codes, scales, out, s);
-        if (tiles == 2) return launch_cw<2>(rows, G, ncol, image, codes, scales, out, s);
+        if (tiles == 2 || (tiles == 0 && ncol <= 32)) return launch_cw<2>(rows, G, ncol, image, codes, scales, out, s);
         return launch_cw<4>(rows, G, ncol, image, codes, scales, out, s);
     }
     if (tiles == 2 || (tiles == 0 && ncol >= 32)) return launch_wave<2>(rows, G, ncol, image, codes, scales, out, s);

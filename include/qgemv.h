@@ -321,8 +321,8 @@ int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink
  *   QG_TUNE_MFMA_FORM     the matrix-core GEMM's form: 1 = LDS ring (tiles and activation operands
  *                         staged by LDS-DMA loads several blocks ahead), 2 = shared operands
  *                         (weight operands built once per workgroup in LDS), 3 = per wave
- *                         (operands in each wave's registers); 0 = derived (the ring where its
- *                         LDS fits, else shared operands from 48 columns, else per wave)
+ *                         (operands in each wave's registers); 0 = derived (up to 16 columns the
+ *                         ring where its LDS fits, else per wave; beyond 16 shared operands)
  *   QG_TUNE_MFMA_COL_TILES 1, 2 or 4: 16-column tiles per workgroup of the ring and shared-operand
  *                         forms (the per-wave form takes 1 or 2); 0 = derived from the columns
  *   QG_TUNE_MFMA_RING_WAVES 1, 2 or 4 waves per 16-row quarter in the ring form, each taking an
