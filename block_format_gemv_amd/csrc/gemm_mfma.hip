@@ -15,7 +15,7 @@
 // Operand roles: the MFMA's M dimension is 16 activation columns, N is 16 weight rows, so
 // lane l of a result owns weight row l%16 and activation columns 4*(l/16) .. +3.
 //
-// The shared-operand form (48 columns and more): a workgroup owns one 64-row group and 16*CW
+// The shared-operand form (more than 16 columns): a workgroup owns one 64-row group and 16*CW
 // columns: wave (r, c) computes rows 16r..16r+15
 // against columns 16c..16c+15.  Per block the workgroup builds, once, the weight operands of
 // its 64 rows (wave (r, c) prepares the 64-element steps c, c+CW, .. of row quarter r) and the
