@@ -75,9 +75,9 @@ MEASURED_TRAFFIC = {
 GEMM_SOURCES = KERNEL_SOURCES + ("block_format_gemv_amd/csrc/gemm_mfma.hip",)
 MFMA_PEAK_TOPS = 5000.0     # dense int8 matrix-core peak of the part, TOP/s
 MEASURED_GEMM = {
-    "q4k_gemm_n2_14336x4096": {"kernel_sha": "4eb487c42457218e", "fetch_kib": 16217.5, "write_kib": 112.0},
-    "q4k_gemm_n8_14336x4096": {"kernel_sha": "4eb487c42457218e", "fetch_kib": 16447.5, "write_kib": 448.0},
-    "q4k_gemm_n64_14336x4096": {"kernel_sha": "4eb487c42457218e", "fetch_kib": 17565.5625, "write_kib": 3584.0, "mops_i8": 44040192.0, "mfma_util_pct": 11.37},
+    "q4k_gemm_n2_14336x4096": {"kernel_sha": "fa8f343d31d297dd", "fetch_kib": 16217.5, "write_kib": 112.0},
+    "q4k_gemm_n8_14336x4096": {"kernel_sha": "fa8f343d31d297dd", "fetch_kib": 16447.5, "write_kib": 448.0},
+    "q4k_gemm_n64_14336x4096": {"kernel_sha": "fa8f343d31d297dd", "fetch_kib": 17567.6875, "write_kib": 3584.0, "mops_i8": 44040192.0, "mfma_util_pct": 11.43},
 }
 
 
