@@ -490,6 +490,25 @@ def test_matrix_core_gemm_16_blocks(qg, ncol):
             qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, 0)
 
 
+@pytest.mark.parametrize("cols", [6144, 8192, 12288])
+def test_matrix_core_gemm_long_rows(qg, cols):
+    """Rows of 24, 32 and 48 blocks through the shared-operand kernel: at 24 blocks the scale
+    tables fit in LDS beside the operand stages (the block loop runs with three prefetch
+    buffers), at 32 and 48 they do not and each block loads its own scales; 40 columns, ragged
+    rows, far block-scale pairs and one row of tiny activations."""
+    rows, ncol = 70, 40
+    f = _adversarial_fields("q4k", rows, cols, 5100 + cols // 256)
+    _subnormal_partial_q4k(f, 3)
+    M = Mat(qg, f)
+    xs = gen.act_outliers(ncol, cols, 5101 + cols // 256)
+    xs[7, :] = np.float32(2.0 ** -112)
+    act, c, m, e, _ = gpu_quant(qg, xs, 0)
+    want = oracle.gemm(f, c, m, e, 0).reshape(ncol, rows)
+    say("matrix-core gemm, long rows", cols)
+    out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+    assert first_mismatch(out, want) is None, (cols, first_mismatch(out, want))
+
+
 def _subnormal_partial_q4k(f, r):
     """Row r of a Q4_K-style matrix (at least 3 blocks) whose PerBlock pieces, under an
     activation block of all 2^-112 (codes 126, scale 130 * 2^-126), are 16380*k*2^-142 with
