@@ -150,6 +150,10 @@ def parse():
     p.add_argument("--tune", action="append", default=[], metavar="KEY=VALUE",
                    help="a speed-only tuning knob (qg_set_tuning): waves_per_wg, mfma_min_cols, mfma_col_tiles, "
                         "mfma_form, mfma_ring_waves, cols_kernel, mfma_tables; output bits do not depend on them")
+    p.add_argument("--ceiling-sweep", action="store_true",
+                   help="only sweep plain-read launch shapes (qg_stream_read_shape) and a library read kernel "
+                        "(torch's amax) over the 4096x4096 and 14336x4096 Q4_K-style image sizes, cold; "
+                        "print a markdown table and exit")
     p.add_argument("--copy-probe", type=float, default=0,
                    help="only run 20 device-to-device copies of this many bytes (counter calibration) and exit")
     return p.parse_args()
@@ -166,6 +170,107 @@ def copy_probe(nbytes: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": nbytes, "copies": 20}), flush=True)
+
+
+def ceiling_sweep() -> None:
+    """Plain reads of the two Q4_K-style image sizes (9,437,184 and 33,030,144 bytes) in many
+    launch shapes, each launch reading the next of the copies of a 1 GiB buffer (cold, as the
+    benchmark reads weights); per shape the time per launch from events around graph replays.
+    Beside our own read kernel, torch's amax over the same bytes (viewed as int32) is timed the
+    same way: a read kernel this library did not write."""
+    import torch
+
+    import block_format_gemv_amd as qg
+
+    dev = torch.device("cuda:0")
+    big = torch.randint(0, 1 << 30, ((1 << 30) // 4,), dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    s = torch.cuda.Stream()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    graph_len = 32
+
+    def per_launch_us(fn, copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(graph_len):
+                fn(i % copies)
+        for _ in range(3):
+            g.replay()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        reps = 8
+        with torch.cuda.stream(s):
+            torch.cuda.synchronize()
+            t0.record(s)
+            for _ in range(reps):
+                g.replay()
+            t1.record(s)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / (reps * graph_len)
+
+    lines = ["| image bytes | read kernel | waves/WG | KiB/wave | workgroups | loads | us/launch | GB/s | % of 8 TB/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    results = []
+    for nbytes in (9437184, 33030144):
+        copies = (1 << 30) // nbytes
+        views = [big.view(torch.uint8)[c * nbytes:(c + 1) * nbytes] for c in range(copies)]
+        shapes = []
+        for w in (4, 8, 16):
+            for k in (1, 2, 4, 9, 16):
+                shapes.append((w, k, 0, 0))
+        for w in (4, 8, 16):
+            for k in (1, 4, 9):
+                for wgs in (cus, 2 * cus, 4 * cus, 8 * cus):
+                    shapes.append((w, k, wgs, 0))
+        shapes += [(16, 9, 0, 1), (4, 4, 0, 1), (8, 4, 2 * cus, 1)]
+        for w, k, wgs, flags in shapes:
+            def fn(c, w=w, k=k, wgs=wgs, flags=flags):
+                qg.qg_stream_read_shape(views[c], nbytes, w, k, wgs, flags, 0x9E3779B9, sink, s)
+            us = per_launch_us(fn, copies)
+            nwg = wgs if wgs else -(-(-(-nbytes // 1024) // k) // w)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            results.append((nbytes, "qg_stream_read_shape", w, k, nwg, "grid-stride" if wgs else "one pass",
+                            "ordinary" if flags else "non-temporal", us, gbs))
+        def gemv_pattern(c):
+            qg.qg_stream_read(views[c], nbytes, 0x9E3779B9, sink, s)
+        us = per_launch_us(gemv_pattern, copies)
+        results.append((nbytes, "qg_stream_read (the GEMV's pattern)", 16, 9, -(-(-(-nbytes // 1024) // 9) // 16),
+                        "one pass", "non-temporal", us, nbytes / (us * 1e-6) / 1e9))
+        # torch's reduction, eager (it is kept out of graphs: it may clear a semaphore with a
+        # memset): a long read first, so that the launches queue up behind it and each pair of
+        # events brackets its kernels back to back
+        ints = [v.view(torch.int32) for v in views]
+        outs = [torch.empty((), dtype=torch.int32, device=dev) for _ in range(copies)]
+        ts = []
+        with torch.cuda.stream(s):
+            torch.amax(ints[0], dim=0, out=outs[0])
+            torch.cuda.synchronize()
+            qg.qg_stream_read(big, big.numel() * 4, 0x9E3779B9, sink, s)
+            evs = []
+            for i in range(24):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                torch.amax(ints[i % copies], dim=0, out=outs[i % copies])
+                e1.record(s)
+                evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs[4:])
+        us = ts[len(ts) // 2]
+        results.append((nbytes, "torch.amax (int32 view, eager, median)", "-", "-", "-", "library", "-", us,
+                        nbytes / (us * 1e-6) / 1e9))
+    for nbytes, kern, w, k, nwg, mode, loads, us, gbs in results:
+        lines.append(f"| {nbytes} | {kern} | {w} | {k} | {nwg} ({mode}) | {loads} | {us:.3f} | {gbs:.1f} | "
+                     f"{100 * gbs / HBM_PEAK_GBS:.1f} |")
+    print("\n".join(lines), flush=True)
+    best = {}
+    for r in results:
+        if r[0] not in best or r[7] < best[r[0]][7]:
+            best[r[0]] = r
+    print(json.dumps({"ceiling_sweep_best": {str(k): {"kernel": v[1], "waves_per_wg": v[2], "kib_per_wave": v[3],
+                                                      "workgroups": v[4], "mode": v[5], "us": round(v[7], 3),
+                                                      "frac_of_peak": round(v[8] / HBM_PEAK_GBS, 4)}
+                                             for k, v in best.items()}}), flush=True)
 
 
 class Hip:
@@ -261,6 +366,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe(int(args.copy_probe))
+        return
+    if args.ceiling_sweep:
+        ceiling_sweep()
         return
     import torch
 

@@ -32,7 +32,7 @@ MAX_MATRICES = 8
 
 EXPORTS = ("qg_reads", "qg_image_bytes", "qg_pack_q4k", "qg_pack_q6k", "qg_pack_b32", "qg_quantize_act",
            "qg_gemv_q", "qg_gemm_q", "qg_quantize_gemv", "qg_quantize_gemv_argmax", "qg_argmax_index",
-           "qg_quantize_gemv_multi", "qg_gemv_q_multi", "qg_block_sums", "qg_stream_read", "qg_set_tuning",
+           "qg_quantize_gemv_multi", "qg_gemv_q_multi", "qg_block_sums", "qg_stream_read", "qg_stream_read_shape", "qg_set_tuning",
            "qg_time_next_launch", "qg_last_error", "qg_version", "qg_kv_cache_rows", "qg_kv_quantize_heads",
            "qg_kv_scores", "qg_kv_weighted")
 VALUE_BLOCK = 32
@@ -63,6 +63,7 @@ def _load():
     L.qg_quantize_gemv.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     L.qg_block_sums.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
     L.qg_stream_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_uint32, vp, vp]
+    L.qg_stream_read_shape.argtypes = [vp, ctypes.c_size_t, i32, i32, i64, i32, ctypes.c_uint32, vp, vp]
     L.qg_quantize_gemv_argmax.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.qg_argmax_index.argtypes = [ctypes.c_uint64]
     L.qg_argmax_index.restype = ctypes.c_int64
@@ -319,6 +320,35 @@ def qg_stream_read(buf, nbytes: int, magic: int, sink, stream=None) -> None:
     _need(buf, nbytes, "buf")
     _need(sink, 4, "sink")
     _check(_lib.qg_stream_read(_dptr(buf), nbytes, magic & 0xFFFFFFFF, _dptr(sink), _stream(stream)))
+
+
+def qg_stream_read_shape(buf, nbytes: int, waves_per_wg: int, kib_per_wave: int, wgs: int, flags: int, magic: int,
+                         sink, stream=None) -> None:
+    """Diagnostic streaming read in a chosen launch geometry; see qgemv.h."""
+    _need(buf, nbytes, "buf")
+    _need(sink, 4, "sink")
+    _check(_lib.qg_stream_read_shape(_dptr(buf), nbytes, waves_per_wg, kib_per_wave, wgs, flags, magic & 0xFFFFFFFF,
+                                     _dptr(sink), _stream(stream)))
+
+
+def check(err_flag, stream=None) -> None:
+    """Wait for the work queued on `stream` (the current stream by default), then map the
+    non-finite flag that qg_quantize_act, qg_quantize_gemv(_multi, _argmax) and
+    qg_kv_quantize_heads set when an activation block holds +-inf to a refusal: QGError with
+    status QG_E_NONFINITE if the flag is set.  The flag is left as it is (the caller clears it
+    before the next call).  A flag in host memory is read as it is."""
+    import torch
+    if err_flag is None:
+        return
+    if err_flag.is_cuda:
+        if stream is None:
+            torch.cuda.current_stream(err_flag.device).synchronize()
+        elif isinstance(stream, int):
+            torch.cuda.synchronize(err_flag.device)
+        else:
+            stream.synchronize()
+    if int(err_flag.reshape(-1)[0].item()) != 0:
+        raise QGError(E_NONFINITE, "an activation block holds an infinity (the non-finite flag is set)")
 
 
 def qg_set_tuning(key: int, value: int) -> None:

@@ -29,7 +29,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Werror",
           "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-fno-gpu-rdc",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

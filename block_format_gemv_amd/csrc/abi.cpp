@@ -323,6 +323,25 @@ int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink
     return launch_stream_read(buf, bytes, magic, sink, static_cast<hipStream_t>(stream));
 }
 
+int qg_stream_read_shape(const void *buf, size_t bytes, int waves_per_wg, int kib_per_wave, int64_t wgs, int flags,
+                         uint32_t magic, uint32_t *sink, void *stream)
+{
+    const char *who = "qg_stream_read_shape";
+    int st;
+    if (waves_per_wg != 1 && waves_per_wg != 2 && waves_per_wg != 4 && waves_per_wg != 8 && waves_per_wg != 16)
+        return fail(QG_E_INVALID, "%s: %d waves per workgroup is not one of 1, 2, 4, 8, 16", who, waves_per_wg);
+    if (kib_per_wave != 1 && kib_per_wave != 2 && kib_per_wave != 4 && kib_per_wave != 8 && kib_per_wave != 9 &&
+        kib_per_wave != 16)
+        return fail(QG_E_INVALID, "%s: %d KiB per wave is not one of 1, 2, 4, 8, 9, 16", who, kib_per_wave);
+    if (wgs < 0 || wgs > 0x7fffffff) return fail(QG_E_INVALID, "%s: workgroup count %lld", who, (long long)wgs);
+    if (flags & ~1) return fail(QG_E_INVALID, "%s: unknown flags 0x%x", who, flags);
+    if (bytes < 1024) return QG_OK;
+    if ((st = check_ptr(who, "buf", buf, 16))) return st;
+    if ((st = check_ptr(who, "sink", sink, 4))) return st;
+    return launch_stream_read_shape(buf, bytes, waves_per_wg, kib_per_wave, wgs, flags, magic, sink,
+                                    static_cast<hipStream_t>(stream));
+}
+
 int qg_kv_cache_rows(int64_t n, int64_t hd, const float *x, uint16_t *scales, int8_t *codes, void *stream)
 {
     const char *who = "qg_kv_cache_rows";

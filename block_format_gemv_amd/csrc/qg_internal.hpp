@@ -68,6 +68,9 @@ int launch_gemm_mfma(int64_t rows, int64_t cols, int64_t ncol, const void *image
 // diagnostic: read `bytes` (a multiple of 1 KiB is read; the rest ignored) with the GEMV's
 // load pattern; sink[0] is written only if some lane's XOR of what it read equals magic
 int launch_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink, hipStream_t s);
+// diagnostic: the same in a chosen launch geometry (qg_stream_read_shape)
+int launch_stream_read_shape(const void *buf, size_t bytes, int waves_per_wg, int kib_per_wave, int64_t wgs,
+                             int flags, uint32_t magic, uint32_t *sink, hipStream_t s);
 int launch_kv_cache_rows(int64_t n, int64_t hd, const float *x, uint16_t *scales, int8_t *codes, hipStream_t s);
 int launch_kv_quantize_heads(int mode, int64_t nh, int64_t hd, const float *q, int8_t *codes, qg_act_scale *scales,
                              int32_t *err_flag, hipStream_t s);

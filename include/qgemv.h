@@ -203,9 +203,10 @@ int qg_quantize_gemv(int fmt, int mode, int64_t rows, int64_t cols, const void *
                      int8_t *codes, qg_act_scale *scales, int32_t *csums, int32_t *err_flag, float *out,
                      void *stream);
 
-/* qg_quantize_gemv plus the argmax of the output row ("Module numerics", Functions argmax:
- * the index of the largest element, the first of equals, +0 and -0 equal, a NaN passed
- * over, 0 when there is none): the greedy pick over an output projection's logits.
+/* qg_quantize_gemv plus the argmax of the output row, per "Module numerics", Functions argmax:
+ * the row holding the greatest output, the lowest such row when several hold equal values
+ * (+0 and -0 count as equal), NaN outputs skipped, and row 0 when every output is NaN.  It is
+ * the greedy pick over an output projection's logits.
  *   argmax_key  device uint64 [1], 8-byte aligned; must hold 0 before the call (the caller
  *               clears it).  Each workgroup folds its rows into it with an atomic max of a
  *               key whose order is the value's, then the lower row's; the result is
@@ -310,6 +311,19 @@ int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const 
  *          being optimised away (an all-zero buffer never writes a nonzero magic)
  * Honours qg_time_next_launch. */
 int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink, void *stream);
+
+/* Diagnostic, not part of the method: the same plain read of the first floor(bytes / 1024)
+ * KiB of buf in a chosen launch geometry, for a sweep of launch shapes:
+ *   waves_per_wg  1, 2, 4, 8 or 16 waves of 64 lanes per workgroup
+ *   kib_per_wave  1, 2, 4, 8, 9 or 16: contiguous 1 KiB chunks each wave reads per pass, all of
+ *                 a pass's loads issued before any is used (16 bytes per lane per chunk)
+ *   wgs           0: one pass, as many workgroups as the bytes need; > 0: that many
+ *                 workgroups in a grid-stride loop over the bytes
+ *   flags         bit 0: ordinary loads (default: non-temporal loads)
+ *   magic, sink   as qg_stream_read
+ * QG_E_INVALID for a value outside these sets.  Honours qg_time_next_launch. */
+int qg_stream_read_shape(const void *buf, size_t bytes, int waves_per_wg, int kib_per_wave, int64_t wgs, int flags,
+                         uint32_t magic, uint32_t *sink, void *stream);
 
 /* Speed-only tuning knobs; they never change output bits.
  *   QG_TUNE_WAVES_PER_WG  waves per GEMV workgroup, splitting a 64-row group's blocks:

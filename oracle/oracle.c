@@ -314,7 +314,8 @@ static int64_t rne_div(float x, int m, int e)
 
 int64_t or_rne_div(float x, int m, int e) { return rne_div(or_ftz(x), m, e); }
 
-/* [N] absmax: the largest magnitude, a denormal read as 0, folded from +0, NaN passed over. */
+/* [N] Functions absmax.  Scans for the greatest |x| starting from +0: each element is flushed
+ * first (a subnormal counts as zero) and NaNs are skipped, so an all-NaN block gives +0. */
 static float absmax(const float *x, int64_t n)
 {
     float a = 0.0f;
@@ -656,9 +657,10 @@ int or_sub_sums_q6k(int64_t rows, int64_t cols, const uint8_t *q, const int8_t *
     return OR_OK;
 }
 
-/* [N] argmax: the index of the largest element, the first of equals (+0 and -0 are equal),
- * a NaN passed over; 0 when there is none (every element NaN, or none at all).  A plain
- * left-to-right scan with binary32 comparisons. */
+/* [N] Functions argmax.  A left-to-right scan with binary32 comparisons that replaces the best
+ * position only on a strictly greater value, so the earliest of equal values wins (and +0
+ * ties with -0); NaNs are skipped; the result is 0 when nothing but NaNs (or nothing) is
+ * seen. */
 int64_t or_argmax(const float *x, int64_t n)
 {
     int64_t best = -1;
@@ -698,6 +700,8 @@ int64_t or_argmax(const float *x, int64_t n)
 /*      u_j = rne(w_j / 2^E), exact (a NaN gives 0); per value element the piece            */
 /*      R32(2^E * sum_j u_j v_j), the pieces added in block order (fadd).  A block holding   */
 /*      an infinite w_j, or a value row whose scale is not finite, gives NaN pieces.         */
+/*      The page does not print VALUE_BLOCK's value: 32 is a reading, and parity of the      */
+/*      weighted sum's block length is unpinned by the pages.                               */
 /* -------------------------------------------------------------------------------------- */
 
 #define OR_VALUE_BLOCK 32

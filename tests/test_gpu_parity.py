@@ -3,8 +3,8 @@
 Activation codes, scales and code sums are compared byte for byte; integer block sums
 exactly; every f32 output by its bits (compared as uint32, NaN canonical), never within a
 tolerance.  Shapes span several tiles with ragged tails; the named workloads run at full
-size in the launch configuration the benchmark times, with the oracle computing either
-every output or a seeded sample of rows.
+size in the launch configuration the benchmark times, every output of every repetition
+compared with the oracle's.
 """
 from __future__ import annotations
 
@@ -162,12 +162,15 @@ def test_quantize_infinity_raises_the_flag(qg):
         a = qg.quantize_act(dev(x), mode, err_flag=flag)
         torch.cuda.synchronize()
         assert int(flag.item()) == 1
+        with pytest.raises(qg.QGError) as ei:
+            qg.check(flag)
+        assert ei.value.status == qg.E_NONFINITE
         oc, om, oe, os_ = oracle.quantize(x, mode, check=False)
         m, e = a.scale_fields()
         assert np.array_equal(a.codes.cpu().numpy(), oc) and np.array_equal(m, om) and np.array_equal(e, oe)
     flag.zero_()
     qg.quantize_act(dev(gen.act_normal(1, 1024, 5)), 0, err_flag=flag)
-    torch.cuda.synchronize()
+    qg.check(flag)
     assert int(flag.item()) == 0
 
 
@@ -310,31 +313,38 @@ def llama(qg):
     return {k: Mat(qg, gen.llama_q4k(k)) for k in ("attn", "ffn")}
 
 
-def test_decode_workload_full_rows_and_1000_reps(qg, llama):
-    """Both Llama-8B-shaped matrices; repetition 0 compared on every row, all 1000
-    repetitions (fresh activations each) on a seeded sample of 48 rows."""
-    g = np.random.Generator(np.random.PCG64(2024))
+def test_decode_workload_every_row_all_1000_reps(qg, llama):
+    """Both Llama-8B-shaped matrices, 1000 repetitions with fresh activations each, every row
+    of every repetition against the oracle: the benchmark's one-launch step
+    (qg_quantize_gemv) and the two-launch path (qg_quantize_act, then qg_gemv_q); the
+    quantized rows of both paths (codes, scales and code sums) byte for byte too."""
+    reps = 1000
+    xs = np.concatenate([gen.decode_act(k) for k in range(reps)])
+    oc, om, oe, osum = oracle.quantize(xs, 0)
+    xd = dev(xs)
     for name, M in llama.items():
-        say("decode workload", name, M.rows, "x", M.cols)
-        out = torch.empty(M.rows, dtype=torch.float32, device=DEV)
-        xs = np.concatenate([gen.decode_act(k) for k in range(1000)])
-        oc, om, oe, _ = oracle.quantize(xs, 0)
-        xd = dev(xs)
-        sample = np.sort(g.choice(M.rows, 48, replace=False))
-        sub = gen.slice_rows(M.f, sample)
-        got = np.empty((1000, 48), np.float32)
-        act = qg.alloc_act(1, M.cols, 0)
-        for k in range(1000):
-            qg.quantize_act(xd[k:k + 1], 0, out=act)
-            run_gemv(qg, M, act, out=out)
-            if k == 0:
-                full = out.cpu().numpy()
-                assert np.array_equal(act.codes.cpu().numpy(), oc[:1])
-                want = oracle.gemv(M.f, oc[:1], om[:1], oe[:1], 0)
-                assert first_mismatch(full, want) is None, name
-            got[k] = out[torch.from_numpy(sample).to(DEV)].cpu().numpy()
-        want = oracle.gemm(sub, oc, om, oe, 0).reshape(1000, 48)
-        assert first_mismatch(got, want) is None, name
+        say("decode workload", name, M.rows, "x", M.cols, "reps", reps)
+        want = oracle.gemm(M.f, oc, om, oe, 0).reshape(reps, M.rows)
+        one = torch.empty((reps, M.rows), dtype=torch.float32, device=DEV)
+        two = torch.empty((reps, M.rows), dtype=torch.float32, device=DEV)
+        a1 = qg.alloc_act(reps, M.cols, 0)
+        a2 = qg.alloc_act(reps, M.cols, 0)
+        for k in range(reps):
+            ak1 = qg.Act(a1.codes[k:k + 1], a1.scales[k:k + 1], a1.csums[k:k + 1], 0)
+            ak2 = qg.Act(a2.codes[k:k + 1], a2.scales[k:k + 1], a2.csums[k:k + 1], 0)
+            qg.quantize_gemv(M.fmt, M.rows, M.cols, M.img, xd[k], 0, act=ak1, out=one[k])
+            qg.quantize_act(xd[k:k + 1], 0, out=ak2)
+            run_gemv(qg, M, ak2, out=two[k])
+        torch.cuda.synchronize()
+        for a in (a1, a2):
+            m, e = a.scale_fields()
+            assert np.array_equal(a.codes.cpu().numpy(), oc), name
+            assert np.array_equal(a.csums.cpu().numpy(), osum), name
+            assert np.array_equal(m.astype(np.int64), om.astype(np.int64)), name
+            assert np.array_equal(e.astype(np.int64), oe.astype(np.int64)), name
+        assert first_mismatch(one, want) is None, ("one launch", name)
+        assert first_mismatch(two, want) is None, ("two launches", name)
+        del one, two, a1, a2
 
 
 def test_output_projection_q6k_logits(qg):
@@ -350,44 +360,51 @@ def test_output_projection_q6k_logits(qg):
     torch.cuda.empty_cache()
 
 
-def test_sub32_workload_reps(qg, llama):
-    """Sub32 on the 14336x4096 matrix: repetition 0 on every row, 100 repetitions on a
-    sample of 64 rows; exponents of each row span -12..4."""
+def test_sub32_workload_every_row_100_reps(qg, llama):
+    """Sub32 on the 14336x4096 matrix, 100 repetitions (the exponents of each row span
+    -12..4), every row of every repetition against the oracle, for the one-launch step and
+    the two-launch path."""
     M = llama["ffn"]
-    g = np.random.Generator(np.random.PCG64(77))
-    sample = np.sort(g.choice(M.rows, 64, replace=False))
-    sub = gen.slice_rows(M.f, sample)
-    out = torch.empty(M.rows, dtype=torch.float32, device=DEV)
-    got, wants = [], []
-    for k in range(100):
-        x, t = gen.sub32_act(k)
-        act, c, m, e, _ = gpu_quant(qg, x, 1)
-        assert np.array_equal(e.astype(np.int32), t)
-        run_gemv(qg, M, act, out=out)
-        if k == 0:
-            want = oracle.gemv(M.f, c, m, e, 1)
-            assert first_mismatch(out, want) is None
-        got.append(out.cpu().numpy()[sample])
-        wants.append(oracle.gemv(sub, c, m, e, 1))
-    assert first_mismatch(np.stack(got), np.stack(wants)) is None
+    reps = 100
+    xs, ts = zip(*(gen.sub32_act(k) for k in range(reps)))
+    xs = np.concatenate(xs)
+    oc, om, oe, osum = oracle.quantize(xs, 1)
+    assert np.array_equal(oe.astype(np.int32), np.concatenate(ts).astype(np.int32))
+    say("oracle: Sub32 over", M.rows, "rows x", reps, "reps")
+    want = oracle.gemm(M.f, oc, om, oe, 1).reshape(reps, M.rows)
+    xd = dev(xs)
+    one = torch.empty((reps, M.rows), dtype=torch.float32, device=DEV)
+    two = torch.empty((reps, M.rows), dtype=torch.float32, device=DEV)
+    a1 = qg.alloc_act(reps, M.cols, 1)
+    a2 = qg.alloc_act(reps, M.cols, 1)
+    for k in range(reps):
+        ak1 = qg.Act(a1.codes[k:k + 1], a1.scales[k:k + 1], a1.csums[k:k + 1], 1)
+        ak2 = qg.Act(a2.codes[k:k + 1], a2.scales[k:k + 1], a2.csums[k:k + 1], 1)
+        qg.quantize_gemv(M.fmt, M.rows, M.cols, M.img, xd[k], 1, act=ak1, out=one[k])
+        qg.quantize_act(xd[k:k + 1], 1, out=ak2)
+        run_gemv(qg, M, ak2, out=two[k])
+    torch.cuda.synchronize()
+    for a in (a1, a2):
+        m, e = a.scale_fields()
+        assert np.array_equal(a.codes.cpu().numpy(), oc)
+        assert np.array_equal(a.csums.cpu().numpy(), osum)
+        assert np.array_equal(m.astype(np.int64), om.astype(np.int64))
+        assert np.array_equal(e.astype(np.int64), oe.astype(np.int64))
+    assert first_mismatch(one, want) is None, "one launch"
+    assert first_mismatch(two, want) is None, "two launches"
 
 
 @pytest.mark.parametrize("n", [2, 8, 64])
 def test_batched_columns(qg, llama, n):
+    """The batched workload on both matrices: every (r, c) against the oracle, and columns 0
+    and n-1 bit for bit equal to the GEMV of that column."""
     xs = gen.batch_act(n)
     for name, M in llama.items():
         say("gemm", name, "n", n)
         act, c, m, e, _ = gpu_quant(qg, xs, 0)
         out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
-        if name == "ffn" and n == 64:
-            g = np.random.Generator(np.random.PCG64(n))
-            sample = np.sort(g.choice(M.rows, 1024, replace=False))
-            want = oracle.gemm(gen.slice_rows(M.f, sample), c, m, e, 0).reshape(n, -1)
-            assert first_mismatch(out[:, torch.from_numpy(sample).to(DEV)], want) is None
-        else:
-            want = oracle.gemm(M.f, c, m, e, 0).reshape(n, M.rows)
-            assert first_mismatch(out, want) is None, (name, n)
-        # each column carries the GEMV's bits
+        want = oracle.gemm(M.f, c, m, e, 0).reshape(n, M.rows)
+        assert first_mismatch(out, want) is None, (name, n)
         one = qg.alloc_act(1, M.cols, 0)
         for k in (0, n - 1):
             one.codes.copy_(act.codes[k:k + 1])
@@ -664,24 +681,6 @@ def test_fused_launch_configuration_and_streams(qg):
     assert np.array_equal(bits(out), ref)
 
 
-def test_fused_decode_workload_matches_two_launches(qg, llama):
-    """The benchmark's step: fused and two-launch paths give the same bits on the
-    14336x4096 matrix for 50 fresh activation rows; row 0 checked against the oracle."""
-    M = llama["ffn"]
-    act = qg.alloc_act(1, M.cols, 0)
-    two = torch.empty(M.rows, dtype=torch.float32, device=DEV)
-    one = torch.empty(M.rows, dtype=torch.float32, device=DEV)
-    for k in range(50):
-        xd = dev(gen.decode_act(k).reshape(-1))
-        qg.quantize_act(xd[None], 0, out=act)
-        run_gemv(qg, M, act, out=two)
-        qg.quantize_gemv(M.fmt, M.rows, M.cols, M.img, xd, 0, out=one)
-        assert np.array_equal(bits(one), bits(two)), k
-        if k == 0:
-            oc, om, oe, _ = oracle.quantize(gen.decode_act(0), 0)
-            assert first_mismatch(one, oracle.gemv(M.f, oc, om, oe, 0)) is None
-
-
 def test_fused_infinity_flag_and_zero_rows(qg):
     f = gen.q4k_fields(100, 1024, 41)
     M = Mat(qg, f)
@@ -715,6 +714,26 @@ def test_stream_read_diagnostic(qg):
     qg.qg_stream_read(buf, buf.numel(), 0x1234, sink)
     torch.cuda.synchronize()
     assert int(sink.item()) == 0x1234
+
+
+@pytest.mark.parametrize("w,k,wgs,flags", [(16, 9, 0, 0), (4, 1, 0, 1), (8, 4, 3, 0), (1, 16, 2, 1)])
+def test_stream_read_shape_diagnostic(qg, w, k, wgs, flags):
+    """The launch-shape read: every shape reads every chunk (a magic planted in the last
+    chunk's first word, the rest zero, reaches the sink through the lane that reads it), and a
+    shape outside the documented sets is refused."""
+    nchunks = 9 * 7 + 5
+    buf = torch.zeros(nchunks * 1024 + 100, dtype=torch.uint8, device=DEV)
+    sink = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    qg.qg_stream_read_shape(buf, buf.numel(), w, k, wgs, flags, 0x1234, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == -1
+    off = (nchunks - 1) * 1024
+    buf[off:off + 4] = torch.tensor([0x34, 0x12, 0, 0], dtype=torch.uint8, device=DEV)
+    qg.qg_stream_read_shape(buf, buf.numel(), w, k, wgs, flags, 0x1234, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0x1234
+    with pytest.raises(qg.QGError):
+        qg.qg_stream_read_shape(buf, buf.numel(), w, 3, wgs, flags, 0x1234, sink)
 
 
 # --- several matrices sharing one activation row ------------------------------------------

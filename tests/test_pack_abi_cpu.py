@@ -308,3 +308,13 @@ def test_argmax_key_decoding():
     for row in (0, 1, 5, 14335, 128255, 2**31 - 1):
         key = (0x80000000 << 32) | (0xFFFFFFFF - row)
         assert qg.qg_argmax_index(key) == row
+
+
+def test_check_maps_the_nonfinite_flag():
+    """check(): a clear flag passes, a set one raises QG_E_NONFINITE (host flag: no device)."""
+    import torch
+    qg.check(torch.zeros(1, dtype=torch.int32))
+    qg.check(None)
+    with pytest.raises(qg.QGError) as ei:
+        qg.check(torch.ones(1, dtype=torch.int32))
+    assert ei.value.status == qg.E_NONFINITE
