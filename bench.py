@@ -149,7 +149,10 @@ def parse():
                    help="time the step as qg_quantize_act + qg_gemv_q instead of qg_quantize_gemv")
     p.add_argument("--tune", action="append", default=[], metavar="KEY=VALUE",
                    help="a speed-only tuning knob (qg_set_tuning): waves_per_wg, mfma_min_cols, mfma_col_tiles, "
-                        "mfma_form, mfma_ring_waves, cols_kernel, mfma_tables; output bits do not depend on them")
+                        "mfma_form, cols_kernel, mfma_tables, gemm_row_tiles; output bits do not depend on them")
+    p.add_argument("--kernel-only", type=int, default=0, metavar="K",
+                   help="only launch the step's dominant kernel K times (eager, over the rotated copies) and exit: "
+                        "for rocprofv3 counter passes")
     p.add_argument("--ceiling-sweep", action="store_true",
                    help="only sweep plain-read launch shapes (qg_stream_read_shape) and a library read kernel "
                         "(torch's amax) over the 4096x4096 and 14336x4096 Q4_K-style image sizes, cold; "
@@ -448,9 +451,12 @@ def main():
     elif ncol == 1:
         kernel_label = ("gemv1_kernel<..., SRC_F32> (one-launch quantize + GEMV)" if fused
                         else "gemv1_kernel<..., SRC_CODES> (GEMV of a quantized row)")
-    elif fmt_s == "q4k" and mode == 0 and ncol >= (tuned.get("mfma_min_cols") or 9):
-        kernel_label = "gemm_mfma_q4k (matrix cores, shared operands)" if ncol > 16 else \
-            "gemm_ring_q4k (matrix cores, LDS-DMA ring)"
+    elif fmt_s == "q4k" and mode == 0 and ncol >= (tuned.get("mfma_min_cols") or (2 if rows < 8192 else 5)):
+        # the library's choice of matrix-core form (qg_gemm_q, launch_gemm_mfma)
+        form = tuned.get("mfma_form") or (1 if cols <= 16 * 256 and ncol <= 16 else 3 if rows < 8192 else 2)
+        kernel_label = {1: "gemm_staged_q4k (matrix cores, columns staged in LDS, one block per wave)",
+                        2: "gemm_mfma_q4k (matrix cores, shared operands)",
+                        3: "gemm_split_q4k (matrix cores, one block per wave)"}[form]
     elif cols <= 16 * 256 and not tuned.get("cols_kernel") and fmt_s in ("q4k", "q6k"):
         kernel_label = "gemv1_cols_kernel (one-column machinery, up to 8 columns a wave)"
     else:
@@ -463,6 +469,14 @@ def main():
         algo_bytes = image_bytes + 4 * cols + act_bytes + out_bytes
     else:
         algo_bytes = image_bytes + act_bytes + out_bytes
+
+    if args.kernel_only:
+        torch.cuda.synchronize()
+        for i in range(args.kernel_only):
+            kernel_fn(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_only": args.kernel_only, "workload": args.workload, "kernel": kernel_label}), flush=True)
+        return
 
     # eager first pass, then a bitwise check of step 0 against the oracle on sampled rows
     torch.cuda.synchronize()

@@ -23,9 +23,10 @@ Q4K, Q6K, Q8_0, Q4_0 = 1, 2, 3, 4
 FORMATS = (Q4K, Q6K, Q8_0, Q4_0)
 PERBLOCK, SUB32 = 0, 1
 OK, E_INVALID, E_SHAPE, E_UNSUPPORTED, E_UNREADABLE, E_NONFINITE, E_RUNTIME = range(7)
-TUNE_WAVES_PER_WG, TUNE_MFMA_MIN_COLS, TUNE_MFMA_COL_TILES, TUNE_MFMA_FORM, TUNE_MFMA_RING_WAVES = 1, 2, 3, 4, 5
+TUNE_WAVES_PER_WG, TUNE_MFMA_MIN_COLS, TUNE_MFMA_COL_TILES, TUNE_MFMA_FORM = 1, 2, 3, 4
 TUNE_COLS_KERNEL = 6
 TUNE_MFMA_TABLES = 7
+TUNE_GEMM_ROW_TILES = 8
 BLOCK = 256
 MAX_COLS = 32768
 MAX_MATRICES = 8

@@ -18,7 +18,7 @@ namespace qg {
 namespace {
 thread_local char g_reason[512] = "";
 thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
-Tuning g_tuning = {0, 0, 0, 0, 0};
+thread_local Tuning g_tuning = {};   // per thread, as the reason string
 
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices];
@@ -144,11 +144,6 @@ int qg_set_tuning(int key, int64_t value)
         if (value > 3) return fail(QG_E_INVALID, "qg_set_tuning: form must be 0, 1, 2 or 3");
         g_tuning.mfma_form = (int)value;
         return QG_OK;
-    case QG_TUNE_MFMA_RING_WAVES:
-        if (value != 0 && value != 1 && value != 2 && value != 4)
-            return fail(QG_E_INVALID, "qg_set_tuning: ring waves per row quarter must be 0, 1, 2 or 4");
-        g_tuning.mfma_ring_waves = (int)value;
-        return QG_OK;
     case QG_TUNE_COLS_KERNEL:
         if (value > 1) return fail(QG_E_INVALID, "qg_set_tuning: the several-column kernel choice must be 0 or 1");
         g_tuning.cols_off = (int)value;
@@ -156,6 +151,11 @@ int qg_set_tuning(int key, int64_t value)
     case QG_TUNE_MFMA_TABLES:
         if (value > 1) return fail(QG_E_INVALID, "qg_set_tuning: the scale tables choice must be 0 or 1");
         g_tuning.mfma_pre_off = (int)value;
+        return QG_OK;
+    case QG_TUNE_GEMM_ROW_TILES:
+        if (value != 0 && value != 1 && value != 2 && value != 4)
+            return fail(QG_E_INVALID, "qg_set_tuning: row tiles must be 0, 1, 2 or 4");
+        g_tuning.gemm_row_tiles = (int)value;
         return QG_OK;
     default:
         return fail(QG_E_INVALID, "qg_set_tuning: unknown key %d", key);
@@ -200,7 +200,9 @@ static int gemm_common(const char *who, int fmt, int mode, int64_t rows, int64_t
     if ((st = check_ptr(who, "image", image, 16))) return st;
     if ((st = check_act(who, codes, scales, csums))) return st;
     if ((st = check_ptr(who, "out", out, 4))) return st;
-    const int min_cols = g_tuning.mfma_min_cols > 0 ? g_tuning.mfma_min_cols : 9;
+    // the matrix cores from 2 columns on fewer than 8192 rows, from 5 on more (below that the
+    // one-column machinery's workgroups already fill the chip and it is faster)
+    const int min_cols = g_tuning.mfma_min_cols > 0 ? g_tuning.mfma_min_cols : rows < 8192 ? 2 : 5;
     if (fmt == QG_Q4K && mode == QG_PERBLOCK && n >= min_cols)
         return launch_gemm_mfma(rows, cols, n, image, codes, scales, out, static_cast<hipStream_t>(stream));
     return launch_gemv(fmt, mode, rows, cols, n, image, codes, scales, csums, out, static_cast<hipStream_t>(stream));

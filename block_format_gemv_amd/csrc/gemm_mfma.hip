@@ -15,12 +15,18 @@
 // Operand roles: the MFMA's M dimension is 16 activation columns, N is 16 weight rows, so
 // lane l of a result owns weight row l%16 and activation columns 4*(l/16) .. +3.
 //
-// The shared-operand form (more than 16 columns): a workgroup owns one 64-row group and 16*CW
-// columns: wave (r, c) computes rows 16r..16r+15
-// against columns 16c..16c+15.  Per block the workgroup builds, once, the weight operands of
-// its 64 rows (wave (r, c) prepares the 64-element steps c, c+CW, .. of row quarter r) and the
-// activation operands of its columns in an LDS stage; every wave reads what it needs from
-// there.  Two stages alternate, and each thread's global loads run two blocks ahead.
+// Three forms, chosen by the shape (launch_gemm_mfma):
+//   - staged (at most 16 columns, rows of at most 16 blocks): the one-column GEMV's structure,
+//     every wave one block of a 16-, 32- or 64-row strip with all its loads issued at once,
+//     the activation codes brought into LDS by LDS-DMA, pieces folded after one barrier;
+//   - split (more columns on fewer rows, or longer rows): the same structure with the
+//     activation operands loaded per wave and rounds of 16 blocks;
+//   - shared operands (more columns on many rows): a workgroup owns one 64-row group and
+//     16*CW columns, wave (r, c) computes rows 16r..16r+15 against columns 16c..16c+15; per
+//     block the workgroup builds, once, the weight operands of its 64 rows (wave (r, c)
+//     prepares the 64-element steps c, c+CW, .. of row quarter r) and the activation operands
+//     of its columns in an LDS stage; every wave reads what it needs from there.  Two stages
+//     alternate, and each thread's global loads run two blocks ahead.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -358,222 +364,11 @@ int launch_cw(int64_t rows, int G, int64_t ncol, const void *image, const int8_t
     return launch_cw_typed<CW, false>(rows, G, ncol, image, codes, scales, out, s, stages);
 }
 
-template <int I>
-__device__ __forceinline__ uint32_t field_s(uint32_t y, uint32_t z, uint32_t w)
-{
-    if constexpr (I < 5) return (uint32_t)(((uint64_t)y | ((uint64_t)z << 32)) >> (12 * I)) & 0xFFFu;
-    else return (uint32_t)(((uint64_t)z | ((uint64_t)w << 32)) >> (12 * I - 32)) & 0xFFFu;
-}
-
-// The per-wave form, for fewer columns: each wave computes 16 rows x 16*CT columns over all
-// blocks from its own registers (weights and activation operands loaded per wave, two
-// register stages).  grid: x = 64-row group, y = batch of 16*CT activation columns; 4 waves,
-// wave w = rows 16w..16w+15
-template <int CT>
-__global__ __launch_bounds__(256) void gemm_mfma_wave(const uint8_t *__restrict__ image, int rows, int G,
-                                                     const int8_t *__restrict__ codes,
-                                                     const qg_act_scale *__restrict__ scales, int ncol,
-                                                     float *__restrict__ out)
-{
-    // LDS: [G][16*CT] activation scales as exact doubles m*2^e, then the same as
-    // qg_act_scale words (for the general combine)
-    extern __shared__ __align__(16) double s_S[];
-    constexpr int NCOLS = 16 * CT;
-    uint32_t *s_sc = reinterpret_cast<uint32_t *>(s_S + (size_t)G * NCOLS);
-    const int C = G * 256;
-    const int g = blockIdx.x;
-    const int colbase = blockIdx.y * NCOLS;
-    const int lane = threadIdx.x & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n = lane & 15;             // weight row within the wave's 16 rows
-    const int grp = lane >> 4;           // K group (16 of each 64-element step)
-    const int trow = 16 * wid + n;       // row within the 64-row tile
-    const int64_t row = (int64_t)g * 64 + trow;
-
-    const uint32_t *scw = reinterpret_cast<const uint32_t *>(scales);
-    for (int i = threadIdx.x; i < G * NCOLS; i += 256) {
-        const int b = i / NCOLS, j = i % NCOLS;
-        const int col = colbase + j;
-        const uint32_t w = col < ncol ? scw[(size_t)col * G + b] : 0u;
-        s_sc[i] = w;
-        s_S[i] = __builtin_ldexp((double)((w >> 16) & 0xFFu), (int)(int16_t)(w & 0xFFFFu));
-    }
-    __syncthreads();
-
-    float y[CT][4];
-#pragma unroll
-    for (int ct = 0; ct < CT; ct++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) y[ct][i] = 0.0f;
-
-    // one block's loads: this lane's row meta, its four 16-byte code chunks, and 16 bytes of
-    // activation codes per column tile and 64-element step
-    struct Stage {
-        uint4 meta;
-        uint4 ch[4];
-        v4i A[CT][4];
-    };
-    // per-lane bases; a block adds a uniform offset
-    const uint8_t *wbase = image + (size_t)g * G * kTileBytesQ4K + 16 * trow;
-    const uint8_t *mbase = wbase + 8192;
-    const uint8_t *cbase = wbase + 1024 * (grp >> 1);
-    const int8_t *abase[CT];
-    bool acol[CT];
-#pragma unroll
-    for (int ct = 0; ct < CT; ct++) {
-        const int col = colbase + 16 * ct + n;
-        acol[ct] = col < ncol;
-        abase[ct] = codes + (size_t)(acol[ct] ? col : 0) * C + 16 * grp;
-    }
-    auto load = [&](Stage &st, int b) {
-        const size_t toff = (size_t)b * kTileBytesQ4K;
-        st.meta = *reinterpret_cast<const uint4 *>(mbase + toff);
-#pragma unroll
-        for (int p = 0; p < 4; p++) st.ch[p] = *reinterpret_cast<const uint4 *>(cbase + toff + 2048 * p);
-#pragma unroll
-        for (int ct = 0; ct < CT; ct++) {
-#pragma unroll
-            for (int p = 0; p < 4; p++) {
-                const v4i v = *reinterpret_cast<const v4i *>(abase[ct] + (size_t)b * 256 + 64 * p);
-                st.A[ct][p] = acol[ct] ? v : v4i{0, 0, 0, 0};
-            }
-        }
-    };
-    auto compute = [&](const Stage &st, int b) {
-        const uint4 meta = st.meta;
-        uint32_t f[8];
-        f[0] = field_s<0>(meta.y, meta.z, meta.w);
-        f[1] = field_s<1>(meta.y, meta.z, meta.w);
-        f[2] = field_s<2>(meta.y, meta.z, meta.w);
-        f[3] = field_s<3>(meta.y, meta.z, meta.w);
-        f[4] = field_s<4>(meta.y, meta.z, meta.w);
-        f[5] = field_s<5>(meta.y, meta.z, meta.w);
-        f[6] = field_s<6>(meta.y, meta.z, meta.w);
-        f[7] = field_s<7>(meta.y, meta.z, meta.w);
-
-        v4i acc_h[CT], acc_l[CT], acc_o[CT];
-#pragma unroll
-        for (int ct = 0; ct < CT; ct++) acc_h[ct] = acc_l[ct] = acc_o[ct] = v4i{0, 0, 0, 0};
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-            // this lane's K group lies in sub-block 2p + grp/2, in the low or high nibbles
-            const uint32_t fsel = 0u - (uint32_t)(grp >> 1);            // all ones for the odd sub-block
-            const uint32_t fj = f[2 * p] ^ ((f[2 * p] ^ f[2 * p + 1]) & fsel);
-            const uint32_t sc = fj & 63u, hi = sc >> 3, lo = sc & 7u, mn = fj >> 6;
-            const int sh = 4 * (grp & 1);
-            const uint32_t q0 = (st.ch[p].x >> sh) & 0x0F0F0F0Fu, q1 = (st.ch[p].y >> sh) & 0x0F0F0F0Fu;
-            const uint32_t q2 = (st.ch[p].z >> sh) & 0x0F0F0F0Fu, q3 = (st.ch[p].w >> sh) & 0x0F0F0F0Fu;
-            const v4i Bh = {bytes_times(q0, hi), bytes_times(q1, hi), bytes_times(q2, hi), bytes_times(q3, hi)};
-            const v4i Bl = {bytes_times(q0, lo), bytes_times(q1, lo), bytes_times(q2, lo), bytes_times(q3, lo)};
-            const int mrep = (int)(mn * 0x01010101u);
-            const v4i Bo = {mrep, mrep, mrep, mrep};
-#pragma unroll
-            for (int ct = 0; ct < CT; ct++) {
-                acc_h[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.A[ct][p], Bh, acc_h[ct], 0, 0, 0);
-                acc_l[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.A[ct][p], Bl, acc_l[ct], 0, 0, 0);
-                acc_o[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.A[ct][p], Bo, acc_o[ct], 0, 0, 0);
-            }
-        }
-
-        // combine each (row, column) of this block once, then add it into the row's sum
-        const F16Scale d = f16_scale(meta.x & 0xFFFFu);
-        const F16Scale dm = f16_scale(meta.x >> 16);
-        const int gap = d.ex > dm.ex ? d.ex - dm.ex : dm.ex - d.ex;
-        const bool near = gap <= 8;
-        const double Dd = __builtin_ldexp((double)d.sig, d.ex);
-        const double Dm = __builtin_ldexp((double)dm.sig, dm.ex);
-        if (__all(near)) {
-            // every row of the wave takes the near-exponent combine: no per-lane branch
-#pragma unroll
-            for (int ct = 0; ct < CT; ct++) {
-                const double *S = s_S + b * NCOLS + 16 * ct + 4 * grp;
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int Cb = 8 * acc_h[ct][i] + acc_l[ct][i];
-                    y[ct][i] = fadd_ftz(y[ct][i], piece_q4k_perblock_near(Cb, acc_o[ct][i], Dd, Dm, S[i]));
-                }
-            }
-        } else {
-#pragma unroll
-            for (int ct = 0; ct < CT; ct++) {
-                const uint32_t *sv = s_sc + b * NCOLS + 16 * ct + 4 * grp;
-                const double *S = s_S + b * NCOLS + 16 * ct + 4 * grp;
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int Cb = 8 * acc_h[ct][i] + acc_l[ct][i];
-                    const int Ob = acc_o[ct][i];
-                    float piece;
-                    if (near) {
-                        piece = piece_q4k_perblock_near(Cb, Ob, Dd, Dm, S[i]);
-                    } else {
-                        const int m = (int)((sv[i] >> 16) & 0xFFu);
-                        const int e = (int)(int16_t)(sv[i] & 0xFFFFu);
-                        piece = piece_q4k_perblock(Cb, Ob, meta.x, m, e);
-                    }
-                    y[ct][i] = fadd_ftz(y[ct][i], piece);
-                }
-            }
-        }
-    };
-
-    // two register sets, no copies: the next block's loads are in flight during this block's work
-    Stage s0, s1;
-    load(s0, 0);
-    for (int b = 0; b < G; b += 2) {
-        if (b + 1 < G) load(s1, b + 1);
-        compute(s0, b);
-        if (b + 1 >= G) break;
-        if (b + 2 < G) load(s0, b + 2);
-        compute(s1, b + 1);
-    }
-
-    if (row < rows) {
-#pragma unroll
-        for (int ct = 0; ct < CT; ct++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int col = colbase + 16 * ct + 4 * grp + i;
-                if (col < ncol) out[(int64_t)col * rows + row] = canon_nan(y[ct][i]);
-            }
-    }
-}
-
-template <int CT>
-int launch_wave(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes, const qg_act_scale *scales,
-              float *out, hipStream_t s)
-{
-    const int64_t groups = (rows + 63) / 64;
-    const dim3 grid((unsigned)groups, (unsigned)((ncol + 16 * CT - 1) / (16 * CT)));
-    const size_t lds = (size_t)G * 16 * CT * (8 + 4);
-    hipEvent_t ev0, ev1;
-    take_timing_events(&ev0, &ev1);
-    if (ev0 && ev1)
-        hipExtLaunchKernelGGL(gemm_mfma_wave<CT>, grid, dim3(256), lds, s, ev0, ev1, 0,
-                              static_cast<const uint8_t *>(image), (int)rows, G, codes, scales, (int)ncol, out);
-    else
-        hipLaunchKernelGGL(gemm_mfma_wave<CT>, grid, dim3(256), lds, s, static_cast<const uint8_t *>(image), (int)rows,
-                           G, codes, scales, (int)ncol, out);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemm (matrix cores) launch: %s", hipGetErrorString(e));
-    return QG_OK;
-}
-
 // ---------------------------------------------------------------------------------------
-// The ring form.  A workgroup owns one 64-row group and 16*CT columns; with WH waves per row
-// quarter, wave w computes rows 16(w%4)..+15 against column tiles (w/4)*CT/WH .. +CT/WH-1,
-// from an LDS ring of D+1 slots.  Each slot holds one block:
-// the weight tile as it lies in the image, then the activation operands already in the order
-// the matrix cores read them (operand (ct, p) = 1 KiB: lane l <- column 16ct + l%16, bytes
-// 64p + 16(l/16) of the block).  The slots are filled by LDS-DMA loads (global_load_lds:
-// lane l's bytes land at the wave-uniform LDS base + size * l) issued D blocks ahead, so the
-// weight stream stays in flight without holding registers.  They are issued from inline
-// asm: the compiler would otherwise wait for every outstanding one before each LDS read.
-// The kernel waits for its own (s_waitcnt vmcnt with the exact count of younger loads) and
-// a barrier then covers every wave's.
-//
-// The epilogue adds each block's pieces into the row sums with plain binary32 adds while no
-// piece of the wave's rows is tiny (tiny_piece); a lane that meets one takes the exact
-// combine and the flushed add from then on, and with it its wave.
+// LDS-DMA: global_load_lds_dwordx4 moves 16 bytes per lane from global memory straight into
+// LDS (at a wave-uniform base + 16 * lane) without passing through registers.  It is issued from
+// inline asm (the compiler would otherwise wait for every outstanding one before each LDS
+// read); the kernel waits for its own (s_waitcnt vmcnt with the exact count of younger loads).
 
 __device__ __forceinline__ uint32_t lds_offset(const void *p)
 {
@@ -599,256 +394,484 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int CT, int D, int WH>
-struct Ring {
-    static constexpr int kWaves = 4 * WH;
-    static constexpr int kA = kTileBytesQ4K;                // activation operands after the tile
-    static constexpr int kSlot = kTileBytesQ4K + CT * 4 * 1024;
-    static constexpr int kSlots = D + 1;                   // the block being computed + D in flight
-    static constexpr int kRing = kSlots * kSlot;
-    // DMA loads per block: the tile's 9 chunks and 4*CT activation operands, dealt out to the
-    // waves in turn; every wave issues kDma (the last ones repeat chunk 8, so that every wave
-    // issues the same count and can wait for an exact one)
-    static constexpr int kLoads = 9 + 4 * CT;
-    static constexpr int kDma = (kLoads + kWaves - 1) / kWaves;
+// ---------------------------------------------------------------------------------------
+// The split form: the one-column GEMV's structure on the matrix cores.  A workgroup of 16
+// waves owns a strip of 16*RTT rows (inside one 64-row image group) and 16*CT activation
+// columns; wave w takes blocks w, w+16, ... (one round of 16 blocks at a time).  Every wave
+// issues all the loads of its block at once (its rows' code chunks and block fields in the
+// matrix cores' operand order, its columns' activation codes and scale words), so a launch
+// keeps the whole weight stream in flight as the GEMV does, with no barrier between loads
+// and use.  Per block the wave forms the three products per (16-row, 16-column) tile, combines
+// each (row, column) once and parks the piece in LDS; after the round's barrier the first
+// RTT*CT waves add each output's pieces in block order, four outputs per lane.
+//
+// grid: strips x column batches, laid out so that the batches of one strip go to the same
+// XCD (workgroups are dealt to the 8 XCDs in turn): x = (s/8 * nbatch + cb) * 8 + s%8, strips
+// padded to a multiple of 8 (the padding workgroups exit at once).
+
+template <int RTT, int CT>
+struct SplitLds {
+    static constexpr int kW = 16;                                // waves
+    static constexpr int kSlot = kW * RTT * CT * 1024;           // pieces of a round: [w][rt][ct][lane] x 4 floats
+    static constexpr int kScale = 16 * CT * 12;                  // per wave: doubles m*2^e, then the words
+    static constexpr int kFlags = 2 * kW;                        // per slot and wave: a tiny piece may occur
+    static size_t bytes(int rounds) { return (size_t)(rounds > 1 ? 2 : 1) * kSlot + (size_t)kW * kScale + kFlags; }
 };
 
-// PerBlock Q4_K-style piece from the activation scale as the exact double S = m*2^e:
-// R32(S * (d*C - dmin*O)), the same value as piece_q4k_perblock
-__device__ __forceinline__ float piece_q4k_perblock_s(int C, int O, uint32_t d_dmin, double S)
+template <int RTT, int CT>
+__global__ __launch_bounds__(1024) void gemm_split_q4k(const uint8_t *image, int rows, int G,
+                                                       const int8_t *__restrict__ codes,
+                                                       const uint32_t *__restrict__ scw, int ncol, int strips,
+                                                       int nbatch, float *__restrict__ out)
 {
-    const F16Scale d = f16_scale(d_dmin & 0xFFFFu);
-    const F16Scale dm = f16_scale(d_dmin >> 16);
-    const double a = __builtin_ldexp((double)C * (double)d.sig * S, d.ex);
-    const double b = __builtin_ldexp(-(double)O * (double)dm.sig * S, dm.ex);
-    return r32_sum2(a, b);
-}
-
-// grid: x = 64-row group, y = batch of 16*CT activation columns; 4*WH waves
-template <int CT, int D, int WH>
-__global__ __launch_bounds__(256 * WH) void gemm_ring_q4k(const uint8_t *__restrict__ image, int rows, int G,
-                                                          const int8_t *__restrict__ codes,
-                                                          const uint32_t *__restrict__ scw, int ncol,
-                                                          float *__restrict__ out)
-{
-    static_assert(D >= 2 && D <= 4, "ring depth");
-    static_assert(CT % WH == 0, "whole column tiles per wave");
-    using Rg = Ring<CT, D, WH>;
+    using L = SplitLds<RTT, CT>;
+    constexpr int W = L::kW;
     constexpr int NC = 16 * CT;
-    constexpr int NW = Rg::kWaves;
-    constexpr int CTW = CT / WH;                       // column tiles per wave
-    constexpr int K = Rg::kDma;
     extern __shared__ __align__(16) unsigned char lds[];
-    double *s_S = reinterpret_cast<double *>(lds + Rg::kRing);     // [G][NC] activation scales m*2^e
+    const int x = (int)blockIdx.x;
+    const int qx = x >> 3;
+    const int cb = qx % nbatch;
+    const int s = (qx / nbatch) * 8 + (x & 7);
+    if (s >= strips) return;                   // padding workgroup: the whole group leaves at once
+    constexpr int SPG = 4 / RTT;               // strips per 64-row group
+    const int g = s / SPG;
+    const int qr0 = (s % SPG) * RTT;           // first 16-row quarter of the strip within the group
+    const int colbase = cb * NC;
     const int C = G * 256;
-    const int g = blockIdx.x;
-    const int colbase = blockIdx.y * NC;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, grp = lane >> 4;
-    const int trow = 16 * (wid & 3) + n;               // row within the 64-row group
-    const int ct0 = (wid >> 2) * CTW;                  // this wave's first column tile
+    const int rounds = (G + W - 1) / W;
+    unsigned char *slots = lds;
+    unsigned char *wscale = lds + (size_t)(rounds > 1 ? 2 : 1) * L::kSlot + (size_t)wid * L::kScale;
+    double *sS = reinterpret_cast<double *>(wscale);
+    uint32_t *sW = reinterpret_cast<uint32_t *>(wscale + NC * 8);
+    unsigned char *flags = lds + (size_t)(rounds > 1 ? 2 : 1) * L::kSlot + (size_t)W * L::kScale;
+
+    // the folding threads: RTT*CT waves, lane l of fold wave u = (rt, ct) owns the four outputs
+    // (row 16(qr0+rt) + l%16, columns 16ct + 4(l/16) .. +3)
+    const bool folder = wid < RTT * CT;
+    float4 y = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+
     const uint8_t *gbase = image + (size_t)g * G * kTileBytesQ4K;
-
-    // the scale table first: its loads are waited for by the compiler, which would also wait
-    // for any DMA issued before them
-    for (int i = threadIdx.x; i < G * NC; i += 64 * NW) {
-        const int b = i / NC, col = colbase + i % NC;
-        const uint32_t w = col < ncol ? scw[(size_t)col * G + b] : 0u;
-        s_S[i] = __builtin_ldexp((double)((w >> 16) & 0xFFu), (int)(int16_t)(w & 0xFFFFu));
-    }
-
-    auto issue = [&](int b) {
-        unsigned char *slot = lds + (b % Rg::kSlots) * Rg::kSlot;
-        const uint8_t *tile = gbase + (size_t)b * kTileBytesQ4K;
+    for (int r = 0; r < rounds; r++) {
+        const int b = r * W + wid;
+        unsigned char *slot = slots + (size_t)(rounds > 1 ? (r & 1) : 0) * L::kSlot;
+        if (b < G) {
+            // ---- loads: all of the block's, issued before any is used
+            const uint8_t *tile = gbase + (size_t)b * kTileBytesQ4K;
+            uint4 ch[RTT][4], meta[RTT];
 #pragma unroll
-        for (int j = 0; j < K; j++) {
-            const int i = wid + NW * j;                 // this wave's j-th load of the block
-            if (i < 9 || i >= Rg::kLoads) {
-                const int ch = min(i, 8);
-                dma16(tile + 1024 * ch + 16 * lane, lds_offset(slot + 1024 * ch));
-            } else {
-                const int k = i - 9;                    // operand (ct, p) = (k / 4, k % 4)
-                const int col = min(colbase + 16 * (k >> 2) + n, ncol - 1);
-                dma16(codes + (size_t)col * C + (size_t)b * 256 + 64 * (k & 3) + 16 * grp,
-                      lds_offset(slot + Rg::kA + 1024 * k));
+            for (int rt = 0; rt < RTT; rt++) {
+                const int trow = 16 * (qr0 + rt) + n;
+                meta[rt] = ld16(tile + 8192 + 16 * trow);
+#pragma unroll
+                for (int st = 0; st < 4; st++) ch[rt][st] = ld16(tile + 1024 * (2 * st + (grp >> 1)) + 16 * trow);
             }
-        }
-    };
-    // own loads of the block after the one waited for still outstanding: nb blocks' worth
-    // (nb < D; an exact count, so that the wait ends as soon as that block has landed)
-    auto wait_blocks_after = [&](int nb) {
-        if (nb >= 3) wait_vm<3 * K>();
-        else if (nb == 2) wait_vm<2 * K>();
-        else if (nb == 1) wait_vm<K>();
-        else wait_vm<0>();
-    };
-
-    const int pre = min(D, G);
-    for (int b = 0; b < pre; b++) issue(b);
-    wait_blocks_after(pre - 1);
-    __syncthreads();
-
-    float y[CTW][4];
+            v4i A[CT][4];
 #pragma unroll
-    for (int ct = 0; ct < CTW; ct++)
+            for (int ct = 0; ct < CT; ct++) {
+                const int col = min(colbase + 16 * ct + n, ncol - 1);
+                const int8_t *ab = codes + (size_t)col * C + (size_t)b * 256 + 16 * grp;
 #pragma unroll
-        for (int i = 0; i < 4; i++) y[ct][i] = 0.0f;
-    bool tainted = false;     // this lane's row has met a tiny piece
-
-    for (int b = 0; b < G; b++) {
-        if (b + D < G) issue(b + D);
-        const unsigned char *slot = lds + (b % Rg::kSlots) * Rg::kSlot;
-        const uint4 meta = *reinterpret_cast<const uint4 *>(slot + 8192 + 16 * trow);
-        uint32_t f[8];
-        f[0] = field_s<0>(meta.y, meta.z, meta.w);
-        f[1] = field_s<1>(meta.y, meta.z, meta.w);
-        f[2] = field_s<2>(meta.y, meta.z, meta.w);
-        f[3] = field_s<3>(meta.y, meta.z, meta.w);
-        f[4] = field_s<4>(meta.y, meta.z, meta.w);
-        f[5] = field_s<5>(meta.y, meta.z, meta.w);
-        f[6] = field_s<6>(meta.y, meta.z, meta.w);
-        f[7] = field_s<7>(meta.y, meta.z, meta.w);
-
-        v4i acc_h[CTW], acc_l[CTW], acc_o[CTW];
-#pragma unroll
-        for (int ct = 0; ct < CTW; ct++) acc_h[ct] = acc_l[ct] = acc_o[ct] = v4i{0, 0, 0, 0};
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-            // this lane's K group lies in sub-block 2p + grp/2, in the low or high nibbles
-            const uint32_t fsel = 0u - (uint32_t)(grp >> 1);
-            const uint32_t fj = f[2 * p] ^ ((f[2 * p] ^ f[2 * p + 1]) & fsel);
-            const uint32_t sc = fj & 63u, hi = sc >> 3, lo = sc & 7u, mn = fj >> 6;
-            const uint4 ch = *reinterpret_cast<const uint4 *>(slot + 1024 * (2 * p + (grp >> 1)) + 16 * trow);
-            const int sh = 4 * (grp & 1);
-            const uint32_t q0 = (ch.x >> sh) & 0x0F0F0F0Fu, q1 = (ch.y >> sh) & 0x0F0F0F0Fu;
-            const uint32_t q2 = (ch.z >> sh) & 0x0F0F0F0Fu, q3 = (ch.w >> sh) & 0x0F0F0F0Fu;
-            const v4i Bh = {bytes_times(q0, hi), bytes_times(q1, hi), bytes_times(q2, hi), bytes_times(q3, hi)};
-            const v4i Bl = {bytes_times(q0, lo), bytes_times(q1, lo), bytes_times(q2, lo), bytes_times(q3, lo)};
-            const int mrep = (int)(mn * 0x01010101u);
-            const v4i Bo = {mrep, mrep, mrep, mrep};
-#pragma unroll
-            for (int ct = 0; ct < CTW; ct++) {
-                const v4i A = *reinterpret_cast<const v4i *>(slot + Rg::kA + 1024 * (4 * (ct0 + ct) + p) + 16 * lane);
-                acc_h[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bh, acc_h[ct], 0, 0, 0);
-                acc_l[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bl, acc_l[ct], 0, 0, 0);
-                acc_o[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bo, acc_o[ct], 0, 0, 0);
+                for (int st = 0; st < 4; st++) A[ct][st] = *reinterpret_cast<const v4i *>(ab + 64 * st);
             }
-        }
+            // this block's activation scales: lane j < NC loads column colbase + j's word
+            const uint32_t w = scw[(size_t)min(colbase + min(lane, NC - 1), ncol - 1) * G + b];
+            if (lane < NC) {
+                sW[lane] = w;
+                sS[lane] = __builtin_ldexp((double)((w >> 16) & 0xFFu), (int)(int16_t)(w & 0xFFFFu));
+            }
+            const bool tiny_col = lane < NC && (int)(int16_t)(w & 0xFFFFu) < kNoTinyExp;
+            const bool tiny = __any(tiny_col);   // a piece of this block may be tiny: flushed combine and fold
 
-        // combine each (row, column) of the block once, then add it into the row's sum
-        const float fd = f16_value(meta.x), fm = f16_value(meta.x >> 16);
-        const bool near = q4k_near(fd, fm);
-        const double Dd = (double)fd, Dm = (double)fm;
-        const double *S = s_S + (size_t)b * NC + 16 * ct0 + 4 * grp;
-        bool fast = false;
-        if (__all(near) && !__any(tainted)) {
-            float pc[CTW][4];
-            int lo = 0;
+            // ---- per row tile: weight operands, products, combine
 #pragma unroll
-            for (int ct = 0; ct < CTW; ct++)
+            for (int rt = 0; rt < RTT; rt++) {
+                // the lane's four sub-block fields: sub-block 2st + grp/2, 12 bits at 12(2st + grp/2)
+                // of the 96-bit string; shifting the string by 12(grp/2) puts them at 24st
+                const uint32_t sh = 12u * (uint32_t)(grp >> 1);
+                const uint64_t lo64 = ((uint64_t)meta[rt].z << 32 | meta[rt].y) >> sh;
+                const uint32_t y0 = (uint32_t)lo64;
+                const uint32_t y1 = (uint32_t)(((uint64_t)meta[rt].w << 32 | meta[rt].z) >> sh);
+                const uint32_t y2 = meta[rt].w >> sh;
+                const uint32_t fs[4] = {y0 & 0xFFFu, (uint32_t)(lo64 >> 24) & 0xFFFu, (y1 >> 16) & 0xFFFu,
+                                        (y2 >> 8) & 0xFFFu};
+                v4i acc_h[CT], acc_l[CT], acc_o[CT];
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int Cb = 8 * acc_h[ct][i] + acc_l[ct][i];
-                    const double X = __builtin_fma((double)Cb, Dd, -((double)acc_o[ct][i] * Dm));
-                    pc[ct][i] = (float)(X * S[16 * ct + i]);
-                    lo = min(lo, __builtin_amdgcn_frexp_expf(pc[ct][i]));
+                for (int ct = 0; ct < CT; ct++) acc_h[ct] = acc_l[ct] = acc_o[ct] = v4i{0, 0, 0, 0};
+#pragma unroll
+                for (int st = 0; st < 4; st++) {
+                    const uint32_t f = fs[st];
+                    const uint32_t hi = (f >> 3) & 7u, lo = f & 7u, mn = f >> 6;
+                    const int shq = 4 * (grp & 1);   // low nibbles: elements 0..15, high: 16..31
+                    const uint4 c4 = ch[rt][st];
+                    const uint32_t q0 = (c4.x >> shq) & 0x0F0F0F0Fu, q1 = (c4.y >> shq) & 0x0F0F0F0Fu;
+                    const uint32_t q2 = (c4.z >> shq) & 0x0F0F0F0Fu, q3 = (c4.w >> shq) & 0x0F0F0F0Fu;
+                    const v4i Bh = {bytes_times(q0, hi), bytes_times(q1, hi), bytes_times(q2, hi), bytes_times(q3, hi)};
+                    const v4i Bl = {bytes_times(q0, lo), bytes_times(q1, lo), bytes_times(q2, lo), bytes_times(q3, lo)};
+                    const int mrep = (int)(mn * 0x01010101u);
+                    const v4i Bo = {mrep, mrep, mrep, mrep};
+#pragma unroll
+                    for (int ct = 0; ct < CT; ct++) {
+                        acc_h[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[ct][st], Bh, acc_h[ct], 0, 0, 0);
+                        acc_l[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[ct][st], Bl, acc_l[ct], 0, 0, 0);
+                        acc_o[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[ct][st], Bo, acc_o[ct], 0, 0, 0);
+                    }
                 }
-            if (!__any(lo <= -102)) {
-                // no tiny piece: every piece is zero or normal, and no partial sum can be
-                // subnormal (nor -0), so plain adds give the flushed adds' bits
-                fast = true;
+                // combine each (row, column) once ("Module numerics", module description: the
+                // block's terms summed exactly and rounded once)
+                const uint32_t dd = meta[rt].x;
+                const float fd = f16_value(dd), fm = f16_value(dd >> 16);
+                const bool near = q4k_near(fd, fm);
+                const double Dd = (double)fd, Dm = (double)fm;
 #pragma unroll
-                for (int ct = 0; ct < CTW; ct++)
+                for (int ct = 0; ct < CT; ct++) {
+                    const double *S = sS + 16 * ct + 4 * grp;
+                    float p[4];
+                    if (__all(near) && !tiny) {
+                        // no piece is tiny: the conversion needs no flush, + 0 turns an exact -0 into +0
 #pragma unroll
-                    for (int i = 0; i < 4; i++) y[ct][i] = y[ct][i] + pc[ct][i];
-            }
-        }
-        if (!fast) {
+                        for (int i = 0; i < 4; i++) {
+                            const int Cb = 8 * acc_h[ct][i] + acc_l[ct][i];
+                            const double X = __builtin_fma((double)Cb, Dd, -((double)acc_o[ct][i] * Dm));
+                            p[i] = (float)(X * S[i]) + 0.0f;
+                        }
+                    } else {
+                        const uint32_t *Wd = sW + 16 * ct + 4 * grp;
 #pragma unroll
-            for (int ct = 0; ct < CTW; ct++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int Cb = 8 * acc_h[ct][i] + acc_l[ct][i];
-                    const int Ob = acc_o[ct][i];
-                    const float piece = near ? piece_q4k_perblock_near(Cb, Ob, Dd, Dm, S[16 * ct + i])
-                                             : piece_q4k_perblock_s(Cb, Ob, meta.x, S[16 * ct + i]);
-                    tainted |= tiny_piece(piece);
-                    y[ct][i] = fadd_ftz(y[ct][i], piece);
+                        for (int i = 0; i < 4; i++) {
+                            const int Cb = 8 * acc_h[ct][i] + acc_l[ct][i];
+                            const int Ob = acc_o[ct][i];
+                            if (near) {
+                                p[i] = piece_q4k_perblock_near(Cb, Ob, Dd, Dm, S[i]);
+                            } else {
+                                const int m = (int)((Wd[i] >> 16) & 0xFFu);
+                                const int e = (int)(int16_t)(Wd[i] & 0xFFFFu);
+                                p[i] = piece_q4k_perblock(Cb, Ob, dd, m, e);
+                            }
+                        }
+                    }
+                    reinterpret_cast<float4 *>(slot)[((wid * RTT + rt) * CT + ct) * 64 + lane] =
+                        make_float4(p[0], p[1], p[2], p[3]);
                 }
+            }
+            if (lane == 0) flags[(r & 1) * W + wid] = tiny ? 1 : 0;
         }
-
-        if (b + 1 < G) wait_blocks_after(min(b + D, G - 1) - (b + 1));
         __syncthreads();
+        if (folder) {
+            // add the round's pieces in block order, plain adds unless one of them may be tiny
+            const int nb = min(W, G - r * W);
+            bool flush = false;
+            for (int k = 0; k < nb; k++) flush |= flags[(r & 1) * W + k] != 0;
+            const float4 *pc = reinterpret_cast<const float4 *>(slot) + (size_t)wid * 64 + lane;
+            const size_t stride = (size_t)RTT * CT * 64;
+            if (flush) {
+                for (int k = 0; k < nb; k++) {
+                    const float4 q = pc[k * stride];
+                    y.x = fadd_ftz(y.x, q.x);
+                    y.y = fadd_ftz(y.y, q.y);
+                    y.z = fadd_ftz(y.z, q.z);
+                    y.w = fadd_ftz(y.w, q.w);
+                }
+            } else if (nb == W) {
+                float4 q[W];
+#pragma unroll
+                for (int k = 0; k < W; k++) q[k] = pc[k * stride];
+#pragma unroll
+                for (int k = 0; k < W; k++) {
+                    y.x = y.x + q[k].x;
+                    y.y = y.y + q[k].y;
+                    y.z = y.z + q[k].z;
+                    y.w = y.w + q[k].w;
+                }
+            } else {
+                for (int k = 0; k < nb; k++) {
+                    const float4 q = pc[k * stride];
+                    y.x = y.x + q.x;
+                    y.y = y.y + q.y;
+                    y.z = y.z + q.z;
+                    y.w = y.w + q.w;
+                }
+            }
+        }
     }
 
-    const int64_t row = (int64_t)g * 64 + trow;
-    if (row < rows) {
-#pragma unroll
-        for (int ct = 0; ct < CTW; ct++)
+    if (folder) {
+        const int rt = wid / CT, ct = wid % CT;
+        const int64_t row = (int64_t)g * 64 + 16 * (qr0 + rt) + n;
+        if (row < rows) {
+            const float v[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int col = colbase + 16 * (ct0 + ct) + 4 * grp + i;
-                if (col < ncol) out[(int64_t)col * rows + row] = canon_nan(y[ct][i]);
+                const int col = colbase + 16 * ct + 4 * grp + i;
+                if (col < ncol) out[(int64_t)col * rows + row] = canon_nan(v[i]);
             }
+        }
     }
 }
 
-template <int CT, int D>
-size_t ring_lds(int G)
+template <int RTT, int CT>
+int launch_split_typed(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
+                       const qg_act_scale *scales, float *out, hipStream_t s)
 {
-    return (size_t)Ring<CT, D, 1>::kRing + (size_t)G * 16 * CT * sizeof(double);
-}
-
-template <int CT, int D, int WH>
-int launch_ring_typed(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
-                      const qg_act_scale *scales, float *out, hipStream_t s)
-{
+    using L = SplitLds<RTT, CT>;
     const int64_t groups = (rows + 63) / 64;
-    const dim3 grid((unsigned)groups, (unsigned)((ncol + 16 * CT - 1) / (16 * CT)));
-    const size_t lds = ring_lds<CT, D>(G);
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_ring_q4k<CT, D, WH>),
+    const int64_t strips = groups * (4 / RTT);
+    const int64_t nbatch = (ncol + 16 * CT - 1) / (16 * CT);
+    const int64_t grid = (strips + 7) / 8 * 8 * nbatch;
+    if (grid > 0x7fffffff) return fail(QG_E_SHAPE, "gemm: %lld rows x %lld columns is too many", (long long)rows,
+                                       (long long)ncol);
+    const int rounds = (G + L::kW - 1) / L::kW;
+    const size_t lds = L::bytes(rounds);
+    if (lds > (size_t)kMaxLds) return QG_E_UNSUPPORTED;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_split_q4k<RTT, CT>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     (void)attr;   // a refusal shows up as a launch error below
     const uint32_t *w = reinterpret_cast<const uint32_t *>(scales);
     hipEvent_t ev0, ev1;
     take_timing_events(&ev0, &ev1);
     if (ev0 && ev1)
-        hipExtLaunchKernelGGL((gemm_ring_q4k<CT, D, WH>), grid, dim3(256 * WH), lds, s, ev0, ev1, 0,
-                              static_cast<const uint8_t *>(image), (int)rows, G, codes, w, (int)ncol, out);
+        hipExtLaunchKernelGGL((gemm_split_q4k<RTT, CT>), dim3((unsigned)grid), dim3(1024), lds, s, ev0, ev1, 0,
+                              static_cast<const uint8_t *>(image), (int)rows, G, codes, w, (int)ncol, (int)strips,
+                              (int)nbatch, out);
     else
-        hipLaunchKernelGGL((gemm_ring_q4k<CT, D, WH>), grid, dim3(256 * WH), lds, s, static_cast<const uint8_t *>(image),
-                           (int)rows, G, codes, w, (int)ncol, out);
+        hipLaunchKernelGGL((gemm_split_q4k<RTT, CT>), dim3((unsigned)grid), dim3(1024), lds, s,
+                           static_cast<const uint8_t *>(image), (int)rows, G, codes, w, (int)ncol, (int)strips,
+                           (int)nbatch, out);
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemm (matrix cores, ring) launch: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemm (matrix cores, split) launch: %s", hipGetErrorString(e));
     return QG_OK;
 }
 
-// the deepest ring that fits the LDS of a workgroup, or QG_E_UNSUPPORTED
-template <int CT, int WH>
-int launch_ring_d(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
-                  const qg_act_scale *scales, float *out, hipStream_t s)
+// ---------------------------------------------------------------------------------------
+// The staged form (at most 16 columns, rows of at most 16 blocks): the split form's workgroup
+// (16 waves, wave w takes block w for the strip's 16*RTT rows) with the activation codes of its
+// columns staged in LDS.  A column's codes of four consecutive blocks are 1 KiB contiguous, so
+// each wave brings those of its own block's group of four with one LDS-DMA instruction per
+// column (each column's row padded by 16 bytes in LDS, so that the 16 lanes of an operand read,
+// one per column, fall in different banks), issued before its weights, and waits for its own
+// loads only: the four waves of a group write the same bytes to the same place.  Weights load
+// straight into registers, each lane 8 bytes of one code chunk per 64-element step (the K
+// order of the tile form).
+//
+// LDS: the codes [nc][C + 16] (nc = the columns, at most 16), the pieces [16 waves][RTT][64
+// lanes] x 4 floats, the waves' scale tables, the tiny-piece flags.
+
+template <int RTT>
+struct StagedLds {
+    // nc = the columns staged (at most 16)
+    __host__ __device__ static size_t codes(int C, int nc) { return (size_t)nc * (C + 16); }
+    static constexpr int kPieces = 16 * RTT * 1024;
+    static constexpr int kScale = 16 * 12;
+    __host__ __device__ static size_t bytes(int C, int nc) { return codes(C, nc) + kPieces + 16 * (size_t)kScale + 16; }
+};
+
+template <int RTT>
+__global__ __launch_bounds__(1024) void gemm_staged_q4k(const uint8_t *image, int rows, int G,
+                                                        const int8_t *__restrict__ codes,
+                                                        const uint32_t *__restrict__ scw, int ncol, int strips,
+                                                        float *__restrict__ out)
 {
-    if (ring_lds<CT, 4>(G) <= (size_t)kMaxLds)
-        return launch_ring_typed<CT, 4, WH>(rows, G, ncol, image, codes, scales, out, s);
-    if (ring_lds<CT, 3>(G) <= (size_t)kMaxLds)
-        return launch_ring_typed<CT, 3, WH>(rows, G, ncol, image, codes, scales, out, s);
-    if (ring_lds<CT, 2>(G) <= (size_t)kMaxLds)
-        return launch_ring_typed<CT, 2, WH>(rows, G, ncol, image, codes, scales, out, s);
-    return QG_E_UNSUPPORTED;
+    using L = StagedLds<RTT>;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int s = (int)blockIdx.x;
+    constexpr int SPG = 4 / RTT;               // strips per 64-row group
+    const int g = s / SPG;
+    const int qr0 = (s % SPG) * RTT;
+    const int C = G * 256, cs = C + 16;
+    const int nc = min(ncol, 16);
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, grp = lane >> 4, h = grp & 1, jo = grp >> 1;
+    const int b = min(wid, G - 1);             // a wave past the last block works on a copy and parks nothing
+    const bool live = wid < G;
+    unsigned char *acodes = lds;
+    float *pieces = reinterpret_cast<float *>(lds + L::codes(C, nc));
+    unsigned char *wscale = lds + L::codes(C, nc) + L::kPieces + (size_t)wid * L::kScale;
+    double *sS = reinterpret_cast<double *>(wscale);
+    uint32_t *sW = reinterpret_cast<uint32_t *>(wscale + 16 * 8);
+    unsigned char *flags = lds + L::codes(C, nc) + L::kPieces + 16 * (size_t)L::kScale;
+
+    // the columns' codes of this wave's group of four blocks (gq = b / 4) into LDS: one DMA
+    // instruction per column, 16 bytes per lane (lane l: block 4gq + l/16).  The four waves of
+    // a group bring the same bytes to the same place, so each wave only waits for its own loads.
+    const int gq = b >> 2;
+    for (int c = 0; c < nc; c++) {
+        if (4 * gq + (lane >> 4) < G)
+            dma16(codes + (size_t)c * C + 1024 * gq + 16 * lane, lds_offset(acodes + (size_t)c * cs + 1024 * gq));
+    }
+    // the block's weights: lane (n, grp) reads row 16(qr0 + rt) + n, 8 bytes at 8h of code chunk
+    // 2st + jo for each step st, and the row's block fields
+    const uint8_t *tile = image + ((size_t)g * G + b) * kTileBytesQ4K;
+    uint2 ch[RTT][4];
+    uint4 meta[RTT];
+#pragma unroll
+    for (int rt = 0; rt < RTT; rt++) {
+        const int trow = 16 * (qr0 + rt) + n;
+        meta[rt] = ld16(tile + 8192 + 16 * trow);
+#pragma unroll
+        for (int st = 0; st < 4; st++)
+            ch[rt][st] = *reinterpret_cast<const uint2 *>(tile + 1024 * (2 * st + jo) + 16 * trow + 8 * h);
+    }
+    const uint32_t w = scw[(size_t)min(lane & 15, ncol - 1) * G + b];
+    // the DMA loads were issued first: waiting for at most 5*RTT + 1 younger loads leaves them done
+    wait_vm<5 * RTT + 1>();
+
+    if (lane < 16) {
+        sW[lane] = w;
+        sS[lane] = __builtin_ldexp((double)((w >> 16) & 0xFFu), (int)(int16_t)(w & 0xFFFFu));
+    }
+    const bool tiny = __any(lane < 16 && (int)(int16_t)(w & 0xFFFFu) < kNoTinyExp);
+    // this lane's activation operand of step st: codes of column n (past the last column, a
+    // copy of it: computed and dropped), elements 32(2st + jo) + 8h .. +7 and +16 .. +23 of block b
+    const unsigned char *arow = acodes + (size_t)min(n, nc - 1) * cs + (size_t)b * 256 + 32 * jo + 8 * h;
+#pragma unroll
+    for (int rt = 0; rt < RTT; rt++) {
+        const uint32_t sh = 12u * (uint32_t)jo;
+        const uint64_t lo64 = ((uint64_t)meta[rt].z << 32 | meta[rt].y) >> sh;
+        const uint32_t y1 = (uint32_t)(((uint64_t)meta[rt].w << 32 | meta[rt].z) >> sh);
+        const uint32_t y2 = meta[rt].w >> sh;
+        const uint32_t fs[4] = {(uint32_t)lo64 & 0xFFFu, (uint32_t)(lo64 >> 24) & 0xFFFu, (y1 >> 16) & 0xFFFu,
+                                (y2 >> 8) & 0xFFFu};
+        v4i ah = {0, 0, 0, 0}, al = {0, 0, 0, 0}, ao = {0, 0, 0, 0};
+#pragma unroll
+        for (int st = 0; st < 4; st++) {
+            const uint2 lo8 = *reinterpret_cast<const uint2 *>(arow + 64 * st);
+            const uint2 hi8 = *reinterpret_cast<const uint2 *>(arow + 64 * st + 16);
+            const v4i A = {(int)lo8.x, (int)lo8.y, (int)hi8.x, (int)hi8.y};
+            const uint32_t f = fs[st];
+            const uint32_t hi = (f >> 3) & 7u, lo = f & 7u;
+            const int mr = (int)__builtin_amdgcn_perm(0u, f >> 6, 0x00000000u);   // mn (< 64) in every byte
+            const uint2 c2 = ch[rt][st];
+            const uint32_t q0 = c2.x & 0x0F0F0F0Fu, q1 = c2.y & 0x0F0F0F0Fu;
+            const uint32_t q2 = (c2.x >> 4) & 0x0F0F0F0Fu, q3 = (c2.y >> 4) & 0x0F0F0F0Fu;
+            const v4i Bh = {bytes_times(q0, hi), bytes_times(q1, hi), bytes_times(q2, hi), bytes_times(q3, hi)};
+            const v4i Bl = {bytes_times(q0, lo), bytes_times(q1, lo), bytes_times(q2, lo), bytes_times(q3, lo)};
+            const v4i Bo = {mr, mr, mr, mr};
+            ah = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bh, ah, 0, 0, 0);
+            al = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bl, al, 0, 0, 0);
+            ao = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bo, ao, 0, 0, 0);
+        }
+        const uint32_t dd = meta[rt].x;
+        const float fd = f16_value(dd), fm = f16_value(dd >> 16);
+        const bool near = q4k_near(fd, fm);
+        const double Dd = (double)fd, Dm = (double)fm;
+        const double *S = sS + 4 * grp;
+        float p[4];
+        if (__all(near) && !tiny) {
+            // no piece is tiny: the conversion needs no flush; an exact -0 is added to +0 or to
+            // a nonzero partial sum by the fold, which gives what +0 would
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int Cb = 8 * ah[i] + al[i];
+                const double X = __builtin_fma((double)Cb, Dd, -((double)ao[i] * Dm));
+                p[i] = (float)(X * S[i]);
+            }
+        } else {
+            const uint32_t *Wd = sW + 4 * grp;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int Cb = 8 * ah[i] + al[i];
+                if (near) {
+                    p[i] = piece_q4k_perblock_near(Cb, ao[i], Dd, Dm, S[i]);
+                } else {
+                    const int m = (int)((Wd[i] >> 16) & 0xFFu);
+                    const int e = (int)(int16_t)(Wd[i] & 0xFFFFu);
+                    p[i] = piece_q4k_perblock(Cb, ao[i], dd, m, e);
+                }
+            }
+        }
+        if (live) reinterpret_cast<float4 *>(pieces)[(wid * RTT + rt) * 64 + lane] = make_float4(p[0], p[1], p[2], p[3]);
+    }
+    if (lane == 0) flags[wid] = live && tiny ? 1 : 0;
+    __syncthreads();
+
+    // fold: thread t takes row tile t/256 and output o = t%256 of it (o = 4 lane' + i: row
+    // lane' % 16, column 4 (lane' / 16) + i); block k's piece of it is float (k*RTT + rt)*256 + o
+    const int t = (int)threadIdx.x;
+    if (t < 256 * RTT) {
+        const int frt = t >> 8, o = t & 255;
+        const uint4 fw = *reinterpret_cast<const uint4 *>(flags);
+        const uint32_t fm4[4] = {fw.x, fw.y, fw.z, fw.w};
+        uint32_t any = 0;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int keep = min(max(G - 4 * q, 0), 4);
+            any |= keep == 4 ? fm4[q] : fm4[q] & ((1u << (8 * keep)) - 1u);
+        }
+        const float *pc = pieces + frt * 256 + o;
+        const size_t stride = (size_t)RTT * 256;
+        float y = 0.0f;
+        if (any != 0) {
+            for (int k = 0; k < G; k++) y = fadd_ftz(y, pc[k * stride]);
+        } else if (G == 16) {
+            float q[16];
+#pragma unroll
+            for (int k = 0; k < 16; k++) q[k] = pc[k * stride];
+#pragma unroll
+            for (int k = 0; k < 16; k++) y = y + q[k];
+        } else {
+            for (int k = 0; k < G; k++) y = y + pc[k * stride];
+        }
+        const int lp = o >> 2, i = o & 3;
+        const int64_t row = (int64_t)g * 64 + 16 * (qr0 + frt) + (lp & 15);
+        const int col = 4 * (lp >> 4) + i;
+        if (row < rows && col < ncol) out[(int64_t)col * rows + row] = canon_nan(y);
+    }
 }
 
-// waves per row quarter: the tuning knob's value where it divides the column tiles, else 1
-template <int CT>
-int launch_ring(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
-                const qg_act_scale *scales, float *out, hipStream_t s)
+template <int RTT>
+int launch_staged_typed(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
+                        const qg_act_scale *scales, float *out, hipStream_t s)
 {
-    const int wh = tuning().mfma_ring_waves;
-    if constexpr (CT >= 4)
-        if (wh == 4) return launch_ring_d<CT, 4>(rows, G, ncol, image, codes, scales, out, s);
-    if constexpr (CT >= 2)
-        if (wh == 2) return launch_ring_d<CT, 2>(rows, G, ncol, image, codes, scales, out, s);
-    return launch_ring_d<CT, 1>(rows, G, ncol, image, codes, scales, out, s);
+    using L = StagedLds<RTT>;
+    const int64_t strips = (rows + 63) / 64 * (4 / RTT);
+    if (strips > 0x7fffffff) return fail(QG_E_SHAPE, "gemm: %lld rows is too many", (long long)rows);
+    const size_t lds = L::bytes(G * 256, (int)std::min<int64_t>(ncol, 16));
+    if (lds > (size_t)kMaxLds) return QG_E_UNSUPPORTED;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_staged_q4k<RTT>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    (void)attr;
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(scales);
+    hipEvent_t ev0, ev1;
+    take_timing_events(&ev0, &ev1);
+    if (ev0 && ev1)
+        hipExtLaunchKernelGGL((gemm_staged_q4k<RTT>), dim3((unsigned)strips), dim3(1024), lds, s, ev0, ev1, 0,
+                              static_cast<const uint8_t *>(image), (int)rows, G, codes, w, (int)ncol, (int)strips, out);
+    else
+        hipLaunchKernelGGL((gemm_staged_q4k<RTT>), dim3((unsigned)strips), dim3(1024), lds, s,
+                           static_cast<const uint8_t *>(image), (int)rows, G, codes, w, (int)ncol, (int)strips, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemm (matrix cores, staged) launch: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+// row tiles and column tiles per workgroup: the tuning knobs if set, else derived from the
+// shape (enough workgroups to fill the CUs, and the widest column batch whose pieces fit)
+int launch_split(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes, const qg_act_scale *scales,
+                 float *out, hipStream_t s)
+{
+    int rtt = tuning().gemm_row_tiles;
+    int ct = tuning().mfma_col_tiles;
+    if (ct == 0) ct = ncol <= 16 ? 1 : 2;
+    if (rtt == 0) rtt = 2;
+    const bool multi = G > 16;
+    if (multi && rtt * ct > 4) {   // two slots of pieces: at most 64 KiB each
+        if (rtt > 1) rtt = 4 / ct > 0 ? 4 / ct : 1;
+        if (rtt * ct > 4) ct = 4 / rtt;
+    }
+    int st = QG_E_UNSUPPORTED;
+    if (rtt == 1 && ct == 1) st = launch_split_typed<1, 1>(rows, G, ncol, image, codes, scales, out, s);
+    else if (rtt == 1 && ct == 2) st = launch_split_typed<1, 2>(rows, G, ncol, image, codes, scales, out, s);
+    else if (rtt == 1 && ct == 4) st = launch_split_typed<1, 4>(rows, G, ncol, image, codes, scales, out, s);
+    else if (rtt == 2 && ct == 1) st = launch_split_typed<2, 1>(rows, G, ncol, image, codes, scales, out, s);
+    else if (rtt == 2 && ct == 2) st = launch_split_typed<2, 2>(rows, G, ncol, image, codes, scales, out, s);
+    else if (rtt == 2 && ct == 4) st = launch_split_typed<2, 4>(rows, G, ncol, image, codes, scales, out, s);
+    else if (rtt == 4 && ct == 1) st = launch_split_typed<4, 1>(rows, G, ncol, image, codes, scales, out, s);
+    else if (rtt == 4 && ct == 2) st = launch_split_typed<4, 2>(rows, G, ncol, image, codes, scales, out, s);
+    if (st == QG_E_UNSUPPORTED) return fail(QG_E_UNSUPPORTED, "gemm: %d row tiles x %d column tiles do not fit", rtt, ct);
+    return st;
 }
 
 }  // namespace
@@ -857,28 +880,29 @@ int launch_gemm_mfma(int64_t rows, int64_t cols, int64_t ncol, const void *image
                      const qg_act_scale *scales, float *out, hipStream_t s)
 {
     const int G = (int)(cols / 256);
-    const int form = tuning().mfma_form;
-    int tiles = tuning().mfma_col_tiles;
-    // derived (measured on the 14336 x 4096 matrix): up to 16 columns the ring with one column
-    // tile, up to 32 the shared-operand form with two, beyond that the shared-operand form
-    // with four
-    if (form == 1 || (form == 0 && ncol <= 16)) {
-        const int ct = tiles > 0 ? tiles : form == 0 ? 1 : ncol >= 48 ? 4 : ncol >= 24 ? 2 : 1;
+    int form = tuning().mfma_form;
+    // derived (measured on the 4096- and 14336-row matrices): up to 16 columns of rows of up to
+    // 16 blocks the staged form; more columns on fewer than 8192 rows the split form (enough
+    // workgroups to fill the chip); otherwise the shared-operand form
+    if (form == 0) form = (G <= 16 && ncol <= 16) ? 1 : rows < 8192 ? 3 : 2;
+    if (form == 1) {
+        if (G > 16 || ncol > 16)
+            return fail(QG_E_UNSUPPORTED, "gemm: the staged form takes at most 16 columns of at most 16 blocks");
+        int rtt = tuning().gemm_row_tiles;
+        if (rtt == 0) rtt = rows < 8192 ? 1 : ncol > 8 ? 4 : 2;
         int st = QG_E_UNSUPPORTED;
-        if (ct == 4) st = launch_ring<4>(rows, G, ncol, image, codes, scales, out, s);
-        else if (ct == 2) st = launch_ring<2>(rows, G, ncol, image, codes, scales, out, s);
-        else st = launch_ring<1>(rows, G, ncol, image, codes, scales, out, s);
-        if (st != QG_E_UNSUPPORTED) return st;
-        if (form == 1) return fail(QG_E_UNSUPPORTED, "gemm: rows of %d blocks do not fit the ring's LDS", G);
+        if (rtt == 4) st = launch_staged_typed<4>(rows, G, ncol, image, codes, scales, out, s);
+        else if (rtt == 2) st = launch_staged_typed<2>(rows, G, ncol, image, codes, scales, out, s);
+        else st = launch_staged_typed<1>(rows, G, ncol, image, codes, scales, out, s);
+        if (st == QG_E_UNSUPPORTED) return fail(QG_E_UNSUPPORTED, "gemm: the staged form's LDS does not fit");
+        return st;
     }
-    if (form == 2 || (form == 0 && ncol > 16)) {
-        // shared operands: 2 column tiles up to 32 columns, else 4, unless asked otherwise
-        if (tiles == 1) return launch_cw<1>(rows, G, ncol, image, codes, scales, out, s);
-        if (tiles == 2 || (tiles == 0 && ncol <= 32)) return launch_cw<2>(rows, G, ncol, image, codes, scales, out, s);
-        return launch_cw<4>(rows, G, ncol, image, codes, scales, out, s);
-    }
-    if (tiles == 2 || (tiles == 0 && ncol >= 32)) return launch_wave<2>(rows, G, ncol, image, codes, scales, out, s);
-    return launch_wave<1>(rows, G, ncol, image, codes, scales, out, s);
+    if (form == 3) return launch_split(rows, G, ncol, image, codes, scales, out, s);
+    // shared operands: 2 column tiles up to 32 columns, else 4, unless asked otherwise
+    const int tiles = tuning().mfma_col_tiles;
+    if (tiles == 1) return launch_cw<1>(rows, G, ncol, image, codes, scales, out, s);
+    if (tiles == 2 || (tiles == 0 && ncol <= 32)) return launch_cw<2>(rows, G, ncol, image, codes, scales, out, s);
+    return launch_cw<4>(rows, G, ncol, image, codes, scales, out, s);
 }
 
 }  // namespace qg

@@ -25,12 +25,12 @@ int fail(int status, const char *fmt, ...);
 
 struct Tuning {
     int waves_per_wg;     // waves per GEMV workgroup (4, 8, 16); 0 = derived from the block count
-    int mfma_min_cols;    // columns from which a Q4_K PerBlock GEMM uses the matrix cores; 0 = 9
-    int mfma_col_tiles;   // matrix-core GEMM: 1, 2 or 4 column tiles per workgroup; 0 = derived
-    int mfma_form;        // matrix-core GEMM: 1 ring, 2 shared operands, 3 per wave; 0 = derived
-    int mfma_ring_waves;  // ring form: waves per 16-row quarter (1, 2 or 4); 0 = derived
+    int mfma_min_cols;    // columns from which a Q4_K PerBlock GEMM uses the matrix cores; 0 = derived
+    int mfma_col_tiles;   // matrix-core GEMM (shared, split): 1, 2 or 4 column tiles per workgroup; 0 = derived
+    int mfma_form;        // matrix-core GEMM: 1 staged, 2 shared operands, 3 split; 0 = derived
     int cols_off;         // 1: several columns take the LDS-staged kernel, not the one-column machinery
     int mfma_pre_off;     // 1: the shared-operand GEMM loads its scales per block, not into tables
+    int gemm_row_tiles;   // staged and split matrix-core GEMM: 16-row tiles per workgroup (1, 2, 4); 0 = derived
 };
 const Tuning &tuning();
 

@@ -22,7 +22,7 @@
  *   - Pointers named *_host are host memory; every other data pointer is device memory
  *     (hipMalloc / torch on the ROCm device).  All memory is owned by the caller; the
  *     library allocates no device memory and keeps no state except a per-thread reason
- *     string and the tuning knobs.
+ *     string and the per-thread tuning knobs (qg_set_tuning).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Launches are asynchronous on it;
  *     the returned status covers only argument validation and launch errors.
  *   - Device pointers must be 16-byte aligned (4-byte for scales, csums, out, err_flag).
@@ -325,37 +325,39 @@ int qg_stream_read(const void *buf, size_t bytes, uint32_t magic, uint32_t *sink
 int qg_stream_read_shape(const void *buf, size_t bytes, int waves_per_wg, int kib_per_wave, int64_t wgs, int flags,
                          uint32_t magic, uint32_t *sink, void *stream);
 
-/* Speed-only tuning knobs; they never change output bits.
+/* Speed-only tuning knobs; they never change output bits.  The knobs are per thread: a value
+ * set by qg_set_tuning applies to the later calls made on the same thread (the library's only
+ * state besides the reason string; other threads keep their own values).
  *   QG_TUNE_WAVES_PER_WG  waves per GEMV workgroup, splitting a 64-row group's blocks:
  *                         4, 8 or 16 (0 = one wave per block, at most 16).  16 applies
  *                         only to a single column of at most 16 blocks; otherwise 8 is used
  *   QG_TUNE_MFMA_MIN_COLS number of columns from which qg_gemm_q on a Q4_K PerBlock matrix
- *                         runs on the int8 matrix cores, columns padded to 16 (0 = 9;
- *                         above 65535 = never)
- *   QG_TUNE_MFMA_FORM     the matrix-core GEMM's form: 1 = LDS ring (tiles and activation operands
- *                         staged by LDS-DMA loads several blocks ahead), 2 = shared operands
- *                         (weight operands built once per workgroup in LDS), 3 = per wave
- *                         (operands in each wave's registers); 0 = derived (up to 16 columns the
- *                         ring where its LDS fits, else per wave; beyond 16 shared operands)
- *   QG_TUNE_MFMA_COL_TILES 1, 2 or 4: 16-column tiles per workgroup of the ring and shared-operand
- *                         forms (the per-wave form takes 1 or 2); 0 = derived from the columns
- *   QG_TUNE_MFMA_RING_WAVES 1, 2 or 4 waves per 16-row quarter in the ring form, each taking an
- *                         equal share of the column tiles (a value that does not divide them
- *                         is taken as 1); 0 = derived
+ *                         runs on the int8 matrix cores (0 = derived: 2 on fewer than 8192
+ *                         rows, 5 on more; above 65535 = never)
+ *   QG_TUNE_MFMA_FORM     the matrix-core GEMM's form: 1 = staged (at most 16 columns of rows of
+ *                         at most 16 blocks: every wave one block, the columns' codes staged in
+ *                         LDS), 2 = shared operands (weight operands built once per workgroup in
+ *                         LDS), 3 = split (every wave one block, the activation operands loaded per
+ *                         wave); 0 = derived from the shape
+ *   QG_TUNE_MFMA_COL_TILES 1, 2 or 4: 16-column tiles per workgroup of the shared-operand and
+ *                         split forms; 0 = derived from the columns
  *   QG_TUNE_COLS_KERNEL   several columns below the matrix-core threshold (Q4_K/Q6_K, at most 16
  *                         blocks per row): 0 = the one-column kernel's machinery, NC columns per
  *                         wave (default); 1 = the kernel that stages the columns in LDS
  *   QG_TUNE_MFMA_TABLES   the shared-operand form: 0 = read every block's block scales, sub-block
  *                         fields and activation scales into LDS tables at the start where they
- *                         fit (default); 1 = load them with each block */
+ *                         fit (default); 1 = load them with each block
+ *   QG_TUNE_GEMM_ROW_TILES the staged and split forms: 16-row tiles per workgroup, 1, 2 or 4 (0 =
+ *                         derived from the rows and columns) */
 enum {
     QG_TUNE_WAVES_PER_WG = 1,
     QG_TUNE_MFMA_MIN_COLS = 2,
     QG_TUNE_MFMA_COL_TILES = 3,
     QG_TUNE_MFMA_FORM = 4,
-    QG_TUNE_MFMA_RING_WAVES = 5,
+    /* 5 is not used */
     QG_TUNE_COLS_KERNEL = 6,
-    QG_TUNE_MFMA_TABLES = 7
+    QG_TUNE_MFMA_TABLES = 7,
+    QG_TUNE_GEMM_ROW_TILES = 8
 };
 int qg_set_tuning(int key, int64_t value);
 

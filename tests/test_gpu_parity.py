@@ -35,6 +35,8 @@ def qg():
     q.qg_set_tuning(q.TUNE_MFMA_COL_TILES, 0)
     q.qg_set_tuning(q.TUNE_COLS_KERNEL, 0)
     q.qg_set_tuning(q.TUNE_MFMA_TABLES, 0)
+    q.qg_set_tuning(q.TUNE_MFMA_FORM, 0)
+    q.qg_set_tuning(q.TUNE_GEMM_ROW_TILES, 0)
     oracle.set_threads(8)
     return q
 
@@ -444,10 +446,10 @@ def test_several_columns_one_column_machinery(qg, fmt, mode):
 
 @pytest.mark.parametrize("ncol", [3, 8, 16, 17, 33, 64, 100])
 def test_matrix_core_gemm_matches_oracle(qg, ncol):
-    """Q4_K PerBlock batches run on v_mfma_i32_16x16x64_i8 (by default from 8 columns; here
-    forced for every count); every (row, column) must carry the oracle's bits, across
-    column-tile settings, ragged rows and columns, and block scales that take both the
-    near-exponent and the general combine."""
+    """Q4_K PerBlock batches run on v_mfma_i32_16x16x64_i8 (by default from 2 or 5 columns; here
+    forced for every count); every (row, column) must carry the oracle's bits in every form,
+    across column-tile and row-tile settings, ragged rows and columns, and block scales that
+    take both the near-exponent and the general combine."""
     f = _adversarial_fields("q4k", 130, 1280, 900 + ncol)
     M = Mat(qg, f)
     xs = gen.act_outliers(ncol, 1280, 901 + ncol)
@@ -456,27 +458,31 @@ def test_matrix_core_gemm_matches_oracle(qg, ncol):
     want = oracle.gemm(f, c, m, e, 0).reshape(ncol, 130)
     try:
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 1)                # matrix cores for any column count
-        for form, wh in ((0, 0), (1, 1), (1, 2), (1, 4), (2, 0), (3, 0)):   # derived, ring, shared, per wave
+        # derived, staged (at most 16 columns), shared operands, split
+        for form in (0, 1, 2, 3):
+            if form == 1 and ncol > 16:
+                continue
             qg.qg_set_tuning(qg.TUNE_MFMA_FORM, form)
-            qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, wh)
             for ct in (0, 1, 2, 4):                                 # 0: derived from the column count
                 qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, ct)
-                for tab in ((0, 1) if form == 2 else (0,)):         # shared operands: scale tables or not
-                    qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, tab)
-                    say("matrix-core gemm", ncol, "form", form, "ring waves", wh, "column tiles", ct, "tables off", tab)
-                    out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
-                    assert first_mismatch(out, want) is None, (ncol, form, wh, ct, tab, first_mismatch(out, want))
-                qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, 0)
+                for rt in ((0, 1, 2, 4) if form in (1, 3) and ct == 0 else (0,)):
+                    qg.qg_set_tuning(qg.TUNE_GEMM_ROW_TILES, rt)
+                    for tab in ((0, 1) if form == 2 else (0,)):     # shared operands: scale tables or not
+                        qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, tab)
+                        say("matrix-core gemm", ncol, "form", form, "column tiles", ct, "row tiles", rt, "tables off", tab)
+                        out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+                        assert first_mismatch(out, want) is None, (ncol, form, ct, rt, tab, first_mismatch(out, want))
+                    qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, 0)
+                qg.qg_set_tuning(qg.TUNE_GEMM_ROW_TILES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 0)
-        qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 65536)          # force the vector-ALU kernel
         out_valu = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
         assert first_mismatch(out_valu, want) is None
     finally:
         qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 0)
-        qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 0)
+        qg.qg_set_tuning(qg.TUNE_GEMM_ROW_TILES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 0)
 
 
@@ -526,6 +532,52 @@ def test_matrix_core_gemm_long_rows(qg, cols):
     assert first_mismatch(out, want) is None, (cols, first_mismatch(out, want))
 
 
+@pytest.mark.parametrize("cols,ncol", [(1280, 5), (1280, 64), (3072, 16), (4096, 1), (4096, 2), (4096, 8), (4096, 33),
+                                       (4096, 100), (6144, 40), (8192, 17)])
+def test_split_gemm_matches_oracle(qg, cols, ncol):
+    """The split and staged matrix-core GEMMs (every wave one block, every load issued at once)
+    in every row-tile x column-tile shape: ragged rows (three 64-row groups, the last partial) and
+    columns, rows of 5 blocks (one partial round of waves), 16 (one round), 24 and 32 (two
+    rounds), block scales that take both the near-exponent and the general combine, a row whose
+    partial sum passes through the subnormal range, and a column of tiny activations."""
+    rows = 130
+    f = _adversarial_fields("q4k", rows, cols, 6100 + cols // 256 + ncol)
+    _subnormal_partial_q4k(f, 65)
+    M = Mat(qg, f)
+    xs = gen.act_outliers(ncol, cols, 6101 + ncol)
+    xs[ncol - 1, :] = np.float32(2.0 ** -112)
+    if ncol > 3:
+        xs[2, 256:512] = 0.0                                    # an all-zero activation block
+    act, c, m, e, _ = gpu_quant(qg, xs, 0)
+    want = oracle.gemm(f, c, m, e, 0).reshape(ncol, rows)
+    try:
+        qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 1)
+        qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 3)
+        for rtt in (0, 1, 2, 4):
+            for ct in (0, 1, 2, 4):
+                if rtt * ct > 8:
+                    continue
+                qg.qg_set_tuning(qg.TUNE_GEMM_ROW_TILES, rtt)
+                qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, ct)
+                say("split gemm", rows, "x", cols, "n", ncol, "row tiles", rtt, "column tiles", ct)
+                out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+                assert first_mismatch(out, want) is None, (rtt, ct, first_mismatch(out, want))
+        qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 0)
+        if cols <= 4096 and ncol <= 16:
+            # the staged form (at most 16 columns staged in LDS), every row-tile count
+            qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 1)
+            for rtt in (0, 1, 2, 4):
+                qg.qg_set_tuning(qg.TUNE_GEMM_ROW_TILES, rtt)
+                say("staged gemm", rows, "x", cols, "n", ncol, "row tiles", rtt)
+                out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+                assert first_mismatch(out, want) is None, ("staged", rtt, first_mismatch(out, want))
+    finally:
+        qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 0)
+        qg.qg_set_tuning(qg.TUNE_GEMM_ROW_TILES, 0)
+        qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 0)
+        qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 0)
+
+
 def _subnormal_partial_q4k(f, r):
     """Row r of a Q4_K-style matrix (at least 3 blocks) whose PerBlock pieces, under an
     activation block of all 2^-112 (codes 126, scale 130 * 2^-126), are 16380*k*2^-142 with
@@ -541,7 +593,7 @@ def _subnormal_partial_q4k(f, r):
     f["dmin"][r, :3] = [0, 801, 0]
 
 
-@pytest.mark.parametrize("ncol,tiny", [(64, (0, 63)), (100, (70,))])
+@pytest.mark.parametrize("ncol,tiny", [(16, (3, 15)), (64, (0, 63)), (100, (70,))])
 def test_subnormal_partial_sums_gemv_and_gemm(qg, ncol, tiny):
     """Rows whose running sum passes through the subnormal range, through the GEMV and every
     GEMM form: all must give the oracle's bits, which differ from unflushed adds.  With 100
@@ -570,16 +622,16 @@ def test_subnormal_partial_sums_gemv_and_gemm(qg, ncol, tiny):
     assert first_mismatch(run_gemv(qg, M, one), want[t0]) is None
     try:
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 1)
-        for form, wh, tab in ((1, 1, 0), (1, 2, 0), (1, 4, 0), (2, 0, 0), (2, 0, 1), (3, 0, 0)):
+        for form, tab in ((1, 0), (2, 0), (2, 1), (3, 0)):       # staged, shared (tables or not), split
+            if form == 1 and ncol > 16:
+                continue
             qg.qg_set_tuning(qg.TUNE_MFMA_FORM, form)
-            qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, wh)
             qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, tab)
-            say("subnormal partial sums, gemm form", form, "ring waves", wh, "tables off", tab, "columns", ncol)
+            say("subnormal partial sums, gemm form", form, "tables off", tab, "columns", ncol)
             out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
-            assert first_mismatch(out, want) is None, (form, wh, tab, first_mismatch(out, want))
+            assert first_mismatch(out, want) is None, (form, tab, first_mismatch(out, want))
     finally:
         qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 0)
-        qg.qg_set_tuning(qg.TUNE_MFMA_RING_WAVES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, 0)
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 0)
 
