@@ -149,7 +149,8 @@ def parse():
                    help="time the step as qg_quantize_act + qg_gemv_q instead of qg_quantize_gemv")
     p.add_argument("--tune", action="append", default=[], metavar="KEY=VALUE",
                    help="a speed-only tuning knob (qg_set_tuning): waves_per_wg, mfma_min_cols, mfma_col_tiles, "
-                        "mfma_form, cols_kernel, mfma_tables, gemm_row_tiles; output bits do not depend on them")
+                        "mfma_form, cols_kernel, mfma_tables, gemm_row_tiles, gemv_quarter; output bits do not depend on "
+                        "them")
     p.add_argument("--kernel-only", type=int, default=0, metavar="K",
                    help="only launch the step's dominant kernel K times (eager, over the rotated copies) and exit: "
                         "for rocprofv3 counter passes")
@@ -448,6 +449,11 @@ def main():
     if ncol == 1 and fmt_s in ("q8_0", "q4_0"):
         kernel_label = ("gemv1_b32_kernel<..., SRC_F32> (one-launch quantize + GEMV)" if fused
                         else "gemv1_b32_kernel<..., SRC_CODES> (GEMV of a quantized row)")
+    elif ncol == 1 and fmt_s == "q4k" and mode == 0 and cols <= 16 * 256 and not tuned.get("waves_per_wg") and (
+            tuned.get("gemv_quarter") == 1 or (not tuned.get("gemv_quarter") and sum((r + 63) // 64 for r in mrows) < 128)):
+        # the library's 16-row workgroups (launch_one_any: fewer than 128 row groups in the launch)
+        kernel_label = ("gemv1_quarter_kernel<SRC_F32> (one-launch quantize + GEMV, 16-row workgroups)" if fused
+                        else "gemv1_quarter_kernel<SRC_CODES> (GEMV of a quantized row, 16-row workgroups)")
     elif ncol == 1:
         kernel_label = ("gemv1_kernel<..., SRC_F32> (one-launch quantize + GEMV)" if fused
                         else "gemv1_kernel<..., SRC_CODES> (GEMV of a quantized row)")

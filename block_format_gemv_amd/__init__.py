@@ -27,6 +27,7 @@ TUNE_WAVES_PER_WG, TUNE_MFMA_MIN_COLS, TUNE_MFMA_COL_TILES, TUNE_MFMA_FORM = 1, 
 TUNE_COLS_KERNEL = 6
 TUNE_MFMA_TABLES = 7
 TUNE_GEMM_ROW_TILES = 8
+TUNE_GEMV_QUARTER = 9
 BLOCK = 256
 MAX_COLS = 32768
 MAX_MATRICES = 8

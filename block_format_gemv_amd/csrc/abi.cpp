@@ -157,6 +157,10 @@ int qg_set_tuning(int key, int64_t value)
             return fail(QG_E_INVALID, "qg_set_tuning: row tiles must be 0, 1, 2 or 4");
         g_tuning.gemm_row_tiles = (int)value;
         return QG_OK;
+    case QG_TUNE_GEMV_QUARTER:
+        if (value > 2) return fail(QG_E_INVALID, "qg_set_tuning: the 16-row GEMV choice must be 0, 1 or 2");
+        g_tuning.gemv_quarter = (int)value;
+        return QG_OK;
     default:
         return fail(QG_E_INVALID, "qg_set_tuning: unknown key %d", key);
     }

@@ -765,9 +765,8 @@ __device__ __forceinline__ P *opaque_global(P *p)
     return (P *)g;
 }
 
-__device__ __forceinline__ Picked pick_matrix(const Targets &tg)
+__device__ __forceinline__ Picked pick_matrix(const Targets &tg, int bx)
 {
-    const int bx = (int)blockIdx.x;
     Picked p{opaque_global(tg.image[0]), opaque_global(tg.out[0]), opaque_sgpr(tg.rows[0]), bx};
     if (tg.nmat == 1) return p;
 #pragma unroll
@@ -825,7 +824,7 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
     // pieces: G per row with DB, else W (one per wave); then one flag byte per wave
     unsigned char *s_small = reinterpret_cast<unsigned char *>(s_piece + (size_t)(DB ? G : W) * 64);
     bool small = false;                          // a block of this wave may give a tiny piece
-    const Picked pm = pick_matrix(tg);           // this workgroup's matrix (wave-uniform)
+    const Picked pm = pick_matrix(tg, (int)blockIdx.x);   // this workgroup's matrix (wave-uniform)
     const int g = pm.g;
     const int rows = pm.rows;
     float *out = pm.out;
@@ -915,6 +914,116 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// One activation column, Q4_K-style, PerBlock, rows of at most 16 blocks, on small matrices: a
+// workgroup owns a quarter of a 64-row group (16 rows), so a matrix of few row groups still
+// spreads over every compute unit.  Wave w takes block w as in gemv1_kernel; lane (r, kk) = (l %
+// 16, l / 16) takes row r of the quarter and sub-blocks 2kk, 2kk+1 of the block (two 16-byte
+// code chunks and the row's block fields).  The block's activation codes are quantized or
+// loaded by the wave as in gemv1_kernel (lane l: codes 4l .. 4l+3) and split into nibble
+// planes; the planes of sub-blocks 2kk, 2kk+1 sit in lanes 16kk .. 16kk+15, the lane group of
+// kk, and reach its lanes by DPP row broadcasts.  Each lane's two integer sub-block sums and
+// offset sums are added over the four lane groups (exact integers), then lanes kk = 0 form the
+// pieces; the first wave adds each row's pieces in block order.
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v)   // lane n of the lane's row of 16 (CTRL = 0x150 + n)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int SRC>
+__global__ __launch_bounds__(1024) void gemv1_quarter_kernel(const Targets tg, int G, ActIO io)
+{
+    __shared__ __align__(16) float s_piece[16 * 16];     // [wave = block][row of the quarter]
+    __shared__ __align__(16) unsigned char s_small[16];
+    const int bx = (int)blockIdx.x;
+    // the workgroup's matrix and 64-row group (the Targets count 64-row groups)
+    const Picked pm = pick_matrix(tg, bx >> 2);
+    const int qr = bx & 3;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, kk = lane >> 4;
+    const bool emit = bx == 0;
+    const int b = min(wid, G - 1);             // a wave past the last block works on a copy and parks nothing
+    const int trow = 16 * qr + r;
+    const uint8_t *tile = pm.image + ((size_t)pm.g * G + b) * kTileBytesQ4K;
+
+    ActRaw<SRC> raw = load_act<SRC, 64>(io, b, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SRC == SRC_F32) __builtin_amdgcn_s_barrier();   // every wave's activation load first
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4 meta = ld_stream(tile + 8192 + 16 * trow);
+    const uint4 w0 = ld_stream(tile + 1024 * (2 * kk) + 16 * trow);
+    const uint4 w1 = ld_stream(tile + 1024 * (2 * kk + 1) + 16 * trow);
+    load_fence();
+    const ActWave a = ready_act<SRC, 8, 64>(raw, wid, G, lane, emit, io);
+
+    // nibble planes of the codes (as ActPlanes): lane 8i + d (d < 4) holds dword d of sub-block
+    // i's planes, so the lane group of kk holds those of sub-blocks 2kk (row lanes 0..3) and
+    // 2kk + 1 (row lanes 8..11)
+    const uint32_t lo = a.packed & 0x0F0F0F0Fu;
+    const uint32_t hi = (a.packed >> 4) & 0x0F0F0F0Fu;
+    const uint32_t AL = lo | ((uint32_t)dpp<kDppRowShl4>((int)lo) << 4);
+    const uint32_t AH = hi | ((uint32_t)dpp<kDppRowShl4>((int)hi) << 4);
+    const uint32_t sh = (uint32_t)quad_sum(__builtin_amdgcn_sdot8((int)AH, 0x11111111, 0, false));
+    const uint32_t al[8] = {row_bcast<0x150>(AL), row_bcast<0x151>(AL), row_bcast<0x152>(AL), row_bcast<0x153>(AL),
+                            row_bcast<0x158>(AL), row_bcast<0x159>(AL), row_bcast<0x15A>(AL), row_bcast<0x15B>(AL)};
+    const uint32_t ah[8] = {row_bcast<0x150>(AH), row_bcast<0x151>(AH), row_bcast<0x152>(AH), row_bcast<0x153>(AH),
+                            row_bcast<0x158>(AH), row_bcast<0x159>(AH), row_bcast<0x15A>(AH), row_bcast<0x15B>(AH)};
+    const int kh0 = 8 * (int)row_bcast<0x150>(sh), kh1 = 8 * (int)row_bcast<0x158>(sh);
+    const int s0 = (int)row_bcast<0x150>((uint32_t)a.s32), s1 = (int)row_bcast<0x158>((uint32_t)a.s32);
+
+    // the fields of sub-blocks 2kk and 2kk + 1: bits 24kk .. 24kk + 23 of the 96-bit string
+    const uint64_t pair = kk < 2 ? ((uint64_t)meta.z << 32 | meta.y) : ((uint64_t)meta.w << 32 | meta.z);
+    const uint32_t f24 = (uint32_t)(pair >> (kk < 2 ? 24 * kk : 24 * kk - 32)) & 0xFFFFFFu;
+    const int sc0 = (int)(f24 & 63u), mn0 = (int)((f24 >> 6) & 63u);
+    const int sc1 = (int)((f24 >> 12) & 63u), mn1 = (int)((f24 >> 18) & 63u);
+
+    // sum q*a = 16 * (sum (q-8)*ah + 8 * sum ah) + sum q*al, per sub-block (as q4k_sub)
+    const uint32_t q0[4] = {w0.x, w0.y, w0.z, w0.w};
+    const uint32_t q1[4] = {w1.x, w1.y, w1.z, w1.w};
+    int X0 = kh0, X1 = kh1;
+    uint32_t Y0 = 0, Y1 = 0;
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        X0 = __builtin_amdgcn_sdot8((int)(q0[d] ^ 0x88888888u), (int)ah[d], X0, false);
+        Y0 = __builtin_amdgcn_udot8(q0[d], al[d], Y0, false);
+        X1 = __builtin_amdgcn_sdot8((int)(q1[d] ^ 0x88888888u), (int)ah[4 + d], X1, false);
+        Y1 = __builtin_amdgcn_udot8(q1[d], al[4 + d], Y1, false);
+    }
+    int Cp = mad_i24(sc0, 16 * X0 + (int)Y0, mul_i24(sc1, 16 * X1 + (int)Y1));
+    int Op = mad_i24(mn0, s0, mul_i24(mn1, s1));
+    // the four lane groups' partial sums (exact integers)
+    Cp += __shfl_xor(Cp, 16, 64);
+    Op += __shfl_xor(Op, 16, 64);
+    Cp += __shfl_xor(Cp, 32, 64);
+    Op += __shfl_xor(Op, 32, 64);
+
+    const qg_act_scale sa = a.scale(b, 0, 1);
+    const float fd = f16_value(meta.x), fm = f16_value(meta.x >> 16);
+    float piece;
+    if (q4k_near(fd, fm)) {
+        const double X = __builtin_fma((double)Cp, (double)fd, -((double)Op * (double)fm)) * __builtin_ldexp((double)sa.m, sa.e);
+        // an activation exponent >= kNoTinyExp: X is 0 or at least 2^-102, no flush needed, and
+        // adding +0 turns an exact -0 into +0
+        piece = sa.e >= kNoTinyExp ? (float)X + 0.0f : r32_exact_double(X);
+    } else {
+        piece = piece_q4k_perblock(Cp, Op, meta.x, sa.m, sa.e);
+    }
+    if (kk == 0 && wid < G) s_piece[wid * 16 + r] = piece;
+    if (lane == 0) s_small[wid] = (wid < G && sa.e < kNoTinyExp) ? 1 : 0;
+    __syncthreads();
+
+    if (wid == 0 && lane < 16) {
+        const int64_t row = (int64_t)pm.g * 64 + trow;
+        float y;
+        if (any_flag<16>(s_small)) y = fold_flushed(0.0f, s_piece + r, G, 16);
+        else y = fold_chain_plain(0.0f, s_piece + r, G, 16);
+        if (row < pm.rows) pm.out[row] = canon_nan(y);
+    }
+}
+
 // Several activation columns on the one-column machinery (a quantized activation matrix, at
 // most 16 blocks per row): each wave keeps its tile in registers and forms its block's piece
 // for NC columns in turn, each column's codes read out into scalar registers as in the
@@ -1000,7 +1109,7 @@ __global__ __launch_bounds__(64 * W) void gemv1_b32_kernel(const Targets tg, int
     extern __shared__ __align__(16) float s_ring[];
     using T = TileRegs<FMT>;
     using A = typename std::conditional<FMT == QG_Q4_0, ActPlanes, ActWaveCodes>::type;
-    const Picked pm = pick_matrix(tg);
+    const Picked pm = pick_matrix(tg, (int)blockIdx.x);
     const int g = pm.g;
     const int rows = pm.rows;
     const int lane = threadIdx.x & 63;
@@ -1218,8 +1327,31 @@ int launch_b32(const Targets &tg, int G, const ActIO &io, hipStream_t s)
 }
 
 template <int SRC>
+int launch_quarter(const Targets &tg, int G, const ActIO &io, hipStream_t s)
+{
+    const int64_t wgs = 4 * (int64_t)tg.gstart[tg.nmat];
+    if (wgs == 0) return QG_OK;
+    if (G > 16) return fail(QG_E_RUNTIME, "gemv: %d blocks do not fit 16 waves", G);
+    hipEvent_t ev0, ev1;
+    take_timing_events(&ev0, &ev1);
+    if (ev0 && ev1)
+        hipExtLaunchKernelGGL((gemv1_quarter_kernel<SRC>), dim3((unsigned)wgs), dim3(1024), 0, s, ev0, ev1, 0, tg, G,
+                              io);
+    else
+        hipLaunchKernelGGL((gemv1_quarter_kernel<SRC>), dim3((unsigned)wgs), dim3(1024), 0, s, tg, G, io);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemv launch: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+template <int SRC>
 int launch_one_any(int fmt, int mode, const Targets &tg, int G, const ActIO &io, hipStream_t s)
 {
+    if (fmt == QG_Q4K && mode == QG_PERBLOCK && G <= 16 && !io.argmax && tuning().waves_per_wg == 0) {
+        // 16-row workgroups where 64-row ones leave compute units idle
+        const int q = tuning().gemv_quarter;
+        if (q == 1 || (q == 0 && tg.gstart[tg.nmat] < 128)) return launch_quarter<SRC>(tg, G, io, s);
+    }
     if (fmt == QG_Q8_0 && mode == QG_PERBLOCK) return launch_b32<QG_Q8_0, QG_PERBLOCK, SRC>(tg, G, io, s);
     if (fmt == QG_Q8_0 && mode == QG_SUB32) return launch_b32<QG_Q8_0, QG_SUB32, SRC>(tg, G, io, s);
     if (fmt == QG_Q4_0 && mode == QG_PERBLOCK) return launch_b32<QG_Q4_0, QG_PERBLOCK, SRC>(tg, G, io, s);

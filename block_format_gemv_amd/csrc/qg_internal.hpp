@@ -31,6 +31,7 @@ struct Tuning {
     int cols_off;         // 1: several columns take the LDS-staged kernel, not the one-column machinery
     int mfma_pre_off;     // 1: the shared-operand GEMM loads its scales per block, not into tables
     int gemm_row_tiles;   // staged and split matrix-core GEMM: 16-row tiles per workgroup (1, 2, 4); 0 = derived
+    int gemv_quarter;     // one-column Q4_K PerBlock GEMV: 1 = 16-row workgroups, 2 = 64-row ones; 0 = derived
 };
 const Tuning &tuning();
 

@@ -348,7 +348,12 @@ int qg_stream_read_shape(const void *buf, size_t bytes, int waves_per_wg, int ki
  *                         fields and activation scales into LDS tables at the start where they
  *                         fit (default); 1 = load them with each block
  *   QG_TUNE_GEMM_ROW_TILES the staged and split forms: 16-row tiles per workgroup, 1, 2 or 4 (0 =
- *                         derived from the rows and columns) */
+ *                         derived from the rows and columns)
+ *   QG_TUNE_GEMV_QUARTER  one column of a Q4_K PerBlock matrix of at most 16 blocks per row,
+ *                         without argmax: 1 = workgroups of 16 rows (four per 64-row group, so
+ *                         a matrix of few row groups still fills the chip), 2 = workgroups of 64
+ *                         rows, 0 = derived (16 rows below 128 row groups in the launch).  A
+ *                         waves-per-workgroup setting takes the 64-row workgroups */
 enum {
     QG_TUNE_WAVES_PER_WG = 1,
     QG_TUNE_MFMA_MIN_COLS = 2,
@@ -357,7 +362,8 @@ enum {
     /* 5 is not used */
     QG_TUNE_COLS_KERNEL = 6,
     QG_TUNE_MFMA_TABLES = 7,
-    QG_TUNE_GEMM_ROW_TILES = 8
+    QG_TUNE_GEMM_ROW_TILES = 8,
+    QG_TUNE_GEMV_QUARTER = 9
 };
 int qg_set_tuning(int key, int64_t value);
 

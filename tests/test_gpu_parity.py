@@ -37,6 +37,7 @@ def qg():
     q.qg_set_tuning(q.TUNE_MFMA_TABLES, 0)
     q.qg_set_tuning(q.TUNE_MFMA_FORM, 0)
     q.qg_set_tuning(q.TUNE_GEMM_ROW_TILES, 0)
+    q.qg_set_tuning(q.TUNE_GEMV_QUARTER, 0)
     oracle.set_threads(8)
     return q
 
@@ -347,6 +348,54 @@ def test_decode_workload_every_row_all_1000_reps(qg, llama):
         assert first_mismatch(one, want) is None, ("one launch", name)
         assert first_mismatch(two, want) is None, ("two launches", name)
         del one, two, a1, a2
+
+
+@pytest.mark.parametrize("quarter", [1, 2])
+def test_gemv_row_group_split_both_ways(qg, llama, quarter):
+    """The one-column Q4_K PerBlock GEMV with 16-row workgroups (1) and with 64-row ones (2),
+    forced, one launch and two: every shape of at most 16 blocks per row, the 14336-row matrix
+    for 20 repetitions and a three-matrix launch, all against the oracle."""
+    try:
+        qg.qg_set_tuning(qg.TUNE_GEMV_QUARTER, quarter)
+        for rows, cols in [s for s in SHAPES if s[1] <= 4096] + [(4096, 4096), (4100, 2048), (8191, 512)]:
+            say("row-group split", quarter, "shape", rows, cols)
+            f = _adversarial_fields("q4k", rows, cols, rows * 7 + cols + quarter)
+            M = Mat(qg, f)
+            x = gen.act_outliers(1, cols, rows + 5 * cols)
+            out, c, m, e, s = _fused(qg, M, x, 0)
+            oc, om, oe, os_ = oracle.quantize(x, 0)
+            assert np.array_equal(c, oc) and np.array_equal(m, om) and np.array_equal(e, oe)
+            assert np.array_equal(s, os_)
+            want = oracle.gemv(f, oc, om, oe, 0)
+            assert first_mismatch(out, want) is None, (rows, cols, first_mismatch(out, want))
+            act, _, _, _, _ = gpu_quant(qg, x, 0)
+            assert first_mismatch(run_gemv(qg, M, act), want) is None, (rows, cols)
+        M = llama["ffn"]
+        reps = 20
+        xs = np.concatenate([gen.decode_act(2000 + k) for k in range(reps)])
+        oc, om, oe, _ = oracle.quantize(xs, 0)
+        want = oracle.gemm(M.f, oc, om, oe, 0).reshape(reps, M.rows)
+        xd = dev(xs)
+        one = torch.empty((reps, M.rows), dtype=torch.float32, device=DEV)
+        for k in range(reps):
+            qg.quantize_gemv(M.fmt, M.rows, M.cols, M.img, xd[k], 0, out=one[k])
+        say("row-group split", quarter, "14336 x 4096,", reps, "reps")
+        assert first_mismatch(one, want) is None
+        shapes = [70, 0, 4096]
+        mats = [Mat(qg, _adversarial_fields("q4k", max(r, 1), 1024, 90 + r)) for r in shapes]
+        x = gen.act_outliers(1, 1024, 91)
+        act = qg.alloc_act(1, 1024, 0)
+        outs = [torch.full((max(r, 1),), -7.0, dtype=torch.float32, device=DEV) for r in shapes]
+        qg.qg_quantize_gemv_multi(qg.Q4K, 0, shapes, 1024, [M.img for M in mats], dev(x.reshape(-1)), act.codes,
+                                  act.scales, act.csums, None, outs)
+        oc, om, oe, _ = oracle.quantize(x, 0)
+        for r, M, o in zip(shapes, mats, outs):
+            if r == 0:
+                assert float(o[0].item()) == -7.0
+            else:
+                assert first_mismatch(o, oracle.gemv(M.f, oc, om, oe, 0)) is None, r
+    finally:
+        qg.qg_set_tuning(qg.TUNE_GEMV_QUARTER, 0)
 
 
 def test_output_projection_q6k_logits(qg):

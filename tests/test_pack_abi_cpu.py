@@ -239,6 +239,8 @@ def test_validation_refuses_before_any_gpu_work():
     assert L.qg_set_tuning(qg.TUNE_MFMA_FORM, 4) == qg.E_INVALID
     assert L.qg_set_tuning(5, 0) == qg.E_INVALID                # no longer a key
     assert L.qg_set_tuning(qg.TUNE_GEMM_ROW_TILES, 3) == qg.E_INVALID
+    assert L.qg_set_tuning(qg.TUNE_GEMV_QUARTER, 3) == qg.E_INVALID
+    assert L.qg_set_tuning(qg.TUNE_GEMV_QUARTER, 2) == qg.OK and L.qg_set_tuning(qg.TUNE_GEMV_QUARTER, 0) == qg.OK
     rows2 = (ctypes.c_int64 * 2)(8, 8)
     imgs2 = (ctypes.c_void_p * 2)(0x1000, 0x1000)
     outs2 = (ctypes.c_void_p * 2)(0x1000, 0x1000)
