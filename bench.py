@@ -22,9 +22,10 @@ Timing:
     bytes per launch and rotated copies (what one launch of this size can reach), and over
     2 GiB (the sustained rate).
   * cpu_baseline: the CPU oracle on the same workload, all rows, fresh activations, for
-    about --cpu-seconds of host time, on the host's cores (threads stated).
+    about --cpu-seconds of wall time on every core it may use (at most OMP_NUM_THREADS),
+    then half that on one thread; the host's core counts and CPU model beside them.
 
-Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+Prints one JSON line.  --gpus above 1 is refused: the benchmark measures one GPU.
 """
 from __future__ import annotations
 
@@ -328,45 +329,84 @@ def make_inputs(wl, n_act):
     return fields, xs
 
 
-def cpu_baseline(mats, xs, mode, seconds, image_bytes):
-    import oracle
-
+def host_threads():
+    """The host description a CPU baseline carries and the thread count of its all-cores run:
+    every core this process may run on, but no more than OMP_NUM_THREADS when that is set (a
+    host shared by several GPUs gives each its share through it)."""
     try:
-        cores = len(os.sched_getaffinity(0))
+        avail = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count() or 1
-    threads = max(1, min(16, cores))
-    oracle.set_threads(threads)
+        avail = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = avail
+    if omp and omp.isdigit() and int(omp) > 0:
+        threads = min(avail, int(omp))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    host = {"nproc": os.cpu_count(), "affinity_cpus": avail, "omp_num_threads": omp, "cpu_model": model}
+    return threads, host
+
+
+def timed_runs(step, seconds):
+    """step(k) repeated for about `seconds` of wall time; (steps, seconds taken)."""
     t0 = time.perf_counter()
     steps = 0
-    outs = []
     while True:
-        x = xs[steps % len(xs)]
-        c, m, e, _ = oracle.quantize(x, mode, block=oracle.act_block(mats[0]["fmt"], mode))
-        out = np.concatenate([oracle.gemm(f, c, m, e, mode).reshape(xs[0].shape[0], -1) for f in mats], axis=1)
-        if steps < 2:
-            outs.append(out)
+        step(steps)
         steps += 1
         dt = time.perf_counter() - t0
         if dt >= seconds:
-            break
+            return steps, dt
+
+
+def cpu_baseline(mats, xs, mode, seconds, image_bytes):
+    """The oracle on the same workload, whole steps with fresh activations: once on all the
+    threads host_threads() allows (the reported value) and once on one thread."""
+    import oracle
+
+    threads, host = host_threads()
+    outs = []
+
+    def step(k):
+        x = xs[k % len(xs)]
+        c, m, e, _ = oracle.quantize(x, mode, block=oracle.act_block(mats[0]["fmt"], mode))
+        out = np.concatenate([oracle.gemm(f, c, m, e, mode).reshape(xs[0].shape[0], -1) for f in mats], axis=1)
+        if k < 2 and len(outs) < 2:
+            outs.append(out)
+
     total_rows = sum(f["rows"] for f in mats)
     rows = total_rows * xs[0].shape[0]
+    what = f"quantize + all {total_rows} rows x {xs[0].shape[0]} column(s)"
+    oracle.set_threads(1)
+    s1, d1 = timed_runs(step, seconds / 2)
+    oracle.set_threads(threads)
+    steps, dt = timed_runs(step, seconds)
     return {
         "value": round(steps * image_bytes / dt / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{steps} whole steps (quantize + all {total_rows} rows x {xs[0].shape[0]} column(s)) "
-                  f"of the same workload with fresh activations, {dt:.1f} s",
+        "sample": f"{steps} whole steps ({what}) of the same workload with fresh activations on {threads} "
+                  f"threads, {dt:.1f} s",
         "rows_per_s": round(steps * rows / dt, 1),
+        "single_thread": {"value": round(s1 * image_bytes / d1 / 1e9, 3), "unit": "GB/s", "threads": 1,
+                          "sample": f"{s1} whole steps ({what}) on one thread, {d1:.1f} s",
+                          "rows_per_s": round(s1 * rows / d1, 1)},
+        "host": host,
     }, outs
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
         copy_probe(int(args.copy_probe))
@@ -793,36 +833,38 @@ def kv_main(args, wl, torch, qg, hip):
     if not args.no_cpu:
         import oracle
 
-        try:
-            cores = len(os.sched_getaffinity(0))
-        except AttributeError:
-            cores = os.cpu_count() or 1
-        threads = max(1, min(16, cores))
-        oracle.set_threads(threads)
+        threads, host = host_threads()
         kh, kcc = oracle.kv_cache_rows(keys.reshape(-1, hd))
         vh, vcc = oracle.kv_cache_rows(vals.reshape(-1, hd))
         kh, kcc = kh.reshape(nkv, npos), kcc.reshape(nkv, npos, hd)
         vh, vcc = vh.reshape(nkv, npos), vcc.reshape(nkv, npos, hd)
         q0 = qs[0].cpu().numpy()
-        t0 = time.perf_counter()
-        steps = 0
-        while True:
-            qn = qs[steps % n_q].cpu().numpy() if steps else q0
-            oracle.kv_cache_rows(new_rows[steps % n_q].cpu().numpy())
+        parity = None
+
+        def step(k):
+            nonlocal parity
+            qn = qs[k % n_q].cpu().numpy() if k else q0
+            oracle.kv_cache_rows(new_rows[k % n_q].cpu().numpy())
             c, m_, e_ = oracle.kv_quantize_heads(qn, mode)
             sc_o = oracle.kv_scores(mode, c, m_, e_, kh, kcc)
             out_o = oracle.kv_weighted(weights, vh, vcc)
-            if steps == 0:
+            if k == 0 and parity is None:
                 parity = bool(np.array_equal(sc_o.view(np.uint32), first_sc.view(np.uint32))
                               and np.array_equal(out_o.view(np.uint32), first_out.view(np.uint32)))
-            steps += 1
-            dt = time.perf_counter() - t0
-            if dt >= args.cpu_seconds:
-                break
+
+        what = "append, quantize, all scores, weighted sum"
+        oracle.set_threads(1)
+        s1, d1 = timed_runs(step, args.cpu_seconds / 2)
+        oracle.set_threads(threads)
+        steps, dt = timed_runs(step, args.cpu_seconds)
         record["cpu_baseline"] = {"value": round(steps * b_step / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
                                   "kind": "oracle",
-                                  "sample": f"{steps} whole steps (append, quantize, all scores, weighted sum) of "
-                                            f"the same workload, {dt:.1f} s"}
+                                  "sample": f"{steps} whole steps ({what}) of the same workload on {threads} "
+                                            f"threads, {dt:.1f} s",
+                                  "single_thread": {"value": round(s1 * b_step / d1 / 1e9, 3), "unit": "GB/s",
+                                                    "threads": 1,
+                                                    "sample": f"{s1} whole steps ({what}) on one thread, {d1:.1f} s"},
+                                  "host": host}
         record["parity_step0"] = parity
     print(json.dumps(record), flush=True)
 

@@ -14,6 +14,8 @@ import pytest
 import block_format_gemv_amd as qg
 from workloads import gen
 
+from image_layout import _tiles, unpack_b32, unpack_q4k, unpack_q6k
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
@@ -32,74 +34,6 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(qg.EXPORTS)
 
 
-# --- independent unpackers (from the layout described in qgemv.h) ---------------------------
-
-def _tiles(img: np.ndarray, rows: int, cols: int, tile_bytes: int):
-    """Image -> array [groups, G, tile_bytes]; tile (g, b) holds rows 64g..64g+63 of block b."""
-    G = cols // 256
-    groups = -(-rows // 64)
-    return img.reshape(groups, G, tile_bytes), G, groups
-
-
-def unpack_q4k(img: np.ndarray, rows: int, cols: int) -> dict:
-    t, G, groups = _tiles(img, rows, cols, 9216)
-    chunks = t[..., :8192].reshape(groups, G, 8, 64, 16)        # [g, b, chunk i, lane, byte k]
-    meta = t[..., 8192:].reshape(groups, G, 64, 16)             # [g, b, lane, 16]
-    sub = np.concatenate([chunks & 15, chunks >> 4], axis=4)    # element 32i + (k | 16 + k)
-    q = sub.transpose(0, 3, 1, 2, 4).reshape(groups * 64, cols)[:rows]
-    m = meta.transpose(0, 2, 1, 3).reshape(groups * 64, G, 16)[:rows].astype(np.uint64)
-    d = (m[..., 0] | (m[..., 1] << 8)).astype(np.uint16)
-    dmin = (m[..., 2] | (m[..., 3] << 8)).astype(np.uint16)
-    sc = np.zeros((rows, G, 8), np.uint8)
-    mn = np.zeros((rows, G, 8), np.uint8)
-    for r in range(rows):
-        for b in range(G):
-            bits = int.from_bytes(bytes(m[r, b, 4:16].astype(np.uint8)), "little")
-            for j in range(8):
-                field = (bits >> (12 * j)) & 0xFFF
-                sc[r, b, j] = field & 63
-                mn[r, b, j] = field >> 6
-    return {"q": q, "sc": sc.reshape(rows, G * 8), "mn": mn.reshape(rows, G * 8), "d": d, "dmin": dmin}
-
-
-def unpack_q6k(img: np.ndarray, rows: int, cols: int) -> dict:
-    t, G, groups = _tiles(img, rows, cols, 13440)
-    ql = t[..., :8192].reshape(groups, G, 8, 64, 16)
-    qh = t[..., 8192:12288].reshape(groups, G, 4, 64, 16)
-    sc = t[..., 12288:13312].reshape(groups, G, 64, 16).view(np.int8)
-    d = t[..., 13312:13440].reshape(groups, G, 64, 2).astype(np.uint16)
-    low = np.concatenate([ql & 15, ql >> 4], axis=4)             # [g, b, i, lane, 32]
-    low = low.transpose(0, 1, 3, 2, 4).reshape(groups, G, 64, 256)
-    high = np.zeros((groups, G, 64, 256), np.uint8)
-    for h in range(4):
-        for f in range(4):
-            high[..., 64 * h + 16 * f:64 * h + 16 * f + 16] = (qh[:, :, h] >> (2 * f)) & 3
-    q = (low | (high << 4)).transpose(0, 2, 1, 3).reshape(groups * 64, cols)[:rows]
-    dd = (d[..., 0] | (d[..., 1] << 8)).transpose(0, 2, 1).reshape(groups * 64, G)[:rows]
-    scs = sc.transpose(0, 2, 1, 3).reshape(groups * 64, G * 16)[:rows]
-    return {"q": q, "sc": scs, "d": dd}
-
-
-def unpack_b32(img: np.ndarray, fmt: int, rows: int, cols: int) -> dict:
-    """Q8_0-style: sixteen chunks of 16 int8 codes (elements 16i..16i+15) then the eight f16
-    scales; Q4_0-style: eight nibble-split chunks (one 32-element block each) then the scales."""
-    tb = 17408 if fmt == qg.Q8_0 else 9216
-    t, G, groups = _tiles(img, rows, cols, tb)
-    if fmt == qg.Q8_0:
-        codes = t[..., :16384].reshape(groups, G, 16, 64, 16).transpose(0, 1, 3, 2, 4).reshape(groups, G, 64, 256)
-        dpart = t[..., 16384:]
-    else:
-        ch = t[..., :8192].reshape(groups, G, 8, 64, 16)
-        codes = np.concatenate([ch & 15, ch >> 4], axis=4).transpose(0, 1, 3, 2, 4).reshape(groups, G, 64, 256)
-        dpart = t[..., 8192:]
-    q = codes.transpose(0, 2, 1, 3).reshape(groups * 64, cols)[:rows]
-    if fmt == qg.Q8_0:
-        q = q.view(np.int8)
-    dp = dpart.reshape(groups, G, 64, 8, 2).astype(np.uint16)
-    d = (dp[..., 0] | (dp[..., 1] << 8)).transpose(0, 2, 1, 3).reshape(groups * 64, G * 8)[:rows]
-    return {"q": q, "d": d}
-
-
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
 @pytest.mark.parametrize("rows,cols", [(1, 256), (5, 768), (64, 1024), (70, 512)])
 def test_b32_pack_roundtrip(fmt, rows, cols):
@@ -107,7 +41,7 @@ def test_b32_pack_roundtrip(fmt, rows, cols):
     code = qg.FMT_CODES[fmt]
     img = qg.pack(f)
     assert img.nbytes == qg.qg_image_bytes(code, rows, cols)
-    u = unpack_b32(img, code, rows, cols)
+    u = unpack_b32(img, code == qg.Q8_0, rows, cols)
     assert np.array_equal(u["q"], f["q"]) and np.array_equal(u["d"], f["d"])
     if rows % 64:
         t, G, groups = _tiles(img, rows, cols, 17408 if code == qg.Q8_0 else 9216)
