@@ -163,6 +163,78 @@ struct ActPlanes {
     __device__ __forceinline__ qg_act_scale scale(int b, int j, int per_block) const { return w.scale(b, j, per_block); }
 };
 
+// The same values as ActPlanes and ActWaveCodes, handed out through a wave-private LDS area
+// instead of v_readlane (one VALU instruction per value): every lane writes its share, then
+// each lane reads the whole set back with broadcast ds_read_b128 (one address for the wave), so
+// the values arrive as wave-uniform VGPRs.  A wave's LDS operations run in order, so its reads
+// see its writes; a later block's writes come after this block's reads in program order.
+constexpr int kActAreaWords = 160;   // per wave: 128 plane (or code) words, then 32 of sums
+
+__device__ __forceinline__ uint4 lds_bcast16(const uint32_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+struct ActPlanesLds {
+    uint32_t al[32], ah[32];
+    int kh[8], s32[8];
+    ActWave w;
+    __device__ __forceinline__ ActPlanesLds(const ActWave &a, uint32_t *area, int lane) : w(a)
+    {
+        const uint32_t lo = a.packed & 0x0F0F0F0Fu;
+        const uint32_t hi = (a.packed >> 4) & 0x0F0F0F0Fu;
+        const uint32_t AL = lo | ((uint32_t)dpp<kDppRowShl4>((int)lo) << 4);
+        const uint32_t AH = hi | ((uint32_t)dpp<kDppRowShl4>((int)hi) << 4);
+        const int sh = quad_sum(__builtin_amdgcn_sdot8((int)AH, 0x11111111, 0, false));
+        area[lane] = AL;
+        area[64 + lane] = AH;
+        if ((lane & 7) == 0) {
+            area[128 + (lane >> 3)] = (uint32_t)(8 * sh);
+            area[136 + (lane >> 3)] = (uint32_t)a.s32;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint4 l4 = lds_bcast16(area + 8 * i), h4 = lds_bcast16(area + 64 + 8 * i);
+            al[4 * i] = l4.x; al[4 * i + 1] = l4.y; al[4 * i + 2] = l4.z; al[4 * i + 3] = l4.w;
+            ah[4 * i] = h4.x; ah[4 * i + 1] = h4.y; ah[4 * i + 2] = h4.z; ah[4 * i + 3] = h4.w;
+        }
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const uint4 a4 = lds_bcast16(area + 128 + 4 * k), s4 = lds_bcast16(area + 136 + 4 * k);
+            kh[4 * k] = (int)a4.x; kh[4 * k + 1] = (int)a4.y; kh[4 * k + 2] = (int)a4.z; kh[4 * k + 3] = (int)a4.w;
+            s32[4 * k] = (int)s4.x; s32[4 * k + 1] = (int)s4.y; s32[4 * k + 2] = (int)s4.z; s32[4 * k + 3] = (int)s4.w;
+        }
+    }
+    __device__ __forceinline__ int sum32(int, int j) const { return s32[j]; }
+    __device__ __forceinline__ int sum16(int b, int k) const { return w.sum16(b, k); }
+    __device__ __forceinline__ qg_act_scale scale(int b, int j, int per_block) const { return w.scale(b, j, per_block); }
+};
+
+struct ActCodesLds {
+    uint32_t c[64];
+    int s16[16];
+    ActWave w;
+    __device__ __forceinline__ ActCodesLds(const ActWave &a, uint32_t *area, int lane) : w(a)
+    {
+        area[lane] = a.packed;
+        if ((lane & 3) == 0) area[128 + (lane >> 2)] = (uint32_t)a.s16;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const uint4 v = lds_bcast16(area + 4 * i);
+            c[4 * i] = v.x; c[4 * i + 1] = v.y; c[4 * i + 2] = v.z; c[4 * i + 3] = v.w;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint4 v = lds_bcast16(area + 128 + 4 * k);
+            s16[4 * k] = (int)v.x; s16[4 * k + 1] = (int)v.y; s16[4 * k + 2] = (int)v.z; s16[4 * k + 3] = (int)v.w;
+        }
+    }
+    __device__ __forceinline__ uint4 codes16(int, int i) const
+    {
+        return make_uint4(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
+    }
+    __device__ __forceinline__ int sum32(int b, int j) const { return w.sum32(b, j); }
+    __device__ __forceinline__ int sum16(int, int k) const { return s16[k]; }
+    __device__ __forceinline__ qg_act_scale scale(int b, int j, int per_block) const { return w.scale(b, j, per_block); }
+};
+
 // ---------------------------------------------------------------------------------------
 // Weight-side decoding
 
@@ -200,6 +272,25 @@ template <class Act>
 __device__ __forceinline__ int q4k_sub(const uint4 &w, int b, int i, const Act &act)
 {
     return q4k_sub_dot(w, act.codes16(b, 2 * i), act.codes16(b, 2 * i + 1));
+}
+
+template <class Planes>
+__device__ __forceinline__ int q4k_sub_planes(const uint4 &w, int i, const Planes &p)
+{
+    int X = p.kh[i];
+    uint32_t Y = 0;
+    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        X = __builtin_amdgcn_sdot8((int)(q[d] ^ 0x88888888u), (int)p.ah[4 * i + d], X, false);
+        Y = __builtin_amdgcn_udot8(q[d], p.al[4 * i + d], Y, false);
+    }
+    return 16 * X + (int)Y;
+}
+
+__device__ __forceinline__ int q4k_sub(const uint4 &w, int, int i, const ActPlanesLds &p)
+{
+    return q4k_sub_planes(w, i, p);
 }
 
 __device__ __forceinline__ int q4k_sub(const uint4 &w, int, int i, const ActPlanes &p)
@@ -713,6 +804,20 @@ __device__ __forceinline__ ActWave ready_act(const ActRaw<SRC> &r, int b, int G,
 // The block's piece: its codes go to scalar registers (as nibble planes for Q4_K-style
 // tiles) before the tile's data is waited for.
 template <int FMT, int MODE>
+__device__ __forceinline__ float piece_one_lds(const TileRegs<FMT> &t, int b, const ActWave &a, uint32_t *area, int lane)
+{
+    if constexpr (FMT == QG_Q4K) {
+        const ActPlanesLds p(a, area, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        return pair_piece<MODE>(t, b, p);
+    } else {
+        const ActCodesLds c(a, area, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        return pair_piece<MODE>(t, b, c);
+    }
+}
+
+template <int FMT, int MODE>
 __device__ __forceinline__ float piece_one(const TileRegs<FMT> &t, int b, const ActWave &a)
 {
     if constexpr (FMT == QG_Q4K) {
@@ -821,8 +926,10 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
     extern __shared__ __align__(16) float s_piece[];
     using T = TileRegs<FMT>;
     constexpr int BITS = ActKind<FMT, MODE>::kBits, GL = ActKind<FMT, MODE>::kLanes;
-    // pieces: G per row with DB, else W (one per wave); then one flag byte per wave
+    // pieces: G per row with DB, else W (one per wave); then one flag byte per wave (16 bytes);
+    // then each wave's activation area
     unsigned char *s_small = reinterpret_cast<unsigned char *>(s_piece + (size_t)(DB ? G : W) * 64);
+    [[maybe_unused]] uint32_t *area = reinterpret_cast<uint32_t *>(s_small + 16) + (threadIdx.x >> 6) * kActAreaWords;
     bool small = false;                          // a block of this wave may give a tiny piece
     const Picked pm = pick_matrix(tg, (int)blockIdx.x);   // this workgroup's matrix (wave-uniform)
     const int g = pm.g;
@@ -884,7 +991,11 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
         } while (true);
     } else {
         // at most one block per wave; a wave past the last block computes a copy and parks +0
-        const float p = piece_one<FMT, MODE>(t0, bf, a0);
+        // Q4_K-style: the activation planes through LDS (the code words of a Q6_K-style block
+        // would not fit the registers of 16 waves beside its tile)
+        float p;
+        if constexpr (FMT == QG_Q4K) p = piece_one_lds<FMT, MODE>(t0, bf, a0, area, lane);
+        else p = piece_one<FMT, MODE>(t0, bf, a0);
         s_piece[(size_t)wid * 64 + lane] = wid < G ? p : 0.0f;
         small |= __ballot(a0.e < kNoTinyExp) != 0;
     }
@@ -925,6 +1036,16 @@ __global__ __launch_bounds__(64 * W) void gemv1_kernel(const Targets tg, int G, 
 // kk, and reach its lanes by DPP row broadcasts.  Each lane's two integer sub-block sums and
 // offset sums are added over the four lane groups (exact integers), then lanes kk = 0 form the
 // pieces; the first wave adds each row's pieces in block order.
+
+// v summed over the four 16-lane rows of the wave, in every lane: each swap with a copy of
+// itself leaves the two halves (rows) to be added side by side in every lane
+__device__ __forceinline__ int sum_over_rows(int v)
+{
+    const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);   // lanes l, l ^ 32
+    const int s = (int)h[0] + (int)h[1];
+    const auto r = __builtin_amdgcn_permlane16_swap(s, s, false, false);   // rows 2k, 2k + 1
+    return (int)r[0] + (int)r[1];
+}
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t row_bcast(uint32_t v)   // lane n of the lane's row of 16 (CTRL = 0x150 + n)
@@ -994,11 +1115,9 @@ __global__ __launch_bounds__(1024) void gemv1_quarter_kernel(const Targets tg, i
     }
     int Cp = mad_i24(sc0, 16 * X0 + (int)Y0, mul_i24(sc1, 16 * X1 + (int)Y1));
     int Op = mad_i24(mn0, s0, mul_i24(mn1, s1));
-    // the four lane groups' partial sums (exact integers)
-    Cp += __shfl_xor(Cp, 16, 64);
-    Op += __shfl_xor(Op, 16, 64);
-    Cp += __shfl_xor(Cp, 32, 64);
-    Op += __shfl_xor(Op, 32, 64);
+    // the four lane groups' partial sums (exact integers), every lane getting the total
+    Cp = sum_over_rows(Cp);
+    Op = sum_over_rows(Op);
 
     const qg_act_scale sa = a.scale(b, 0, 1);
     const float fd = f16_value(meta.x), fm = f16_value(meta.x >> 16);
@@ -1259,7 +1378,8 @@ int launch_one_typed(const Targets &tg, int G, const ActIO &io, hipStream_t s)
     const int64_t groups = tg.gstart[tg.nmat];
     if (groups == 0) return QG_OK;
     if (!DB && G > W) return fail(QG_E_RUNTIME, "gemv: %d blocks do not fit %d waves", G, W);
-    const size_t lds = (size_t)(DB ? G : W) * 64 * sizeof(float) + 16;
+    const size_t area = FMT == QG_Q4K && !DB ? (size_t)W * kActAreaWords * sizeof(uint32_t) : 0;
+    const size_t lds = (size_t)(DB ? G : W) * 64 * sizeof(float) + 16 + area;
     hipEvent_t ev0, ev1;
     take_timing_events(&ev0, &ev1);
     if (ev0 && ev1)

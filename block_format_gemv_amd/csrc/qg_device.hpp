@@ -506,6 +506,22 @@ __device__ __forceinline__ bool sum8_pair(const double (&T)[8], int low, float &
     return true;
 }
 
+// The last steps of the first Sub32 path below: R32(2^emin * (d*IC - dmin*IO)) for the exact
+// integer sums IC = sum F_j C_j and IO = sum F_j O_j (F_j = m_j 2^(e_j - emin)); see there.
+__device__ __forceinline__ float sub32_near_finish(double IC, double IO, float fd, float fm, int emin)
+{
+    const double Dd = (double)fd;
+    const double p1 = IC * Dd;
+    const double e1 = __builtin_fma(IC, Dd, -p1);
+    const double p2 = -(IO * (double)fm);
+    const double s = p1 + p2;
+    const double bv = s - p1;
+    const double av = s - bv;
+    const double t = (p1 - av) + (p2 - bv);
+    const double u = t + e1;
+    return r32_sum2(__builtin_ldexp(s, emin), __builtin_ldexp(u, emin));
+}
+
 // Sub32, Q4_K-style: R32(sum_j m_j 2^e_j (d*C_j - dmin*O_j)), the sixteen terms of exact_sum.
 // When the block scales are near (q4k_near), X_j = d*C_j - dmin*O_j is exact in one fma (|C_j|
 // < 2^22, |O_j| < 2^18) and T_j = X_j * m_j 2^e_j too (m_j has 4 significant bits); with the sum
@@ -541,16 +557,7 @@ __device__ __forceinline__ float piece_q4k_sub32(const int (&C)[8], const int (&
             IC = __builtin_fma(F, (double)C[j], IC);
             IO = __builtin_fma(F, (double)O[j], IO);
         }
-        const double Dd = (double)fd;
-        const double p1 = IC * Dd;
-        const double e1 = __builtin_fma(IC, Dd, -p1);
-        const double p2 = -(IO * (double)fm);
-        const double s = p1 + p2;
-        const double bv = s - p1;
-        const double av = s - bv;
-        const double t = (p1 - av) + (p2 - bv);
-        const double u = t + e1;
-        return r32_sum2(__builtin_ldexp(s, emin), __builtin_ldexp(u, emin));
+        return sub32_near_finish(IC, IO, fd, fm, emin);
     }
     if (near) {
         double T[8];
