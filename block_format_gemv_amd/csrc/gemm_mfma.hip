@@ -854,7 +854,9 @@ int launch_split(int64_t rows, int G, int64_t ncol, const void *image, const int
 {
     int rtt = tuning().gemm_row_tiles;
     int ct = tuning().mfma_col_tiles;
-    if (ct == 0) ct = ncol <= 16 ? 1 : 2;
+    // derived: two row tiles of one column tile (two of each need more registers than 16 waves
+    // have and spill to scratch; one row tile of two column tiles measured slower)
+    if (ct == 0) ct = 1;
     if (rtt == 0) rtt = 2;
     const bool multi = G > 16;
     if (multi && rtt * ct > 4) {   // two slots of pieces: at most 64 KiB each

@@ -340,7 +340,8 @@ int qg_stream_read_shape(const void *buf, size_t bytes, int waves_per_wg, int ki
  *                         LDS), 3 = split (every wave one block, the activation operands loaded per
  *                         wave); 0 = derived from the shape
  *   QG_TUNE_MFMA_COL_TILES 1, 2 or 4: 16-column tiles per workgroup of the shared-operand and
- *                         split forms; 0 = derived from the columns
+ *                         split forms; 0 = derived (one for the split form, from the columns for
+ *                         the shared-operand form)
  *   QG_TUNE_COLS_KERNEL   several columns below the matrix-core threshold (Q4_K/Q6_K, at most 16
  *                         blocks per row): 0 = the one-column kernel's machinery, NC columns per
  *                         wave (default); 1 = the kernel that stages the columns in LDS
