@@ -55,16 +55,18 @@ KERNEL_SOURCES = ("block_format_gemv_amd/csrc/gemv.hip", "block_format_gemv_amd/
                   "block_format_gemv_amd/csrc/qg_internal.hpp")
 MEASURED_TRAFFIC = {
     # (workload, dominant kernel): medians per dispatch, kernel sources hash
-    ("q4k_ffn_up_14336x4096", "fused"): {"kernel_sha": "e22e074b3cb4621a", "fetch_kib": 16242.5, "write_kib": 61.0625},
-    ("q4k_ffn_up_14336x4096", "gemv"): {"kernel_sha": "e22e074b3cb4621a", "fetch_kib": 16189.5, "write_kib": 56.0},
-    ("q4k_sub32_14336x4096", "fused"): {"kernel_sha": "e22e074b3cb4621a", "fetch_kib": 16286.0, "write_kib": 61.5},
-    ("q4k_sub32_14336x4096", "gemv"): {"kernel_sha": "e22e074b3cb4621a", "fetch_kib": 16238.5, "write_kib": 56.0},
-    ("q6k_output_128256x4096", "fused"): {"kernel_sha": "e22e074b3cb4621a", "fetch_kib": 210544.5, "write_kib": 506.0625},
-    ("q6k_output_128256x4096", "gemv"): {"kernel_sha": "e22e074b3cb4621a", "fetch_kib": 210485.0, "write_kib": 501.0},
-    ("q8_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "e22e074b3cb4621a", "fetch_kib": 30578.5, "write_kib": 61.5},
-    ("q8_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "e22e074b3cb4621a", "fetch_kib": 30527.0, "write_kib": 56.0},
-    ("q4_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "e22e074b3cb4621a", "fetch_kib": 16252.0, "write_kib": 61.5},
-    ("q4_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "e22e074b3cb4621a", "fetch_kib": 16195.5, "write_kib": 56.0},
+    ("q4k_ffn_up_14336x4096", "fused"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 16242.5, "write_kib": 61.0625},
+    ("q4k_ffn_up_14336x4096", "gemv"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 16183.0, "write_kib": 56.0},
+    ("q4k_attn_4096x4096", "fused"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 4716.5, "write_kib": 21.0625},
+    ("q4k_attn_4096x4096", "gemv"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 4656.5, "write_kib": 16.0},
+    ("q4k_sub32_14336x4096", "fused"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 16289.5, "write_kib": 61.5},
+    ("q4k_sub32_14336x4096", "gemv"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 16234.0, "write_kib": 56.0},
+    ("q6k_output_128256x4096", "fused"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 210543.5, "write_kib": 506.0625},
+    ("q6k_output_128256x4096", "gemv"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 210481.0, "write_kib": 501.0},
+    ("q8_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 30581.0, "write_kib": 61.5},
+    ("q8_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 30520.5, "write_kib": 56.0},
+    ("q4_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 16252.0, "write_kib": 61.5},
+    ("q4_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 16190.5, "write_kib": 56.0},
 }
 
 # The batched GEMM kernels (several columns): HBM traffic as above, and for the int8
@@ -76,9 +78,12 @@ MEASURED_TRAFFIC = {
 GEMM_SOURCES = KERNEL_SOURCES + ("block_format_gemv_amd/csrc/gemm_mfma.hip",)
 MFMA_PEAK_TOPS = 5000.0     # dense int8 matrix-core peak of the part, TOP/s
 MEASURED_GEMM = {
-    "q4k_gemm_n2_14336x4096": {"kernel_sha": "fa8f343d31d297dd", "fetch_kib": 16217.5, "write_kib": 112.0},
-    "q4k_gemm_n8_14336x4096": {"kernel_sha": "fa8f343d31d297dd", "fetch_kib": 16447.5, "write_kib": 448.0},
-    "q4k_gemm_n64_14336x4096": {"kernel_sha": "fa8f343d31d297dd", "fetch_kib": 17567.6875, "write_kib": 3584.0, "mops_i8": 44040192.0, "mfma_util_pct": 11.43},
+    "q4k_gemm_n2_4096x4096": {"kernel_sha": "1cefc69e291f08b9", "fetch_kib": 4687.5, "write_kib": 32.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.43},
+    "q4k_gemm_n8_4096x4096": {"kernel_sha": "1cefc69e291f08b9", "fetch_kib": 4785.0, "write_kib": 128.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.3},
+    "q4k_gemm_n64_4096x4096": {"kernel_sha": "1cefc69e291f08b9", "fetch_kib": 5724.5, "write_kib": 1024.0, "mops_i8": 12582912.0, "mfma_util_pct": 5.98},
+    "q4k_gemm_n2_14336x4096": {"kernel_sha": "1cefc69e291f08b9", "fetch_kib": 16213.5, "write_kib": 112.0},
+    "q4k_gemm_n8_14336x4096": {"kernel_sha": "1cefc69e291f08b9", "fetch_kib": 16328.5, "write_kib": 448.0, "mops_i8": 11010048.0, "mfma_util_pct": 5.29},
+    "q4k_gemm_n64_14336x4096": {"kernel_sha": "1cefc69e291f08b9", "fetch_kib": 17570.9375, "write_kib": 3584.0, "mops_i8": 44040192.0, "mfma_util_pct": 12.51},
 }
 
 
