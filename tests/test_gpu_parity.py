@@ -537,7 +537,7 @@ def test_matrix_core_gemm_matches_oracle(qg, ncol):
 
 @pytest.mark.parametrize("ncol", [64, 100])
 def test_matrix_core_gemm_16_blocks(qg, ncol):
-    """Rows of 16 blocks take the shared-operand kernel whose block loop is unrolled when
+    """Rows of 16 blocks through the shared-operand kernel, whose block loop is unrolled when
     compiled: ragged rows and columns, block scales that take both the near-exponent and the
     general combine, and (in the second run) a row of tiny activations, which makes its batch
     of 64 columns take the flushed combine; with and without the scale tables."""
@@ -553,6 +553,7 @@ def test_matrix_core_gemm_16_blocks(qg, ncol):
         act, c, m, e, _ = gpu_quant(qg, xs, 0)
         want = oracle.gemm(f, c, m, e, 0).reshape(ncol, rows)
         try:
+            qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 2)      # the shared-operand form on these 130 rows too
             for tab in (0, 1):
                 qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, tab)
                 say("matrix-core gemm, 16 blocks", ncol, "tiny row", tiny, "tables off", tab)
@@ -560,6 +561,7 @@ def test_matrix_core_gemm_16_blocks(qg, ncol):
                 assert first_mismatch(out, want) is None, (ncol, tiny, tab, first_mismatch(out, want))
         finally:
             qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, 0)
+            qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 0)
 
 
 @pytest.mark.parametrize("cols", [6144, 8192, 12288])
@@ -567,7 +569,8 @@ def test_matrix_core_gemm_long_rows(qg, cols):
     """Rows of 24, 32 and 48 blocks through the shared-operand kernel: at 24 blocks the scale
     tables fit in LDS beside the operand stages (the block loop runs with three prefetch
     buffers), at 32 and 48 they do not and each block loads its own scales; 40 columns, ragged
-    rows, far block-scale pairs and one row of tiny activations."""
+    rows, far block-scale pairs and one row of tiny activations; and the form the dispatch
+    derives for these 70 rows (split)."""
     rows, ncol = 70, 40
     f = _adversarial_fields("q4k", rows, cols, 5100 + cols // 256)
     _subnormal_partial_q4k(f, 3)
@@ -576,9 +579,14 @@ def test_matrix_core_gemm_long_rows(qg, cols):
     xs[7, :] = np.float32(2.0 ** -112)
     act, c, m, e, _ = gpu_quant(qg, xs, 0)
     want = oracle.gemm(f, c, m, e, 0).reshape(ncol, rows)
-    say("matrix-core gemm, long rows", cols)
-    out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
-    assert first_mismatch(out, want) is None, (cols, first_mismatch(out, want))
+    try:
+        for form in (2, 0):
+            qg.qg_set_tuning(qg.TUNE_MFMA_FORM, form)
+            say("matrix-core gemm, long rows", cols, "form", form)
+            out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+            assert first_mismatch(out, want) is None, (cols, form, first_mismatch(out, want))
+    finally:
+        qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 0)
 
 
 @pytest.mark.parametrize("cols,ncol", [(1280, 5), (1280, 64), (3072, 16), (4096, 1), (4096, 2), (4096, 8), (4096, 33),
