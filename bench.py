@@ -701,9 +701,10 @@ def kv_main(args, wl, torch, qg, hip):
     """One decode step of attention over an int8 KV cache: the step appends the new
     position's key and value rows to the cache (qg_kv_cache_rows), quantizes the query heads
     (qg_kv_quantize_heads), scores them against every cached key (qg_kv_scores) and forms the
-    weighted sum of the cached values (qg_kv_weighted) with given attention weights (the
-    softmax between the two is the caller's and is not timed).  The caches rotate over copies
-    of at least --cold-bytes, like the GEMV's weights."""
+    weighted sum of the cached values in two passes (qg_kv_weighted_with_workspace; the
+    one-pass qg_kv_weighted is timed beside it) with given attention weights (the softmax
+    between the two is the caller's and is not timed).  The caches rotate over copies of at
+    least --cold-bytes, like the GEMV's weights."""
     from workloads import gen
 
     _, nh, nkv, npos, hd, mode = wl
@@ -742,7 +743,14 @@ def kv_main(args, wl, torch, qg, hip):
         k = caches[i % copies]
         qg.qg_kv_scores(mode, nh, nkv, npos, hd, qc[i % slots], qsc[i % slots], k[0], k[1], sc[i % slots], stream)
 
+    ws = [torch.empty(qg.qg_kv_weighted_workspace(nh, npos, hd), dtype=torch.uint8, device=dev)
+          for _ in range(2)]
+
     def weighted(i, stream=None):
+        k = caches[i % copies]
+        qg.qg_kv_weighted_with_workspace(nh, nkv, npos, hd, probs, k[2], k[3], out[i % slots], ws[i % 2], stream)
+
+    def weighted_one_pass(i, stream=None):
         k = caches[i % copies]
         qg.qg_kv_weighted(nh, nkv, npos, hd, probs, k[2], k[3], out[i % slots], stream)
 
@@ -801,10 +809,11 @@ def kv_main(args, wl, torch, qg, hip):
     ms_per_step = ms_total / args.steps
     us_scores = per_call_us(scores, args.kernel_launches)
     us_weighted = per_call_us(weighted, args.kernel_launches)
+    us_weighted_one = per_call_us(weighted_one_pass, args.kernel_launches // 4)
     us_quant = per_call_us(quant, args.kernel_launches // 4)
     us_append = per_call_us(append, args.kernel_launches // 4)
     dom = ("kv_scores_kernel", us_scores, b_scores) if us_scores >= us_weighted else \
-        ("kv_weighted_kernel", us_weighted, b_weighted)
+        ("kv_weighted_pieces_kernel + kv_weighted_fold_kernel", us_weighted, b_weighted)
     achieved = dom[2] / (dom[1] * 1e-6) / 1e9
     value = b_step / (ms_per_step * 1e-3) / 1e9
     record = {
@@ -826,10 +835,12 @@ def kv_main(args, wl, torch, qg, hip):
             "query_scaling": "perblock" if mode == 0 else "sub32",
             "cache": "cold, rotating over %d copies (%.0f MB)" % (copies, copies * cache_bytes / 1e6)
                      if copies > 1 else "warm, one copy (cache-resident)",
-            "step": "qg_kv_cache_rows + qg_kv_quantize_heads + qg_kv_scores + qg_kv_weighted, HIP graph replay",
+            "step": "qg_kv_cache_rows + qg_kv_quantize_heads + qg_kv_scores + qg_kv_weighted_with_workspace, "
+                    "HIP graph replay",
         },
         "algorithmic_bytes_per_step": b_step,
-        "kernels_us": {"kv_scores": round(us_scores, 3), "kv_weighted": round(us_weighted, 3),
+        "kernels_us": {"kv_scores": round(us_scores, 3), "kv_weighted_two_pass": round(us_weighted, 3),
+                       "kv_weighted_one_pass": round(us_weighted_one, 3),
                        "kv_quantize_heads": round(us_quant, 3), "kv_cache_rows": round(us_append, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom[0],

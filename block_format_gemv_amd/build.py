@@ -2,7 +2,8 @@
 
 Every source under csrc/ is compiled by hipcc for --offload-arch=gfx950 with
 -ffp-contract=off (no contraction of the exact f64/f32 steps), no fast-math and IEEE
-denormal handling, and with packed-f32 instruction selection disabled; objects go to
+denormal handling (but for the weighted sum's fold, kv_fold.hip, which flushes binary32
+subnormals), and with packed-f32 instruction selection disabled; objects go to
 _build/ and are linked into one shared library exporting the C ABI of include/qgemv.h.
 """
 from __future__ import annotations
@@ -36,8 +37,10 @@ DEVICE = [f"--offload-arch={ARCH}", "-fno-gpu-rdc",
 
 
 # per-source device flags: the matrix-core GEMM keeps its MFMA accumulators in ordinary VGPRs
-# (no copies out of AGPRs before the epilogue reads them)
-EXTRA = {"gemm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# (no copies out of AGPRs before the epilogue reads them); the weighted sum's fold runs with
+# binary32 subnormals flushed (preserve-sign), the flushed add of its definition in hardware
+EXTRA = {"gemm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "kv_fold.hip": ["-fgpu-flush-denormals-to-zero"]}
 
 
 def sources():

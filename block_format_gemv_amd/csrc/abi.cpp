@@ -409,6 +409,38 @@ int qg_kv_weighted(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const floa
     return launch_kv_weighted(nh, nkv, npos, hd, probs, vscales, vcodes, out, static_cast<hipStream_t>(stream));
 }
 
+int qg_kv_weighted_workspace(int64_t nh, int64_t npos, int64_t hd, size_t *bytes)
+{
+    const char *who = "qg_kv_weighted_workspace";
+    int st;
+    if ((st = check_kv(who, nh, 1, npos, hd))) return st;
+    if (bytes == nullptr) return fail(QG_E_INVALID, "%s: bytes is null", who);
+    *bytes = kv_weighted_workspace_bytes(nh, npos, hd);
+    return QG_OK;
+}
+
+int qg_kv_weighted_with_workspace(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs,
+                                  const uint16_t *vscales, const int8_t *vcodes, float *out, void *workspace,
+                                  size_t ws_bytes, void *stream)
+{
+    const char *who = "qg_kv_weighted_with_workspace";
+    int st;
+    if ((st = check_kv(who, nh, nkv, npos, hd))) return st;
+    if (nh == 0) return QG_OK;
+    if ((st = check_ptr(who, "out", out, 4))) return st;
+    const size_t need = kv_weighted_workspace_bytes(nh, npos, hd);
+    if (ws_bytes < need)
+        return fail(QG_E_INVALID, "%s: workspace of %zu bytes, %zu needed", who, ws_bytes, need);
+    if (npos > 0) {
+        if ((st = check_ptr(who, "probs", probs, 4))) return st;
+        if ((st = check_ptr(who, "vscales", vscales, 2))) return st;
+        if ((st = check_ptr(who, "vcodes", vcodes, 4))) return st;
+        if ((st = check_ptr(who, "workspace", workspace, 16))) return st;
+    }
+    return launch_kv_weighted_two_pass(nh, nkv, npos, hd, probs, vscales, vcodes, static_cast<float *>(workspace),
+                                       out, static_cast<hipStream_t>(stream));
+}
+
 int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
                   int32_t *csum_out, int32_t *osum_out, void *stream)
 {

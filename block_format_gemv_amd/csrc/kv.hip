@@ -176,6 +176,115 @@ __global__ __launch_bounds__(256) void kv_scores_kernel(int nh, int grp, int64_t
     if (have) out[(size_t)h * npos + j] = canon_nan(y);
 }
 
+// Lane quad k's share of one block of a query head (eight positions a lane): the weights p_j
+// and the value scales' bits.  Every load is issued, from position min(j, nj - 1) (nj >= 1), so
+// that none waits on a branch; the coding ignores positions past nj.
+__device__ __forceinline__ void load_weights(const float *ph, const uint16_t *vs, int64_t j0, int nj, int qq,
+                                             float (&p)[8], uint32_t (&sb)[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int j = min(qq * 8 + i, nj - 1);
+        p[i] = ph[j0 + j];
+        sb[i] = vs[j0 + j];
+    }
+}
+
+// A lane quad's coding of one block: w_j = p_j * d_j in binary32, absmax and the flags reduced
+// over the quad (quad_perm DPP), E from the absmax, and the codes rne(w_j / 2^E) of the lane's
+// eight positions, four to a word.  No branches around it, so that the loads feeding it stay
+// where they are issued.  The quotient is formed in binary32: when it is 0.5 or more in
+// magnitude it is a normal number and exact, and below that the hardware's result, however
+// rounded or flushed, is below 0.5 too, so the code is 0 as for the exact quotient.
+__device__ __forceinline__ void code_quad(const float (&p)[8], const uint32_t (&sb)[8], int nj, int qq,
+                                          uint32_t (&word)[2], int &E, bool &badb)
+{
+    uint32_t amax = 0;
+    int bad = 0;
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const bool in = qq * 8 + i < nj;
+        bad |= (in && ((sb[i] >> 10) & 31u) == 31u) ? 1 : 0;
+        w[i] = in ? p[i] * half_bits_value(sb[i]) : 0.0f;              // binary32 product
+        const uint32_t a = __float_as_uint(ftz(w[i])) & 0x7FFFFFFFu;
+        amax = (a <= 0x7F800000u && a > amax) ? a : amax;                // NaN passed over
+    }
+    amax = max(amax, (uint32_t)dpp<kDppQuadSwap1>((int)amax));
+    amax = max(amax, (uint32_t)dpp<kDppQuadSwap2>((int)amax));
+    bad |= dpp<kDppQuadSwap1>(bad);
+    bad |= dpp<kDppQuadSwap2>(bad);
+    badb = bad != 0 || amax == 0x7F800000u;
+    E = 0;
+    int m1 = 1;
+    if (!badb && amax != 0) least_scale<1>(__uint_as_float(amax), m1, E);
+#pragma unroll
+    for (int kw = 0; kw < 2; kw++) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const float f = ftz(w[4 * kw + t]);
+            const int u = (badb || f != f) ? 0 : (int)__builtin_rintf(__builtin_ldexpf(f, -E));
+            v |= ((uint32_t)u & 255u) << (8 * t);
+        }
+        word[kw] = v;
+    }
+}
+
+// The block's 32 value rows, four bytes of each (elements el .. el+3), rows past nj read from
+// row nj - 1 and then zeroed: every load unconditional.
+__device__ __forceinline__ void load_rows(const int8_t *vc, int hd, int64_t j0, int nj, int el,
+                                          uint32_t (&rows)[kValueBlock])
+{
+#pragma unroll
+    for (int t = 0; t < kValueBlock; t++)
+        rows[t] = *reinterpret_cast<const uint32_t *>(vc + (size_t)(j0 + min(t, nj - 1)) * hd + el);
+#pragma unroll
+    for (int t = 0; t < kValueBlock; t++) rows[t] = t < nj ? rows[t] : 0u;
+}
+
+// The rows transposed by byte permutes (v_perm: selector bytes 0..3 take the second operand's
+// bytes, 4..7 the first's): col[e][g] holds element e of positions 4g .. 4g+3, one byte each.
+__device__ __forceinline__ void transpose_rows(const uint32_t (&rows)[kValueBlock], uint32_t (&col)[4][kValueBlock / 4])
+{
+#pragma unroll
+    for (int g = 0; g < kValueBlock / 4; g++) {
+        const uint32_t *r4 = rows + 4 * g;
+        // interleave rows pairwise: (a0 b0 a1 b1) and (a2 b2 a3 b3), then pair the pairs
+        const uint32_t p01l = __builtin_amdgcn_perm(r4[1], r4[0], 0x05010400u);
+        const uint32_t p01h = __builtin_amdgcn_perm(r4[1], r4[0], 0x07030602u);
+        const uint32_t p23l = __builtin_amdgcn_perm(r4[3], r4[2], 0x05010400u);
+        const uint32_t p23h = __builtin_amdgcn_perm(r4[3], r4[2], 0x07030602u);
+        col[0][g] = __builtin_amdgcn_perm(p23l, p01l, 0x05040100u);
+        col[1][g] = __builtin_amdgcn_perm(p23l, p01l, 0x07060302u);
+        col[2][g] = __builtin_amdgcn_perm(p23h, p01h, 0x05040100u);
+        col[3][g] = __builtin_amdgcn_perm(p23h, p01h, 0x07060302u);
+    }
+}
+
+// A piece R32(T * 2^E) (flushed) for |T| < 2^24 and E >= -132, the least exponent a normal
+// absmax's scale has: (float)T is exact, and T * 2^E, a multiple of 2^-132 with at most 24
+// significant bits, lies on the binary32 grid (normal or subnormal) wherever it is below
+// 2^128, so ldexp is exact there and the flush is R32's; beyond, both are infinite.
+__device__ __forceinline__ float value_piece(int T, int E) { return ftz(__builtin_ldexpf((float)T, E)); }
+
+// The four elements' exact sums over the block, their dot chains interleaved, and the pieces
+// (NaN for a bad block), selected without a branch.
+__device__ __forceinline__ void block_pieces(const uint32_t (&col)[4][kValueBlock / 4], const uint32_t (&cw)[8], int E,
+                                             bool bad, float (&pc)[4])
+{
+    int T[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int g = 0; g < kValueBlock / 4; g++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) T[e] = __builtin_amdgcn_sdot4((int)col[e][g], (int)cw[g], T[e], false);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const float v = value_piece(T[e], E);
+        pc[e] = bad ? __uint_as_float(0x7FC00000u) : v;
+    }
+}
+
 // ---------------------------------------------------------------------------------------
 // weighted sum: one workgroup of W waves per (head, group of EG value elements).  A wave
 // covers BPW = 256 / EG blocks of 32 positions at a time, EG / 4 lanes per block, each lane
@@ -195,7 +304,12 @@ __global__ __launch_bounds__(64 * W) void kv_weighted_kernel(int grp, int64_t np
     constexpr int BPW = 64 / LPB;              // blocks per wave
     constexpr int RB = W * BPW;                // blocks per round
     __shared__ float s_piece[RB * EG];
-    const int h = blockIdx.x;
+    // workgroups go to the eight XCDs in turn (linear id mod 8); with the head count a multiple
+    // of 8 (then the linear id mod 8 is blockIdx.x mod 8), XCD x takes the consecutive heads
+    // x * nh / 8 .. (x + 1) * nh / 8 - 1, so heads that share a KV head share that XCD's L2
+    // and its value rows come from HBM once
+    const int nh = (int)gridDim.x, bx = (int)blockIdx.x;
+    const int h = (nh & 7) == 0 ? (bx & 7) * (nh >> 3) + (bx >> 3) : bx;
     const int kv = h / grp;
     const int eg0 = (int)blockIdx.y * EG;      // this workgroup's first value element
     const int lane = threadIdx.x & 63;
@@ -208,87 +322,39 @@ __global__ __launch_bounds__(64 * W) void kv_weighted_kernel(int grp, int64_t np
     const int8_t *vc = vcodes + (size_t)kv * npos * HD;
     float y = 0.0f;                            // folding lanes: element threadIdx.x's running sum
     const int64_t rounds = (nblk + RB - 1) / RB;
+    static_assert(LPB == 4, "the block's lanes are one quad");
+    const int q = lane % LPB;
     for (int64_t r = 0; r < rounds; r++) {
         const int kb = wid * BPW + sub;                    // block within the round
         const int64_t blk = r * RB + kb;
-        float piece[4] = {0.f, 0.f, 0.f, 0.f};
-        if (blk < nblk) {
-            const int64_t j0 = blk * kValueBlock;
-            const int nj = (int)(npos - j0 < kValueBlock ? npos - j0 : kValueBlock);
-            // the block's codes, each of its LPB lanes coding PPL = 32 / LPB consecutive positions:
-            // absmax and the flags reduced over the block's lanes, the packed codes (four
-            // positions a dword) handed to every lane of the block
-            constexpr int PPL = kValueBlock / LPB;
-            const int q = lane % LPB;
-            uint32_t amax = 0;
-            int bad = 0;
-            float w[PPL];
+        // a lane past the last block reads the last block again and its pieces go unread
+        const int64_t j0 = (blk < nblk ? blk : nblk - 1) * kValueBlock;
+        const int nj = (int)(npos - j0 < kValueBlock ? npos - j0 : kValueBlock);
+        // the quad's weights, then the block's rows, all in flight together; lane q of the
+        // quad codes positions 8q .. 8q+7
+        float p[8];
+        uint32_t sb[8];
+        load_weights(ph, vs, j0, nj, q, p, sb);
+        uint32_t rows[kValueBlock];
+        load_rows(vc, HD, j0, nj, el, rows);
+        uint32_t mine[2];
+        int E;
+        bool badb;
+        code_quad(p, sb, nj, q, mine, E, badb);
+        // code word d (positions 4d .. 4d+3) is word d % 2 of the quad's lane d / 2
+        uint32_t codes4[kValueBlock / 4];
 #pragma unroll
-            for (int i = 0; i < PPL; i++) {
-                const int j = q * PPL + i;
-                w[i] = 0.0f;
-                if (j < nj) {
-                    const uint32_t sb = vs[j0 + j];
-                    bad |= ((sb >> 10) & 31u) == 31u;
-                    w[i] = ph[j0 + j] * half_bits_value(sb);            // binary32 product
-                    const uint32_t a = __float_as_uint(ftz(w[i])) & 0x7FFFFFFFu;
-                    if (a <= 0x7F800000u && a > amax) amax = a;
-                }
-            }
-            static_assert(LPB == 4, "the block's lanes are one quad");
-            amax = max(amax, (uint32_t)dpp<kDppQuadSwap1>((int)amax));
-            amax = max(amax, (uint32_t)dpp<kDppQuadSwap2>((int)amax));
-            bad |= dpp<kDppQuadSwap1>(bad);
-            bad |= dpp<kDppQuadSwap2>(bad);
-            const bool badb = bad != 0 || amax == 0x7F800000u;
-            int E = 0, m1 = 1;
-            if (!badb && amax != 0) least_scale<1>(__uint_as_float(amax), m1, E);
-            uint32_t mine[PPL / 4];
-#pragma unroll
-            for (int k = 0; k < PPL / 4; k++) {
-                uint32_t word = 0;
-#pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    const float f = ftz(w[4 * k + t]);
-                    const int u = (badb || f != f) ? 0 : (int)__builtin_rint(__builtin_ldexp((double)f, -E));
-                    word |= ((uint32_t)u & 255u) << (8 * t);
-                }
-                mine[k] = word;
-            }
-            // dword d (positions 4d .. 4d+3) is held by the block's lane d / (PPL / 4)
-            uint32_t codes4[kValueBlock / 4];
-#pragma unroll
-            for (int d = 0; d < kValueBlock / 4; d++) {
-                constexpr int K = PPL / 4;
-                const int src = d / K;
-                const int ctrl = src | (src << 2) | (src << 4) | (src << 6);   // quad_perm [src x4]
-                const uint32_t v = mine[d % K];
-                codes4[d] = (uint32_t)(ctrl == 0x00 ? dpp<0x00>((int)v)
-                                     : ctrl == 0x55 ? dpp<0x55>((int)v)
-                                     : ctrl == 0xAA ? dpp<0xAA>((int)v) : dpp<0xFF>((int)v));
-            }
-            // value element sums: rows j..j+3 of the lane's four elements, transposed to per
-            // element dwords of four positions, against four codes at a time
-            int T[4] = {0, 0, 0, 0};
-#pragma unroll
-            for (int j = 0; j < kValueBlock; j += 4) {
-                uint32_t r4[4];
-#pragma unroll
-                for (int t = 0; t < 4; t++)
-                    r4[t] = j + t < nj ? *reinterpret_cast<const uint32_t *>(vc + (size_t)(j0 + j + t) * HD + el) : 0u;
-                const uint32_t uu = codes4[j / 4];
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const uint32_t col = ((r4[0] >> (8 * e)) & 255u) | (((r4[1] >> (8 * e)) & 255u) << 8) |
-                                         (((r4[2] >> (8 * e)) & 255u) << 16) | (((r4[3] >> (8 * e)) & 255u) << 24);
-                    T[e] = __builtin_amdgcn_sdot4((int)col, (int)uu, T[e], false);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-                piece[e] = badb ? __uint_as_float(0x7FC00000u)
-                               : r32_exact_double(__builtin_ldexp((double)T[e], E));
+        for (int d = 0; d < kValueBlock / 4; d++) {
+            const uint32_t v = mine[d % 2];
+            const int src = d / 2;
+            codes4[d] = (uint32_t)(src == 0 ? dpp<0x00>((int)v)
+                                 : src == 1 ? dpp<0x55>((int)v)
+                                 : src == 2 ? dpp<0xAA>((int)v) : dpp<0xFF>((int)v));   // quad_perm [src x4]
         }
+        uint32_t col[4][kValueBlock / 4];
+        transpose_rows(rows, col);
+        float piece[4];
+        block_pieces(col, codes4, E, badb, piece);
 #pragma unroll
         for (int e = 0; e < 4; e++) s_piece[kb * EG + (el - eg0) + e] = piece[e];
         __syncthreads();
@@ -299,6 +365,107 @@ __global__ __launch_bounds__(64 * W) void kv_weighted_kernel(int grp, int64_t np
         __syncthreads();
     }
     if (threadIdx.x < EG) out[(size_t)h * HD + eg0 + threadIdx.x] = canon_nan(y);
+}
+
+// ---------------------------------------------------------------------------------------
+// weighted sum in two passes over a caller's workspace of pieces, f32 [nh][nblk][HD]:
+//
+//   pieces  grid = (ceil(nblk / 4), nkv), four waves; wave w takes block 4x + w of KV head y for
+//           every query head that shares it, so each cached value row is read once.  The
+//           weights and scales of the first 16 heads are loaded first, then the block's rows
+//           (every load unconditional, from clamped positions, all in flight together)
+//           (lane: four consecutive elements, EL = HD / 4 lanes a row, HS = 64 / EL head
+//           slots); lane quad k codes head k while the rows arrive and parks its eight code
+//           words, E and the bad flag in the wave's LDS record k; the rows are transposed to
+//           per-element words of four positions, and head slot s forms heads s, s + HS, ...
+//           from the records: per element 8 v_dot4 (the four elements' chains interleaved) and
+//           one rounding, four pieces a lane, stored as one 16-byte write.  No barrier: a wave's LDS operations run in order.
+//   fold    kv_fold.hip: one lane per (head, element) adds the pieces in block order.
+
+constexpr int kRec = 12;   // LDS words per head record: eight code words, E, the bad flag, padding
+
+template <int HD>
+__global__ __launch_bounds__(256) void kv_weighted_pieces_kernel(int grp, int64_t npos, int64_t nblk,
+                                                                 const float *__restrict__ probs,
+                                                                 const uint16_t *__restrict__ vscales,
+                                                                 const int8_t *__restrict__ vcodes,
+                                                                 float *__restrict__ pieces)
+{
+    constexpr int EL = HD / 4;                 // lanes per value row
+    constexpr int HS = 64 / EL;                // head slots per wave
+    __shared__ __align__(16) uint32_t s_rec[4][16 * kRec];
+    const int kv = (int)blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
+    const int64_t blk = (int64_t)blockIdx.x * 4 + wid;
+    if (blk >= nblk) return;                   // nothing waits for this wave
+    const int64_t j0 = blk * kValueBlock;
+    const int nj = (int)(npos - j0 < kValueBlock ? npos - j0 : kValueBlock);
+    const uint16_t *vs = vscales + (size_t)kv * npos;
+    const int8_t *vc = vcodes + (size_t)kv * npos * HD;
+    const float *pk = probs + (size_t)kv * grp * npos;   // the first query head of this KV head
+    uint32_t *rec = s_rec[wid];
+    const int q = lane % EL, slot = lane / EL;
+    const int k = lane >> 2, qq = lane & 3;
+    // lane quad k codes query head k of the batch; the record k gets its codes, E and flag
+    auto park = [&](const float (&pw)[8], const uint32_t (&sw)[8], bool keep) {
+        uint32_t word[2];
+        int E;
+        bool badb;
+        code_quad(pw, sw, nj, qq, word, E, badb);
+        if (keep) {
+            uint32_t *r = rec + k * kRec;
+            r[2 * qq] = word[0];                // code words 2qq, 2qq+1: positions 8qq .. 8qq+7
+            r[2 * qq + 1] = word[1];
+            if (qq == 0) {
+                r[8] = (uint32_t)E;
+                r[9] = badb ? 1u : 0u;
+            }
+        }
+    };
+
+    // the first batch's weights, then the block's rows, all in flight together
+    int nheads = grp < 16 ? grp : 16;
+    float p[8];
+    uint32_t sb[8];
+    load_weights(pk + (size_t)min(k, nheads - 1) * npos, vs, j0, nj, qq, p, sb);
+    uint32_t rows[kValueBlock];
+    load_rows(vc, HD, j0, nj, 4 * q, rows);
+    park(p, sb, k < nheads);
+    uint32_t col[4][kValueBlock / 4];
+    transpose_rows(rows, col);
+
+    // head slot `slot` forms heads slot, slot + HS, ... of the batch at hbase
+    auto form = [&](int hbase, int nh_batch) {
+        for (int k2 = slot; k2 < nh_batch; k2 += HS) {
+            const uint32_t *r = rec + k2 * kRec;
+            const uint4 c0 = *reinterpret_cast<const uint4 *>(r);
+            const uint4 c1 = *reinterpret_cast<const uint4 *>(r + 4);
+            const uint4 eb = *reinterpret_cast<const uint4 *>(r + 8);
+            const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            float pc[4];
+            block_pieces(col, cw, (int)eb.x, eb.y != 0, pc);
+            float *dst = pieces + ((size_t)(kv * grp + hbase + k2) * nblk + blk) * HD + 4 * q;
+            *reinterpret_cast<float4 *>(dst) = make_float4(pc[0], pc[1], pc[2], pc[3]);
+        }
+    };
+    form(0, nheads);
+    // more than 16 query heads per KV head: the next batches, the record reused (the reads
+    // above come first in the wave's LDS order)
+    for (int hbase = 16; hbase < grp; hbase += 16) {
+        nheads = grp - hbase < 16 ? grp - hbase : 16;
+        load_weights(pk + (size_t)(hbase + min(k, nheads - 1)) * npos, vs, j0, nj, qq, p, sb);
+        park(p, sb, k < nheads);
+        form(hbase, nheads);
+    }
+}
+
+template <int HD>
+void weighted_pieces_typed(int nkv, int grp, int64_t npos, int64_t nblk, const float *p, const uint16_t *vs,
+                           const int8_t *vc, float *ws, hipStream_t s)
+{
+    hipLaunchKernelGGL((kv_weighted_pieces_kernel<HD>), dim3((unsigned)((nblk + 3) / 4), (unsigned)nkv), dim3(256), 0,
+                       s, grp, npos, nblk, p, vs, vc, ws);
 }
 
 }  // namespace
@@ -401,6 +568,35 @@ int launch_kv_weighted(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const 
     else weighted_typed<256>((int)nh, grp, npos, probs, vscales, vcodes, out, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_E_RUNTIME, "kv weighted launch: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+size_t kv_weighted_workspace_bytes(int64_t nh, int64_t npos, int64_t hd)
+{
+    return (size_t)nh * (size_t)((npos + kValueBlock - 1) / kValueBlock) * (size_t)hd * sizeof(float);
+}
+
+int launch_kv_weighted_two_pass(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs,
+                                const uint16_t *vscales, const int8_t *vcodes, float *ws, float *out, hipStream_t s)
+{
+    if (nh == 0) return QG_OK;
+    const int grp = (int)(nh / nkv), g = (int)nkv;
+    const int64_t nblk = (npos + kValueBlock - 1) / kValueBlock;
+    hipEvent_t ev0, ev1;
+    take_timing_events(&ev0, &ev1);   // the span of both passes
+    if (ev0 && ev1 && hipEventRecord(ev0, s) != hipSuccess)
+        return fail(QG_E_RUNTIME, "kv weighted: recording the start event failed");
+    if (nblk > 0) {
+        if (hd == 32) weighted_pieces_typed<32>(g, grp, npos, nblk, probs, vscales, vcodes, ws, s);
+        else if (hd == 64) weighted_pieces_typed<64>(g, grp, npos, nblk, probs, vscales, vcodes, ws, s);
+        else if (hd == 128) weighted_pieces_typed<128>(g, grp, npos, nblk, probs, vscales, vcodes, ws, s);
+        else weighted_pieces_typed<256>(g, grp, npos, nblk, probs, vscales, vcodes, ws, s);
+    }
+    launch_kv_fold_pieces(nh * hd, (int)hd, nblk, ws, out, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_E_RUNTIME, "kv weighted (two passes) launch: %s", hipGetErrorString(e));
+    if (ev0 && ev1 && hipEventRecord(ev1, s) != hipSuccess)
+        return fail(QG_E_RUNTIME, "kv weighted: recording the stop event failed");
     return QG_OK;
 }
 

@@ -80,6 +80,10 @@ int launch_kv_scores(int mode, int64_t nh, int64_t nkv, int64_t npos, int64_t hd
                      hipStream_t s);
 int launch_kv_weighted(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs, const uint16_t *vscales,
                        const int8_t *vcodes, float *out, hipStream_t s);
+size_t kv_weighted_workspace_bytes(int64_t nh, int64_t npos, int64_t hd);
+void launch_kv_fold_pieces(int64_t total, int hd, int64_t nblk, const float *pieces, float *out, hipStream_t s);
+int launch_kv_weighted_two_pass(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs,
+                                const uint16_t *vscales, const int8_t *vcodes, float *ws, float *out, hipStream_t s);
 
 int launch_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
                       int32_t *csum_out, int32_t *osum_out, hipStream_t s);

@@ -291,6 +291,25 @@ int qg_kv_scores(int mode, int64_t nh, int64_t nkv, int64_t npos, int64_t hd, co
 int qg_kv_weighted(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs, const uint16_t *vscales,
                    const int8_t *vcodes, float *out, void *stream);
 
+/* Bytes of workspace qg_kv_weighted_with_workspace needs for nh heads over npos positions of
+ * head size hd: one f32 piece per (head, block of QG_VALUE_BLOCK positions, value element),
+ * nh * ceil(npos / QG_VALUE_BLOCK) * hd * 4.  Written to *bytes; QG_E_SHAPE for a head size or
+ * count qg_kv_weighted refuses, QG_E_INVALID for a null bytes. */
+int qg_kv_weighted_workspace(int64_t nh, int64_t npos, int64_t hd, size_t *bytes);
+
+/* qg_kv_weighted in two passes, bit for bit the same result (weighted_int8): the first pass
+ * reads each KV head's value rows once for every query head that shares them and writes each
+ * block's pieces to the workspace, f32 [nh][ceil(npos / QG_VALUE_BLOCK)][hd]; the second adds
+ * every head's pieces in block order.  The arguments are qg_kv_weighted's, plus
+ *   workspace  device memory of ws_bytes >= qg_kv_weighted_workspace's figure (16-byte
+ *              aligned), the caller's, overwritten; NULL allowed when that figure is 0.
+ * QG_E_INVALID when ws_bytes is short or a pointer is null or misaligned.  Calls on one stream
+ * may share a workspace; calls on concurrent streams need one each.  Honours
+ * qg_time_next_launch (the events span both passes). */
+int qg_kv_weighted_with_workspace(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs,
+                                  const uint16_t *vscales, const int8_t *vcodes, float *out, void *workspace,
+                                  size_t ws_bytes, void *stream);
+
 /* Integer sums per (row, sub-block), before any scale ("Module lane", Functions
  * block_sums), for one activation row:
  *   Q4K: csum_out int32 [rows][cols/32] = sum sc_j*q*c over sub-block j,

@@ -270,16 +270,27 @@ def test_scores_one_position_and_heads_per_kv(qg):
 
 # --- weighted sum -------------------------------------------------------------------------
 
-def run_weighted(qg, probs, vs, vc, fill=7.0):
+def run_weighted(qg, probs, vs, vc, fill=7.0, passes=1):
+    """qg_kv_weighted (passes=1) or qg_kv_weighted_with_workspace (passes=2, over a workspace
+    filled with NaN beforehand, a few words longer than needed, so that a piece left unwritten
+    shows)."""
     nh, npos = probs.shape
     nkv, _, hd = vc.shape
     out = torch.full((nh, hd), fill, dtype=torch.float32, device=DEV)
-    if npos:
-        qg.qg_kv_weighted(nh, nkv, npos, hd, dev(probs), u16_dev(vs), dev(vc), out)
+    args = (dev(probs), u16_dev(vs), dev(vc)) if npos else (None, None, None)
+    if passes == 1:
+        qg.qg_kv_weighted(nh, nkv, npos, hd, *args, out)
     else:
-        qg.qg_kv_weighted(nh, nkv, 0, hd, None, None, None, out)
+        need = qg.qg_kv_weighted_workspace(nh, npos, hd)
+        ws = torch.full((need // 4 + 5,), float("nan"), dtype=torch.float32, device=DEV)
+        qg.qg_kv_weighted_with_workspace(nh, nkv, npos, hd, *args, out, ws)
     torch.cuda.synchronize()
     return host(out)
+
+
+@pytest.fixture(params=[1, 2], ids=["one_pass", "two_pass"])
+def passes(request):
+    return request.param
 
 
 def cached_values(nkv, npos, hd, seed):
@@ -290,17 +301,17 @@ def cached_values(nkv, npos, hd, seed):
 
 @pytest.mark.parametrize("hd", HDS)
 @pytest.mark.parametrize("npos", [1, 31, 32, 33, 300, 1000])
-def test_weighted(qg, hd, npos):
+def test_weighted(qg, hd, npos, passes):
     nh, nkv = 8, 2
     vs, vc = cached_values(nkv, npos, hd, 500 + hd + npos)
     probs = gen.attn_weights(nh, npos, 600 + npos)
-    say(f"weighted hd={hd} npos={npos}")
+    say(f"weighted hd={hd} npos={npos} passes={passes}")
     want = oracle.kv_weighted(probs, vs, vc)
-    same_bits(run_weighted(qg, probs, vs, vc), want, f"weighted hd={hd} npos={npos}")
+    same_bits(run_weighted(qg, probs, vs, vc, passes=passes), want, f"weighted hd={hd} npos={npos}")
 
 
 @pytest.mark.parametrize("hd", [32, 128, 256])
-def test_weighted_special_blocks(qg, hd):
+def test_weighted_special_blocks(qg, hd, passes):
     """One head per KV head, each with one special block: zero weights, weights whose products
     are subnormal (read as zero), a NaN weight, an infinite product, tiny equal products (the
     scale near the bottom), the largest value scale, and value scales that are not finite
@@ -320,14 +331,46 @@ def test_weighted_special_blocks(qg, hd):
     vs[5, 160:192] = 0x7BFF                             # the largest finite value scale
     vs[6, 200] = 0x7C00                                 # an infinite value scale
     vs[7, 260] = 0x7E01                                 # a NaN value scale
-    say(f"weighted special blocks hd={hd}")
+    say(f"weighted special blocks hd={hd} passes={passes}")
     want = oracle.kv_weighted(probs, vs, vc)
-    same_bits(run_weighted(qg, probs, vs, vc), want, f"weighted special hd={hd}")
+    same_bits(run_weighted(qg, probs, vs, vc, passes=passes), want, f"weighted special hd={hd}")
     assert np.isnan(want[3]).all() and np.isnan(want[6]).all() and np.isnan(want[7]).all()
     assert np.isfinite(want[[0, 1, 2, 4, 5]]).all()
 
 
-def test_weighted_order_of_blocks(qg):
+@pytest.mark.parametrize("nh,nkv,npos,hd", [(40, 2, 100, 64), (36, 1, 65, 256), (64, 2, 97, 32),
+                                            (5, 5, 129, 128), (16, 1, 32, 128)])
+def test_weighted_grouped_heads(qg, nh, nkv, npos, hd, passes):
+    """Query heads per KV head from 1 to 32: the two-pass form codes them 16 at a time from
+    one read of the block's value rows."""
+    vs, vc = cached_values(nkv, npos, hd, 900 + nh + npos)
+    probs = gen.attn_weights(nh, npos, 950 + nh)
+    probs[nh - 1, npos - 1] = np.nan
+    say(f"weighted grouped nh={nh} nkv={nkv} npos={npos} hd={hd} passes={passes}")
+    want = oracle.kv_weighted(probs, vs, vc)
+    same_bits(run_weighted(qg, probs, vs, vc, passes=passes), want, f"grouped nh={nh} nkv={nkv}")
+
+
+def test_weighted_workspace_reused_across_shapes(qg):
+    """One workspace, sized for the largest call, serves calls of other shapes in turn; each
+    result matches the oracle and the one-pass entry point."""
+    shapes = [(32, 8, 1000, 128), (8, 2, 33, 64), (32, 8, 1000, 128), (4, 4, 1, 256), (8, 1, 0, 32)]
+    need = max(qg.qg_kv_weighted_workspace(nh, npos, hd) for nh, _, npos, hd in shapes)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    for k, (nh, nkv, npos, hd) in enumerate(shapes):
+        vs, vc = cached_values(nkv, npos, hd, 1000 + k)
+        probs = gen.attn_weights(nh, npos, 1100 + k)
+        out = torch.full((nh, hd), 7.0, dtype=torch.float32, device=DEV)
+        args = (dev(probs), u16_dev(vs), dev(vc)) if npos else (None, None, None)
+        say(f"weighted workspace reuse {k}: nh={nh} nkv={nkv} npos={npos} hd={hd}")
+        qg.qg_kv_weighted_with_workspace(nh, nkv, npos, hd, *args, out, ws)
+        torch.cuda.synchronize()
+        want = oracle.kv_weighted(probs, vs, vc)
+        same_bits(host(out), want, f"reuse {k}")
+        same_bits(host(out), run_weighted(qg, probs, vs, vc), f"reuse {k} against one pass")
+
+
+def test_weighted_order_of_blocks(qg, passes):
     """Three blocks whose pieces are 1, 2^-24, 2^-24: added in order they give 1; the order of
     the blocks decides the result."""
     hd, npos = 32, 96
@@ -342,15 +385,33 @@ def test_weighted_order_of_blocks(qg):
     vc[0, 64, :] = 1
     want = oracle.kv_weighted(probs, vs, vc)
     assert (want == 1.0).all()
-    same_bits(run_weighted(qg, probs, vs, vc), want, "order")
+    same_bits(run_weighted(qg, probs, vs, vc, passes=passes), want, "order")
 
 
-def test_weighted_empty_context(qg):
+def test_weighted_flushed_running_sum_keeps_its_sign(qg, passes):
+    """A running sum of -2^-127 flushes to -0; a zero block after it gives +0 (hand-worked
+    two-head case: pieces 2^-125, -5 * 2^-127, then 0 for head 0; the zero block first for
+    head 1)."""
+    hd, npos = 32, 96
+    p = np.zeros((2, npos), np.float32)
+    vs = np.full((2, npos), 0x3C00, np.uint16)
+    vc = np.zeros((2, npos, hd), np.int8)
+    for h, b0 in ((0, 0), (1, 32)):
+        p[h, b0] = np.float32(2.0 ** -125)
+        vc[h, b0, :] = 1
+        p[h, b0 + 32] = np.float32(5 * 2.0 ** -127)
+        vc[h, b0 + 32, :] = -1
+    want = oracle.kv_weighted(p, vs, vc)
+    assert (want[0].view(np.uint32) == 0).all() and (want[1].view(np.uint32) == 0x80000000).all()
+    same_bits(run_weighted(qg, p, vs, vc, passes=passes), want, "flushed sign")
+
+
+def test_weighted_empty_context(qg, passes):
     vc = np.zeros((2, 0, 64), np.int8)
     vs = np.zeros((2, 0), np.uint16)
     probs = np.zeros((4, 0), np.float32)
     want = oracle.kv_weighted(probs, vs, vc)
-    got = run_weighted(qg, probs, vs, vc, fill=7.0)
+    got = run_weighted(qg, probs, vs, vc, fill=7.0, passes=passes)
     assert (want == 0).all()
     same_bits(got, want, "empty")
 
@@ -400,15 +461,19 @@ def test_decode_full_size_chain(qg, decode, mode):
     p = (p / p.sum(axis=1, keepdims=True)).astype(np.float32)
     out = torch.zeros((nh, hd), dtype=torch.float32, device=DEV)
     qg.qg_kv_weighted(nh, nkv, npos, hd, dev(p), vs_d, vc_d, out)
+    out2 = torch.zeros((nh, hd), dtype=torch.float32, device=DEV)
+    ws = torch.empty(qg.qg_kv_weighted_workspace(nh, npos, hd), dtype=torch.uint8, device=DEV)
+    qg.qg_kv_weighted_with_workspace(nh, nkv, npos, hd, dev(p), vs_d, vc_d, out2, ws)
     torch.cuda.synchronize()
     want = oracle.kv_weighted(p, vs.reshape(nkv, npos), vc.reshape(nkv, npos, hd))
     same_bits(host(out), want, f"decode weighted mode={mode}")
+    same_bits(host(out2), want, f"decode weighted, two passes, mode={mode}")
 
 
-def test_decode_full_size_weighted(qg, decode):
+def test_decode_full_size_weighted(qg, decode, passes):
     keys, vals, query, weights = decode
     nkv, npos, hd = vals.shape
     vs, vc = oracle.kv_cache_rows(vals.reshape(-1, hd))
     vs, vc = vs.reshape(nkv, npos), vc.reshape(nkv, npos, hd)
     want = oracle.kv_weighted(weights, vs, vc)
-    same_bits(run_weighted(qg, weights, vs, vc), want, "decode weighted")
+    same_bits(run_weighted(qg, weights, vs, vc, passes=passes), want, "decode weighted")

@@ -204,6 +204,32 @@ def test_weighted_adds_blocks_in_order():
     assert float(got[0, 0]) == 1.0
 
 
+def _flushed_sign_case():
+    """Two heads, each over its own KV head of 96 positions (scales 1.0), hand-worked: head 0's
+    blocks give the pieces 2^-125, -5 * 2^-127 and 0 (block 0: w = 2^-125, E = -131 as
+    127 * 2^-132 < 2^-125 <= 127 * 2^-131, code 64, value 1; block 1: w = 5 * 2^-127, E = -131,
+    code 80, value -1); head 1 has the zero block first.  The running sum 2^-125 - 5 * 2^-127 =
+    -2^-127 is subnormal and flushes to -0: head 1 ends there (-0), while head 0 adds the zero
+    block's +0 after it (-0 + +0 = +0 under round to nearest)."""
+    npos, hd = 96, 32
+    p = np.zeros((2, npos), np.float32)
+    vs = np.full((2, npos), 0x3C00, np.uint16)
+    vc = np.zeros((2, npos, hd), np.int8)
+    for h, b0 in ((0, 0), (1, 32)):
+        p[h, b0] = np.float32(2.0 ** -125)
+        vc[h, b0, :] = 1
+        p[h, b0 + 32] = np.float32(5 * 2.0 ** -127)
+        vc[h, b0 + 32, :] = -1
+    return p, vs, vc
+
+
+def test_weighted_flushes_a_subnormal_running_sum_to_a_signed_zero():
+    p, vs, vc = _flushed_sign_case()
+    got = oracle.kv_weighted(p, vs, vc).view(np.uint32)
+    assert (got[0] == 0x00000000).all()
+    assert (got[1] == 0x80000000).all()
+
+
 def _kv_quick_pins(mutant: int) -> bool:
     try:
         for x in (np.float32(1 + 2.0 ** -11), np.float32(2.0 ** -25), np.float32(1 + 3 * 2.0 ** -11)):

@@ -228,6 +228,32 @@ def test_kv_validation_refuses_before_any_gpu_work():
     assert L.qg_kv_weighted(0, 2, 10, 64, None, None, None, None, None) == qg.OK
 
 
+def test_kv_weighted_workspace_size_and_refusals():
+    """qg_kv_weighted_workspace: one f32 piece per (head, 32-position block, element), the last
+    block possibly short; qg_kv_weighted_with_workspace refuses a short, null or misaligned
+    workspace and everything qg_kv_weighted refuses, before any GPU work (no GPU here)."""
+    L = qg.lib()
+    for nh, npos, hd in [(32, 4096, 128), (8, 1, 64), (4, 33, 32), (6, 0, 256), (0, 100, 128), (1, 31, 256)]:
+        assert qg.qg_kv_weighted_workspace(nh, npos, hd) == nh * (-(-npos // 32)) * hd * 4
+    with pytest.raises(qg.QGError) as ei:
+        qg.qg_kv_weighted_workspace(4, 10, 48)
+    assert ei.value.status == qg.E_SHAPE
+    with pytest.raises(qg.QGError):
+        qg.qg_kv_weighted_workspace(4, -1, 64)
+    assert L.qg_kv_weighted_workspace(4, 10, 64, None) == qg.E_INVALID
+    fake = ctypes.c_void_p(0x1000)
+    need = 8 * 1 * 64 * 4
+    args = (fake, fake, fake, fake)
+    assert L.qg_kv_weighted_with_workspace(8, 2, 10, 64, *args, fake, need - 1, None) == qg.E_INVALID
+    assert "workspace" in qg.qg_last_error()
+    assert L.qg_kv_weighted_with_workspace(8, 2, 10, 64, *args, None, need, None) == qg.E_INVALID
+    assert L.qg_kv_weighted_with_workspace(8, 2, 10, 64, *args, ctypes.c_void_p(0x1008), need, None) == qg.E_INVALID
+    assert L.qg_kv_weighted_with_workspace(8, 3, 10, 64, *args, fake, need, None) == qg.E_SHAPE
+    assert L.qg_kv_weighted_with_workspace(8, 2, 10, 96, *args, fake, need, None) == qg.E_SHAPE
+    assert L.qg_kv_weighted_with_workspace(8, 2, 10, 64, fake, fake, fake, None, fake, need, None) == qg.E_INVALID
+    assert L.qg_kv_weighted_with_workspace(0, 2, 10, 64, None, None, None, None, None, 0, None) == qg.OK
+
+
 def test_kv_binding_refuses_short_buffers():
     """The binding checks buffer sizes the C ABI cannot see."""
     import torch
