@@ -15,58 +15,42 @@
 namespace qg {
 namespace {
 
-constexpr int kFoldLanes = 64;    // (head, element) sums a workgroup
-constexpr int kFoldRound = 128;   // blocks a round
-constexpr int kFoldPer = kFoldRound * kFoldLanes / 256;   // pieces a thread loads per round
+constexpr int kFoldChunk = 128;   // pieces a lane has in flight
 
-// grid = ceil(total / 64) workgroups of 256 threads; workgroup x folds the sums t = 64x + i
-// (i < 64; head t / hd, element t % hd) over the workspace f32 [nh][nblk][hd].  Per round of up
-// to 128 blocks every thread loads 32 pieces (a wave's load: one block's 64 sums), all in
-// flight together, into LDS [block][i]; after the barrier wave 0 adds them in block order.
-__global__ __launch_bounds__(256) void kv_weighted_fold_kernel(int64_t total, int hd, int64_t nblk,
-                                                               const float *__restrict__ pieces,
-                                                               float *__restrict__ out)
+// grid = ceil(total / 64) one-wave workgroups; lane t = h * HD + e folds the pieces of head h,
+// element e from the workspace f32 [nh][nblk][HD] in chunks of 128 blocks: every load of a
+// chunk issued first (a short last chunk reads block min(b, last) again, so that none waits on
+// a branch), then the adds, each waiting only for its own piece (loads return in order).
+template <int HD>
+__global__ __launch_bounds__(64) void kv_weighted_fold_kernel(int64_t total, int nblk, const float *__restrict__ pieces,
+                                                              float *__restrict__ out)
 {
-    __shared__ float s_p[kFoldRound * kFoldLanes];
-    const int tid = threadIdx.x;
-    const int i = tid & (kFoldLanes - 1);
-    const int64_t t = (int64_t)blockIdx.x * kFoldLanes + i;
-    const bool live = t < total;
-    const int64_t h = live ? t / hd : 0;
-    const float *p = pieces + ((size_t)h * nblk * hd + (size_t)(live ? t - h * hd : 0));
+    const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (t >= total) return;
+    const int64_t h = t / HD;
+    const float *p = pieces + ((size_t)h * (size_t)nblk * HD + (size_t)(t - h * HD));
     float y = 0.0f;
-    for (int64_t r0 = 0; r0 < nblk; r0 += kFoldRound) {
-        const int nb = (int)(nblk - r0 < kFoldRound ? nblk - r0 : kFoldRound);
-        float v[kFoldPer];
+    // block counts in 32 bits (below 2^26): uniform compares and selects stay scalar
+    for (int c0 = 0; c0 < nblk; c0 += kFoldChunk) {
+        const int nb = min(nblk - c0, kFoldChunk);
+        const float *pc = p + (size_t)c0 * HD;
+        float a[kFoldChunk];
+        if (nb == kFoldChunk) {
 #pragma unroll
-        for (int j = 0; j < kFoldPer; j++) {
-            const int b = (tid >> 6) + 4 * j;                  // block within the round
-            v[j] = (live && b < nb) ? p[(size_t)(r0 + b) * hd] : 0.0f;
-        }
+            for (int k = 0; k < kFoldChunk; k++) a[k] = pc[k * HD];
 #pragma unroll
-        for (int j = 0; j < kFoldPer; j++) s_p[((tid >> 6) + 4 * j) * kFoldLanes + i] = v[j];
-        __syncthreads();
-        if (tid < kFoldLanes && nb == kFoldRound) {
-            // a whole round: every LDS read issued ahead of the adds it feeds
-            float a[kFoldRound];
+            for (int k = 0; k < kFoldChunk; k++) y = y + a[k];
+        } else {
 #pragma unroll
-            for (int k = 0; k < kFoldRound; k++) a[k] = s_p[k * kFoldLanes + i];
+            for (int k = 0; k < kFoldChunk; k++) a[k] = pc[(size_t)min(k, nb - 1) * HD];
 #pragma unroll
-            for (int k = 0; k < kFoldRound; k++) y = y + a[k];
-        } else if (tid < kFoldLanes) {
-            int b = 0;
-            for (; b + 8 <= nb; b += 8) {
-                float a[8];
-#pragma unroll
-                for (int k = 0; k < 8; k++) a[k] = s_p[(b + k) * kFoldLanes + i];
-#pragma unroll
-                for (int k = 0; k < 8; k++) y = y + a[k];
+            for (int k = 0; k < kFoldChunk; k++) {
+                const float z = y + a[k];
+                y = k < nb ? z : y;
             }
-            for (; b < nb; b++) y = y + s_p[b * kFoldLanes + i];
         }
-        __syncthreads();
     }
-    if (tid < kFoldLanes && live) out[t] = (y != y) ? __uint_as_float(0x7FC00000u) : y;
+    out[t] = (y != y) ? __uint_as_float(0x7FC00000u) : y;
 }
 
 }  // namespace
@@ -74,8 +58,11 @@ __global__ __launch_bounds__(256) void kv_weighted_fold_kernel(int64_t total, in
 void launch_kv_fold_pieces(int64_t total, int hd, int64_t nblk, const float *pieces, float *out, hipStream_t s)
 {
     if (total == 0) return;
-    hipLaunchKernelGGL(kv_weighted_fold_kernel, dim3((unsigned)((total + kFoldLanes - 1) / kFoldLanes)), dim3(256), 0, s,
-                       total, hd, nblk, pieces, out);
+    const dim3 grid((unsigned)((total + 63) / 64)), block(64);
+    if (hd == 32) hipLaunchKernelGGL((kv_weighted_fold_kernel<32>), grid, block, 0, s, total, (int)nblk, pieces, out);
+    else if (hd == 64) hipLaunchKernelGGL((kv_weighted_fold_kernel<64>), grid, block, 0, s, total, (int)nblk, pieces, out);
+    else if (hd == 128) hipLaunchKernelGGL((kv_weighted_fold_kernel<128>), grid, block, 0, s, total, (int)nblk, pieces, out);
+    else hipLaunchKernelGGL((kv_weighted_fold_kernel<256>), grid, block, 0, s, total, (int)nblk, pieces, out);
 }
 
 }  // namespace qg
