@@ -384,6 +384,61 @@ __global__ __launch_bounds__(64 * W) void kv_weighted_kernel(int grp, int64_t np
 
 constexpr int kRec = 12;   // LDS words per head record: eight code words, E, the bad flag, padding
 
+// Lane quad k's coding of its query head over the block, parked in the head's record r
+// (eight code words, E, the bad flag) when `keep`.
+__device__ __forceinline__ void park_record(const float (&p)[8], const uint32_t (&sb)[8], int nj, int qq, bool keep,
+                                            uint32_t *r)
+{
+    uint32_t word[2];
+    int E;
+    bool badb;
+    code_quad(p, sb, nj, qq, word, E, badb);
+    if (keep) {
+        r[2 * qq] = word[0];                    // code words 2qq, 2qq+1: positions 8qq .. 8qq+7
+        r[2 * qq + 1] = word[1];
+        if (qq == 0) {
+            r[8] = (uint32_t)E;
+            r[9] = badb ? 1u : 0u;
+        }
+    }
+}
+
+// Head slot `slot` forms N of its heads slot + (it0 + it) * HS of a batch of nh_batch heads:
+// every record read issued before the dots; a head past the batch reads the batch's last
+// record and stores nothing.  Head k2's pieces go to dst + k2 * head_stride.
+template <int HS, int N>
+__device__ __forceinline__ void form_heads(const uint32_t *rec, const uint32_t (&col)[4][kValueBlock / 4], int slot,
+                                           int nh_batch, int it0, float *dst, size_t head_stride)
+{
+    uint4 c0[N], c1[N], eb[N];
+#pragma unroll
+    for (int it = 0; it < N; it++) {
+        const uint32_t *r = rec + min(slot + (it0 + it) * HS, nh_batch - 1) * kRec;
+        c0[it] = *reinterpret_cast<const uint4 *>(r);
+        c1[it] = *reinterpret_cast<const uint4 *>(r + 4);
+        eb[it] = *reinterpret_cast<const uint4 *>(r + 8);
+    }
+#pragma unroll
+    for (int it = 0; it < N; it++) {
+        const int k2 = slot + (it0 + it) * HS;
+        const uint32_t cw[8] = {c0[it].x, c0[it].y, c0[it].z, c0[it].w, c1[it].x, c1[it].y, c1[it].z, c1[it].w};
+        float pc[4];
+        block_pieces(col, cw, (int)eb[it].x, eb[it].y != 0, pc);
+        if (k2 < nh_batch) *reinterpret_cast<float4 *>(dst + k2 * head_stride) = make_float4(pc[0], pc[1], pc[2], pc[3]);
+    }
+}
+
+template <int HS>
+__device__ __forceinline__ void form_batch(const uint32_t *rec, const uint32_t (&col)[4][kValueBlock / 4], int slot,
+                                           int nh_batch, float *dst, size_t head_stride)
+{
+    const int iters = (nh_batch + HS - 1) / HS;
+    if (iters == 1) form_heads<HS, 1>(rec, col, slot, nh_batch, 0, dst, head_stride);
+    else if (iters == 2) form_heads<HS, 2>(rec, col, slot, nh_batch, 0, dst, head_stride);
+    else
+        for (int it0 = 0; it0 < iters; it0 += 4) form_heads<HS, 4>(rec, col, slot, nh_batch, it0, dst, head_stride);
+}
+
 template <int HD>
 __global__ __launch_bounds__(256) void kv_weighted_pieces_kernel(int grp, int64_t npos, int64_t nblk,
                                                                  const float *__restrict__ probs,
@@ -407,56 +462,28 @@ __global__ __launch_bounds__(256) void kv_weighted_pieces_kernel(int grp, int64_
     uint32_t *rec = s_rec[wid];
     const int q = lane % EL, slot = lane / EL;
     const int k = lane >> 2, qq = lane & 3;
-    // lane quad k codes query head k of the batch; the record k gets its codes, E and flag
-    auto park = [&](const float (&pw)[8], const uint32_t (&sw)[8], bool keep) {
-        uint32_t word[2];
-        int E;
-        bool badb;
-        code_quad(pw, sw, nj, qq, word, E, badb);
-        if (keep) {
-            uint32_t *r = rec + k * kRec;
-            r[2 * qq] = word[0];                // code words 2qq, 2qq+1: positions 8qq .. 8qq+7
-            r[2 * qq + 1] = word[1];
-            if (qq == 0) {
-                r[8] = (uint32_t)E;
-                r[9] = badb ? 1u : 0u;
-            }
-        }
-    };
+    const size_t head_stride = (size_t)nblk * HD;
+    float *dst = pieces + ((size_t)kv * grp * nblk + blk) * HD + 4 * q;   // head 0 of the batch
 
-    // the first batch's weights, then the block's rows, all in flight together
+    // the first batch's weights, then the block's rows, all in flight together; lane quad k
+    // codes query head k of the batch into record k
     int nheads = grp < 16 ? grp : 16;
     float p[8];
     uint32_t sb[8];
     load_weights(pk + (size_t)min(k, nheads - 1) * npos, vs, j0, nj, qq, p, sb);
     uint32_t rows[kValueBlock];
     load_rows(vc, HD, j0, nj, 4 * q, rows);
-    park(p, sb, k < nheads);
+    park_record(p, sb, nj, qq, k < nheads, rec + min(k, 15) * kRec);
     uint32_t col[4][kValueBlock / 4];
     transpose_rows(rows, col);
-
-    // head slot `slot` forms heads slot, slot + HS, ... of the batch at hbase
-    auto form = [&](int hbase, int nh_batch) {
-        for (int k2 = slot; k2 < nh_batch; k2 += HS) {
-            const uint32_t *r = rec + k2 * kRec;
-            const uint4 c0 = *reinterpret_cast<const uint4 *>(r);
-            const uint4 c1 = *reinterpret_cast<const uint4 *>(r + 4);
-            const uint4 eb = *reinterpret_cast<const uint4 *>(r + 8);
-            const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-            float pc[4];
-            block_pieces(col, cw, (int)eb.x, eb.y != 0, pc);
-            float *dst = pieces + ((size_t)(kv * grp + hbase + k2) * nblk + blk) * HD + 4 * q;
-            *reinterpret_cast<float4 *>(dst) = make_float4(pc[0], pc[1], pc[2], pc[3]);
-        }
-    };
-    form(0, nheads);
-    // more than 16 query heads per KV head: the next batches, the record reused (the reads
+    form_batch<HS>(rec, col, slot, nheads, dst, head_stride);
+    // more than 16 query heads per KV head: the next batches, the records reused (the reads
     // above come first in the wave's LDS order)
     for (int hbase = 16; hbase < grp; hbase += 16) {
         nheads = grp - hbase < 16 ? grp - hbase : 16;
         load_weights(pk + (size_t)(hbase + min(k, nheads - 1)) * npos, vs, j0, nj, qq, p, sb);
-        park(p, sb, k < nheads);
-        form(hbase, nheads);
+        park_record(p, sb, nj, qq, k < nheads, rec + min(k, 15) * kRec);
+        form_batch<HS>(rec, col, slot, nheads, dst + hbase * head_stride, head_stride);
     }
 }
 
