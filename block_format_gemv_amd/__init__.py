@@ -36,7 +36,8 @@ EXPORTS = ("qg_reads", "qg_image_bytes", "qg_pack_q4k", "qg_pack_q6k", "qg_pack_
            "qg_gemv_q", "qg_gemm_q", "qg_quantize_gemv", "qg_quantize_gemv_argmax", "qg_argmax_index",
            "qg_quantize_gemv_multi", "qg_gemv_q_multi", "qg_block_sums", "qg_stream_read", "qg_stream_read_shape", "qg_set_tuning",
            "qg_time_next_launch", "qg_last_error", "qg_version", "qg_kv_cache_rows", "qg_kv_quantize_heads",
-           "qg_kv_scores", "qg_kv_weighted", "qg_kv_weighted_workspace", "qg_kv_weighted_with_workspace")
+           "qg_kv_scores", "qg_kv_weighted", "qg_kv_weighted_workspace", "qg_kv_weighted_with_workspace",
+           "qg_kv_weighted_noalloc")
 VALUE_BLOCK = 32
 KV_HEAD_SIZES = (32, 64, 128, 256)
 
@@ -78,6 +79,7 @@ def _load():
     L.qg_kv_weighted.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp]
     L.qg_kv_weighted_workspace.argtypes = [i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
     L.qg_kv_weighted_with_workspace.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.qg_kv_weighted_noalloc.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp]
     L.qg_time_next_launch.argtypes = [vp, vp]
     L.qg_last_error.restype = ctypes.c_char_p
     return L
@@ -337,6 +339,21 @@ def qg_kv_weighted_with_workspace(nh, nkv, npos, hd, probs, vscales, vcodes, out
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.qg_kv_weighted_with_workspace(nh, nkv, npos, hd, _dptr(probs), _dptr(vscales), _dptr(vcodes),
                                               _dptr(out), _dptr(workspace), ws_bytes, _stream(stream)))
+
+
+KV_NOALLOC_BYTES = 4 << 20
+
+
+def qg_kv_weighted_noalloc(nh, nkv, npos, hd, probs, vscales, vcodes, out, stream=None) -> None:
+    """qg_kv_weighted over the library's fixed per-device workspace (no allocation)."""
+    if _kv_shape_ok(nh, nkv, npos, hd) and nh > 0:
+        _need(out, 4 * nh * hd, "out")
+        if npos > 0:
+            _need(probs, 4 * nh * npos, "probs")
+            _need(vscales, 2 * nkv * npos, "vscales")
+            _need(vcodes, nkv * npos * hd, "vcodes")
+    _check(_lib.qg_kv_weighted_noalloc(nh, nkv, npos, hd, _dptr(probs), _dptr(vscales), _dptr(vcodes), _dptr(out),
+                                       _stream(stream)))
 
 
 def qg_stream_read(buf, nbytes: int, magic: int, sink, stream=None) -> None:

@@ -441,6 +441,26 @@ int qg_kv_weighted_with_workspace(int64_t nh, int64_t nkv, int64_t npos, int64_t
                                        out, static_cast<hipStream_t>(stream));
 }
 
+int qg_kv_weighted_noalloc(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs,
+                           const uint16_t *vscales, const int8_t *vcodes, float *out, void *stream)
+{
+    const char *who = "qg_kv_weighted_noalloc";
+    int st;
+    if ((st = check_kv(who, nh, nkv, npos, hd))) return st;
+    if (nh == 0) return QG_OK;
+    const size_t need = kv_weighted_workspace_bytes(nh, npos, hd);
+    if (need > QG_KV_NOALLOC_BYTES)
+        return fail(QG_E_SHAPE, "%s: the pieces need %zu bytes, the fixed workspace holds %zu", who, need,
+                    (size_t)QG_KV_NOALLOC_BYTES);
+    if ((st = check_ptr(who, "out", out, 4))) return st;
+    if (npos > 0) {
+        if ((st = check_ptr(who, "probs", probs, 4))) return st;
+        if ((st = check_ptr(who, "vscales", vscales, 2))) return st;
+        if ((st = check_ptr(who, "vcodes", vcodes, 4))) return st;
+    }
+    return launch_kv_weighted_noalloc(nh, nkv, npos, hd, probs, vscales, vcodes, out, static_cast<hipStream_t>(stream));
+}
+
 int qg_block_sums(int fmt, int64_t rows, int64_t cols, const void *image, const int8_t *codes,
                   int32_t *csum_out, int32_t *osum_out, void *stream)
 {

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "qg_device.hpp"
 #include "qg_internal.hpp"
 
@@ -596,6 +598,38 @@ int launch_kv_weighted(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_E_RUNTIME, "kv weighted launch: %s", hipGetErrorString(e));
     return QG_OK;
+}
+
+// The fixed workspace of qg_kv_weighted_noalloc: one copy on every device the library runs
+// on, held until the process ends.  Host code reaches it only through the device address
+// hipGetSymbolAddress gives for the current device (the array's name is not that address).
+static __device__ __align__(256) float scratch[QG_KV_NOALLOC_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+void *g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+std::once_flag g_scratch_once[kScratchDevices];
+}  // namespace
+
+int launch_kv_weighted_noalloc(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs,
+                               const uint16_t *vscales, const int8_t *vcodes, float *out, hipStream_t s)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(QG_E_RUNTIME, "kv weighted (no allocation): hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(QG_E_RUNTIME, "kv weighted (no allocation): device %d beyond the %d supported", dev, kScratchDevices);
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (g_scratch_err[dev] == hipSuccess) g_scratch_ptr[dev] = ptr;
+    });
+    if (g_scratch_ptr[dev] == nullptr)
+        return fail(QG_E_RUNTIME, "kv weighted (no allocation): the workspace's address on device %d: %s", dev,
+                    hipGetErrorString(g_scratch_err[dev]));
+    return launch_kv_weighted_two_pass(nh, nkv, npos, hd, probs, vscales, vcodes,
+                                       static_cast<float *>(g_scratch_ptr[dev]), out, s);
 }
 
 size_t kv_weighted_workspace_bytes(int64_t nh, int64_t npos, int64_t hd)

@@ -310,6 +310,20 @@ int qg_kv_weighted_with_workspace(int64_t nh, int64_t nkv, int64_t npos, int64_t
                                   const uint16_t *vscales, const int8_t *vcodes, float *out, void *workspace,
                                   size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under stream capture, tight serving
+ * loops, harnesses that forbid hipMalloc): qg_kv_weighted_with_workspace over a fixed
+ * workspace the library holds on each device, QG_KV_NOALLOC_BYTES long and kept until the
+ * process ends, so that the call allocates nothing.  Same arguments as qg_kv_weighted and the
+ * same bits.  QG_E_SHAPE when the pieces need more than QG_KV_NOALLOC_BYTES (nh *
+ * ceil(npos / QG_VALUE_BLOCK) * hd * 4 bytes: 32 heads over 8192 positions of head size 128
+ * fit); QG_E_RUNTIME when the workspace's device address cannot be had.  Every call on one
+ * device uses the same workspace: calls on one stream follow each other safely, calls that
+ * overlap on one GPU (concurrent streams or host threads) race and give wrong results.
+ * Honours qg_time_next_launch. */
+#define QG_KV_NOALLOC_BYTES ((size_t)4 << 20)
+int qg_kv_weighted_noalloc(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs,
+                           const uint16_t *vscales, const int8_t *vcodes, float *out, void *stream);
+
 /* Integer sums per (row, sub-block), before any scale ("Module lane", Functions
  * block_sums), for one activation row:
  *   Q4K: csum_out int32 [rows][cols/32] = sum sc_j*q*c over sub-block j,

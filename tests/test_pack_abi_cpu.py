@@ -252,6 +252,13 @@ def test_kv_weighted_workspace_size_and_refusals():
     assert L.qg_kv_weighted_with_workspace(8, 2, 10, 96, *args, fake, need, None) == qg.E_SHAPE
     assert L.qg_kv_weighted_with_workspace(8, 2, 10, 64, fake, fake, fake, None, fake, need, None) == qg.E_INVALID
     assert L.qg_kv_weighted_with_workspace(0, 2, 10, 64, None, None, None, None, None, 0, None) == qg.OK
+    # the fixed workspace of qg_kv_weighted_noalloc: 4 MiB, refused beyond it before any GPU work
+    assert qg.KV_NOALLOC_BYTES == 4 << 20
+    assert L.qg_kv_weighted_noalloc(64, 8, 8192, 128, *args, None) == qg.E_SHAPE
+    assert "fixed workspace" in qg.qg_last_error()
+    assert L.qg_kv_weighted_noalloc(8, 3, 10, 64, *args, None) == qg.E_SHAPE
+    assert L.qg_kv_weighted_noalloc(8, 2, 10, 64, fake, fake, fake, None, None) == qg.E_INVALID
+    assert L.qg_kv_weighted_noalloc(0, 2, 10, 64, None, None, None, None, None) == qg.OK
 
 
 def test_kv_binding_refuses_short_buffers():
