@@ -504,10 +504,12 @@ def main():
                         else "gemv1_kernel<..., SRC_CODES> (GEMV of a quantized row)")
     elif fmt_s == "q4k" and mode == 0 and ncol >= (tuned.get("mfma_min_cols") or (2 if rows < 8192 else 5)):
         # the library's choice of matrix-core form (qg_gemm_q, launch_gemm_mfma)
-        form = tuned.get("mfma_form") or (1 if cols <= 16 * 256 and ncol <= 16 else 3 if rows < 8192 else 2)
+        form = tuned.get("mfma_form") or (1 if cols <= 16 * 256 and ncol <= 16 else 3 if rows < 8192
+                                          else 4 if cols <= 16 * 256 else 2)
         kernel_label = {1: "gemm_staged_q4k (matrix cores, columns staged in LDS, one block per wave)",
                         2: "gemm_mfma_q4k (matrix cores, shared operands)",
-                        3: "gemm_split_q4k (matrix cores, one block per wave)"}[form]
+                        3: "gemm_split_q4k (matrix cores, one block per wave)",
+                        4: "gemm_resident_q4k (matrix cores, columns resident in LDS, one row tile per wave)"}[form]
     elif cols <= 16 * 256 and not tuned.get("cols_kernel") and fmt_s in ("q4k", "q6k"):
         kernel_label = "gemv1_cols_kernel (one-column machinery, up to 8 columns a wave)"
     else:

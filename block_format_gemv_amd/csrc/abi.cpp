@@ -141,7 +141,7 @@ int qg_set_tuning(int key, int64_t value)
         g_tuning.mfma_col_tiles = (int)value;
         return QG_OK;
     case QG_TUNE_MFMA_FORM:
-        if (value > 3) return fail(QG_E_INVALID, "qg_set_tuning: form must be 0, 1, 2 or 3");
+        if (value > 4) return fail(QG_E_INVALID, "qg_set_tuning: form must be 0, 1, 2, 3 or 4");
         g_tuning.mfma_form = (int)value;
         return QG_OK;
     case QG_TUNE_COLS_KERNEL:

@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "qg_device.hpp"
 #include "qg_internal.hpp"
 
@@ -847,6 +849,274 @@ int launch_staged_typed(int64_t rows, int G, int64_t ncol, const void *image, co
     return QG_OK;
 }
 
+// ---------------------------------------------------------------------------------------
+// The column-resident form (rows of at most 16 blocks with two column tiles, at most 32 with
+// one): a workgroup of W <= 8 waves owns W row tiles of 16 rows (tile t: rows 16t .. 16t+15, quarter
+// t%4 of 64-row image group t/4) and 16*CT activation columns.  At the start it brings every
+// block's codes of its columns into LDS by LDS-DMA (the staged form's layout: column rows
+// padded by 16 bytes) and its columns' activation scales per block into tables; one barrier.
+// After it each wave walks its tile's blocks alone, with no further barrier: its rows' code
+// chunks and block fields loaded three blocks ahead into a register ring, the three products
+// per column tile from LDS operands (the staged form's K order), each (row, column) combined
+// once and added in block order to the lane's running sums in registers.  The waves of a SIMD
+// drift apart, so the matrix unit and the vector ALU serve different waves at once.
+//
+// grid: row chunks x column batches, the batches of one chunk on one XCD (x = (chunk/8 *
+// nbatch + cb) * 8 + chunk%8, chunks padded to a multiple of 8), so that L2 serves the weight
+// tiles to both.
+
+#ifndef QG_RESIDENT_RING
+#define QG_RESIDENT_RING 6
+#endif
+constexpr int kResidentRing = QG_RESIDENT_RING;   // blocks of weight loads in flight per wave
+
+template <int CT>
+struct ResidentLds {
+    __host__ __device__ static size_t codes(int C) { return (size_t)16 * CT * (C + 16); }
+    // the activation scales per (block, column): m*2^e as a double, then the word
+    __host__ __device__ static size_t bytes(int C, int G) { return codes(C) + (size_t)G * 16 * CT * 12; }
+};
+
+// one block's loads of a row tile: the row's block fields and, per 64-element step st, the 8
+// bytes at 8h of code chunk 2st + jo (the staged form's K order)
+__device__ __forceinline__ void resident_load(const uint8_t *tile, int trow, int jo, int h, uint4 &meta, uint2 (&ch)[4])
+{
+    meta = ld16(tile + 8192 + 16 * trow);
+#pragma unroll
+    for (int st = 0; st < 4; st++) ch[st] = *reinterpret_cast<const uint2 *>(tile + 1024 * (2 * st + jo) + 16 * trow + 8 * h);
+}
+
+// one block of a wave's row tile against its CT column tiles, added to y (TINY: some piece of
+// the workgroup may be tiny, so every piece is combined with the flush and added flushed)
+template <int CT, bool TINY>
+__device__ __forceinline__ void resident_block(const uint4 &meta, const uint2 (&ch)[4], const unsigned char *acodes,
+                                               int cs, int b, const double *sSb, const uint32_t *sWb, int lane,
+                                               float (&y)[CT][4])
+{
+    const int n = lane & 15, grp = lane >> 4, h = grp & 1, jo = grp >> 1;
+    const uint32_t sh = 12u * (uint32_t)jo;
+    const uint64_t lo64 = ((uint64_t)meta.z << 32 | meta.y) >> sh;
+    const uint32_t y1 = (uint32_t)(((uint64_t)meta.w << 32 | meta.z) >> sh);
+    const uint32_t y2 = meta.w >> sh;
+    const uint32_t fs[4] = {(uint32_t)lo64 & 0xFFFu, (uint32_t)(lo64 >> 24) & 0xFFFu, (y1 >> 16) & 0xFFFu,
+                            (y2 >> 8) & 0xFFFu};
+    v4i ah[CT], al[CT], ao[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ct++) ah[ct] = al[ct] = ao[ct] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int st = 0; st < 4; st++) {
+        const uint32_t f = fs[st];
+        const uint32_t hi = (f >> 3) & 7u, lo = f & 7u;
+        const int mr = (int)__builtin_amdgcn_perm(0u, f >> 6, 0x00000000u);   // mn (< 64) in every byte
+        const uint2 c2 = ch[st];
+        const uint32_t q0 = c2.x & 0x0F0F0F0Fu, q1 = c2.y & 0x0F0F0F0Fu;
+        const uint32_t q2 = (c2.x >> 4) & 0x0F0F0F0Fu, q3 = (c2.y >> 4) & 0x0F0F0F0Fu;
+        const v4i Bh = {bytes_times(q0, hi), bytes_times(q1, hi), bytes_times(q2, hi), bytes_times(q3, hi)};
+        const v4i Bl = {bytes_times(q0, lo), bytes_times(q1, lo), bytes_times(q2, lo), bytes_times(q3, lo)};
+        const v4i Bo = {mr, mr, mr, mr};
+#pragma unroll
+        for (int ct = 0; ct < CT; ct++) {
+            // column 16ct + n, elements 32(2st + jo) + 8h .. +7 and +16 .. +23 of block b
+            const unsigned char *arow = acodes + (size_t)(16 * ct + n) * cs + (size_t)b * 256 + 32 * jo + 8 * h + 64 * st;
+            const uint2 lo8 = *reinterpret_cast<const uint2 *>(arow);
+            const uint2 hi8 = *reinterpret_cast<const uint2 *>(arow + 16);
+            const v4i A = {(int)lo8.x, (int)lo8.y, (int)hi8.x, (int)hi8.y};
+            ah[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bh, ah[ct], 0, 0, 0);
+            al[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bl, al[ct], 0, 0, 0);
+            ao[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bo, ao[ct], 0, 0, 0);
+        }
+    }
+    // combine each (row, column) once ("Module numerics", module description) and add it
+    const uint32_t dd = meta.x;
+    const float fd = f16_value(dd), fm = f16_value(dd >> 16);
+    const bool near = q4k_near(fd, fm);
+    const double Dd = (double)fd, Dm = (double)fm;
+    const bool fast = !TINY && __all(near);
+#pragma unroll
+    for (int ct = 0; ct < CT; ct++) {
+        const double *S = sSb + 16 * ct + 4 * grp;
+        const uint32_t *Wd = sWb + 16 * ct + 4 * grp;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int Cb = 8 * ah[ct][i] + al[ct][i];
+            float pc;
+            if (fast) {
+                // no piece is tiny: the conversion needs no flush; an exact -0 added to +0 or to a
+                // nonzero partial sum gives what +0 would
+                const double X = __builtin_fma((double)Cb, Dd, -((double)ao[ct][i] * Dm));
+                pc = (float)(X * S[i]);
+            } else if (near) {
+                pc = piece_q4k_perblock_near(Cb, ao[ct][i], Dd, Dm, S[i]);
+            } else {
+                const int m = (int)((Wd[i] >> 16) & 0xFFu);
+                const int e = (int)(int16_t)(Wd[i] & 0xFFFFu);
+                pc = piece_q4k_perblock(Cb, ao[ct][i], dd, m, e);
+            }
+            y[ct][i] = TINY ? fadd_ftz(y[ct][i], pc) : y[ct][i] + pc;
+        }
+    }
+}
+
+template <int CT, bool TINY, int D>
+__device__ __forceinline__ void resident_walk(const uint8_t *gbase, int G, int trow, const unsigned char *acodes,
+                                              int cs, const double *sS, const uint32_t *sW, int lane, float (&y)[CT][4])
+{
+    constexpr int NC = 16 * CT;
+    const int grp = lane >> 4, h = grp & 1, jo = grp >> 1;
+    // a ring of D register sets, set k holding blocks k, k+D, ...: each is used and then
+    // refilled in place with the block D ahead (past the last block: the last again, unused),
+    // so no register with a load in flight is ever copied and the compiler's wait before a use
+    // counts the younger loads exactly, across the loop's back edge too
+    uint4 m[D];
+    uint2 c[D][4];
+#pragma unroll
+    for (int k = 0; k < D; k++) resident_load(gbase + (size_t)min(k, G - 1) * kTileBytesQ4K, trow, jo, h, m[k], c[k]);
+    int b = 0;
+#pragma unroll 1
+    for (; b + D <= G; b += D) {             // whole rounds: a straight-line body
+#pragma unroll
+        for (int k = 0; k < D; k++) {
+            resident_block<CT, TINY>(m[k], c[k], acodes, cs, b + k, sS + (size_t)(b + k) * NC, sW + (size_t)(b + k) * NC,
+                                     lane, y);
+            resident_load(gbase + (size_t)min(b + k + D, G - 1) * kTileBytesQ4K, trow, jo, h, m[k], c[k]);
+        }
+    }
+    // the last blocks, fewer than D
+#pragma unroll
+    for (int k = 0; k < D - 1; k++)
+        if (b + k < G)
+            resident_block<CT, TINY>(m[k], c[k], acodes, cs, b + k, sS + (size_t)(b + k) * NC, sW + (size_t)(b + k) * NC,
+                                     lane, y);
+}
+
+template <int CT, int GT>
+__global__ __launch_bounds__(512) void gemm_resident_q4k(const uint8_t *image, int rows, int G_arg,
+                                                          const int8_t *__restrict__ codes,
+                                                          const uint32_t *__restrict__ scw, int ncol, int tiles,
+                                                          int chunks, int nbatch, float *__restrict__ out)
+{
+    using L = ResidentLds<CT>;
+    constexpr int NC = 16 * CT;
+    const int G = GT ? GT : G_arg;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int x = (int)blockIdx.x;
+    const int qx = x >> 3;
+    const int cb = qx % nbatch;
+    const int chunk = (qx / nbatch) * 8 + (x & 7);
+    if (chunk >= chunks) return;               // padding workgroup: the whole group leaves at once
+    const int W = (int)(blockDim.x >> 6);
+    const int C = G * 256, cs = C + 16;
+    const int colbase = cb * NC;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    unsigned char *acodes = lds;
+    double *sS = reinterpret_cast<double *>(lds + L::codes(C));
+    uint32_t *sW = reinterpret_cast<uint32_t *>(sS + (size_t)G * NC);
+
+    // the columns' codes: DMA instruction k moves 1 KiB (piece k % P of column k / P, P = the
+    // 1 KiB pieces of a row, the last possibly partial: its lanes past the row load nothing);
+    // wave w issues k = w, w + W, ...  A column past the last is a copy of the last (dropped).
+    const int P = (C + 1023) / 1024;
+    for (int k = wid; k < NC * P; k += W) {
+        const int j = k / P, pk = k % P;
+        if (1024 * pk + 16 * lane < C)
+            dma16(codes + (size_t)min(colbase + j, ncol - 1) * C + 1024 * pk + 16 * lane,
+                  lds_offset(acodes + (size_t)j * cs + 1024 * pk));
+    }
+    // the activation scales, [block][column]
+    for (int i = threadIdx.x; i < NC * G; i += (int)blockDim.x) {
+        const int b = i / NC, j = i % NC;
+        const uint32_t w = scw[(size_t)min(colbase + j, ncol - 1) * G + b];
+        sW[i] = w;
+        sS[i] = __builtin_ldexp((double)((w >> 16) & 0xFFu), (int)(int16_t)(w & 0xFFFFu));
+    }
+    wait_vm<0>();                              // this wave's DMA and table loads have landed
+    __syncthreads();
+
+    const int t = chunk * W + wid;             // this wave's row tile
+    if (t >= tiles) return;                    // no barrier follows
+    // whether any piece of the workgroup may be tiny: an activation exponent below the bound
+    bool tiny = false;
+    for (int i = lane; i < NC * G; i += 64) tiny |= (int)(int16_t)(sW[i] & 0xFFFFu) < kNoTinyExp;
+    tiny = __any(tiny);
+
+    const int g = t >> 2, trow = 16 * (t & 3) + (lane & 15);
+    const uint8_t *gbase = image + (size_t)g * G * kTileBytesQ4K;
+    float y[CT][4];
+#pragma unroll
+    for (int ct = 0; ct < CT; ct++) y[ct][0] = y[ct][1] = y[ct][2] = y[ct][3] = 0.0f;
+    if (tiny) resident_walk<CT, true, kResidentRing>(gbase, G, trow, acodes, cs, sS, sW, lane, y);
+    else resident_walk<CT, false, kResidentRing>(gbase, G, trow, acodes, cs, sS, sW, lane, y);
+
+    const int64_t row = (int64_t)g * 64 + trow;
+    if (row < rows) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ct++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int col = colbase + 16 * ct + 4 * (lane >> 4) + i;
+                if (col < ncol) out[(int64_t)col * rows + row] = canon_nan(y[ct][i]);
+            }
+    }
+}
+
+template <int CT, int GT>
+int launch_resident_typed(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
+                          const qg_act_scale *scales, float *out, hipStream_t s)
+{
+    using L = ResidentLds<CT>;
+    const size_t lds = L::bytes(G * 256, G);
+    if (lds > (size_t)kMaxLds) return QG_E_UNSUPPORTED;
+    const int64_t tiles = (rows + 63) / 64 * 4;
+    const int64_t nbatch = (ncol + 16 * CT - 1) / (16 * CT);
+    // waves per workgroup: the tuning knob if set, else enough to spread every (tile, batch)
+    // over the CUs one workgroup each
+    int W = tuning().gemm_row_tiles;
+    if (W <= 0) {
+        const int64_t cus = device_cu_count();
+        W = (int)std::min<int64_t>(8, std::max<int64_t>(1, (tiles * nbatch + cus - 1) / cus));
+    }
+    if (W > 8) W = 8;                          // 512 threads: 256 registers a lane
+    const int64_t chunks = (tiles + W - 1) / W;
+    const int64_t grid = (chunks + 7) / 8 * 8 * nbatch;
+    if (grid > 0x7fffffff) return fail(QG_E_SHAPE, "gemm: %lld rows x %lld columns is too many", (long long)rows,
+                                       (long long)ncol);
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_resident_q4k<CT, GT>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    (void)attr;   // a refusal shows up as a launch error below
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(scales);
+    hipEvent_t ev0, ev1;
+    take_timing_events(&ev0, &ev1);
+    if (ev0 && ev1)
+        hipExtLaunchKernelGGL((gemm_resident_q4k<CT, GT>), dim3((unsigned)grid), dim3(64 * W), lds, s, ev0, ev1, 0,
+                              static_cast<const uint8_t *>(image), (int)rows, G, codes, w, (int)ncol, (int)tiles,
+                              (int)chunks, (int)nbatch, out);
+    else
+        hipLaunchKernelGGL((gemm_resident_q4k<CT, GT>), dim3((unsigned)grid), dim3(64 * W), lds, s,
+                           static_cast<const uint8_t *>(image), (int)rows, G, codes, w, (int)ncol, (int)tiles,
+                           (int)chunks, (int)nbatch, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_E_RUNTIME, "gemm (matrix cores, column-resident) launch: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+// two column tiles per workgroup where the rows' codes fit (at most 16 blocks), else one
+int launch_resident(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes,
+                    const qg_act_scale *scales, float *out, hipStream_t s)
+{
+    int ct = tuning().mfma_col_tiles;
+    if (ct == 0) ct = G <= 16 && ncol > 16 ? 2 : 1;
+    int st = QG_E_UNSUPPORTED;
+    if (ct == 2) st = G == 16 ? launch_resident_typed<2, 16>(rows, G, ncol, image, codes, scales, out, s)
+                              : launch_resident_typed<2, 0>(rows, G, ncol, image, codes, scales, out, s);
+    else if (ct == 1) st = G == 16 ? launch_resident_typed<1, 16>(rows, G, ncol, image, codes, scales, out, s)
+                                   : launch_resident_typed<1, 0>(rows, G, ncol, image, codes, scales, out, s);
+    if (st == QG_E_UNSUPPORTED)
+        return fail(QG_E_UNSUPPORTED, "gemm: the column-resident form's LDS does not fit %d blocks of %d column tiles",
+                    G, ct);
+    return st;
+}
+
 // row tiles and column tiles per workgroup: the tuning knobs if set, else derived from the
 // shape (enough workgroups to fill the CUs, and the widest column batch whose pieces fit)
 int launch_split(int64_t rows, int G, int64_t ncol, const void *image, const int8_t *codes, const qg_act_scale *scales,
@@ -885,8 +1155,10 @@ int launch_gemm_mfma(int64_t rows, int64_t cols, int64_t ncol, const void *image
     int form = tuning().mfma_form;
     // derived (measured on the 4096- and 14336-row matrices): up to 16 columns of rows of up to
     // 16 blocks the staged form; more columns on fewer than 8192 rows the split form (enough
-    // workgroups to fill the chip); otherwise the shared-operand form
-    if (form == 0) form = (G <= 16 && ncol <= 16) ? 1 : rows < 8192 ? 3 : 2;
+    // workgroups to fill the chip); more on larger matrices of rows of up to 16 blocks the
+    // column-resident form (29.4 against 31.0 us at 64 columns on 14336 rows); otherwise the
+    // shared-operand form
+    if (form == 0) form = (G <= 16 && ncol <= 16) ? 1 : rows < 8192 ? 3 : G <= 16 ? 4 : 2;
     if (form == 1) {
         if (G > 16 || ncol > 16)
             return fail(QG_E_UNSUPPORTED, "gemm: the staged form takes at most 16 columns of at most 16 blocks");
@@ -900,6 +1172,7 @@ int launch_gemm_mfma(int64_t rows, int64_t cols, int64_t ncol, const void *image
         return st;
     }
     if (form == 3) return launch_split(rows, G, ncol, image, codes, scales, out, s);
+    if (form == 4) return launch_resident(rows, G, ncol, image, codes, scales, out, s);
     // shared operands: 2 column tiles up to 32 columns, else 4, unless asked otherwise
     const int tiles = tuning().mfma_col_tiles;
     if (tiles == 1) return launch_cw<1>(rows, G, ncol, image, codes, scales, out, s);

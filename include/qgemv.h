@@ -371,17 +371,22 @@ int qg_stream_read_shape(const void *buf, size_t bytes, int waves_per_wg, int ki
  *                         at most 16 blocks: every wave one block, the columns' codes staged in
  *                         LDS), 2 = shared operands (weight operands built once per workgroup in
  *                         LDS), 3 = split (every wave one block, the activation operands loaded per
- *                         wave); 0 = derived from the shape
- *   QG_TUNE_MFMA_COL_TILES 1, 2 or 4: 16-column tiles per workgroup of the shared-operand and
- *                         split forms; 0 = derived (one for the split form, from the columns for
- *                         the shared-operand form)
+ *                         wave), 4 = column-resident (every block's activation codes of 16 or 32
+ *                         columns staged in LDS once, every wave one 16-row tile over all blocks;
+ *                         rows of at most 16 blocks with two column tiles, 32 with one); 0 =
+ *                         derived from the shape
+ *   QG_TUNE_MFMA_COL_TILES 1, 2 or 4: 16-column tiles per workgroup of the shared-operand,
+ *                         split and (1 or 2) column-resident forms; 0 = derived (one for the split
+ *                         form, from the columns for the shared-operand form, two for the
+ *                         column-resident form on rows of at most 16 blocks)
  *   QG_TUNE_COLS_KERNEL   several columns below the matrix-core threshold (Q4_K/Q6_K, at most 16
  *                         blocks per row): 0 = the one-column kernel's machinery, NC columns per
  *                         wave (default); 1 = the kernel that stages the columns in LDS
  *   QG_TUNE_MFMA_TABLES   the shared-operand form: 0 = read every block's block scales, sub-block
  *                         fields and activation scales into LDS tables at the start where they
  *                         fit (default); 1 = load them with each block
- *   QG_TUNE_GEMM_ROW_TILES the staged and split forms: 16-row tiles per workgroup, 1, 2 or 4 (0 =
+ *   QG_TUNE_GEMM_ROW_TILES the staged and split forms: 16-row tiles per workgroup, 1, 2 or 4; the
+ *                         column-resident form: waves (16-row tiles) per workgroup, 1, 2 or 4 (0 =
  *                         derived from the rows and columns)
  *   QG_TUNE_GEMV_QUARTER  one column of a Q4_K PerBlock matrix of at most 16 blocks per row,
  *                         without argmax: 1 = workgroups of 16 rows (four per 64-row group, so

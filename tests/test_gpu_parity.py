@@ -497,8 +497,9 @@ def test_several_columns_one_column_machinery(qg, fmt, mode):
 def test_matrix_core_gemm_matches_oracle(qg, ncol):
     """Q4_K PerBlock batches run on v_mfma_i32_16x16x64_i8 (by default from 2 or 5 columns; here
     forced for every count); every (row, column) must carry the oracle's bits in every form,
-    across column-tile and row-tile settings, ragged rows and columns, and block scales that
-    take both the near-exponent and the general combine."""
+    across column-tile and row-tile (for the column-resident form: waves per workgroup)
+    settings, ragged rows and columns, and block scales that take both the near-exponent and
+    the general combine."""
     f = _adversarial_fields("q4k", 130, 1280, 900 + ncol)
     M = Mat(qg, f)
     xs = gen.act_outliers(ncol, 1280, 901 + ncol)
@@ -507,14 +508,14 @@ def test_matrix_core_gemm_matches_oracle(qg, ncol):
     want = oracle.gemm(f, c, m, e, 0).reshape(ncol, 130)
     try:
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 1)                # matrix cores for any column count
-        # derived, staged (at most 16 columns), shared operands, split
-        for form in (0, 1, 2, 3):
+        # derived, staged (at most 16 columns), shared operands, split, column-resident
+        for form in (0, 1, 2, 3, 4):
             if form == 1 and ncol > 16:
                 continue
             qg.qg_set_tuning(qg.TUNE_MFMA_FORM, form)
-            for ct in (0, 1, 2, 4):                                 # 0: derived from the column count
+            for ct in ((0, 1, 2) if form == 4 else (0, 1, 2, 4)):   # 0: derived from the column count
                 qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, ct)
-                for rt in ((0, 1, 2, 4) if form in (1, 3) and ct == 0 else (0,)):
+                for rt in ((0, 1, 2, 4) if form in (1, 3, 4) and ct == 0 else (0,)):
                     qg.qg_set_tuning(qg.TUNE_GEMM_ROW_TILES, rt)
                     for tab in ((0, 1) if form == 2 else (0,)):     # shared operands: scale tables or not
                         qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, tab)
@@ -538,9 +539,10 @@ def test_matrix_core_gemm_matches_oracle(qg, ncol):
 @pytest.mark.parametrize("ncol", [64, 100])
 def test_matrix_core_gemm_16_blocks(qg, ncol):
     """Rows of 16 blocks through the shared-operand kernel, whose block loop is unrolled when
-    compiled: ragged rows and columns, block scales that take both the near-exponent and the
-    general combine, and (in the second run) a row of tiny activations, which makes its batch
-    of 64 columns take the flushed combine; with and without the scale tables."""
+    compiled, and the column-resident kernel, compiled for 16 blocks too: ragged rows and
+    columns, block scales that take both the near-exponent and the general combine, and (in the
+    second run) a row of tiny activations, which makes its batch of columns take the flushed
+    combine; with and without the scale tables."""
     rows, cols = 130, 4096
     f = _adversarial_fields("q4k", rows, cols, 4400 + ncol)
     for r in (1, 66):
@@ -559,8 +561,16 @@ def test_matrix_core_gemm_16_blocks(qg, ncol):
                 say("matrix-core gemm, 16 blocks", ncol, "tiny row", tiny, "tables off", tab)
                 out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
                 assert first_mismatch(out, want) is None, (ncol, tiny, tab, first_mismatch(out, want))
+            qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, 0)
+            qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 4)      # the column-resident form, one or two column tiles
+            for ct in (0, 1, 2):
+                qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, ct)
+                say("matrix-core gemm, 16 blocks, column-resident", ncol, "tiny row", tiny, "column tiles", ct)
+                out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
+                assert first_mismatch(out, want) is None, (ncol, tiny, "resident", ct, first_mismatch(out, want))
         finally:
             qg.qg_set_tuning(qg.TUNE_MFMA_TABLES, 0)
+            qg.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 0)
             qg.qg_set_tuning(qg.TUNE_MFMA_FORM, 0)
 
 
@@ -570,7 +580,7 @@ def test_matrix_core_gemm_long_rows(qg, cols):
     tables fit in LDS beside the operand stages (the block loop runs with three prefetch
     buffers), at 32 and 48 they do not and each block loads its own scales; 40 columns, ragged
     rows, far block-scale pairs and one row of tiny activations; and the form the dispatch
-    derives for these 70 rows (split)."""
+    derives for these 70 rows (split); the column-resident form at 24 and 32 blocks."""
     rows, ncol = 70, 40
     f = _adversarial_fields("q4k", rows, cols, 5100 + cols // 256)
     _subnormal_partial_q4k(f, 3)
@@ -580,7 +590,7 @@ def test_matrix_core_gemm_long_rows(qg, cols):
     act, c, m, e, _ = gpu_quant(qg, xs, 0)
     want = oracle.gemm(f, c, m, e, 0).reshape(ncol, rows)
     try:
-        for form in (2, 0):
+        for form in ((2, 0, 4) if cols <= 8192 else (2, 0)):   # column-resident: one column tile to 32 blocks
             qg.qg_set_tuning(qg.TUNE_MFMA_FORM, form)
             say("matrix-core gemm, long rows", cols, "form", form)
             out = qg.gemm(M.fmt, M.rows, M.cols, M.img, act)
