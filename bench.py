@@ -78,12 +78,12 @@ MEASURED_TRAFFIC = {
 GEMM_SOURCES = KERNEL_SOURCES + ("block_format_gemv_amd/csrc/gemm_mfma.hip",)
 MFMA_PEAK_TOPS = 5000.0     # dense int8 matrix-core peak of the part, TOP/s
 MEASURED_GEMM = {
-    "q4k_gemm_n2_4096x4096": {"kernel_sha": "1cefc69e291f08b9", "fetch_kib": 4687.5, "write_kib": 32.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.43},
-    "q4k_gemm_n8_4096x4096": {"kernel_sha": "1cefc69e291f08b9", "fetch_kib": 4785.0, "write_kib": 128.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.3},
-    "q4k_gemm_n64_4096x4096": {"kernel_sha": "1cefc69e291f08b9", "fetch_kib": 5724.5, "write_kib": 1024.0, "mops_i8": 12582912.0, "mfma_util_pct": 5.98},
-    "q4k_gemm_n2_14336x4096": {"kernel_sha": "1cefc69e291f08b9", "fetch_kib": 16213.5, "write_kib": 112.0},
-    "q4k_gemm_n8_14336x4096": {"kernel_sha": "1cefc69e291f08b9", "fetch_kib": 16328.5, "write_kib": 448.0, "mops_i8": 11010048.0, "mfma_util_pct": 5.29},
-    "q4k_gemm_n64_14336x4096": {"kernel_sha": "1cefc69e291f08b9", "fetch_kib": 17570.9375, "write_kib": 3584.0, "mops_i8": 44040192.0, "mfma_util_pct": 12.51},
+    "q4k_gemm_n2_4096x4096": {"kernel_sha": "f7b45f04a8af2468", "fetch_kib": 4687.5, "write_kib": 32.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.43},
+    "q4k_gemm_n8_4096x4096": {"kernel_sha": "f7b45f04a8af2468", "fetch_kib": 4785.0, "write_kib": 128.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.2},
+    "q4k_gemm_n64_4096x4096": {"kernel_sha": "f7b45f04a8af2468", "fetch_kib": 5724.5, "write_kib": 1024.0, "mops_i8": 12582912.0, "mfma_util_pct": 6.05},
+    "q4k_gemm_n2_14336x4096": {"kernel_sha": "f7b45f04a8af2468", "fetch_kib": 16213.5, "write_kib": 112.0},
+    "q4k_gemm_n8_14336x4096": {"kernel_sha": "f7b45f04a8af2468", "fetch_kib": 16328.5, "write_kib": 448.0, "mops_i8": 11010048.0, "mfma_util_pct": 5.3},
+    "q4k_gemm_n64_14336x4096": {"kernel_sha": "f7b45f04a8af2468", "fetch_kib": 17576.875, "write_kib": 3584.0, "mops_i8": 44040192.0, "mfma_util_pct": 12.69},
 }
 
 
