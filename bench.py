@@ -55,18 +55,18 @@ KERNEL_SOURCES = ("block_format_gemv_amd/csrc/gemv.hip", "block_format_gemv_amd/
                   "block_format_gemv_amd/csrc/qg_internal.hpp")
 MEASURED_TRAFFIC = {
     # (workload, dominant kernel): medians per dispatch, kernel sources hash
-    ("q4k_ffn_up_14336x4096", "fused"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 16242.5, "write_kib": 61.0625},
-    ("q4k_ffn_up_14336x4096", "gemv"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 16183.0, "write_kib": 56.0},
-    ("q4k_attn_4096x4096", "fused"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 4716.5, "write_kib": 21.0625},
-    ("q4k_attn_4096x4096", "gemv"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 4656.5, "write_kib": 16.0},
-    ("q4k_sub32_14336x4096", "fused"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 16289.5, "write_kib": 61.5},
-    ("q4k_sub32_14336x4096", "gemv"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 16234.0, "write_kib": 56.0},
-    ("q6k_output_128256x4096", "fused"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 210543.5, "write_kib": 506.0625},
-    ("q6k_output_128256x4096", "gemv"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 210481.0, "write_kib": 501.0},
-    ("q8_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 30581.0, "write_kib": 61.5},
-    ("q8_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 30520.5, "write_kib": 56.0},
-    ("q4_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 16252.0, "write_kib": 61.5},
-    ("q4_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "8f5c2e969cd740f3", "fetch_kib": 16190.5, "write_kib": 56.0},
+    ("q4k_ffn_up_14336x4096", "fused"): {"kernel_sha": "af7f3f7cdc0c9599", "fetch_kib": 16242.5, "write_kib": 61.0625},
+    ("q4k_ffn_up_14336x4096", "gemv"): {"kernel_sha": "af7f3f7cdc0c9599", "fetch_kib": 16183.0, "write_kib": 56.0},
+    ("q4k_attn_4096x4096", "fused"): {"kernel_sha": "af7f3f7cdc0c9599", "fetch_kib": 4716.5, "write_kib": 21.0625},
+    ("q4k_attn_4096x4096", "gemv"): {"kernel_sha": "af7f3f7cdc0c9599", "fetch_kib": 4656.5, "write_kib": 16.0},
+    ("q4k_sub32_14336x4096", "fused"): {"kernel_sha": "af7f3f7cdc0c9599", "fetch_kib": 16289.5, "write_kib": 61.5},
+    ("q4k_sub32_14336x4096", "gemv"): {"kernel_sha": "af7f3f7cdc0c9599", "fetch_kib": 16234.0, "write_kib": 56.0},
+    ("q6k_output_128256x4096", "fused"): {"kernel_sha": "af7f3f7cdc0c9599", "fetch_kib": 210543.5, "write_kib": 506.0625},
+    ("q6k_output_128256x4096", "gemv"): {"kernel_sha": "af7f3f7cdc0c9599", "fetch_kib": 210481.0, "write_kib": 501.0},
+    ("q8_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "af7f3f7cdc0c9599", "fetch_kib": 30581.0, "write_kib": 61.5},
+    ("q8_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "af7f3f7cdc0c9599", "fetch_kib": 30520.5, "write_kib": 56.0},
+    ("q4_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "af7f3f7cdc0c9599", "fetch_kib": 16252.0, "write_kib": 61.5},
+    ("q4_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "af7f3f7cdc0c9599", "fetch_kib": 16190.5, "write_kib": 56.0},
 }
 
 # The batched GEMM kernels (several columns): HBM traffic as above, and for the int8
