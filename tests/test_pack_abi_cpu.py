@@ -170,7 +170,7 @@ def test_validation_refuses_before_any_gpu_work():
     assert L.qg_set_tuning(qg.TUNE_WAVES_PER_WG, 3) == qg.E_INVALID
     assert L.qg_set_tuning(qg.TUNE_MFMA_COL_TILES, 3) == qg.E_INVALID
     assert L.qg_set_tuning(qg.TUNE_MFMA_TABLES, 2) == qg.E_INVALID
-    assert L.qg_set_tuning(qg.TUNE_MFMA_FORM, 4) == qg.E_INVALID
+    assert L.qg_set_tuning(qg.TUNE_MFMA_FORM, 5) == qg.E_INVALID
     assert L.qg_set_tuning(5, 0) == qg.E_INVALID                # no longer a key
     assert L.qg_set_tuning(qg.TUNE_GEMM_ROW_TILES, 3) == qg.E_INVALID
     assert L.qg_set_tuning(qg.TUNE_GEMV_QUARTER, 3) == qg.E_INVALID
