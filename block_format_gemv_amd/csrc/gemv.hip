@@ -86,6 +86,7 @@ struct ActWave {
     int s16;           // lane l: sum of the 16 codes of its quad
     int s32;           // lane l: sum of the 32 codes of its octet
     int m, e;          // lane l: the scale of its activation block
+    uint32_t me;       // the same packed as a qg_act_scale (e in bits 0..15, m in 16..23)
     __device__ __forceinline__ uint4 codes16(int, int i) const
     {
         return make_uint4((uint32_t)__builtin_amdgcn_readlane((int)packed, 4 * i),
@@ -98,9 +99,10 @@ struct ActWave {
     __device__ __forceinline__ qg_act_scale scale(int, int j, int per_block) const
     {
         const int l = per_block == 1 ? 0 : 8 * j;
+        const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)me, l);
         qg_act_scale s;
-        s.e = (int16_t)__builtin_amdgcn_readlane(e, l);
-        s.m = (uint8_t)__builtin_amdgcn_readlane(m, l);
+        s.e = (int16_t)(v & 0xFFFFu);
+        s.m = (uint8_t)(v >> 16);
         s.pad = 0;
         return s;
     }
@@ -464,17 +466,20 @@ __device__ __forceinline__ float pair_piece(const TileRegs<QG_Q4K> &T, int b, co
         }
         return piece_q4k_perblock(Cb, Ob, T.meta.x, s.m, s.e);
     } else {
-        int Cj[8], Oj[8], m[8], e[8];
+        // the sub-block sums, then the activation side (the same for every row)
+        int m[8], e[8], Cj[8], Oj[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int P = q4k_sub(T.w[i], b, i, act);
-            Cj[i] = mul_i24((int)(f[i] & 63u), P);
+            Cj[i] = mul_i24((int)(f[i] & 63u), q4k_sub(T.w[i], b, i, act));
             Oj[i] = mul_i24((int)(f[i] >> 6), act.sum32(b, i));
             const qg_act_scale s = act.scale(b, i, 8);
             m[i] = s.m;
             e[i] = s.e;
         }
-        return piece_q4k_sub32(Cj, Oj, m, e, T.meta.x);
+        const Sub32Act g = sub32_act(m, e);
+        float r;
+        if (g.fast && sub32_first_route(Cj, Oj, g, T.meta.x, r)) return r;
+        return piece_q4k_sub32(Cj, Oj, g, T.meta.x);
     }
 }
 
@@ -767,6 +772,7 @@ __device__ __forceinline__ ActWave quantize_block_in_wave(float4 v, int b, int G
     a.s32 = octet_sum_of_quads(a.s16);
     a.m = q.m;
     a.e = q.e;
+    a.me = ((uint32_t)q.e & 0xFFFFu) | ((uint32_t)q.m << 16);
     if (b < G) {
         const bool leader = (lane & (GROUP_LANES - 1)) == 0;
         if (emit) {
@@ -797,6 +803,7 @@ __device__ __forceinline__ ActWave ready_act(const ActRaw<SRC> &r, int b, int G,
         a.s32 = octet_sum_of_quads(a.s16);
         a.m = (int)((r.scale >> 16) & 0xFFu);
         a.e = (int)(int16_t)(r.scale & 0xFFFFu);
+        a.me = r.scale;
         return a;
     }
 }

@@ -506,77 +506,115 @@ __device__ __forceinline__ bool sum8_pair(const double (&T)[8], int low, float &
     return true;
 }
 
-// The last steps of the first Sub32 path below: R32(2^emin * (d*IC - dmin*IO)) for the exact
-// integer sums IC = sum F_j C_j and IO = sum F_j O_j (F_j = m_j 2^(e_j - emin)); see there.
-__device__ __forceinline__ float sub32_near_finish(double IC, double IO, float fd, float fm, int emin)
+// A whole number F < 2^21 as a binary64, built from its bits: exact, and when F is the same
+// for every lane the work stays in scalar registers (no vector conversion).  The low word of
+// the result is zero: F has at most 21 significant bits, all of them in the high word.
+__device__ __forceinline__ double small_uint_f64(uint32_t F)
 {
-    const double Dd = (double)fd;
-    const double p1 = IC * Dd;
-    const double e1 = __builtin_fma(IC, Dd, -p1);
-    const double p2 = -(IO * (double)fm);
-    const double s = p1 + p2;
-    const double bv = s - p1;
-    const double av = s - bv;
-    const double t = (p1 - av) + (p2 - bv);
-    const double u = t + e1;
-    return r32_sum2(__builtin_ldexp(s, emin), __builtin_ldexp(u, emin));
+    const int lz = __builtin_clz(F | 1u);
+    const uint32_t hi = ((F << (lz - 11)) + ((uint32_t)(1053 - lz) << 20)) & (0u - (uint32_t)(F != 0u));
+    return __builtin_bit_cast(double, (uint64_t)hi << 32);
+}
+
+// R32 of y = 2^emin * V when y is V's binary64 rounding scaled by a power of two (no underflow):
+// the two roundings give V's own binary32 rounding unless y lies on a binary32 rounding boundary
+// (bit 28 of the binary64 significand set, bits 0..27 clear: the midpoint of two binary32
+// neighbours) or below the least binary32 normal.  True, with out set, when neither holds or
+// y is zero (+0 then, whatever the sign).
+__device__ __forceinline__ bool r32_of_rounded(double y, float &out)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, y);
+    const uint32_t hi = (uint32_t)(b >> 32), lo = (uint32_t)b;
+    const bool ok = ((hi & 0x7FF00000u) >= ((1023u - 126u) << 20) && (lo & 0x1FFFFFFFu) != 0x10000000u) || y == 0.0;
+    out = (float)y + 0.0f;
+    return ok;
+}
+
+// The activation side of a Q4_K-style Sub32 group, the same on every lane of a tile: the scales,
+// their exponent extremes, whether the first route below applies (significands at most 15, the
+// quantizer's, and exponents within 16 places) and then F_j = m_j * 2^(e_j - emin) (< 2^20,
+// built in scalar registers), else F_j = 0.
+struct Sub32Act {
+    int m[8], e[8];
+    int emin, emax;
+    bool fast;
+    double F[8];
+};
+
+__device__ __forceinline__ Sub32Act sub32_act(const int (&m)[8], const int (&e)[8])
+{
+    Sub32Act g;
+    // extremes in scalar registers (a read of the first lane after each step keeps them there)
+    int emin = e[0], emax = e[0], mmax = m[0];
+#pragma unroll
+    for (int j = 1; j < 8; j++) {
+        emin = __builtin_amdgcn_readfirstlane(e[j] < emin ? e[j] : emin);
+        emax = __builtin_amdgcn_readfirstlane(e[j] > emax ? e[j] : emax);
+        mmax = __builtin_amdgcn_readfirstlane(m[j] > mmax ? m[j] : mmax);
+    }
+    g.emin = emin;
+    g.emax = emax;
+    g.fast = emax - emin <= 16 && mmax <= 15;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        g.m[j] = m[j];
+        g.e[j] = e[j];
+        g.F[j] = small_uint_f64(g.fast ? (uint32_t)m[j] << (e[j] - emin) : 0u);
+    }
+    return g;
 }
 
 // Sub32, Q4_K-style: R32(sum_j m_j 2^e_j (d*C_j - dmin*O_j)), the sixteen terms of exact_sum.
-// When the block scales are near (q4k_near), X_j = d*C_j - dmin*O_j is exact in one fma (|C_j|
-// < 2^22, |O_j| < 2^18) and T_j = X_j * m_j 2^e_j too (m_j has 4 significant bits); with the sum
-// window not engaged the eight T_j are summed by sum8_pair.  Otherwise the 128-bit sum.
 //
-// First, when the group's activation exponents span at most 16 places: with F_j = m_j *
-// 2^(e_j - emin) (below 2^20; the activation scales are the same for every row of a tile),
-// IC = sum F_j C_j (< 2^45) and IO = sum F_j O_j (< 2^41) are exact integer sums in f64, and the
-// piece is R32(2^emin * (d*IC - dmin*IO)).  d*IC is split exactly into p1 + e1 (its rounded
-// product and the fma residual), dmin*IO is exact (< 2^52), TwoSum gives p1 - dmin*IO = s + t
-// exactly, and u = t + e1 is exact: both are multiples of the lesser least place of d and
-// dmin, below 2^6 times the greater (the block scales are near, so their exponents differ by
-// at most 12).  Then r32_sum2 rounds 2^emin * (s + u) once.
-__device__ __forceinline__ float piece_q4k_sub32(const int (&C)[8], const int (&O)[8], const int (&m)[8],
-                                                 const int (&e)[8], uint32_t d_dmin)
+// First route (g.fast; all sixteen term exponents then lie within 16 + 29 places, so the sum
+// window cannot engage): IC = sum F_j C_j (< 2^45) and IO = sum F_j O_j (< 2^41) are exact f64
+// sums and the group is 2^emin * (d*IC - dmin*IO).  dmin*IO is exact (< 2^52), so one fma
+// gives V = d*IC - dmin*IO rounded once to binary64, and r32_of_rounded turns 2^emin times that
+// into the piece.  False (out untouched) when it sits on a binary32 rounding boundary or below
+// the normal range: then piece_q4k_sub32.
+__device__ __forceinline__ bool sub32_first_route(const int (&C)[8], const int (&O)[8], const Sub32Act &g,
+                                                  uint32_t d_dmin, float &out)
 {
+    double IC = 0.0, IO = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        IC = __builtin_fma(g.F[j], (double)C[j], IC);
+        IO = __builtin_fma(g.F[j], (double)O[j], IO);
+    }
+    const float fd = f16_value(d_dmin), fm = f16_value(d_dmin >> 16);
+    const double V = __builtin_fma(IC, (double)fd, -(IO * (double)fm));
+    return r32_of_rounded(__builtin_ldexp(V, g.emin), out);
+}
+
+// The other groups (and the first route's boundary cases): when the block scales are near
+// (q4k_near), X_j = d*C_j - dmin*O_j is exact in one fma (|C_j| < 2^22, |O_j| < 2^18) and T_j =
+// X_j * m_j 2^e_j too; with the sum window not engaged the eight T_j are summed by sum8_pair.
+// Failing that, the 128-bit sum of the sixteen terms.
+__device__ __forceinline__ float piece_q4k_sub32(const int (&C)[8], const int (&O)[8], const Sub32Act &g,
+                                                 uint32_t d_dmin)
+{
+    const float fd = f16_value(d_dmin), fm = f16_value(d_dmin >> 16);
     const F16Scale d = f16_scale(d_dmin & 0xFFFFu);
     const F16Scale dm = f16_scale(d_dmin >> 16);
-    int emin = e[0], emax = e[0];
-#pragma unroll
-    for (int j = 1; j < 8; j++) {
-        emin = e[j] < emin ? e[j] : emin;
-        emax = e[j] > emax ? e[j] : emax;
-    }
     const int dlo = d.ex < dm.ex ? d.ex : dm.ex, dhi = d.ex < dm.ex ? dm.ex : d.ex;
-    const float fd = f16_value(d_dmin), fm = f16_value(d_dmin >> 16);
-    const bool near = q4k_near(fd, fm) && (emax - emin) + (dhi - dlo) <= kSumWindow;
-    if (near && emax - emin <= 16) {
-        double IC = 0.0, IO = 0.0;
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const double F = __builtin_ldexp((double)m[j], e[j] - emin);
-            IC = __builtin_fma(F, (double)C[j], IC);
-            IO = __builtin_fma(F, (double)O[j], IO);
-        }
-        return sub32_near_finish(IC, IO, fd, fm, emin);
-    }
-    if (near) {
+    if (q4k_near(fd, fm) && (g.emax - g.emin) + (dhi - dlo) <= kSumWindow) {
         double T[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const double X = __builtin_fma((double)C[j], (double)fd, -((double)O[j] * (double)fm));
-            T[j] = X * __builtin_ldexp((double)m[j], e[j]);
+            T[j] = X * __builtin_ldexp((double)g.m[j], g.e[j]);
         }
         float r;
-        if (sum8_pair(T, emin + dlo, r)) return r;
+        if (sum8_pair(T, g.emin + dlo, r)) return r;
     }
     long long v[16];
     int ex[16];
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        v[2 * j] = (long long)(d.sig * m[j]) * C[j];
-        ex[2 * j] = e[j] + d.ex;
-        v[2 * j + 1] = -(long long)(dm.sig * m[j]) * O[j];
-        ex[2 * j + 1] = e[j] + dm.ex;
+        v[2 * j] = (long long)(d.sig * g.m[j]) * C[j];
+        ex[2 * j] = g.e[j] + d.ex;
+        v[2 * j + 1] = -(long long)(dm.sig * g.m[j]) * O[j];
+        ex[2 * j + 1] = g.e[j] + dm.ex;
     }
     return exact_sum<16>(v, ex);
 }

@@ -726,6 +726,26 @@ def test_sub32_exponent_spans(qg, span):
         assert first_mismatch(out, want) is None, (span, k)
 
 
+def test_sub32_pieces_on_binary32_boundaries(qg):
+    """Sub32 group values on a binary32 rounding boundary and one binary64 step either side of
+    it (where a binary64 rounding taken first lands on the boundary), and group values below the
+    binary32 normal range: two columns at once, the quantized-row GEMV and the one-launch step
+    give the oracle's bits."""
+    f, x = gen.sub32_boundary_rows()
+    M = Mat(qg, f)
+    c, m, e, _ = oracle.quantize(x, 1)
+    want = oracle.gemm(f, c, m, e, 1).reshape(2, f["rows"])
+    say("sub32 boundary rows")
+    act, gc, gm, ge, _ = gpu_quant(qg, x, 1)
+    assert np.array_equal(gc, c) and np.array_equal(ge, e)
+    assert first_mismatch(qg.gemm(M.fmt, M.rows, M.cols, M.img, act), want) is None
+    for k in range(2):
+        one, *_ = gpu_quant(qg, x[k:k + 1], 1)
+        assert first_mismatch(run_gemv(qg, M, one), want[k]) is None, k
+        out, *_ = _fused(qg, M, x[k:k + 1], 1)
+        assert first_mismatch(out, want[k]) is None, k
+
+
 @pytest.mark.parametrize("cols", [4096, 8192])
 def test_subnormal_partial_sums_wide_rows(qg, cols):
     """The same cancelling rows at 16 blocks (one wave per block) and 32 blocks (two tiles

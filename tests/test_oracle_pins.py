@@ -267,6 +267,35 @@ def test_sub32_group_closed_form():
     assert Fraction(float(got)) != want
 
 
+def test_sub32_group_values_beside_binary32_boundaries():
+    """Hand-laid Sub32 groups (workloads.gen.sub32_boundary_rows): with F = 8 * 2^16 on block 0
+    and 8 on block 1, the integer sums are IC = 2^32 + 768 (768 without block 0) and IO = 8, so
+    a group is 2^emin * (d * IC - dmin * IO) with emin = -16 (or -128 for the second row).  Its
+    one rounding, by exact rationals, is the oracle's output; for dmin = +-2^-24 the value lies
+    2^-37 beside the midpoint 2^16 + 3 * 2^-8, where rounding to binary64 first (which lands on
+    the midpoint) and then to binary32 gives the other neighbour."""
+    f, x = gen.sub32_boundary_rows()
+    c, m, e, _ = oracle.quantize(x, oracle.SUB32)
+    assert list(e[0]) == [0, -16] + [-8] * 6 and list(e[1]) == [-112, -128] + [-120] * 6
+    assert (m == 8).all()
+    two = Fraction(2)
+    d = [1, 1, 1, -1, 1, two ** -24, -two ** -24]
+    dmin = [two ** -24, -two ** -24, 0, two ** -24, two ** -24, 0, 0]
+    IC = [2 ** 32 + 768] * 4 + [768] * 3
+    for k, emin in ((0, -16), (1, -128)):
+        got = oracle.gemv(f, c[k:k + 1], m[k:k + 1], e[k:k + 1], oracle.SUB32)
+        for r in range(7):
+            want = two ** emin * (d[r] * IC[r] - dmin[r] * 8)
+            if k == 1 and r >= 5:
+                assert float(got[r]) == 0.0                  # below 2^-126: flushed
+                continue
+            assert f32bits(got[r]) == f32bits(exact.round_f32(want)), (k, r)
+    got0 = oracle.gemv(f, c[:1], m[:1], e[:1], oracle.SUB32)
+    assert float(got0[0]) == 2.0 ** 16 + 2.0 ** -7 and float(got0[1]) == 2.0 ** 16 + 2.0 ** -6
+    assert float(got0[2]) == 2.0 ** 16 + 2.0 ** -6                 # the exact tie, to even
+    assert float(np.float32(float(two ** -16 * (IC[0] - dmin[0] * 8)))) != float(got0[0])
+
+
 # --- integer sums (Module lane: the excess-form identity) ----------------------------------
 
 def test_excess_form_identity_on_random_units():

@@ -214,3 +214,46 @@ def kv_decode(nh: int = 32, nkv: int = 8, npos: int = 4096, hd: int = 128, seed:
     query = act_normal(nh, hd, seed + 2)
     weights = attn_weights(nh, npos, seed + 3)
     return keys, vals, query, weights
+
+
+# --- hand-laid inputs ----------------------------------------------------------------------
+
+def sub32_boundary_rows():
+    """A 7 x 256 Q4_K-style matrix and two activation rows laid out by hand so that Sub32 group
+    values fall on or just beside a binary32 rounding boundary, where a binary64 value rounded
+    again to binary32 would be off, and (second row) below the binary32 normal range.
+
+    Activation row 0: block 0 holds 1016 and 256 (the scale 8 * 2^0, codes 127 and 32), block 1
+    holds 127, 12, -11 and -127 times 2^-13 (the scale 8 * 2^-16, codes of those values), each
+    of the other six blocks one element 1016 * 2^-8 (weights 0 there; the group's exponents
+    span 16 places).  Row 1 is row 0 times 2^-112.  Weights: nibble 8 at element 1
+    (against the code 32) and at element 33 (against the code 12), every other nibble 0;
+    sub-block scales 32 and 1, offset 1 on sub-block 1 alone.  The rows differ in d and dmin
+    (binary16 bits) and in whether sub-block 0 counts:
+        row  d       dmin    sc[0]
+        0    0x3C00  0x0001  32      1.0, 2^-24
+        1    0x3C00  0x8001  32      1.0, -2^-24
+        2    0x3C00  0x0000  32      1.0, 0
+        3    0xBC00  0x0001  32      -1.0, 2^-24
+        4    0x3C00  0x0001  0       1.0, 2^-24
+        5    0x0001  0x0000  0       2^-24, 0
+        6    0x8001  0x0000  0       -2^-24, 0
+    """
+    rows, cols = 7, 256
+    x = np.zeros((2, cols), np.float32)
+    x[0, 0], x[0, 1] = 1016.0, 256.0
+    x[0, 32:36] = np.array([127.0, 12.0, -11.0, -127.0]) * 2.0 ** -13
+    x[0, 64::32] = 1016.0 * 2.0 ** -8
+    x[1] = x[0] * np.float32(2.0 ** -112)
+    q = np.zeros((rows, cols), np.uint8)
+    q[:, 1] = 8
+    q[:, 33] = 8
+    sc = np.zeros((rows, cols // 32), np.uint8)
+    sc[:, 0], sc[:, 1] = 32, 1
+    sc[4:, 0] = 0
+    mn = np.zeros((rows, cols // 32), np.uint8)
+    mn[:, 1] = 1
+    d = np.array([[0x3C00], [0x3C00], [0x3C00], [0xBC00], [0x3C00], [0x0001], [0x8001]], np.uint16)
+    dmin = np.array([[0x0001], [0x8001], [0x0000], [0x0001], [0x0001], [0x0000], [0x0000]], np.uint16)
+    f = {"fmt": "q4k", "rows": rows, "cols": cols, "q": q, "sc": sc, "mn": mn, "d": d, "dmin": dmin}
+    return f, x
