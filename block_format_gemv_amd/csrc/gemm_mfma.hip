@@ -931,7 +931,22 @@ __device__ __forceinline__ void resident_block(const uint4 &meta, const uint2 (&
     const float fd = f16_value(dd), fm = f16_value(dd >> 16);
     const bool near = q4k_near(fd, fm);
     const double Dd = (double)fd, Dm = (double)fm;
-    const bool fast = !TINY && __all(near);
+    if (!TINY && __all(near)) {
+        // no piece is tiny: the conversion needs no flush; an exact -0 added to +0 or to a
+        // nonzero partial sum gives what +0 would.  One straight run for the whole block, so
+        // the scale reads are issued together.
+#pragma unroll
+        for (int ct = 0; ct < CT; ct++) {
+            const double *S = sSb + 16 * ct + 4 * grp;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int Cb = 8 * ah[ct][i] + al[ct][i];
+                const double X = __builtin_fma((double)Cb, Dd, -((double)ao[ct][i] * Dm));
+                y[ct][i] = y[ct][i] + (float)(X * S[i]);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int ct = 0; ct < CT; ct++) {
         const double *S = sSb + 16 * ct + 4 * grp;
@@ -940,12 +955,7 @@ __device__ __forceinline__ void resident_block(const uint4 &meta, const uint2 (&
         for (int i = 0; i < 4; i++) {
             const int Cb = 8 * ah[ct][i] + al[ct][i];
             float pc;
-            if (fast) {
-                // no piece is tiny: the conversion needs no flush; an exact -0 added to +0 or to a
-                // nonzero partial sum gives what +0 would
-                const double X = __builtin_fma((double)Cb, Dd, -((double)ao[ct][i] * Dm));
-                pc = (float)(X * S[i]);
-            } else if (near) {
+            if (near) {
                 pc = piece_q4k_perblock_near(Cb, ao[ct][i], Dd, Dm, S[i]);
             } else {
                 const int m = (int)((Wd[i] >> 16) & 0xFFu);
