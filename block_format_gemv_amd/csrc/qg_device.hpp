@@ -506,16 +506,6 @@ __device__ __forceinline__ bool sum8_pair(const double (&T)[8], int low, float &
     return true;
 }
 
-// A whole number F < 2^21 as a binary64, built from its bits: exact, and when F is the same
-// for every lane the work stays in scalar registers (no vector conversion).  The low word of
-// the result is zero: F has at most 21 significant bits, all of them in the high word.
-__device__ __forceinline__ double small_uint_f64(uint32_t F)
-{
-    const int lz = __builtin_clz(F | 1u);
-    const uint32_t hi = ((F << (lz - 11)) + ((uint32_t)(1053 - lz) << 20)) & (0u - (uint32_t)(F != 0u));
-    return __builtin_bit_cast(double, (uint64_t)hi << 32);
-}
-
 // R32 of y = 2^emin * V when y is V's binary64 rounding scaled by a power of two (no underflow):
 // the two roundings give V's own binary32 rounding unless y lies on a binary32 rounding boundary
 // (bit 28 of the binary64 significand set, bits 0..27 clear: the midpoint of two binary32
@@ -531,9 +521,10 @@ __device__ __forceinline__ bool r32_of_rounded(double y, float &out)
 }
 
 // The activation side of a Q4_K-style Sub32 group, the same on every lane of a tile: the scales,
-// their exponent extremes, whether the first route below applies (significands at most 15, the
-// quantizer's, and exponents within 16 places) and then F_j = m_j * 2^(e_j - emin) (< 2^20,
-// built in scalar registers), else F_j = 0.
+// their exponent extremes, whether the first route below applies (every significand in 8..15, as
+// the quantizer gives them, and the exponents within 16 places) and then F_j = m_j * 2^(e_j -
+// emin), else F_j = 0.  F_j is built from its bits in scalar registers: with m = 8 + r (r < 8),
+// m * 2^d has the binary64 exponent 3 + d and the top three fraction bits r, all in the high word.
 struct Sub32Act {
     int m[8], e[8];
     int emin, emax;
@@ -544,22 +535,25 @@ struct Sub32Act {
 __device__ __forceinline__ Sub32Act sub32_act(const int (&m)[8], const int (&e)[8])
 {
     Sub32Act g;
-    // extremes in scalar registers (a read of the first lane after each step keeps them there)
-    int emin = e[0], emax = e[0], mmax = m[0];
+    // the extremes, and (m ^ 8) or-ed together (below 8 exactly when every m is in 8..15), in
+    // scalar registers: a read of the first lane after each step keeps them there
+    int emin = e[0], emax = e[0];
+    uint32_t mo = (uint32_t)m[0] ^ 8u;
 #pragma unroll
     for (int j = 1; j < 8; j++) {
         emin = __builtin_amdgcn_readfirstlane(e[j] < emin ? e[j] : emin);
         emax = __builtin_amdgcn_readfirstlane(e[j] > emax ? e[j] : emax);
-        mmax = __builtin_amdgcn_readfirstlane(m[j] > mmax ? m[j] : mmax);
+        mo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(mo | ((uint32_t)m[j] ^ 8u)));
     }
     g.emin = emin;
     g.emax = emax;
-    g.fast = emax - emin <= 16 && mmax <= 15;
+    g.fast = emax - emin <= 16 && mo < 8u;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         g.m[j] = m[j];
         g.e[j] = e[j];
-        g.F[j] = small_uint_f64(g.fast ? (uint32_t)m[j] << (e[j] - emin) : 0u);
+        const uint32_t hi = ((uint32_t)(1026 + e[j] - emin) << 20) | (((uint32_t)m[j] & 7u) << 17);
+        g.F[j] = __builtin_bit_cast(double, (uint64_t)(g.fast ? hi : 0u) << 32);
     }
     return g;
 }
@@ -567,7 +561,7 @@ __device__ __forceinline__ Sub32Act sub32_act(const int (&m)[8], const int (&e)[
 // Sub32, Q4_K-style: R32(sum_j m_j 2^e_j (d*C_j - dmin*O_j)), the sixteen terms of exact_sum.
 //
 // First route (g.fast; all sixteen term exponents then lie within 16 + 29 places, so the sum
-// window cannot engage): IC = sum F_j C_j (< 2^45) and IO = sum F_j O_j (< 2^41) are exact f64
+// window cannot engage; F_j < 2^20): IC = sum F_j C_j (< 2^45) and IO = sum F_j O_j (< 2^41) are exact f64
 // sums and the group is 2^emin * (d*IC - dmin*IO).  dmin*IO is exact (< 2^52), so one fma
 // gives V = d*IC - dmin*IO rounded once to binary64, and r32_of_rounded turns 2^emin times that
 // into the piece.  False (out untouched) when it sits on a binary32 rounding boundary or below
