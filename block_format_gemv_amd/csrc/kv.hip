@@ -442,7 +442,7 @@ __device__ __forceinline__ void form_batch(const uint32_t *rec, const uint32_t (
 }
 
 template <int HD>
-__global__ __launch_bounds__(256) void kv_weighted_pieces_kernel(int grp, int64_t npos, int64_t nblk,
+__global__ __launch_bounds__(256) void kv_weighted_pieces_kernel(int nkv, int grp, int64_t npos, int64_t nblk,
                                                                  const float *__restrict__ probs,
                                                                  const uint16_t *__restrict__ vscales,
                                                                  const int8_t *__restrict__ vcodes,
@@ -451,10 +451,12 @@ __global__ __launch_bounds__(256) void kv_weighted_pieces_kernel(int grp, int64_
     constexpr int EL = HD / 4;                 // lanes per value row
     constexpr int HS = 64 / EL;                // head slots per wave
     __shared__ __align__(16) uint32_t s_rec[4][16 * kRec];
-    const int kv = (int)blockIdx.y;
+    // workgroup i takes KV head i % nkv and blocks 4(i / nkv) ..: workgroups are dealt to the 8
+    // XCDs in turn, so with nkv a multiple of 8 every piece of a KV head is written from one XCD
+    const int kv = (int)(blockIdx.x % (unsigned)nkv);
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
-    const int64_t blk = (int64_t)blockIdx.x * 4 + wid;
+    const int64_t blk = (int64_t)(blockIdx.x / (unsigned)nkv) * 4 + wid;
     if (blk >= nblk) return;                   // nothing waits for this wave
     const int64_t j0 = blk * kValueBlock;
     const int nj = (int)(npos - j0 < kValueBlock ? npos - j0 : kValueBlock);
@@ -493,8 +495,8 @@ template <int HD>
 void weighted_pieces_typed(int nkv, int grp, int64_t npos, int64_t nblk, const float *p, const uint16_t *vs,
                            const int8_t *vc, float *ws, hipStream_t s)
 {
-    hipLaunchKernelGGL((kv_weighted_pieces_kernel<HD>), dim3((unsigned)((nblk + 3) / 4), (unsigned)nkv), dim3(256), 0,
-                       s, grp, npos, nblk, p, vs, vc, ws);
+    hipLaunchKernelGGL((kv_weighted_pieces_kernel<HD>), dim3((unsigned)((nblk + 3) / 4 * nkv)), dim3(256), 0,
+                       s, nkv, grp, npos, nblk, p, vs, vc, ws);
 }
 
 }  // namespace
@@ -643,6 +645,9 @@ int launch_kv_weighted_two_pass(int64_t nh, int64_t nkv, int64_t npos, int64_t h
     if (nh == 0) return QG_OK;
     const int grp = (int)(nh / nkv), g = (int)nkv;
     const int64_t nblk = (npos + kValueBlock - 1) / kValueBlock;
+    if ((nblk + 3) / 4 * nkv > 0x7fffffff)
+        return fail(QG_E_SHAPE, "kv weighted: %lld positions x %lld KV heads is too many", (long long)npos,
+                    (long long)nkv);
     hipEvent_t ev0, ev1;
     take_timing_events(&ev0, &ev1);   // the span of both passes
     if (ev0 && ev1 && hipEventRecord(ev0, s) != hipSuccess)
@@ -653,7 +658,7 @@ int launch_kv_weighted_two_pass(int64_t nh, int64_t nkv, int64_t npos, int64_t h
         else if (hd == 128) weighted_pieces_typed<128>(g, grp, npos, nblk, probs, vscales, vcodes, ws, s);
         else weighted_pieces_typed<256>(g, grp, npos, nblk, probs, vscales, vcodes, ws, s);
     }
-    launch_kv_fold_pieces(nh * hd, (int)hd, nblk, ws, out, s);
+    launch_kv_fold_pieces(nh * hd, (int)hd, nblk, nkv, ws, out, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_E_RUNTIME, "kv weighted (two passes) launch: %s", hipGetErrorString(e));
     if (ev0 && ev1 && hipEventRecord(ev1, s) != hipSuccess)

@@ -21,11 +21,16 @@ constexpr int kFoldChunk = 128;   // pieces a lane has in flight
 // element e from the workspace f32 [nh][nblk][HD] in chunks of 128 blocks: every load of a
 // chunk issued first (a short last chunk reads block min(b, last) again, so that none waits on
 // a branch), then the adds, each waiting only for its own piece (loads return in order).
+// With per_kv > 0 (the workgroups of one KV head's query heads), workgroup i takes the
+// elements of workgroup (i % nkv) * per_kv + i / nkv: the heads of KV head k then run on the XCD
+// that wrote their pieces (the pieces kernel deals KV head k's workgroups to XCD k mod 8).
 template <int HD>
-__global__ __launch_bounds__(64) void kv_weighted_fold_kernel(int64_t total, int nblk, const float *__restrict__ pieces,
-                                                              float *__restrict__ out)
+__global__ __launch_bounds__(64) void kv_weighted_fold_kernel(int64_t total, int nblk, int nkv, int per_kv,
+                                                              const float *__restrict__ pieces, float *__restrict__ out)
 {
-    const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    const unsigned i = blockIdx.x;
+    const int64_t w = per_kv > 0 ? (int64_t)(i % (unsigned)nkv) * per_kv + i / (unsigned)nkv : (int64_t)i;
+    const int64_t t = w * 64 + threadIdx.x;
     if (t >= total) return;
     const int64_t h = t / HD;
     const float *p = pieces + ((size_t)h * (size_t)nblk * HD + (size_t)(t - h * HD));
@@ -55,14 +60,18 @@ __global__ __launch_bounds__(64) void kv_weighted_fold_kernel(int64_t total, int
 
 }  // namespace
 
-void launch_kv_fold_pieces(int64_t total, int hd, int64_t nblk, const float *pieces, float *out, hipStream_t s)
+void launch_kv_fold_pieces(int64_t total, int hd, int64_t nblk, int64_t nkv, const float *pieces, float *out,
+                           hipStream_t s)
 {
     if (total == 0) return;
     const dim3 grid((unsigned)((total + 63) / 64)), block(64);
-    if (hd == 32) hipLaunchKernelGGL((kv_weighted_fold_kernel<32>), grid, block, 0, s, total, (int)nblk, pieces, out);
-    else if (hd == 64) hipLaunchKernelGGL((kv_weighted_fold_kernel<64>), grid, block, 0, s, total, (int)nblk, pieces, out);
-    else if (hd == 128) hipLaunchKernelGGL((kv_weighted_fold_kernel<128>), grid, block, 0, s, total, (int)nblk, pieces, out);
-    else hipLaunchKernelGGL((kv_weighted_fold_kernel<256>), grid, block, 0, s, total, (int)nblk, pieces, out);
+    // the workgroups per KV head: whole ones from head size 64 (total = nkv * grp * hd)
+    const int per_kv = hd >= 64 ? (int)(total / nkv / 64) : 0;
+    const int n = (int)nblk, g = (int)nkv;
+    if (hd == 32) hipLaunchKernelGGL((kv_weighted_fold_kernel<32>), grid, block, 0, s, total, n, g, per_kv, pieces, out);
+    else if (hd == 64) hipLaunchKernelGGL((kv_weighted_fold_kernel<64>), grid, block, 0, s, total, n, g, per_kv, pieces, out);
+    else if (hd == 128) hipLaunchKernelGGL((kv_weighted_fold_kernel<128>), grid, block, 0, s, total, n, g, per_kv, pieces, out);
+    else hipLaunchKernelGGL((kv_weighted_fold_kernel<256>), grid, block, 0, s, total, n, g, per_kv, pieces, out);
 }
 
 }  // namespace qg

@@ -81,7 +81,8 @@ int launch_kv_scores(int mode, int64_t nh, int64_t nkv, int64_t npos, int64_t hd
 int launch_kv_weighted(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs, const uint16_t *vscales,
                        const int8_t *vcodes, float *out, hipStream_t s);
 size_t kv_weighted_workspace_bytes(int64_t nh, int64_t npos, int64_t hd);
-void launch_kv_fold_pieces(int64_t total, int hd, int64_t nblk, const float *pieces, float *out, hipStream_t s);
+void launch_kv_fold_pieces(int64_t total, int hd, int64_t nblk, int64_t nkv, const float *pieces, float *out,
+                           hipStream_t s);
 int launch_kv_weighted_noalloc(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs,
                                const uint16_t *vscales, const int8_t *vcodes, float *out, hipStream_t s);
 int launch_kv_weighted_two_pass(int64_t nh, int64_t nkv, int64_t npos, int64_t hd, const float *probs,
