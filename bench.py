@@ -55,18 +55,18 @@ KERNEL_SOURCES = ("block_format_gemv_amd/csrc/gemv.hip", "block_format_gemv_amd/
                   "block_format_gemv_amd/csrc/qg_internal.hpp")
 MEASURED_TRAFFIC = {
     # (workload, dominant kernel): medians per dispatch, kernel sources hash
-    ("q4k_ffn_up_14336x4096", "fused"): {"kernel_sha": "8902980ef5c89fb3", "fetch_kib": 16240.5, "write_kib": 61.0625},
-    ("q4k_ffn_up_14336x4096", "gemv"): {"kernel_sha": "8902980ef5c89fb3", "fetch_kib": 16183.5, "write_kib": 56.0},
-    ("q4k_attn_4096x4096", "fused"): {"kernel_sha": "8902980ef5c89fb3", "fetch_kib": 4716.5, "write_kib": 21.0625},
-    ("q4k_attn_4096x4096", "gemv"): {"kernel_sha": "8902980ef5c89fb3", "fetch_kib": 4659.0, "write_kib": 16.0},
-    ("q4k_sub32_14336x4096", "fused"): {"kernel_sha": "8902980ef5c89fb3", "fetch_kib": 16265.0, "write_kib": 61.5},
-    ("q4k_sub32_14336x4096", "gemv"): {"kernel_sha": "8902980ef5c89fb3", "fetch_kib": 16207.9375, "write_kib": 56.0},
-    ("q6k_output_128256x4096", "fused"): {"kernel_sha": "8902980ef5c89fb3", "fetch_kib": 210538.5, "write_kib": 506.0625},
-    ("q6k_output_128256x4096", "gemv"): {"kernel_sha": "8902980ef5c89fb3", "fetch_kib": 210483.5, "write_kib": 501.0},
-    ("q8_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "8902980ef5c89fb3", "fetch_kib": 30580.5, "write_kib": 61.5},
-    ("q8_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "8902980ef5c89fb3", "fetch_kib": 30526.0, "write_kib": 56.0},
-    ("q4_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "8902980ef5c89fb3", "fetch_kib": 16244.5, "write_kib": 61.5},
-    ("q4_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "8902980ef5c89fb3", "fetch_kib": 16195.5, "write_kib": 56.0},
+    ("q4k_ffn_up_14336x4096", "fused"): {"kernel_sha": "ee861e45e0dbc1ee", "fetch_kib": 16240.5, "write_kib": 61.0625},
+    ("q4k_ffn_up_14336x4096", "gemv"): {"kernel_sha": "ee861e45e0dbc1ee", "fetch_kib": 16184.5, "write_kib": 56.0},
+    ("q4k_attn_4096x4096", "fused"): {"kernel_sha": "ee861e45e0dbc1ee", "fetch_kib": 4716.5, "write_kib": 21.0625},
+    ("q4k_attn_4096x4096", "gemv"): {"kernel_sha": "ee861e45e0dbc1ee", "fetch_kib": 4659.0, "write_kib": 16.0},
+    ("q4k_sub32_14336x4096", "fused"): {"kernel_sha": "ee861e45e0dbc1ee", "fetch_kib": 16264.4375, "write_kib": 61.5},
+    ("q4k_sub32_14336x4096", "gemv"): {"kernel_sha": "ee861e45e0dbc1ee", "fetch_kib": 16209.0, "write_kib": 56.0},
+    ("q6k_output_128256x4096", "fused"): {"kernel_sha": "ee861e45e0dbc1ee", "fetch_kib": 210541.0, "write_kib": 506.0625},
+    ("q6k_output_128256x4096", "gemv"): {"kernel_sha": "ee861e45e0dbc1ee", "fetch_kib": 210487.0, "write_kib": 501.0},
+    ("q8_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "ee861e45e0dbc1ee", "fetch_kib": 30580.5, "write_kib": 61.5},
+    ("q8_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "ee861e45e0dbc1ee", "fetch_kib": 30526.0, "write_kib": 56.0},
+    ("q4_0_ffn_up_14336x4096", "fused"): {"kernel_sha": "ee861e45e0dbc1ee", "fetch_kib": 16244.5, "write_kib": 61.5},
+    ("q4_0_ffn_up_14336x4096", "gemv"): {"kernel_sha": "ee861e45e0dbc1ee", "fetch_kib": 16195.5, "write_kib": 56.0},
 }
 
 # The batched GEMM kernels (several columns): HBM traffic as above, and for the int8
@@ -78,12 +78,12 @@ MEASURED_TRAFFIC = {
 GEMM_SOURCES = KERNEL_SOURCES + ("block_format_gemv_amd/csrc/gemm_mfma.hip",)
 MFMA_PEAK_TOPS = 5000.0     # dense int8 matrix-core peak of the part, TOP/s
 MEASURED_GEMM = {
-    "q4k_gemm_n2_4096x4096": {"kernel_sha": "53183223e1fbd6e8", "fetch_kib": 4687.0, "write_kib": 32.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.27},
-    "q4k_gemm_n8_4096x4096": {"kernel_sha": "53183223e1fbd6e8", "fetch_kib": 4784.5, "write_kib": 128.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.33},
-    "q4k_gemm_n64_4096x4096": {"kernel_sha": "53183223e1fbd6e8", "fetch_kib": 5722.5, "write_kib": 1024.0, "mops_i8": 12582912.0, "mfma_util_pct": 6.05},
-    "q4k_gemm_n2_14336x4096": {"kernel_sha": "53183223e1fbd6e8", "fetch_kib": 16220.0, "write_kib": 112.0},
-    "q4k_gemm_n8_14336x4096": {"kernel_sha": "53183223e1fbd6e8", "fetch_kib": 16328.5, "write_kib": 448.0, "mops_i8": 11010048.0, "mfma_util_pct": 5.3},
-    "q4k_gemm_n64_14336x4096": {"kernel_sha": "53183223e1fbd6e8", "fetch_kib": 17588.625, "write_kib": 3584.0, "mops_i8": 44040192.0, "mfma_util_pct": 13.88},
+    "q4k_gemm_n2_4096x4096": {"kernel_sha": "7b8527e8a94b503f", "fetch_kib": 4687.0, "write_kib": 32.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.3},
+    "q4k_gemm_n8_4096x4096": {"kernel_sha": "7b8527e8a94b503f", "fetch_kib": 4784.5, "write_kib": 128.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.25},
+    "q4k_gemm_n64_4096x4096": {"kernel_sha": "7b8527e8a94b503f", "fetch_kib": 5722.5, "write_kib": 1024.0, "mops_i8": 12582912.0, "mfma_util_pct": 5.78},
+    "q4k_gemm_n2_14336x4096": {"kernel_sha": "7b8527e8a94b503f", "fetch_kib": 16220.0, "write_kib": 112.0},
+    "q4k_gemm_n8_14336x4096": {"kernel_sha": "7b8527e8a94b503f", "fetch_kib": 16328.5, "write_kib": 448.0, "mops_i8": 11010048.0, "mfma_util_pct": 5.26},
+    "q4k_gemm_n64_14336x4096": {"kernel_sha": "7b8527e8a94b503f", "fetch_kib": 17588.625, "write_kib": 3584.0, "mops_i8": 44040192.0, "mfma_util_pct": 13.89},
 }
 
 
