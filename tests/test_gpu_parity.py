@@ -660,16 +660,30 @@ def _subnormal_partial_q4k(f, r):
     f["dmin"][r, :3] = [0, 801, 0]
 
 
+def _negative_zero_tail_q4k(f, r):
+    """Row r as in _subnormal_partial_q4k, but block 2's piece is -1 * 16380 * 2^-142: a negative
+    subnormal, flushed to -0 and added to the partial sum that is already -0, which stays -0 (an
+    add of +0 there would give +0)."""
+    _subnormal_partial_q4k(f, r)
+    f["q"][r, 512:768] = 0
+    f["sc"][r, 16:24] = 0
+    f["mn"][r, 16:24] = 1
+    f["d"][r, 2] = 0
+    f["dmin"][r, 2] = 1
+
+
 @pytest.mark.parametrize("ncol,tiny", [(16, (3, 15)), (64, (0, 63)), (100, (70,))])
 def test_subnormal_partial_sums_gemv_and_gemm(qg, ncol, tiny):
-    """Rows whose running sum passes through the subnormal range, through the GEMV and every
-    GEMM form: all must give the oracle's bits, which differ from unflushed adds.  With 100
+    """Rows whose running sum passes through the subnormal range (one of them then adds a piece
+    that is itself flushed to -0, keeping the -0), through the GEMV and every GEMM form: all
+    must give the oracle's bits, which differ from unflushed adds.  With 100
     columns the tiny activation row lies in the second batch of 64 only, so the first batch
     takes the matrix-core kernel's plain-add combine and the second its flushed one."""
     rows, cols = 70, 768
     f = gen.q4k_fields(rows, cols, 77)
     for r in (0, 5, 69):
         _subnormal_partial_q4k(f, r)
+    _negative_zero_tail_q4k(f, 33)
     M = Mat(qg, f)
     xs = gen.act_outliers(ncol, cols, 78)
     for t in tiny:
@@ -684,12 +698,14 @@ def test_subnormal_partial_sums_gemv_and_gemm(qg, ncol, tiny):
     plain = np.float32(plain + np.float32(8 * unit))
     assert plain.view(np.uint32) != bits(want[t0])[0]
     assert bits(want[t0])[0] == np.float32(8 * unit).view(np.uint32)
+    assert bits(want[t0])[33] == 0x80000000                     # -0 kept through a -0 piece
     one = qg.alloc_act(1, cols, 0)
     one.codes.copy_(act.codes[t0:t0 + 1]); one.scales.copy_(act.scales[t0:t0 + 1]); one.csums.copy_(act.csums[t0:t0 + 1])
     assert first_mismatch(run_gemv(qg, M, one), want[t0]) is None
     try:
         qg.qg_set_tuning(qg.TUNE_MFMA_MIN_COLS, 1)
-        for form, tab in ((1, 0), (2, 0), (2, 1), (3, 0)):       # staged, shared (tables or not), split
+        # staged, shared (tables or not), split, column-resident
+        for form, tab in ((1, 0), (2, 0), (2, 1), (3, 0), (4, 0)):
             if form == 1 and ncol > 16:
                 continue
             qg.qg_set_tuning(qg.TUNE_MFMA_FORM, form)

@@ -465,6 +465,40 @@ def test_fold_is_sequential_float32_and_order_matters():
     assert np.max(np.abs(tree - out) / np.maximum(np.abs(out), 1e-30)) < 1e-5
 
 
+def test_fold_keeps_negative_zero_through_a_flushed_piece():
+    """One row of three blocks under an activation block of all 2^-112 (codes 126, scale
+    130 * 2^-126) whose pieces are 800u, -801u and -1u, u = 16380 * 2^-142: the first two cancel
+    to a negative subnormal partial sum, which the flushed add turns into -0; the third piece is
+    itself a negative subnormal, so it is -0, and -0 + -0 stays -0.  Had that piece been +0 (or
+    been added as +0 + piece), the row would end at +0."""
+    f = gen.q4k_fields(1, 768, 77)
+    f["q"][0, :768] = 1
+    f["q"][0, 256:768] = 0
+    f["sc"][0, :24] = 0
+    f["sc"][0, :8] = 1
+    f["mn"][0, :24] = 1
+    f["mn"][0, :8] = 0
+    f["d"][0, :3] = [800, 0, 0]                     # binary16 subnormals k * 2^-24
+    f["dmin"][0, :3] = [0, 801, 1]
+    x = np.full((1, 768), np.float32(2.0 ** -112))
+    c, m, e, _ = oracle.quantize(x, oracle.PERBLOCK)
+    assert int(c[0, 0]) == 126 and int(m[0, 0]) == 130 and int(e[0, 0]) == -126
+    unit = 16380.0 * 2.0 ** -142
+    # the pieces from the exact sum of each block's two products (C * d * s and -O * dmin * s)
+    p0 = oracle.exact_sum([32256 * 800 * 130], [-150])
+    p1 = oracle.exact_sum([-32256 * 801 * 130], [-150])
+    p2 = oracle.exact_sum([-32256 * 1 * 130], [-150])
+    assert p0 == np.float32(800 * unit) and p1 == np.float32(-801 * unit)
+    assert f32bits(p2) == 0x80000000
+    y = ftz_np(np.float32(0.0) + np.float32(p0))
+    y = ftz_np(y + np.float32(p1))
+    assert f32bits(y) == 0x80000000
+    assert f32bits(ftz_np(y + np.float32(p2))) == 0x80000000
+    assert f32bits(ftz_np(y + np.float32(0.0))) == 0
+    out = oracle.gemv(f, c, m, e, oracle.PERBLOCK)
+    assert f32bits(out[0]) == 0x80000000
+
+
 def test_exponent_invariance():
     f, x = gen.tiny_q4k()
     for mode in (oracle.PERBLOCK, oracle.SUB32):
