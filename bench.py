@@ -78,12 +78,12 @@ MEASURED_TRAFFIC = {
 GEMM_SOURCES = KERNEL_SOURCES + ("block_format_gemv_amd/csrc/gemm_mfma.hip",)
 MFMA_PEAK_TOPS = 5000.0     # dense int8 matrix-core peak of the part, TOP/s
 MEASURED_GEMM = {
-    "q4k_gemm_n2_4096x4096": {"kernel_sha": "7b8527e8a94b503f", "fetch_kib": 4687.0, "write_kib": 32.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.3},
-    "q4k_gemm_n8_4096x4096": {"kernel_sha": "7b8527e8a94b503f", "fetch_kib": 4784.5, "write_kib": 128.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.25},
-    "q4k_gemm_n64_4096x4096": {"kernel_sha": "7b8527e8a94b503f", "fetch_kib": 5722.5, "write_kib": 1024.0, "mops_i8": 12582912.0, "mfma_util_pct": 5.78},
-    "q4k_gemm_n2_14336x4096": {"kernel_sha": "7b8527e8a94b503f", "fetch_kib": 16220.0, "write_kib": 112.0},
-    "q4k_gemm_n8_14336x4096": {"kernel_sha": "7b8527e8a94b503f", "fetch_kib": 16328.5, "write_kib": 448.0, "mops_i8": 11010048.0, "mfma_util_pct": 5.26},
-    "q4k_gemm_n64_14336x4096": {"kernel_sha": "7b8527e8a94b503f", "fetch_kib": 17588.625, "write_kib": 3584.0, "mops_i8": 44040192.0, "mfma_util_pct": 13.89},
+    "q4k_gemm_n2_4096x4096": {"kernel_sha": "0798631ed8d0ef3a", "fetch_kib": 4687.5, "write_kib": 32.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.43},
+    "q4k_gemm_n8_4096x4096": {"kernel_sha": "0798631ed8d0ef3a", "fetch_kib": 4785.0, "write_kib": 128.0, "mops_i8": 3145728.0, "mfma_util_pct": 2.2},
+    "q4k_gemm_n64_4096x4096": {"kernel_sha": "0798631ed8d0ef3a", "fetch_kib": 5724.5, "write_kib": 1024.0, "mops_i8": 12582912.0, "mfma_util_pct": 5.95},
+    "q4k_gemm_n2_14336x4096": {"kernel_sha": "0798631ed8d0ef3a", "fetch_kib": 16220.0, "write_kib": 112.0},
+    "q4k_gemm_n8_14336x4096": {"kernel_sha": "0798631ed8d0ef3a", "fetch_kib": 16328.5, "write_kib": 448.0, "mops_i8": 11010048.0, "mfma_util_pct": 5.27},
+    "q4k_gemm_n64_14336x4096": {"kernel_sha": "0798631ed8d0ef3a", "fetch_kib": 17589.625, "write_kib": 3584.0625, "mops_i8": 44040192.0, "mfma_util_pct": 14.15},
 }
 
 

@@ -856,9 +856,10 @@ int launch_staged_typed(int64_t rows, int G, int64_t ncol, const void *image, co
 // block's codes of its columns into LDS by LDS-DMA (the staged form's layout: column rows
 // padded by 16 bytes) and its columns' activation scales per block into tables; one barrier.
 // After it each wave walks its tile's blocks alone, with no further barrier: its rows' code
-// chunks and block fields loaded three blocks ahead into a register ring, the three products
-// per column tile from LDS operands (the staged form's K order), each (row, column) combined
-// once and added in block order to the lane's running sums in registers.  The waves of a SIMD
+// chunks and block fields loaded six blocks ahead into a register ring, blocks taken two at a
+// time (the three products per column tile of both, from LDS operands in the staged form's K
+// order, formed step by step together), each (row, column) combined once and added in block
+// order to the lane's running sums in registers.  The waves of a SIMD
 // drift apart, so the matrix unit and the vector ALU serve different waves at once.
 //
 // grid: row chunks x column batches, the batches of one chunk on one XCD (x = (chunk/8 *
@@ -967,6 +968,103 @@ __device__ __forceinline__ void resident_block(const uint4 &meta, const uint2 (&
     }
 }
 
+// two consecutive blocks of a wave's row tile: the products of both formed step by step
+// together (twice the independent matrix and vector work between waits), then each block
+// combined and added to y in block order, as resident_block does
+template <int CT, bool TINY>
+__device__ __forceinline__ void resident_pair(const uint4 &m0, const uint2 (&c0)[4], const uint4 &m1,
+                                              const uint2 (&c1)[4], const unsigned char *acodes, int cs, int b,
+                                              const double *sSb, const uint32_t *sWb, int lane, float (&y)[CT][4])
+{
+    constexpr int NC = 16 * CT;
+    const int n = lane & 15, grp = lane >> 4, h = grp & 1, jo = grp >> 1;
+    const uint32_t sh = 12u * (uint32_t)jo;
+    uint32_t fs[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const uint4 &meta = u ? m1 : m0;
+        const uint64_t lo64 = ((uint64_t)meta.z << 32 | meta.y) >> sh;
+        const uint32_t y1 = (uint32_t)(((uint64_t)meta.w << 32 | meta.z) >> sh);
+        const uint32_t y2 = meta.w >> sh;
+        fs[u][0] = (uint32_t)lo64 & 0xFFFu;
+        fs[u][1] = (uint32_t)(lo64 >> 24) & 0xFFFu;
+        fs[u][2] = (y1 >> 16) & 0xFFFu;
+        fs[u][3] = (y2 >> 8) & 0xFFFu;
+    }
+    v4i ah[2][CT], al[2][CT], ao[2][CT];
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+        for (int ct = 0; ct < CT; ct++) ah[u][ct] = al[u][ct] = ao[u][ct] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int st = 0; st < 4; st++) {
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const uint32_t f = fs[u][st];
+            const uint32_t hi = (f >> 3) & 7u, lo = f & 7u;
+            const int mr = (int)__builtin_amdgcn_perm(0u, f >> 6, 0x00000000u);
+            const uint2 c2 = u ? c1[st] : c0[st];
+            const uint32_t q0 = c2.x & 0x0F0F0F0Fu, q1 = c2.y & 0x0F0F0F0Fu;
+            const uint32_t q2 = (c2.x >> 4) & 0x0F0F0F0Fu, q3 = (c2.y >> 4) & 0x0F0F0F0Fu;
+            const v4i Bh = {bytes_times(q0, hi), bytes_times(q1, hi), bytes_times(q2, hi), bytes_times(q3, hi)};
+            const v4i Bl = {bytes_times(q0, lo), bytes_times(q1, lo), bytes_times(q2, lo), bytes_times(q3, lo)};
+            const v4i Bo = {mr, mr, mr, mr};
+#pragma unroll
+            for (int ct = 0; ct < CT; ct++) {
+                const unsigned char *arow =
+                    acodes + (size_t)(16 * ct + n) * cs + (size_t)(b + u) * 256 + 32 * jo + 8 * h + 64 * st;
+                const uint2 lo8 = *reinterpret_cast<const uint2 *>(arow);
+                const uint2 hi8 = *reinterpret_cast<const uint2 *>(arow + 16);
+                const v4i A = {(int)lo8.x, (int)lo8.y, (int)hi8.x, (int)hi8.y};
+                ah[u][ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bh, ah[u][ct], 0, 0, 0);
+                al[u][ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bl, al[u][ct], 0, 0, 0);
+                ao[u][ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Bo, ao[u][ct], 0, 0, 0);
+            }
+        }
+    }
+    // combine each (row, column) once ("Module numerics", module description) and add it
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const uint32_t dd = u ? m1.x : m0.x;
+        const double *S0 = sSb + (size_t)u * NC;
+        const uint32_t *W0 = sWb + (size_t)u * NC;
+        const float fd = f16_value(dd), fm = f16_value(dd >> 16);
+        const bool near = q4k_near(fd, fm);
+        const double Dd = (double)fd, Dm = (double)fm;
+        if (!TINY && __all(near)) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ct++) {
+                const double *S = S0 + 16 * ct + 4 * grp;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int Cb = 8 * ah[u][ct][i] + al[u][ct][i];
+                    const double X = __builtin_fma((double)Cb, Dd, -((double)ao[u][ct][i] * Dm));
+                    y[ct][i] = y[ct][i] + (float)(X * S[i]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int ct = 0; ct < CT; ct++) {
+                const double *S = S0 + 16 * ct + 4 * grp;
+                const uint32_t *Wd = W0 + 16 * ct + 4 * grp;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int Cb = 8 * ah[u][ct][i] + al[u][ct][i];
+                    float pc;
+                    if (near) {
+                        pc = piece_q4k_perblock_near(Cb, ao[u][ct][i], Dd, Dm, S[i]);
+                    } else {
+                        const int m = (int)((Wd[i] >> 16) & 0xFFu);
+                        const int e = (int)(int16_t)(Wd[i] & 0xFFFFu);
+                        pc = piece_q4k_perblock(Cb, ao[u][ct][i], dd, m, e);
+                    }
+                    y[ct][i] = TINY ? fadd_ftz(y[ct][i], pc) : y[ct][i] + pc;
+                }
+            }
+        }
+    }
+}
+
 template <int CT, bool TINY, int D>
 __device__ __forceinline__ void resident_walk(const uint8_t *gbase, int G, int trow, const unsigned char *acodes,
                                               int cs, const double *sS, const uint32_t *sW, int lane, float (&y)[CT][4])
@@ -985,18 +1083,23 @@ __device__ __forceinline__ void resident_walk(const uint8_t *gbase, int G, int t
 #pragma unroll 1
     for (; b + D <= G; b += D) {             // whole rounds: a straight-line body
 #pragma unroll
-        for (int k = 0; k < D; k++) {
-            resident_block<CT, TINY>(m[k], c[k], acodes, cs, b + k, sS + (size_t)(b + k) * NC, sW + (size_t)(b + k) * NC,
-                                     lane, y);
+        for (int k = 0; k < D; k += 2) {
+            resident_pair<CT, TINY>(m[k], c[k], m[k + 1], c[k + 1], acodes, cs, b + k, sS + (size_t)(b + k) * NC,
+                                    sW + (size_t)(b + k) * NC, lane, y);
             resident_load(gbase + (size_t)min(b + k + D, G - 1) * kTileBytesQ4K, trow, jo, h, m[k], c[k]);
+            resident_load(gbase + (size_t)min(b + k + 1 + D, G - 1) * kTileBytesQ4K, trow, jo, h, m[k + 1], c[k + 1]);
         }
     }
     // the last blocks, fewer than D
 #pragma unroll
-    for (int k = 0; k < D - 1; k++)
-        if (b + k < G)
+    for (int k = 0; k < D - 1; k += 2) {
+        if (b + k + 1 < G)
+            resident_pair<CT, TINY>(m[k], c[k], m[k + 1], c[k + 1], acodes, cs, b + k, sS + (size_t)(b + k) * NC,
+                                    sW + (size_t)(b + k) * NC, lane, y);
+        else if (b + k < G)
             resident_block<CT, TINY>(m[k], c[k], acodes, cs, b + k, sS + (size_t)(b + k) * NC, sW + (size_t)(b + k) * NC,
                                      lane, y);
+    }
 }
 
 template <int CT, int GT>
